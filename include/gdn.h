@@ -1,0 +1,140 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the Gated DeltaNet gated delta rule on AMD Instinct MI355X
+ * (gfx950), chunked prefill and single-token recurrent decode.
+ *
+ * The operation (page "Gated DeltaNet 架构详解与 Qwen 3.5 的联系", section 6; page
+ * "Gated DeltaNet与推理脚手架：两个模糊边界的发现", section 发现一, the Gated DeltaNet update
+ * rule): for every sequence n and head h independently, with a state S in R^{dv x dk},
+ *
+ *     S_t = S_{t-1} * alpha_t * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,    o_t = scale * S_t q_t
+ *
+ * with alpha_t = exp(g_t).  The equivalent form every kernel evaluates is
+ *     u_t = beta_t (v_t - alpha_t S_{t-1} k_t),   S_t = alpha_t S_{t-1} + u_t k_t^T.
+ * The page maplevalley.com.cn/news/1910399, section 2.1 (门控机制的精准控制), gives the gate
+ * parameterisation g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b); the caller passes
+ * g and beta.  With GDN_QK_L2NORM, q and k are replaced by x * rsqrt(sum(x^2) + 1e-6) over the
+ * key dimension, per (token, head), inside the kernels.
+ *
+ * Conventions shared by every entry point
+ *  - All pointers are DEVICE pointers to contiguous, row-major memory, 16-byte aligned, except
+ *    where stated.  Nothing is copied to or from the host.
+ *  - Ownership: the caller allocates and frees every buffer.  The library allocates nothing,
+ *    frees nothing, keeps no mutable global state, launches only on `hip_stream` (a
+ *    hipStream_t; NULL = the null stream) and never synchronises.  Buffers must stay alive until
+ *    the stream's work has completed.  Calls are asynchronous: a returned GDN_OK means the
+ *    arguments were valid and the launches were enqueued without a launch error.
+ *  - Errors: every argument check runs on the host before any HIP call; on an invalid argument
+ *    nothing is launched and nothing is written.  No C++ exception crosses this ABI.  Device-side
+ *    contents (cu_seqlens values, NaN/Inf in data) are not checked: inconsistent cu_seqlens is
+ *    undefined behaviour; a NaN in one (sequence, head) never reaches another.
+ *  - Determinism: no atomics; results are bitwise reproducible run to run on the same device.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define GDN_OK 0
+#define GDN_ERR_INVALID_ARG 1  /* null pointer where one is required, negative size, bad alignment */
+#define GDN_ERR_UNSUPPORTED 2  /* shape/dtype/chunk this build does not implement                  */
+#define GDN_ERR_WORKSPACE 3    /* workspace missing or smaller than *workspace_bytes               */
+#define GDN_ERR_HIP 4          /* a HIP launch reported an error (hipGetLastError after launch)    */
+
+/* Element types of q, k, v and o.  g, beta and every state are always fp32. */
+#define GDN_F32 0
+#define GDN_BF16 1
+
+/* flags */
+#define GDN_QK_L2NORM 1u       /* L2-normalise q and k per (token, head) over dk, eps = 1e-6 */
+
+/*
+ * gdn_chunk_fwd -- chunked prefill over packed variable-length sequences.
+ *
+ * Defines: the call chunk_gated_delta_rule(query, key, value, g, beta, initial_state) ->
+ * (core_attn_out, last_state) on page maplevalley.com.cn/news/1910399, section 3.1
+ * (记忆系统的工程优化), computed by chunks: tokens inside a chunk in parallel, the state carried
+ * serially from chunk to chunk (page pzsr.cn/news/750, section 1、为什么要设计为chunk的模式).
+ * The chunk size changes only the rounding, never the result in exact arithmetic.
+ *
+ * Arguments (T_tot = total tokens of all sequences, packed back to back):
+ *  q, k        [T_tot, H, dk]  dtype   raw queries / keys (before conv, before L2 norm)
+ *  v           [T_tot, H, dv]  dtype   raw values
+ *  g           [T_tot, H]      fp32    log decay, alpha = exp(g); g <= 0 expected (any finite g works)
+ *  beta        [T_tot, H]      fp32    write strength
+ *  initial_state [N, H, dv, dk] fp32   S_0 per (sequence, head), S as in o = S q; NULL = zeros
+ *  cu_seqlens  [N + 1]         int32   sequence offsets into the packed token axis, non-decreasing,
+ *                                      cu_seqlens[0] = 0, cu_seqlens[N] = T_tot; NULL = N equal
+ *                                      sequences of T_tot / N tokens (then N must divide T_tot).
+ *                                      Zero-length sequences are allowed: final = initial, no o.
+ *  conv_w      [H*(2*dk + dv), 4] fp32 NULL, or the depthwise causal conv1d (4 taps) applied per
+ *                                      channel to q, k and v before SiLU and the L2 norm (page
+ *                                      maplevalley.com.cn/news/1910399, section 3.1, 卷积预处理).
+ *                                      Channel c < H*dk is q channel (h*dk + i), the next H*dk are
+ *                                      k channels, the last H*dv are v channels.  Tap j multiplies
+ *                                      token t-3+j (tap 3 = current token); history before a
+ *                                      sequence start is zero; no bias.
+ *  o           [T_tot, H, dv]  dtype   output; must not alias any input
+ *  final_state [N, H, dv, dk] fp32     last state per (sequence, head), or NULL = not written.
+ *                                      May alias initial_state exactly (same pointer).
+ *  workspace, workspace_bytes          device scratch for the long-sequence path.  If
+ *                                      *workspace_bytes is smaller than the size this call needs,
+ *                                      the call sets *workspace_bytes to that size and returns
+ *                                      GDN_ERR_WORKSPACE without launching (a NULL workspace with
+ *                                      *workspace_bytes = 0 is the size query).  workspace_bytes
+ *                                      may be NULL only when the call needs no workspace.
+ *                                      Needed only when cu_seqlens is NULL and (N*H) is small
+ *                                      against T_tot; see gdn_chunk_workspace_size.
+ *  N, T_tot, H, dk, dv                 sizes; dk, dv in {32, 64, 128}; N >= 1, T_tot >= 0, H >= 1
+ *  dtype       GDN_F32 or GDN_BF16     (fp32 path: exact fp32 arithmetic throughout; bf16 path:
+ *                                      bf16 MFMA operands, fp32 accumulation, fp32 state)
+ *  chunk       64                      chunk length; other values -> GDN_ERR_UNSUPPORTED
+ *  scale       output scale (1.0 = o_t = S_t q_t)
+ *  flags       GDN_QK_L2NORM or 0
+ *  hip_stream  hipStream_t to launch on
+ */
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, const float* conv_w,
+                  void* o, float* final_state, void* workspace, size_t* workspace_bytes, int N,
+                  int T_tot, int H, int dk, int dv, int dtype, int chunk, float scale,
+                  unsigned flags, void* hip_stream);
+
+/*
+ * gdn_chunk_workspace_size -- the workspace gdn_chunk_fwd needs for these sizes (0 when the
+ * call runs without one).  Pure host function; returns GDN_OK and sets *bytes, or an error code
+ * for arguments gdn_chunk_fwd would reject.
+ */
+int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype, int chunk,
+                             int has_cu_seqlens, size_t* bytes);
+
+/*
+ * gdn_recurrent_step -- one decode token per sequence, state updated in place.
+ *
+ * Defines: the incremental (recurrent) update with a fixed-size state (page pzsr.cn/news/750,
+ * section a、增量更新: decay the whole state by alpha first, then erase and write along the
+ * current key with strength beta), which is the rule above with T = 1:
+ *     u = beta (v - alpha S k),  S <- alpha S + u k^T,  o = scale * S q.
+ *
+ *  q, k   [N, H, dk] dtype;  v [N, H, dv] dtype;  g, beta [N, H] fp32
+ *  state  [N, H, dv, dk] fp32, read and overwritten in place
+ *  o      [N, H, dv] dtype, must not alias any input
+ *  N, H >= 1 (N = 0 is a no-op returning GDN_OK); dk, dv in {32, 64, 128}
+ *  dtype, scale, flags, hip_stream as for gdn_chunk_fwd
+ */
+int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, float* state, void* o, int N, int H, int dk, int dv,
+                       int dtype, float scale, unsigned flags, void* hip_stream);
+
+/* gdn_status_string -- static, human-readable name of a status code (never NULL). */
+const char* gdn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,128 @@
+"""TEST INFRASTRUCTURE ONLY: the fp64 CPU oracle of the gated delta rule.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this package.  The product library (``linear_attention_sequence_rule_amd``) never imports, links
+or executes anything here, and nothing here imports the product library: the two share no code.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain C, double precision, token by token; see its
+header for the passages of the pages it follows).  This module only marshals numpy arrays into
+that library and builds it with gcc when it is missing.
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py`` (closed forms,
+special cases, brute-force products, numpy.convolve for the conv prologue).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "libgdn_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gdn_oracle.c into libgdn_oracle.so with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC",
+                               "-shared", "-o", tmp, _SRC, "-lpthread", "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        lib.gdn_oracle_forward.restype = ctypes.c_int
+        lib.gdn_oracle_forward.argtypes = [P] * 11 + [ctypes.c_int] * 4 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_int]
+        lib.gdn_oracle_step.restype = ctypes.c_int
+        lib.gdn_oracle_step.argtypes = [P] * 7 + [ctypes.c_int] * 4 + [
+            ctypes.c_double, ctypes.c_int, ctypes.c_int]
+        lib.gdn_oracle_gates.restype = None
+        lib.gdn_oracle_gates.argtypes = [P] * 6 + [ctypes.c_long, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def forward(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=None, *, N=None,
+            scale=1.0, l2norm=True, pairs=None, nthreads=0, want_o=True):
+    """Token-by-token fp64 gated delta rule over packed sequences.
+
+    q, k: [T_tot, H, dk]; v: [T_tot, H, dv]; g, beta: [T_tot, H]; initial_state [N, H, dv, dk]
+    or None (zeros); cu_seqlens [N+1] or None (then N equal sequences); conv_w [H*(2dk+dv), 4]
+    or None.  ``pairs``: optional iterable of (n, h) to compute; other pairs are left as NaN.
+    Returns (o [T_tot, H, dv] or None, final_state [N, H, dv, dk], threads_used).
+    """
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    T_tot, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is None:
+        if N is None:
+            N = 1
+        assert T_tot % N == 0
+        cu = np.arange(N + 1, dtype=np.int64) * (T_tot // N)
+    else:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+        N = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == T_tot and np.all(np.diff(cu) >= 0)
+    s0 = _f64(initial_state)
+    if s0 is not None:
+        assert s0.shape == (N, H, dv, dk)
+    cw = _f64(conv_w)
+    if cw is not None:
+        assert cw.shape == (H * (2 * dk + dv), 4)
+    mask = None
+    if pairs is not None:
+        mask = np.zeros(N * H, dtype=np.uint8)
+        for n, h in pairs:
+            mask[n * H + h] = 1
+    o = np.full((T_tot, H, dv), np.nan) if want_o else None
+    sfin = np.full((N, H, dv, dk), np.nan)
+    used = _load().gdn_oracle_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(cu), _ptr(cw), _ptr(o),
+        _ptr(sfin), _ptr(mask), N, H, dk, dv, float(scale), 1 if l2norm else 0, int(nthreads))
+    return o, sfin, used
+
+
+def step(q, k, v, g, beta, state, *, scale=1.0, l2norm=True, nthreads=0):
+    """One decode token per (sequence, head).  q, k [N,H,dk]; v [N,H,dv]; g, beta [N,H];
+    state [N,H,dv,dk].  Returns (o [N,H,dv], new_state) without modifying the inputs."""
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    st = np.array(state, dtype=np.float64, copy=True, order="C")
+    assert st.shape == (N, H, dv, dk)
+    o = np.empty((N, H, dv))
+    _load().gdn_oracle_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(st), _ptr(o),
+                            N, H, dk, dv, float(scale), 1 if l2norm else 0, int(nthreads))
+    return o, st
+
+
+def gates(a, b, A_log, dt_bias):
+    """g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b) in fp64.
+    a, b [T, H]; A_log, dt_bias [H].  Returns (g, beta) [T, H]."""
+    a, b, A_log, dt_bias = (_f64(x) for x in (a, b, A_log, dt_bias))
+    T, H = a.shape
+    g = np.empty((T, H))
+    beta = np.empty((T, H))
+    _load().gdn_oracle_gates(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(beta),
+                             T, H)
+    return g, beta
