@@ -1,0 +1,166 @@
+"""Gated DeltaNet gated delta rule on AMD Instinct MI355X (gfx950): Python binding of libgdn.so.
+
+The functions here carry the names of the C ABI (``include/gdn.h``) and only marshal arguments:
+they check tensor placement and dtypes, allocate outputs with torch (memory only), and pass raw
+device pointers and the current HIP stream to the library.  Every step of the computation runs
+in the library's HIP kernels; there is no CPU or PyTorch fallback.  If ``libgdn.so`` has not
+been built (``__graft_entry__.build()``) every call raises.
+
+    o, final_state = gdn_chunk_fwd(q, k, v, g, beta, initial_state, cu_seqlens)
+    o = gdn_recurrent_step(q, k, v, g, beta, state)          # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = ["gdn_chunk_fwd", "gdn_recurrent_step", "gdn_status_string", "gdn_chunk_workspace_size",
+           "GdnError", "lib_path", "load_library", "GDN_OK", "GDN_ERR_INVALID_ARG",
+           "GDN_ERR_UNSUPPORTED", "GDN_ERR_WORKSPACE", "GDN_ERR_HIP", "GDN_F32", "GDN_BF16",
+           "GDN_QK_L2NORM"]
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 0, 1, 2, 3, 4
+GDN_F32, GDN_BF16 = 0, 1
+GDN_QK_L2NORM = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdn.so")
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s returned %s" % (where, gdn_status_string(status)))
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgdn.so (built in-tree).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libgdn.so is not built (%s); run __graft_entry__.build() first" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, U, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_float
+    lib.gdn_chunk_fwd.restype = I
+    lib.gdn_chunk_fwd.argtypes = [P] * 12 + [I] * 7 + [F, U, P]
+    lib.gdn_chunk_workspace_size.restype = I
+    lib.gdn_chunk_workspace_size.argtypes = [I] * 8 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_recurrent_step.restype = I
+    lib.gdn_recurrent_step.argtypes = [P] * 7 + [I] * 5 + [F, U, P]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [I]
+    _lib = lib
+    return lib
+
+
+def gdn_status_string(status: int) -> str:
+    return load_library().gdn_status_string(int(status)).decode()
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _check_dev(name, t, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype=GDN_BF16, chunk=64, has_cu_seqlens=False) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype, chunk, int(bool(has_cu_seqlens)),
+                                                 ctypes.byref(n))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_chunk_workspace_size")
+    return int(n.value)
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=None, *, N=None, o=None,
+                  final_state=None, output_final_state=True, scale=1.0, l2norm=True, chunk=64, workspace=None,
+                  stream=None):
+    """Chunked prefill.  q, k [T_tot, H, dk]; v [T_tot, H, dv] (bf16 or fp32); g, beta [T_tot, H] fp32;
+    initial_state [N, H, dv, dk] fp32 or None; cu_seqlens [N+1] int32 or None (N equal sequences, N
+    given or 1); conv_w [H*(2dk+dv), 4] fp32 or None.  Returns (o, final_state or None)."""
+    import torch
+    lib = load_library()
+    T_tot, H, dk = q.shape
+    dv = v.shape[2]
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    for name, t in (("g", g), ("beta", beta), ("initial_state", initial_state), ("conv_w", conv_w),
+                    ("final_state", final_state)):
+        _check_dev(name, t, torch.float32)
+    _check_dev("cu_seqlens", cu_seqlens, torch.int32)
+    if cu_seqlens is not None:
+        N = cu_seqlens.shape[0] - 1
+    elif N is None:
+        N = initial_state.shape[0] if initial_state is not None else 1
+    if o is None:
+        o = torch.empty((T_tot, H, dv), dtype=q.dtype, device=q.device)
+    _check_dev("o", o, q.dtype)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    ws_bytes = ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size())
+    need = gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dt, chunk, cu_seqlens is not None)
+    if need > ws_bytes.value:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = ctypes.c_size_t(need)
+    st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+                           _ptr(conv_w), _ptr(o), _ptr(final_state), _ptr(workspace), ctypes.byref(ws_bytes), N,
+                           T_tot, H, dk, dv, dt, chunk, float(scale), GDN_QK_L2NORM if l2norm else 0,
+                           _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_recurrent_step(q, k, v, g, beta, state, *, o=None, scale=1.0, l2norm=True, stream=None):
+    """One decode token per sequence.  q, k [N, H, dk]; v [N, H, dv]; g, beta [N, H] fp32;
+    state [N, H, dv, dk] fp32, updated in place.  Returns o [N, H, dv]."""
+    import torch
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    for name, t in (("g", g), ("beta", beta), ("state", state)):
+        _check_dev(name, t, torch.float32)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    _check_dev("o", o, q.dtype)
+    st = lib.gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o), N, H, dk, dv,
+                                dt, float(scale), GDN_QK_L2NORM if l2norm else 0, _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_recurrent_step")
+    return o

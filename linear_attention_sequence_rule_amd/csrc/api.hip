@@ -1,0 +1,165 @@
+// api.hip -- the C ABI of libgdn.so (declared in include/gdn.h): host-side argument checks, then
+// dispatch to the gfx950 kernels on the caller's stream.  No allocation, no synchronisation, no
+// global mutable state; every check runs before the first HIP call.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+#include "kernels.hpp"
+
+namespace {
+
+bool dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges); null or empty never overlaps.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int check_common(int H, int dk, int dv, int dtype, float scale, unsigned flags) {
+    if (H < 1) return GDN_ERR_INVALID_ARG;
+    if (flags & ~GDN_QK_L2NORM) return GDN_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return GDN_ERR_INVALID_ARG;
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (!dim_ok(dk) || !dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(int status) {
+    switch (status) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    }
+    return "GDN_ERR_UNKNOWN";
+}
+
+int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype, int chunk, int has_cu_seqlens,
+                             size_t* bytes) {
+    if (!bytes) return GDN_ERR_INVALID_ARG;
+    if (N < 1 || T_tot < 0) return GDN_ERR_INVALID_ARG;
+    int st = check_common(H, dk, dv, dtype, 1.0f, 0);
+    if (st != GDN_OK) return st;
+    if (chunk != 64) return GDN_ERR_UNSUPPORTED;
+    if (!has_cu_seqlens && T_tot % N != 0) return GDN_ERR_INVALID_ARG;
+    *bytes = dtype == GDN_BF16 ? gdn::chunk_bf16_workspace(N, T_tot, H, dk, dv, has_cu_seqlens != 0) : 0;
+    return GDN_OK;
+}
+
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, const float* conv_w, void* o,
+                  float* final_state, void* workspace, size_t* workspace_bytes, int N, int T_tot, int H, int dk,
+                  int dv, int dtype, int chunk, float scale, unsigned flags, void* hip_stream) {
+    if (N < 1 || T_tot < 0) return GDN_ERR_INVALID_ARG;
+    int st = check_common(H, dk, dv, dtype, scale, flags);
+    if (st != GDN_OK) return st;
+    if (chunk != 64) return GDN_ERR_UNSUPPORTED;
+    if (!cu_seqlens && T_tot % N != 0) return GDN_ERR_INVALID_ARG;
+    if (T_tot > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, initial_state, cu_seqlens, conv_w, o, final_state};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
+
+    const size_t es = dtype == GDN_BF16 ? 2 : 4;
+    const size_t tq = (size_t)T_tot * H * dk * es, tv = (size_t)T_tot * H * dv * es;
+    const size_t tg = (size_t)T_tot * H * 4, ts = (size_t)N * H * dv * dk * 4;
+    const size_t tcu = cu_seqlens ? (size_t)(N + 1) * 4 : 0, tcw = conv_w ? (size_t)H * (2 * dk + dv) * 16 : 0;
+    // o must not overlap any input; final_state may equal initial_state exactly but not overlap otherwise.
+    if (overlaps(o, tv, q, tq) || overlaps(o, tv, k, tq) || overlaps(o, tv, v, tv) || overlaps(o, tv, g, tg) ||
+        overlaps(o, tv, beta, tg) || overlaps(o, tv, initial_state, ts) || overlaps(o, tv, final_state, ts) ||
+        overlaps(o, tv, cu_seqlens, tcu) || overlaps(o, tv, conv_w, tcw))
+        return GDN_ERR_INVALID_ARG;
+    if (final_state && final_state != initial_state &&
+        (overlaps(final_state, ts, initial_state, ts) || overlaps(final_state, ts, q, tq) ||
+         overlaps(final_state, ts, k, tq) || overlaps(final_state, ts, v, tv) || overlaps(final_state, ts, g, tg) ||
+         overlaps(final_state, ts, beta, tg) || overlaps(final_state, ts, cu_seqlens, tcu) ||
+         overlaps(final_state, ts, conv_w, tcw)))
+        return GDN_ERR_INVALID_ARG;
+
+    const size_t need =
+        dtype == GDN_BF16 ? gdn::chunk_bf16_workspace(N, T_tot, H, dk, dv, cu_seqlens != nullptr) : 0;
+    if (need > 0) {
+        if (!workspace_bytes) return GDN_ERR_INVALID_ARG;
+        if (!workspace || *workspace_bytes < need) {
+            *workspace_bytes = need;
+            return GDN_ERR_WORKSPACE;
+        }
+        if (!aligned16(workspace)) return GDN_ERR_INVALID_ARG;
+    }
+
+    gdn::ChunkArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.s0 = initial_state;
+    a.cu = cu_seqlens;
+    a.conv_w = conv_w;
+    a.o = o;
+    a.sfin = final_state;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes ? *workspace_bytes : 0;
+    a.N = N;
+    a.T_tot = T_tot;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.bf16 = dtype == GDN_BF16;
+    a.scale = scale;
+    a.l2norm = (flags & GDN_QK_L2NORM) ? 1 : 0;
+    a.stream = static_cast<hipStream_t>(hip_stream);
+    const hipError_t e = a.bf16 ? gdn::launch_chunk_bf16(a) : gdn::launch_chunk_f32(a);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
+                       void* o, int N, int H, int dk, int dv, int dtype, float scale, unsigned flags,
+                       void* hip_stream) {
+    if (N < 0) return GDN_ERR_INVALID_ARG;
+    int st = check_common(H, dk, dv, dtype, scale, flags);
+    if (st != GDN_OK) return st;
+    if (N == 0) return GDN_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, state, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN_ERR_INVALID_ARG;
+    const size_t es = dtype == GDN_BF16 ? 2 : 4;
+    const size_t tq = (size_t)N * H * dk * es, tv = (size_t)N * H * dv * es, tg = (size_t)N * H * 4;
+    const size_t ts = (size_t)N * H * dv * dk * 4;
+    if (overlaps(o, tv, q, tq) || overlaps(o, tv, k, tq) || overlaps(o, tv, v, tv) || overlaps(o, tv, g, tg) ||
+        overlaps(o, tv, beta, tg) || overlaps(o, tv, state, ts) || overlaps(state, ts, q, tq) ||
+        overlaps(state, ts, k, tq) || overlaps(state, ts, v, tv) || overlaps(state, ts, g, tg) ||
+        overlaps(state, ts, beta, tg))
+        return GDN_ERR_INVALID_ARG;
+    gdn::StepArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.o = o;
+    a.N = N;
+    a.H = H;
+    a.dk = dk;
+    a.dv = dv;
+    a.bf16 = dtype == GDN_BF16;
+    a.scale = scale;
+    a.l2norm = (flags & GDN_QK_L2NORM) ? 1 : 0;
+    a.stream = static_cast<hipStream_t>(hip_stream);
+    const hipError_t e = gdn::launch_step(a);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

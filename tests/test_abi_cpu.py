@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: the library loads, exports every function include/gdn.h declares, and
+rejects bad arguments on the host before any HIP call (so these run on a CPU-only machine)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_rule_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return gdn.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*|void)\s+(gdn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_recurrent_step",
+                                    "gdn_status_string"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert gdn.gdn_status_string(0) == "GDN_OK"
+    assert gdn.gdn_status_string(3) == "GDN_ERR_WORKSPACE"
+    assert gdn.gdn_status_string(99) == "GDN_ERR_UNKNOWN"
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every case below fails validation first
+
+
+def chunk(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, s0=None, cu=None, conv=None,
+             o=FAKE * 6, sf=None, ws=None, wsb=None, N=1, T=64, H=1, dk=32, dv=32, dtype=1, chunk=64,
+             scale=1.0, flags=1)
+    a.update(kw)
+    return lib.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["conv"], a["o"],
+                             a["sf"], a["ws"], a["wsb"], a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"],
+                             a["chunk"], a["scale"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=48), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dv=256), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(dtype=7), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(chunk=32), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(q=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(N=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(H=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(T=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(N=3, T=64), gdn.GDN_ERR_INVALID_ARG),          # T_tot not divisible without cu_seqlens
+    (dict(flags=8), gdn.GDN_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(q=FAKE + 4), gdn.GDN_ERR_INVALID_ARG),          # misaligned
+    (dict(o=FAKE), gdn.GDN_ERR_INVALID_ARG),              # o aliases q
+    (dict(sf=FAKE * 3), gdn.GDN_ERR_INVALID_ARG),         # final state overlaps v
+    (dict(s0=FAKE * 20, sf=FAKE * 20 + 16), gdn.GDN_ERR_INVALID_ARG),  # partial state overlap
+])
+def test_chunk_validation(lib, kw, status):
+    assert chunk(lib, **kw) == status
+
+
+def test_workspace_query(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_workspace_size(1, 262144, 16, 128, 128, gdn.GDN_BF16, 64, 0, ctypes.byref(n)) == 0
+    need = n.value
+    if need == 0:
+        pytest.skip("this configuration needs no workspace")
+    wsb = ctypes.c_size_t(0)
+    st = chunk(lib, N=1, T=262144, H=16, dk=128, dv=128, q=FAKE * 64, k=FAKE * 640000, v=FAKE * 1280000,
+               g=FAKE * 1920000, beta=FAKE * 2000000, o=FAKE * 2100000, ws=None, wsb=ctypes.byref(wsb))
+    assert st == gdn.GDN_ERR_WORKSPACE and wsb.value == need
+
+
+def test_workspace_size_validation(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_workspace_size(1, 64, 1, 33, 32, 1, 64, 0, ctypes.byref(n)) == gdn.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_workspace_size(3, 64, 1, 32, 32, 1, 64, 0, ctypes.byref(n)) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_chunk_workspace_size(1, 64, 1, 32, 32, 1, 64, 0, None) == gdn.GDN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=16), gdn.GDN_ERR_UNSUPPORTED),
+    (dict(state=None), gdn.GDN_ERR_INVALID_ARG),
+    (dict(N=-1), gdn.GDN_ERR_INVALID_ARG),
+    (dict(o=FAKE * 6 + 64), gdn.GDN_ERR_INVALID_ARG),   # o inside the state
+    (dict(flags=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(N=0), gdn.GDN_OK),                        # empty batch: no-op, no launch
+])
+def test_step_validation(lib, kw, status):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, state=FAKE * 6, o=FAKE * 100, N=2, H=1,
+             dk=32, dv=32, dtype=1, scale=1.0, flags=1)
+    a.update(kw)
+    assert lib.gdn_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["o"], a["N"], a["H"],
+                                  a["dk"], a["dv"], a["dtype"], a["scale"], a["flags"], None) == status
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(gdn, "_lib", None)
+    monkeypatch.setattr(gdn, "_LIB_PATH", "/nonexistent/libgdn.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        gdn.load_library()

@@ -1,0 +1,153 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle on identical seeded inputs.
+
+Sizes span several 64-token chunks and ragged tails; the named workloads run at full size where
+the oracle finishes in seconds, and on sampled (sequence, head) chains otherwise (chains are
+independent, so a sampled chain is checked exactly as in a full run).
+"""
+import numpy as np
+import pytest
+
+import gdn_testlib as TL
+import oracle
+from linear_attention_sequence_rule_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------------- prefill
+
+def test_tiny_f32_workload():
+    """B=1, T=256, H=2, d=32, fp32, zero initial state, seed 0: max relative error <= 1e-4."""
+    wl = W.tiny_f32()
+    o, s = TL.run_gpu(wl)
+    o_ref, s_ref = TL.run_oracle(wl)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("tiny_f32 %s" % e)
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 64), (128, 128)])
+def test_f32_ragged_varlen(dk, dv):
+    wl = W.make("f32_ragged", seed=100 + dk + dv, lengths=[130, 0, 64, 1, 77], H=3, dk=dk, dv=dv,
+                dtype="f32", s0_std=0.5, varlen=True)
+    o, s = TL.run_gpu(wl, scale=0.5)
+    o_ref, s_ref = TL.run_oracle(wl, scale=0.5)
+    TL.compare(wl, o, s, o_ref, s_ref)
+    # zero-length sequence: final state equals the initial one exactly
+    np.testing.assert_array_equal(s[1], wl.s0[1])
+
+
+def test_f32_equal_lengths_no_state():
+    wl = W.make("f32_eq", seed=7, N=3, T=190, H=2, dk=64, dv=64, dtype="f32")
+    o, s = TL.run_gpu(wl)
+    o_ref, s_ref = TL.run_oracle(wl)
+    TL.compare(wl, o, s, o_ref, s_ref)
+
+
+def test_f32_conv_prologue():
+    wl = W.make("f32_conv", seed=8, lengths=[70, 3, 129], H=2, dk=32, dv=64, dtype="f32", s0_std=0.1,
+                conv=True, varlen=True)
+    o, s = TL.run_gpu(wl)
+    o_ref, s_ref = TL.run_oracle(wl)
+    TL.compare(wl, o, s, o_ref, s_ref)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 32)])
+def test_bf16_ragged_varlen(dk, dv):
+    wl = W.make("bf16_ragged", seed=200 + dk + dv, lengths=[300, 0, 64, 1, 129], H=4, dk=dk, dv=dv,
+                dtype="bf16", s0_std=0.02, varlen=True)
+    o, s = TL.run_gpu(wl)
+    o_ref, s_ref = TL.run_oracle(wl)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("bf16_ragged %d %d %s" % (dk, dv, e))
+    np.testing.assert_array_equal(s[1], wl.s0[1])
+
+
+def test_bf16_conv_varlen_small():
+    wl = W.varlen(lengths=[520, 64, 7, 1000], H=4)
+    o, s = TL.run_gpu(wl)
+    o_ref, s_ref = TL.run_oracle(wl)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("bf16_conv %s" % e)
+
+
+def test_bf16_slow_decay():
+    """Slow decay (g ~ -1e-3) keeps the whole history alive: the hardest case for bf16 operands."""
+    wl = W.make("slow", seed=9, N=2, T=1024, H=4, dk=128, dv=128, dtype="bf16", s0_std=0.02)
+    wl.g = np.full_like(wl.g, -1e-3)
+    o, s = TL.run_gpu(wl)
+    o_ref, s_ref = TL.run_oracle(wl)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("slow_decay %s" % e)
+
+
+def test_prefill_workload_full():
+    """B=4, T=4096, H=16, d=128, bf16, initial state ~N(0, 0.02): every chain checked."""
+    wl = W.prefill()
+    o, s = TL.run_gpu(wl)
+    o_ref, s_ref = TL.run_oracle(wl)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("prefill full %s" % e)
+
+
+# ----------------------------------------------------------------------------------- decode
+
+def _decode_check(dw, scale=1.0):
+    from linear_attention_sequence_rule_amd import gdn_recurrent_step
+    import torch
+    st = TL.to_dev(dw.state)
+    o = gdn_recurrent_step(TL.to_dev(dw.q), TL.to_dev(dw.k), TL.to_dev(dw.v), TL.to_dev(dw.g), TL.to_dev(dw.beta), st,
+                           scale=scale)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.step(dw.as_float("q"), dw.as_float("k"), dw.as_float("v"), dw.g, dw.beta, dw.state,
+                               scale=scale)
+    og = TL.o_to_f64(o)
+    sg = st.cpu().numpy().astype(np.float64)
+    if dw.dtype == "f32":
+        assert np.abs(og - o_ref).max() / np.abs(o_ref).max() <= TL.F32_REL
+        assert np.abs(sg - s_ref).max() / np.abs(s_ref).max() <= TL.F32_REL
+    else:
+        assert np.abs(og - o_ref).max() <= TL.BF16_O_ABS
+        d = np.linalg.norm((sg - s_ref).reshape(dw.N * dw.H, -1), axis=1)
+        r = np.linalg.norm(s_ref.reshape(dw.N * dw.H, -1), axis=1)
+        assert (d / r).max() <= TL.BF16_S_RELF
+    return float(np.abs(og - o_ref).max())
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 32), (32, 128), (64, 64), (128, 32), (128, 128)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_dims(dk, dv, dtype):
+    dw = W.decode(N=5, H=3, dk=dk, dv=dv, dtype=dtype, seed=dk * 3 + dv, state_std=0.3)
+    _decode_check(dw, scale=0.75)
+
+
+def test_decode_workload_full():
+    """256 sequences x 32 heads, d=128, bf16 tokens, fp32 state ~N(0, 0.02) (512 MiB), in place."""
+    dw = W.decode()
+    err = _decode_check(dw)
+    _flush("decode full o_abs=%g" % err)
+
+
+def test_decode_then_prefill_consistency():
+    """prefill(T) followed by one decode step equals prefill(T+1) (within bf16 tolerance)."""
+    from linear_attention_sequence_rule_amd import gdn_recurrent_step
+    import torch
+    wl = W.make("pd", seed=31, N=2, T=129, H=2, dk=128, dv=128, dtype="bf16", s0_std=0.02)
+    q, k, v = TL.to_dev(wl.q), TL.to_dev(wl.k), TL.to_dev(wl.v)
+    g, b = TL.to_dev(wl.g), TL.to_dev(wl.beta)
+    from linear_attention_sequence_rule_amd import gdn_chunk_fwd
+    o_full, s_full = gdn_chunk_fwd(q, k, v, g, b, TL.to_dev(wl.s0), N=2)
+    # first 128 tokens of each sequence, then one step
+    idx = torch.cat([torch.arange(0, 128), torch.arange(129, 257)]).cuda()
+    last = torch.tensor([128, 257]).cuda()
+    o_a, s_a = gdn_chunk_fwd(q[idx].contiguous(), k[idx].contiguous(), v[idx].contiguous(), g[idx].contiguous(),
+                             b[idx].contiguous(), TL.to_dev(wl.s0), N=2)
+    o_step = gdn_recurrent_step(q[last].contiguous(), k[last].contiguous(), v[last].contiguous(),
+                                g[last].contiguous(), b[last].contiguous(), s_a)
+    torch.cuda.synchronize()
+    assert (o_step.float() - o_full[last].float()).abs().max().item() <= TL.BF16_O_ABS
+    rel = ((s_a - s_full).norm() / s_full.norm()).item()
+    assert rel <= TL.BF16_S_RELF
