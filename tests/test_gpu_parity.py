@@ -55,7 +55,7 @@ def test_f32_conv_prologue():
     TL.compare(wl, o, s, o_ref, s_ref)
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 32)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 32), (32, 64), (128, 32), (64, 128)])
 def test_bf16_ragged_varlen(dk, dv):
     wl = W.make("bf16_ragged", seed=200 + dk + dv, lengths=[300, 0, 64, 1, 129], H=4, dk=dk, dv=dv,
                 dtype="bf16", s0_std=0.02, varlen=True)
