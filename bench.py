@@ -1,0 +1,204 @@
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+A step is one gdn_chunk_fwd call over the prefill workload (B=4 sequences x T=4096 tokens, H=16
+heads, d_k=d_v=128, bf16 q/k/v, fp32 gates, fp32 initial state ~N(0, 0.02), chunk 64): every
+prefill row of the path runs inside it.  Inputs are resident in HBM before the timed region.
+To keep the 256 MB Infinity Cache from serving the inputs, the timed loop rotates over several
+independent copies of the inputs (more than twice the cache in total).
+
+The JSON line reports prefill tokens/s as `value`, the HBM roofline of the prefill kernel
+(algorithmic bytes per launch / mean launch time from HIP events on the launch stream), the bf16
+MFMA fraction under algorithmic flop accounting, the decode step (256 sequences x 32 heads, state
+updated in place) as GB/s against HBM, and the fp64 CPU oracle's throughput on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA, TFLOP/s
+C_ACCOUNT = 64               # chunk length used for the algorithmic flop count
+
+
+def prefill_alg_flops_per_token_head(dk, dv, C=C_ACCOUNT):
+    """Triangles only: K K^T strict lower, Q K^T and Pm U lower incl. diagonal, forward
+    substitution on [beta Gamma K | beta V], plus the three state products."""
+    return 2 * (C * dk + (C - 1) * (dk + dv) / 2 + (C + 1) * dv / 2 + 3 * dk * dv)
+
+
+def prefill_alg_bytes(tokens, N, H, dk, dv, with_states=True):
+    per_th = (2 * dk + dv) * 2 + dv * 2 + 8   # q, k, v, o (bf16) + g, beta (fp32)
+    b = tokens * H * per_th
+    if with_states:
+        b += 2 * N * H * dv * dk * 4
+    return b
+
+
+def decode_alg_bytes(N, H, dk, dv):
+    return N * H * (2 * dv * dk * 4 + (2 * dk + dv) * 2 + dv * 2 + 8)
+
+
+def load_traffic(kernel_tag):
+    """HBM traffic per launch measured with rocprofv3 counters (profiles/traffic.json), valid
+    only while the kernel source hash matches the one recorded with the counters."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_tag)
+    except Exception:
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "linear_attention_sequence_rule_amd", "csrc", rec["source"])
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return rec["bytes_per_launch"] if h == rec["source_sha"] else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=4, help="input copies rotated through the timed loop")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs the gated delta rule on a single device "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import linear_attention_sequence_rule_amd as gdn
+    from linear_attention_sequence_rule_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        # 1 GiB read + 1 GiB written per copy: the scale for FETCH_SIZE / WRITE_SIZE counters
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": src.numel() * 4, "launches": 3}))
+        return
+
+    def to_dev(x):
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    # ---------------------------------------------------------------- prefill (the step)
+    wl = W.prefill()
+    N, H, dk, dv, T = wl.N, wl.H, wl.dk, wl.dv, wl.T_tot // wl.N
+    tokens = wl.T_tot
+    base = [to_dev(x) for x in (wl.q, wl.k, wl.v, wl.g, wl.beta, wl.s0)]
+    copies = [base] + [[t.clone() for t in base] for _ in range(args.copies - 1)]
+    outs = [(torch.empty((tokens, H, dv), dtype=torch.bfloat16, device=dev),
+             torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)) for _ in copies]
+
+    def step(i):
+        q, k, v, g, b, s0 = copies[i % len(copies)]
+        o, sf = outs[i % len(outs)]
+        gdn.gdn_chunk_fwd(q, k, v, g, b, s0, N=N, o=o, final_state=sf, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    mean_launch_s = sum(launch_ms) / len(launch_ms) * 1e-3
+
+    alg_bytes = prefill_alg_bytes(tokens, N, H, dk, dv)
+    alg_flops = tokens * H * prefill_alg_flops_per_token_head(dk, dv)
+    gbs = alg_bytes / mean_launch_s / 1e9
+    tflops = alg_flops / mean_launch_s / 1e12
+    value = tokens / (ms_per_step * 1e-3)
+
+    # ---------------------------------------------------------------- decode
+    dw = W.decode()
+    dq, dk_, dv_, dg, db, st = (to_dev(x) for x in (dw.q, dw.k, dw.v, dw.g, dw.beta, dw.state))
+    od = torch.empty_like(dv_)
+    for _ in range(3):
+        gdn.gdn_recurrent_step(dq, dk_, dv_, dg, db, st, o=od, stream=stream)
+    torch.cuda.synchronize()
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in dev_ev:
+        a.record(stream)
+        gdn.gdn_recurrent_step(dq, dk_, dv_, dg, db, st, o=od, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    dec_s = sum(a.elapsed_time(b) for a, b in dev_ev) / len(dev_ev) * 1e-3
+    dec_bytes = decode_alg_bytes(dw.N, dw.H, dw.dk, dw.dv)
+    dec_gbs = dec_bytes / dec_s / 1e9
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cu = np.concatenate([[0], np.cumsum(wl.lengths)])
+        qf, kf, vf = wl.as_float("q"), wl.as_float("k"), wl.as_float("v")
+        t1 = time.perf_counter()
+        _, _, used = oracle.forward(qf, kf, vf, wl.g, wl.beta, wl.s0, cu, None)
+        cpu_s = time.perf_counter() - t1
+        cpu = {"value": tokens / cpu_s, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+               "sample": "the whole prefill workload (4 x 4096 tokens, 16 heads), fp64 token-by-token "
+                         "recurrence, threads over (sequence, head) chains; %.2f s" % cpu_s}
+
+    out = {
+        "metric": "GDN chunked-prefill tokens/s (+% bf16 MFMA peak); decode-step GB/s (+% HBM)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill B=4 T=4096 H=16 dk=dv=128 bf16 q/k/v, fp32 gates and state, chunk 64",
+                   "global_batch": N, "seq_len": T, "heads": H, "dk": dk, "dv": dv},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic("chunk_bf16_kernel")},
+        "mfma": {"achieved_tflops_alg": tflops, "peak": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS,
+                 "flops_per_token_head": prefill_alg_flops_per_token_head(dk, dv)},
+        "prefill_kernel_us": mean_launch_s * 1e6,
+        "decode": {"workload": "decode 256 sequences x 32 heads, dk=dv=128, bf16 tokens, fp32 state in place",
+                   "value": dec_gbs, "unit": "GB/s", "us_per_step": dec_s * 1e6,
+                   "tokens_per_s": dw.N / dec_s,
+                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dec_gbs / HBM_PEAK_GBS, "traffic": load_traffic("step_kernel")}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -97,8 +97,10 @@ struct Smem {
     static constexpr int oG = oTt + C * LSTR * 4;                  // fp32 gate arrays [12][C]
     static constexpr int bytes = oG + 12 * C * 4;
 };
-// gate array slots (fp32 [C] each)
-enum { G_RAW = 0, G_BETA, G_RK, G_RQ, G_KK, G_ORQ, G_DRK, G_GAM0, G_GAM1, G_GC, G_NSLOT };
+// gate array slots (fp32 [C] each).  Each state wave w keeps its own decay factors in slots
+// G_SKK + 3w (beta Gamma rk), G_SORQ + 3w (Gamma rq) and G_SDRK + 3w (exp(gamma_C - gamma) rk).
+enum { G_RAW = 0, G_BETA, G_RK, G_RQ, G_GAM0, G_GAM1, G_SKK, G_SORQ, G_SDRK, G_NSLOT = G_SKK + 6 };
+static_assert(G_NSLOT <= 12, "gate slots");
 
 template <int DK>
 struct Params {
@@ -128,32 +130,25 @@ struct ChunkRegs {
 template <int DK>
 __device__ __forceinline__ void fetch_chunk(const Params<DK>& p, ChunkRegs<DK>& R, long t0, int len, int h, int vb,
                                             int tid) {
+    // Rows past the tail re-read the last valid row (len >= 1) and are zeroed when stored: the
+    // loads stay unconditional, so no wait is forced between them.
     using CR = ChunkRegs<DK>;
     const int part = tid % CR::PPR;
 #pragma unroll
     for (int j = 0; j < CR::NP; ++j) {
-        const int r = tid / CR::PPR + j * CR::RPP;
-        if (r < len) {
-            const size_t off = ((size_t)(t0 + r) * p.H + h) * DK + 8 * part;
-            R.kr[j] = *reinterpret_cast<const uint4*>(p.k + off);
-            R.qr[j] = *reinterpret_cast<const uint4*>(p.q + off);
-        } else {
-            R.kr[j] = make_uint4(0, 0, 0, 0);
-            R.qr[j] = make_uint4(0, 0, 0, 0);
-        }
+        const int r = min(tid / CR::PPR + j * CR::RPP, len - 1);
+        const size_t off = ((size_t)(t0 + r) * p.H + h) * DK + 8 * part;
+        R.kr[j] = *reinterpret_cast<const uint4*>(p.k + off);
+        R.qr[j] = *reinterpret_cast<const uint4*>(p.q + off);
     }
     {
-        const int r = tid / 4, pv = tid % 4;
-        if (r < len)
-            R.vr = *reinterpret_cast<const uint4*>(p.v + ((size_t)(t0 + r) * p.H + h) * p.dv + vb * BV + 8 * pv);
-        else
-            R.vr = make_uint4(0, 0, 0, 0);
+        // V: one token per lane (part = wave) so the transposed LDS writes are contiguous
+        const int r = min(tid % C, len - 1), pv = tid / C;
+        R.vr = *reinterpret_cast<const uint4*>(p.v + ((size_t)(t0 + r) * p.H + h) * p.dv + vb * BV + 8 * pv);
     }
-    if (tid < C) {
-        const bool in = tid < len;
-        R.gr = in ? p.g[(size_t)(t0 + tid) * p.H + h] : 0.f;
-        R.br = in ? p.beta[(size_t)(t0 + tid) * p.H + h] : 0.f;
-    }
+    const int r = min(tid % C, len - 1);
+    R.gr = p.g[(size_t)(t0 + r) * p.H + h];
+    R.br = p.beta[(size_t)(t0 + r) * p.H + h];
 }
 
 __device__ __forceinline__ float sumsq8(uint4 u) {
@@ -173,37 +168,36 @@ __device__ __forceinline__ void store_chunk(const ChunkRegs<DK>& R, unsigned cha
     using CR = ChunkRegs<DK>;
     __bf16* sK = reinterpret_cast<__bf16*>(sm + S::oK);
     __bf16* sQ = reinterpret_cast<__bf16*>(sm + S::oQ);
-    __bf16* sKt = reinterpret_cast<__bf16*>(sm + S::oKt);
     __bf16* sVt = reinterpret_cast<__bf16*>(sm + S::oVt);
     float* sG = reinterpret_cast<float*>(sm + S::oG);
     const int part = tid % CR::PPR;
+    const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int j = 0; j < CR::NP; ++j) {
         const int r = tid / CR::PPR + j * CR::RPP;
-        *reinterpret_cast<uint4*>(sK + r * S::KSTR + 8 * part) = R.kr[j];
-        *reinterpret_cast<uint4*>(sQ + r * S::KSTR + 8 * part) = R.qr[j];
-        const uint16_t* kh = reinterpret_cast<const uint16_t*>(&R.kr[j]);
-        uint16_t* kt = reinterpret_cast<uint16_t*>(sKt);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kt[(8 * part + e) * TSTR + r] = kh[e];
-        float sk = group_sum<CR::PPR>(sumsq8(R.kr[j]));
-        float sq = group_sum<CR::PPR>(sumsq8(R.qr[j]));
+        const bool in = r < len;
+        const uint4 kv = in ? R.kr[j] : z, qv = in ? R.qr[j] : z;
+        *reinterpret_cast<uint4*>(sK + r * S::KSTR + 8 * part) = kv;
+        *reinterpret_cast<uint4*>(sQ + r * S::KSTR + 8 * part) = qv;
+        float sk = group_sum<CR::PPR>(sumsq8(kv));
+        float sq = group_sum<CR::PPR>(sumsq8(qv));
         if (part == 0) {
-            const bool in = r < len;
             sG[G_RK * C + r] = in ? (l2norm ? rsqrtf(sk + kL2Eps) : 1.f) : 0.f;
             sG[G_RQ * C + r] = in ? (l2norm ? rsqrtf(sq + kL2Eps) : 1.f) : 0.f;
         }
     }
     {
-        const int r = tid / 4, pv = tid % 4;
-        const uint16_t* vh = reinterpret_cast<const uint16_t*>(&R.vr);
+        const int r = tid % C, pv = tid / C;
+        const uint4 vv = r < len ? R.vr : z;
+        const uint16_t* vh = reinterpret_cast<const uint16_t*>(&vv);
         uint16_t* vt = reinterpret_cast<uint16_t*>(sVt);
 #pragma unroll
         for (int e = 0; e < 8; ++e) vt[(8 * pv + e) * TSTR + r] = vh[e];
     }
     if (tid < C) {
-        sG[G_RAW * C + tid] = R.gr;
-        sG[G_BETA * C + tid] = R.br;
+        const bool in = tid < len;
+        sG[G_RAW * C + tid] = in ? R.gr : 0.f;
+        sG[G_BETA * C + tid] = in ? R.br : 0.f;
     }
 }
 
@@ -220,7 +214,8 @@ __device__ __forceinline__ float wave_scan(float x, int lane) {
     return x;
 }
 
-// Wave p0: gate arrays for the state waves and the strict-lower masked Gram L (fp32, row-major).
+// Wave p0: the strict-lower masked Gram L = strict_lower(diag(beta) (M o Khat Khat^T)), fp32,
+// row-major.  K fragments stay in registers: A and B operands of K K^T are the same data.
 template <int DK>
 __device__ void prep_gram_L(unsigned char* sm, int lane) {
     using S = Smem<DK>;
@@ -230,41 +225,34 @@ __device__ void prep_gram_L(unsigned char* sm, int lane) {
     float* sL = reinterpret_cast<float*>(sm + S::oL);
     const int g = lane / 16, l16 = lane % 16;
 
-    // gates
-    const float gam = wave_scan(sG[G_RAW * C + lane], lane);
-    const float gl = __shfl(gam, C - 1);
-    const float Gi = __expf(gam);
-    const float b = sG[G_BETA * C + lane], rk = sG[G_RK * C + lane], rq = sG[G_RQ * C + lane];
-    sG[G_GAM0 * C + lane] = gam;
-    sG[G_KK * C + lane] = b * Gi * rk;
-    sG[G_ORQ * C + lane] = Gi * rq;
-    sG[G_DRK * C + lane] = __expf(gl - gam) * rk;
-    sG[G_GC * C + lane] = __expf(gl);
-
     bf16x8 kf[4][KS];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kf[rb][ks] = frag_nat(sK + (16 * rb + l16) * S::KSTR, 32 * ks, g);
+    sG[G_GAM0 * C + lane] = wave_scan(sG[G_RAW * C + lane], lane);
 
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
+        fx4 acc[4];
+#pragma unroll
+        for (int jt = 0; jt <= it; ++jt) acc[jt] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int jt = 0; jt <= it; ++jt) acc[jt] = mfma(kf[it][ks], kf[jt][ks], acc[jt]);
         const int i0 = 16 * it + 4 * g;
         const fx4 gi = *reinterpret_cast<const fx4*>(sG + G_GAM0 * C + i0);
         const fx4 bi = *reinterpret_cast<const fx4*>(sG + G_BETA * C + i0);
         const fx4 ri = *reinterpret_cast<const fx4*>(sG + G_RK * C + i0);
 #pragma unroll
         for (int jt = 0; jt <= it; ++jt) {
-            fx4 acc = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mfma(kf[it][ks], kf[jt][ks], acc);
             const int j = 16 * jt + l16;
             const float gj = sG[G_GAM0 * C + j], rj = sG[G_RK * C + j];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = i0 + e;
-                const float val = j < i ? bi[e] * ri[e] * rj * __expf(gi[e] - gj) * acc[e] : 0.f;
-                sL[i * LSTR + j] = val;
+                sL[i * LSTR + j] = j < i ? bi[e] * ri[e] * rj * __expf(gi[e] - gj) * acc[jt][e] : 0.f;
             }
         }
     }
@@ -282,9 +270,6 @@ __device__ void prep_gram_P(unsigned char* sm, int lane) {
     __bf16* sPm = reinterpret_cast<__bf16*>(sm + S::oPm);
     const int g = lane / 16, l16 = lane % 16;
 
-    const float gam = wave_scan(sG[G_RAW * C + lane], lane);
-    sG[G_GAM1 * C + lane] = gam;
-
     bf16x8 kf[4][KS], qf[4][KS];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
@@ -293,37 +278,49 @@ __device__ void prep_gram_P(unsigned char* sm, int lane) {
             kf[rb][ks] = frag_nat(sK + (16 * rb + l16) * S::KSTR, 32 * ks, g);
             qf[rb][ks] = frag_nat(sQ + (16 * rb + l16) * S::KSTR, 32 * ks, g);
         }
+    sG[G_GAM1 * C + lane] = wave_scan(sG[G_RAW * C + lane], lane);
+
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
+        fx4 acc[4];
+#pragma unroll
+        for (int mt = 0; mt <= it; ++mt) acc[mt] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt <= it; ++mt) acc[mt] = mfma(kf[mt][ks], qf[it][ks], acc[mt]);
         const int i = 16 * it + l16;
         const float gi = sG[G_GAM1 * C + i], rqi = sG[G_RQ * C + i];
 #pragma unroll
         for (int mt = 0; mt <= it; ++mt) {
-            fx4 acc = zero4();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mfma(kf[mt][ks], qf[it][ks], acc);
             const int m0 = 16 * mt + 4 * g;
             const fx4 gm = *reinterpret_cast<const fx4*>(sG + G_GAM1 * C + m0);
             const fx4 rkm = *reinterpret_cast<const fx4*>(sG + G_RK * C + m0);
             bf16x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                out[e] = (__bf16)(m0 + e <= i ? rqi * rkm[e] * __expf(gi - gm[e]) * acc[e] : 0.f);
+                out[e] = (__bf16)(m0 + e <= i ? rqi * rkm[e] * __expf(gi - gm[e]) * acc[mt][e] : 0.f);
             *reinterpret_cast<bf16x4*>(sPm + i * TSTR + m0) = out;
         }
     }
 }
 
 // Solve level 0: invert the 16x16 unit-lower diagonal blocks b0, b0+1 of (I + L) by forward
-// substitution, one column per lane (lanes 0..31).  Writes T (fp32 row- and column-major and
-// bf16 row-major).
+// substitution, one column per lane (lanes 0..31).  The block's rows of L are read once with
+// 16-byte loads; the right-looking update keeps one FMA on the critical path per step.  Writes
+// T (fp32 row- and column-major and bf16 row-major).
 __device__ void solve_diag(unsigned char* sm, int b0, int lane, int oL, int oTf, int oTt, int oT) {
     const float* sL = reinterpret_cast<const float*>(sm + oL);
     float* sTf = reinterpret_cast<float*>(sm + oTf);
     float* sTt = reinterpret_cast<float*>(sm + oTt);
     __bf16* sT = reinterpret_cast<__bf16*>(sm + oT);
-    if (lane >= 32) return;
-    const int b = b0 + lane / 16, j = lane % 16, base = 16 * b;
+    const int b = b0 + (lane / 16) % 2, j = lane % 16, base = 16 * b;
+    fx4 Lr[16][4];
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (4 * q < i) Lr[i][q] = *reinterpret_cast<const fx4*>(sL + (base + i) * LSTR + base + 4 * q);
     float acc[16], t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
@@ -332,8 +329,9 @@ __device__ void solve_diag(unsigned char* sm, int b0, int lane, int oL, int oTf,
         const float tm = m == j ? 1.f : (m > j ? -acc[m] : 0.f);
         t[m] = tm;
 #pragma unroll
-        for (int i = m + 1; i < 16; ++i) acc[i] += sL[(base + i) * LSTR + base + m] * tm;
+        for (int i = m + 1; i < 16; ++i) acc[i] += Lr[i][m / 4][m % 4] * tm;
     }
+    if (lane >= 32) return;
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
         sTf[(base + m) * LSTR + base + j] = t[m];
@@ -354,11 +352,20 @@ __device__ void solve_level1(unsigned char* sm, int b, int lane, int oL, int oTf
     const int r0 = 16 * (b + 1), c0 = 16 * b;
     // Y = L_{b+1,b} T_bb : A = L rows r0+l16, k = m (natural order, k >= 16 zero)
     float a[8], bb[8];
+    {
+        const int gg = g & 1;  // lanes with g >= 2 read valid memory and zero it (k >= 16 is padding)
+        const fx4 a0 = *reinterpret_cast<const fx4*>(sL + (r0 + l16) * LSTR + c0 + 8 * gg);
+        const fx4 a1 = *reinterpret_cast<const fx4*>(sL + (r0 + l16) * LSTR + c0 + 8 * gg + 4);
+        const fx4 b0v = *reinterpret_cast<const fx4*>(sTt + (c0 + l16) * LSTR + c0 + 8 * gg);  // T_bb column l16
+        const fx4 b1v = *reinterpret_cast<const fx4*>(sTt + (c0 + l16) * LSTR + c0 + 8 * gg + 4);
+        const float keep = g < 2 ? 1.f : 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int m = 8 * g + e;
-        a[e] = m < 16 ? sL[(r0 + l16) * LSTR + c0 + m] : 0.f;
-        bb[e] = m < 16 ? sTt[(c0 + l16) * LSTR + c0 + m] : 0.f;  // T_bb[m][j], column-major
+        for (int e = 0; e < 4; ++e) {
+            a[e] = keep * a0[e];
+            a[4 + e] = keep * a1[e];
+            bb[e] = keep * b0v[e];
+            bb[4 + e] = keep * b1v[e];
+        }
     }
     bf16x8 ah, al, bh, bl;
     split8(a, ah, al);
@@ -366,10 +373,15 @@ __device__ void solve_level1(unsigned char* sm, int b, int lane, int oL, int oTf
     fx4 y = mfma3(ah, al, bh, bl, zero4());
     // T_{b+1,b} = -T_{b+1,b+1} Y : B = Y from registers (k = 4g+e), A = T rows in the same order
     float a2[8], y2[8];
+    {
+        const fx4 tv = *reinterpret_cast<const fx4*>(sTf + (r0 + l16) * LSTR + r0 + 4 * g);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        a2[e] = e < 4 ? sTf[(r0 + l16) * LSTR + r0 + 4 * g + e] : 0.f;
-        y2[e] = e < 4 ? y[e] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+            a2[e] = tv[e];
+            y2[e] = y[e];
+            a2[4 + e] = 0.f;
+            y2[4 + e] = 0.f;
+        }
     }
     split8(a2, ah, al);
     split8(y2, bh, bl);
@@ -395,16 +407,28 @@ __device__ void solve_level2(unsigned char* sm, int half, int lane, int oL, int 
     const int jc = 16 * half + l16;  // column of T_AA / T_BA handled by this lane (as N index)
     // B operand: T_AA[m][jc], m = 8g+e (natural order over K = 32), column-major source
     float bb[8];
+    {
+        const fx4 b0v = *reinterpret_cast<const fx4*>(sTt + jc * LSTR + 8 * g);
+        const fx4 b1v = *reinterpret_cast<const fx4*>(sTt + jc * LSTR + 8 * g + 4);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bb[e] = sTt[jc * LSTR + 8 * g + e];
+        for (int e = 0; e < 4; ++e) {
+            bb[e] = b0v[e];
+            bb[4 + e] = b1v[e];
+        }
+    }
     bf16x8 bh, bl;
     split8(bb, bh, bl);
     fx4 y[2];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         float a[8];
+        const fx4 a0 = *reinterpret_cast<const fx4*>(sL + (32 + 16 * it + l16) * LSTR + 8 * g);
+        const fx4 a1 = *reinterpret_cast<const fx4*>(sL + (32 + 16 * it + l16) * LSTR + 8 * g + 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = sL[(32 + 16 * it + l16) * LSTR + 8 * g + e];
+        for (int e = 0; e < 4; ++e) {
+            a[e] = a0[e];
+            a[4 + e] = a1[e];
+        }
         bf16x8 ah, al;
         split8(a, ah, al);
         y[it] = mfma3(ah, al, bh, bl, zero4());
@@ -422,10 +446,12 @@ __device__ void solve_level2(unsigned char* sm, int half, int lane, int oL, int 
     for (int it = 0; it < 2; ++it) {
         float a[8];
         const float* row = sTf + (32 + 16 * it + l16) * LSTR + 32;
+        const fx4 a0 = *reinterpret_cast<const fx4*>(row + 4 * g);
+        const fx4 a1 = *reinterpret_cast<const fx4*>(row + 16 + 4 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            a[e] = row[4 * g + e];
-            a[4 + e] = row[16 + 4 * g + e];
+            a[e] = a0[e];
+            a[4 + e] = a1[e];
         }
         bf16x8 ah, al;
         split8(a, ah, al);
@@ -440,113 +466,172 @@ __device__ void solve_level2(unsigned char* sm, int half, int lane, int oL, int 
 template <int DK>
 struct StateRegs {
     static constexpr int DT = DK / 16;
-    fx4 S[DT];  // S^T tiles: lane (c = l%16, g) holds S[c][16 dt + 4g + e]
+    fx4 S[DT];     // S^T tiles: lane (c = l%16, g) holds S[c][16 dt + 4g + e]
+    bf16x8 xb[2];  // X (chain order over tokens), carried from phase 1 to phase 4
+    fx4 ot[4];     // O^T accumulators (S Q^T part, already scaled by Gamma rq)
+    float gc;      // Gamma_C = exp(gamma of the last token)
 };
 
+// K^T (token-contiguous copy of K for the state update), written by the two state waves: each
+// lane owns one token, so consecutive lanes write consecutive 2-byte slots of a K^T row.
 template <int DK>
-__device__ void state_chunk(const Params<DK>& p, StateRegs<DK>& st, unsigned char* sm, int lane, int cbase, long t0,
-                            int len, int h, int vb) {
+__device__ void transpose_k(unsigned char* sm, int lane, int sw) {
+    using S = Smem<DK>;
+    constexpr int PPR = DK / 8;
+    const __bf16* sK = reinterpret_cast<const __bf16*>(sm + S::oK);
+    uint16_t* kt = reinterpret_cast<uint16_t*>(sm + S::oKt);
+#pragma unroll
+    for (int q = 0; q < PPR / 2; ++q) {
+        const int part = sw * (PPR / 2) + q;
+        const uint4 v = *reinterpret_cast<const uint4*>(sK + lane * S::KSTR + 8 * part);
+        const uint16_t* vh = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kt[(8 * part + e) * TSTR + lane] = vh[e];
+    }
+}
+
+// Phase 1 (needs only the chunk inputs and S): own decay factors, K S^T, S Q^T and X.
+template <int DK>
+__device__ void state_phase1(StateRegs<DK>& st, unsigned char* sm, int lane, int sw, int cbase) {
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
-    constexpr int DT = DK / 16;
     const __bf16* sK = reinterpret_cast<const __bf16*>(sm + S::oK);
     const __bf16* sQ = reinterpret_cast<const __bf16*>(sm + S::oQ);
-    const __bf16* sKt = reinterpret_cast<const __bf16*>(sm + S::oKt);
     const __bf16* sVt = reinterpret_cast<const __bf16*>(sm + S::oVt);
-    const __bf16* sT = reinterpret_cast<const __bf16*>(sm + S::oT);
-    const __bf16* sPm = reinterpret_cast<const __bf16*>(sm + S::oPm);
-    const float* sG = reinterpret_cast<const float*>(sm + S::oG);
+    float* sG = reinterpret_cast<float*>(sm + S::oG);
     const int g = lane / 16, l16 = lane % 16;
+    const int oKK = (G_SKK + 3 * sw) * C, oORQ = (G_SORQ + 3 * sw) * C, oDRK = (G_SDRK + 3 * sw) * C;
 
-    // S as bf16 operand (chain order over d): usable as B (K S^T) and as A (S Q^T)
+    // operand fragments first (chain order: B/A partner is S from registers)
+    bf16x8 kfr[4][KS], qfr[4][KS];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            kfr[t][ks] = frag_chain(sK + (16 * t + l16) * S::KSTR, 32 * ks, g);
+            qfr[t][ks] = frag_chain(sQ + (16 * t + l16) * S::KSTR, 32 * ks, g);
+        }
+
+    // decay factors of this chunk (lane = token)
+    {
+        const float gam = wave_scan(sG[G_RAW * C + lane], lane);
+        const float gl = __shfl(gam, C - 1);
+        const float Gi = __expf(gam);
+        sG[oKK + lane] = sG[G_BETA * C + lane] * Gi * sG[G_RK * C + lane];
+        sG[oORQ + lane] = Gi * sG[G_RQ * C + lane];
+        sG[oDRK + lane] = __expf(gl - gam) * sG[G_RK * C + lane];
+        st.gc = __expf(gl);
+    }
+
     bf16x8 sb[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) sb[ks] = pack_chain(st.S[2 * ks], st.S[2 * ks + 1]);
 
-    // X = diag(beta) V - diag(beta Gamma rk) K S^T   (tiles over tokens m)
+    fx4 ks_acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        ks_acc[t] = zero4();
+        st.ot[t] = zero4();
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            ks_acc[t] = mfma(kfr[t][ks], sb[ks], ks_acc[t]);   // K S^T  (M = token, N = c)
+            st.ot[t] = mfma(sb[ks], qfr[t][ks], st.ot[t]);     // S Q^T  (M = c, N = token)
+        }
+
     fx4 x[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        fx4 acc = zero4();
-        const __bf16* row = sK + (16 * mt + l16) * S::KSTR;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma(frag_chain(row, 32 * ks, g), sb[ks], acc);
         const int m0 = 16 * mt + 4 * g;
         const fx4 bm = *reinterpret_cast<const fx4*>(sG + G_BETA * C + m0);
-        const fx4 kk = *reinterpret_cast<const fx4*>(sG + G_KK * C + m0);
+        const fx4 kk = *reinterpret_cast<const fx4*>(sG + oKK + m0);
         const bf16x4 vv = *reinterpret_cast<const bf16x4*>(sVt + (cbase + l16) * TSTR + m0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[mt][e] = bm[e] * (float)vv[e] - kk[e] * acc[e];
+        for (int e = 0; e < 4; ++e) x[mt][e] = bm[e] * (float)vv[e] - kk[e] * ks_acc[mt][e];
+        const float orq = sG[oORQ + 16 * mt + l16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.ot[mt][e] *= orq;
     }
-    bf16x8 xb[2];
-    xb[0] = pack_chain(x[0], x[1]);
-    xb[1] = pack_chain(x[2], x[3]);
+    st.xb[0] = pack_chain(x[0], x[1]);
+    st.xb[1] = pack_chain(x[2], x[3]);
+}
 
-    // O^T = diag(Gamma rq) (S Q^T) ... (tiles over query tokens i)
-    fx4 ot[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        fx4 acc = zero4();
-        const __bf16* row = sQ + (16 * it + l16) * S::KSTR;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma(sb[ks], frag_chain(row, 32 * ks, g), acc);
-        const float orq = sG[G_ORQ * C + 16 * it + l16];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] *= orq;
-        ot[it] = acc;
-    }
+// Phase 4 (after T is ready): U = T X, O += Pm U (stored), S <- Gamma_C S + U^T D K.
+template <int DK>
+__device__ void state_phase4(const Params<DK>& p, StateRegs<DK>& st, unsigned char* sm, int lane, int sw, int cbase,
+                             long t0, int len, int h, int vb) {
+    using S = Smem<DK>;
+    constexpr int DT = DK / 16;
+    const __bf16* sKt = reinterpret_cast<const __bf16*>(sm + S::oKt);
+    const __bf16* sT = reinterpret_cast<const __bf16*>(sm + S::oT);
+    const __bf16* sPm = reinterpret_cast<const __bf16*>(sm + S::oPm);
+    const float* sG = reinterpret_cast<const float*>(sm + S::oG);
+    const int g = lane / 16, l16 = lane % 16;
+    const int oDRK = (G_SDRK + 3 * sw) * C;
 
-    // U = T X (T lower triangular: i-tiles 0,1 need only m < 32)
+    // T and Pm fragments (k-step 1 only for row tiles 2, 3: both are lower triangular)
+    bf16x8 tf[4][2], pf[4][2];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+            if (s2 == 0 || it >= 2) {
+                tf[it][s2] = frag_chain(sT + (16 * it + l16) * TSTR, 32 * s2, g);
+                pf[it][s2] = frag_chain(sPm + (16 * it + l16) * TSTR, 32 * s2, g);
+            }
+    bf16x8 kt[DT][2];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) kt[dt][s2] = frag_chain(sKt + (16 * dt + l16) * TSTR, 32 * s2, g);
+
     fx4 u[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        fx4 acc = zero4();
-        const __bf16* row = sT + (16 * it + l16) * TSTR;
-        acc = mfma(frag_chain(row, 0, g), xb[0], acc);
-        if (it >= 2) acc = mfma(frag_chain(row, 32, g), xb[1], acc);
-        u[it] = acc;
-    }
+    for (int it = 0; it < 4; ++it) u[it] = mfma(tf[it][0], st.xb[0], zero4());
+#pragma unroll
+    for (int it = 2; it < 4; ++it) u[it] = mfma(tf[it][1], st.xb[1], u[it]);
     bf16x8 ub[2];
     ub[0] = pack_chain(u[0], u[1]);
     ub[1] = pack_chain(u[2], u[3]);
 
-    // O^T += U^T Pm^T, then store O (lane: token i = 16 it + l16, rows c = cbase + 4g .. +3)
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const __bf16* row = sPm + (16 * it + l16) * TSTR;
-        fx4 acc = ot[it];
-        acc = mfma(ub[0], frag_chain(row, 0, g), acc);
-        if (it >= 2) acc = mfma(ub[1], frag_chain(row, 32, g), acc);
-        const int i = 16 * it + l16;
-        if (i < len) {
-            bf16x4 out;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * acc[e]);
-            *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
-        }
-    }
-
-    // S <- Gamma_C S + U^T diag(exp(gamma_C - gamma) rk) K    (S^T tiles over d)
+    // U^T scaled by exp(gamma_C - gamma) rk for the state update
     fx4 ut[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        const fx4 d = *reinterpret_cast<const fx4*>(sG + G_DRK * C + 16 * it + 4 * g);
+        const fx4 d = *reinterpret_cast<const fx4*>(sG + oDRK + 16 * it + 4 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) ut[it][e] = u[it][e] * d[e];
     }
     bf16x8 utb[2];
     utb[0] = pack_chain(ut[0], ut[1]);
     utb[1] = pack_chain(ut[2], ut[3]);
-    const float gc = sG[G_GC * C];
+
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        fx4 acc = st.S[dt];
+    for (int it = 0; it < 4; ++it) st.ot[it] = mfma(ub[0], pf[it][0], st.ot[it]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] *= gc;
-        const __bf16* row = sKt + (16 * dt + l16) * TSTR;
-        acc = mfma(frag_chain(row, 0, g), utb[0], acc);
-        acc = mfma(frag_chain(row, 32, g), utb[1], acc);
-        st.S[dt] = acc;
+    for (int it = 2; it < 4; ++it) st.ot[it] = mfma(ub[1], pf[it][1], st.ot[it]);
+
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.S[dt][e] *= st.gc;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][s2], utb[s2], st.S[dt]);
+
+    // store O (lane: token i = 16 it + l16, state rows cbase + 4g .. +3)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int i = 16 * it + l16;
+        if (i < len) {
+            bf16x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e]);
+            *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
+        }
     }
 }
 
@@ -631,6 +716,10 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
         __syncthreads();
         if (wid == 2) prep_gram_L<DK>(sm, lane);
         if (wid == 3) prep_gram_P<DK>(sm, lane);
+        if (is_state) {
+            transpose_k<DK>(sm, lane, wid);
+            state_phase1<DK>(st, sm, lane, wid, cbase);
+        }
         __syncthreads();
         if (wid == 2) {
             solve_diag(sm, 0, lane, S::oL, S::oTf, S::oTt, S::oT);
@@ -643,7 +732,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
         __syncthreads();
         if (wid >= 2) solve_level2(sm, wid - 2, lane, S::oL, S::oTf, S::oTt, S::oT);
         __syncthreads();
-        if (is_state) state_chunk<DK>(p, st, sm, lane, cbase, t0, len, h, vb);
+        if (is_state) state_phase4<DK>(p, st, sm, lane, wid, cbase, t0, len, h, vb);
         __syncthreads();
     }
 
