@@ -4,28 +4,36 @@
 // Method: page pzsr.cn/news/750, section 1、为什么要设计为chunk的模式 -- cut the sequence into chunks,
 // compute inside a chunk in parallel, carry the state serially between chunks, and block the K/V
 // dimensions.  The chunk algebra (derived from u_t = beta_t (v_t - alpha_t S_{t-1} k_t),
-// S_t = alpha_t S_{t-1} + u_t k_t^T; no chunk algebra is printed on the pages):
+// S_t = alpha_t S_{t-1} + u_t k_t^T; the pages print no chunk algebra):
 //   gamma = inclusive prefix sum of g in the chunk, M_ij = exp(gamma_i - gamma_j) (j <= i),
 //   L = strict_lower(diag(beta) (M o Khat Khat^T)),  T = (I + L)^-1,
 //   X = diag(beta) V - diag(beta Gamma) Khat S^T,  U = T X,
 //   O = diag(Gamma) Qhat S^T + lower(M o Qhat Khat^T) U,
 //   S <- Gamma_C S + U^T diag(exp(gamma_C - gamma)) Khat.
 // Khat = diag(rk) K with rk = rsqrt(|k|^2 + eps) (likewise Qhat): the raw bf16 rows are the MFMA
-// operands (exact), the norms are folded into the row/column scalings above.
+// operands (exact); the norms come from the diagonals of K K^T and Q Q^T and are folded into the
+// row and column scalings above.  Every decay factor is exp of a non-positive number.
 //
 // Work decomposition: one workgroup (4 wavefronts) per (sequence n, head h, block of 32 state
-// rows).  State rows are independent, so the split over row blocks is exact.
-//   * waves 0-1 ("state waves") each own 16 state rows c.  The whole state chain of a chunk
-//     (K S^T -> X -> U = T X -> O, S update) stays in registers: every 16x16 MFMA output tile is
-//     fed to the next product as an operand without leaving the wave, by reading the LDS operand
-//     of that product in the matching k order ("chain order": k = 4g+e and 16+4g+e for lane
-//     group g = lane/16).  S lives in fp32 accumulators for the whole sequence.
-//   * waves 2-3 ("prep waves") compute the state-independent part: the gate prefix sum and decay
-//     factors, the masked Gram matrices L and Pm, and T = (I + L)^-1 (16x16 diagonal blocks by
-//     fp32 forward substitution, then two block-merge levels on MFMA with bf16 hi/lo operand
-//     splitting, accurate to about 2^-16).
-// MFMA: v_mfma_f32_16x16x32_bf16.  A: lane l holds A[l%16][8(l/16)+e]; B: B[8(l/16)+e][l%16];
-// D: D[4(l/16)+e][l%16] (e = element index).
+// rows); state rows are independent, so the split is exact.  Software pipeline over chunks: in
+// iteration k the two "prep" waves (2, 3) build the state-independent operands of chunk k (gates,
+// norms, Pm = lower(M o Qhat Khat^T), T = (I + L)^-1) while the two "state" waves (0, 1) run the
+// state chain of chunk k-1, and every wave issues direct global->LDS loads (global_load_lds_dwordx4,
+// no registers involved) of chunk k+1.  Raw chunk inputs are triple buffered, prep outputs double
+// buffered.  Three barriers per iteration separate the sub-stages:
+//   A: prep: Gram tiles, norms, masks (L^T, Pm), gates  | state: K S^T, S Q^T, X
+//   B: prep: 16x16 diagonal blocks of T, first merge    | state: U, O (stored), S update
+//   C: prep: second merge level of T                    | all: wait for the chunk k+1 loads
+// K, Q and V rows are stored unpadded with their 16-byte slots XOR-swizzled by the row index
+// (slot = part ^ (row mod parts-per-row)), which keeps every fragment read conflict-free and
+// lets a 1 KB load instruction fill whole rows.
+// The state chain stays in registers: each 16x16 MFMA output tile is fed to the next product as an
+// operand ("chain order": lane group g = lane/16 holds k = 4g+e and 16+4g+e).  Operands stored in
+// the other orientation (T, V, K for the state update) are read with the gfx950 transposing LDS
+// read ds_read_b64_tr_b16 (within each 16-lane group, output lane i element e is element i%4 of
+// the 8 bytes addressed by lane 4e + i/4).
+// MFMA v_mfma_f32_16x16x32_bf16: A lane l holds A[l%16][8(l/16)+e]; B: B[8(l/16)+e][l%16];
+// D: D[4(l/16)+e][l%16].
 #include "common.hpp"
 #include "kernels.hpp"
 #include "prologue.hpp"
@@ -37,28 +45,103 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float fx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-constexpr int C = 64;       // chunk length
-constexpr int BV = 32;      // state rows per workgroup
-constexpr int TSTR = C + 8; // bf16 row stride of token-contiguous tiles (K^T, V^T, T, Pm)
-constexpr int LSTR = C + 4; // fp32 row stride of the solve tiles
+constexpr int C = 64;        // chunk length
+constexpr int BV = 32;       // state rows per workgroup
+constexpr int TSTR = C + 8;  // bf16 row stride of T^T, Pm and L^T
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ fx4 mfma(bf16x8 a, bf16x8 b, fx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
 __device__ __forceinline__ fx4 zero4() { return fx4{0.f, 0.f, 0.f, 0.f}; }
 
-// 16-byte natural-order fragment: row[kb + 8g .. +7]
-__device__ __forceinline__ bf16x8 frag_nat(const __bf16* row, int kb, int g) {
-    return *reinterpret_cast<const bf16x8*>(row + kb + 8 * g);
+// Swizzled row-major tile of R rows x W bf16 (W/8 16-byte slots per row): element (r, c) lives at
+// r*W + 8*((c/8) ^ (r % (W/8))) + c%8.
+template <int W>
+__device__ __forceinline__ int swz(int r, int c) {
+    return r * W + 8 * ((c / 8) ^ (r % (W / 8))) + (c % 8);
 }
-// chain-order fragment: row[kb + 4g .. +3] and row[kb + 16 + 4g .. +3]
+// 16-byte natural-order fragment of a swizzled tile: row r, columns kb + 8g .. +7
+template <int W>
+__device__ __forceinline__ bf16x8 sfrag_nat(const __bf16* M, int r, int kb, int g) {
+    return *reinterpret_cast<const bf16x8*>(M + swz<W>(r, kb + 8 * g));
+}
+// chain-order fragment of a swizzled tile: row r, columns kb + 4g .. +3 and kb + 16 + 4g .. +3
+template <int W>
+__device__ __forceinline__ bf16x8 sfrag_chain(const __bf16* M, int r, int kb, int g) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(M + swz<W>(r, kb + 4 * g));
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(M + swz<W>(r, kb + 16 + 4 * g));
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// chain-order fragment of a padded row-major tile: row[kb + 4g .. +3] and row[kb + 16 + 4g .. +3]
 __device__ __forceinline__ bf16x8 frag_chain(const __bf16* row, int kb, int g) {
     const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + kb + 4 * g);
     const bf16x4 b = *reinterpret_cast<const bf16x4*>(row + kb + 16 + 4 * g);
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// Transposing reads (ds_read_b64_tr_b16): the calling lane, lane i of its 16-lane group, receives
+// M[r0 .. r0+3][c0 + i].  r0, c0 are group-uniform.  Source lane s of the group addresses
+// M[r0 + s/4][c0 + 4(s%4) .. +3].
+__device__ __forceinline__ bf16x4 tr_read(const __bf16* src) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const void*)src);
+}
+template <int W>
+__device__ __forceinline__ bf16x4 str4(const __bf16* M, int r0, int c0, int l16) {  // swizzled tile
+    return tr_read(M + swz<W>(r0 + l16 / 4, c0 + 4 * (l16 % 4)));
+}
+__device__ __forceinline__ bf16x4 tr4(const __bf16* M, int stride, int r0, int c0, int l16) {  // padded tile
+    return tr_read(M + (r0 + l16 / 4) * stride + c0 + 4 * (l16 % 4));
+}
+// chain-order fragments of the transpose: lane (i, g) gets M[kb + 4g .. +3][c0 + i] and
+// M[kb + 16 + 4g .. +3][c0 + i]
+template <int W>
+__device__ __forceinline__ bf16x8 sfrag_tr_chain(const __bf16* M, int kb, int c0, int g, int l16) {
+    const bf16x4 a = str4<W>(M, kb + 4 * g, c0, l16);
+    const bf16x4 b = str4<W>(M, kb + 16 + 4 * g, c0, l16);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x8 frag_tr_chain(const __bf16* M, int stride, int kb, int c0, int g, int l16) {
+    const bf16x4 a = tr4(M, stride, kb + 4 * g, c0, l16);
+    const bf16x4 b = tr4(M, stride, kb + 16 + 4 * g, c0, l16);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// natural-order fragment of the transpose: lane (i, g) gets M[kb + 8g .. +7][c0 + i]
+__device__ __forceinline__ bf16x8 frag_tr_nat(const __bf16* M, int stride, int kb, int c0, int g, int l16) {
+    const bf16x4 a = tr4(M, stride, kb + 8 * g, c0, l16);
+    const bf16x4 b = tr4(M, stride, kb + 8 * g + 4, c0, l16);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// Lane-constant element offsets into a swizzled DK-wide tile (PPR = DK/8 slots per row), so that
+// fragment reads become base + constant + immediate.  For rows 16t + l16 the XOR key is l16 % PPR.
+//   chain(ks, h): row l16, columns 32ks + 16h + 4g .. +3   (add 16t*DK for row tile t)
+//   nat(ks):      row l16, columns 32ks + 8g .. +7         (add 16t*DK)
+//   trk(dt):      row 4g + l16/4, columns 16dt + 4(l16%4)  (transposing source; add row offset kb*DK)
+template <int DK>
+__device__ __forceinline__ int off_chain(int ks, int h, int g, int l16) {
+    constexpr int PPR = DK / 8;
+    const int key = l16 % PPR;
+    return l16 * DK + 8 * ((4 * ks + 2 * h + g / 2) ^ key) + 4 * (g % 2);
+}
+template <int DK>
+__device__ __forceinline__ int off_nat(int ks, int g, int l16) {
+    constexpr int PPR = DK / 8;
+    const int key = l16 % PPR;
+    return l16 * DK + 8 * ((4 * ks + g) ^ key);
+}
+template <int DK>
+__device__ __forceinline__ int off_trk(int dt, int g, int l16) {
+    constexpr int PPR = DK / 8;
+    const int row = 4 * g + l16 / 4;
+    const int key = row % PPR;
+    return row * DK + 8 * ((2 * dt + (l16 % 4) / 2) ^ key) + 4 * (l16 % 2);
+}
+template <typename T>
+__device__ __forceinline__ T lds_at(const __bf16* base, int off) {
+    return *reinterpret_cast<const T*>(base + off);
+}
+
 // Two D fragments (rows 4g+e of consecutive 16-row tiles) as one chain-order operand.
 __device__ __forceinline__ bf16x8 pack_chain(fx4 a, fx4 b) {
     bf16x8 r;
@@ -66,41 +149,43 @@ __device__ __forceinline__ bf16x8 pack_chain(fx4 a, fx4 b) {
     r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
     return r;
 }
-// fp32 x -> (hi, lo) bf16 with hi + lo = x to about 2^-16 relative.
-__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)x[e];
-        hi[e] = h;
-        lo[e] = (__bf16)(x[e] - (float)h);
-    }
-}
-// hi/lo product: A B ~ Ah Bh + Ah Bl + Al Bh
-__device__ __forceinline__ fx4 mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, fx4 c) {
-    c = mfma(ah, bh, c);
-    c = mfma(ah, bl, c);
-    return mfma(al, bh, c);
+__device__ __forceinline__ float sel4(fx4 v, int e) {
+    return e == 0 ? v[0] : (e == 1 ? v[1] : (e == 2 ? v[2] : v[3]));
 }
 
+// ------------------------------------------------------------------------------------------
+// LDS layout (bytes).  Raw chunk buffers R0..R2 rotate by chunk index mod 3, prep-output buffers
+// P0/P1 by chunk parity; L^T and the per-prep-wave norm/gate arrays are prep scratch.
 template <int DK>
 struct Smem {
-    static constexpr int KSTR = DK + 8;  // bf16 row stride of token-major K and Q
-    static constexpr int oK = 0;                                   // bf16 [C][KSTR]
-    static constexpr int oQ = oK + C * KSTR * 2;                   // bf16 [C][KSTR]
-    static constexpr int oKt = oQ + C * KSTR * 2;                  // bf16 [DK][TSTR]
-    static constexpr int oVt = oKt + DK * TSTR * 2;                // bf16 [BV][TSTR]
-    static constexpr int oT = oVt + BV * TSTR * 2;                 // bf16 [C][TSTR]  T, row-major
-    static constexpr int oPm = oT + C * TSTR * 2;                  // bf16 [C][TSTR]  Pm, row-major
-    static constexpr int oL = oPm + C * TSTR * 2;                  // fp32 [C][LSTR]  L, row-major
-    static constexpr int oTf = oL + C * LSTR * 4;                  // fp32 [C][LSTR]  T, row-major
-    static constexpr int oTt = oTf + C * LSTR * 4;                 // fp32 [C][LSTR]  T, column-major
-    static constexpr int oG = oTt + C * LSTR * 4;                  // fp32 gate arrays [12][C]
-    static constexpr int bytes = oG + 12 * C * 4;
+    // raw buffer (K, Q, V swizzled, unpadded)
+    static constexpr int rK = 0;                     // bf16 [C][DK]
+    static constexpr int rQ = rK + C * DK * 2;       // bf16 [C][DK]
+    static constexpr int rV = rQ + C * DK * 2;       // bf16 [C][BV]
+    static constexpr int rG = rV + C * BV * 2;       // raw g [C]
+    static constexpr int rB = rG + C * 4;            // beta [C]
+    static constexpr int rBytes = rB + C * 4;
+    // prep-output buffer
+    static constexpr int pT = 0;                     // T^T bf16 [C][TSTR]: pT[m][i] = T[i][m]
+    static constexpr int pPm = pT + C * TSTR * 2;    // Pm bf16 [C][TSTR], row-major [i][m]
+    static constexpr int pKK = pPm + C * TSTR * 2;   // beta Gamma rk [C]
+    static constexpr int pORQ = pKK + C * 4;         // Gamma rq [C]
+    static constexpr int pDRK = pORQ + C * 4;        // exp(gamma_C - gamma) rk [C]
+    static constexpr int pBETA = pDRK + C * 4;       // beta [C]
+    static constexpr int pGC = pBETA + C * 4;        // Gamma_C (first of 16 floats)
+    static constexpr int pBytes = pGC + 64;
+    // layout
+    static constexpr int R0 = 0;
+    static constexpr int P0 = R0 + 3 * rBytes;
+    static constexpr int L = P0 + 2 * pBytes;        // L^T bf16 [C][TSTR]: L[j][i] = L_ij
+    static constexpr int W2 = L + C * TSTR * 2;      // wave 2: rk, row exponent, column exponent [3][C]
+    static constexpr int W3 = W2 + 3 * C * 4;        // wave 3: rk, rq, row exponent, column exponent [4][C]
+    static constexpr int bytes = W3 + 4 * C * 4;
+    static_assert(rBytes % 16 == 0, "alignment");
+    static_assert(pBytes % 16 == 0, "alignment");
+    static __device__ __forceinline__ int raw(int c) { return R0 + (c % 3) * rBytes; }
+    static __device__ __forceinline__ int prep(int c) { return P0 + (c & 1) * pBytes; }
 };
-// gate array slots (fp32 [C] each).  Each state wave w keeps its own decay factors in slots
-// G_SKK + 3w (beta Gamma rk), G_SORQ + 3w (Gamma rq) and G_SDRK + 3w (exp(gamma_C - gamma) rk).
-enum { G_RAW = 0, G_BETA, G_RK, G_RQ, G_GAM0, G_GAM1, G_SKK, G_SORQ, G_SDRK, G_NSLOT = G_SKK + 6 };
-static_assert(G_NSLOT <= 12, "gate slots");
 
 template <int DK>
 struct Params {
@@ -115,96 +200,71 @@ struct Params {
 };
 
 // ------------------------------------------------------------------------------------------
-// chunk loader: global -> LDS (token-major K/Q, transposed K and V), norms, raw gates.
-// 256 lanes; one 16-byte part (8 elements) of a K or Q row per lane per pass.
+// chunk loads: direct global -> LDS (global_load_lds_dwordx4 / _dword).  One instruction moves
+// 1 KB (64 lanes x 16 B) into a contiguous LDS range; lane l fills 16-byte slot l of that range,
+// so each lane fetches the global part that the swizzle places in its slot.  Wave w loads rows
+// [16w, 16w + 16) of K, Q and V; wave 0 loads g, wave 1 beta.  Rows past the tail re-read the
+// last valid row and are cleared by zero_tail once the loads have landed.
 template <int DK>
-struct ChunkRegs {
-    static constexpr int PPR = DK / 8;          // 16-byte parts per row
-    static constexpr int RPP = 256 / PPR;       // rows per pass
-    static constexpr int NP = C / RPP;          // passes
-    uint4 kr[NP], qr[NP];
-    uint4 vr;
-    float gr, br;
-};
-
-template <int DK>
-__device__ __forceinline__ void fetch_chunk(const Params<DK>& p, ChunkRegs<DK>& R, long t0, int len, int h, int vb,
-                                            int tid) {
-    // Rows past the tail re-read the last valid row (len >= 1) and are zeroed when stored: the
-    // loads stay unconditional, so no wait is forced between them.
-    using CR = ChunkRegs<DK>;
-    const int part = tid % CR::PPR;
+__device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned char* sm, int rawoff, long t0, int len, int h,
+                                          int vb, int wid, int lane) {
+    using S = Smem<DK>;
+    constexpr int PPR = DK / 8;       // 16-byte slots per K/Q row
+    constexpr int RPI = 64 / PPR;     // rows per 1 KB instruction
+    const size_t rowq = (size_t)p.H * DK;
 #pragma unroll
-    for (int j = 0; j < CR::NP; ++j) {
-        const int r = min(tid / CR::PPR + j * CR::RPP, len - 1);
-        const size_t off = ((size_t)(t0 + r) * p.H + h) * DK + 8 * part;
-        R.kr[j] = *reinterpret_cast<const uint4*>(p.k + off);
-        R.qr[j] = *reinterpret_cast<const uint4*>(p.q + off);
+    for (int j = 0; j < 16 / RPI; ++j) {
+        const int row0 = 16 * wid + RPI * j;
+        const int row = row0 + lane / PPR, slot = lane % PPR;
+        const int part = slot ^ (row % PPR);
+        const size_t off = (size_t)(t0 + min(row, len - 1)) * rowq + (size_t)h * DK + 8 * part;
+        const int lo = rawoff + row0 * DK * 2;
+        __builtin_amdgcn_global_load_lds(p.k + off, (lds_void*)(sm + lo + S::rK), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(p.q + off, (lds_void*)(sm + lo + S::rQ), 16, 0, 0);
     }
     {
-        // V: one token per lane (part = wave) so the transposed LDS writes are contiguous
-        const int r = min(tid % C, len - 1), pv = tid / C;
-        R.vr = *reinterpret_cast<const uint4*>(p.v + ((size_t)(t0 + r) * p.H + h) * p.dv + vb * BV + 8 * pv);
+        const int row = 16 * wid + lane / 4, slot = lane % 4, part = slot ^ (row % 4);
+        const size_t off = ((size_t)(t0 + min(row, len - 1)) * p.H + h) * p.dv + vb * BV + 8 * part;
+        __builtin_amdgcn_global_load_lds(p.v + off, (lds_void*)(sm + rawoff + S::rV + 16 * wid * BV * 2), 16, 0, 0);
     }
-    const int r = min(tid % C, len - 1);
-    R.gr = p.g[(size_t)(t0 + r) * p.H + h];
-    R.br = p.beta[(size_t)(t0 + r) * p.H + h];
+    if (wid < 2) {
+        const size_t off = (size_t)(t0 + min(lane, len - 1)) * p.H + h;
+        __builtin_amdgcn_global_load_lds(wid == 0 ? p.g + off : p.beta + off,
+                                         (lds_void*)(sm + rawoff + (wid == 0 ? S::rG : S::rB)), 4, 0, 0);
+    }
 }
 
-__device__ __forceinline__ float sumsq8(uint4 u) {
-    float s = 0.f;
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float a = __builtin_bit_cast(float, w[i] << 16), b = __builtin_bit_cast(float, w[i] & 0xffff0000u);
-        s += a * a + b * b;
-    }
-    return s;
-}
-
+// After this wave's loads landed: clear its rows past the tail (last chunk of a sequence only).
 template <int DK>
-__device__ __forceinline__ void store_chunk(const ChunkRegs<DK>& R, unsigned char* sm, int len, int l2norm, int tid) {
+__device__ __forceinline__ void zero_tail(unsigned char* raw, int len, int wid, int lane) {
     using S = Smem<DK>;
-    using CR = ChunkRegs<DK>;
-    __bf16* sK = reinterpret_cast<__bf16*>(sm + S::oK);
-    __bf16* sQ = reinterpret_cast<__bf16*>(sm + S::oQ);
-    __bf16* sVt = reinterpret_cast<__bf16*>(sm + S::oVt);
-    float* sG = reinterpret_cast<float*>(sm + S::oG);
-    const int part = tid % CR::PPR;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < CR::NP; ++j) {
-        const int r = tid / CR::PPR + j * CR::RPP;
-        const bool in = r < len;
-        const uint4 kv = in ? R.kr[j] : z, qv = in ? R.qr[j] : z;
-        *reinterpret_cast<uint4*>(sK + r * S::KSTR + 8 * part) = kv;
-        *reinterpret_cast<uint4*>(sQ + r * S::KSTR + 8 * part) = qv;
-        float sk = group_sum<CR::PPR>(sumsq8(kv));
-        float sq = group_sum<CR::PPR>(sumsq8(qv));
-        if (part == 0) {
-            sG[G_RK * C + r] = in ? (l2norm ? rsqrtf(sk + kL2Eps) : 1.f) : 0.f;
-            sG[G_RQ * C + r] = in ? (l2norm ? rsqrtf(sq + kL2Eps) : 1.f) : 0.f;
+    if (len >= C) return;
+    __bf16* K = reinterpret_cast<__bf16*>(raw + S::rK);
+    __bf16* Q = reinterpret_cast<__bf16*>(raw + S::rQ);
+    __bf16* V = reinterpret_cast<__bf16*>(raw + S::rV);
+    const __bf16 z = (__bf16)0.f;
+    for (int i = lane; i < 16 * DK; i += 64) {
+        const int row = 16 * wid + i / DK;
+        if (row >= len) {
+            K[row * DK + i % DK] = z;
+            Q[row * DK + i % DK] = z;
         }
     }
-    {
-        const int r = tid % C, pv = tid / C;
-        const uint4 vv = r < len ? R.vr : z;
-        const uint16_t* vh = reinterpret_cast<const uint16_t*>(&vv);
-        uint16_t* vt = reinterpret_cast<uint16_t*>(sVt);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vt[(8 * pv + e) * TSTR + r] = vh[e];
+    for (int i = lane; i < 16 * BV; i += 64) {
+        const int row = 16 * wid + i / BV;
+        if (row >= len) V[row * BV + i % BV] = z;
     }
-    if (tid < C) {
-        const bool in = tid < len;
-        sG[G_RAW * C + tid] = in ? R.gr : 0.f;
-        sG[G_BETA * C + tid] = in ? R.br : 0.f;
-    }
+    if (wid < 2 && lane >= len) reinterpret_cast<float*>(raw + (wid == 0 ? S::rG : S::rB))[lane] = 0.f;
+}
+
+__device__ __forceinline__ void wait_loads() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
 // ------------------------------------------------------------------------------------------
 // prep waves
 
-// inclusive prefix sum of the raw gate over the 64 lanes of a wave
+// inclusive prefix sum over the 64 lanes of a wave
 __device__ __forceinline__ float wave_scan(float x, int lane) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -214,113 +274,174 @@ __device__ __forceinline__ float wave_scan(float x, int lane) {
     return x;
 }
 
-// Wave p0: the strict-lower masked Gram L = strict_lower(diag(beta) (M o Khat Khat^T)), fp32,
-// row-major.  K fragments stay in registers: A and B operands of K K^T are the same data.
+// Norm of row 16 t + l16 from a diagonal Gram tile held in D layout: lane (l16, g = l16/4) holds
+// the diagonal at element l16 % 4.  Writes rsqrt(x + eps) (0 past the tail, 1 without L2 norm).
+__device__ __forceinline__ void write_norm(float* dst, fx4 diag, int t, int lane, int len, int l2norm) {
+    const int g = lane / 16, l16 = lane % 16;
+    if (g == l16 / 4) {
+        const int i = 16 * t + l16;
+        const float x = sel4(diag, l16 % 4);
+        dst[i] = i < len ? (l2norm ? rsqrtf(x + kL2Eps) : 1.f) : 0.f;
+    }
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Wave 2: K K^T (all lower tiles), rk, gates for the state waves, and L^T (bf16, L^T[j][i] = L_ij,
+// strict lower L masked with beta_i rk_i rk_j exp(gamma_i - gamma_j)).  The mask is evaluated in the
+// log2 domain: L_ij = exp2(a_i - b_j) G_ij with a_i = gamma_i log2e + log2(beta_i rk_i) and
+// b_j = gamma_j log2e - log2(rk_j); the decay part of the exponent is never positive, and a zero
+// beta or norm gives exp2(-inf) = 0.
 template <int DK>
-__device__ void prep_gram_L(unsigned char* sm, int lane) {
+__device__ void prep_L(const unsigned char* raw, unsigned char* pb, unsigned char* sm, int lane, int len,
+                       int l2norm) {
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
-    const __bf16* sK = reinterpret_cast<const __bf16*>(sm + S::oK);
-    float* sG = reinterpret_cast<float*>(sm + S::oG);
-    float* sL = reinterpret_cast<float*>(sm + S::oL);
+    const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
+    const float* gr = reinterpret_cast<const float*>(raw + S::rG);
+    const float* br = reinterpret_cast<const float*>(raw + S::rB);
+    __bf16* sLt = reinterpret_cast<__bf16*>(sm + S::L);
+    float* own = reinterpret_cast<float*>(sm + S::W2);  // rk [C], a [C], b [C]
+    float* pKK = reinterpret_cast<float*>(pb + S::pKK);
+    float* pDRK = reinterpret_cast<float*>(pb + S::pDRK);
+    float* pBETA = reinterpret_cast<float*>(pb + S::pBETA);
+    float* pGC = reinterpret_cast<float*>(pb + S::pGC);
     const int g = lane / 16, l16 = lane % 16;
 
     bf16x8 kf[4][KS];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int ks = 0; ks < KS; ++ks) {
+        const int o = off_nat<DK>(ks, g, l16);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[rb][ks] = frag_nat(sK + (16 * rb + l16) * S::KSTR, 32 * ks, g);
-    sG[G_GAM0 * C + lane] = wave_scan(sG[G_RAW * C + lane], lane);
+        for (int rb = 0; rb < 4; ++rb) kf[rb][ks] = lds_at<bf16x8>(K, o + 16 * rb * DK);
+    }
+    const float gam = wave_scan(gr[lane], lane);
+    const float gl = __shfl(gam, C - 1);
 
+    fx4 acc[4][4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        fx4 acc[4];
 #pragma unroll
-        for (int jt = 0; jt <= it; ++jt) acc[jt] = zero4();
+        for (int jt = 0; jt <= it; ++jt) acc[it][jt] = zero4();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int jt = 0; jt <= it; ++jt) acc[jt] = mfma(kf[it][ks], kf[jt][ks], acc[jt]);
+            for (int jt = 0; jt <= it; ++jt) acc[it][jt] = mfma(kf[it][ks], kf[jt][ks], acc[it][jt]);
+        write_norm(own, acc[it][it], it, lane, len, l2norm);
+    }
+    // gates of this chunk for the state waves and the mask exponents (lane = token)
+    {
+        const float rk = own[lane], b = br[lane];
+        pKK[lane] = b * __expf(gam) * rk;
+        pDRK[lane] = __expf(gl - gam) * rk;
+        pBETA[lane] = b;
+        if (lane == 0) pGC[0] = __expf(gl);
+        const float g2 = gam * kLog2e;
+        own[C + lane] = g2 + __builtin_amdgcn_logf(b * rk);
+        own[2 * C + lane] = g2 - __builtin_amdgcn_logf(rk);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
         const int i0 = 16 * it + 4 * g;
-        const fx4 gi = *reinterpret_cast<const fx4*>(sG + G_GAM0 * C + i0);
-        const fx4 bi = *reinterpret_cast<const fx4*>(sG + G_BETA * C + i0);
-        const fx4 ri = *reinterpret_cast<const fx4*>(sG + G_RK * C + i0);
+        const fx4 ai = *reinterpret_cast<const fx4*>(own + C + i0);
 #pragma unroll
         for (int jt = 0; jt <= it; ++jt) {
             const int j = 16 * jt + l16;
-            const float gj = sG[G_GAM0 * C + j], rj = sG[G_RK * C + j];
+            const float bj = own[2 * C + j];
+            bf16x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int i = i0 + e;
-                sL[i * LSTR + j] = j < i ? bi[e] * ri[e] * rj * __expf(gi[e] - gj) * acc[jt][e] : 0.f;
+                const float val = __builtin_amdgcn_exp2f(ai[e] - bj) * acc[it][jt][e];
+                out[e] = (__bf16)((jt < it || j < i0 + e) ? val : 0.f);
             }
+            *reinterpret_cast<bf16x4*>(sLt + j * TSTR + i0) = out;
         }
     }
 }
 
-// Wave p1: Pm = lower(M o Qhat Khat^T) (bf16, row-major [i][m]), computed as D = K Q^T so that
-// a lane holds 4 consecutive m of one row i.
+// Wave 3: norms (diagonals of K K^T and Q Q^T), Gamma rq, and Pm = lower(M o Qhat Khat^T) computed
+// as D = K Q^T so that a lane holds 4 consecutive m of row i (bf16, row-major).  Mask in the log2
+// domain: Pm_im = exp2(a_i - b_m) P_im, a_i = gamma_i log2e + log2(rq_i), b_m = gamma_m log2e - log2(rk_m).
 template <int DK>
-__device__ void prep_gram_P(unsigned char* sm, int lane) {
+__device__ void prep_P(const unsigned char* raw, unsigned char* pb, unsigned char* sm, int lane, int len,
+                       int l2norm) {
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
-    const __bf16* sK = reinterpret_cast<const __bf16*>(sm + S::oK);
-    const __bf16* sQ = reinterpret_cast<const __bf16*>(sm + S::oQ);
-    float* sG = reinterpret_cast<float*>(sm + S::oG);
-    __bf16* sPm = reinterpret_cast<__bf16*>(sm + S::oPm);
+    const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
+    const __bf16* Q = reinterpret_cast<const __bf16*>(raw + S::rQ);
+    const float* gr = reinterpret_cast<const float*>(raw + S::rG);
+    float* own = reinterpret_cast<float*>(sm + S::W3);  // rk [C], rq [C], a [C], b [C]
+    __bf16* Pm = reinterpret_cast<__bf16*>(pb + S::pPm);
+    float* pORQ = reinterpret_cast<float*>(pb + S::pORQ);
     const int g = lane / 16, l16 = lane % 16;
 
     bf16x8 kf[4][KS], qf[4][KS];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int ks = 0; ks < KS; ++ks) {
+        const int o = off_nat<DK>(ks, g, l16);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kf[rb][ks] = frag_nat(sK + (16 * rb + l16) * S::KSTR, 32 * ks, g);
-            qf[rb][ks] = frag_nat(sQ + (16 * rb + l16) * S::KSTR, 32 * ks, g);
+        for (int rb = 0; rb < 4; ++rb) {
+            kf[rb][ks] = lds_at<bf16x8>(K, o + 16 * rb * DK);
+            qf[rb][ks] = lds_at<bf16x8>(Q, o + 16 * rb * DK);
         }
-    sG[G_GAM1 * C + lane] = wave_scan(sG[G_RAW * C + lane], lane);
+    }
+    const float gam = wave_scan(gr[lane], lane);
 
+    fx4 acc[4][4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        fx4 acc[4];
+        fx4 dk = zero4(), dq = zero4();
 #pragma unroll
-        for (int mt = 0; mt <= it; ++mt) acc[mt] = zero4();
+        for (int mt = 0; mt <= it; ++mt) acc[it][mt] = zero4();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-            for (int mt = 0; mt <= it; ++mt) acc[mt] = mfma(kf[mt][ks], qf[it][ks], acc[mt]);
+            for (int mt = 0; mt <= it; ++mt) acc[it][mt] = mfma(kf[mt][ks], qf[it][ks], acc[it][mt]);
+            dk = mfma(kf[it][ks], kf[it][ks], dk);
+            dq = mfma(qf[it][ks], qf[it][ks], dq);
+        }
+        write_norm(own, dk, it, lane, len, l2norm);
+        write_norm(own + C, dq, it, lane, len, l2norm);
+    }
+    {
+        const float rq = own[C + lane], rk = own[lane];
+        pORQ[lane] = __expf(gam) * rq;
+        const float g2 = gam * kLog2e;
+        own[2 * C + lane] = g2 + __builtin_amdgcn_logf(rq);
+        own[3 * C + lane] = g2 - __builtin_amdgcn_logf(rk);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
         const int i = 16 * it + l16;
-        const float gi = sG[G_GAM1 * C + i], rqi = sG[G_RQ * C + i];
+        const float ai = own[2 * C + i];
 #pragma unroll
         for (int mt = 0; mt <= it; ++mt) {
             const int m0 = 16 * mt + 4 * g;
-            const fx4 gm = *reinterpret_cast<const fx4*>(sG + G_GAM1 * C + m0);
-            const fx4 rkm = *reinterpret_cast<const fx4*>(sG + G_RK * C + m0);
+            const fx4 bm = *reinterpret_cast<const fx4*>(own + 3 * C + m0);
             bf16x4 out;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                out[e] = (__bf16)(m0 + e <= i ? rqi * rkm[e] * __expf(gi - gm[e]) * acc[mt][e] : 0.f);
-            *reinterpret_cast<bf16x4*>(sPm + i * TSTR + m0) = out;
+            for (int e = 0; e < 4; ++e) {
+                const float val = __builtin_amdgcn_exp2f(ai - bm[e]) * acc[it][mt][e];
+                out[e] = (__bf16)((mt < it || m0 + e <= i) ? val : 0.f);
+            }
+            *reinterpret_cast<bf16x4*>(Pm + i * TSTR + m0) = out;
         }
     }
 }
 
 // Solve level 0: invert the 16x16 unit-lower diagonal blocks b0, b0+1 of (I + L) by forward
-// substitution, one column per lane (lanes 0..31).  The block's rows of L are read once with
-// 16-byte loads; the right-looking update keeps one FMA on the critical path per step.  Writes
-// T (fp32 row- and column-major and bf16 row-major).
-__device__ void solve_diag(unsigned char* sm, int b0, int lane, int oL, int oTf, int oTt, int oT) {
-    const float* sL = reinterpret_cast<const float*>(sm + oL);
-    float* sTf = reinterpret_cast<float*>(sm + oTf);
-    float* sTt = reinterpret_cast<float*>(sm + oTt);
-    __bf16* sT = reinterpret_cast<__bf16*>(sm + oT);
+// substitution, one column per lane (lanes 0..31; lanes 32..63 compute a duplicate and discard
+// it).  Column m of the block is row m of L^T: read once with 16-byte loads.  The right-looking
+// update keeps one FMA on the critical path per step.  Writes the blocks of T^T (bf16; column j
+// of T = row j of T^T).
+__device__ void solve_diag(const __bf16* sLt, __bf16* Tt, int b0, int lane) {
     const int b = b0 + (lane / 16) % 2, j = lane % 16, base = 16 * b;
-    fx4 Lr[16][4];
+    bf16x8 Lc[16][2];
 #pragma unroll
-    for (int i = 1; i < 16; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (4 * q < i) Lr[i][q] = *reinterpret_cast<const fx4*>(sL + (base + i) * LSTR + base + 4 * q);
+    for (int m = 0; m < 15; ++m) {
+        Lc[m][0] = *reinterpret_cast<const bf16x8*>(sLt + (base + m) * TSTR + base);
+        Lc[m][1] = *reinterpret_cast<const bf16x8*>(sLt + (base + m) * TSTR + base + 8);
+    }
     float acc[16], t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
@@ -329,204 +450,102 @@ __device__ void solve_diag(unsigned char* sm, int b0, int lane, int oL, int oTf,
         const float tm = m == j ? 1.f : (m > j ? -acc[m] : 0.f);
         t[m] = tm;
 #pragma unroll
-        for (int i = m + 1; i < 16; ++i) acc[i] += Lr[i][m / 4][m % 4] * tm;
+        for (int i = m + 1; i < 16; ++i) acc[i] += (float)Lc[m][i / 8][i % 8] * tm;
     }
-    if (lane >= 32) return;
+    if (lane < 32) {
+        bf16x8 lo, hi;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        sTf[(base + m) * LSTR + base + j] = t[m];
-        sT[(base + m) * TSTR + base + j] = (__bf16)t[m];
+        for (int e = 0; e < 8; ++e) {
+            lo[e] = (__bf16)t[e];
+            hi[e] = (__bf16)t[8 + e];
+        }
+        *reinterpret_cast<bf16x8*>(Tt + (base + j) * TSTR + base) = lo;
+        *reinterpret_cast<bf16x8*>(Tt + (base + j) * TSTR + base + 8) = hi;
     }
-#pragma unroll
-    for (int m = 0; m < 16; m += 4)
-        *reinterpret_cast<fx4*>(sTt + (base + j) * LSTR + base + m) = fx4{t[m], t[m + 1], t[m + 2], t[m + 3]};
 }
 
-// Solve level 1: T_{b+1,b} = -T_{b+1,b+1} L_{b+1,b} T_{b,b} for the 16x16 block pair (b, b+1).
-__device__ void solve_level1(unsigned char* sm, int b, int lane, int oL, int oTf, int oTt, int oT) {
-    const float* sL = reinterpret_cast<const float*>(sm + oL);
-    float* sTf = reinterpret_cast<float*>(sm + oTf);
-    float* sTt = reinterpret_cast<float*>(sm + oTt);
-    __bf16* sT = reinterpret_cast<__bf16*>(sm + oT);
+// Solve level 1: T_{b+1,b} = -T_{b+1,b+1} (L_{b+1,b} T_{b,b}) for the 16x16 block pair (b, b+1).
+// bf16 operands (K = 16 real, padded to 32 with zeros).
+__device__ void solve_level1(const __bf16* sLt, __bf16* Tt, int b, int lane) {
     const int g = lane / 16, l16 = lane % 16;
     const int r0 = 16 * (b + 1), c0 = 16 * b;
-    // Y = L_{b+1,b} T_bb : A = L rows r0+l16, k = m (natural order, k >= 16 zero)
-    float a[8], bb[8];
-    {
-        const int gg = g & 1;  // lanes with g >= 2 read valid memory and zero it (k >= 16 is padding)
-        const fx4 a0 = *reinterpret_cast<const fx4*>(sL + (r0 + l16) * LSTR + c0 + 8 * gg);
-        const fx4 a1 = *reinterpret_cast<const fx4*>(sL + (r0 + l16) * LSTR + c0 + 8 * gg + 4);
-        const fx4 b0v = *reinterpret_cast<const fx4*>(sTt + (c0 + l16) * LSTR + c0 + 8 * gg);  // T_bb column l16
-        const fx4 b1v = *reinterpret_cast<const fx4*>(sTt + (c0 + l16) * LSTR + c0 + 8 * gg + 4);
-        const float keep = g < 2 ? 1.f : 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = keep * a0[e];
-            a[4 + e] = keep * a1[e];
-            bb[e] = keep * b0v[e];
-            bb[4 + e] = keep * b1v[e];
-        }
+    const int gg = g & 1;
+    // Y = L_{b+1,b} T_bb: A = L[r0 + l16][c0 + 8gg ..] (= L^T columns, transposing read),
+    // B = T_bb[c0 + 8gg ..][c0 + l16] (= T^T row c0 + l16)
+    bf16x8 a = frag_tr_nat(sLt, TSTR, c0, r0, gg, l16);
+    bf16x8 bt = *reinterpret_cast<const bf16x8*>(Tt + (c0 + l16) * TSTR + c0 + 8 * gg);
+    if (g >= 2) {
+        const bf16x8 zb = {};
+        a = zb;
+        bt = zb;
     }
-    bf16x8 ah, al, bh, bl;
-    split8(a, ah, al);
-    split8(bb, bh, bl);
-    fx4 y = mfma3(ah, al, bh, bl, zero4());
-    // T_{b+1,b} = -T_{b+1,b+1} Y : B = Y from registers (k = 4g+e), A = T rows in the same order
-    float a2[8], y2[8];
-    {
-        const fx4 tv = *reinterpret_cast<const fx4*>(sTf + (r0 + l16) * LSTR + r0 + 4 * g);
+    const fx4 y = mfma(a, bt, zero4());
+    // T_{b+1,b} = -T_{b+1,b+1} Y: A = rows of T_{b+1,b+1} (chain order, k = 4g+e real), B = Y
+    const bf16x4 tr = tr4(Tt, TSTR, r0 + 4 * g, r0, l16);  // T[r0 + l16][r0 + 4g .. +3]
+    const bf16x4 z4 = {};
+    const bf16x8 at = __builtin_shufflevector(tr, z4, 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8 by = pack_chain(y, zero4());
+    const fx4 t = mfma(at, by, zero4());
+    // lane holds T[r0 + 4g + e][c0 + l16] = -t[e] -> T^T row c0 + l16
+    bf16x4 out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a2[e] = tv[e];
-            y2[e] = y[e];
-            a2[4 + e] = 0.f;
-            y2[4 + e] = 0.f;
-        }
-    }
-    split8(a2, ah, al);
-    split8(y2, bh, bl);
-    fx4 t = mfma3(ah, al, bh, bl, zero4());
-    // lane holds T[r0 + 4g + e][c0 + l16] = -t[e]
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float v = -t[e];
-        sTf[(r0 + 4 * g + e) * LSTR + c0 + l16] = v;
-        sT[(r0 + 4 * g + e) * TSTR + c0 + l16] = (__bf16)v;
-    }
-    *reinterpret_cast<fx4*>(sTt + (c0 + l16) * LSTR + r0 + 4 * g) = fx4{-t[0], -t[1], -t[2], -t[3]};
+    for (int e = 0; e < 4; ++e) out[e] = (__bf16)(-t[e]);
+    *reinterpret_cast<bf16x4*>(Tt + (c0 + l16) * TSTR + r0 + 4 * g) = out;
 }
 
-// Solve level 2: columns [16 half, 16 half + 16) of T_BA = -T_BB L_BA T_AA (32x32 blocks A = rows
-// 0..31, B = rows 32..63).  Writes bf16 T only.
-__device__ void solve_level2(unsigned char* sm, int half, int lane, int oL, int oTf, int oTt, int oT) {
-    const float* sL = reinterpret_cast<const float*>(sm + oL);
-    const float* sTf = reinterpret_cast<const float*>(sm + oTf);
-    const float* sTt = reinterpret_cast<const float*>(sm + oTt);
-    __bf16* sT = reinterpret_cast<__bf16*>(sm + oT);
+// Solve level 2: columns [16 half, 16 half + 16) of T_BA = -T_BB (L_BA T_AA), 32x32 blocks
+// A = rows 0..31, B = rows 32..63.
+__device__ void solve_level2(const __bf16* sLt, __bf16* Tt, int half, int lane) {
     const int g = lane / 16, l16 = lane % 16;
-    const int jc = 16 * half + l16;  // column of T_AA / T_BA handled by this lane (as N index)
-    // B operand: T_AA[m][jc], m = 8g+e (natural order over K = 32), column-major source
-    float bb[8];
-    {
-        const fx4 b0v = *reinterpret_cast<const fx4*>(sTt + jc * LSTR + 8 * g);
-        const fx4 b1v = *reinterpret_cast<const fx4*>(sTt + jc * LSTR + 8 * g + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bb[e] = b0v[e];
-            bb[4 + e] = b1v[e];
-        }
-    }
-    bf16x8 bh, bl;
-    split8(bb, bh, bl);
+    const int jc = 16 * half + l16;
+    // B operand: T_AA[8g .. +7][jc] = T^T row jc
+    const bf16x8 bt = *reinterpret_cast<const bf16x8*>(Tt + jc * TSTR + 8 * g);
     fx4 y[2];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-        float a[8];
-        const fx4 a0 = *reinterpret_cast<const fx4*>(sL + (32 + 16 * it + l16) * LSTR + 8 * g);
-        const fx4 a1 = *reinterpret_cast<const fx4*>(sL + (32 + 16 * it + l16) * LSTR + 8 * g + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = a0[e];
-            a[4 + e] = a1[e];
-        }
-        bf16x8 ah, al;
-        split8(a, ah, al);
-        y[it] = mfma3(ah, al, bh, bl, zero4());
+        // A = L[32 + 16 it + l16][8g .. +7] via transposing reads of L^T
+        const bf16x8 a = frag_tr_nat(sLt, TSTR, 0, 32 + 16 * it, g, l16);
+        y[it] = mfma(a, bt, zero4());
     }
-    // T_BA = -T_BB Y : B = Y (chain order: tiles 0/1 rows 4g+e), A = T_BB rows, chain order
-    float yv[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        yv[e] = y[0][e];
-        yv[4 + e] = y[1][e];
-    }
-    bf16x8 yh, yl;
-    split8(yv, yh, yl);
+    const bf16x8 yb = pack_chain(y[0], y[1]);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-        float a[8];
-        const float* row = sTf + (32 + 16 * it + l16) * LSTR + 32;
-        const fx4 a0 = *reinterpret_cast<const fx4*>(row + 4 * g);
-        const fx4 a1 = *reinterpret_cast<const fx4*>(row + 16 + 4 * g);
+        // A = T_BB rows 32 + 16 it + l16, chain order over m in 32..63
+        const bf16x8 at = frag_tr_chain(Tt, TSTR, 32, 32 + 16 * it, g, l16);
+        const fx4 t = mfma(at, yb, zero4());
+        bf16x4 out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = a0[e];
-            a[4 + e] = a1[e];
-        }
-        bf16x8 ah, al;
-        split8(a, ah, al);
-        const fx4 t = mfma3(ah, al, yh, yl, zero4());
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sT[(32 + 16 * it + 4 * g + e) * TSTR + jc] = (__bf16)(-t[e]);
+        for (int e = 0; e < 4; ++e) out[e] = (__bf16)(-t[e]);
+        *reinterpret_cast<bf16x4*>(Tt + jc * TSTR + 32 + 16 * it + 4 * g) = out;
     }
 }
 
 // ------------------------------------------------------------------------------------------
-// state waves: everything of one chunk for 16 state rows, in registers.
+// state waves: the chain of one chunk for 16 state rows, in registers.
 template <int DK>
 struct StateRegs {
     static constexpr int DT = DK / 16;
     fx4 S[DT];     // S^T tiles: lane (c = l%16, g) holds S[c][16 dt + 4g + e]
-    bf16x8 xb[2];  // X (chain order over tokens), carried from phase 1 to phase 4
-    fx4 ot[4];     // O^T accumulators (S Q^T part, already scaled by Gamma rq)
-    float gc;      // Gamma_C = exp(gamma of the last token)
+    bf16x8 xb[2];  // X, chain order over tokens
+    fx4 ot[4];     // O^T accumulators
 };
 
-// K^T (token-contiguous copy of K for the state update), written by the two state waves: each
-// lane owns one token, so consecutive lanes write consecutive 2-byte slots of a K^T row.
+// Part 1: K S^T, S Q^T (scaled by Gamma rq), X = beta V - beta Gamma rk K S^T.
 template <int DK>
-__device__ void transpose_k(unsigned char* sm, int lane, int sw) {
-    using S = Smem<DK>;
-    constexpr int PPR = DK / 8;
-    const __bf16* sK = reinterpret_cast<const __bf16*>(sm + S::oK);
-    uint16_t* kt = reinterpret_cast<uint16_t*>(sm + S::oKt);
-#pragma unroll
-    for (int q = 0; q < PPR / 2; ++q) {
-        const int part = sw * (PPR / 2) + q;
-        const uint4 v = *reinterpret_cast<const uint4*>(sK + lane * S::KSTR + 8 * part);
-        const uint16_t* vh = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kt[(8 * part + e) * TSTR + lane] = vh[e];
-    }
-}
-
-// Phase 1 (needs only the chunk inputs and S): own decay factors, K S^T, S Q^T and X.
-template <int DK>
-__device__ void state_phase1(StateRegs<DK>& st, unsigned char* sm, int lane, int sw, int cbase) {
+__device__ void state_part1(StateRegs<DK>& st, const unsigned char* raw, const unsigned char* pb, int lane, int cbase) {
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
-    const __bf16* sK = reinterpret_cast<const __bf16*>(sm + S::oK);
-    const __bf16* sQ = reinterpret_cast<const __bf16*>(sm + S::oQ);
-    const __bf16* sVt = reinterpret_cast<const __bf16*>(sm + S::oVt);
-    float* sG = reinterpret_cast<float*>(sm + S::oG);
+    const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
+    const __bf16* Q = reinterpret_cast<const __bf16*>(raw + S::rQ);
+    const __bf16* V = reinterpret_cast<const __bf16*>(raw + S::rV);
+    const float* pKK = reinterpret_cast<const float*>(pb + S::pKK);
+    const float* pORQ = reinterpret_cast<const float*>(pb + S::pORQ);
+    const float* pBETA = reinterpret_cast<const float*>(pb + S::pBETA);
     const int g = lane / 16, l16 = lane % 16;
-    const int oKK = (G_SKK + 3 * sw) * C, oORQ = (G_SORQ + 3 * sw) * C, oDRK = (G_SDRK + 3 * sw) * C;
-
-    // operand fragments first (chain order: B/A partner is S from registers)
-    bf16x8 kfr[4][KS], qfr[4][KS];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kfr[t][ks] = frag_chain(sK + (16 * t + l16) * S::KSTR, 32 * ks, g);
-            qfr[t][ks] = frag_chain(sQ + (16 * t + l16) * S::KSTR, 32 * ks, g);
-        }
-
-    // decay factors of this chunk (lane = token)
-    {
-        const float gam = wave_scan(sG[G_RAW * C + lane], lane);
-        const float gl = __shfl(gam, C - 1);
-        const float Gi = __expf(gam);
-        sG[oKK + lane] = sG[G_BETA * C + lane] * Gi * sG[G_RK * C + lane];
-        sG[oORQ + lane] = Gi * sG[G_RQ * C + lane];
-        sG[oDRK + lane] = __expf(gl - gam) * sG[G_RK * C + lane];
-        st.gc = __expf(gl);
-    }
 
     bf16x8 sb[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) sb[ks] = pack_chain(st.S[2 * ks], st.S[2 * ks + 1]);
-
     fx4 ks_acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -534,23 +553,32 @@ __device__ void state_phase1(StateRegs<DK>& st, unsigned char* sm, int lane, int
         st.ot[t] = zero4();
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 kfr[4], qfr[4];
+        const int o0 = off_chain<DK>(ks, 0, g, l16), o1 = off_chain<DK>(ks, 1, g, l16);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            ks_acc[t] = mfma(kfr[t][ks], sb[ks], ks_acc[t]);   // K S^T  (M = token, N = c)
-            st.ot[t] = mfma(sb[ks], qfr[t][ks], st.ot[t]);     // S Q^T  (M = c, N = token)
+            kfr[t] = __builtin_shufflevector(lds_at<bf16x4>(K, o0 + 16 * t * DK), lds_at<bf16x4>(K, o1 + 16 * t * DK),
+                                             0, 1, 2, 3, 4, 5, 6, 7);
+            qfr[t] = __builtin_shufflevector(lds_at<bf16x4>(Q, o0 + 16 * t * DK), lds_at<bf16x4>(Q, o1 + 16 * t * DK),
+                                             0, 1, 2, 3, 4, 5, 6, 7);
         }
-
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            ks_acc[t] = mfma(kfr[t], sb[ks], ks_acc[t]);  // K S^T  (M = token, N = c)
+            st.ot[t] = mfma(sb[ks], qfr[t], st.ot[t]);    // S Q^T  (M = c, N = token)
+        }
+    }
     fx4 x[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int m0 = 16 * mt + 4 * g;
-        const fx4 bm = *reinterpret_cast<const fx4*>(sG + G_BETA * C + m0);
-        const fx4 kk = *reinterpret_cast<const fx4*>(sG + oKK + m0);
-        const bf16x4 vv = *reinterpret_cast<const bf16x4*>(sVt + (cbase + l16) * TSTR + m0);
+        const fx4 bm = *reinterpret_cast<const fx4*>(pBETA + m0);
+        const fx4 kk = *reinterpret_cast<const fx4*>(pKK + m0);
+        const bf16x4 vv = str4<BV>(V, m0, cbase, l16);  // V[m0 .. +3][cbase + l16]
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[mt][e] = bm[e] * (float)vv[e] - kk[e] * ks_acc[mt][e];
-        const float orq = sG[oORQ + 16 * mt + l16];
+        const float orq = pORQ[16 * mt + l16];
 #pragma unroll
         for (int e = 0; e < 4; ++e) st.ot[mt][e] *= orq;
     }
@@ -558,71 +586,33 @@ __device__ void state_phase1(StateRegs<DK>& st, unsigned char* sm, int lane, int
     st.xb[1] = pack_chain(x[2], x[3]);
 }
 
-// Phase 4 (after T is ready): U = T X, O += Pm U (stored), S <- Gamma_C S + U^T D K.
+// Part 2: U = T X, O += Pm U (stored), S <- Gamma_C S + (D U)^T K.
 template <int DK>
-__device__ void state_phase4(const Params<DK>& p, StateRegs<DK>& st, unsigned char* sm, int lane, int sw, int cbase,
-                             long t0, int len, int h, int vb) {
+__device__ void state_part2(const Params<DK>& p, StateRegs<DK>& st, const unsigned char* raw, const unsigned char* pb,
+                            int lane, int cbase, long t0, int len, int h, int vb) {
     using S = Smem<DK>;
     constexpr int DT = DK / 16;
-    const __bf16* sKt = reinterpret_cast<const __bf16*>(sm + S::oKt);
-    const __bf16* sT = reinterpret_cast<const __bf16*>(sm + S::oT);
-    const __bf16* sPm = reinterpret_cast<const __bf16*>(sm + S::oPm);
-    const float* sG = reinterpret_cast<const float*>(sm + S::oG);
+    const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
+    const __bf16* Tt = reinterpret_cast<const __bf16*>(pb + S::pT);
+    const __bf16* Pm = reinterpret_cast<const __bf16*>(pb + S::pPm);
+    const float* pDRK = reinterpret_cast<const float*>(pb + S::pDRK);
+    const float gc = *reinterpret_cast<const float*>(pb + S::pGC);
     const int g = lane / 16, l16 = lane % 16;
-    const int oDRK = (G_SDRK + 3 * sw) * C;
 
-    // T and Pm fragments (k-step 1 only for row tiles 2, 3: both are lower triangular)
-    bf16x8 tf[4][2], pf[4][2];
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-            if (s2 == 0 || it >= 2) {
-                tf[it][s2] = frag_chain(sT + (16 * it + l16) * TSTR, 32 * s2, g);
-                pf[it][s2] = frag_chain(sPm + (16 * it + l16) * TSTR, 32 * s2, g);
-            }
-    bf16x8 kt[DT][2];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) kt[dt][s2] = frag_chain(sKt + (16 * dt + l16) * TSTR, 32 * s2, g);
-
+    // U = T X (T lower triangular: i-tiles 0, 1 need only m < 32)
     fx4 u[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) u[it] = mfma(tf[it][0], st.xb[0], zero4());
+    for (int it = 0; it < 4; ++it) u[it] = mfma(frag_tr_chain(Tt, TSTR, 0, 16 * it, g, l16), st.xb[0], zero4());
 #pragma unroll
-    for (int it = 2; it < 4; ++it) u[it] = mfma(tf[it][1], st.xb[1], u[it]);
-    bf16x8 ub[2];
-    ub[0] = pack_chain(u[0], u[1]);
-    ub[1] = pack_chain(u[2], u[3]);
+    for (int it = 2; it < 4; ++it) u[it] = mfma(frag_tr_chain(Tt, TSTR, 32, 16 * it, g, l16), st.xb[1], u[it]);
+    const bf16x8 ub0 = pack_chain(u[0], u[1]), ub1 = pack_chain(u[2], u[3]);
 
-    // U^T scaled by exp(gamma_C - gamma) rk for the state update
-    fx4 ut[4];
+    // O^T += U^T Pm^T, store O
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        const fx4 d = *reinterpret_cast<const fx4*>(sG + oDRK + 16 * it + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ut[it][e] = u[it][e] * d[e];
+        st.ot[it] = mfma(ub0, frag_chain(Pm + (16 * it + l16) * TSTR, 0, g), st.ot[it]);
+        if (it >= 2) st.ot[it] = mfma(ub1, frag_chain(Pm + (16 * it + l16) * TSTR, 32, g), st.ot[it]);
     }
-    bf16x8 utb[2];
-    utb[0] = pack_chain(ut[0], ut[1]);
-    utb[1] = pack_chain(ut[2], ut[3]);
-
-#pragma unroll
-    for (int it = 0; it < 4; ++it) st.ot[it] = mfma(ub[0], pf[it][0], st.ot[it]);
-#pragma unroll
-    for (int it = 2; it < 4; ++it) st.ot[it] = mfma(ub[1], pf[it][1], st.ot[it]);
-
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st.S[dt][e] *= st.gc;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][s2], utb[s2], st.S[dt]);
-
-    // store O (lane: token i = 16 it + l16, state rows cbase + 4g .. +3)
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int i = 16 * it + l16;
@@ -632,6 +622,29 @@ __device__ void state_phase4(const Params<DK>& p, StateRegs<DK>& st, unsigned ch
             for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e]);
             *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
         }
+    }
+
+    // S^T = Gamma_C S^T + K^T (D U): A = K^T via transposing reads of row-major K
+    fx4 ut[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const fx4 d = *reinterpret_cast<const fx4*>(pDRK + 16 * it + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ut[it][e] = u[it][e] * d[e];
+    }
+    const bf16x8 utb0 = pack_chain(ut[0], ut[1]), utb1 = pack_chain(ut[2], ut[3]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        fx4 acc = st.S[dt];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= gc;
+        const int o = off_trk<DK>(dt, g, l16);
+        const bf16x8 a0 = __builtin_shufflevector(tr_read(K + o), tr_read(K + o + 16 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 a1 = __builtin_shufflevector(tr_read(K + o + 32 * DK), tr_read(K + o + 48 * DK), 0, 1, 2, 3, 4, 5,
+                                                  6, 7);
+        acc = mfma(a0, utb0, acc);
+        acc = mfma(a1, utb1, acc);
+        st.S[dt] = acc;
     }
 }
 
@@ -643,6 +656,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
+    const int g = lane / 16, l16 = lane % 16;
 
     // XCD-aware order: the nv row-block workgroups of one (n, h) share blockIdx mod 8 (same XCD,
     // same L2) when the pair count allows it.
@@ -662,34 +676,25 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
         bos = p.cu[n];
         eos = p.cu[n + 1];
     } else {
-        const long L = p.T_tot / p.N;
-        bos = (long)n * L;
-        eos = bos + L;
+        const long Ls = p.T_tot / p.N;
+        bos = (long)n * Ls;
+        eos = bos + Ls;
     }
     const int nchunks = (int)((eos - bos + C - 1) / C);
 
-    // The strict-upper off-diagonal blocks of T (bf16 and both fp32 copies) and the masked-out
-    // tiles of Pm are read as zeros but never written: clear them once.
-    {
-        __bf16* sT = reinterpret_cast<__bf16*>(sm + S::oT);
-        __bf16* sPm = reinterpret_cast<__bf16*>(sm + S::oPm);
-        float* sTf = reinterpret_cast<float*>(sm + S::oTf);
-        float* sTt = reinterpret_cast<float*>(sm + S::oTt);
-        for (int i = tid; i < C * TSTR; i += 256) {
-            sT[i] = (__bf16)0.f;
-            sPm[i] = (__bf16)0.f;
-        }
-        for (int i = tid; i < C * LSTR; i += 256) {
-            sTf[i] = 0.f;
-            sTt[i] = 0.f;
-        }
+    // T^T blocks above the block diagonal and Pm tiles above the diagonal are read as zeros but
+    // never written: clear both prep buffers once.
+    for (int i = tid; i < C * TSTR; i += 256) {
+        reinterpret_cast<__bf16*>(sm + S::prep(0) + S::pT)[i] = (__bf16)0.f;
+        reinterpret_cast<__bf16*>(sm + S::prep(1) + S::pT)[i] = (__bf16)0.f;
+        reinterpret_cast<__bf16*>(sm + S::prep(0) + S::pPm)[i] = (__bf16)0.f;
+        reinterpret_cast<__bf16*>(sm + S::prep(1) + S::pPm)[i] = (__bf16)0.f;
     }
 
-    StateRegs<DK> st;
     const bool is_state = wid < 2;
     const int cbase = 16 * wid;
-    const int g = lane / 16, l16 = lane % 16;
-    const size_t srow0 = ((size_t)pair * p.dv + vb * BV + cbase + l16) * DK;  // state row c of this lane
+    StateRegs<DK> st;
+    const size_t srow0 = ((size_t)pair * p.dv + vb * BV + cbase + l16) * DK;  // state row of this lane
     if (is_state) {
 #pragma unroll
         for (int dt = 0; dt < StateRegs<DK>::DT; ++dt) {
@@ -701,38 +706,49 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
             }
         }
     }
+    if (nchunks > 0) {
+        const int len0 = (int)min((long)C, eos - bos);
+        dma_chunk<DK>(p, sm, S::raw(0), bos, len0, h, vb, wid, lane);
+        wait_loads();
+        zero_tail<DK>(sm + S::raw(0), len0, wid, lane);
+    }
+    __syncthreads();
 
-    ChunkRegs<DK> R;
-    if (nchunks > 0) fetch_chunk<DK>(p, R, bos, (int)min((long)C, eos - bos), h, vb, tid);
-
-    for (int c = 0; c < nchunks; ++c) {
-        const long t0 = bos + (long)c * C;
-        const int len = (int)min((long)C, eos - t0);
-        store_chunk<DK>(R, sm, len, p.l2norm, tid);
-        if (c + 1 < nchunks) {
-            const long t1 = t0 + C;
-            fetch_chunk<DK>(p, R, t1, (int)min((long)C, eos - t1), h, vb, tid);
-        }
+    // iteration k: prep on chunk k, state on chunk k-1, loads of chunk k+1
+    for (int k = 0; k <= nchunks; ++k) {
+        unsigned char* rawk = sm + S::raw(k);
+        unsigned char* rawp = sm + S::raw(k + 2);  // chunk k-1
+        unsigned char* rawn = sm + S::raw(k + 1);  // chunk k+1
+        unsigned char* pbk = sm + S::prep(k);
+        unsigned char* pbp = sm + S::prep(k + 1);  // chunk k-1
+        const bool prep_on = k < nchunks;
+        const bool state_on = k > 0;
+        const bool next_on = k + 1 < nchunks;
+        const long tk = bos + (long)k * C;
+        const int lenk = prep_on ? (int)min((long)C, eos - tk) : 0;
+        const int lenp = state_on ? (int)min((long)C, eos - (tk - C)) : 0;
+        const int lenn = next_on ? (int)min((long)C, eos - (tk + C)) : 0;
+        // ---- A
+        if (next_on) dma_chunk<DK>(p, sm, S::raw(k + 1), tk + C, lenn, h, vb, wid, lane);
+        if (wid == 2 && prep_on) prep_L<DK>(rawk, pbk, sm, lane, lenk, p.l2norm);
+        if (wid == 3 && prep_on) prep_P<DK>(rawk, pbk, sm, lane, lenk, p.l2norm);
+        if (is_state && state_on) state_part1<DK>(st, rawp, pbp, lane, cbase);
         __syncthreads();
-        if (wid == 2) prep_gram_L<DK>(sm, lane);
-        if (wid == 3) prep_gram_P<DK>(sm, lane);
-        if (is_state) {
-            transpose_k<DK>(sm, lane, wid);
-            state_phase1<DK>(st, sm, lane, wid, cbase);
+        // ---- B
+        const __bf16* sLt = reinterpret_cast<const __bf16*>(sm + S::L);
+        __bf16* Tt = reinterpret_cast<__bf16*>(pbk + S::pT);
+        if (wid >= 2 && prep_on) {
+            solve_diag(sLt, Tt, wid == 2 ? 0 : 2, lane);
+            solve_level1(sLt, Tt, wid == 2 ? 0 : 2, lane);
         }
+        if (is_state && state_on) state_part2<DK>(p, st, rawp, pbp, lane, cbase, tk - C, lenp, h, vb);
         __syncthreads();
-        if (wid == 2) {
-            solve_diag(sm, 0, lane, S::oL, S::oTf, S::oTt, S::oT);
-            solve_level1(sm, 0, lane, S::oL, S::oTf, S::oTt, S::oT);
+        // ---- C
+        if (wid >= 2 && prep_on) solve_level2(sLt, Tt, wid - 2, lane);
+        if (next_on) {
+            wait_loads();
+            zero_tail<DK>(rawn, lenn, wid, lane);
         }
-        if (wid == 3) {
-            solve_diag(sm, 2, lane, S::oL, S::oTf, S::oTt, S::oT);
-            solve_level1(sm, 2, lane, S::oL, S::oTf, S::oTt, S::oT);
-        }
-        __syncthreads();
-        if (wid >= 2) solve_level2(sm, wid - 2, lane, S::oL, S::oTf, S::oTt, S::oT);
-        __syncthreads();
-        if (is_state) state_phase4<DK>(p, st, sm, lane, wid, cbase, t0, len, h, vb);
         __syncthreads();
     }
 
@@ -766,8 +782,13 @@ hipError_t launch_t(const ChunkArgs& a) {
     p.scale = a.scale;
     p.l2norm = a.l2norm;
     const int smem = Smem<DK>::bytes;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_bf16_kernel<DK>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    int dev = 0, lds_max = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return e;
+    if (lds_max < smem) return hipErrorInvalidConfiguration;  // needs the 160 KiB LDS of gfx950
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_bf16_kernel<DK>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     const int grid = a.N * a.H * p.nv;
     hipLaunchKernelGGL((chunk_bf16_kernel<DK>), dim3(grid), dim3(256), smem, a.stream, p);
