@@ -56,6 +56,9 @@ __device__ __forceinline__ fx4 mfma(bf16x8 a, bf16x8 b, fx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ fx4 zero4() { return fx4{0.f, 0.f, 0.f, 0.f}; }
+// Keep every instruction before this point (typically a batch of LDS operand reads) ahead of
+// everything after it: with one wavefront per SIMD the reads must be in flight early.
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Swizzled row-major tile of R rows x W bf16 (W/8 16-byte slots per row): element (r, c) lives at
 // r*W + 8*((c/8) ^ (r % (W/8))) + c%8.
@@ -205,32 +208,60 @@ struct Params {
 // so each lane fetches the global part that the swizzle places in its slot.  Wave w loads rows
 // [16w, 16w + 16) of K, Q and V; wave 0 loads g, wave 1 beta.  Rows past the tail re-read the
 // last valid row and are cleared by zero_tail once the loads have landed.
+// One global_load_lds instruction (scalar-base form): lane l copies 16 (or 4) bytes from
+// base + voff(l) to LDS byte address lds + 16 l (4 l).  base and lds are wave-uniform; voff is a
+// per-lane byte offset below 4 GiB (the base already points at the chunk's first token).  Issued
+// through asm so that the compiler does not make every later LDS read of this wave wait for it:
+// the issuing wave waits explicitly (wait_loads) before the data is published.
+__device__ __forceinline__ void dma16(const void* base, unsigned voff, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, unsigned voff, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
+    return __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(void*)p)));
+}
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+    const uintptr_t u = reinterpret_cast<uintptr_t>(p);
+    const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u));
+    const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(u >> 32));
+    return reinterpret_cast<const T*>((static_cast<uintptr_t>(hi) << 32) | lo);
+}
+
 template <int DK>
 __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned char* sm, int rawoff, long t0, int len, int h,
                                           int vb, int wid, int lane) {
     using S = Smem<DK>;
     constexpr int PPR = DK / 8;       // 16-byte slots per K/Q row
     constexpr int RPI = 64 / PPR;     // rows per 1 KB instruction
-    const size_t rowq = (size_t)p.H * DK;
+    const size_t tok0 = (size_t)t0 * p.H + h;
+    const __bf16* kb = uniform_ptr(p.k + tok0 * DK);
+    const __bf16* qb = uniform_ptr(p.q + tok0 * DK);
+    const unsigned rowq = (unsigned)(p.H * DK) * 2u;  // bytes between tokens
 #pragma unroll
     for (int j = 0; j < 16 / RPI; ++j) {
         const int row0 = 16 * wid + RPI * j;
         const int row = row0 + lane / PPR, slot = lane % PPR;
         const int part = slot ^ (row % PPR);
-        const size_t off = (size_t)(t0 + min(row, len - 1)) * rowq + (size_t)h * DK + 8 * part;
+        const unsigned voff = (unsigned)min(row, len - 1) * rowq + 16u * part;
         const int lo = rawoff + row0 * DK * 2;
-        __builtin_amdgcn_global_load_lds(p.k + off, (lds_void*)(sm + lo + S::rK), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(p.q + off, (lds_void*)(sm + lo + S::rQ), 16, 0, 0);
+        dma16(kb, voff, lds_addr(sm + lo + S::rK));
+        dma16(qb, voff, lds_addr(sm + lo + S::rQ));
     }
     {
         const int row = 16 * wid + lane / 4, slot = lane % 4, part = slot ^ (row % 4);
-        const size_t off = ((size_t)(t0 + min(row, len - 1)) * p.H + h) * p.dv + vb * BV + 8 * part;
-        __builtin_amdgcn_global_load_lds(p.v + off, (lds_void*)(sm + rawoff + S::rV + 16 * wid * BV * 2), 16, 0, 0);
+        const __bf16* vbase = uniform_ptr(p.v + tok0 * p.dv + vb * BV);
+        const unsigned voff = (unsigned)min(row, len - 1) * (unsigned)(p.H * p.dv) * 2u + 16u * part;
+        dma16(vbase, voff, lds_addr(sm + rawoff + S::rV + 16 * wid * BV * 2));
     }
     if (wid < 2) {
-        const size_t off = (size_t)(t0 + min(lane, len - 1)) * p.H + h;
-        __builtin_amdgcn_global_load_lds(wid == 0 ? p.g + off : p.beta + off,
-                                         (lds_void*)(sm + rawoff + (wid == 0 ? S::rG : S::rB)), 4, 0, 0);
+        const float* gbase = uniform_ptr((wid == 0 ? p.g : p.beta) + tok0);
+        const unsigned voff = (unsigned)min(lane, len - 1) * (unsigned)p.H * 4u;
+        dma4(gbase, voff, lds_addr(sm + rawoff + (wid == 0 ? S::rG : S::rB)));
     }
 }
 
@@ -258,7 +289,18 @@ __device__ __forceinline__ void zero_tail(unsigned char* raw, int len, int wid, 
 }
 
 __device__ __forceinline__ void wait_loads() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's global->LDS loads have landed
+}
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS accesses (lgkmcnt(0)) but,
+// unlike __syncthreads(), not for its global loads and stores, so the chunk prefetch and the
+// output stores stay in flight across it.  The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // ------------------------------------------------------------------------------------------
@@ -293,7 +335,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // b_j = gamma_j log2e - log2(rk_j); the decay part of the exponent is never positive, and a zero
 // beta or norm gives exp2(-inf) = 0.
 template <int DK>
-__device__ void prep_L(const unsigned char* raw, unsigned char* pb, unsigned char* sm, int lane, int len,
+__device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* pb, unsigned char* sm, int lane, int len,
                        int l2norm) {
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
@@ -363,7 +405,7 @@ __device__ void prep_L(const unsigned char* raw, unsigned char* pb, unsigned cha
 // as D = K Q^T so that a lane holds 4 consecutive m of row i (bf16, row-major).  Mask in the log2
 // domain: Pm_im = exp2(a_i - b_m) P_im, a_i = gamma_i log2e + log2(rq_i), b_m = gamma_m log2e - log2(rk_m).
 template <int DK>
-__device__ void prep_P(const unsigned char* raw, unsigned char* pb, unsigned char* sm, int lane, int len,
+__device__ __forceinline__ void prep_P(const unsigned char* raw, unsigned char* pb, unsigned char* sm, int lane, int len,
                        int l2norm) {
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
@@ -434,7 +476,7 @@ __device__ void prep_P(const unsigned char* raw, unsigned char* pb, unsigned cha
 // it).  Column m of the block is row m of L^T: read once with 16-byte loads.  The right-looking
 // update keeps one FMA on the critical path per step.  Writes the blocks of T^T (bf16; column j
 // of T = row j of T^T).
-__device__ void solve_diag(const __bf16* sLt, __bf16* Tt, int b0, int lane) {
+__device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, int b0, int lane) {
     const int b = b0 + (lane / 16) % 2, j = lane % 16, base = 16 * b;
     bf16x8 Lc[16][2];
 #pragma unroll
@@ -466,7 +508,7 @@ __device__ void solve_diag(const __bf16* sLt, __bf16* Tt, int b0, int lane) {
 
 // Solve level 1: T_{b+1,b} = -T_{b+1,b+1} (L_{b+1,b} T_{b,b}) for the 16x16 block pair (b, b+1).
 // bf16 operands (K = 16 real, padded to 32 with zeros).
-__device__ void solve_level1(const __bf16* sLt, __bf16* Tt, int b, int lane) {
+__device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, int b, int lane) {
     const int g = lane / 16, l16 = lane % 16;
     const int r0 = 16 * (b + 1), c0 = 16 * b;
     const int gg = g & 1;
@@ -495,7 +537,7 @@ __device__ void solve_level1(const __bf16* sLt, __bf16* Tt, int b, int lane) {
 
 // Solve level 2: columns [16 half, 16 half + 16) of T_BA = -T_BB (L_BA T_AA), 32x32 blocks
 // A = rows 0..31, B = rows 32..63.
-__device__ void solve_level2(const __bf16* sLt, __bf16* Tt, int half, int lane) {
+__device__ __forceinline__ void solve_level2(const __bf16* sLt, __bf16* Tt, int half, int lane) {
     const int g = lane / 16, l16 = lane % 16;
     const int jc = 16 * half + l16;
     // B operand: T_AA[8g .. +7][jc] = T^T row jc
@@ -532,7 +574,7 @@ struct StateRegs {
 
 // Part 1: K S^T, S Q^T (scaled by Gamma rq), X = beta V - beta Gamma rk K S^T.
 template <int DK>
-__device__ void state_part1(StateRegs<DK>& st, const unsigned char* raw, const unsigned char* pb, int lane, int cbase) {
+__device__ __forceinline__ void state_part1(StateRegs<DK>& st, const unsigned char* raw, const unsigned char* pb, int lane, int cbase) {
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
@@ -546,6 +588,19 @@ __device__ void state_part1(StateRegs<DK>& st, const unsigned char* raw, const u
     bf16x8 sb[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) sb[ks] = pack_chain(st.S[2 * ks], st.S[2 * ks + 1]);
+    bf16x8 kfr[KS][4], qfr[KS][4];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int o0 = off_chain<DK>(ks, 0, g, l16), o1 = off_chain<DK>(ks, 1, g, l16);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            kfr[ks][t] = __builtin_shufflevector(lds_at<bf16x4>(K, o0 + 16 * t * DK),
+                                                 lds_at<bf16x4>(K, o1 + 16 * t * DK), 0, 1, 2, 3, 4, 5, 6, 7);
+            qfr[ks][t] = __builtin_shufflevector(lds_at<bf16x4>(Q, o0 + 16 * t * DK),
+                                                 lds_at<bf16x4>(Q, o1 + 16 * t * DK), 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    }
+    issue_fence();
     fx4 ks_acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -554,19 +609,10 @@ __device__ void state_part1(StateRegs<DK>& st, const unsigned char* raw, const u
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 kfr[4], qfr[4];
-        const int o0 = off_chain<DK>(ks, 0, g, l16), o1 = off_chain<DK>(ks, 1, g, l16);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            kfr[t] = __builtin_shufflevector(lds_at<bf16x4>(K, o0 + 16 * t * DK), lds_at<bf16x4>(K, o1 + 16 * t * DK),
-                                             0, 1, 2, 3, 4, 5, 6, 7);
-            qfr[t] = __builtin_shufflevector(lds_at<bf16x4>(Q, o0 + 16 * t * DK), lds_at<bf16x4>(Q, o1 + 16 * t * DK),
-                                             0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            ks_acc[t] = mfma(kfr[t], sb[ks], ks_acc[t]);  // K S^T  (M = token, N = c)
-            st.ot[t] = mfma(sb[ks], qfr[t], st.ot[t]);    // S Q^T  (M = c, N = token)
+            ks_acc[t] = mfma(kfr[ks][t], sb[ks], ks_acc[t]);  // K S^T  (M = token, N = c)
+            st.ot[t] = mfma(sb[ks], qfr[ks][t], st.ot[t]);    // S Q^T  (M = c, N = token)
         }
     }
     fx4 x[4];
@@ -588,7 +634,7 @@ __device__ void state_part1(StateRegs<DK>& st, const unsigned char* raw, const u
 
 // Part 2: U = T X, O += Pm U (stored), S <- Gamma_C S + (D U)^T K.
 template <int DK>
-__device__ void state_part2(const Params<DK>& p, StateRegs<DK>& st, const unsigned char* raw, const unsigned char* pb,
+__device__ __forceinline__ void state_part2(const Params<DK>& p, StateRegs<DK>& st, const unsigned char* raw, const unsigned char* pb,
                             int lane, int cbase, long t0, int len, int h, int vb) {
     using S = Smem<DK>;
     constexpr int DT = DK / 16;
@@ -599,19 +645,58 @@ __device__ void state_part2(const Params<DK>& p, StateRegs<DK>& st, const unsign
     const float gc = *reinterpret_cast<const float*>(pb + S::pGC);
     const int g = lane / 16, l16 = lane % 16;
 
+    // operand fragments first: T rows (transposing reads of T^T), Pm rows, K^T (transposing reads of K)
+    bf16x8 tf[4][2], pf[4][2], kt[DT][2];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+            if (s2 == 0 || it >= 2) {
+                tf[it][s2] = frag_tr_chain(Tt, TSTR, 32 * s2, 16 * it, g, l16);
+                pf[it][s2] = frag_chain(Pm + (16 * it + l16) * TSTR, 32 * s2, g);
+            }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const int o = off_trk<DK>(dt, g, l16);
+        kt[dt][0] = __builtin_shufflevector(tr_read(K + o), tr_read(K + o + 16 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
+        kt[dt][1] = __builtin_shufflevector(tr_read(K + o + 32 * DK), tr_read(K + o + 48 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    const fx4 dr0 = *reinterpret_cast<const fx4*>(pDRK + 4 * g), dr1 = *reinterpret_cast<const fx4*>(pDRK + 16 + 4 * g);
+    const fx4 dr2 = *reinterpret_cast<const fx4*>(pDRK + 32 + 4 * g), dr3 = *reinterpret_cast<const fx4*>(pDRK + 48 + 4 * g);
+    issue_fence();
+
     // U = T X (T lower triangular: i-tiles 0, 1 need only m < 32)
     fx4 u[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) u[it] = mfma(frag_tr_chain(Tt, TSTR, 0, 16 * it, g, l16), st.xb[0], zero4());
+    for (int it = 0; it < 4; ++it) u[it] = mfma(tf[it][0], st.xb[0], zero4());
 #pragma unroll
-    for (int it = 2; it < 4; ++it) u[it] = mfma(frag_tr_chain(Tt, TSTR, 32, 16 * it, g, l16), st.xb[1], u[it]);
+    for (int it = 2; it < 4; ++it) u[it] = mfma(tf[it][1], st.xb[1], u[it]);
     const bf16x8 ub0 = pack_chain(u[0], u[1]), ub1 = pack_chain(u[2], u[3]);
 
-    // O^T += U^T Pm^T, store O
+    // U scaled by exp(gamma_C - gamma) rk for the state update
+    const fx4 drk[4] = {dr0, dr1, dr2, dr3};
+    fx4 ut[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ut[it][e] = u[it][e] * drk[it][e];
+    const bf16x8 utb0 = pack_chain(ut[0], ut[1]), utb1 = pack_chain(ut[2], ut[3]);
+
+    // S^T = Gamma_C S^T + K^T (D U)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.S[dt][e] *= gc;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][s2], s2 ? utb1 : utb0, st.S[dt]);
+
+    // O^T += U^T Pm^T, store O (lane: token i = 16 it + l16, state rows cbase + 4g .. +3)
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        st.ot[it] = mfma(ub0, frag_chain(Pm + (16 * it + l16) * TSTR, 0, g), st.ot[it]);
-        if (it >= 2) st.ot[it] = mfma(ub1, frag_chain(Pm + (16 * it + l16) * TSTR, 32, g), st.ot[it]);
+        st.ot[it] = mfma(ub0, pf[it][0], st.ot[it]);
+        if (it >= 2) st.ot[it] = mfma(ub1, pf[it][1], st.ot[it]);
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -622,29 +707,6 @@ __device__ void state_part2(const Params<DK>& p, StateRegs<DK>& st, const unsign
             for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e]);
             *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
         }
-    }
-
-    // S^T = Gamma_C S^T + K^T (D U): A = K^T via transposing reads of row-major K
-    fx4 ut[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const fx4 d = *reinterpret_cast<const fx4*>(pDRK + 16 * it + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ut[it][e] = u[it][e] * d[e];
-    }
-    const bf16x8 utb0 = pack_chain(ut[0], ut[1]), utb1 = pack_chain(ut[2], ut[3]);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        fx4 acc = st.S[dt];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] *= gc;
-        const int o = off_trk<DK>(dt, g, l16);
-        const bf16x8 a0 = __builtin_shufflevector(tr_read(K + o), tr_read(K + o + 16 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 a1 = __builtin_shufflevector(tr_read(K + o + 32 * DK), tr_read(K + o + 48 * DK), 0, 1, 2, 3, 4, 5,
-                                                  6, 7);
-        acc = mfma(a0, utb0, acc);
-        acc = mfma(a1, utb1, acc);
-        st.S[dt] = acc;
     }
 }
 
@@ -712,7 +774,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
         wait_loads();
         zero_tail<DK>(sm + S::raw(0), len0, wid, lane);
     }
-    __syncthreads();
+    lds_barrier();
 
     // iteration k: prep on chunk k, state on chunk k-1, loads of chunk k+1
     for (int k = 0; k <= nchunks; ++k) {
@@ -729,11 +791,11 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
         const int lenp = state_on ? (int)min((long)C, eos - (tk - C)) : 0;
         const int lenn = next_on ? (int)min((long)C, eos - (tk + C)) : 0;
         // ---- A
-        if (next_on) dma_chunk<DK>(p, sm, S::raw(k + 1), tk + C, lenn, h, vb, wid, lane);
         if (wid == 2 && prep_on) prep_L<DK>(rawk, pbk, sm, lane, lenk, p.l2norm);
         if (wid == 3 && prep_on) prep_P<DK>(rawk, pbk, sm, lane, lenk, p.l2norm);
         if (is_state && state_on) state_part1<DK>(st, rawp, pbp, lane, cbase);
-        __syncthreads();
+        if (next_on) dma_chunk<DK>(p, sm, S::raw(k + 1), tk + C, lenn, h, vb, wid, lane);
+        lds_barrier();
         // ---- B
         const __bf16* sLt = reinterpret_cast<const __bf16*>(sm + S::L);
         __bf16* Tt = reinterpret_cast<__bf16*>(pbk + S::pT);
@@ -742,14 +804,14 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
             solve_level1(sLt, Tt, wid == 2 ? 0 : 2, lane);
         }
         if (is_state && state_on) state_part2<DK>(p, st, rawp, pbp, lane, cbase, tk - C, lenp, h, vb);
-        __syncthreads();
+        lds_barrier();
         // ---- C
         if (wid >= 2 && prep_on) solve_level2(sLt, Tt, wid - 2, lane);
         if (next_on) {
             wait_loads();
             zero_tail<DK>(rawn, lenn, wid, lane);
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     if (is_state && p.sfin) {
