@@ -52,6 +52,9 @@ extern "C" {
 
 /* flags */
 #define GDN_QK_L2NORM 1u       /* L2-normalise q and k per (token, head) over dk, eps = 1e-6 */
+/* Segments per sequence for gdn_chunk_fwd (bits 8..15; 0 = chosen automatically).  See
+ * "Long sequences" under gdn_chunk_fwd.  Not accepted by gdn_recurrent_step. */
+#define GDN_SEGMENTS(n) ((((unsigned)(n)) & 0xFFu) << 8)
 
 /*
  * gdn_chunk_fwd -- chunked prefill over packed variable-length sequences.
@@ -82,21 +85,32 @@ extern "C" {
  *  o           [T_tot, H, dv]  dtype   output; must not alias any input
  *  final_state [N, H, dv, dk] fp32     last state per (sequence, head), or NULL = not written.
  *                                      May alias initial_state exactly (same pointer).
- *  workspace, workspace_bytes          device scratch for the long-sequence path.  If
+ *  workspace, workspace_bytes          device scratch for the long-sequence path (below).  If
  *                                      *workspace_bytes is smaller than the size this call needs,
  *                                      the call sets *workspace_bytes to that size and returns
  *                                      GDN_ERR_WORKSPACE without launching (a NULL workspace with
  *                                      *workspace_bytes = 0 is the size query).  workspace_bytes
- *                                      may be NULL only when the call needs no workspace.
- *                                      Needed only when cu_seqlens is NULL and (N*H) is small
- *                                      against T_tot; see gdn_chunk_workspace_size.
+ *                                      may be NULL only when the call needs no workspace.  The
+ *                                      workspace must not overlap any other buffer; its contents
+ *                                      on entry are ignored and on return are unspecified.
  *  N, T_tot, H, dk, dv                 sizes; dk, dv in {32, 64, 128}; N >= 1, T_tot >= 0, H >= 1
  *  dtype       GDN_F32 or GDN_BF16     (fp32 path: exact fp32 arithmetic throughout; bf16 path:
  *                                      bf16 MFMA operands, fp32 accumulation, fp32 state)
  *  chunk       64                      chunk length; other values -> GDN_ERR_UNSUPPORTED
  *  scale       output scale (1.0 = o_t = S_t q_t)
- *  flags       GDN_QK_L2NORM or 0
+ *  flags       GDN_QK_L2NORM, optionally | GDN_SEGMENTS(n)
  *  hip_stream  hipStream_t to launch on
+ *
+ * Long sequences (bf16 path without conv).  Each sequence is cut into P segments of whole chunks
+ * that run in parallel; the exact affine map of a segment, S_out = S_in A_p + B_p, joins them:
+ * the segments run from a zero state (B_p and o), then as transitions (A_p: identity in, zero
+ * values), a P-step combine gives the true entering states, and a last pass adds their
+ * contribution to o (linear in the state).  A transition or a correction stops once the bound
+ * exp(sum of g since the segment start) on its norm is <= 2^-40 (the bound holds with
+ * GDN_QK_L2NORM and 0 <= beta <= 2; otherwise nothing stops early).  o in the first chunk(s) of
+ * a segment is thus rounded to dtype twice.  P = 1 is the plain single pass.  With
+ * GDN_SEGMENTS(0), P is chosen so that (N * P * H * dv/32) workgroups cover the current device's
+ * compute units, with at least 16 chunks per segment.
  */
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   const float* initial_state, const int32_t* cu_seqlens, const float* conv_w,
@@ -105,12 +119,14 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   unsigned flags, void* hip_stream);
 
 /*
- * gdn_chunk_workspace_size -- the workspace gdn_chunk_fwd needs for these sizes (0 when the
- * call runs without one).  Pure host function; returns GDN_OK and sets *bytes, or an error code
- * for arguments gdn_chunk_fwd would reject.
+ * gdn_chunk_workspace_size -- the workspace gdn_chunk_fwd needs for these sizes, flags and
+ * (nonzero = present) cu_seqlens / conv_w (0 bytes when the call runs as a single pass).  Host
+ * function; with automatic segments it reads the compute-unit count of the current device (256
+ * when no device can be queried), exactly as gdn_chunk_fwd does.  Returns GDN_OK and sets *bytes,
+ * or the error code gdn_chunk_fwd would return for these arguments.
  */
 int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype, int chunk,
-                             int has_cu_seqlens, size_t* bytes);
+                             int has_cu_seqlens, int has_conv, unsigned flags, size_t* bytes);
 
 /*
  * gdn_recurrent_step -- one decode token per sequence, state updated in place.

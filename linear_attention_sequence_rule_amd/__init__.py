@@ -18,11 +18,16 @@ from typing import Optional
 __all__ = ["gdn_chunk_fwd", "gdn_recurrent_step", "gdn_status_string", "gdn_chunk_workspace_size",
            "GdnError", "lib_path", "load_library", "GDN_OK", "GDN_ERR_INVALID_ARG",
            "GDN_ERR_UNSUPPORTED", "GDN_ERR_WORKSPACE", "GDN_ERR_HIP", "GDN_F32", "GDN_BF16",
-           "GDN_QK_L2NORM"]
+           "GDN_QK_L2NORM", "GDN_SEGMENTS"]
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 0, 1, 2, 3, 4
 GDN_F32, GDN_BF16 = 0, 1
 GDN_QK_L2NORM = 1
+
+
+def GDN_SEGMENTS(n: int) -> int:
+    """Flag bits requesting n segments per sequence (0 = automatic)."""
+    return (int(n) & 0xFF) << 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdn.so")
@@ -51,7 +56,7 @@ def load_library():
     lib.gdn_chunk_fwd.restype = I
     lib.gdn_chunk_fwd.argtypes = [P] * 12 + [I] * 7 + [F, U, P]
     lib.gdn_chunk_workspace_size.restype = I
-    lib.gdn_chunk_workspace_size.argtypes = [I] * 8 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_chunk_workspace_size.argtypes = [I] * 9 + [U, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdn_recurrent_step.restype = I
     lib.gdn_recurrent_step.argtypes = [P] * 7 + [I] * 5 + [F, U, P]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -95,10 +100,11 @@ def _check_dev(name, t, dtype=None):
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
-def gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype=GDN_BF16, chunk=64, has_cu_seqlens=False) -> int:
+def gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype=GDN_BF16, chunk=64, has_cu_seqlens=False, has_conv=False,
+                             flags=GDN_QK_L2NORM) -> int:
     n = ctypes.c_size_t(0)
     st = load_library().gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype, chunk, int(bool(has_cu_seqlens)),
-                                                 ctypes.byref(n))
+                                                 int(bool(has_conv)), flags, ctypes.byref(n))
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_workspace_size")
     return int(n.value)
@@ -106,10 +112,12 @@ def gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype=GDN_BF16, chunk=64, has_
 
 def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=None, *, N=None, o=None,
                   final_state=None, output_final_state=True, scale=1.0, l2norm=True, chunk=64, workspace=None,
-                  stream=None):
+                  segments=0, stream=None):
     """Chunked prefill.  q, k [T_tot, H, dk]; v [T_tot, H, dv] (bf16 or fp32); g, beta [T_tot, H] fp32;
     initial_state [N, H, dv, dk] fp32 or None; cu_seqlens [N+1] int32 or None (N equal sequences, N
-    given or 1); conv_w [H*(2dk+dv), 4] fp32 or None.  Returns (o, final_state or None)."""
+    given or 1); conv_w [H*(2dk+dv), 4] fp32 or None; segments per sequence (0 = automatic).
+    A workspace (uint8 device tensor) is allocated here when the call needs one and none large
+    enough is given.  Returns (o, final_state or None)."""
     import torch
     lib = load_library()
     T_tot, H, dk = q.shape
@@ -130,15 +138,15 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=
     _check_dev("o", o, q.dtype)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
+    flags = (GDN_QK_L2NORM if l2norm else 0) | GDN_SEGMENTS(segments)
     ws_bytes = ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size())
-    need = gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dt, chunk, cu_seqlens is not None)
+    need = gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dt, chunk, cu_seqlens is not None, conv_w is not None, flags)
     if need > ws_bytes.value:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = ctypes.c_size_t(need)
     st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
                            _ptr(conv_w), _ptr(o), _ptr(final_state), _ptr(workspace), ctypes.byref(ws_bytes), N,
-                           T_tot, H, dk, dv, dt, chunk, float(scale), GDN_QK_L2NORM if l2norm else 0,
-                           _stream(stream))
+                           T_tot, H, dk, dv, dt, chunk, float(scale), flags, _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_fwd")
     return o, final_state

@@ -20,13 +20,32 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+constexpr unsigned kSegMask = 0xFFu << 8;
+
 int check_common(int H, int dk, int dv, int dtype, float scale, unsigned flags) {
     if (H < 1) return GDN_ERR_INVALID_ARG;
-    if (flags & ~GDN_QK_L2NORM) return GDN_ERR_INVALID_ARG;
+    if (flags & ~(GDN_QK_L2NORM | kSegMask)) return GDN_ERR_INVALID_ARG;
     if (!isfinite(scale)) return GDN_ERR_INVALID_ARG;
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!dim_ok(dk) || !dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
+}
+
+// Segments per sequence for this call (1 = single pass).  A request for more than one segment is
+// honoured on the bf16 path without conv only.
+int segments_for(int N, int T_tot, int H, int dv, int dtype, bool has_conv, unsigned flags, int* P) {
+    const int req = (int)((flags & kSegMask) >> 8);
+    if (dtype != GDN_BF16 || has_conv) {
+        if (req > 1) return GDN_ERR_UNSUPPORTED;
+        *P = 1;
+        return GDN_OK;
+    }
+    *P = gdn::plan_segments(N, T_tot, H, dv, req);
+    return GDN_OK;
+}
+
+size_t workspace_for(int N, int H, int dk, int dv, int P) {
+    return P > 1 ? gdn::seg_layout(N, H, dk, dv, P).bytes : 0;
 }
 
 }  // namespace
@@ -45,14 +64,17 @@ const char* gdn_status_string(int status) {
 }
 
 int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype, int chunk, int has_cu_seqlens,
-                             size_t* bytes) {
+                             int has_conv, unsigned flags, size_t* bytes) {
     if (!bytes) return GDN_ERR_INVALID_ARG;
     if (N < 1 || T_tot < 0) return GDN_ERR_INVALID_ARG;
-    int st = check_common(H, dk, dv, dtype, 1.0f, 0);
+    int st = check_common(H, dk, dv, dtype, 1.0f, flags);
     if (st != GDN_OK) return st;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (!has_cu_seqlens && T_tot % N != 0) return GDN_ERR_INVALID_ARG;
-    *bytes = dtype == GDN_BF16 ? gdn::chunk_bf16_workspace(N, T_tot, H, dk, dv, has_cu_seqlens != 0) : 0;
+    int P = 1;
+    st = segments_for(N, T_tot, H, dv, dtype, has_conv != 0, flags, &P);
+    if (st != GDN_OK) return st;
+    *bytes = workspace_for(N, H, dk, dv, P);
     return GDN_OK;
 }
 
@@ -86,8 +108,10 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
          overlaps(final_state, ts, conv_w, tcw)))
         return GDN_ERR_INVALID_ARG;
 
-    const size_t need =
-        dtype == GDN_BF16 ? gdn::chunk_bf16_workspace(N, T_tot, H, dk, dv, cu_seqlens != nullptr) : 0;
+    int P = 1;
+    st = segments_for(N, T_tot, H, dv, dtype, conv_w != nullptr, flags, &P);
+    if (st != GDN_OK) return st;
+    const size_t need = workspace_for(N, H, dk, dv, P);
     if (need > 0) {
         if (!workspace_bytes) return GDN_ERR_INVALID_ARG;
         if (!workspace || *workspace_bytes < need) {
@@ -95,6 +119,13 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
             return GDN_ERR_WORKSPACE;
         }
         if (!aligned16(workspace)) return GDN_ERR_INVALID_ARG;
+        const size_t tw = *workspace_bytes;
+        if (overlaps(workspace, tw, q, tq) || overlaps(workspace, tw, k, tq) || overlaps(workspace, tw, v, tv) ||
+            overlaps(workspace, tw, g, tg) || overlaps(workspace, tw, beta, tg) ||
+            overlaps(workspace, tw, initial_state, ts) || overlaps(workspace, tw, final_state, ts) ||
+            overlaps(workspace, tw, o, tv) || overlaps(workspace, tw, cu_seqlens, tcu) ||
+            overlaps(workspace, tw, conv_w, tcw))
+            return GDN_ERR_INVALID_ARG;
     }
 
     gdn::ChunkArgs a;
@@ -118,6 +149,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     a.bf16 = dtype == GDN_BF16;
     a.scale = scale;
     a.l2norm = (flags & GDN_QK_L2NORM) ? 1 : 0;
+    a.segments = P;
     a.stream = static_cast<hipStream_t>(hip_stream);
     const hipError_t e = a.bf16 ? gdn::launch_chunk_bf16(a) : gdn::launch_chunk_f32(a);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
@@ -126,7 +158,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
                        void* o, int N, int H, int dk, int dv, int dtype, float scale, unsigned flags,
                        void* hip_stream) {
-    if (N < 0) return GDN_ERR_INVALID_ARG;
+    if (N < 0 || (flags & kSegMask)) return GDN_ERR_INVALID_ARG;
     int st = check_common(H, dk, dv, dtype, scale, flags);
     if (st != GDN_OK) return st;
     if (N == 0) return GDN_OK;

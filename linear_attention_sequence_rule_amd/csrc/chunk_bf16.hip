@@ -175,7 +175,7 @@ struct Smem {
     static constexpr int pORQ = pKK + C * 4;         // Gamma rq [C]
     static constexpr int pDRK = pORQ + C * 4;        // exp(gamma_C - gamma) rk [C]
     static constexpr int pBETA = pDRK + C * 4;       // beta [C]
-    static constexpr int pGC = pBETA + C * 4;        // Gamma_C (first of 16 floats)
+    static constexpr int pGC = pBETA + C * 4;        // Gamma_C, then the chunk's decay bound (2 of 16 floats)
     static constexpr int pBytes = pGC + 64;
     // layout
     static constexpr int R0 = 0;
@@ -190,14 +190,27 @@ struct Smem {
     static __device__ __forceinline__ int prep(int c) { return P0 + (c & 1) * pBytes; }
 };
 
+// How a workgroup starts its state, and what it does with o (one launch runs one of the passes of
+// the segmented long-sequence path, or the plain single pass).
+enum InitMode { INIT_S0 = 0, INIT_IDENTITY = 1, INIT_PREV = 2 };
+enum OutMode { OUT_NONE = 0, OUT_STORE = 1, OUT_ACCUMULATE = 2 };
+
 template <int DK>
 struct Params {
     const __bf16 *q, *k, *v;
     const float *g, *beta, *s0, *conv_w;
     const int32_t* cu;
     __bf16* o;
-    float* sfin;
+    float* sfin;   // end state per (segment, head): [N*P, H, dv, dk]
+    int* negl;     // per (segment, head): 1 if the run stopped at the decay bound, else 0 (or null)
     int N, T_tot, H, dv, nv;
+    int P;         // segments per sequence (1 = the sequence in one piece)
+    int init;      // InitMode: S0 = s0[n] for segment 0 and zero for the others; IDENTITY = I
+                   // (dv = dk rows); PREV = s0[(n P + p - 1) H + h], the state entering segment p
+    int out;       // OutMode
+    int v_zero;    // values taken as zero (v is not read)
+    int early_exit;  // stop once the product of the decays since the start is <= 2^-40
+    int skip_first;  // segment 0 does nothing
     float scale;
     int l2norm;
 };
@@ -252,7 +265,7 @@ __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned char* sm
         dma16(kb, voff, lds_addr(sm + lo + S::rK));
         dma16(qb, voff, lds_addr(sm + lo + S::rQ));
     }
-    {
+    if (!p.v_zero) {
         const int row = 16 * wid + lane / 4, slot = lane % 4, part = slot ^ (row % 4);
         const __bf16* vbase = uniform_ptr(p.v + tok0 * p.dv + vb * BV);
         const unsigned voff = (unsigned)min(row, len - 1) * (unsigned)(p.H * p.dv) * 2u + 16u * part;
@@ -377,7 +390,15 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
         pKK[lane] = b * __expf(gam) * rk;
         pDRK[lane] = __expf(gl - gam) * rk;
         pBETA[lane] = b;
-        if (lane == 0) pGC[0] = __expf(gl);
+        // log of the bound on the norm of this chunk's state transition: every token multiplies
+        // the state by alpha (I - beta khat khat^T), whose norm is <= alpha when 0 <= beta <= 2
+        // and |khat| <= 1 (L2 norm on); no bound otherwise.
+        const bool in_range = b >= 0.f && b <= 2.f && l2norm;
+        const bool all_in = __ballot(!in_range) == 0;
+        if (lane == 0) {
+            pGC[0] = __expf(gl);
+            pGC[1] = all_in ? gl : 1e30f;
+        }
         const float g2 = gam * kLog2e;
         own[C + lane] = g2 + __builtin_amdgcn_logf(b * rk);
         own[2 * C + lane] = g2 - __builtin_amdgcn_logf(rk);
@@ -701,16 +722,27 @@ __device__ __forceinline__ void state_part2(const Params<DK>& p, StateRegs<DK>& 
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int i = 16 * it + l16;
-        if (i < len) {
+        if (i < len && p.out != OUT_NONE) {
+            bf16x4* dst = reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g);
             bf16x4 out;
+            if (p.out == OUT_ACCUMULATE) {
+                const bf16x4 prev = *dst;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e]);
-            *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
+                for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e] + (float)prev[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e]);
+            }
+            *dst = out;
         }
     }
 }
 
 // ------------------------------------------------------------------------------------------
+// exp(-27.73) = 2^-40: below this bound on the state transition since the start, whatever the
+// state carried in, its remaining contribution is far under fp32 rounding.
+constexpr float kExitLog = -27.7258872f;
+
 template <int DK>
 __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
     using S = Smem<DK>;
@@ -720,19 +752,21 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
     const int lane = tid % 64;
     const int g = lane / 16, l16 = lane % 16;
 
-    // XCD-aware order: the nv row-block workgroups of one (n, h) share blockIdx mod 8 (same XCD,
-    // same L2) when the pair count allows it.
-    const int P = p.N * p.H;
+    // XCD-aware order: the nv row-block workgroups of one (segment, head) share blockIdx mod 8
+    // (same XCD, same L2) when the pair count allows it.
+    const int npairs = p.N * p.P * p.H;
     int pair, vb;
     const int b = blockIdx.x;
-    if (P % 8 == 0) {
+    if (npairs % 8 == 0) {
         vb = (b / 8) % p.nv;
         pair = (b / (8 * p.nv)) * 8 + b % 8;
     } else {
         vb = b % p.nv;
         pair = b / p.nv;
     }
-    const int n = pair / p.H, h = pair % p.H;
+    const int nseg = pair / p.H, h = pair % p.H;
+    const int n = nseg / p.P, seg = nseg % p.P;
+    if (p.skip_first && seg == 0) return;
     long bos, eos;
     if (p.cu) {
         bos = p.cu[n];
@@ -742,27 +776,47 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
         bos = (long)n * Ls;
         eos = bos + Ls;
     }
+    if (p.P > 1) {  // segment seg: ceil(chunks / P) whole chunks of the sequence
+        const long per = (((eos - bos + C - 1) / C + p.P - 1) / p.P) * C;
+        const long sb = min(eos, bos + seg * per);
+        eos = min(eos, sb + per);
+        bos = sb;
+    }
     const int nchunks = (int)((eos - bos + C - 1) / C);
 
     // T^T blocks above the block diagonal and Pm tiles above the diagonal are read as zeros but
-    // never written: clear both prep buffers once.
+    // never written: clear both prep buffers once.  Zero values: clear V in every raw buffer.
     for (int i = tid; i < C * TSTR; i += 256) {
         reinterpret_cast<__bf16*>(sm + S::prep(0) + S::pT)[i] = (__bf16)0.f;
         reinterpret_cast<__bf16*>(sm + S::prep(1) + S::pT)[i] = (__bf16)0.f;
         reinterpret_cast<__bf16*>(sm + S::prep(0) + S::pPm)[i] = (__bf16)0.f;
         reinterpret_cast<__bf16*>(sm + S::prep(1) + S::pPm)[i] = (__bf16)0.f;
     }
+    if (p.v_zero) {
+        for (int i = tid; i < C * BV; i += 256)
+#pragma unroll
+            for (int r = 0; r < 3; ++r) reinterpret_cast<__bf16*>(sm + S::raw(r) + S::rV)[i] = (__bf16)0.f;
+    }
 
     const bool is_state = wid < 2;
     const int cbase = 16 * wid;
     StateRegs<DK> st;
-    const size_t srow0 = ((size_t)pair * p.dv + vb * BV + cbase + l16) * DK;  // state row of this lane
+    const int row = vb * BV + cbase + l16;  // state row of this lane
+    const size_t srow0 = ((size_t)pair * p.dv + row) * DK;
     if (is_state) {
+        const float* src = nullptr;
+        if (p.init == INIT_S0 && p.s0 && seg == 0)
+            src = p.s0 + (((size_t)n * p.H + h) * p.dv + row) * DK;
+        else if (p.init == INIT_PREV)
+            src = p.s0 + (((size_t)(nseg - 1) * p.H + h) * p.dv + row) * DK;
 #pragma unroll
         for (int dt = 0; dt < StateRegs<DK>::DT; ++dt) {
-            if (p.s0) {
-                const float4 v = *reinterpret_cast<const float4*>(p.s0 + srow0 + 16 * dt + 4 * g);
+            if (src) {
+                const float4 v = *reinterpret_cast<const float4*>(src + 16 * dt + 4 * g);
                 st.S[dt] = fx4{v.x, v.y, v.z, v.w};
+            } else if (p.init == INIT_IDENTITY) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.S[dt][e] = (16 * dt + 4 * g + e == row) ? 1.f : 0.f;
             } else {
                 st.S[dt] = zero4();
             }
@@ -777,6 +831,8 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
     lds_barrier();
 
     // iteration k: prep on chunk k, state on chunk k-1, loads of chunk k+1
+    float decay = 0.f;  // log bound of the transition over the chunks the state has passed
+    int stopped = 0;
     for (int k = 0; k <= nchunks; ++k) {
         unsigned char* rawk = sm + S::raw(k);
         unsigned char* rawp = sm + S::raw(k + 2);  // chunk k-1
@@ -807,11 +863,19 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
         lds_barrier();
         // ---- C
         if (wid >= 2 && prep_on) solve_level2(sLt, Tt, wid - 2, lane);
+        if (p.early_exit && state_on)
+            decay += __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                   __builtin_bit_cast(int, reinterpret_cast<const float*>(pbp + S::pGC)[1])));
         if (next_on) {
             wait_loads();
             zero_tail<DK>(rawn, lenn, wid, lane);
         }
         lds_barrier();
+        // every wave read the same bounds in the same order: the exit is uniform
+        if (p.early_exit && decay <= kExitLog) {
+            stopped = 1;
+            break;
+        }
     }
 
     if (is_state && p.sfin) {
@@ -821,26 +885,42 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
             *reinterpret_cast<float4*>(p.sfin + srow0 + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
         }
     }
+    if (p.negl && vb == 0 && tid == 0) p.negl[pair] = stopped;
 }
 
+// One pass of the kernel.  rows = state rows (dv, or dk for the transition pass).
+struct Pass {
+    int P, init, out, v_zero, early_exit, skip_first, rows;
+    const float* s0;
+    float* sfin;
+    int* negl;
+};
+
 template <int DK>
-hipError_t launch_t(const ChunkArgs& a) {
+hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     Params<DK> p;
     p.q = static_cast<const __bf16*>(a.q);
     p.k = static_cast<const __bf16*>(a.k);
     p.v = static_cast<const __bf16*>(a.v);
     p.g = a.g;
     p.beta = a.beta;
-    p.s0 = a.s0;
+    p.s0 = c.s0;
     p.conv_w = a.conv_w;
     p.cu = a.cu;
     p.o = static_cast<__bf16*>(a.o);
-    p.sfin = a.sfin;
+    p.sfin = c.sfin;
+    p.negl = c.negl;
     p.N = a.N;
     p.T_tot = a.T_tot;
     p.H = a.H;
-    p.dv = a.dv;
-    p.nv = a.dv / BV;
+    p.dv = c.rows;
+    p.nv = c.rows / BV;
+    p.P = c.P;
+    p.init = c.init;
+    p.out = c.out;
+    p.v_zero = c.v_zero;
+    p.early_exit = c.early_exit;
+    p.skip_first = c.skip_first;
     p.scale = a.scale;
     p.l2norm = a.l2norm;
     const int smem = Smem<DK>::bytes;
@@ -852,21 +932,44 @@ hipError_t launch_t(const ChunkArgs& a) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_bf16_kernel<DK>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
-    const int grid = a.N * a.H * p.nv;
+    const int grid = a.N * c.P * a.H * p.nv;
     hipLaunchKernelGGL((chunk_bf16_kernel<DK>), dim3(grid), dim3(256), smem, a.stream, p);
     return hipGetLastError();
 }
 
-}  // namespace
+template <int DK>
+hipError_t run(const ChunkArgs& a, int P) {
+    if (P <= 1) return launch_t<DK>(a, Pass{1, INIT_S0, OUT_STORE, 0, 0, 0, a.dv, a.s0, a.sfin, nullptr});
+    // Segmented path for long sequences (each sequence cut into P segments of whole chunks).
+    // The chunk map is affine in the state: S_out = S_in A_p + B_p.
+    //  1. every segment from its own start: B_p (zero state in, the true initial state for p = 0)
+    //     and o without the contribution of the state entering the segment;
+    //  2. A_p = the transition of segment p (identity in, zero values), stopped once its norm
+    //     bound is below 2^-40 (then marked negligible);
+    //  3. combine: E_0 = B_0, E_p = E_{p-1} A_p + B_p (the true end states), final = E_{P-1};
+    //  4. correction: o += the contribution of E_{p-1} through segment p (zero values, linear),
+    //     stopped at the same bound.
+    const SegLayout L = seg_layout(a.N, a.H, a.dk, a.dv, P);
+    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+    float* E = reinterpret_cast<float*>(ws + L.off_E);
+    float* A = reinterpret_cast<float*>(ws + L.off_A);
+    int* negl = reinterpret_cast<int*>(ws + L.off_negl);
+    const int ex = a.l2norm ? 1 : 0;
+    hipError_t e = launch_t<DK>(a, Pass{P, INIT_S0, OUT_STORE, 0, 0, 0, a.dv, a.s0, E, nullptr});
+    if (e == hipSuccess) e = launch_t<DK>(a, Pass{P, INIT_IDENTITY, OUT_NONE, 1, ex, 1, a.dk, nullptr, A, negl});
+    if (e == hipSuccess) e = launch_seg_combine(E, A, negl, a.sfin, a.N, P, a.H, a.dk, a.dv, a.stream);
+    if (e == hipSuccess) e = launch_t<DK>(a, Pass{P, INIT_PREV, OUT_ACCUMULATE, 1, ex, 1, a.dv, E, nullptr, nullptr});
+    return e;
+}
 
-size_t chunk_bf16_workspace(int, int, int, int, int, bool) { return 0; }
+}  // namespace
 
 hipError_t launch_chunk_bf16(const ChunkArgs& a) {
     if (a.conv_w) return launch_chunk_valu_bf16(a);  // conv prologue: VALU path until the fused loader lands
     switch (a.dk) {
-        case 32: return launch_t<32>(a);
-        case 64: return launch_t<64>(a);
-        case 128: return launch_t<128>(a);
+        case 32: return run<32>(a, a.segments);
+        case 64: return run<64>(a, a.segments);
+        case 128: return run<128>(a, a.segments);
     }
     return hipErrorInvalidValue;
 }

@@ -33,13 +33,28 @@ struct ChunkArgs {
     bool bf16;
     float scale;
     int l2norm;
+    int segments;             // segments per sequence (1 = single pass), from plan_segments
     hipStream_t stream;
 };
+
+// Workspace of the segmented long-sequence path (P segments per sequence), byte offsets.
+struct SegLayout {
+    size_t off_E;     // fp32 [N*P, H, dv, dk]: B_p, overwritten by the true end states E_p
+    size_t off_A;     // fp32 [N*P, H, dk, dk]: segment transitions A_p
+    size_t off_negl;  // int32 [N*P, H]: 1 where A_p is below the decay bound
+    size_t bytes;
+};
+SegLayout seg_layout(int N, int H, int dk, int dv, int P);
+// Segments per sequence for a bf16 call without conv: `requested` if > 0, else enough to give
+// every compute unit of the current device a workgroup when (sequence, head, row block) units
+// alone do not, and only for sequences of at least 16 chunks per segment.
+int plan_segments(int N, int T_tot, int H, int dv, int requested);
 
 hipError_t launch_step(const StepArgs& a);
 hipError_t launch_chunk_f32(const ChunkArgs& a);
 hipError_t launch_chunk_bf16(const ChunkArgs& a);
 hipError_t launch_chunk_valu_bf16(const ChunkArgs& a);
-size_t chunk_bf16_workspace(int N, int T_tot, int H, int dk, int dv, bool has_cu);
+hipError_t launch_seg_combine(float* E, const float* A, const int* negl, float* sfin, int N, int P, int H, int dk,
+                              int dv, hipStream_t stream);
 
 }  // namespace gdn

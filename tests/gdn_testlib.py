@@ -32,7 +32,7 @@ def o_to_f64(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def run_gpu(wl: W.Workload, *, scale=1.0, l2norm=True, pass_state=True, want_final=True, stream=None):
+def run_gpu(wl: W.Workload, *, scale=1.0, l2norm=True, pass_state=True, want_final=True, stream=None, segments=0):
     from linear_attention_sequence_rule_amd import gdn_chunk_fwd
     import torch
     q, k, v = to_dev(wl.q), to_dev(wl.k), to_dev(wl.v)
@@ -41,7 +41,7 @@ def run_gpu(wl: W.Workload, *, scale=1.0, l2norm=True, pass_state=True, want_fin
     cu = to_dev(wl.cu_seqlens)
     cw = to_dev(wl.conv_w)
     o, sf = gdn_chunk_fwd(q, k, v, g, beta, s0, cu, cw, N=wl.N, scale=scale, l2norm=l2norm,
-                          output_final_state=want_final, stream=stream)
+                          output_final_state=want_final, stream=stream, segments=segments)
     torch.cuda.synchronize()
     return o_to_f64(o), (sf.cpu().numpy().astype(np.float64) if sf is not None else None)
 
@@ -54,6 +54,25 @@ def run_oracle(wl: W.Workload, *, scale=1.0, l2norm=True, pairs=None, pass_state
                               wl.s0 if pass_state else None, cu, wl.conv_w, scale=scale,
                               l2norm=l2norm, pairs=pairs, nthreads=nthreads)
     return o, sf
+
+
+def head_slice(wl: W.Workload, heads) -> W.Workload:
+    """The same workload restricted to the given heads (heads are independent chains, so the
+    oracle on the slice is exactly the oracle on those heads of the whole workload)."""
+    import copy
+    hs = np.asarray(list(heads))
+    sub = copy.copy(wl)
+    sub.H = len(hs)
+    sub.q, sub.k, sub.v = (np.ascontiguousarray(x[:, hs]) for x in (wl.q, wl.k, wl.v))
+    sub.g, sub.beta = np.ascontiguousarray(wl.g[:, hs]), np.ascontiguousarray(wl.beta[:, hs])
+    sub.s0 = None if wl.s0 is None else np.ascontiguousarray(wl.s0[:, hs])
+    if wl.conv_w is not None:
+        H, dk, dv = wl.H, wl.dk, wl.dv
+        rows = np.concatenate([np.arange(h * dk, (h + 1) * dk) for h in hs] +
+                              [H * dk + np.arange(h * dk, (h + 1) * dk) for h in hs] +
+                              [2 * H * dk + np.arange(h * dv, (h + 1) * dv) for h in hs])
+        sub.conv_w = np.ascontiguousarray(wl.conv_w[rows])
+    return sub
 
 
 def pair_rows(wl, n, h):

@@ -79,21 +79,48 @@ def test_chunk_validation(lib, kw, status):
 
 def test_workspace_query(lib):
     n = ctypes.c_size_t(0)
-    assert lib.gdn_chunk_workspace_size(1, 262144, 16, 128, 128, gdn.GDN_BF16, 64, 0, ctypes.byref(n)) == 0
+    # one long sequence, 16 heads: too few (head, row block) units for the device -> segments
+    assert lib.gdn_chunk_workspace_size(1, 262144, 16, 128, 128, gdn.GDN_BF16, 64, 0, 0, 1, ctypes.byref(n)) == 0
     need = n.value
-    if need == 0:
-        pytest.skip("this configuration needs no workspace")
+    assert need > 0
     wsb = ctypes.c_size_t(0)
-    st = chunk(lib, N=1, T=262144, H=16, dk=128, dv=128, q=FAKE * 64, k=FAKE * 640000, v=FAKE * 1280000,
-               g=FAKE * 1920000, beta=FAKE * 2000000, o=FAKE * 2100000, ws=None, wsb=ctypes.byref(wsb))
+    big = 1 << 32  # disjoint fake ranges, never dereferenced (the call fails before any launch)
+    st = chunk(lib, N=1, T=262144, H=16, dk=128, dv=128, q=big, k=2 * big, v=3 * big, g=4 * big, beta=5 * big,
+               o=6 * big, ws=None, wsb=ctypes.byref(wsb))
     assert st == gdn.GDN_ERR_WORKSPACE and wsb.value == need
+    # a workspace overlapping an input is rejected
+    wsb = ctypes.c_size_t(need)
+    st = chunk(lib, N=1, T=262144, H=16, dk=128, dv=128, q=big, k=2 * big, v=3 * big, g=4 * big, beta=5 * big,
+               o=6 * big, ws=3 * big + 64, wsb=ctypes.byref(wsb))
+    assert st == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_workspace_segments_flag(lib):
+    n = ctypes.c_size_t(0)
+    seg = lambda p: (p & 0xFF) << 8
+    # explicit single segment: no workspace; explicit 4 segments on a short input: workspace
+    assert lib.gdn_chunk_workspace_size(1, 262144, 16, 128, 128, 1, 64, 0, 0, 1 | seg(1), ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.gdn_chunk_workspace_size(2, 256, 2, 64, 32, 1, 64, 0, 0, 1 | seg(4), ctypes.byref(n)) == 0
+    units = 2 * 4 * 2
+    assert n.value >= units * (32 * 64 + 64 * 64 + 1) * 4
+    # many (sequence, head) units: automatic single pass
+    assert lib.gdn_chunk_workspace_size(64, 64 * 4096, 32, 128, 128, 1, 64, 1, 0, 1, ctypes.byref(n)) == 0
+    assert n.value == 0
+    # segments need the bf16 path without conv
+    assert lib.gdn_chunk_workspace_size(1, 4096, 1, 32, 32, 0, 64, 0, 0, 1 | seg(2), ctypes.byref(n)) == \
+        gdn.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_workspace_size(1, 4096, 1, 32, 32, 1, 64, 0, 1, 1 | seg(2), ctypes.byref(n)) == \
+        gdn.GDN_ERR_UNSUPPORTED
 
 
 def test_workspace_size_validation(lib):
     n = ctypes.c_size_t(0)
-    assert lib.gdn_chunk_workspace_size(1, 64, 1, 33, 32, 1, 64, 0, ctypes.byref(n)) == gdn.GDN_ERR_UNSUPPORTED
-    assert lib.gdn_chunk_workspace_size(3, 64, 1, 32, 32, 1, 64, 0, ctypes.byref(n)) == gdn.GDN_ERR_INVALID_ARG
-    assert lib.gdn_chunk_workspace_size(1, 64, 1, 32, 32, 1, 64, 0, None) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_chunk_workspace_size(1, 64, 1, 33, 32, 1, 64, 0, 0, 1, ctypes.byref(n)) == gdn.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_workspace_size(3, 64, 1, 32, 32, 1, 64, 0, 0, 1, ctypes.byref(n)) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_chunk_workspace_size(1, 64, 1, 32, 32, 1, 64, 0, 0, 1, None) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_chunk_workspace_size(1, 64, 1, 32, 32, 1, 64, 0, 0, 1 << 16, ctypes.byref(n)) == \
+        gdn.GDN_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -102,6 +129,7 @@ def test_workspace_size_validation(lib):
     (dict(N=-1), gdn.GDN_ERR_INVALID_ARG),
     (dict(o=FAKE * 6 + 64), gdn.GDN_ERR_INVALID_ARG),   # o inside the state
     (dict(flags=2), gdn.GDN_ERR_INVALID_ARG),
+    (dict(flags=1 | (2 << 8)), gdn.GDN_ERR_INVALID_ARG),  # segments are a prefill option
     (dict(N=0), gdn.GDN_OK),                        # empty batch: no-op, no launch
 ])
 def test_step_validation(lib, kw, status):

@@ -93,6 +93,65 @@ def test_prefill_workload_full():
     _flush("prefill full %s" % e)
 
 
+# ------------------------------------------------------------------- segmented long sequences
+
+@pytest.mark.parametrize("segs", [2, 3, 5])
+def test_bf16_segments_forced(segs):
+    """Sequences cut into segments (the last one empty for segs=5); workload gates, so transitions
+    and corrections stop at the decay bound after a chunk or two."""
+    wl = W.make("seg", seed=40 + segs, N=2, T=1000, H=3, dk=128, dv=64, dtype="bf16", s0_std=0.02)
+    o, s = TL.run_gpu(wl, segments=segs)
+    o_ref, s_ref = TL.run_oracle(wl)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("segments %d %s" % (segs, e))
+
+
+def test_bf16_segments_slow_decay_mixed():
+    """Head 0 decays slowly (g = -1e-3: full transitions A_p, full corrections, combine products);
+    heads 1, 2 keep the workload gates (negligible transitions).  No initial state passed."""
+    wl = W.make("seg_slow", seed=47, N=1, T=1024, H=3, dk=128, dv=128, dtype="bf16")
+    wl.g[:, 0] = -1e-3
+    o, s = TL.run_gpu(wl, segments=4)
+    o_ref, s_ref = TL.run_oracle(wl)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("segments slow %s" % e)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (32, 32)])
+def test_bf16_segments_varlen(dk, dv):
+    wl = W.make("seg_var", seed=48 + dk, lengths=[300, 0, 64, 1, 700], H=2, dk=dk, dv=dv, dtype="bf16",
+                s0_std=0.05, varlen=True)
+    wl.g[:, 1] = -2e-3
+    o, s = TL.run_gpu(wl, segments=3)
+    o_ref, s_ref = TL.run_oracle(wl)
+    TL.compare(wl, o, s, o_ref, s_ref)
+    np.testing.assert_array_equal(s[1], wl.s0[1])
+
+
+def test_bf16_segments_without_final_state():
+    wl = W.make("seg_nofinal", seed=49, N=1, T=700, H=2, dk=64, dv=64, dtype="bf16", s0_std=0.02)
+    o, s = TL.run_gpu(wl, segments=3, want_final=False)
+    assert s is None
+    o_ref, _ = TL.run_oracle(wl)
+    TL.compare(wl, o, None, o_ref, None)
+
+
+def test_long_prefill_workload_sampled():
+    """B=1, T=262144, H=16, d=128, bf16, zero initial state: the automatic segmented path at full
+    size, every output and final state of three sampled heads checked against the oracle."""
+    import torch
+    from linear_attention_sequence_rule_amd import gdn_chunk_workspace_size
+    wl = W.long_prefill()
+    need = gdn_chunk_workspace_size(wl.N, wl.T_tot, wl.H, wl.dk, wl.dv, has_cu_seqlens=False)
+    _flush("long prefill workspace %d bytes" % need)
+    o, s = TL.run_gpu(wl)
+    heads = [0, 7, 15]
+    sub = TL.head_slice(wl, heads)
+    o_ref, s_ref = TL.run_oracle(sub)
+    e = TL.compare(sub, o[:, heads], s[:, heads], o_ref, s_ref)
+    _flush("long prefill sampled heads %s %s" % (heads, e))
+
+
 # ----------------------------------------------------------------------------------- decode
 
 def _decode_check(dw, scale=1.0):
