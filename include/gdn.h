@@ -101,14 +101,15 @@ extern "C" {
  *  flags       GDN_QK_L2NORM, optionally | GDN_SEGMENTS(n)
  *  hip_stream  hipStream_t to launch on
  *
- * Long sequences (bf16 path without conv).  Each sequence is cut into P segments of whole chunks
+ * Long sequences (bf16 path).  Each sequence is cut into P segments of whole chunks
  * that run in parallel; the exact affine map of a segment, S_out = S_in A_p + B_p, joins them:
  * the segments run from a zero state (B_p and o), then as transitions (A_p: identity in, zero
- * values), a P-step combine gives the true entering states, and a last pass adds their
- * contribution to o (linear in the state).  A transition or a correction stops once the bound
- * exp(sum of g since the segment start) on its norm is <= 2^-40 (the bound holds with
- * GDN_QK_L2NORM and 0 <= beta <= 2; otherwise nothing stops early).  o in the first chunk(s) of
- * a segment is thus rounded to dtype twice.  P = 1 is the plain single pass.  With
+ * values), a P-step combine gives the true entering states E_p, and a last pass reruns each
+ * segment from E_{p-1}, overwriting o.  A transition and a rerun stop once the bound
+ * exp(sum of g since the segment start) on the segment's transition is <= 2^-40: past that
+ * point the state entering the segment has no effect above that factor (the bound holds with
+ * GDN_QK_L2NORM and 0 <= beta <= 2; otherwise nothing stops early and every pass runs the whole
+ * segment).  P = 1 is the plain single pass.  With
  * GDN_SEGMENTS(0), P is chosen so that (N * P * H * dv/32) workgroups cover the current device's
  * compute units, with at least 16 chunks per segment.
  */

@@ -32,10 +32,10 @@ int check_common(int H, int dk, int dv, int dtype, float scale, unsigned flags) 
 }
 
 // Segments per sequence for this call (1 = single pass).  A request for more than one segment is
-// honoured on the bf16 path without conv only.
-int segments_for(int N, int T_tot, int H, int dv, int dtype, bool has_conv, unsigned flags, int* P) {
+// honoured on the bf16 path only.
+int segments_for(int N, int T_tot, int H, int dv, int dtype, bool, unsigned flags, int* P) {
     const int req = (int)((flags & kSegMask) >> 8);
-    if (dtype != GDN_BF16 || has_conv) {
+    if (dtype != GDN_BF16) {
         if (req > 1) return GDN_ERR_UNSUPPORTED;
         *P = 1;
         return GDN_OK;

@@ -50,7 +50,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 constexpr int C = 64;        // chunk length
 constexpr int BV = 32;       // state rows per workgroup
 constexpr int TSTR = C + 8;  // bf16 row stride of T^T, Pm and L^T
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ fx4 mfma(bf16x8 a, bf16x8 b, fx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -193,7 +192,7 @@ struct Smem {
 // How a workgroup starts its state, and what it does with o (one launch runs one of the passes of
 // the segmented long-sequence path, or the plain single pass).
 enum InitMode { INIT_S0 = 0, INIT_IDENTITY = 1, INIT_PREV = 2 };
-enum OutMode { OUT_NONE = 0, OUT_STORE = 1, OUT_ACCUMULATE = 2 };
+enum OutMode { OUT_NONE = 0, OUT_STORE = 1 };
 
 template <int DK>
 struct Params {
@@ -207,7 +206,7 @@ struct Params {
     int P;         // segments per sequence (1 = the sequence in one piece)
     int init;      // InitMode: S0 = s0[n] for segment 0 and zero for the others; IDENTITY = I
                    // (dv = dk rows); PREV = s0[(n P + p - 1) H + h], the state entering segment p
-    int out;       // OutMode
+    int out;       // OutMode: o stored, or not written
     int v_zero;    // values taken as zero (v is not read)
     int early_exit;  // stop once the product of the decays since the start is <= 2^-40
     int skip_first;  // segment 0 does nothing
@@ -234,9 +233,14 @@ __device__ __forceinline__ void dma4(const void* base, unsigned voff, unsigned l
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
                  : "memory", "m0");
 }
-__device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
-    return __builtin_amdgcn_readfirstlane(static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)(void*)p)));
+// LDS byte addresses are formed as integers from the address of the shared array itself (a
+// constant), never by converting a computed flat pointer into LDS: that conversion made the
+// backend materialise the shared aperture base under register pressure, illegally.
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+__device__ __forceinline__ unsigned lds_base(unsigned char* sm) {
+    return static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_u8*)(void*)sm));
 }
+__device__ __forceinline__ unsigned lds_addr(unsigned a) { return __builtin_amdgcn_readfirstlane(a); }
 template <typename T>
 __device__ __forceinline__ const T* uniform_ptr(const T* p) {
     const uintptr_t u = reinterpret_cast<uintptr_t>(p);
@@ -246,7 +250,7 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 }
 
 template <int DK>
-__device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned char* sm, int rawoff, long t0, int len, int h,
+__device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned smb, int rawoff, long t0, int len, int h,
                                           int vb, int wid, int lane) {
     using S = Smem<DK>;
     constexpr int PPR = DK / 8;       // 16-byte slots per K/Q row
@@ -262,19 +266,19 @@ __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned char* sm
         const int part = slot ^ (row % PPR);
         const unsigned voff = (unsigned)min(row, len - 1) * rowq + 16u * part;
         const int lo = rawoff + row0 * DK * 2;
-        dma16(kb, voff, lds_addr(sm + lo + S::rK));
-        dma16(qb, voff, lds_addr(sm + lo + S::rQ));
+        dma16(kb, voff, lds_addr(smb + lo + S::rK));
+        dma16(qb, voff, lds_addr(smb + lo + S::rQ));
     }
     if (!p.v_zero) {
         const int row = 16 * wid + lane / 4, slot = lane % 4, part = slot ^ (row % 4);
         const __bf16* vbase = uniform_ptr(p.v + tok0 * p.dv + vb * BV);
         const unsigned voff = (unsigned)min(row, len - 1) * (unsigned)(p.H * p.dv) * 2u + 16u * part;
-        dma16(vbase, voff, lds_addr(sm + rawoff + S::rV + 16 * wid * BV * 2));
+        dma16(vbase, voff, lds_addr(smb + rawoff + S::rV + 16 * wid * BV * 2));
     }
     if (wid < 2) {
         const float* gbase = uniform_ptr((wid == 0 ? p.g : p.beta) + tok0);
         const unsigned voff = (unsigned)min(lane, len - 1) * (unsigned)p.H * 4u;
-        dma4(gbase, voff, lds_addr(sm + rawoff + (wid == 0 ? S::rG : S::rB)));
+        dma4(gbase, voff, lds_addr(smb + rawoff + (wid == 0 ? S::rG : S::rB)));
     }
 }
 
@@ -314,6 +318,112 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// ------------------------------------------------------------------------------------------
+// Conv prologue (page maplevalley.com.cn/news/1910399, section 3.1, 卷积预处理): a depthwise causal
+// conv over 4 tokens (tap 3 = current token, zero history before the sequence start) and SiLU on
+// every q, k and v channel, in place in the chunk's LDS tile once its loads have landed.  Lane t
+// owns the channel pair (2c, 2c+1) of one tile -- K, Q, or this workgroup's V columns -- for every
+// chunk, walks the chunk's rows in order, and carries the last three raw values of its channels in
+// registers into the next chunk, so no halo is re-read.  fp32 arithmetic, bf16 result.
+struct ConvLane {
+    int kind;        // 0 idle, 1 K, 2 Q, 3 V
+    int c;           // first channel of the pair within the tile
+    int wrow;        // conv_w row of channel c
+    float hx[2][3];  // raw history of the two channels, oldest first
+};
+
+__device__ __forceinline__ float silu(float x) {
+    return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
+
+template <int DK>
+__device__ __forceinline__ void conv_setup(ConvLane& cl, const Params<DK>& p, int tid, int h, int vb, long bos,
+                                           bool history) {
+    constexpr int NP = DK / 2;  // channel pairs per K or Q row
+    cl.kind = 0;
+    cl.c = 0;
+    cl.wrow = 0;
+    const __bf16* src = nullptr;
+    int width = DK, col = 0;
+    if (tid < NP) {
+        cl.kind = 1;
+        cl.c = 2 * tid;
+        cl.wrow = (p.H + h) * DK + cl.c;
+        src = p.k;
+        col = h * DK + cl.c;
+    } else if (tid < 2 * NP) {
+        cl.kind = 2;
+        cl.c = 2 * (tid - NP);
+        cl.wrow = h * DK + cl.c;
+        src = p.q;
+        col = h * DK + cl.c;
+    } else if (tid < 2 * NP + BV / 2 && !p.v_zero) {
+        cl.kind = 3;
+        cl.c = 2 * (tid - 2 * NP);
+        cl.wrow = 2 * p.H * DK + h * p.dv + vb * BV + cl.c;
+        src = p.v;
+        width = p.dv;
+        col = h * p.dv + vb * BV + cl.c;
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        float a = 0.f, b = 0.f;
+        if (cl.kind && history) {  // a segment that starts inside a sequence: its three previous tokens
+            const __bf16* x = src + (size_t)(bos - 3 + j) * p.H * width + col;
+            a = (float)x[0];
+            b = (float)x[1];
+        }
+        cl.hx[0][j] = a;
+        cl.hx[1][j] = b;
+    }
+}
+
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+// tile: LDS byte address of the swizzled tile (channel pairs are 4-byte aligned words).  Rows go
+// in batches of 16: all loads of a batch are issued before its first store (rows past the tail
+// are read -- they lie inside the tile -- but not written, so they stay zero).
+template <int W>
+__device__ __forceinline__ void conv_rows(ConvLane& cl, unsigned tile, float4 w0, float4 w1, int len) {
+    for (int r0 = 0; r0 < len; r0 += 16) {
+        uint32_t xx[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            xx[j] = *reinterpret_cast<lds_u32*>(static_cast<uintptr_t>(tile + 2u * swz<W>(r0 + j, cl.c)));
+        uint32_t yy[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float x0 = __uint_as_float(xx[j] << 16), x1 = __uint_as_float(xx[j] & 0xFFFF0000u);
+            const float y0 = w0.x * cl.hx[0][0] + w0.y * cl.hx[0][1] + w0.z * cl.hx[0][2] + w0.w * x0;
+            const float y1 = w1.x * cl.hx[1][0] + w1.y * cl.hx[1][1] + w1.z * cl.hx[1][2] + w1.w * x1;
+            cl.hx[0][0] = cl.hx[0][1];
+            cl.hx[0][1] = cl.hx[0][2];
+            cl.hx[0][2] = x0;
+            cl.hx[1][0] = cl.hx[1][1];
+            cl.hx[1][1] = cl.hx[1][2];
+            cl.hx[1][2] = x1;
+            const __bf16 o0 = (__bf16)silu(y0), o1 = (__bf16)silu(y1);
+            yy[j] = (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (r0 + j < len) *reinterpret_cast<lds_u32*>(static_cast<uintptr_t>(tile + 2u * swz<W>(r0 + j, cl.c))) = yy[j];
+    }
+}
+
+// raw: LDS byte address of the chunk's raw buffer
+template <int DK>
+__device__ __forceinline__ void conv_chunk(ConvLane& cl, const Params<DK>& p, unsigned raw, int len) {
+    using S = Smem<DK>;
+    if (!cl.kind) return;
+    const float4 w0 = *reinterpret_cast<const float4*>(p.conv_w + (size_t)cl.wrow * 4);
+    const float4 w1 = *reinterpret_cast<const float4*>(p.conv_w + (size_t)cl.wrow * 4 + 4);
+    if (cl.kind == 3)
+        conv_rows<BV>(cl, raw + S::rV, w0, w1, len);
+    else
+        conv_rows<DK>(cl, raw + (cl.kind == 1 ? S::rK : S::rQ), w0, w1, len);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -722,18 +832,11 @@ __device__ __forceinline__ void state_part2(const Params<DK>& p, StateRegs<DK>& 
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int i = 16 * it + l16;
-        if (i < len && p.out != OUT_NONE) {
-            bf16x4* dst = reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g);
+        if (i < len && p.out == OUT_STORE) {
             bf16x4 out;
-            if (p.out == OUT_ACCUMULATE) {
-                const bf16x4 prev = *dst;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e] + (float)prev[e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e]);
-            }
-            *dst = out;
+            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e]);
+            *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
         }
     }
 }
@@ -822,13 +925,23 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
             }
         }
     }
+    const unsigned smb = lds_base(sm);
+    const bool conv = p.conv_w != nullptr;
+    ConvLane cl;
+    if (conv) conv_setup<DK>(cl, p, tid, h, vb, bos, seg > 0 && nchunks > 0);
     if (nchunks > 0) {
         const int len0 = (int)min((long)C, eos - bos);
-        dma_chunk<DK>(p, sm, S::raw(0), bos, len0, h, vb, wid, lane);
+        dma_chunk<DK>(p, smb, S::raw(0), bos, len0, h, vb, wid, lane);
         wait_loads();
         zero_tail<DK>(sm + S::raw(0), len0, wid, lane);
+        lds_barrier();
+        if (conv) {
+            conv_chunk<DK>(cl, p, smb + S::raw(0), len0);
+            lds_barrier();
+        }
+    } else {
+        lds_barrier();
     }
-    lds_barrier();
 
     // iteration k: prep on chunk k, state on chunk k-1, loads of chunk k+1
     float decay = 0.f;  // log bound of the transition over the chunks the state has passed
@@ -850,7 +963,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
         if (wid == 2 && prep_on) prep_L<DK>(rawk, pbk, sm, lane, lenk, p.l2norm);
         if (wid == 3 && prep_on) prep_P<DK>(rawk, pbk, sm, lane, lenk, p.l2norm);
         if (is_state && state_on) state_part1<DK>(st, rawp, pbp, lane, cbase);
-        if (next_on) dma_chunk<DK>(p, sm, S::raw(k + 1), tk + C, lenn, h, vb, wid, lane);
+        if (next_on) dma_chunk<DK>(p, smb, S::raw(k + 1), tk + C, lenn, h, vb, wid, lane);
         lds_barrier();
         // ---- B
         const __bf16* sLt = reinterpret_cast<const __bf16*>(sm + S::L);
@@ -875,6 +988,11 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
         if (p.early_exit && decay <= kExitLog) {
             stopped = 1;
             break;
+        }
+        // ---- D (conv only): the prologue on chunk k+1, whose loads have all landed
+        if (conv && next_on) {
+            conv_chunk<DK>(cl, p, smb + S::raw(k + 1), lenn);
+            lds_barrier();
         }
     }
 
@@ -947,8 +1065,9 @@ hipError_t run(const ChunkArgs& a, int P) {
     //  2. A_p = the transition of segment p (identity in, zero values), stopped once its norm
     //     bound is below 2^-40 (then marked negligible);
     //  3. combine: E_0 = B_0, E_p = E_{p-1} A_p + B_p (the true end states), final = E_{P-1};
-    //  4. correction: o += the contribution of E_{p-1} through segment p (zero values, linear),
-    //     stopped at the same bound.
+    //  4. rerun: segment p again from E_{p-1}, overwriting o, until the bound on the transition
+    //     since the segment start is <= 2^-40; from there on the state of step 1 differs from the
+    //     true one by less than that factor of |E_{p-1}|, so step 1's o stands.
     const SegLayout L = seg_layout(a.N, a.H, a.dk, a.dv, P);
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     float* E = reinterpret_cast<float*>(ws + L.off_E);
@@ -958,14 +1077,13 @@ hipError_t run(const ChunkArgs& a, int P) {
     hipError_t e = launch_t<DK>(a, Pass{P, INIT_S0, OUT_STORE, 0, 0, 0, a.dv, a.s0, E, nullptr});
     if (e == hipSuccess) e = launch_t<DK>(a, Pass{P, INIT_IDENTITY, OUT_NONE, 1, ex, 1, a.dk, nullptr, A, negl});
     if (e == hipSuccess) e = launch_seg_combine(E, A, negl, a.sfin, a.N, P, a.H, a.dk, a.dv, a.stream);
-    if (e == hipSuccess) e = launch_t<DK>(a, Pass{P, INIT_PREV, OUT_ACCUMULATE, 1, ex, 1, a.dv, E, nullptr, nullptr});
+    if (e == hipSuccess) e = launch_t<DK>(a, Pass{P, INIT_PREV, OUT_STORE, 0, ex, 1, a.dv, E, nullptr, nullptr});
     return e;
 }
 
 }  // namespace
 
 hipError_t launch_chunk_bf16(const ChunkArgs& a) {
-    if (a.conv_w) return launch_chunk_valu_bf16(a);  // conv prologue: VALU path until the fused loader lands
     switch (a.dk) {
         case 32: return run<32>(a, a.segments);
         case 64: return run<64>(a, a.segments);

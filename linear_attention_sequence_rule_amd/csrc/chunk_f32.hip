@@ -294,7 +294,5 @@ hipError_t launch_valu(const ChunkArgs& a) {
 
 hipError_t launch_chunk_f32(const ChunkArgs& a) { return launch_valu<float>(a); }
 
-// The same exact-fp32 VALU algebra on bf16 inputs/outputs: a slow cross-check of the MFMA path.
-hipError_t launch_chunk_valu_bf16(const ChunkArgs& a) { return launch_valu<bf16>(a); }
 
 }  // namespace gdn

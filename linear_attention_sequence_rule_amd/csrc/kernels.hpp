@@ -53,7 +53,6 @@ int plan_segments(int N, int T_tot, int H, int dv, int requested);
 hipError_t launch_step(const StepArgs& a);
 hipError_t launch_chunk_f32(const ChunkArgs& a);
 hipError_t launch_chunk_bf16(const ChunkArgs& a);
-hipError_t launch_chunk_valu_bf16(const ChunkArgs& a);
 hipError_t launch_seg_combine(float* E, const float* A, const int* negl, float* sfin, int N, int P, int H, int dk,
                               int dv, hipStream_t stream);
 

@@ -107,11 +107,11 @@ def test_workspace_segments_flag(lib):
     # many (sequence, head) units: automatic single pass
     assert lib.gdn_chunk_workspace_size(64, 64 * 4096, 32, 128, 128, 1, 64, 1, 0, 1, ctypes.byref(n)) == 0
     assert n.value == 0
-    # segments need the bf16 path without conv
+    # segments need the bf16 path (with or without conv)
     assert lib.gdn_chunk_workspace_size(1, 4096, 1, 32, 32, 0, 64, 0, 0, 1 | seg(2), ctypes.byref(n)) == \
         gdn.GDN_ERR_UNSUPPORTED
-    assert lib.gdn_chunk_workspace_size(1, 4096, 1, 32, 32, 1, 64, 0, 1, 1 | seg(2), ctypes.byref(n)) == \
-        gdn.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_workspace_size(1, 4096, 1, 32, 32, 1, 64, 0, 1, 1 | seg(2), ctypes.byref(n)) == 0
+    assert n.value > 0
 
 
 def test_workspace_size_validation(lib):

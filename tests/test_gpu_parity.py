@@ -74,6 +74,28 @@ def test_bf16_conv_varlen_small():
     _flush("bf16_conv %s" % e)
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 32), (32, 128), (128, 64)])
+def test_bf16_conv_dims(dk, dv):
+    wl = W.make("bf16_conv", seed=300 + dk + dv, lengths=[200, 3, 64, 0, 131], H=3, dk=dk, dv=dv, dtype="bf16",
+                s0_std=0.05, conv=True, varlen=True)
+    o, s = TL.run_gpu(wl, scale=0.8)
+    o_ref, s_ref = TL.run_oracle(wl, scale=0.8)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("bf16_conv %d %d %s" % (dk, dv, e))
+
+
+def test_bf16_conv_segments():
+    """Conv prologue on the segmented path: segments that start inside a sequence take the three
+    previous raw tokens as conv history; one head decays slowly so the corrections run long."""
+    wl = W.make("conv_seg", seed=51, lengths=[700, 130, 1, 520], H=2, dk=128, dv=64, dtype="bf16", s0_std=0.02,
+                conv=True, varlen=True)
+    wl.g[:, 1] = -1e-3
+    o, s = TL.run_gpu(wl, segments=3)
+    o_ref, s_ref = TL.run_oracle(wl)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("conv segments %s" % e)
+
+
 def test_bf16_slow_decay():
     """Slow decay (g ~ -1e-3) keeps the whole history alive: the hardest case for bf16 operands."""
     wl = W.make("slow", seed=9, N=2, T=1024, H=4, dk=128, dv=128, dtype="bf16", s0_std=0.02)
@@ -150,6 +172,22 @@ def test_long_prefill_workload_sampled():
     o_ref, s_ref = TL.run_oracle(sub)
     e = TL.compare(sub, o[:, heads], s[:, heads], o_ref, s_ref)
     _flush("long prefill sampled heads %s %s" % (heads, e))
+
+
+def test_varlen_workload_sampled():
+    """64 sequences, lengths ~U{512..16384}, H=32, d=128, bf16, conv + SiLU, per-sequence initial
+    states, seed 4: the whole workload on the GPU; 3 heads x 6 sequences (shortest, longest and
+    four others) checked against the oracle."""
+    wl = W.varlen()
+    o, s = TL.run_gpu(wl)
+    heads = [0, 13, 31]
+    order = np.argsort(wl.lengths)
+    seqs = sorted({int(order[0]), int(order[-1]), 5, 17, 40, 63})
+    sub = TL.head_slice(wl, heads)
+    pairs = [(n, j) for n in seqs for j in range(len(heads))]
+    o_ref, s_ref = TL.run_oracle(sub, pairs=pairs)
+    e = TL.compare(sub, o[:, heads], s[:, heads], o_ref, s_ref, pairs=pairs)
+    _flush("varlen sampled %s" % e)
 
 
 # ----------------------------------------------------------------------------------- decode
