@@ -9,9 +9,12 @@ independent copies of the inputs (more than twice the cache in total).
 The JSON line reports prefill tokens/s as `value`, the HBM roofline of the prefill kernel
 (algorithmic bytes per launch / mean launch time from HIP events on the launch stream), the bf16
 MFMA fraction under algorithmic flop accounting, the decode step (256 sequences x 32 heads, state
-updated in place) as GB/s against HBM, and the fp64 CPU oracle's throughput on the host cores.
+updated in place) as GB/s against HBM, the long-sequence prefill (1 x 262144 tokens, 16 heads,
+segmented) and the packed variable-length prefill with the conv prologue (64 sequences of
+512..16384 tokens, 32 heads) as tokens/s and GB/s, and the fp64 CPU oracle's throughput on the
+host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
 """
 import argparse
 import json
@@ -69,6 +72,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long-sequence and varlen lines")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated through the timed loop")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -157,6 +161,50 @@ def main():
     dec_bytes = decode_alg_bytes(dw.N, dw.H, dw.dk, dw.dv)
     dec_gbs = dec_bytes / dec_s / 1e9
 
+    # ---------------------------------------------------------------- long sequence, varlen + conv
+    def timed(fn, iters):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        return ts[len(ts) // 2] * 1e-3
+
+    extra = {}
+    if not args.no_extra:
+        lw = W.long_prefill()
+        lq, lk, lv, lg, lb = (to_dev(x) for x in (lw.q, lw.k, lw.v, lw.g, lw.beta))
+        lo = torch.empty_like(lv)
+        lsf = torch.empty((lw.N, lw.H, lw.dv, lw.dk), dtype=torch.float32, device=dev)
+        need = gdn.gdn_chunk_workspace_size(lw.N, lw.T_tot, lw.H, lw.dk, lw.dv)
+        lws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        ls = timed(lambda: gdn.gdn_chunk_fwd(lq, lk, lv, lg, lb, None, N=lw.N, o=lo, final_state=lsf, workspace=lws,
+                                             stream=stream), 5)
+        lbytes = lw.T_tot * lw.H * ((2 * lw.dk + lw.dv) * 2 + lw.dv * 2 + 8) + lw.N * lw.H * lw.dv * lw.dk * 4
+        extra["long_prefill"] = {
+            "workload": "long prefill B=1 T=262144 H=16 dk=dv=128 bf16, zero initial state, segmented",
+            "value": lw.T_tot / ls, "unit": "tokens/s", "us": ls * 1e6, "workspace_bytes": need,
+            "hbm_alg_gbs": lbytes / ls / 1e9, "hbm_frac": lbytes / ls / 1e9 / HBM_PEAK_GBS}
+        del lq, lk, lv, lg, lb, lo, lsf, lws, lw
+        vw = W.varlen()
+        vq, vk, vv, vg, vb, vs0, vcu, vcw = (to_dev(x) for x in (vw.q, vw.k, vw.v, vw.g, vw.beta, vw.s0, vw.cu_seqlens,
+                                                                  vw.conv_w))
+        vo = torch.empty_like(vv)
+        vsf = torch.empty_like(vs0)
+        vsec = timed(lambda: gdn.gdn_chunk_fwd(vq, vk, vv, vg, vb, vs0, vcu, vcw, o=vo, final_state=vsf, stream=stream), 3)
+        vbytes = vw.T_tot * vw.H * ((2 * vw.dk + vw.dv) * 2 + vw.dv * 2 + 8) + 2 * vw.N * vw.H * vw.dv * vw.dk * 4
+        extra["varlen"] = {
+            "workload": "varlen 64 sequences, lengths U{512..16384} (%d tokens), H=32, dk=dv=128 bf16, conv(4)+SiLU, "
+                        "initial states" % vw.T_tot,
+            "value": vw.T_tot / vsec, "unit": "tokens/s", "us": vsec * 1e6,
+            "hbm_alg_gbs": vbytes / vsec / 1e9, "hbm_frac": vbytes / vsec / 1e9 / HBM_PEAK_GBS}
+        del vq, vk, vv, vg, vb, vs0, vcu, vcw, vo, vsf, vw
+        torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -197,6 +245,7 @@ def main():
                                 "frac": dec_gbs / HBM_PEAK_GBS, "traffic": load_traffic("step_kernel")}},
         "cpu_baseline": cpu,
     }
+    out.update(extra)
     print(json.dumps(out))
 
 

@@ -14,26 +14,36 @@
 // operands (exact); the norms come from the diagonals of K K^T and Q Q^T and are folded into the
 // row and column scalings above.  Every decay factor is exp of a non-positive number.
 //
-// Work decomposition: one workgroup (4 wavefronts) per (sequence n, head h, block of 32 state
-// rows); state rows are independent, so the split is exact.  Software pipeline over chunks: in
-// iteration k the two "prep" waves (2, 3) build the state-independent operands of chunk k (gates,
-// norms, Pm = lower(M o Qhat Khat^T), T = (I + L)^-1) while the two "state" waves (0, 1) run the
-// state chain of chunk k-1, and every wave issues direct global->LDS loads (global_load_lds_dwordx4,
-// no registers involved) of chunk k+1.  Raw chunk inputs are triple buffered, prep outputs double
-// buffered.  Three barriers per iteration separate the sub-stages:
-//   A: prep: Gram tiles, norms, masks (L^T, Pm), gates  | state: K S^T, S Q^T, X
-//   B: prep: 16x16 diagonal blocks of T, first merge    | state: U, O (stored), S update
-//   C: prep: second merge level of T                    | all: wait for the chunk k+1 loads
+// Work decomposition: one workgroup of 8 wavefronts per (sequence n, head h, block of 32 state
+// rows); state rows are independent, so the split is exact.  Roles:
+//   waves 0, 1  state chain of 16 rows each, entirely in registers: K S^T, X, U, S update;
+//   waves 2, 3  output of the same 16 rows: S Q^T and Pm U, then the stores of o;
+//   waves 4..7  preparation: waves 4, 7 K K^T, norms, gates and L of chunk k+1 (two row-tile
+//               halves); waves 5, 6 the masked Pm = lower(M o Qhat Khat^T) of chunk k (likewise);
+//               in the second sub-stage waves 4, 5 invert the two 32x32 diagonal blocks of I + L
+//               and wave 6 copies the off-diagonal block L_BA next to them.
+//   The output waves also issue the direct global->LDS loads of chunk k+2 (after S Q^T) and wait
+//   for them after their stores.
+// U = T X is applied blockwise, so T's off-diagonal 32x32 block is never formed:
+//   U_A = T_AA X_A,  U_B = T_BB (X_B - L_BA U_A).
+// Two barriers per chunk: sub-stage A (state: K S^T, X, U | output: S Q^T | prep: Gram products,
+// masks), sub-stage B (state: S update | output: O | prep: diagonal-block solves, load waits).
+// With the conv prologue a third sub-stage runs it on chunk k+2 once its loads have landed.
+// Hand-offs between waves go through LDS: U (state -> output, within a chunk) and S in bf16
+// (state -> output, for the next chunk).  Raw chunk inputs are triple buffered, the gates double
+// buffered, T, Pm, L and the hand-offs single buffered (each is rewritten only after the barrier
+// that ends its readers' sub-stage).
 // K, Q and V rows are stored unpadded with their 16-byte slots XOR-swizzled by the row index
 // (slot = part ^ (row mod parts-per-row)), which keeps every fragment read conflict-free and
-// lets a 1 KB load instruction fill whole rows.
-// The state chain stays in registers: each 16x16 MFMA output tile is fed to the next product as an
-// operand ("chain order": lane group g = lane/16 holds k = 4g+e and 16+4g+e).  Operands stored in
-// the other orientation (T, V, K for the state update) are read with the gfx950 transposing LDS
-// read ds_read_b64_tr_b16 (within each 16-lane group, output lane i element e is element i%4 of
-// the 8 bytes addressed by lane 4e + i/4).
+// lets a 1 KB load instruction fill whole rows.  Each 16x16 MFMA output tile is fed to the next
+// product as an operand ("chain order": lane group g = lane/16 holds k = 4g+e and 16+4g+e).
+// Operands stored in the other orientation (T, V, K for the state update) are read with the
+// gfx950 transposing LDS read ds_read_b64_tr_b16 (within each 16-lane group, output lane i
+// element e is element i%4 of the 8 bytes addressed by lane 4e + i/4).
 // MFMA v_mfma_f32_16x16x32_bf16: A lane l holds A[l%16][8(l/16)+e]; B: B[8(l/16)+e][l%16];
 // D: D[4(l/16)+e][l%16].
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "prologue.hpp"
@@ -55,6 +65,13 @@ __device__ __forceinline__ fx4 mfma(bf16x8 a, bf16x8 b, fx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ fx4 zero4() { return fx4{0.f, 0.f, 0.f, 0.f}; }
+// A copy of x that the compiler cannot see through: lane-dependent address arithmetic derived
+// from it is recomputed where it is used instead of being hoisted out of the chunk loop, where
+// it would stay live in registers across every role's code.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 // Keep every instruction before this point (typically a batch of LDS operand reads) ahead of
 // everything after it: with one wavefront per SIMD the reads must be in flight early.
 __device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -134,11 +151,18 @@ __device__ __forceinline__ int off_nat(int ks, int g, int l16) {
 }
 template <int DK>
 __device__ __forceinline__ int off_trk(int dt, int g, int l16) {
+    // source lane 4e + q of the group addresses row 4g + e, columns kcol(dt, 4q) .. +3, so that
+    // output lane i receives column kcol(dt, i) (the state tile's key order, see kcol)
     constexpr int PPR = DK / 8;
     const int row = 4 * g + l16 / 4;
     const int key = row % PPR;
-    return row * DK + 8 * ((2 * dt + (l16 % 4) / 2) ^ key) + 4 * (l16 % 2);
+    return row * DK + 8 * ((4 * (dt / 2) + (l16 % 4)) ^ key) + 4 * (dt % 2);
 }
+// Key column held by row r (0..15) of state tile dt: the tiles are ordered so that the pair
+// (2ks, 2ks+1) gives lane group g the eight consecutive columns 32ks + 8g .. +7 (the natural
+// operand order of a 16x16x32 MFMA), i.e. tile 2ks holds 32ks + 8(r/4) + r%4 and tile 2ks+1 the
+// same plus 4.
+__device__ __forceinline__ int kcol(int dt, int r) { return 32 * (dt / 2) + 8 * (r / 4) + 4 * (dt % 2) + r % 4; }
 template <typename T>
 __device__ __forceinline__ T lds_at(const __bf16* base, int off) {
     return *reinterpret_cast<const T*>(base + off);
@@ -156,37 +180,39 @@ __device__ __forceinline__ float sel4(fx4 v, int e) {
 }
 
 // ------------------------------------------------------------------------------------------
-// LDS layout (bytes).  Raw chunk buffers R0..R2 rotate by chunk index mod 3, prep-output buffers
-// P0/P1 by chunk parity; L^T and the per-prep-wave norm/gate arrays are prep scratch.
+// LDS layout (bytes).  Raw chunk buffers rotate by chunk index mod 3, gate buffers by chunk parity.
 template <int DK>
 struct Smem {
-    // raw buffer (K, Q, V swizzled, unpadded)
+    // raw chunk buffer (K, Q, V swizzled, unpadded)
     static constexpr int rK = 0;                     // bf16 [C][DK]
     static constexpr int rQ = rK + C * DK * 2;       // bf16 [C][DK]
     static constexpr int rV = rQ + C * DK * 2;       // bf16 [C][BV]
     static constexpr int rG = rV + C * BV * 2;       // raw g [C]
     static constexpr int rB = rG + C * 4;            // beta [C]
     static constexpr int rBytes = rB + C * 4;
-    // prep-output buffer
-    static constexpr int pT = 0;                     // T^T bf16 [C][TSTR]: pT[m][i] = T[i][m]
-    static constexpr int pPm = pT + C * TSTR * 2;    // Pm bf16 [C][TSTR], row-major [i][m]
-    static constexpr int pKK = pPm + C * TSTR * 2;   // beta Gamma rk [C]
-    static constexpr int pORQ = pKK + C * 4;         // Gamma rq [C]
-    static constexpr int pDRK = pORQ + C * 4;        // exp(gamma_C - gamma) rk [C]
-    static constexpr int pBETA = pDRK + C * 4;       // beta [C]
-    static constexpr int pGC = pBETA + C * 4;        // Gamma_C, then the chunk's decay bound (2 of 16 floats)
-    static constexpr int pBytes = pGC + 64;
+    // gates of a chunk
+    static constexpr int gKK = 0;                    // beta Gamma rk [C]
+    static constexpr int gDRK = gKK + C * 4;         // exp(gamma_C - gamma) rk [C]
+    static constexpr int gBETA = gDRK + C * 4;       // beta [C]
+    static constexpr int gBP = gBETA + C * 4;        // gamma log2e - log2 rk [C] (column exponent of the masks)
+    static constexpr int gGC = gBP + C * 4;          // Gamma_C, log bound of the chunk's transition (2 of 16 floats)
+    static constexpr int gBytes = gGC + 64;
     // layout
     static constexpr int R0 = 0;
-    static constexpr int P0 = R0 + 3 * rBytes;
-    static constexpr int L = P0 + 2 * pBytes;        // L^T bf16 [C][TSTR]: L[j][i] = L_ij
-    static constexpr int W2 = L + C * TSTR * 2;      // wave 2: rk, row exponent, column exponent [3][C]
-    static constexpr int W3 = W2 + 3 * C * 4;        // wave 3: rk, rq, row exponent, column exponent [4][C]
-    static constexpr int bytes = W3 + 4 * C * 4;
-    static_assert(rBytes % 16 == 0, "alignment");
-    static_assert(pBytes % 16 == 0, "alignment");
+    static constexpr int G0 = R0 + 3 * rBytes;
+    static constexpr int T = G0 + 2 * gBytes;        // T^T bf16 [C][TSTR] (T^T[m][i] = T_im); L_BA in the T_BA block
+    static constexpr int PM = T + C * TSTR * 2;      // Pm bf16 [C][TSTR], row-major [i][m]
+    static constexpr int L = PM + C * TSTR * 2;      // L^T bf16 [C][TSTR]: L^T[j][i] = L_ij
+    static constexpr int ORQ = L + C * TSTR * 2;     // Gamma rq [C]
+    static constexpr int UH = ORQ + C * 4;           // U hand-off [2 waves][64 lanes][16 bf16]
+    static constexpr int UT = UH + 2 * 64 * 32;      // scaled U, state sub-stage A -> B [2 waves][64 lanes][16 bf16]
+    static constexpr int SH = UT + 2 * 64 * 32;      // S hand-off [2 waves][64 lanes][DK/32][8 bf16]
+    static constexpr int WL = SH + 2 * 64 * (DK / 32) * 16;  // L-prep scratch, per wave: rk, a, b [2][3][C]
+    static constexpr int WP = WL + 6 * C * 4;        // P-prep scratch, per wave: rq, a [2][2][C]
+    static constexpr int bytes = WP + 4 * C * 4;
+    static_assert(rBytes % 16 == 0 && gBytes % 16 == 0, "alignment");
     static __device__ __forceinline__ int raw(int c) { return R0 + (c % 3) * rBytes; }
-    static __device__ __forceinline__ int prep(int c) { return P0 + (c & 1) * pBytes; }
+    static __device__ __forceinline__ int gates(int c) { return G0 + (c & 1) * gBytes; }
 };
 
 // How a workgroup starts its state, and what it does with o (one launch runs one of the passes of
@@ -252,6 +278,7 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 template <int DK>
 __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned smb, int rawoff, long t0, int len, int h,
                                           int vb, int wid, int lane) {
+    lane = opaque(lane);
     using S = Smem<DK>;
     constexpr int PPR = DK / 8;       // 16-byte slots per K/Q row
     constexpr int RPI = 64 / PPR;     // rows per 1 KB instruction
@@ -285,6 +312,7 @@ __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned smb, int
 // After this wave's loads landed: clear its rows past the tail (last chunk of a sequence only).
 template <int DK>
 __device__ __forceinline__ void zero_tail(unsigned char* raw, int len, int wid, int lane) {
+    lane = opaque(lane);
     using S = Smem<DK>;
     if (len >= C) return;
     __bf16* K = reinterpret_cast<__bf16*>(raw + S::rK);
@@ -378,6 +406,7 @@ __device__ __forceinline__ void conv_setup(ConvLane& cl, const Params<DK>& p, in
         cl.hx[0][j] = a;
         cl.hx[1][j] = b;
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of this stays pending into the chunk loop
 }
 
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
@@ -420,6 +449,10 @@ __device__ __forceinline__ void conv_chunk(ConvLane& cl, const Params<DK>& p, un
     if (!cl.kind) return;
     const float4 w0 = *reinterpret_cast<const float4*>(p.conv_w + (size_t)cl.wrow * 4);
     const float4 w1 = *reinterpret_cast<const float4*>(p.conv_w + (size_t)cl.wrow * 4 + 4);
+    // Wait for these loads here: otherwise on paths that skip the rows they stay pending across
+    // the chunk loop, and the waits the compiler then places before reusing their registers also
+    // wait for the in-flight chunk prefetch (vmcnt counts in order).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     if (cl.kind == 3)
         conv_rows<BV>(cl, raw + S::rV, w0, w1, len);
     else
@@ -430,13 +463,22 @@ __device__ __forceinline__ void conv_chunk(ConvLane& cl, const Params<DK>& p, un
 // prep waves
 
 // inclusive prefix sum over the 64 lanes of a wave
+// (DPP row shifts inside each 16-lane row, then the three row totals added through readlane).
+template <int N>
+__device__ __forceinline__ float dpp_shr(float x) {  // lane l - N of the row, 0 for the first N lanes
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
 __device__ __forceinline__ float wave_scan(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    return x;
+    x += dpp_shr<1>(x);
+    x += dpp_shr<2>(x);
+    x += dpp_shr<4>(x);
+    x += dpp_shr<8>(x);
+    const float s0 = lane_value(x, 15), s1 = lane_value(x, 31), s2 = lane_value(x, 47);
+    const int r = lane >> 4;
+    return x + (r == 0 ? 0.f : (r == 1 ? s0 : (r == 2 ? s0 + s1 : (s0 + s1) + s2)));
 }
 
 // Norm of row 16 t + l16 from a diagonal Gram tile held in D layout: lane (l16, g = l16/4) holds
@@ -452,79 +494,101 @@ __device__ __forceinline__ void write_norm(float* dst, fx4 diag, int t, int lane
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Wave 2: K K^T (all lower tiles), rk, gates for the state waves, and L^T (bf16, L^T[j][i] = L_ij,
-// strict lower L masked with beta_i rk_i rk_j exp(gamma_i - gamma_j)).  The mask is evaluated in the
-// log2 domain: L_ij = exp2(a_i - b_j) G_ij with a_i = gamma_i log2e + log2(beta_i rk_i) and
-// b_j = gamma_j log2e - log2(rk_j); the decay part of the exponent is never positive, and a zero
-// beta or norm gives exp2(-inf) = 0.
-template <int DK>
-__device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* pb, unsigned char* sm, int lane, int len,
-                       int l2norm) {
+
+// Waves 4 and 7 on chunk k+1: K K^T row tiles {0, 3} (part 0) or {1, 2} (part 1), each with all
+// four diagonal tiles (the norms rk of every row), and those rows of L^T (bf16, L^T[j][i] = L_ij,
+// strict lower L masked with beta_i rk_i rk_j exp(gamma_i - gamma_j)); part 0 also writes the
+// chunk's gates.  The mask is evaluated in the log2 domain: L_ij = exp2(a_i - b_j) G_ij with
+// a_i = gamma_i log2e + log2(beta_i rk_i) and b_j = gamma_j log2e - log2(rk_j); the decay part of
+// the exponent is never positive, and a zero beta or norm gives exp2(-inf) = 0.  b is also the
+// column exponent of Pm.
+template <int DK, int part>
+__device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* gb, unsigned char* sm, int lane,
+                                       int len, int l2norm) {
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
+    constexpr int t0 = part ? 1 : 0, t1 = part ? 2 : 3;  // my row tiles
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
     const float* gr = reinterpret_cast<const float*>(raw + S::rG);
     const float* br = reinterpret_cast<const float*>(raw + S::rB);
     __bf16* sLt = reinterpret_cast<__bf16*>(sm + S::L);
-    float* own = reinterpret_cast<float*>(sm + S::W2);  // rk [C], a [C], b [C]
-    float* pKK = reinterpret_cast<float*>(pb + S::pKK);
-    float* pDRK = reinterpret_cast<float*>(pb + S::pDRK);
-    float* pBETA = reinterpret_cast<float*>(pb + S::pBETA);
-    float* pGC = reinterpret_cast<float*>(pb + S::pGC);
+    float* own = reinterpret_cast<float*>(sm + S::WL) + part * 3 * C;  // rk [C], a [C], b [C]
     const int g = lane / 16, l16 = lane % 16;
 
-    bf16x8 kf[4][KS];
+    const float gam = wave_scan(gr[lane], lane);
+    const float b = br[lane];
+
+    // k-step outer: only one k-step of fragments is live at a time
+    constexpr int ot0 = part ? 0 : 1, ot1 = part ? 3 : 2;  // diagonal tiles of the other part's rows
+    fx4 acc[2][4], dg[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) acc[s2][jt] = zero4();
+        dg[s2] = zero4();
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const int o = off_nat<DK>(ks, g, l16);
+        bf16x8 kf[4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) kf[rb][ks] = lds_at<bf16x8>(K, o + 16 * rb * DK);
-    }
-    const float gam = wave_scan(gr[lane], lane);
-    const float gl = __shfl(gam, C - 1);
-
-    fx4 acc[4][4];
+        for (int rb = 0; rb < 4; ++rb) kf[rb] = lds_at<bf16x8>(K, o + 16 * rb * DK);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int it = s2 ? t1 : t0;
 #pragma unroll
-        for (int jt = 0; jt <= it; ++jt) acc[it][jt] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int jt = 0; jt <= it; ++jt) acc[it][jt] = mfma(kf[it][ks], kf[jt][ks], acc[it][jt]);
-        write_norm(own, acc[it][it], it, lane, len, l2norm);
-    }
-    // gates of this chunk for the state waves and the mask exponents (lane = token)
-    {
-        const float rk = own[lane], b = br[lane];
-        pKK[lane] = b * __expf(gam) * rk;
-        pDRK[lane] = __expf(gl - gam) * rk;
-        pBETA[lane] = b;
-        // log of the bound on the norm of this chunk's state transition: every token multiplies
-        // the state by alpha (I - beta khat khat^T), whose norm is <= alpha when 0 <= beta <= 2
-        // and |khat| <= 1 (L2 norm on); no bound otherwise.
-        const bool in_range = b >= 0.f && b <= 2.f && l2norm;
-        const bool all_in = __ballot(!in_range) == 0;
-        if (lane == 0) {
-            pGC[0] = __expf(gl);
-            pGC[1] = all_in ? gl : 1e30f;
+            for (int jt = 0; jt < 4; ++jt)
+                if (jt <= it) acc[s2][jt] = mfma(kf[it], kf[jt], acc[s2][jt]);
+            const int od = s2 ? ot1 : ot0;
+            dg[s2] = mfma(kf[od], kf[od], dg[s2]);
         }
+    }
+    write_norm(own, acc[0][t0], t0, lane, len, l2norm);
+    write_norm(own, acc[1][t1], t1, lane, len, l2norm);
+    write_norm(own, dg[0], part ? 0 : 1, lane, len, l2norm);
+    write_norm(own, dg[1], part ? 3 : 2, lane, len, l2norm);
+    {
+        const float rk = own[lane];
         const float g2 = gam * kLog2e;
+        const float bj = g2 - __builtin_amdgcn_logf(rk);
         own[C + lane] = g2 + __builtin_amdgcn_logf(b * rk);
-        own[2 * C + lane] = g2 - __builtin_amdgcn_logf(rk);
+        own[2 * C + lane] = bj;
+        if (part == 0) {
+            float* gKK = reinterpret_cast<float*>(gb + S::gKK);
+            float* gDRK = reinterpret_cast<float*>(gb + S::gDRK);
+            float* gBETA = reinterpret_cast<float*>(gb + S::gBETA);
+            float* gBP = reinterpret_cast<float*>(gb + S::gBP);
+            float* gGC = reinterpret_cast<float*>(gb + S::gGC);
+            const float gl = lane_value(gam, C - 1);
+            gKK[lane] = b * __expf(gam) * rk;
+            gDRK[lane] = __expf(gl - gam) * rk;
+            gBETA[lane] = b;
+            gBP[lane] = bj;
+            // log of the bound on the norm of this chunk's state transition: every token
+            // multiplies the state by alpha (I - beta khat khat^T), whose norm is <= alpha when
+            // 0 <= beta <= 2 and |khat| <= 1 (L2 norm on); no bound otherwise.
+            const bool in_range = b >= 0.f && b <= 2.f && l2norm;
+            const bool all_in = __ballot(!in_range) == 0;
+            if (lane == 0) {
+                gGC[0] = __expf(gl);
+                gGC[1] = all_in ? gl : 1e30f;
+            }
+        }
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const int it = s2 ? t1 : t0;
         const int i0 = 16 * it + 4 * g;
         const fx4 ai = *reinterpret_cast<const fx4*>(own + C + i0);
 #pragma unroll
-        for (int jt = 0; jt <= it; ++jt) {
+        for (int jt = 0; jt < 4; ++jt) {
+            if (jt > it) continue;
             const int j = 16 * jt + l16;
             const float bj = own[2 * C + j];
             bf16x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float val = __builtin_amdgcn_exp2f(ai[e] - bj) * acc[it][jt][e];
+                const float val = __builtin_amdgcn_exp2f(ai[e] - bj) * acc[s2][jt][e];
                 out[e] = (__bf16)((jt < it || j < i0 + e) ? val : 0.f);
             }
             *reinterpret_cast<bf16x4*>(sLt + j * TSTR + i0) = out;
@@ -532,69 +596,74 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
     }
 }
 
-// Wave 3: norms (diagonals of K K^T and Q Q^T), Gamma rq, and Pm = lower(M o Qhat Khat^T) computed
-// as D = K Q^T so that a lane holds 4 consecutive m of row i (bf16, row-major).  Mask in the log2
-// domain: Pm_im = exp2(a_i - b_m) P_im, a_i = gamma_i log2e + log2(rq_i), b_m = gamma_m log2e - log2(rk_m).
-template <int DK>
-__device__ __forceinline__ void prep_P(const unsigned char* raw, unsigned char* pb, unsigned char* sm, int lane, int len,
-                       int l2norm) {
+// Waves 5, 6 on chunk k: rows tiles {0, 3} (half 0) or {1, 2} (half 1) of Pm = lower(M o Qhat
+// Khat^T), computed as D = K Q^T so that a lane holds 4 consecutive m of row i (bf16, row-major),
+// plus rq of those rows (diagonal of Q Q^T) and Gamma rq.  Mask in the log2 domain:
+// Pm_im = exp2(a_i - b_m) P_im, a_i = gamma_i log2e + log2(rq_i), b_m from the chunk's gates.
+template <int DK, int half>
+__device__ __forceinline__ void prep_P(const unsigned char* raw, const unsigned char* gb, unsigned char* sm, int lane,
+                                       int len, int l2norm) {
+    lane = opaque(lane);
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
     const __bf16* Q = reinterpret_cast<const __bf16*>(raw + S::rQ);
     const float* gr = reinterpret_cast<const float*>(raw + S::rG);
-    float* own = reinterpret_cast<float*>(sm + S::W3);  // rk [C], rq [C], a [C], b [C]
-    __bf16* Pm = reinterpret_cast<__bf16*>(pb + S::pPm);
-    float* pORQ = reinterpret_cast<float*>(pb + S::pORQ);
+    const float* gBP = reinterpret_cast<const float*>(gb + S::gBP);
+    float* own = reinterpret_cast<float*>(sm + S::WP) + half * 2 * C;  // rq [C], a [C]
+    __bf16* Pm = reinterpret_cast<__bf16*>(sm + S::PM);
+    float* orq = reinterpret_cast<float*>(sm + S::ORQ);
     const int g = lane / 16, l16 = lane % 16;
+    constexpr int t0 = half ? 1 : 0, t1 = half ? 2 : 3;  // my row tiles
 
-    bf16x8 kf[4][KS], qf[4][KS];
+    const float gam = wave_scan(gr[lane], lane);
+
+    fx4 acc[2][4], dq[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        dq[s] = zero4();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[s][mt] = zero4();
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const int o = off_nat<DK>(ks, g, l16);
+        bf16x8 kf[4], qf[2];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            kf[rb][ks] = lds_at<bf16x8>(K, o + 16 * rb * DK);
-            qf[rb][ks] = lds_at<bf16x8>(Q, o + 16 * rb * DK);
+        for (int rb = 0; rb < 4; ++rb)
+            if (rb <= t1) kf[rb] = lds_at<bf16x8>(K, o + 16 * rb * DK);
+        qf[0] = lds_at<bf16x8>(Q, o + 16 * t0 * DK);
+        qf[1] = lds_at<bf16x8>(Q, o + 16 * t1 * DK);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int it = s ? t1 : t0;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                if (mt <= it) acc[s][mt] = mfma(kf[mt], qf[s], acc[s][mt]);
+            dq[s] = mfma(qf[s], qf[s], dq[s]);
         }
     }
-    const float gam = wave_scan(gr[lane], lane);
-
-    fx4 acc[4][4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        fx4 dk = zero4(), dq = zero4();
-#pragma unroll
-        for (int mt = 0; mt <= it; ++mt) acc[it][mt] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int mt = 0; mt <= it; ++mt) acc[it][mt] = mfma(kf[mt][ks], qf[it][ks], acc[it][mt]);
-            dk = mfma(kf[it][ks], kf[it][ks], dk);
-            dq = mfma(qf[it][ks], qf[it][ks], dq);
-        }
-        write_norm(own, dk, it, lane, len, l2norm);
-        write_norm(own + C, dq, it, lane, len, l2norm);
-    }
-    {
-        const float rq = own[C + lane], rk = own[lane];
-        pORQ[lane] = __expf(gam) * rq;
-        const float g2 = gam * kLog2e;
-        own[2 * C + lane] = g2 + __builtin_amdgcn_logf(rq);
-        own[3 * C + lane] = g2 - __builtin_amdgcn_logf(rk);
+    write_norm(own, dq[0], t0, lane, len, l2norm);
+    write_norm(own, dq[1], t1, lane, len, l2norm);
+    if (lane / 16 == t0 || lane / 16 == t1) {
+        const float rq = own[lane];
+        orq[lane] = __expf(gam) * rq;
+        own[C + lane] = gam * kLog2e + __builtin_amdgcn_logf(rq);
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int s = 0; s < 2; ++s) {
+        const int it = s ? t1 : t0;
         const int i = 16 * it + l16;
-        const float ai = own[2 * C + i];
+        const float ai = own[C + i];
 #pragma unroll
-        for (int mt = 0; mt <= it; ++mt) {
+        for (int mt = 0; mt < 4; ++mt) {
+            if (mt > it) continue;
             const int m0 = 16 * mt + 4 * g;
-            const fx4 bm = *reinterpret_cast<const fx4*>(own + 3 * C + m0);
+            const fx4 bm = *reinterpret_cast<const fx4*>(gBP + m0);
             bf16x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float val = __builtin_amdgcn_exp2f(ai - bm[e]) * acc[it][mt][e];
+                const float val = __builtin_amdgcn_exp2f(ai - bm[e]) * acc[s][mt][e];
                 out[e] = (__bf16)((mt < it || m0 + e <= i) ? val : 0.f);
             }
             *reinterpret_cast<bf16x4*>(Pm + i * TSTR + m0) = out;
@@ -603,28 +672,51 @@ __device__ __forceinline__ void prep_P(const unsigned char* raw, unsigned char* 
 }
 
 // Solve level 0: invert the 16x16 unit-lower diagonal blocks b0, b0+1 of (I + L) by forward
-// substitution, one column per lane (lanes 0..31; lanes 32..63 compute a duplicate and discard
-// it).  Column m of the block is row m of L^T: read once with 16-byte loads.  The right-looking
-// update keeps one FMA on the critical path per step.  Writes the blocks of T^T (bf16; column j
-// of T = row j of T^T).
-__device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, int b0, int lane) {
-    const int b = b0 + (lane / 16) % 2, j = lane % 16, base = 16 * b;
-    bf16x8 Lc[16][2];
+// substitution, one column per lane (lanes 0..15 block b0, 16..31 block b0+1; lanes 32..63 compute
+// a duplicate and discard it).  Each lane reads its own column of L once (row j of L^T, two
+// 16-byte loads); at step m the column of lane m is broadcast within the 16-lane row with the DPP
+// row broadcast (as a DPP operand of the FMA), so the substitution reads nothing else from LDS.  The right-looking update keeps
+// one FMA on the critical path per step.  Writes the blocks of T^T (bf16; column j of T = row j
+// of T^T).
+// step M: t_M is final; acc[i] += L[i][M] t_M for i > M, L[i][M] taken from lane M of the row by
+// the FMA's DPP row-broadcast operand
+template <int M>
+__device__ __forceinline__ void fmac_bcast(float& acc, float l, float t) {  // acc += (lane M's l) * t
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc) : "v"(l), "v"(t), "i"(M));
+}
+template <int M>
+__device__ __forceinline__ void solve_step(const float (&col)[16], float (&acc)[16], float (&t)[16], int j) {
+    const float tm = M == j ? 1.f : (M > j ? -acc[M] : 0.f);
+    t[M] = tm;
 #pragma unroll
-    for (int m = 0; m < 15; ++m) {
-        Lc[m][0] = *reinterpret_cast<const bf16x8*>(sLt + (base + m) * TSTR + base);
-        Lc[m][1] = *reinterpret_cast<const bf16x8*>(sLt + (base + m) * TSTR + base + 8);
+    for (int i = M + 1; i < 16; ++i) fmac_bcast<M>(acc[i], col[i], tm);
+}
+template <int... Ms>
+__device__ __forceinline__ void solve_steps(const float (&col)[16], float (&acc)[16], float (&t)[16], int j,
+                                            std::integer_sequence<int, Ms...>) {
+    (solve_step<Ms>(col, acc, t, j), ...);
+}
+__device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, int b0, int lane) {
+    lane = opaque(lane);
+    const int b = b0 + (lane / 16) % 2, j = lane % 16, base = 16 * b;
+    const bf16x8 c0 = *reinterpret_cast<const bf16x8*>(sLt + (base + j) * TSTR + base);
+    const bf16x8 c1 = *reinterpret_cast<const bf16x8*>(sLt + (base + j) * TSTR + base + 8);
+    float col[16], acc[16], t[16];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        col[e] = (float)c0[e];
+        col[8 + e] = (float)c1[e];
     }
-    float acc[16], t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const float tm = m == j ? 1.f : (m > j ? -acc[m] : 0.f);
-        t[m] = tm;
-#pragma unroll
-        for (int i = m + 1; i < 16; ++i) acc[i] += (float)Lc[m][i / 8][i % 8] * tm;
-    }
+    // two wait states between the VALU writes of col and its first DPP read; the operands pin the
+    // writes before this point
+    asm volatile("s_nop 1"
+                 : "+v"(col[0]), "+v"(col[1]), "+v"(col[2]), "+v"(col[3]), "+v"(col[4]), "+v"(col[5]),
+                   "+v"(col[6]), "+v"(col[7]), "+v"(col[8]), "+v"(col[9]), "+v"(col[10]), "+v"(col[11]),
+                   "+v"(col[12]), "+v"(col[13]), "+v"(col[14]), "+v"(col[15]));
+    solve_steps(col, acc, t, j, std::make_integer_sequence<int, 16>{});
     if (lane < 32) {
         bf16x8 lo, hi;
 #pragma unroll
@@ -640,6 +732,7 @@ __device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, int b0
 // Solve level 1: T_{b+1,b} = -T_{b+1,b+1} (L_{b+1,b} T_{b,b}) for the 16x16 block pair (b, b+1).
 // bf16 operands (K = 16 real, padded to 32 with zeros).
 __device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, int b, int lane) {
+    lane = opaque(lane);
     const int g = lane / 16, l16 = lane % 16;
     const int r0 = 16 * (b + 1), c0 = 16 * b;
     const int gg = g & 1;
@@ -666,154 +759,132 @@ __device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, int 
     *reinterpret_cast<bf16x4*>(Tt + (c0 + l16) * TSTR + r0 + 4 * g) = out;
 }
 
-// Solve level 2: columns [16 half, 16 half + 16) of T_BA = -T_BB (L_BA T_AA), 32x32 blocks
-// A = rows 0..31, B = rows 32..63.
-__device__ __forceinline__ void solve_level2(const __bf16* sLt, __bf16* Tt, int half, int lane) {
-    const int g = lane / 16, l16 = lane % 16;
-    const int jc = 16 * half + l16;
-    // B operand: T_AA[8g .. +7][jc] = T^T row jc
-    const bf16x8 bt = *reinterpret_cast<const bf16x8*>(Tt + jc * TSTR + 8 * g);
-    fx4 y[2];
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        // A = L[32 + 16 it + l16][8g .. +7] via transposing reads of L^T
-        const bf16x8 a = frag_tr_nat(sLt, TSTR, 0, 32 + 16 * it, g, l16);
-        y[it] = mfma(a, bt, zero4());
-    }
-    const bf16x8 yb = pack_chain(y[0], y[1]);
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        // A = T_BB rows 32 + 16 it + l16, chain order over m in 32..63
-        const bf16x8 at = frag_tr_chain(Tt, TSTR, 32, 32 + 16 * it, g, l16);
-        const fx4 t = mfma(at, yb, zero4());
-        bf16x4 out;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = (__bf16)(-t[e]);
-        *reinterpret_cast<bf16x4*>(Tt + jc * TSTR + 32 + 16 * it + 4 * g) = out;
-    }
+// Wave 6: L_BA (rows 32..63, columns 0..31 of L) into the T_BA block of T^T, which the state
+// waves read in its place (U_B = T_BB (X_B - L_BA U_A)).  Both are stored transposed.
+__device__ __forceinline__ void copy_LBA(const __bf16* sLt, __bf16* Tt, int lane) {
+    lane = opaque(lane);
+    const int m = lane / 2, c = 32 + 16 * (lane % 2);
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sLt + m * TSTR + c);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(sLt + m * TSTR + c + 8);
+    *reinterpret_cast<bf16x8*>(Tt + m * TSTR + c) = a;
+    *reinterpret_cast<bf16x8*>(Tt + m * TSTR + c + 8) = b;
 }
 
 // ------------------------------------------------------------------------------------------
 // state waves: the chain of one chunk for 16 state rows, in registers.
+// Only S stays in registers across the barriers (every wave carries the registers of every role,
+// so whatever one role keeps live is lost to the others).
 template <int DK>
 struct StateRegs {
-    static constexpr int DT = DK / 16;
-    fx4 S[DT];     // S^T tiles: lane (c = l%16, g) holds S[c][16 dt + 4g + e]
-    bf16x8 xb[2];  // X, chain order over tokens
-    fx4 ot[4];     // O^T accumulators
+    static constexpr int DT = DK / 16, KS = DK / 32;
+    fx4 S[DT];       // S^T tiles: lane (c = l%16, g) holds S[c][kcol(dt, 4g + e)]
 };
 
-// Part 1: K S^T, S Q^T (scaled by Gamma rq), X = beta V - beta Gamma rk K S^T.
+// Hand-off slot i (16 bytes) of a lane: slots are stored slab by slab ([wave][slot][lane]), so
+// every 16-byte access instruction covers 1 KB of consecutive bytes.
+__device__ __forceinline__ bf16x8* handoff(unsigned char* sm, int base, int wave, int nslots, int slot, int lane) {
+    return reinterpret_cast<bf16x8*>(sm + base + ((wave * nslots + slot) * 64 + lane) * 16);
+}
+
+// Sub-stage A: K S^T, X = beta V - beta Gamma rk K S^T, U = T X blockwise; U goes to the output
+// wave, U scaled for the state update to sub-stage B (both through LDS).
 template <int DK>
-__device__ __forceinline__ void state_part1(StateRegs<DK>& st, const unsigned char* raw, const unsigned char* pb, int lane, int cbase) {
+__device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
+                                        const unsigned char* gb, int wave, int lane) {
+    lane = opaque(lane);
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
-    const __bf16* Q = reinterpret_cast<const __bf16*>(raw + S::rQ);
     const __bf16* V = reinterpret_cast<const __bf16*>(raw + S::rV);
-    const float* pKK = reinterpret_cast<const float*>(pb + S::pKK);
-    const float* pORQ = reinterpret_cast<const float*>(pb + S::pORQ);
-    const float* pBETA = reinterpret_cast<const float*>(pb + S::pBETA);
-    const int g = lane / 16, l16 = lane % 16;
+    const __bf16* Tt = reinterpret_cast<const __bf16*>(sm + S::T);
+    const float* gKK = reinterpret_cast<const float*>(gb + S::gKK);
+    const float* gBETA = reinterpret_cast<const float*>(gb + S::gBETA);
+    const float* gDRK = reinterpret_cast<const float*>(gb + S::gDRK);
+    const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
 
     bf16x8 sb[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) sb[ks] = pack_chain(st.S[2 * ks], st.S[2 * ks + 1]);
-    bf16x8 kfr[KS][4], qfr[KS][4];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int o0 = off_chain<DK>(ks, 0, g, l16), o1 = off_chain<DK>(ks, 1, g, l16);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            kfr[ks][t] = __builtin_shufflevector(lds_at<bf16x4>(K, o0 + 16 * t * DK),
-                                                 lds_at<bf16x4>(K, o1 + 16 * t * DK), 0, 1, 2, 3, 4, 5, 6, 7);
-            qfr[ks][t] = __builtin_shufflevector(lds_at<bf16x4>(Q, o0 + 16 * t * DK),
-                                                 lds_at<bf16x4>(Q, o1 + 16 * t * DK), 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-    }
-    issue_fence();
+    // K S^T, k-step outer so that one k-step of K fragments is live at a time
     fx4 ks_acc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        ks_acc[t] = zero4();
-        st.ot[t] = zero4();
-    }
+    for (int t = 0; t < 4; ++t) ks_acc[t] = zero4();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+        const int o = off_nat<DK>(ks, g, l16);
+        bf16x8 kfr[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            ks_acc[t] = mfma(kfr[ks][t], sb[ks], ks_acc[t]);  // K S^T  (M = token, N = c)
-            st.ot[t] = mfma(sb[ks], qfr[ks][t], st.ot[t]);    // S Q^T  (M = c, N = token)
-        }
+        for (int t = 0; t < 4; ++t) kfr[t] = lds_at<bf16x8>(K, o + 16 * t * DK);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ks_acc[t] = mfma(kfr[t], sb[ks], ks_acc[t]);  // K S^T (M = token, N = c)
     }
+    bf16x4 vv[4];
+    fx4 bm[4], kk[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int m0 = 16 * t + 4 * g;
+        vv[t] = str4<BV>(V, m0, cbase, l16);  // V[m0 .. +3][cbase + l16]
+        bm[t] = *reinterpret_cast<const fx4*>(gBETA + m0);
+        kk[t] = *reinterpret_cast<const fx4*>(gKK + m0);
+    }
+    // T blocks: T_AA rows 0..31, L_BA rows 32..63 (k over tokens 0..31), T_BB rows 32..63
+    const bf16x8 ta0 = frag_tr_chain(Tt, TSTR, 0, 0, g, l16), ta1 = frag_tr_chain(Tt, TSTR, 0, 16, g, l16);
+    const bf16x8 la2 = frag_tr_chain(Tt, TSTR, 0, 32, g, l16), la3 = frag_tr_chain(Tt, TSTR, 0, 48, g, l16);
+    const bf16x8 tb2 = frag_tr_chain(Tt, TSTR, 32, 32, g, l16), tb3 = frag_tr_chain(Tt, TSTR, 32, 48, g, l16);
     fx4 x[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int m0 = 16 * mt + 4 * g;
-        const fx4 bm = *reinterpret_cast<const fx4*>(pBETA + m0);
-        const fx4 kk = *reinterpret_cast<const fx4*>(pKK + m0);
-        const bf16x4 vv = str4<BV>(V, m0, cbase, l16);  // V[m0 .. +3][cbase + l16]
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[mt][e] = bm[e] * (float)vv[e] - kk[e] * ks_acc[mt][e];
-        const float orq = pORQ[16 * mt + l16];
+        for (int e = 0; e < 4; ++e) x[t][e] = bm[t][e] * (float)vv[t][e] - kk[t][e] * ks_acc[t][e];
+
+    const bf16x8 xa = pack_chain(x[0], x[1]);
+    fx4 u[4];
+    u[0] = mfma(ta0, xa, zero4());
+    u[1] = mfma(ta1, xa, zero4());
+    const bf16x8 ub0 = pack_chain(u[0], u[1]);
+    const fx4 y2 = mfma(la2, ub0, zero4()), y3 = mfma(la3, ub0, zero4());
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st.ot[mt][e] *= orq;
+    for (int e = 0; e < 4; ++e) {
+        x[2][e] -= y2[e];
+        x[3][e] -= y3[e];
     }
-    st.xb[0] = pack_chain(x[0], x[1]);
-    st.xb[1] = pack_chain(x[2], x[3]);
+    const bf16x8 xb = pack_chain(x[2], x[3]);
+    u[2] = mfma(tb2, xb, zero4());
+    u[3] = mfma(tb3, xb, zero4());
+    const bf16x8 ub1 = pack_chain(u[2], u[3]);
+    *handoff(sm, S::UH, wave, 2, 0, lane) = ub0;
+    *handoff(sm, S::UH, wave, 2, 1, lane) = ub1;
+
+    fx4 ut[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const fx4 dr = *reinterpret_cast<const fx4*>(gDRK + 16 * it + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ut[it][e] = u[it][e] * dr[e];
+    }
+    *handoff(sm, S::UT, wave, 2, 0, lane) = pack_chain(ut[0], ut[1]);
+    *handoff(sm, S::UT, wave, 2, 1, lane) = pack_chain(ut[2], ut[3]);
 }
 
-// Part 2: U = T X, O += Pm U (stored), S <- Gamma_C S + (D U)^T K.
+// Sub-stage B: S^T <- Gamma_C S^T + K^T (D U); the new S in bf16 goes to the output wave.
 template <int DK>
-__device__ __forceinline__ void state_part2(const Params<DK>& p, StateRegs<DK>& st, const unsigned char* raw, const unsigned char* pb,
-                            int lane, int cbase, long t0, int len, int h, int vb) {
+__device__ __forceinline__ void state_B(StateRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
+                                        const unsigned char* gb, int wave, int lane) {
+    lane = opaque(lane);
     using S = Smem<DK>;
-    constexpr int DT = DK / 16;
+    constexpr int DT = DK / 16, KS = DK / 32;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
-    const __bf16* Tt = reinterpret_cast<const __bf16*>(pb + S::pT);
-    const __bf16* Pm = reinterpret_cast<const __bf16*>(pb + S::pPm);
-    const float* pDRK = reinterpret_cast<const float*>(pb + S::pDRK);
-    const float gc = *reinterpret_cast<const float*>(pb + S::pGC);
+    const float gc = reinterpret_cast<const float*>(gb + S::gGC)[0];
     const int g = lane / 16, l16 = lane % 16;
-
-    // operand fragments first: T rows (transposing reads of T^T), Pm rows, K^T (transposing reads of K)
-    bf16x8 tf[4][2], pf[4][2], kt[DT][2];
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-            if (s2 == 0 || it >= 2) {
-                tf[it][s2] = frag_tr_chain(Tt, TSTR, 32 * s2, 16 * it, g, l16);
-                pf[it][s2] = frag_chain(Pm + (16 * it + l16) * TSTR, 32 * s2, g);
-            }
+    const bf16x8 utb[2] = {*handoff(sm, S::UT, wave, 2, 0, lane), *handoff(sm, S::UT, wave, 2, 1, lane)};
+    bf16x8 kt[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         const int o = off_trk<DK>(dt, g, l16);
         kt[dt][0] = __builtin_shufflevector(tr_read(K + o), tr_read(K + o + 16 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
         kt[dt][1] = __builtin_shufflevector(tr_read(K + o + 32 * DK), tr_read(K + o + 48 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    const fx4 dr0 = *reinterpret_cast<const fx4*>(pDRK + 4 * g), dr1 = *reinterpret_cast<const fx4*>(pDRK + 16 + 4 * g);
-    const fx4 dr2 = *reinterpret_cast<const fx4*>(pDRK + 32 + 4 * g), dr3 = *reinterpret_cast<const fx4*>(pDRK + 48 + 4 * g);
     issue_fence();
-
-    // U = T X (T lower triangular: i-tiles 0, 1 need only m < 32)
-    fx4 u[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) u[it] = mfma(tf[it][0], st.xb[0], zero4());
-#pragma unroll
-    for (int it = 2; it < 4; ++it) u[it] = mfma(tf[it][1], st.xb[1], u[it]);
-    const bf16x8 ub0 = pack_chain(u[0], u[1]), ub1 = pack_chain(u[2], u[3]);
-
-    // U scaled by exp(gamma_C - gamma) rk for the state update
-    const fx4 drk[4] = {dr0, dr1, dr2, dr3};
-    fx4 ut[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ut[it][e] = u[it][e] * drk[it][e];
-    const bf16x8 utb0 = pack_chain(ut[0], ut[1]), utb1 = pack_chain(ut[2], ut[3]);
-
-    // S^T = Gamma_C S^T + K^T (D U)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -821,21 +892,72 @@ __device__ __forceinline__ void state_part2(const Params<DK>& p, StateRegs<DK>& 
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][s2], s2 ? utb1 : utb0, st.S[dt]);
+        for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][s2], utb[s2], st.S[dt]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) *handoff(sm, S::SH, wave, KS, ks, lane) = pack_chain(st.S[2 * ks], st.S[2 * ks + 1]);
+}
 
-    // O^T += U^T Pm^T, store O (lane: token i = 16 it + l16, state rows cbase + 4g .. +3)
+// Output sub-stage A: O^T = S Q^T for 16 state rows (S from the state wave, in bf16).
+template <int DK>
+__device__ __forceinline__ void out_A(fx4 (&ot)[4], unsigned char* sm, const unsigned char* raw, int wave, int lane) {
+    lane = opaque(lane);
+    using S = Smem<DK>;
+    constexpr int KS = DK / 32;
+    const __bf16* Q = reinterpret_cast<const __bf16*>(raw + S::rQ);
+    const int g = lane / 16, l16 = lane % 16;
+    bf16x8 sb[KS], qfr[KS][4];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        sb[ks] = *handoff(sm, S::SH, wave, KS, ks, lane);
+        const int o = off_nat<DK>(ks, g, l16);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) qfr[ks][t] = lds_at<bf16x8>(Q, o + 16 * t * DK);
+    }
+    issue_fence();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ot[t] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ot[t] = mfma(sb[ks], qfr[ks][t], ot[t]);  // S Q^T (M = c, N = token)
+}
+
+// Output sub-stage B: O^T = diag(Gamma rq) (S Q^T) + U^T Pm^T, stored (lane: token 16 it + l16,
+// state rows cbase + 4g .. +3).
+template <int DK>
+__device__ __forceinline__ void out_B(const Params<DK>& p, fx4 (&ot)[4], unsigned char* sm, int wave, int lane, long t0,
+                                      int len, int h, int vb) {
+    lane = opaque(lane);
+    using S = Smem<DK>;
+    const __bf16* Pm = reinterpret_cast<const __bf16*>(sm + S::PM);
+    const float* orq = reinterpret_cast<const float*>(sm + S::ORQ);
+    const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
+    const bf16x8 ub0 = *handoff(sm, S::UH, wave, 2, 0, lane), ub1 = *handoff(sm, S::UH, wave, 2, 1, lane);
+    bf16x8 pf[4][2];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+            if (s2 == 0 || it >= 2) pf[it][s2] = frag_chain(Pm + (16 * it + l16) * TSTR, 32 * s2, g);
+    float r[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) r[it] = orq[16 * it + l16];
+    issue_fence();
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        st.ot[it] = mfma(ub0, pf[it][0], st.ot[it]);
-        if (it >= 2) st.ot[it] = mfma(ub1, pf[it][1], st.ot[it]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ot[it][e] *= r[it];
+        ot[it] = mfma(ub0, pf[it][0], ot[it]);
+        if (it >= 2) ot[it] = mfma(ub1, pf[it][1], ot[it]);
     }
+    if (p.out != OUT_STORE) return;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int i = 16 * it + l16;
-        if (i < len && p.out == OUT_STORE) {
+        if (i < len) {
             bf16x4 out;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e]);
+            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * ot[it][e]);
             *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
         }
     }
@@ -847,13 +969,15 @@ __device__ __forceinline__ void state_part2(const Params<DK>& p, StateRegs<DK>& 
 constexpr float kExitLog = -27.7258872f;
 
 template <int DK>
-__global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
+__global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     using S = Smem<DK>;
     extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
     const int g = lane / 16, l16 = lane % 16;
+    const bool is_state = wid < 2, is_out = wid == 2 || wid == 3, is_prep = wid >= 4;
+    const int pw = wid - 4;  // prep wave index
 
     // XCD-aware order: the nv row-block workgroups of one (segment, head) share blockIdx mod 8
     // (same XCD, same L2) when the pair count allows it.
@@ -886,25 +1010,22 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
         bos = sb;
     }
     const int nchunks = (int)((eos - bos + C - 1) / C);
+    auto clen = [&](int c) { return (int)min((long)C, eos - (bos + (long)c * C)); };
 
-    // T^T blocks above the block diagonal and Pm tiles above the diagonal are read as zeros but
-    // never written: clear both prep buffers once.  Zero values: clear V in every raw buffer.
-    for (int i = tid; i < C * TSTR; i += 256) {
-        reinterpret_cast<__bf16*>(sm + S::prep(0) + S::pT)[i] = (__bf16)0.f;
-        reinterpret_cast<__bf16*>(sm + S::prep(1) + S::pT)[i] = (__bf16)0.f;
-        reinterpret_cast<__bf16*>(sm + S::prep(0) + S::pPm)[i] = (__bf16)0.f;
-        reinterpret_cast<__bf16*>(sm + S::prep(1) + S::pPm)[i] = (__bf16)0.f;
+    // T^T blocks above the diagonal blocks and Pm tiles above the diagonal are read as zeros but
+    // never written: clear both once.  Zero values: clear V in every raw buffer.
+    for (int i = tid; i < C * TSTR; i += 512) {
+        reinterpret_cast<__bf16*>(sm + S::T)[i] = (__bf16)0.f;
+        reinterpret_cast<__bf16*>(sm + S::PM)[i] = (__bf16)0.f;
     }
     if (p.v_zero) {
-        for (int i = tid; i < C * BV; i += 256)
+        for (int i = tid; i < C * BV; i += 512)
 #pragma unroll
             for (int r = 0; r < 3; ++r) reinterpret_cast<__bf16*>(sm + S::raw(r) + S::rV)[i] = (__bf16)0.f;
     }
 
-    const bool is_state = wid < 2;
-    const int cbase = 16 * wid;
     StateRegs<DK> st;
-    const int row = vb * BV + cbase + l16;  // state row of this lane
+    const int row = vb * BV + 16 * wid + l16;  // state row of this lane (state waves)
     const size_t srow0 = ((size_t)pair * p.dv + row) * DK;
     if (is_state) {
         const float* src = nullptr;
@@ -915,73 +1036,82 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
 #pragma unroll
         for (int dt = 0; dt < StateRegs<DK>::DT; ++dt) {
             if (src) {
-                const float4 v = *reinterpret_cast<const float4*>(src + 16 * dt + 4 * g);
+                const float4 v = *reinterpret_cast<const float4*>(src + kcol(dt, 4 * g));
                 st.S[dt] = fx4{v.x, v.y, v.z, v.w};
             } else if (p.init == INIT_IDENTITY) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) st.S[dt][e] = (16 * dt + 4 * g + e == row) ? 1.f : 0.f;
+                for (int e = 0; e < 4; ++e) st.S[dt][e] = (kcol(dt, 4 * g + e) == row) ? 1.f : 0.f;
             } else {
                 st.S[dt] = zero4();
             }
         }
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) *handoff(sm, S::SH, wid, DK / 32, ks, lane) = pack_chain(st.S[2 * ks], st.S[2 * ks + 1]);
     }
+
     const unsigned smb = lds_base(sm);
     const bool conv = p.conv_w != nullptr;
     ConvLane cl;
-    if (conv) conv_setup<DK>(cl, p, tid, h, vb, bos, seg > 0 && nchunks > 0);
-    if (nchunks > 0) {
-        const int len0 = (int)min((long)C, eos - bos);
-        dma_chunk<DK>(p, smb, S::raw(0), bos, len0, h, vb, wid, lane);
+    if (conv && is_prep) conv_setup<DK>(cl, p, tid - 256, h, vb, bos, seg > 0 && nchunks > 0);
+    if (nchunks > 0 && is_prep) {
+        dma_chunk<DK>(p, smb, S::raw(0), bos, clen(0), h, vb, pw, lane);
         wait_loads();
-        zero_tail<DK>(sm + S::raw(0), len0, wid, lane);
-        lds_barrier();
-        if (conv) {
-            conv_chunk<DK>(cl, p, smb + S::raw(0), len0);
-            lds_barrier();
-        }
-    } else {
+        zero_tail<DK>(sm + S::raw(0), clen(0), pw, lane);
+    }
+    lds_barrier();
+    if (conv && nchunks > 0) {
+        if (is_prep) conv_chunk<DK>(cl, p, smb + S::raw(0), clen(0));
         lds_barrier();
     }
 
-    // iteration k: prep on chunk k, state on chunk k-1, loads of chunk k+1
+    // iteration k: state and output on chunk k, Pm of chunk k, L and T of chunk k+1, loads of k+2
+    fx4 ot[4];
     float decay = 0.f;  // log bound of the transition over the chunks the state has passed
     int stopped = 0;
-    for (int k = 0; k <= nchunks; ++k) {
-        unsigned char* rawk = sm + S::raw(k);
-        unsigned char* rawp = sm + S::raw(k + 2);  // chunk k-1
-        unsigned char* rawn = sm + S::raw(k + 1);  // chunk k+1
-        unsigned char* pbk = sm + S::prep(k);
-        unsigned char* pbp = sm + S::prep(k + 1);  // chunk k-1
-        const bool prep_on = k < nchunks;
-        const bool state_on = k > 0;
-        const bool next_on = k + 1 < nchunks;
+    for (int k = -1; k < nchunks; ++k) {
+        const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
         const long tk = bos + (long)k * C;
-        const int lenk = prep_on ? (int)min((long)C, eos - tk) : 0;
-        const int lenp = state_on ? (int)min((long)C, eos - (tk - C)) : 0;
-        const int lenn = next_on ? (int)min((long)C, eos - (tk + C)) : 0;
         // ---- A
-        if (wid == 2 && prep_on) prep_L<DK>(rawk, pbk, sm, lane, lenk, p.l2norm);
-        if (wid == 3 && prep_on) prep_P<DK>(rawk, pbk, sm, lane, lenk, p.l2norm);
-        if (is_state && state_on) state_part1<DK>(st, rawp, pbp, lane, cbase);
-        if (next_on) dma_chunk<DK>(p, smb, S::raw(k + 1), tk + C, lenn, h, vb, wid, lane);
+        if (cur) {
+            unsigned char* rawk = sm + S::raw(k);
+            unsigned char* gbk = sm + S::gates(k);
+            if (is_state) state_A<DK>(st, sm, rawk, gbk, wid, lane);
+            if (is_out) out_A<DK>(ot, sm, rawk, wid - 2, lane);
+            if (pw == 1) prep_P<DK, 0>(rawk, gbk, sm, lane, clen(k), p.l2norm);
+            if (pw == 2) prep_P<DK, 1>(rawk, gbk, sm, lane, clen(k), p.l2norm);
+        }
+        if (nxt && pw == 0) prep_L<DK, 0>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, clen(k + 1), p.l2norm);
+        if (nxt && pw == 3) prep_L<DK, 1>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, clen(k + 1), p.l2norm);
+        // the loads of chunk k+2 from the output waves, which have slack here (rows 32 (w-2) ..)
+        if (far && is_out) {
+            dma_chunk<DK>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, vb, 2 * (wid - 2), lane);
+            dma_chunk<DK>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, vb, 2 * (wid - 2) + 1, lane);
+        }
         lds_barrier();
         // ---- B
-        const __bf16* sLt = reinterpret_cast<const __bf16*>(sm + S::L);
-        __bf16* Tt = reinterpret_cast<__bf16*>(pbk + S::pT);
-        if (wid >= 2 && prep_on) {
-            solve_diag(sLt, Tt, wid == 2 ? 0 : 2, lane);
-            solve_level1(sLt, Tt, wid == 2 ? 0 : 2, lane);
+        if (cur) {
+            unsigned char* rawk = sm + S::raw(k);
+            unsigned char* gbk = sm + S::gates(k);
+            if (is_state) state_B<DK>(st, sm, rawk, gbk, wid, lane);
+            if (is_out) out_B<DK>(p, ot, sm, wid - 2, lane, tk, clen(k), h, vb);
+            if (p.early_exit)
+                decay += __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                                                       int, reinterpret_cast<const float*>(gbk + S::gGC)[1])));
         }
-        if (is_state && state_on) state_part2<DK>(p, st, rawp, pbp, lane, cbase, tk - C, lenp, h, vb);
-        lds_barrier();
-        // ---- C
-        if (wid >= 2 && prep_on) solve_level2(sLt, Tt, wid - 2, lane);
-        if (p.early_exit && state_on)
-            decay += __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                                                   __builtin_bit_cast(int, reinterpret_cast<const float*>(pbp + S::pGC)[1])));
-        if (next_on) {
+        if (nxt && (pw == 0 || pw == 1)) {
+            // the solve is this sub-stage's longest chain: its instructions go first on the SIMD
+            __builtin_amdgcn_s_setprio(3);
+            const __bf16* sLt = reinterpret_cast<const __bf16*>(sm + S::L);
+            __bf16* Tt = reinterpret_cast<__bf16*>(sm + S::T);
+            solve_diag(sLt, Tt, 2 * pw, lane);
+            solve_level1(sLt, Tt, 2 * pw, lane);
+            __builtin_amdgcn_s_setprio(0);
+        }
+        if (nxt && pw == 2) copy_LBA(reinterpret_cast<const __bf16*>(sm + S::L), reinterpret_cast<__bf16*>(sm + S::T), lane);
+        if (far && is_out) {
             wait_loads();
-            zero_tail<DK>(rawn, lenn, wid, lane);
+            zero_tail<DK>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2), lane);
+            zero_tail<DK>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2) + 1, lane);
         }
         lds_barrier();
         // every wave read the same bounds in the same order: the exit is uniform
@@ -989,9 +1119,9 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
             stopped = 1;
             break;
         }
-        // ---- D (conv only): the prologue on chunk k+1, whose loads have all landed
-        if (conv && next_on) {
-            conv_chunk<DK>(cl, p, smb + S::raw(k + 1), lenn);
+        // ---- C (conv only): the prologue on chunk k+2, whose loads have all landed
+        if (conv && far) {
+            if (is_prep) conv_chunk<DK>(cl, p, smb + S::raw(k + 2), clen(k + 2));
             lds_barrier();
         }
     }
@@ -1000,7 +1130,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(Params<DK> p) {
 #pragma unroll
         for (int dt = 0; dt < StateRegs<DK>::DT; ++dt) {
             const fx4 v = st.S[dt];
-            *reinterpret_cast<float4*>(p.sfin + srow0 + 16 * dt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(p.sfin + srow0 + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
         }
     }
     if (p.negl && vb == 0 && tid == 0) p.negl[pair] = stopped;
@@ -1051,7 +1181,7 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     const int grid = a.N * c.P * a.H * p.nv;
-    hipLaunchKernelGGL((chunk_bf16_kernel<DK>), dim3(grid), dim3(256), smem, a.stream, p);
+    hipLaunchKernelGGL((chunk_bf16_kernel<DK>), dim3(grid), dim3(512), smem, a.stream, p);
     return hipGetLastError();
 }
 
