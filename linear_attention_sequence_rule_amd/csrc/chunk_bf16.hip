@@ -209,7 +209,8 @@ struct Smem {
     static constexpr int SH = UT + 2 * 64 * 32;      // S hand-off [2 waves][64 lanes][DK/32][8 bf16]
     static constexpr int WL = SH + 2 * 64 * (DK / 32) * 16;  // L-prep scratch, per wave: rk, a, b [2][3][C]
     static constexpr int WP = WL + 6 * C * 4;        // P-prep scratch, per wave: rq, a [2][2][C]
-    static constexpr int bytes = WP + 4 * C * 4;
+    static constexpr int HB = WP + 4 * C * 4;        // conv halo: 3 raw rows [3][DK + BV/2] channel pairs
+    static constexpr int bytes = HB + 3 * (DK + BV / 2) * 4;
     static_assert(rBytes % 16 == 0 && gBytes % 16 == 0, "alignment");
     static __device__ __forceinline__ int raw(int c) { return R0 + (c % 3) * rBytes; }
     static __device__ __forceinline__ int gates(int c) { return G0 + (c & 1) * gBytes; }
@@ -351,112 +352,150 @@ __device__ __forceinline__ void lds_barrier() {
 // ------------------------------------------------------------------------------------------
 // Conv prologue (page maplevalley.com.cn/news/1910399, section 3.1, 卷积预处理): a depthwise causal
 // conv over 4 tokens (tap 3 = current token, zero history before the sequence start) and SiLU on
-// every q, k and v channel, in place in the chunk's LDS tile once its loads have landed.  Lane t
-// owns the channel pair (2c, 2c+1) of one tile -- K, Q, or this workgroup's V columns -- for every
-// chunk, walks the chunk's rows in order, and carries the last three raw values of its channels in
-// registers into the next chunk, so no halo is re-read.  fp32 arithmetic, bf16 result.
-struct ConvLane {
-    int kind;        // 0 idle, 1 K, 2 Q, 3 V
-    int c;           // first channel of the pair within the tile
-    int wrow;        // conv_w row of channel c
-    float hx[2][3];  // raw history of the two channels, oldest first
-};
+// every q, k and v channel, in place in the chunk's LDS tiles once all of its loads have landed.
+// Work item = (channel pair, block of 8 rows), taken in turn by all 512 lanes.  An item first
+// reads its 8 raw rows and the 3 raw rows before them (from the tile, or for the first block from
+// the halo buffer that keeps the previous chunk's last 3 raw rows); after a barrier -- no raw row
+// is overwritten before every item has read it -- it writes its results, and the items of the last
+// block store their raw rows in the halo buffer for the next chunk.  fp32 arithmetic, bf16 result.
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+__device__ __forceinline__ uint32_t ld32(unsigned a) { return *reinterpret_cast<lds_u32*>(static_cast<uintptr_t>(a)); }
+__device__ __forceinline__ void st32(unsigned a, uint32_t v) { *reinterpret_cast<lds_u32*>(static_cast<uintptr_t>(a)) = v; }
 
 __device__ __forceinline__ float silu(float x) {
     return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
 template <int DK>
-__device__ __forceinline__ void conv_setup(ConvLane& cl, const Params<DK>& p, int tid, int h, int vb, long bos,
-                                           bool history) {
-    constexpr int NP = DK / 2;  // channel pairs per K or Q row
-    cl.kind = 0;
-    cl.c = 0;
-    cl.wrow = 0;
-    const __bf16* src = nullptr;
-    int width = DK, col = 0;
-    if (tid < NP) {
-        cl.kind = 1;
-        cl.c = 2 * tid;
-        cl.wrow = (p.H + h) * DK + cl.c;
-        src = p.k;
-        col = h * DK + cl.c;
-    } else if (tid < 2 * NP) {
-        cl.kind = 2;
-        cl.c = 2 * (tid - NP);
-        cl.wrow = h * DK + cl.c;
-        src = p.q;
-        col = h * DK + cl.c;
-    } else if (tid < 2 * NP + BV / 2 && !p.v_zero) {
-        cl.kind = 3;
-        cl.c = 2 * (tid - 2 * NP);
-        cl.wrow = 2 * p.H * DK + h * p.dv + vb * BV + cl.c;
-        src = p.v;
-        width = p.dv;
-        col = h * p.dv + vb * BV + cl.c;
-    }
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        float a = 0.f, b = 0.f;
-        if (cl.kind && history) {  // a segment that starts inside a sequence: its three previous tokens
-            const __bf16* x = src + (size_t)(bos - 3 + j) * p.H * width + col;
-            a = (float)x[0];
-            b = (float)x[1];
+struct ConvPlan {
+    static constexpr int NP = DK + BV / 2;              // channel pairs: K (DK/2), Q (DK/2), V (BV/2)
+    static constexpr int ITEMS = NP * (C / 8);
+    static constexpr int PER = (ITEMS + 511) / 512;     // items per lane, at most
+};
+
+// Where channel pair pc lives in a raw buffer: tile offset, row width W (bf16), its 16-byte slot
+// and offset in the slot; then row r is at tile + 2 (r W + 8 (slot ^ (r mod W/8)) + off)
+// (the swizzle of swz<W>), computed without branches.
+struct PairLoc {
+    unsigned tile, w, mask, slot, off;
+};
+template <int DK>
+__device__ __forceinline__ PairLoc pair_loc(int pc) {
+    using S = Smem<DK>;
+    const bool isv = pc >= DK, isq = !isv && pc >= DK / 2;
+    const int c = 2 * (isv ? pc - DK : (isq ? pc - DK / 2 : pc));
+    PairLoc l;
+    l.tile = isv ? S::rV : (isq ? S::rQ : S::rK);
+    l.w = isv ? BV : DK;
+    l.mask = l.w / 8 - 1;
+    l.slot = c / 8;
+    l.off = c % 8;
+    return l;
+}
+__device__ __forceinline__ unsigned pair_addr(unsigned raw, const PairLoc& l, int r) {
+    return raw + l.tile + 2u * (r * l.w + 8u * (l.slot ^ (r & l.mask)) + l.off);
+}
+// conv_w row of the first channel of pair pc (q channels, then k, then v)
+template <int DK>
+__device__ __forceinline__ int pair_wrow(const Params<DK>& p, int pc, int h, int vb) {
+    if (pc < DK / 2) return (p.H + h) * DK + 2 * pc;
+    if (pc < DK) return h * DK + 2 * (pc - DK / 2);
+    return 2 * p.H * DK + h * p.dv + vb * BV + 2 * (pc - DK);
+}
+
+// Halo before the first chunk: zero at a sequence start; the three previous raw tokens when a
+// segment starts inside a sequence.  Layout [3 rows][NP pairs] of 4-byte words, oldest row first.
+template <int DK>
+__device__ void conv_halo_init(const Params<DK>& p, unsigned halo, int tid, int h, int vb, long bos, bool history) {
+    constexpr int NP = ConvPlan<DK>::NP;
+    for (int i = tid; i < 3 * NP; i += 512) {
+        const int j = i / NP, pc = i % NP;
+        uint32_t v = 0;
+        if (history && !(pc >= DK && p.v_zero)) {
+            const __bf16* src;
+            int width, col;
+            if (pc < DK / 2) {
+                src = p.k, width = DK, col = h * DK + 2 * pc;
+            } else if (pc < DK) {
+                src = p.q, width = DK, col = h * DK + 2 * (pc - DK / 2);
+            } else {
+                src = p.v, width = p.dv, col = h * p.dv + vb * BV + 2 * (pc - DK);
+            }
+            v = *reinterpret_cast<const uint32_t*>(src + (size_t)(bos - 3 + j) * p.H * width + col);
         }
-        cl.hx[0][j] = a;
-        cl.hx[1][j] = b;
+        st32(halo + 4u * (j * NP + pc), v);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of this stays pending into the chunk loop
 }
 
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-
-// tile: LDS byte address of the swizzled tile (channel pairs are 4-byte aligned words).  Rows go
-// in batches of 16: all loads of a batch are issued before its first store (rows past the tail
-// are read -- they lie inside the tile -- but not written, so they stay zero).
-template <int W>
-__device__ __forceinline__ void conv_rows(ConvLane& cl, unsigned tile, float4 w0, float4 w1, int len) {
-    for (int r0 = 0; r0 < len; r0 += 16) {
-        uint32_t xx[16];
+// The weights of a lane's items: the same items every chunk, so they are loaded once.
+template <int DK>
+struct ConvW {
+    float w[ConvPlan<DK>::PER][8];  // taps 0..3 of the pair's first channel, then of the second
+};
+template <int DK>
+__device__ void conv_weights(ConvW<DK>& cw, const Params<DK>& p, int tid, int h, int vb) {
+    using CP = ConvPlan<DK>;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            xx[j] = *reinterpret_cast<lds_u32*>(static_cast<uintptr_t>(tile + 2u * swz<W>(r0 + j, cl.c)));
-        uint32_t yy[16];
+    for (int q = 0; q < CP::PER; ++q) {
+        const int it = tid + 512 * q, pc = it % CP::NP;
+        const bool on = it < CP::ITEMS && !(pc >= DK && p.v_zero);
+        const float* w = p.conv_w + (size_t)(on ? pair_wrow<DK>(p, pc, h, vb) : 0) * 4;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float x0 = __uint_as_float(xx[j] << 16), x1 = __uint_as_float(xx[j] & 0xFFFF0000u);
-            const float y0 = w0.x * cl.hx[0][0] + w0.y * cl.hx[0][1] + w0.z * cl.hx[0][2] + w0.w * x0;
-            const float y1 = w1.x * cl.hx[1][0] + w1.y * cl.hx[1][1] + w1.z * cl.hx[1][2] + w1.w * x1;
-            cl.hx[0][0] = cl.hx[0][1];
-            cl.hx[0][1] = cl.hx[0][2];
-            cl.hx[0][2] = x0;
-            cl.hx[1][0] = cl.hx[1][1];
-            cl.hx[1][1] = cl.hx[1][2];
-            cl.hx[1][2] = x1;
-            const __bf16 o0 = (__bf16)silu(y0), o1 = (__bf16)silu(y1);
-            yy[j] = (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-            if (r0 + j < len) *reinterpret_cast<lds_u32*>(static_cast<uintptr_t>(tile + 2u * swz<W>(r0 + j, cl.c))) = yy[j];
+        for (int e = 0; e < 8; ++e) cw.w[q][e] = on ? w[e] : 0.f;
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of this stays pending into the chunk loop
 }
 
-// raw: LDS byte address of the chunk's raw buffer
+// The conv + SiLU of one chunk (raw: LDS byte address of its raw buffer); called by every lane.
 template <int DK>
-__device__ __forceinline__ void conv_chunk(ConvLane& cl, const Params<DK>& p, unsigned raw, int len) {
-    using S = Smem<DK>;
-    if (!cl.kind) return;
-    const float4 w0 = *reinterpret_cast<const float4*>(p.conv_w + (size_t)cl.wrow * 4);
-    const float4 w1 = *reinterpret_cast<const float4*>(p.conv_w + (size_t)cl.wrow * 4 + 4);
-    // Wait for these loads here: otherwise on paths that skip the rows they stay pending across
-    // the chunk loop, and the waits the compiler then places before reusing their registers also
-    // wait for the in-flight chunk prefetch (vmcnt counts in order).
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    if (cl.kind == 3)
-        conv_rows<BV>(cl, raw + S::rV, w0, w1, len);
-    else
-        conv_rows<DK>(cl, raw + (cl.kind == 1 ? S::rK : S::rQ), w0, w1, len);
+__device__ void conv_chunk(const Params<DK>& p, const ConvW<DK>& cw, unsigned raw, unsigned halo, int len, int tid) {
+    tid = opaque(tid);
+    using CP = ConvPlan<DK>;
+    constexpr int NP = CP::NP, PER = CP::PER;
+    uint32_t xr[PER][11];
+    bool act[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int it = tid + 512 * q, pc = it % NP, rb = it / NP;
+        act[q] = it < CP::ITEMS && !(pc >= DK && p.v_zero);
+        if (!act[q]) continue;
+        const PairLoc l = pair_loc<DK>(pc);
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            xr[q][j] = ld32(rb == 0 ? halo + 4u * (j * NP + pc) : pair_addr(raw, l, 8 * rb - 3 + j));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xr[q][3 + j] = ld32(pair_addr(raw, l, 8 * rb + j));
+    }
+    lds_barrier();  // every raw row has been read
+    tid = opaque(tid);                   // recompute the store addresses rather than keep them live
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        if (!act[q]) continue;
+        const int it = tid + 512 * q, pc = it % NP, rb = it / NP;
+        const PairLoc l = pair_loc<DK>(pc);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 8 * rb + j;
+            float lo[4], hi[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                lo[d] = __uint_as_float(xr[q][j + d] << 16);
+                hi[d] = __uint_as_float(xr[q][j + d] & 0xFFFF0000u);
+            }
+            const float* a = cw.w[q];
+            const float y0 = a[0] * lo[0] + a[1] * lo[1] + a[2] * lo[2] + a[3] * lo[3];
+            const float y1 = a[4] * hi[0] + a[5] * hi[1] + a[6] * hi[2] + a[7] * hi[3];
+            const __bf16 o0 = (__bf16)silu(y0), o1 = (__bf16)silu(y1);
+            if (r < len)  // rows past the tail stay zero
+                st32(pair_addr(raw, l, r),
+                     (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16));
+        }
+        if (rb == C / 8 - 1)
+#pragma unroll
+            for (int j = 0; j < 3; ++j) st32(halo + 4u * (j * NP + pc), xr[q][8 + j]);
+    }
+    lds_barrier();
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1051,18 +1090,18 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
 
     const unsigned smb = lds_base(sm);
     const bool conv = p.conv_w != nullptr;
-    ConvLane cl;
-    if (conv && is_prep) conv_setup<DK>(cl, p, tid - 256, h, vb, bos, seg > 0 && nchunks > 0);
+    ConvW<DK> cw;
+    if (conv) {
+        conv_weights<DK>(cw, p, tid, h, vb);
+        conv_halo_init<DK>(p, smb + S::HB, tid, h, vb, bos, seg > 0 && nchunks > 0);
+    }
     if (nchunks > 0 && is_prep) {
         dma_chunk<DK>(p, smb, S::raw(0), bos, clen(0), h, vb, pw, lane);
         wait_loads();
         zero_tail<DK>(sm + S::raw(0), clen(0), pw, lane);
     }
     lds_barrier();
-    if (conv && nchunks > 0) {
-        if (is_prep) conv_chunk<DK>(cl, p, smb + S::raw(0), clen(0));
-        lds_barrier();
-    }
+    if (conv && nchunks > 0) conv_chunk<DK>(p, cw, smb + S::raw(0), smb + S::HB, clen(0), tid);
 
     // iteration k: state and output on chunk k, Pm of chunk k, L and T of chunk k+1, loads of k+2
     fx4 ot[4];
@@ -1120,10 +1159,7 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
             break;
         }
         // ---- C (conv only): the prologue on chunk k+2, whose loads have all landed
-        if (conv && far) {
-            if (is_prep) conv_chunk<DK>(cl, p, smb + S::raw(k + 2), clen(k + 2));
-            lds_barrier();
-        }
+        if (conv && far) conv_chunk<DK>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
     }
 
     if (is_state && p.sfin) {
