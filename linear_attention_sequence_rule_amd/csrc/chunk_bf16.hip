@@ -18,10 +18,10 @@
 // rows); state rows are independent, so the split is exact.  Roles:
 //   waves 0, 1  state chain of 16 rows each, entirely in registers: K S^T, X, U, S update;
 //   waves 2, 3  output of the same 16 rows: S Q^T and Pm U, then the stores of o;
-//   waves 4..7  preparation: waves 4, 7 K K^T, norms, gates and L of chunk k+1 (two row-tile
-//               halves); waves 5, 6 the masked Pm = lower(M o Qhat Khat^T) of chunk k (likewise);
-//               in the second sub-stage waves 4, 5 invert the two 32x32 diagonal blocks of I + L
-//               and wave 6 copies the off-diagonal block L_BA next to them.
+//   waves 4..7  preparation: waves 4, 7 K K^T and the masked L of chunk k+1 (two row-tile halves,
+//               wave 4 also the norms); waves 5, 6 the masked Pm of chunk k (likewise);
+//               in the second sub-stage waves 4, 5 invert the two 32x32 diagonal blocks of I + L,
+//               wave 6 copies the off-diagonal block L_BA next to them and wave 7 writes the gates.
 //   The output waves also issue the direct global->LDS loads of chunk k+2 (after S Q^T) and wait
 //   for them after their stores.
 // U = T X is applied blockwise, so T's off-diagonal 32x32 block is never formed:
@@ -191,11 +191,11 @@ struct Smem {
     static constexpr int rB = rG + C * 4;            // beta [C]
     static constexpr int rBytes = rB + C * 4;
     // gates of a chunk
-    static constexpr int gKK = 0;                    // beta Gamma rk [C]
-    static constexpr int gDRK = gKK + C * 4;         // exp(gamma_C - gamma) rk [C]
-    static constexpr int gBETA = gDRK + C * 4;       // beta [C]
-    static constexpr int gBP = gBETA + C * 4;        // gamma log2e - log2 rk [C] (column exponent of the masks)
-    static constexpr int gGC = gBP + C * 4;          // Gamma_C, log bound of the chunk's transition (2 of 16 floats)
+    static constexpr int gKK = 0;                    // beta Gamma rk^2 [C]
+    static constexpr int gVB = gKK + C * 4;          // beta rk [C]
+    static constexpr int gDR = gVB + C * 4;          // exp(gamma_C - gamma) [C]
+    static constexpr int gGAM = gDR + C * 4;         // Gamma [C]
+    static constexpr int gGC = gGAM + C * 4;         // Gamma_C, log bound of the chunk's transition (2 of 16 floats)
     static constexpr int gBytes = gGC + 64;
     // layout
     static constexpr int R0 = 0;
@@ -203,12 +203,12 @@ struct Smem {
     static constexpr int T = G0 + 2 * gBytes;        // T^T bf16 [C][TSTR] (T^T[m][i] = T_im); L_BA in the T_BA block
     static constexpr int PM = T + C * TSTR * 2;      // Pm bf16 [C][TSTR], row-major [i][m]
     static constexpr int L = PM + C * TSTR * 2;      // L^T bf16 [C][TSTR]: L^T[j][i] = L_ij
-    static constexpr int ORQ = L + C * TSTR * 2;     // Gamma rq [C]
+    static constexpr int ORQ = L + C * TSTR * 2;     // rq [C]
     static constexpr int UH = ORQ + C * 4;           // U hand-off [2 waves][64 lanes][16 bf16]
     static constexpr int UT = UH + 2 * 64 * 32;      // scaled U, state sub-stage A -> B [2 waves][64 lanes][16 bf16]
     static constexpr int SH = UT + 2 * 64 * 32;      // S hand-off [2 waves][64 lanes][DK/32][8 bf16]
-    static constexpr int WL = SH + 2 * 64 * (DK / 32) * 16;  // L-prep scratch, per wave: rk, a, b [2][3][C]
-    static constexpr int WP = WL + 6 * C * 4;        // P-prep scratch, per wave: rq, a [2][2][C]
+    static constexpr int WL = SH + 2 * 64 * (DK / 32) * 16;  // L-prep scratch, per wave: rk, gamma log2e [2][2][C]
+    static constexpr int WP = WL + 4 * C * 4;        // P-prep scratch, per wave: rq, gamma log2e [2][2][C]
     static constexpr int HB = WP + 4 * C * 4;        // conv halo: 3 raw rows [3][DK + BV/2] channel pairs
     static constexpr int bytes = HB + 3 * (DK + BV / 2) * 4;
     static_assert(rBytes % 16 == 0 && gBytes % 16 == 0, "alignment");
@@ -534,16 +534,22 @@ __device__ __forceinline__ void write_norm(float* dst, fx4 diag, int t, int lane
 constexpr float kLog2e = 1.4426950408889634f;
 
 
-// Waves 4 and 7 on chunk k+1: K K^T row tiles {0, 3} (part 0) or {1, 2} (part 1), each with all
-// four diagonal tiles (the norms rk of every row), and those rows of L^T (bf16, L^T[j][i] = L_ij,
-// strict lower L masked with beta_i rk_i rk_j exp(gamma_i - gamma_j)); part 0 also writes the
-// chunk's gates.  The mask is evaluated in the log2 domain: L_ij = exp2(a_i - b_j) G_ij with
-// a_i = gamma_i log2e + log2(beta_i rk_i) and b_j = gamma_j log2e - log2(rk_j); the decay part of
-// the exponent is never positive, and a zero beta or norm gives exp2(-inf) = 0.  b is also the
-// column exponent of Pm.
+// The norms are kept out of the masks by a diagonal similarity.  With D = diag(rk) (rk = 1 on
+// padded rows, whose K, V and beta are zero), G = K K^T of the raw rows and
+// G_m = strict_lower(M o G):  I + L = D^-1 (I + L') D  with  L' = diag(f) G_m,  f = beta rk^2,
+// so T = D^-1 T' D with T' = (I + L')^-1, and with U' = D U:
+//   U' = T' Y,   Y = diag(beta rk) V - diag(beta Gamma rk^2) K S^T,
+//   O  = diag(rq) [ diag(Gamma) Q S^T + lower(M o Q K^T) U' ],
+//   S <- Gamma_C S + U'^T diag(exp(gamma_C - gamma)) K.
+// The masks need only the gates; f enters the solve as a row factor.
+
+// Waves 4 and 7 on chunk k+1: K K^T row tiles {0, 3} (part 0) or {1, 2} (part 1) masked with
+// M (those rows of L^T: bf16, L^T[j][i] = M_ij G_ij for j < i); part 0 also leaves the norms rk of
+// every row (from the four diagonal tiles) and gamma log2e for the next sub-stage.
+// exp(gamma_i - gamma_j) = exp2 of a non-positive number.
 template <int DK, int part>
-__device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* gb, unsigned char* sm, int lane,
-                                       int len, int l2norm) {
+__device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* sm, int lane, int len, int l2norm) {
+    lane = opaque(lane);
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
     constexpr int t0 = part ? 1 : 0, t1 = part ? 2 : 3;  // my row tiles
@@ -551,11 +557,12 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
     const float* gr = reinterpret_cast<const float*>(raw + S::rG);
     const float* br = reinterpret_cast<const float*>(raw + S::rB);
     __bf16* sLt = reinterpret_cast<__bf16*>(sm + S::L);
-    float* own = reinterpret_cast<float*>(sm + S::WL) + part * 3 * C;  // rk [C], a [C], b [C]
+    float* own = reinterpret_cast<float*>(sm + S::WL) + part * 2 * C;  // rk [C], gamma log2e [C]
     const int g = lane / 16, l16 = lane % 16;
 
     const float gam = wave_scan(gr[lane], lane);
     const float b = br[lane];
+    own[C + lane] = gam * kLog2e;
 
     // k-step outer: only one k-step of fragments is live at a time
     constexpr int ot0 = part ? 0 : 1, ot1 = part ? 3 : 2;  // diagonal tiles of the other part's rows
@@ -578,52 +585,23 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
                 if (jt <= it) acc[s2][jt] = mfma(kf[it], kf[jt], acc[s2][jt]);
-            const int od = s2 ? ot1 : ot0;
-            dg[s2] = mfma(kf[od], kf[od], dg[s2]);
-        }
-    }
-    write_norm(own, acc[0][t0], t0, lane, len, l2norm);
-    write_norm(own, acc[1][t1], t1, lane, len, l2norm);
-    write_norm(own, dg[0], part ? 0 : 1, lane, len, l2norm);
-    write_norm(own, dg[1], part ? 3 : 2, lane, len, l2norm);
-    {
-        const float rk = own[lane];
-        const float g2 = gam * kLog2e;
-        const float bj = g2 - __builtin_amdgcn_logf(rk);
-        own[C + lane] = g2 + __builtin_amdgcn_logf(b * rk);
-        own[2 * C + lane] = bj;
-        if (part == 0) {
-            float* gKK = reinterpret_cast<float*>(gb + S::gKK);
-            float* gDRK = reinterpret_cast<float*>(gb + S::gDRK);
-            float* gBETA = reinterpret_cast<float*>(gb + S::gBETA);
-            float* gBP = reinterpret_cast<float*>(gb + S::gBP);
-            float* gGC = reinterpret_cast<float*>(gb + S::gGC);
-            const float gl = lane_value(gam, C - 1);
-            gKK[lane] = b * __expf(gam) * rk;
-            gDRK[lane] = __expf(gl - gam) * rk;
-            gBETA[lane] = b;
-            gBP[lane] = bj;
-            // log of the bound on the norm of this chunk's state transition: every token
-            // multiplies the state by alpha (I - beta khat khat^T), whose norm is <= alpha when
-            // 0 <= beta <= 2 and |khat| <= 1 (L2 norm on); no bound otherwise.
-            const bool in_range = b >= 0.f && b <= 2.f && l2norm;
-            const bool all_in = __ballot(!in_range) == 0;
-            if (lane == 0) {
-                gGC[0] = __expf(gl);
-                gGC[1] = all_in ? gl : 1e30f;
+            if (part == 0) {  // part 0 computes the norms
+                const int od = s2 ? ot1 : ot0;
+                dg[s2] = mfma(kf[od], kf[od], dg[s2]);
             }
         }
     }
+    const float* g2 = own + C;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
         const int it = s2 ? t1 : t0;
         const int i0 = 16 * it + 4 * g;
-        const fx4 ai = *reinterpret_cast<const fx4*>(own + C + i0);
+        const fx4 ai = *reinterpret_cast<const fx4*>(g2 + i0);
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             if (jt > it) continue;
             const int j = 16 * jt + l16;
-            const float bj = own[2 * C + j];
+            const float bj = g2[j];
             bf16x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -633,29 +611,71 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
             *reinterpret_cast<bf16x4*>(sLt + j * TSTR + i0) = out;
         }
     }
+    if (part == 0) {  // rk of every row, for the solve and the gates (next sub-stage)
+        write_norm(own, acc[0][t0], t0, lane, len, l2norm);
+        write_norm(own, acc[1][t1], t1, lane, len, l2norm);
+        write_norm(own, dg[0], ot0, lane, len, l2norm);
+        write_norm(own, dg[1], ot1, lane, len, l2norm);
+    }
 }
 
-// Waves 5, 6 on chunk k: rows tiles {0, 3} (half 0) or {1, 2} (half 1) of Pm = lower(M o Qhat
-// Khat^T), computed as D = K Q^T so that a lane holds 4 consecutive m of row i (bf16, row-major),
-// plus rq of those rows (diagonal of Q Q^T) and Gamma rq.  Mask in the log2 domain:
-// Pm_im = exp2(a_i - b_m) P_im, a_i = gamma_i log2e + log2(rq_i), b_m from the chunk's gates.
+// Wave 7, sub-stage B, on chunk k+1: the gates, from rk and gamma log2e left by part 0 of prep_L.
+template <int DK>
+__device__ __forceinline__ void make_gates(const unsigned char* raw, unsigned char* gb, const unsigned char* sm,
+                                           int lane, int l2norm) {
+    lane = opaque(lane);
+    using S = Smem<DK>;
+    const float* own = reinterpret_cast<const float*>(sm + S::WL);  // part 0: rk [C], gamma log2e [C]
+    const float b = reinterpret_cast<const float*>(raw + S::rB)[lane];
+    const float rk = own[lane];
+    const float gam = own[C + lane] * (1.f / kLog2e);
+    const float gl = lane_value(gam, C - 1);
+    const float G = __expf(gam);
+    reinterpret_cast<float*>(gb + S::gKK)[lane] = b * G * rk * rk;
+    reinterpret_cast<float*>(gb + S::gVB)[lane] = b * rk;
+    reinterpret_cast<float*>(gb + S::gDR)[lane] = __expf(gl - gam);
+    reinterpret_cast<float*>(gb + S::gGAM)[lane] = G;
+    // log of the bound on the norm of this chunk's state transition: every token multiplies the
+    // state by alpha (I - beta khat khat^T), whose norm is <= alpha when 0 <= beta <= 2 and
+    // |khat| <= 1 (L2 norm on); no bound otherwise.
+    const bool in_range = b >= 0.f && b <= 2.f && l2norm;
+    const bool all_in = __ballot(!in_range) == 0;
+    if (lane == 0) {
+        float* gGC = reinterpret_cast<float*>(gb + S::gGC);
+        gGC[0] = __expf(gl);
+        gGC[1] = all_in ? gl : 1e30f;
+    }
+}
+
+// Row factors f_i = beta_i rk_i^2 of L' for rows i0 .. i0 + 4n - 1 (rk from part 0 of prep_L).
+template <int N>
+__device__ __forceinline__ void row_factors(float (&f)[4 * N], const float* rk, const float* beta, int i0) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+        const fx4 r = *reinterpret_cast<const fx4*>(rk + i0 + 4 * q), bb = *reinterpret_cast<const fx4*>(beta + i0 + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[4 * q + e] = bb[e] * r[e] * r[e];
+    }
+}
+
+// Waves 5, 6 on chunk k: row tiles {0, 3} (half 0) or {1, 2} (half 1) of Pm' = lower(M o Q K^T)
+// of the raw rows, computed as D = K Q^T so that a lane holds 4 consecutive m of row i (bf16,
+// row-major), and rq of those rows (diagonal of Q Q^T).
 template <int DK, int half>
-__device__ __forceinline__ void prep_P(const unsigned char* raw, const unsigned char* gb, unsigned char* sm, int lane,
-                                       int len, int l2norm) {
+__device__ __forceinline__ void prep_P(const unsigned char* raw, unsigned char* sm, int lane, int len, int l2norm) {
     lane = opaque(lane);
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
     const __bf16* Q = reinterpret_cast<const __bf16*>(raw + S::rQ);
     const float* gr = reinterpret_cast<const float*>(raw + S::rG);
-    const float* gBP = reinterpret_cast<const float*>(gb + S::gBP);
-    float* own = reinterpret_cast<float*>(sm + S::WP) + half * 2 * C;  // rq [C], a [C]
+    float* own = reinterpret_cast<float*>(sm + S::WP) + half * 2 * C;  // rq [C], gamma log2e [C]
     __bf16* Pm = reinterpret_cast<__bf16*>(sm + S::PM);
     float* orq = reinterpret_cast<float*>(sm + S::ORQ);
     const int g = lane / 16, l16 = lane % 16;
     constexpr int t0 = half ? 1 : 0, t1 = half ? 2 : 3;  // my row tiles
 
-    const float gam = wave_scan(gr[lane], lane);
+    own[C + lane] = wave_scan(gr[lane], lane) * kLog2e;
 
     fx4 acc[2][4], dq[2];
 #pragma unroll
@@ -682,23 +702,17 @@ __device__ __forceinline__ void prep_P(const unsigned char* raw, const unsigned 
             dq[s] = mfma(qf[s], qf[s], dq[s]);
         }
     }
-    write_norm(own, dq[0], t0, lane, len, l2norm);
-    write_norm(own, dq[1], t1, lane, len, l2norm);
-    if (lane / 16 == t0 || lane / 16 == t1) {
-        const float rq = own[lane];
-        orq[lane] = __expf(gam) * rq;
-        own[C + lane] = gam * kLog2e + __builtin_amdgcn_logf(rq);
-    }
+    const float* g2 = own + C;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const int it = s ? t1 : t0;
         const int i = 16 * it + l16;
-        const float ai = own[C + i];
+        const float ai = g2[i];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             if (mt > it) continue;
             const int m0 = 16 * mt + 4 * g;
-            const fx4 bm = *reinterpret_cast<const fx4*>(gBP + m0);
+            const fx4 bm = *reinterpret_cast<const fx4*>(g2 + m0);
             bf16x4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -708,6 +722,9 @@ __device__ __forceinline__ void prep_P(const unsigned char* raw, const unsigned 
             *reinterpret_cast<bf16x4*>(Pm + i * TSTR + m0) = out;
         }
     }
+    write_norm(own, dq[0], t0, lane, len, l2norm);
+    write_norm(own, dq[1], t1, lane, len, l2norm);
+    if (lane / 16 == t0 || lane / 16 == t1) orq[lane] = own[lane];
 }
 
 // Solve level 0: invert the 16x16 unit-lower diagonal blocks b0, b0+1 of (I + L) by forward
@@ -725,20 +742,24 @@ __device__ __forceinline__ void fmac_bcast(float& acc, float l, float t) {  // a
                  : "+v"(acc) : "v"(l), "v"(t), "i"(M));
 }
 template <int M>
-__device__ __forceinline__ void solve_step(const float (&col)[16], float (&acc)[16], float (&t)[16], int j) {
-    const float tm = M == j ? 1.f : (M > j ? -acc[M] : 0.f);
+__device__ __forceinline__ void solve_step(const float (&col)[16], const float (&f)[16], float (&acc)[16],
+                                           float (&t)[16], int j) {
+    const float tm = M == j ? 1.f : (M > j ? -f[M] * acc[M] : 0.f);
     t[M] = tm;
 #pragma unroll
     for (int i = M + 1; i < 16; ++i) fmac_bcast<M>(acc[i], col[i], tm);
 }
 template <int... Ms>
-__device__ __forceinline__ void solve_steps(const float (&col)[16], float (&acc)[16], float (&t)[16], int j,
-                                            std::integer_sequence<int, Ms...>) {
-    (solve_step<Ms>(col, acc, t, j), ...);
+__device__ __forceinline__ void solve_steps(const float (&col)[16], const float (&f)[16], float (&acc)[16],
+                                            float (&t)[16], int j, std::integer_sequence<int, Ms...>) {
+    (solve_step<Ms>(col, f, acc, t, j), ...);
 }
-__device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, int b0, int lane) {
+__device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, const float* rk, const float* beta, int b0,
+                                           int lane) {
     lane = opaque(lane);
     const int b = b0 + (lane / 16) % 2, j = lane % 16, base = 16 * b;
+    float f[16];  // row factors of the block
+    row_factors<4>(f, rk, beta, base);
     const bf16x8 c0 = *reinterpret_cast<const bf16x8*>(sLt + (base + j) * TSTR + base);
     const bf16x8 c1 = *reinterpret_cast<const bf16x8*>(sLt + (base + j) * TSTR + base + 8);
     float col[16], acc[16], t[16];
@@ -755,7 +776,7 @@ __device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, int b0
                  : "+v"(col[0]), "+v"(col[1]), "+v"(col[2]), "+v"(col[3]), "+v"(col[4]), "+v"(col[5]),
                    "+v"(col[6]), "+v"(col[7]), "+v"(col[8]), "+v"(col[9]), "+v"(col[10]), "+v"(col[11]),
                    "+v"(col[12]), "+v"(col[13]), "+v"(col[14]), "+v"(col[15]));
-    solve_steps(col, acc, t, j, std::make_integer_sequence<int, 16>{});
+    solve_steps(col, f, acc, t, j, std::make_integer_sequence<int, 16>{});
     if (lane < 32) {
         bf16x8 lo, hi;
 #pragma unroll
@@ -768,9 +789,11 @@ __device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, int b0
     }
 }
 
-// Solve level 1: T_{b+1,b} = -T_{b+1,b+1} (L_{b+1,b} T_{b,b}) for the 16x16 block pair (b, b+1).
-// bf16 operands (K = 16 real, padded to 32 with zeros).
-__device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, int b, int lane) {
+// Solve level 1: T_{b+1,b} = -T_{b+1,b+1} (L_{b+1,b} T_{b,b}) for the 16x16 block pair (b, b+1)
+// (L' = diag(f) G_m: the row factor is applied to the first product).  bf16 operands (K = 16 real,
+// padded to 32 with zeros).
+__device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, const float* rk, const float* beta, int b,
+                                             int lane) {
     lane = opaque(lane);
     const int g = lane / 16, l16 = lane % 16;
     const int r0 = 16 * (b + 1), c0 = 16 * b;
@@ -784,7 +807,9 @@ __device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, int 
         a = zb;
         bt = zb;
     }
-    const fx4 y = mfma(a, bt, zero4());
+    float f[4];
+    row_factors<1>(f, rk, beta, r0 + 4 * g);
+    const fx4 y = mfma(a, bt, zero4()) * fx4{f[0], f[1], f[2], f[3]};  // rows r0 + 4g + e
     // T_{b+1,b} = -T_{b+1,b+1} Y: A = rows of T_{b+1,b+1} (chain order, k = 4g+e real), B = Y
     const bf16x4 tr = tr4(Tt, TSTR, r0 + 4 * g, r0, l16);  // T[r0 + l16][r0 + 4g .. +3]
     const bf16x4 z4 = {};
@@ -798,15 +823,21 @@ __device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, int 
     *reinterpret_cast<bf16x4*>(Tt + (c0 + l16) * TSTR + r0 + 4 * g) = out;
 }
 
-// Wave 6: L_BA (rows 32..63, columns 0..31 of L) into the T_BA block of T^T, which the state
-// waves read in its place (U_B = T_BB (X_B - L_BA U_A)).  Both are stored transposed.
-__device__ __forceinline__ void copy_LBA(const __bf16* sLt, __bf16* Tt, int lane) {
+// Wave 6: L'_BA = diag(f) G_m (rows 32..63, columns 0..31) into the T_BA block of T^T, which the
+// state waves read in its place (U'_B = T'_BB (Y_B - L'_BA U'_A)).  Both are stored transposed.
+__device__ __forceinline__ void copy_LBA(const __bf16* sLt, __bf16* Tt, const float* rk, const float* beta, int lane) {
     lane = opaque(lane);
     const int m = lane / 2, c = 32 + 16 * (lane % 2);
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(sLt + m * TSTR + c);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(sLt + m * TSTR + c + 8);
-    *reinterpret_cast<bf16x8*>(Tt + m * TSTR + c) = a;
-    *reinterpret_cast<bf16x8*>(Tt + m * TSTR + c + 8) = b;
+    float f[16];
+    row_factors<4>(f, rk, beta, c);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sLt + m * TSTR + c + 8 * hf);
+        bf16x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (__bf16)((float)a[e] * f[8 * hf + e]);
+        *reinterpret_cast<bf16x8*>(Tt + m * TSTR + c + 8 * hf) = o;
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -825,8 +856,8 @@ __device__ __forceinline__ bf16x8* handoff(unsigned char* sm, int base, int wave
     return reinterpret_cast<bf16x8*>(sm + base + ((wave * nslots + slot) * 64 + lane) * 16);
 }
 
-// Sub-stage A: K S^T, X = beta V - beta Gamma rk K S^T, U = T X blockwise; U goes to the output
-// wave, U scaled for the state update to sub-stage B (both through LDS).
+// Sub-stage A: K S^T, Y = beta rk V - beta Gamma rk^2 K S^T, U' = T' Y blockwise; U' goes to the
+// output wave, U' scaled for the state update to sub-stage B (both through LDS).
 template <int DK>
 __device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
                                         const unsigned char* gb, int wave, int lane) {
@@ -837,8 +868,8 @@ __device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, co
     const __bf16* V = reinterpret_cast<const __bf16*>(raw + S::rV);
     const __bf16* Tt = reinterpret_cast<const __bf16*>(sm + S::T);
     const float* gKK = reinterpret_cast<const float*>(gb + S::gKK);
-    const float* gBETA = reinterpret_cast<const float*>(gb + S::gBETA);
-    const float* gDRK = reinterpret_cast<const float*>(gb + S::gDRK);
+    const float* gVB = reinterpret_cast<const float*>(gb + S::gVB);
+    const float* gDR = reinterpret_cast<const float*>(gb + S::gDR);
     const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
 
     bf16x8 sb[KS];
@@ -863,10 +894,10 @@ __device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, co
     for (int t = 0; t < 4; ++t) {
         const int m0 = 16 * t + 4 * g;
         vv[t] = str4<BV>(V, m0, cbase, l16);  // V[m0 .. +3][cbase + l16]
-        bm[t] = *reinterpret_cast<const fx4*>(gBETA + m0);
+        bm[t] = *reinterpret_cast<const fx4*>(gVB + m0);
         kk[t] = *reinterpret_cast<const fx4*>(gKK + m0);
     }
-    // T blocks: T_AA rows 0..31, L_BA rows 32..63 (k over tokens 0..31), T_BB rows 32..63
+    // T' blocks: T'_AA rows 0..31, L'_BA rows 32..63 (k over tokens 0..31), T'_BB rows 32..63
     const bf16x8 ta0 = frag_tr_chain(Tt, TSTR, 0, 0, g, l16), ta1 = frag_tr_chain(Tt, TSTR, 0, 16, g, l16);
     const bf16x8 la2 = frag_tr_chain(Tt, TSTR, 0, 32, g, l16), la3 = frag_tr_chain(Tt, TSTR, 0, 48, g, l16);
     const bf16x8 tb2 = frag_tr_chain(Tt, TSTR, 32, 32, g, l16), tb3 = frag_tr_chain(Tt, TSTR, 32, 48, g, l16);
@@ -897,7 +928,7 @@ __device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, co
     fx4 ut[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        const fx4 dr = *reinterpret_cast<const fx4*>(gDRK + 16 * it + 4 * g);
+        const fx4 dr = *reinterpret_cast<const fx4*>(gDR + 16 * it + 4 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) ut[it][e] = u[it][e] * dr[e];
     }
@@ -905,7 +936,8 @@ __device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, co
     *handoff(sm, S::UT, wave, 2, 1, lane) = pack_chain(ut[2], ut[3]);
 }
 
-// Sub-stage B: S^T <- Gamma_C S^T + K^T (D U); the new S in bf16 goes to the output wave.
+// Sub-stage B: S^T <- Gamma_C S^T + K^T diag(exp(gamma_C - gamma)) U'; the new S in bf16 goes to
+// the output wave.
 template <int DK>
 __device__ __forceinline__ void state_B(StateRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
                                         const unsigned char* gb, int wave, int lane) {
@@ -961,11 +993,11 @@ __device__ __forceinline__ void out_A(fx4 (&ot)[4], unsigned char* sm, const uns
         for (int t = 0; t < 4; ++t) ot[t] = mfma(sb[ks], qfr[ks][t], ot[t]);  // S Q^T (M = c, N = token)
 }
 
-// Output sub-stage B: O^T = diag(Gamma rq) (S Q^T) + U^T Pm^T, stored (lane: token 16 it + l16,
-// state rows cbase + 4g .. +3).
+// Output sub-stage B: O^T = [diag(Gamma) (S Q^T) + U'^T Pm'^T] diag(rq), stored (lane: token
+// 16 it + l16, state rows cbase + 4g .. +3).
 template <int DK>
-__device__ __forceinline__ void out_B(const Params<DK>& p, fx4 (&ot)[4], unsigned char* sm, int wave, int lane, long t0,
-                                      int len, int h, int vb) {
+__device__ __forceinline__ void out_B(const Params<DK>& p, fx4 (&ot)[4], unsigned char* sm, const unsigned char* gb,
+                                      int wave, int lane, long t0, int len, int h, int vb) {
     lane = opaque(lane);
     using S = Smem<DK>;
     const __bf16* Pm = reinterpret_cast<const __bf16*>(sm + S::PM);
@@ -978,16 +1010,22 @@ __device__ __forceinline__ void out_B(const Params<DK>& p, fx4 (&ot)[4], unsigne
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
             if (s2 == 0 || it >= 2) pf[it][s2] = frag_chain(Pm + (16 * it + l16) * TSTR, 32 * s2, g);
-    float r[4];
+    const float* gam = reinterpret_cast<const float*>(gb + S::gGAM);
+    float r[4], G[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) r[it] = orq[16 * it + l16];
+    for (int it = 0; it < 4; ++it) {
+        r[it] = orq[16 * it + l16];
+        G[it] = gam[16 * it + l16];
+    }
     issue_fence();
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ot[it][e] *= r[it];
+        for (int e = 0; e < 4; ++e) ot[it][e] *= G[it];
         ot[it] = mfma(ub0, pf[it][0], ot[it]);
         if (it >= 2) ot[it] = mfma(ub1, pf[it][1], ot[it]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ot[it][e] *= r[it];
     }
     if (p.out != OUT_STORE) return;
 #pragma unroll
@@ -1116,11 +1154,11 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
             unsigned char* gbk = sm + S::gates(k);
             if (is_state) state_A<DK>(st, sm, rawk, gbk, wid, lane);
             if (is_out) out_A<DK>(ot, sm, rawk, wid - 2, lane);
-            if (pw == 1) prep_P<DK, 0>(rawk, gbk, sm, lane, clen(k), p.l2norm);
-            if (pw == 2) prep_P<DK, 1>(rawk, gbk, sm, lane, clen(k), p.l2norm);
+            if (pw == 1) prep_P<DK, 0>(rawk, sm, lane, clen(k), p.l2norm);
+            if (pw == 2) prep_P<DK, 1>(rawk, sm, lane, clen(k), p.l2norm);
         }
-        if (nxt && pw == 0) prep_L<DK, 0>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, clen(k + 1), p.l2norm);
-        if (nxt && pw == 3) prep_L<DK, 1>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, clen(k + 1), p.l2norm);
+        if (nxt && pw == 0) prep_L<DK, 0>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
+        if (nxt && pw == 3) prep_L<DK, 1>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
         // the loads of chunk k+2 from the output waves, which have slack here (rows 32 (w-2) ..)
         if (far && is_out) {
             dma_chunk<DK>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, vb, 2 * (wid - 2), lane);
@@ -1132,7 +1170,7 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
             unsigned char* rawk = sm + S::raw(k);
             unsigned char* gbk = sm + S::gates(k);
             if (is_state) state_B<DK>(st, sm, rawk, gbk, wid, lane);
-            if (is_out) out_B<DK>(p, ot, sm, wid - 2, lane, tk, clen(k), h, vb);
+            if (is_out) out_B<DK>(p, ot, sm, gbk, wid - 2, lane, tk, clen(k), h, vb);
             if (p.early_exit)
                 decay += __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                                                        int, reinterpret_cast<const float*>(gbk + S::gGC)[1])));
@@ -1142,11 +1180,17 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
             __builtin_amdgcn_s_setprio(3);
             const __bf16* sLt = reinterpret_cast<const __bf16*>(sm + S::L);
             __bf16* Tt = reinterpret_cast<__bf16*>(sm + S::T);
-            solve_diag(sLt, Tt, 2 * pw, lane);
-            solve_level1(sLt, Tt, 2 * pw, lane);
+            const float* rk = reinterpret_cast<const float*>(sm + S::WL);
+            const float* beta = reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB);
+            solve_diag(sLt, Tt, rk, beta, 2 * pw, lane);
+            solve_level1(sLt, Tt, rk, beta, 2 * pw, lane);
             __builtin_amdgcn_s_setprio(0);
         }
-        if (nxt && pw == 2) copy_LBA(reinterpret_cast<const __bf16*>(sm + S::L), reinterpret_cast<__bf16*>(sm + S::T), lane);
+        if (nxt && pw == 2)
+            copy_LBA(reinterpret_cast<const __bf16*>(sm + S::L), reinterpret_cast<__bf16*>(sm + S::T),
+                     reinterpret_cast<const float*>(sm + S::WL), reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB),
+                     lane);
+        if (nxt && pw == 3) make_gates<DK>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
         if (far && is_out) {
             wait_loads();
             zero_tail<DK>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2), lane);
