@@ -14,8 +14,10 @@
  *   and the read-out o_t = scale * S_t q_t.
  *
  *   Optional prologue (page maplevalley.com.cn/news/1910399, section 3.1, 卷积预处理): a
- *   causal depthwise conv1d with 4 taps per channel, zero history before each sequence start,
- *   followed by SiLU(x) = x / (1 + exp(-x)).  Optional L2 normalisation of q and k over the key
+ *   causal depthwise conv1d with 4 taps per channel, followed by SiLU(x) = x / (1 + exp(-x)).
+ *   The three raw inputs before a sequence start come from a given conv history (zeros when
+ *   none is given), and the conv history after the sequence (its last three raw inputs) can be
+ *   returned, so that a sequence can be continued by a later call or by decode steps.  Optional L2 normalisation of q and k over the key
  *   dimension, x / sqrt(sum x^2 + 1e-6) (not on the pages; the eps is this library's reading).
  *
  * Everything is double precision.  Callers pass the exact values the GPU receives, promoted to
@@ -36,7 +38,8 @@
 #include <unistd.h>
 
 typedef struct {
-    const double *q, *k, *v, *g, *beta, *s0, *conv_w;
+    const double *q, *k, *v, *g, *beta, *s0, *conv_w, *hist;
+    double* hist_out;
     const int64_t* cu;
     const unsigned char* mask;
     double *o, *sfin;
@@ -48,15 +51,21 @@ typedef struct {
 
 static double silu(double x) { return x / (1.0 + exp(-x)); }
 
-/* Causal depthwise conv (4 taps, zero history before the sequence start) then SiLU, for one
- * channel of one sequence.  x_t' = SiLU(sum_j w[j] * x_{t-3+j}). */
-static void conv_silu(const double* x, long stride, long len, const double* w, double* out) {
+/* Raw input s of one channel of one sequence, s in [-3, len): tokens of the sequence, or for
+ * s < 0 the history value 3 + s (hist holds the three inputs before the sequence start, oldest
+ * first, at a stride of hstride doubles; NULL = zeros). */
+static double conv_input(const double* x, long stride, const double* hist, long hstride, long s) {
+    if (s >= 0) return x[s * stride];
+    return hist ? hist[(3 + s) * hstride] : 0.0;
+}
+
+/* Causal depthwise conv (4 taps) then SiLU, for one channel of one sequence:
+ * x_t' = SiLU(sum_j w[j] * x_{t-3+j}). */
+static void conv_silu(const double* x, long stride, const double* hist, long hstride, long len, const double* w,
+                      double* out) {
     for (long t = 0; t < len; ++t) {
         double acc = 0.0;
-        for (int j = 0; j < 4; ++j) {
-            long src = t - 3 + j;
-            if (src >= 0) acc += w[j] * x[src * stride];
-        }
+        for (int j = 0; j < 4; ++j) acc += w[j] * conv_input(x, stride, hist, hstride, t - 3 + j);
         out[t] = silu(acc);
     }
 }
@@ -76,24 +85,30 @@ static void run_pair(job_t* J, int n, int h) {
     else
         memset(S, 0, sizeof(double) * (size_t)dv * dk);
 
-    if (J->conv_w && len > 0) {
+    if (J->conv_w) {
+        /* Channel c of the conv: q channels h*dk + i, then k (H*dk + h*dk + i), then v
+         * (2*H*dk + h*dv + i); the history rows of sequence n are [3][C] at n*3*C. */
+        const long C = (long)H * (2 * dk + dv);
+        const double* hist = J->hist ? J->hist + (size_t)n * 3 * C : NULL;
+        double* hout = J->hist_out ? J->hist_out + (size_t)n * 3 * C : NULL;
         /* Pre-compute the conv+SiLU channels of this (sequence, head), token-major. */
-        cq = (double*)malloc(sizeof(double) * (size_t)len * dk);
-        ck = (double*)malloc(sizeof(double) * (size_t)len * dk);
-        cv = (double*)malloc(sizeof(double) * (size_t)len * dv);
-        double* tmp = (double*)malloc(sizeof(double) * (size_t)len);
-        for (int i = 0; i < dk; ++i) {
-            conv_silu(J->q + (bos * H + h) * dk + i, (long)H * dk, len,
-                      J->conv_w + 4 * ((size_t)h * dk + i), tmp);
-            for (long t = 0; t < len; ++t) cq[t * dk + i] = tmp[t];
-            conv_silu(J->k + (bos * H + h) * dk + i, (long)H * dk, len,
-                      J->conv_w + 4 * ((size_t)H * dk + (size_t)h * dk + i), tmp);
-            for (long t = 0; t < len; ++t) ck[t * dk + i] = tmp[t];
-        }
-        for (int i = 0; i < dv; ++i) {
-            conv_silu(J->v + (bos * H + h) * dv + i, (long)H * dv, len,
-                      J->conv_w + 4 * ((size_t)2 * H * dk + (size_t)h * dv + i), tmp);
-            for (long t = 0; t < len; ++t) cv[t * dv + i] = tmp[t];
+        cq = (double*)malloc(sizeof(double) * (size_t)(len + 1) * dk);
+        ck = (double*)malloc(sizeof(double) * (size_t)(len + 1) * dk);
+        cv = (double*)malloc(sizeof(double) * (size_t)(len + 1) * dv);
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)(len + 1));
+        for (int part = 0; part < 3; ++part) {
+            const int d = part < 2 ? dk : dv;
+            const double* x = part == 0 ? J->q : (part == 1 ? J->k : J->v);
+            double* dst = part == 0 ? cq : (part == 1 ? ck : cv);
+            for (int i = 0; i < d; ++i) {
+                const long c = part < 2 ? (long)part * H * dk + (long)h * dk + i : 2L * H * dk + (long)h * dv + i;
+                const double* xc = x + ((size_t)bos * H + h) * d + i;
+                const double* hc = hist ? hist + c : NULL;
+                conv_silu(xc, (long)H * d, hc, C, len, J->conv_w + 4 * c, tmp);
+                for (long t = 0; t < len; ++t) dst[t * d + i] = tmp[t];
+                if (hout) /* the last three raw inputs, oldest first */
+                    for (int j = 0; j < 3; ++j) hout[j * C + c] = conv_input(xc, (long)H * d, hc, C, len - 3 + j);
+            }
         }
         free(tmp);
     }
@@ -166,17 +181,21 @@ static void* worker(void* arg) {
 /*
  * gdn_oracle_forward -- o and final state of the gated delta rule over packed sequences.
  *  q, k [T_tot,H,dk]; v [T_tot,H,dv]; g, beta [T_tot,H]; s0 [N,H,dv,dk] or NULL (zeros);
- *  cu [N+1] int64 offsets; conv_w [H*(2dk+dv),4] or NULL; o [T_tot,H,dv] or NULL;
+ *  cu [N+1] int64 offsets; conv_w [H*(2dk+dv),4] or NULL; conv_hist [N,3,H*(2dk+dv)] or NULL
+ *  (zeros): the raw inputs before each sequence start; conv_hist_out [N,3,H*(2dk+dv)] or NULL:
+ *  the last three raw inputs of each sequence (may not alias conv_hist); o [T_tot,H,dv] or NULL;
  *  sfin [N,H,dv,dk] or NULL; mask [N*H] or NULL: only pairs with mask != 0 are computed (their
- *  o rows and final states are written; others are left untouched).  nthreads <= 0: all cores.
- *  Returns the number of threads used.
+ *  o rows, final states and conv history channels are written; others are left untouched).
+ *  nthreads <= 0: all cores.  Returns the number of threads used.
  */
 int gdn_oracle_forward(const double* q, const double* k, const double* v, const double* g,
                        const double* beta, const double* s0, const int64_t* cu,
-                       const double* conv_w, double* o, double* sfin, const unsigned char* mask,
-                       int N, int H, int dk, int dv, double scale, int l2norm, int nthreads) {
+                       const double* conv_w, const double* conv_hist, double* conv_hist_out, double* o,
+                       double* sfin, const unsigned char* mask, int N, int H, int dk, int dv, double scale,
+                       int l2norm, int nthreads) {
     job_t J;
     J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.s0 = s0; J.conv_w = conv_w;
+    J.hist = conv_hist; J.hist_out = conv_hist_out;
     J.cu = cu; J.mask = mask; J.o = o; J.sfin = sfin;
     J.N = N; J.H = H; J.dk = dk; J.dv = dv; J.l2norm = l2norm; J.scale = scale;
     J.next_pair = 0;
@@ -195,17 +214,26 @@ int gdn_oracle_forward(const double* q, const double* k, const double* v, const 
 
 /*
  * gdn_oracle_step -- one decode token per sequence (the same update with T = 1), state
- * updated in place.  q, k [N,H,dk]; v [N,H,dv]; g, beta [N,H]; state [N,H,dv,dk]; o [N,H,dv].
+ * updated in place.  q, k [N,H,dk]; v [N,H,dv]; g, beta [N,H]; state [N,H,dv,dk]; o [N,H,dv];
+ * conv_w [H*(2dk+dv),4] or NULL; conv_hist [N,3,H*(2dk+dv)] (with conv_w): the three previous
+ * raw inputs, read and replaced by the three latest.
  * Page pzsr.cn/news/750, section a、增量更新: decay the whole state first, then erase and write
  * along the current key.
  */
 int gdn_oracle_step(const double* q, const double* k, const double* v, const double* g,
-                    const double* beta, double* state, double* o, int N, int H, int dk, int dv,
-                    double scale, int l2norm, int nthreads) {
+                    const double* beta, const double* conv_w, double* conv_hist, double* state, double* o,
+                    int N, int H, int dk, int dv, double scale, int l2norm, int nthreads) {
     int64_t* cu = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N + 1));
     for (int n = 0; n <= N; ++n) cu[n] = n;
-    int used = gdn_oracle_forward(q, k, v, g, beta, state, cu, NULL, o, state, NULL, N, H, dk,
-                                  dv, scale, l2norm, nthreads);
+    double* hout = NULL;
+    const size_t hn = (size_t)N * 3 * H * (2 * dk + dv);
+    if (conv_w) hout = (double*)malloc(sizeof(double) * hn);
+    int used = gdn_oracle_forward(q, k, v, g, beta, state, cu, conv_w, conv_hist, hout, o, state, NULL, N, H,
+                                  dk, dv, scale, l2norm, nthreads);
+    if (conv_w) {
+        memcpy(conv_hist, hout, sizeof(double) * hn);
+        free(hout);
+    }
     free(cu);
     return used;
 }

@@ -387,3 +387,105 @@ def test_gates_formula():
     np.testing.assert_allclose(g[0], -np.exp(A_log) * np.logaddexp(0, a[0] + dt), rtol=1e-15)
     np.testing.assert_allclose(g[0, 2], -16 * math.exp(-50), rtol=1e-14)
     np.testing.assert_allclose(beta[0], 1 / (1 + np.exp(-b[0])), rtol=1e-15)
+
+
+def _raw_rows(q, k, v):
+    """Token rows of the conv channels in the order [q heads, k heads, v heads]."""
+    T = q.shape[0]
+    return np.concatenate([q.reshape(T, -1), k.reshape(T, -1), v.reshape(T, -1)], 1)
+
+
+def test_conv_history_matches_numpy_convolve():
+    """A given conv history acts as the three raw tokens before the sequence: the read-back of
+    the conv+SiLU output of v (alpha = 0, beta = 1, q = k) equals numpy.convolve over the
+    history followed by the sequence, with the history positions dropped."""
+    r = rnd(18)
+    lengths = [5, 2, 7]
+    H, dk, dv = 2, 4, 3
+    T = sum(lengths)
+    C = H * (2 * dk + dv)
+    x = r.standard_normal((T, H, dk))
+    v = r.standard_normal((T, H, dv))
+    wq = r.normal(0, 0.5, size=(H * dk, 4))
+    wv = r.normal(0, 0.5, size=(H * dv, 4))
+    conv_w = np.concatenate([wq, wq, wv])
+    hist = r.standard_normal((3, 3, C))
+    hist[:, :, H * dk:2 * H * dk] = hist[:, :, :H * dk]   # k history = q history (q = k)
+    cu = np.array([0, 5, 7, 14])
+    o, sf, _ = oracle.forward(x, x, v, np.full((T, H), -1000.0), np.ones((T, H)), None, cu, conv_w,
+                              conv_hist=hist)
+    for n in range(3):
+        a, b = cu[n], cu[n + 1]
+        for h in range(H):
+            kcols = [np.concatenate([hist[n, :, h * dk + i], x[a:b, h, i]]) for i in range(dk)]
+            vcols = [np.concatenate([hist[n, :, 2 * H * dk + h * dv + i], v[a:b, h, i]]) for i in range(dv)]
+            kp = np.stack([_conv_ref(c, wq[h * dk + i])[3:] for i, c in enumerate(kcols)], 1)
+            vp = np.stack([_conv_ref(c, wv[h * dv + i])[3:] for i, c in enumerate(vcols)], 1)
+            n2 = (kp * kp).sum(1)
+            np.testing.assert_allclose(o[a:b, h], vp * (n2 / (n2 + 1e-6))[:, None], rtol=1e-12,
+                                       atol=1e-15)
+
+
+def test_conv_history_out_is_last_three_raw_tokens():
+    """The history after a sequence is, by definition, its last three raw inputs, continued from
+    the history before it when the sequence is shorter than three (zero length keeps it)."""
+    r = rnd(19)
+    lengths = [0, 1, 2, 3, 6]
+    H, dk, dv = 2, 4, 2
+    q, k, v, g, beta, s0, cu = _pack(r, lengths, H, dk, dv)
+    C = H * (2 * dk + dv)
+    conv_w = r.normal(0, 0.5, size=(C, 4))
+    hist = r.standard_normal((len(lengths), 3, C))
+    _, _, _, hout = oracle.forward(q, k, v, g, beta, s0, cu, conv_w, conv_hist=hist,
+                                   want_conv_hist=True)
+    raw = _raw_rows(q, k, v)
+    for n in range(len(lengths)):
+        seq = np.concatenate([hist[n], raw[cu[n]:cu[n + 1]]])
+        np.testing.assert_array_equal(hout[n], seq[-3:])
+    # without a history the rows before the sequence are zeros
+    _, _, _, hz = oracle.forward(q, k, v, g, beta, s0, cu, conv_w, want_conv_hist=True)
+    np.testing.assert_array_equal(hz[1], np.concatenate([np.zeros((2, C)), raw[0:1]]))
+
+
+def test_conv_split_and_resume():
+    """One sequence run whole equals its first part followed by the rest, the second part given
+    the state and the conv history the first one left (split points inside the conv window)."""
+    r = rnd(20)
+    H, dk, dv = 2, 8, 4
+    q, k, v, g, beta, s0, _ = _pack(r, [40], H, dk, dv)
+    conv_w = r.normal(0, 0.5, size=(H * (2 * dk + dv), 4))
+    o, sf, _, hf = oracle.forward(q, k, v, g, beta, s0, None, conv_w, N=1, want_conv_hist=True)
+    for cut in (1, 2, 17):
+        o1, s1, _, h1 = oracle.forward(q[:cut], k[:cut], v[:cut], g[:cut], beta[:cut], s0, None,
+                                       conv_w, N=1, want_conv_hist=True)
+        o2, s2, _, h2 = oracle.forward(q[cut:], k[cut:], v[cut:], g[cut:], beta[cut:], s1, None,
+                                       conv_w, N=1, conv_hist=h1, want_conv_hist=True)
+        np.testing.assert_array_equal(o[:cut], o1)
+        np.testing.assert_array_equal(o[cut:], o2)
+        np.testing.assert_array_equal(sf, s2)
+        np.testing.assert_array_equal(hf, h2)
+
+
+def test_step_with_conv_is_forward_last_token():
+    """A decode step with conv, given the state and history after T - 1 tokens, reproduces the
+    last token of the whole-sequence forward pass, and its history equals the forward pass's."""
+    r = rnd(21)
+    lengths = [9, 4, 12]
+    H, dk, dv = 2, 8, 4
+    q, k, v, g, beta, s0, cu = _pack(r, lengths, H, dk, dv)
+    C = H * (2 * dk + dv)
+    conv_w = r.normal(0, 0.5, size=(C, 4))
+    hist = r.standard_normal((3, 3, C))
+    o, sf, _, hf = oracle.forward(q, k, v, g, beta, s0, cu, conv_w, conv_hist=hist,
+                                  want_conv_hist=True)
+    last = cu[1:] - 1
+    keep = np.ones(cu[-1], bool)
+    keep[last] = False
+    cu_head = cu - np.arange(len(cu))
+    _, s_h, _, h_h = oracle.forward(q[keep], k[keep], v[keep], g[keep], beta[keep], s0, cu_head,
+                                    conv_w, conv_hist=hist, want_conv_hist=True)
+    o_s, s_s, h_s = oracle.step(q[last], k[last], v[last], g[last], beta[last], s_h,
+                                conv_w=conv_w, conv_hist=h_h)
+    np.testing.assert_array_equal(o_s, o[last])
+    np.testing.assert_array_equal(s_s, sf)
+    np.testing.assert_array_equal(h_s, hf)
