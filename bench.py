@@ -11,7 +11,8 @@ The JSON line reports prefill tokens/s as `value`, the HBM roofline of the prefi
 MFMA fraction under algorithmic flop accounting, the decode step (256 sequences x 32 heads, state
 updated in place) as GB/s against HBM, the long-sequence prefill (1 x 262144 tokens, 16 heads,
 segmented) and the packed variable-length prefill with the conv prologue (64 sequences of
-512..16384 tokens, 32 heads) as tokens/s and GB/s, and the fp64 CPU oracle's throughput on the
+512..16384 tokens, 32 heads) as tokens/s and GB/s, the prefill step with raw gate inputs, the
+decode step with the conv prologue and a conv state, and the fp64 CPU oracle's throughput on the
 host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
@@ -204,6 +205,33 @@ def main():
             "hbm_alg_gbs": vbytes / vsec / 1e9, "hbm_frac": vbytes / vsec / 1e9 / HBM_PEAK_GBS}
         del vq, vk, vv, vg, vb, vs0, vcu, vcw, vo, vsf, vw
         torch.cuda.empty_cache()
+
+        # the prefill step again, the gates formed in the kernel from the raw a, b, A_log, dt_bias
+        ra, rb, rgp = (to_dev(x) for x in W.raw_gate_inputs(wl.meta["seed"], wl.lengths, H))
+        q, k, v, _, _, s0 = copies[0]
+        o, sf = outs[0]
+        rsec = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, ra, rb, s0, N=N, o=o, final_state=sf, gate_params=rgp,
+                                               stream=stream), 20)
+        extra["prefill_raw_gates"] = {
+            "workload": "prefill B=4 T=4096 H=16 dk=dv=128 bf16, raw gate inputs a, b [T,H] fp32 + A_log, dt_bias [H]",
+            "value": tokens / rsec, "unit": "tokens/s", "us": rsec * 1e6,
+            "hbm_alg_gbs": alg_bytes / rsec / 1e9, "hbm_frac": alg_bytes / rsec / 1e9 / HBM_PEAK_GBS}
+        del ra, rb, rgp
+
+        # the decode step with the conv prologue on the raw token (history in a conv state updated in
+        # place) and raw gates: the decode side of a layer whose prefill ran the conv
+        cw, hist = W.conv_inputs(3, dw.N, dw.H, dw.dk, dw.dv, "bf16")
+        dcw, dcs = to_dev(cw), to_dev(hist)
+        da, dbr, dgp = (to_dev(x) for x in W.raw_gate_inputs(3, np.ones(dw.N, np.int64), dw.H))
+        csec = timed(lambda: gdn.gdn_recurrent_step(dq, dk_, dv_, da, dbr, st, o=od, gate_params=dgp, conv_w=dcw,
+                                                    conv_state=dcs, stream=stream), 20)
+        cbytes = dec_bytes + dw.N * 2 * 3 * dw.H * (2 * dw.dk + dw.dv) * 2 + dw.H * (2 * dw.dk + dw.dv) * 16
+        extra["decode_conv"] = {
+            "workload": "decode 256 sequences x 32 heads, dk=dv=128, raw bf16 token -> conv(4)+SiLU with a bf16 conv "
+                        "state updated in place, raw gates, fp32 state in place",
+            "value": cbytes / csec / 1e9, "unit": "GB/s", "us_per_step": csec * 1e6,
+            "hbm_frac": cbytes / csec / 1e9 / HBM_PEAK_GBS}
+        del dcw, dcs, da, dbr, dgp
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None

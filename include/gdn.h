@@ -11,9 +11,25 @@
  * with alpha_t = exp(g_t).  The equivalent form every kernel evaluates is
  *     u_t = beta_t (v_t - alpha_t S_{t-1} k_t),   S_t = alpha_t S_{t-1} + u_t k_t^T.
  * The page maplevalley.com.cn/news/1910399, section 2.1 (门控机制的精准控制), gives the gate
- * parameterisation g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b); the caller passes
- * g and beta.  With GDN_QK_L2NORM, q and k are replaced by x * rsqrt(sum(x^2) + 1e-6) over the
- * key dimension, per (token, head), inside the kernels.
+ * parameterisation g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b).  The caller passes
+ * either g and beta, or (with gate_params) the raw a and b, which the kernels turn into g and beta
+ * as they load them ("Raw gates" below).  With GDN_QK_L2NORM, q and k are replaced by
+ * x * rsqrt(sum(x^2) + 1e-6) over the key dimension, per (token, head), inside the kernels.
+ *
+ * Raw gates (both entry points).  gate_params = NULL: g and beta are the log decay and the write
+ * strength.  gate_params = [2, H] fp32, row 0 = A_log, row 1 = dt_bias: g holds the raw a and beta
+ * the raw b (same shapes, fp32), and every use computes
+ *     g = -exp(A_log[h]) * softplus(a + dt_bias[h]),   beta = 1 / (1 + exp(-b))
+ * in fp32, softplus(x) = max(x, 0) + log1p(exp(-|x|)) (no threshold).  The inputs are not modified.
+ *
+ * Conv state (both entry points).  conv_state [N, 3, H*(2*dk + dv)] dtype holds, per sequence, the
+ * three raw inputs (before conv) that precede its next token, oldest first, in the channel order of
+ * conv_w.  It makes the conv prologue continue across calls: a prefill reads it as the history
+ * before each sequence start instead of zeros, and both entry points overwrite it in place with the
+ * three raw inputs before the token that would come next (for a sequence shorter than three tokens
+ * the newest entries of the old state move down; a zero-length sequence keeps it).  The values are
+ * stored in the input dtype exactly, so a prefill split at any point and resumed, or followed by
+ * decode steps, sees the same conv inputs as one call over the whole sequence.
  *
  * Conventions shared by every entry point
  *  - All pointers are DEVICE pointers to contiguous, row-major memory, 16-byte aligned, except
@@ -68,8 +84,10 @@ extern "C" {
  * Arguments (T_tot = total tokens of all sequences, packed back to back):
  *  q, k        [T_tot, H, dk]  dtype   raw queries / keys (before conv, before L2 norm)
  *  v           [T_tot, H, dv]  dtype   raw values
- *  g           [T_tot, H]      fp32    log decay, alpha = exp(g); g <= 0 expected (any finite g works)
- *  beta        [T_tot, H]      fp32    write strength
+ *  g           [T_tot, H]      fp32    log decay, alpha = exp(g); g <= 0 expected (any finite g
+ *                                      works); with gate_params: the raw a
+ *  beta        [T_tot, H]      fp32    write strength; with gate_params: the raw b
+ *  gate_params [2, H]          fp32    NULL, or A_log and dt_bias ("Raw gates" above)
  *  initial_state [N, H, dv, dk] fp32   S_0 per (sequence, head), S as in o = S q; NULL = zeros
  *  cu_seqlens  [N + 1]         int32   sequence offsets into the packed token axis, non-decreasing,
  *                                      cu_seqlens[0] = 0, cu_seqlens[N] = T_tot; NULL = N equal
@@ -81,7 +99,10 @@ extern "C" {
  *                                      Channel c < H*dk is q channel (h*dk + i), the next H*dk are
  *                                      k channels, the last H*dv are v channels.  Tap j multiplies
  *                                      token t-3+j (tap 3 = current token); history before a
- *                                      sequence start is zero; no bias.
+ *                                      sequence start is conv_state, else zero; no bias.
+ *  conv_state  [N, 3, H*(2*dk + dv)] dtype  NULL, or the conv history, read and overwritten in
+ *                                      place ("Conv state" above); requires conv_w.  Must not
+ *                                      overlap any other buffer.
  *  o           [T_tot, H, dv]  dtype   output; must not alias any input
  *  final_state [N, H, dv, dk] fp32     last state per (sequence, head), or NULL = not written.
  *                                      May alias initial_state exactly (same pointer).
@@ -114,8 +135,9 @@ extern "C" {
  * compute units, with at least 16 chunks per segment.
  */
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                  const float* initial_state, const int32_t* cu_seqlens, const float* conv_w,
-                  void* o, float* final_state, void* workspace, size_t* workspace_bytes, int N,
+                  const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,
+                  const float* conv_w, void* conv_state, void* o, float* final_state,
+                  void* workspace, size_t* workspace_bytes, int N,
                   int T_tot, int H, int dk, int dv, int dtype, int chunk, float scale,
                   unsigned flags, void* hip_stream);
 
@@ -137,14 +159,21 @@ int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype,
  * current key with strength beta), which is the rule above with T = 1:
  *     u = beta (v - alpha S k),  S <- alpha S + u k^T,  o = scale * S q.
  *
- *  q, k   [N, H, dk] dtype;  v [N, H, dv] dtype;  g, beta [N, H] fp32
+ *  q, k   [N, H, dk] dtype;  v [N, H, dv] dtype;  g, beta [N, H] fp32 (raw a, b with
+ *         gate_params)
+ *  gate_params [2, H] fp32 or NULL, as for gdn_chunk_fwd
  *  state  [N, H, dv, dk] fp32, read and overwritten in place
+ *  conv_w [H*(2*dk + dv), 4] fp32 and conv_state [N, 3, H*(2*dk + dv)] dtype: both NULL, or both
+ *         given: then q, k and v are the raw inputs of the conv prologue, conv + SiLU (and the L2
+ *         norm) run on them with the three previous raw inputs from conv_state, and conv_state is
+ *         shifted in place by one token (the oldest dropped, this token's raw inputs appended)
  *  o      [N, H, dv] dtype, must not alias any input
  *  N, H >= 1 (N = 0 is a no-op returning GDN_OK); dk, dv in {32, 64, 128}
  *  dtype, scale, flags, hip_stream as for gdn_chunk_fwd
  */
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
-                       const float* beta, float* state, void* o, int N, int H, int dk, int dv,
+                       const float* beta, const float* gate_params, float* state,
+                       const float* conv_w, void* conv_state, void* o, int N, int H, int dk, int dv,
                        int dtype, float scale, unsigned flags, void* hip_stream);
 
 /* gdn_status_string -- static, human-readable name of a status code (never NULL). */

@@ -79,16 +79,18 @@ int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype,
 }
 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                  const float* initial_state, const int32_t* cu_seqlens, const float* conv_w, void* o,
-                  float* final_state, void* workspace, size_t* workspace_bytes, int N, int T_tot, int H, int dk,
-                  int dv, int dtype, int chunk, float scale, unsigned flags, void* hip_stream) {
+                  const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,
+                  const float* conv_w, void* conv_state, void* o, float* final_state, void* workspace,
+                  size_t* workspace_bytes, int N, int T_tot, int H, int dk, int dv, int dtype, int chunk, float scale,
+                  unsigned flags, void* hip_stream) {
     if (N < 1 || T_tot < 0) return GDN_ERR_INVALID_ARG;
     int st = check_common(H, dk, dv, dtype, scale, flags);
     if (st != GDN_OK) return st;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (!cu_seqlens && T_tot % N != 0) return GDN_ERR_INVALID_ARG;
     if (T_tot > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_INVALID_ARG;
-    const void* ptrs[] = {q, k, v, g, beta, initial_state, cu_seqlens, conv_w, o, final_state};
+    if (conv_state && !conv_w) return GDN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, gate_params, initial_state, cu_seqlens, conv_w, conv_state, o, final_state};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
 
@@ -96,16 +98,26 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     const size_t tq = (size_t)T_tot * H * dk * es, tv = (size_t)T_tot * H * dv * es;
     const size_t tg = (size_t)T_tot * H * 4, ts = (size_t)N * H * dv * dk * 4;
     const size_t tcu = cu_seqlens ? (size_t)(N + 1) * 4 : 0, tcw = conv_w ? (size_t)H * (2 * dk + dv) * 16 : 0;
+    const size_t tgp = gate_params ? (size_t)H * 8 : 0;
+    const size_t tcs = conv_state ? (size_t)N * 3 * H * (2 * dk + dv) * es : 0;
     // o must not overlap any input; final_state may equal initial_state exactly but not overlap otherwise.
     if (overlaps(o, tv, q, tq) || overlaps(o, tv, k, tq) || overlaps(o, tv, v, tv) || overlaps(o, tv, g, tg) ||
         overlaps(o, tv, beta, tg) || overlaps(o, tv, initial_state, ts) || overlaps(o, tv, final_state, ts) ||
-        overlaps(o, tv, cu_seqlens, tcu) || overlaps(o, tv, conv_w, tcw))
+        overlaps(o, tv, cu_seqlens, tcu) || overlaps(o, tv, conv_w, tcw) || overlaps(o, tv, gate_params, tgp) ||
+        overlaps(o, tv, conv_state, tcs))
         return GDN_ERR_INVALID_ARG;
     if (final_state && final_state != initial_state &&
         (overlaps(final_state, ts, initial_state, ts) || overlaps(final_state, ts, q, tq) ||
          overlaps(final_state, ts, k, tq) || overlaps(final_state, ts, v, tv) || overlaps(final_state, ts, g, tg) ||
          overlaps(final_state, ts, beta, tg) || overlaps(final_state, ts, cu_seqlens, tcu) ||
-         overlaps(final_state, ts, conv_w, tcw)))
+         overlaps(final_state, ts, conv_w, tcw) || overlaps(final_state, ts, gate_params, tgp)))
+        return GDN_ERR_INVALID_ARG;
+    // conv_state is written in place: it may share memory with nothing else.
+    if (overlaps(conv_state, tcs, q, tq) || overlaps(conv_state, tcs, k, tq) || overlaps(conv_state, tcs, v, tv) ||
+        overlaps(conv_state, tcs, g, tg) || overlaps(conv_state, tcs, beta, tg) ||
+        overlaps(conv_state, tcs, gate_params, tgp) || overlaps(conv_state, tcs, initial_state, ts) ||
+        overlaps(conv_state, tcs, final_state, ts) || overlaps(conv_state, tcs, cu_seqlens, tcu) ||
+        overlaps(conv_state, tcs, conv_w, tcw))
         return GDN_ERR_INVALID_ARG;
 
     int P = 1;
@@ -124,7 +136,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
             overlaps(workspace, tw, g, tg) || overlaps(workspace, tw, beta, tg) ||
             overlaps(workspace, tw, initial_state, ts) || overlaps(workspace, tw, final_state, ts) ||
             overlaps(workspace, tw, o, tv) || overlaps(workspace, tw, cu_seqlens, tcu) ||
-            overlaps(workspace, tw, conv_w, tcw))
+            overlaps(workspace, tw, conv_w, tcw) || overlaps(workspace, tw, gate_params, tgp) ||
+            overlaps(workspace, tw, conv_state, tcs))
             return GDN_ERR_INVALID_ARG;
     }
 
@@ -134,9 +147,11 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     a.v = v;
     a.g = g;
     a.beta = beta;
+    a.gate_params = gate_params;
     a.s0 = initial_state;
     a.cu = cu_seqlens;
     a.conv_w = conv_w;
+    a.conv_state = conv_state;
     a.o = o;
     a.sfin = final_state;
     a.workspace = workspace;
@@ -151,36 +166,46 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     a.l2norm = (flags & GDN_QK_L2NORM) ? 1 : 0;
     a.segments = P;
     a.stream = static_cast<hipStream_t>(hip_stream);
-    const hipError_t e = a.bf16 ? gdn::launch_chunk_bf16(a) : gdn::launch_chunk_f32(a);
+    hipError_t e = a.bf16 ? gdn::launch_chunk_bf16(a) : gdn::launch_chunk_f32(a);
+    if (e == hipSuccess && conv_state) e = gdn::launch_conv_state_update(a);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta, float* state,
-                       void* o, int N, int H, int dk, int dv, int dtype, float scale, unsigned flags,
-                       void* hip_stream) {
+int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const float* gate_params, float* state, const float* conv_w, void* conv_state, void* o, int N,
+                       int H, int dk, int dv, int dtype, float scale, unsigned flags, void* hip_stream) {
     if (N < 0 || (flags & kSegMask)) return GDN_ERR_INVALID_ARG;
     int st = check_common(H, dk, dv, dtype, scale, flags);
     if (st != GDN_OK) return st;
     if (N == 0) return GDN_OK;
     if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_INVALID_ARG;
-    const void* ptrs[] = {q, k, v, g, beta, state, o};
+    if ((conv_w == nullptr) != (conv_state == nullptr)) return GDN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, gate_params, state, conv_w, conv_state, o};
     for (const void* p : ptrs)
-        if (!aligned16(p)) return GDN_ERR_INVALID_ARG;
+        if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
     const size_t es = dtype == GDN_BF16 ? 2 : 4;
     const size_t tq = (size_t)N * H * dk * es, tv = (size_t)N * H * dv * es, tg = (size_t)N * H * 4;
-    const size_t ts = (size_t)N * H * dv * dk * 4;
-    if (overlaps(o, tv, q, tq) || overlaps(o, tv, k, tq) || overlaps(o, tv, v, tv) || overlaps(o, tv, g, tg) ||
-        overlaps(o, tv, beta, tg) || overlaps(o, tv, state, ts) || overlaps(state, ts, q, tq) ||
-        overlaps(state, ts, k, tq) || overlaps(state, ts, v, tv) || overlaps(state, ts, g, tg) ||
-        overlaps(state, ts, beta, tg))
-        return GDN_ERR_INVALID_ARG;
+    const size_t ts = (size_t)N * H * dv * dk * 4, tgp = gate_params ? (size_t)H * 8 : 0;
+    const size_t tcw = conv_w ? (size_t)H * (2 * dk + dv) * 16 : 0;
+    const size_t tcs = conv_state ? (size_t)N * 3 * H * (2 * dk + dv) * es : 0;
+    // o, state and conv_state are written: none of them may share memory with another buffer.
+    const void* bufs[] = {q, k, v, g, beta, gate_params, state, conv_w, conv_state, o};
+    const size_t lens[] = {tq, tq, tv, tg, tg, tgp, ts, tcw, tcs, tv};
+    for (int w = 6; w < 10; ++w) {
+        if (w == 7) continue;  // conv_w is read only
+        for (int i = 0; i < 10; ++i)
+            if (i != w && overlaps(bufs[w], lens[w], bufs[i], lens[i])) return GDN_ERR_INVALID_ARG;
+    }
     gdn::StepArgs a;
     a.q = q;
     a.k = k;
     a.v = v;
     a.g = g;
     a.beta = beta;
+    a.gate_params = gate_params;
     a.state = state;
+    a.conv_w = conv_w;
+    a.conv_state = conv_state;
     a.o = o;
     a.N = N;
     a.H = H;

@@ -225,6 +225,8 @@ template <int DK>
 struct Params {
     const __bf16 *q, *k, *v;
     const float *g, *beta, *s0, *conv_w;
+    const float* gate_params;  // [2, H]: g and beta hold the raw a and b; or null
+    const __bf16* conv_state;  // [N, 3, H (2 DK + dv)]: conv history before each sequence; or null
     const int32_t* cu;
     __bf16* o;
     float* sfin;   // end state per (segment, head): [N*P, H, dv, dk]
@@ -334,6 +336,19 @@ __device__ __forceinline__ void zero_tail(unsigned char* raw, int len, int wid, 
     if (wid < 2 && lane >= len) reinterpret_cast<float*>(raw + (wid == 0 ? S::rG : S::rB))[lane] = 0.f;
 }
 
+// After this wave's loads landed: with raw gates, turn the raw a (part 0) and b (part 1) of the
+// chunk's valid rows into g and beta in place, before anything reads them.
+template <int DK>
+__device__ __forceinline__ void raw_gates(const Params<DK>& p, unsigned char* raw, int len, int part, int lane, int h) {
+    using S = Smem<DK>;
+    if (part >= 2) return;
+    float* x = reinterpret_cast<float*>(raw + (part == 0 ? S::rG : S::rB));
+    if (lane < len) {
+        const float a = x[lane];
+        x[lane] = part == 0 ? raw_decay(a, -expf(p.gate_params[h]), p.gate_params[p.H + h]) : raw_beta(a);
+    }
+}
+
 __device__ __forceinline__ void wait_loads() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's global->LDS loads have landed
 }
@@ -351,8 +366,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ------------------------------------------------------------------------------------------
 // Conv prologue (page maplevalley.com.cn/news/1910399, section 3.1, 卷积预处理): a depthwise causal
-// conv over 4 tokens (tap 3 = current token, zero history before the sequence start) and SiLU on
-// every q, k and v channel, in place in the chunk's LDS tiles once all of its loads have landed.
+// conv over 4 tokens (tap 3 = current token; before the sequence start the given conv history, else
+// zeros) and SiLU on every q, k and v channel, in place in the chunk's LDS tiles once all of its
+// loads have landed.
 // Work item = (channel pair, block of 8 rows), taken in turn by all 512 lanes.  An item first
 // reads its 8 raw rows and the 3 raw rows before them (from the tile, or for the first block from
 // the halo buffer that keeps the previous chunk's last 3 raw rows); after a barrier -- no raw row
@@ -403,25 +419,35 @@ __device__ __forceinline__ int pair_wrow(const Params<DK>& p, int pc, int h, int
     return 2 * p.H * DK + h * p.dv + vb * BV + 2 * (pc - DK);
 }
 
-// Halo before the first chunk: zero at a sequence start; the three previous raw tokens when a
-// segment starts inside a sequence.  Layout [3 rows][NP pairs] of 4-byte words, oldest row first.
+// Halo before the first chunk, by `from`: HALO_ZERO; HALO_TOKENS, the three raw tokens before bos
+// (a segment that starts inside a sequence); HALO_STATE, the conv history of sequence n (a sequence
+// start with conv_state).  Layout [3 rows][NP pairs] of 4-byte words, oldest row first.
+enum HaloFrom { HALO_ZERO = 0, HALO_TOKENS = 1, HALO_STATE = 2 };
 template <int DK>
-__device__ void conv_halo_init(const Params<DK>& p, unsigned halo, int tid, int h, int vb, long bos, bool history) {
+__device__ void conv_halo_init(const Params<DK>& p, unsigned halo, int tid, int n, int h, int vb, long bos,
+                               int from) {
     constexpr int NP = ConvPlan<DK>::NP;
+    const size_t CC = (size_t)p.H * (2 * DK + p.dv);  // conv channels per token
     for (int i = tid; i < 3 * NP; i += 512) {
         const int j = i / NP, pc = i % NP;
         uint32_t v = 0;
-        if (history && !(pc >= DK && p.v_zero)) {
-            const __bf16* src;
-            int width, col;
-            if (pc < DK / 2) {
-                src = p.k, width = DK, col = h * DK + 2 * pc;
-            } else if (pc < DK) {
-                src = p.q, width = DK, col = h * DK + 2 * (pc - DK / 2);
+        const bool isv = pc >= DK, isq = !isv && pc >= DK / 2;
+        if (from != HALO_ZERO && !(isv && p.v_zero)) {
+            // one load per source tensor (no selected pointer, which the compiler would keep in memory)
+            const int c2 = 2 * (isv ? pc - DK : (isq ? pc - DK / 2 : pc));  // channel within the head's block
+            if (from == HALO_STATE) {
+                const size_t hc = isv ? (size_t)2 * p.H * DK + h * p.dv + vb * BV + c2
+                                      : (isq ? (size_t)h * DK + c2 : (size_t)(p.H + h) * DK + c2);
+                v = *reinterpret_cast<const uint32_t*>(p.conv_state + ((size_t)n * 3 + j) * CC + hc);
             } else {
-                src = p.v, width = p.dv, col = h * p.dv + vb * BV + 2 * (pc - DK);
+                const size_t t = (size_t)(bos - 3 + j);
+                if (isv)
+                    v = *reinterpret_cast<const uint32_t*>(p.v + (t * p.H + h) * p.dv + vb * BV + c2);
+                else if (isq)
+                    v = *reinterpret_cast<const uint32_t*>(p.q + (t * p.H + h) * DK + c2);
+                else
+                    v = *reinterpret_cast<const uint32_t*>(p.k + (t * p.H + h) * DK + c2);
             }
-            v = *reinterpret_cast<const uint32_t*>(src + (size_t)(bos - 3 + j) * p.H * width + col);
         }
         st32(halo + 4u * (j * NP + pc), v);
     }
@@ -1045,7 +1071,9 @@ __device__ __forceinline__ void out_B(const Params<DK>& p, fx4 (&ot)[4], unsigne
 // state carried in, its remaining contribution is far under fp32 rounding.
 constexpr float kExitLog = -27.7258872f;
 
-template <int DK>
+// RAW: g and beta hold the raw gate inputs (a separate instantiation, so that the plain one carries
+// no trace of the gate transform).
+template <int DK, bool RAW>
 __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     using S = Smem<DK>;
     extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
@@ -1131,11 +1159,13 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     ConvW<DK> cw;
     if (conv) {
         conv_weights<DK>(cw, p, tid, h, vb);
-        conv_halo_init<DK>(p, smb + S::HB, tid, h, vb, bos, seg > 0 && nchunks > 0);
+        const int from = seg > 0 ? (nchunks > 0 ? HALO_TOKENS : HALO_ZERO) : (p.conv_state ? HALO_STATE : HALO_ZERO);
+        conv_halo_init<DK>(p, smb + S::HB, tid, n, h, vb, bos, from);
     }
     if (nchunks > 0 && is_prep) {
         dma_chunk<DK>(p, smb, S::raw(0), bos, clen(0), h, vb, pw, lane);
         wait_loads();
+        if constexpr (RAW) raw_gates<DK>(p, sm + S::raw(0), clen(0), pw, lane, h);
         zero_tail<DK>(sm + S::raw(0), clen(0), pw, lane);
     }
     lds_barrier();
@@ -1193,6 +1223,10 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
         if (nxt && pw == 3) make_gates<DK>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
         if (far && is_out) {
             wait_loads();
+            if (RAW && wid == 2) {
+                raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 0, lane, h);
+                raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 1, lane, h);
+            }
             zero_tail<DK>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2), lane);
             zero_tail<DK>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2) + 1, lane);
         }
@@ -1234,6 +1268,8 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     p.beta = a.beta;
     p.s0 = c.s0;
     p.conv_w = a.conv_w;
+    p.gate_params = a.gate_params;
+    p.conv_state = static_cast<const __bf16*>(a.conv_state);
     p.cu = a.cu;
     p.o = static_cast<__bf16*>(a.o);
     p.sfin = c.sfin;
@@ -1257,11 +1293,15 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (e != hipSuccess) return e;
     if (lds_max < smem) return hipErrorInvalidConfiguration;  // needs the 160 KiB LDS of gfx950
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_bf16_kernel<DK>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    const void* fn = a.gate_params ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, true>)
+                                   : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, false>);
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     const int grid = a.N * c.P * a.H * p.nv;
-    hipLaunchKernelGGL((chunk_bf16_kernel<DK>), dim3(grid), dim3(512), smem, a.stream, p);
+    if (a.gate_params)
+        hipLaunchKernelGGL((chunk_bf16_kernel<DK, true>), dim3(grid), dim3(512), smem, a.stream, p);
+    else
+        hipLaunchKernelGGL((chunk_bf16_kernel<DK, false>), dim3(grid), dim3(512), smem, a.stream, p);
     return hipGetLastError();
 }
 

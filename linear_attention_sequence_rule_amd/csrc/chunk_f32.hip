@@ -29,7 +29,8 @@ constexpr int C = 64;
 template <typename T>
 struct F32Params {
     const T *q, *k, *v;
-    const float *g, *beta, *s0, *conv_w;
+    const float *g, *beta, *gate_params, *s0, *conv_w;
+    const T* conv_state;  // [N,3,H*(2dk+dv)] history before each sequence, or null (zeros)
     const int32_t* cu;
     T* o;
     float* sfin;
@@ -91,6 +92,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(F32Params<T> p) {
         eos = bos + len;
     }
     const int H = p.H, dv = p.dv;
+    const size_t hstride = (size_t)H * (2 * DK + dv);  // conv channels per token
+    const T* hist = p.conv_state ? p.conv_state + (size_t)n * 3 * hstride : nullptr;
     const size_t sbase = ((size_t)n * H + h) * dv * DK + (size_t)vb * BV * DK;
 
     for (int idx = tid; idx < BV * DK; idx += 256) {
@@ -108,9 +111,9 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(F32Params<T> p) {
             if (r < len) {
                 const long t = cs + r;
                 if (p.conv_w) {
-                    qv = conv_silu_at(p.q, p.conv_w + 4 * ((size_t)h * DK + c), t, bos, (size_t)H * DK, (size_t)h * DK + c);
-                    kv = conv_silu_at(p.k, p.conv_w + 4 * ((size_t)H * DK + (size_t)h * DK + c), t, bos, (size_t)H * DK,
-                                      (size_t)h * DK + c);
+                    const size_t cq = (size_t)h * DK + c, ck = (size_t)H * DK + cq;
+                    qv = conv_silu_at(p.q, p.conv_w + 4 * cq, t, bos, (size_t)H * DK, cq, hist ? hist + cq : nullptr, hstride);
+                    kv = conv_silu_at(p.k, p.conv_w + 4 * ck, t, bos, (size_t)H * DK, cq, hist ? hist + ck : nullptr, hstride);
                 } else {
                     qv = load1(p.q + ((size_t)t * H + h) * DK + c);
                     kv = load1(p.k + ((size_t)t * H + h) * DK + c);
@@ -125,16 +128,23 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(F32Params<T> p) {
             if (r < len) {
                 const long t = cs + r;
                 const int ch = vb * BV + c;
-                vv = p.conv_w ? conv_silu_at(p.v, p.conv_w + 4 * ((size_t)2 * H * DK + (size_t)h * dv + ch), t, bos,
-                                             (size_t)H * dv, (size_t)h * dv + ch)
+                const size_t cv = (size_t)2 * H * DK + (size_t)h * dv + ch;
+                vv = p.conv_w ? conv_silu_at(p.v, p.conv_w + 4 * cv, t, bos, (size_t)H * dv, (size_t)h * dv + ch,
+                                             hist ? hist + cv : nullptr, hstride)
                               : load1(p.v + ((size_t)t * H + h) * dv + ch);
             }
             sV[r * L::VS + c] = vv;
         }
         if (tid < C) {
             const bool in = tid < len;
-            sG[tid] = in ? p.g[(size_t)(cs + tid) * H + h] : 0.f;
-            sB[tid] = in ? p.beta[(size_t)(cs + tid) * H + h] : 0.f;
+            float gv = in ? p.g[(size_t)(cs + tid) * H + h] : 0.f;
+            float bv = in ? p.beta[(size_t)(cs + tid) * H + h] : 0.f;
+            if (p.gate_params && in) {
+                gv = raw_decay(gv, -expf(p.gate_params[h]), p.gate_params[H + h]);
+                bv = raw_beta(bv);
+            }
+            sG[tid] = gv;
+            sB[tid] = bv;
         }
         __syncthreads();
         // ---- L2 norm of q and k rows (4 lanes per row) and the gate prefix sum ----
@@ -259,8 +269,10 @@ hipError_t launch_f32_t(const ChunkArgs& a) {
     p.v = static_cast<const T*>(a.v);
     p.g = a.g;
     p.beta = a.beta;
+    p.gate_params = a.gate_params;
     p.s0 = a.s0;
     p.conv_w = a.conv_w;
+    p.conv_state = static_cast<const T*>(a.conv_state);
     p.cu = a.cu;
     p.o = static_cast<T*>(a.o);
     p.sfin = a.sfin;

@@ -48,6 +48,13 @@ __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ float load1(const bf16* p) { return bf16_to_f32(p->bits); }
 __device__ __forceinline__ void store1(float* p, float x) { *p = x; }
 __device__ __forceinline__ void store1(bf16* p, float x) { p->bits = f32_to_bf16(x); }
+// Store 4 consecutive elements (16-byte aligned for float, 8-byte for bf16).
+__device__ __forceinline__ void store4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void store4(bf16* p, float4 v) {
+    const uint2 r = {(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                     (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
+    *reinterpret_cast<uint2*>(p) = r;
+}
 
 // ---- cross-lane sums over aligned lane groups (DPP / swizzle, no LDS traffic) ---------------
 template <int CTRL>

@@ -10,7 +10,10 @@ namespace gdn {
 struct StepArgs {
     const void *q, *k, *v;
     const float *g, *beta;
+    const float* gate_params; // [2,H] (A_log, dt_bias): g, beta hold the raw a, b; or null
     float* state;
+    const float* conv_w;      // [H*(2dk+dv),4] or null
+    void* conv_state;         // [N,3,H*(2dk+dv)] dtype, with conv_w
     void* o;
     int N, H, dk, dv;
     bool bf16;
@@ -22,9 +25,11 @@ struct StepArgs {
 struct ChunkArgs {
     const void *q, *k, *v;
     const float *g, *beta;
+    const float* gate_params; // [2,H] (A_log, dt_bias): g, beta hold the raw a, b; or null
     const float* s0;          // [N,H,dv,dk] or null
     const int32_t* cu;        // [N+1] or null (equal lengths T_tot / N)
     const float* conv_w;      // [H*(2dk+dv),4] or null
+    void* conv_state;         // [N,3,H*(2dk+dv)] dtype: history before each sequence, or null
     void* o;
     float* sfin;              // [N,H,dv,dk] or null
     void* workspace;
@@ -45,7 +50,7 @@ struct SegLayout {
     size_t bytes;
 };
 SegLayout seg_layout(int N, int H, int dk, int dv, int P);
-// Segments per sequence for a bf16 call without conv: `requested` if > 0, else enough to give
+// Segments per sequence for a bf16 call: `requested` if > 0, else enough to give
 // every compute unit of the current device a workgroup when (sequence, head, row block) units
 // alone do not, and only for sequences of at least 16 chunks per segment.
 int plan_segments(int N, int T_tot, int H, int dv, int requested);
@@ -53,6 +58,9 @@ int plan_segments(int N, int T_tot, int H, int dv, int requested);
 hipError_t launch_step(const StepArgs& a);
 hipError_t launch_chunk_f32(const ChunkArgs& a);
 hipError_t launch_chunk_bf16(const ChunkArgs& a);
+// conv_state <- the three raw inputs before the token after each sequence (in place, after the
+// chunk kernels have read it as history).
+hipError_t launch_conv_state_update(const ChunkArgs& a);
 hipError_t launch_seg_combine(float* E, const float* A, const int* negl, float* sfin, int N, int P, int H, int dk,
                               int dv, hipStream_t stream);
 

@@ -16,23 +16,75 @@
 // stores are non-temporal: each state byte is touched once per step.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "prologue.hpp"
 
 namespace gdn {
 
+// Conv prologue of one decode token (page maplevalley.com.cn/news/1910399, section 3.1, 卷积预处理):
+// channel i of the (n, h) pair's 2 DK + DV channels (q, then k, then v) becomes
+// SiLU(w0 h0 + w1 h1 + w2 h2 + w3 x) from the three previous raw inputs h0, h1, h2 (oldest first)
+// in conv_state [N, 3, H (2 DK + DV)] and the raw input x; the result goes to xs[i] (LDS) and the
+// channel's history is shifted by one token in place.  Every history entry is read and written by
+// the one lane that owns its channel, so the shift needs no synchronisation.
 template <int DK, int DV, typename T>
-__global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, const T* __restrict__ k,
+__device__ __forceinline__ void conv_token(const T* q, const T* k, const T* v, const float* conv_w, T* conv_state,
+                                           float* xs, int nh, int H, int tid) {
+    const size_t CC = (size_t)H * (2 * DK + DV);  // conv channels per token
+    const int h = nh % H;
+    T* hs = conv_state + (size_t)(nh / H) * 3 * CC;
+    for (int i = tid; i < 2 * DK + DV; i += 256) {
+        size_t c;
+        float x;
+        if (i < DK) {
+            c = (size_t)h * DK + i;
+            x = load1(q + (size_t)nh * DK + i);
+        } else if (i < 2 * DK) {
+            c = (size_t)(H + h) * DK + (i - DK);
+            x = load1(k + (size_t)nh * DK + (i - DK));
+        } else {
+            c = (size_t)2 * H * DK + (size_t)h * DV + (i - 2 * DK);
+            x = load1(v + (size_t)nh * DV + (i - 2 * DK));
+        }
+        const float h0 = load1(hs + c), h1 = load1(hs + CC + c), h2 = load1(hs + 2 * CC + c);
+        const float4 w = load4(conv_w + 4 * c);
+        const float acc = w.x * h0 + w.y * h1 + w.z * h2 + w.w * x;
+        xs[i] = acc / (1.f + expf(-acc));
+        store1(hs + c, h1);
+        store1(hs + CC + c, h2);
+        store1(hs + 2 * CC + c, x);
+    }
+}
+
+// With CONV, q, k and v are the raw inputs of the conv prologue (conv_token above) and conv_state
+// carries the history; with gate_params, g and beta are the raw a and b of the gate
+// parameterisation (section 2.1 of the same page).
+// At least 4 waves per SIMD (at most 128 VGPRs): the state streams through at full occupancy.
+template <int DK, int DV, typename T, bool CONV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const float* __restrict__ g,
-                                                   const float* __restrict__ beta, float* __restrict__ state,
-                                                   T* __restrict__ o, float scale, int l2norm) {
+                                                   const float* __restrict__ beta, const float* __restrict__ gate_params,
+                                                   float* __restrict__ state, const float* __restrict__ conv_w,
+                                                   T* __restrict__ conv_state, T* __restrict__ o, int H, float scale,
+                                                   int l2norm) {
     constexpr int LPR = DK / 4;             // lanes per state row
     constexpr int RPP = 256 / LPR;          // rows per pass of the workgroup
     constexpr int RPL = DV / RPP > 0 ? DV / RPP : 1;  // rows per lane
     static_assert(DV % RPP == 0 || RPP > DV, "row tiling");
+    __shared__ float xs[CONV ? 2 * DK + DV : 1];
     const int nh = blockIdx.x;
     const int tid = threadIdx.x;
     const int c = tid % LPR;        // float4 column of this lane
     const int r0 = tid / LPR;       // first row of this lane
     const bool active = r0 < DV;    // only when RPP > DV (small heads)
+
+    // the gates first: their temporaries are dead before the state rows arrive
+    float gg = g[nh], b = beta[nh];
+    if (gate_params) {
+        const int h = nh % H;
+        gg = raw_decay(gg, -expf(gate_params[h]), gate_params[H + h]);
+        b = raw_beta(b);
+    }
+    const float alpha = expf(gg);
 
     float* S = state + (size_t)nh * DV * DK;
     float4 s[RPL];
@@ -42,14 +94,23 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
             s[j] = nt_load4(S + (size_t)(r0 + j * RPP) * DK + 4 * c);
     }
 
-    float4 kk = load4(k + (size_t)nh * DK + 4 * c);
-    float4 qq = load4(q + (size_t)nh * DK + 4 * c);
-    const float alpha = expf(g[nh]);
-    const float b = beta[nh];
+    float4 kk, qq;
     float vr[RPL];
+    if constexpr (CONV) {
+        conv_token<DK, DV, T>(q, k, v, conv_w, conv_state, xs, nh, H, tid);
+        // LDS hand-off only: the barrier need not wait for the state loads in flight
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        qq = *reinterpret_cast<const float4*>(xs + 4 * c);
+        kk = *reinterpret_cast<const float4*>(xs + DK + 4 * c);
 #pragma unroll
-    for (int j = 0; j < RPL; ++j) vr[j] = active ? load1(v + (size_t)nh * DV + r0 + j * RPP) : 0.f;
-
+        for (int j = 0; j < RPL; ++j) vr[j] = active ? xs[2 * DK + r0 + j * RPP] : 0.f;
+    } else {
+        kk = load4(k + (size_t)nh * DK + 4 * c);
+        qq = load4(q + (size_t)nh * DK + 4 * c);
+#pragma unroll
+        for (int j = 0; j < RPL; ++j) vr[j] = active ? load1(v + (size_t)nh * DV + r0 + j * RPP) : 0.f;
+    }
     if (l2norm) {
         float sk = group_sum<LPR>(kk.x * kk.x + kk.y * kk.y + kk.z * kk.z + kk.w * kk.w);
         float sq = group_sum<LPR>(qq.x * qq.x + qq.y * qq.y + qq.z * qq.z + qq.w * qq.w);
@@ -78,9 +139,16 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
 
 template <int DK, int DV, typename T>
 static hipError_t launch_step_t(const StepArgs& a) {
-    hipLaunchKernelGGL((step_kernel<DK, DV, T>), dim3(a.N * a.H), dim3(256), 0, a.stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                       a.g, a.beta, a.state, static_cast<T*>(a.o), a.scale, a.l2norm);
+    if (a.conv_w)
+        hipLaunchKernelGGL((step_kernel<DK, DV, T, true>), dim3(a.N * a.H), dim3(256), 0, a.stream,
+                           static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                           a.g, a.beta, a.gate_params, a.state, a.conv_w, static_cast<T*>(a.conv_state),
+                           static_cast<T*>(a.o), a.H, a.scale, a.l2norm);
+    else
+        hipLaunchKernelGGL((step_kernel<DK, DV, T, false>), dim3(a.N * a.H), dim3(256), 0, a.stream,
+                           static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                           a.g, a.beta, a.gate_params, a.state, nullptr, nullptr, static_cast<T*>(a.o), a.H,
+                           a.scale, a.l2norm);
     return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ import numpy as np
 
 TOKEN_BLOCK = 4096
 _IDS = {"lengths": 0, "A_log": 1, "dt_bias": 2, "a": 3, "b": 4, "q": 5, "k": 6, "v": 7,
-        "s0": 8, "conv_w": 9}
+        "s0": 8, "conv_w": 9, "conv_hist": 10}
 
 
 def _workers() -> int:
@@ -144,6 +144,24 @@ def raw_gates(seed, lengths, H):
     b = np.concatenate([_rng(seed, "b", n).standard_normal((int(L), H))
                         for n, L in enumerate(lengths)])
     return a, b, A_log, dt_bias
+
+
+def raw_gate_inputs(seed, lengths, H):
+    """The raw gate inputs as a caller passes them with gate_params: a, b [T, H] float32 and
+    gate_params [2, H] float32 (row 0 = A_log, row 1 = dt_bias), from the draws of ``raw_gates``."""
+    a, b, A_log, dt_bias = raw_gates(seed, lengths, H)
+    gp = np.stack([A_log, dt_bias]).astype(np.float32)
+    return a.astype(np.float32), b.astype(np.float32), np.ascontiguousarray(gp)
+
+
+def conv_inputs(seed, N, H, dk, dv, dtype):
+    """Conv weights ~N(0, 0.5) [H(2dk+dv), 4] float32 and a conv history [N, 3, H(2dk+dv)] of
+    standard normals in the storage dtype (bf16 bit patterns or float32): the three raw inputs
+    before each sequence, as a previous call would have left them."""
+    C = H * (2 * dk + dv)
+    cw = _rng(seed, "conv_w").normal(0.0, 0.5, size=(C, 4)).astype(np.float32)
+    x = _rng(seed, "conv_hist").standard_normal((N, 3, C), dtype=np.float32)
+    return cw, (f32_to_bf16_bits(x) if dtype == "bf16" else x)
 
 
 def _states(seed, N, H, dv, dk, std, pool):

@@ -46,13 +46,13 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every case below fails va
 
 
 def chunk(lib, **kw):
-    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, s0=None, cu=None, conv=None,
-             o=FAKE * 6, sf=None, ws=None, wsb=None, N=1, T=64, H=1, dk=32, dv=32, dtype=1, chunk=64,
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, gp=None, s0=None, cu=None, conv=None,
+             cst=None, o=FAKE * 6, sf=None, ws=None, wsb=None, N=1, T=64, H=1, dk=32, dv=32, dtype=1, chunk=64,
              scale=1.0, flags=1)
     a.update(kw)
-    return lib.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["cu"], a["conv"], a["o"],
-                             a["sf"], a["ws"], a["wsb"], a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"],
-                             a["chunk"], a["scale"], a["flags"], None)
+    return lib.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["gp"], a["s0"], a["cu"], a["conv"],
+                             a["cst"], a["o"], a["sf"], a["ws"], a["wsb"], a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                             a["dtype"], a["chunk"], a["scale"], a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -72,6 +72,12 @@ def chunk(lib, **kw):
     (dict(o=FAKE), gdn.GDN_ERR_INVALID_ARG),              # o aliases q
     (dict(sf=FAKE * 3), gdn.GDN_ERR_INVALID_ARG),         # final state overlaps v
     (dict(s0=FAKE * 20, sf=FAKE * 20 + 16), gdn.GDN_ERR_INVALID_ARG),  # partial state overlap
+    (dict(gp=FAKE * 7 + 8), gdn.GDN_ERR_INVALID_ARG),     # misaligned gate parameters
+    (dict(gp=FAKE * 6 + 64), gdn.GDN_ERR_INVALID_ARG),    # o overlaps the gate parameters
+    (dict(cst=FAKE * 8), gdn.GDN_ERR_INVALID_ARG),        # conv state without conv weights
+    (dict(conv=FAKE * 7, cst=FAKE + 256), gdn.GDN_ERR_INVALID_ARG),    # conv state inside q
+    (dict(conv=FAKE * 7, cst=FAKE * 7 + 64), gdn.GDN_ERR_INVALID_ARG),  # conv state overlaps conv_w
+    (dict(conv=FAKE * 7, cst=FAKE * 8 + 4), gdn.GDN_ERR_INVALID_ARG),   # misaligned conv state
 ])
 def test_chunk_validation(lib, kw, status):
     assert chunk(lib, **kw) == status
@@ -131,13 +137,21 @@ def test_workspace_size_validation(lib):
     (dict(flags=2), gdn.GDN_ERR_INVALID_ARG),
     (dict(flags=1 | (2 << 8)), gdn.GDN_ERR_INVALID_ARG),  # segments are a prefill option
     (dict(N=0), gdn.GDN_OK),                        # empty batch: no-op, no launch
+    (dict(conv=FAKE * 7), gdn.GDN_ERR_INVALID_ARG),         # conv weights without a conv state
+    (dict(cst=FAKE * 8), gdn.GDN_ERR_INVALID_ARG),          # conv state without conv weights
+    (dict(conv=FAKE * 7, cst=FAKE * 6 + 128), gdn.GDN_ERR_INVALID_ARG),  # conv state inside the state
+    (dict(conv=FAKE * 7, cst=FAKE * 2 + 32), gdn.GDN_ERR_INVALID_ARG),   # conv state overlaps k
+    (dict(conv=FAKE * 7, cst=FAKE * 8 + 2), gdn.GDN_ERR_INVALID_ARG),    # misaligned
+    (dict(gp=FAKE * 100 + 16), gdn.GDN_ERR_INVALID_ARG),    # gate parameters inside o
+    (dict(gp=FAKE * 9 + 4), gdn.GDN_ERR_INVALID_ARG),       # misaligned gate parameters
 ])
 def test_step_validation(lib, kw, status):
-    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, state=FAKE * 6, o=FAKE * 100, N=2, H=1,
-             dk=32, dv=32, dtype=1, scale=1.0, flags=1)
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, gp=None, state=FAKE * 6, conv=None, cst=None,
+             o=FAKE * 100, N=2, H=1, dk=32, dv=32, dtype=1, scale=1.0, flags=1)
     a.update(kw)
-    assert lib.gdn_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["o"], a["N"], a["H"],
-                                  a["dk"], a["dv"], a["dtype"], a["scale"], a["flags"], None) == status
+    assert lib.gdn_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["gp"], a["state"], a["conv"],
+                                  a["cst"], a["o"], a["N"], a["H"], a["dk"], a["dv"], a["dtype"], a["scale"],
+                                  a["flags"], None) == status
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch):
