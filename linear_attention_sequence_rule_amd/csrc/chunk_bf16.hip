@@ -337,7 +337,10 @@ __device__ __forceinline__ void zero_tail(unsigned char* raw, int len, int wid, 
 }
 
 // After this wave's loads landed: with raw gates, turn the raw a (part 0) and b (part 1) of the
-// chunk's valid rows into g and beta in place, before anything reads them.
+// chunk's valid rows into g and beta in place, before anything reads them.  The same formulas as
+// raw_decay / raw_beta, on the hardware exp2 / log2 / reciprocal: log1p(y) for y = exp(-|x|) in
+// (0, 1] is taken as log(1 + y), whose absolute error (below 2^-23) is far under the bf16 path's
+// rounding, and this runs once per token on the wave that loaded the chunk.
 template <int DK>
 __device__ __forceinline__ void raw_gates(const Params<DK>& p, unsigned char* raw, int len, int part, int lane, int h) {
     using S = Smem<DK>;
@@ -345,7 +348,15 @@ __device__ __forceinline__ void raw_gates(const Params<DK>& p, unsigned char* ra
     float* x = reinterpret_cast<float*>(raw + (part == 0 ? S::rG : S::rB));
     if (lane < len) {
         const float a = x[lane];
-        x[lane] = part == 0 ? raw_decay(a, -expf(p.gate_params[h]), p.gate_params[p.H + h]) : raw_beta(a);
+        float r;
+        if (part == 0) {
+            const float z = a + p.gate_params[p.H + h];
+            const float sp = fmaxf(z, 0.f) + __logf(1.f + __expf(-fabsf(z)));
+            r = -__expf(p.gate_params[h]) * sp;
+        } else {
+            r = __builtin_amdgcn_rcpf(1.f + __expf(-a));
+        }
+        x[lane] = r;
     }
 }
 
