@@ -43,10 +43,10 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         lib.gdn_oracle_forward.restype = ctypes.c_int
-        lib.gdn_oracle_forward.argtypes = [P] * 13 + [ctypes.c_int] * 4 + [
+        lib.gdn_oracle_forward.argtypes = [P] * 13 + [ctypes.c_int] * 5 + [
             ctypes.c_double, ctypes.c_int, ctypes.c_int]
         lib.gdn_oracle_step.restype = ctypes.c_int
-        lib.gdn_oracle_step.argtypes = [P] * 9 + [ctypes.c_int] * 4 + [
+        lib.gdn_oracle_step.argtypes = [P] * 9 + [ctypes.c_int] * 5 + [
             ctypes.c_double, ctypes.c_int, ctypes.c_int]
         lib.gdn_oracle_gates.restype = None
         lib.gdn_oracle_gates.argtypes = [P] * 6 + [ctypes.c_long, ctypes.c_int]
@@ -66,16 +66,19 @@ def forward(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=None, 
             scale=1.0, l2norm=True, pairs=None, nthreads=0, want_o=True, conv_hist=None, want_conv_hist=False):
     """Token-by-token fp64 gated delta rule over packed sequences.
 
-    q, k: [T_tot, H, dk]; v: [T_tot, H, dv]; g, beta: [T_tot, H]; initial_state [N, H, dv, dk]
-    or None (zeros); cu_seqlens [N+1] or None (then N equal sequences); conv_w [H*(2dk+dv), 4]
-    or None; conv_hist [N, 3, H*(2dk+dv)] or None (zeros): the raw inputs before each sequence.
+    q, k: [T_tot, Hk, dk]; v: [T_tot, H, dv]; g, beta: [T_tot, H]; initial_state [N, H, dv, dk]
+    or None (zeros); cu_seqlens [N+1] or None (then N equal sequences); conv_w [C, 4] or None
+    with C = 2*Hk*dk + H*dv; conv_hist [N, 3, C] or None (zeros): the raw inputs before each
+    sequence.  H must be a multiple of Hk; value head h reads query/key head h // (H // Hk).
     ``pairs``: optional iterable of (n, h) to compute; other pairs are left as NaN.
     Returns (o [T_tot, H, dv] or None, final_state [N, H, dv, dk], threads_used), plus the conv
     history after each sequence [N, 3, H*(2dk+dv)] when ``want_conv_hist``.
     """
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
-    T_tot, H, dk = q.shape
-    dv = v.shape[2]
+    T_tot, Hk, dk = q.shape
+    H, dv = v.shape[1], v.shape[2]
+    assert k.shape == q.shape and H % Hk == 0
+    C = 2 * Hk * dk + H * dv
     if cu_seqlens is None:
         if N is None:
             N = 1
@@ -90,7 +93,7 @@ def forward(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=None, 
         assert s0.shape == (N, H, dv, dk)
     cw = _f64(conv_w)
     if cw is not None:
-        assert cw.shape == (H * (2 * dk + dv), 4)
+        assert cw.shape == (C, 4)
     mask = None
     if pairs is not None:
         mask = np.zeros(N * H, dtype=np.uint8)
@@ -98,36 +101,37 @@ def forward(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=None, 
             mask[n * H + h] = 1
     hist = _f64(conv_hist)
     if hist is not None:
-        assert cw is not None and hist.shape == (N, 3, H * (2 * dk + dv))
-    hout = np.full((N, 3, H * (2 * dk + dv)), np.nan) if (want_conv_hist and cw is not None) else None
+        assert cw is not None and hist.shape == (N, 3, C)
+    hout = np.full((N, 3, C), np.nan) if (want_conv_hist and cw is not None) else None
     o = np.full((T_tot, H, dv), np.nan) if want_o else None
     sfin = np.full((N, H, dv, dk), np.nan)
     used = _load().gdn_oracle_forward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), _ptr(cu), _ptr(cw), _ptr(hist), _ptr(hout),
-        _ptr(o), _ptr(sfin), _ptr(mask), N, H, dk, dv, float(scale), 1 if l2norm else 0, int(nthreads))
+        _ptr(o), _ptr(sfin), _ptr(mask), N, H, Hk, dk, dv, float(scale), 1 if l2norm else 0, int(nthreads))
     if want_conv_hist:
         return o, sfin, used, hout
     return o, sfin, used
 
 
 def step(q, k, v, g, beta, state, *, scale=1.0, l2norm=True, nthreads=0, conv_w=None, conv_hist=None):
-    """One decode token per (sequence, head).  q, k [N,H,dk]; v [N,H,dv]; g, beta [N,H];
-    state [N,H,dv,dk]; optional conv_w [H*(2dk+dv),4] with conv_hist [N,3,H*(2dk+dv)] (the three
+    """One decode token per (sequence, head).  q, k [N,Hk,dk]; v [N,H,dv]; g, beta [N,H];
+    state [N,H,dv,dk]; optional conv_w [C,4] with conv_hist [N,3,C], C = 2*Hk*dk + H*dv (the three
     previous raw inputs).  Returns (o [N,H,dv], new_state), plus the new conv history when conv_w
     is given, without modifying the inputs."""
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
-    N, H, dk = q.shape
-    dv = v.shape[2]
+    N, Hk, dk = q.shape
+    H, dv = v.shape[1], v.shape[2]
+    assert k.shape == q.shape and H % Hk == 0
     st = np.array(state, dtype=np.float64, copy=True, order="C")
     assert st.shape == (N, H, dv, dk)
     cw = _f64(conv_w)
     hist = None
     if cw is not None:
         hist = np.array(conv_hist, dtype=np.float64, copy=True, order="C")
-        assert hist.shape == (N, 3, H * (2 * dk + dv))
+        assert hist.shape == (N, 3, 2 * Hk * dk + H * dv)
     o = np.empty((N, H, dv))
     _load().gdn_oracle_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cw), _ptr(hist), _ptr(st), _ptr(o),
-                            N, H, dk, dv, float(scale), 1 if l2norm else 0, int(nthreads))
+                            N, H, Hk, dk, dv, float(scale), 1 if l2norm else 0, int(nthreads))
     if cw is not None:
         return o, st, hist
     return o, st

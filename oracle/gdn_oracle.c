@@ -17,8 +17,13 @@
  *   causal depthwise conv1d with 4 taps per channel, followed by SiLU(x) = x / (1 + exp(-x)).
  *   The three raw inputs before a sequence start come from a given conv history (zeros when
  *   none is given), and the conv history after the sequence (its last three raw inputs) can be
- *   returned, so that a sequence can be continued by a later call or by decode steps.  Optional L2 normalisation of q and k over the key
- *   dimension, x / sqrt(sum x^2 + 1e-6) (not on the pages; the eps is this library's reading).
+ *   returned, so that a sequence can be continued by a later call or by decode steps.
+ *   Optional L2 normalisation of q and k over the key dimension, x / sqrt(sum x^2 + 1e-6) (not
+ *   on the pages; the eps is this library's reading).
+ *
+ *   Heads: the model configuration on page "Gated DeltaNet 架构详解与 Qwen 3.5 的联系", section 6,
+ *   counts query/key heads and value heads separately.  Value head h uses query/key head
+ *   h / (H / Hk): consecutive value heads share one query/key head (this library's reading).
  *
  * Everything is double precision.  Callers pass the exact values the GPU receives, promoted to
  * double.  Parallelism: POSIX threads over independent (n, h) pairs only; the arithmetic of
@@ -43,7 +48,7 @@ typedef struct {
     const int64_t* cu;
     const unsigned char* mask;
     double *o, *sfin;
-    int N, H, dk, dv, l2norm;
+    int N, H, Hk, dk, dv, l2norm; /* H value heads, Hk query/key heads (H a multiple of Hk) */
     double scale;
     int next_pair; /* work counter, protected by lock */
     pthread_mutex_t lock;
@@ -71,7 +76,8 @@ static void conv_silu(const double* x, long stride, const double* hist, long hst
 }
 
 static void run_pair(job_t* J, int n, int h) {
-    const int H = J->H, dk = J->dk, dv = J->dv;
+    const int H = J->H, Hk = J->Hk, dk = J->dk, dv = J->dv;
+    const int hk = h / (H / Hk); /* the query/key head shared by this group of value heads */
     const long bos = (long)J->cu[n], len = (long)(J->cu[n + 1] - J->cu[n]);
     double* S = (double*)malloc(sizeof(double) * (size_t)dv * dk);
     double* Sk = (double*)malloc(sizeof(double) * dv);
@@ -86,9 +92,9 @@ static void run_pair(job_t* J, int n, int h) {
         memset(S, 0, sizeof(double) * (size_t)dv * dk);
 
     if (J->conv_w) {
-        /* Channel c of the conv: q channels h*dk + i, then k (H*dk + h*dk + i), then v
-         * (2*H*dk + h*dv + i); the history rows of sequence n are [3][C] at n*3*C. */
-        const long C = (long)H * (2 * dk + dv);
+        /* Channel c of the conv: q channels hk*dk + i, then k (Hk*dk + hk*dk + i), then v
+         * (2*Hk*dk + h*dv + i); the history rows of sequence n are [3][C] at n*3*C. */
+        const long C = 2L * Hk * dk + (long)H * dv;
         const double* hist = J->hist ? J->hist + (size_t)n * 3 * C : NULL;
         double* hout = J->hist_out ? J->hist_out + (size_t)n * 3 * C : NULL;
         /* Pre-compute the conv+SiLU channels of this (sequence, head), token-major. */
@@ -98,26 +104,29 @@ static void run_pair(job_t* J, int n, int h) {
         double* tmp = (double*)malloc(sizeof(double) * (size_t)(len + 1));
         for (int part = 0; part < 3; ++part) {
             const int d = part < 2 ? dk : dv;
+            const int heads = part < 2 ? Hk : H, hh = part < 2 ? hk : h;
             const double* x = part == 0 ? J->q : (part == 1 ? J->k : J->v);
             double* dst = part == 0 ? cq : (part == 1 ? ck : cv);
             for (int i = 0; i < d; ++i) {
-                const long c = part < 2 ? (long)part * H * dk + (long)h * dk + i : 2L * H * dk + (long)h * dv + i;
-                const double* xc = x + ((size_t)bos * H + h) * d + i;
+                const long c = part < 2 ? (long)part * Hk * dk + (long)hk * dk + i : 2L * Hk * dk + (long)h * dv + i;
+                const double* xc = x + ((size_t)bos * heads + hh) * d + i;
                 const double* hc = hist ? hist + c : NULL;
-                conv_silu(xc, (long)H * d, hc, C, len, J->conv_w + 4 * c, tmp);
+                conv_silu(xc, (long)heads * d, hc, C, len, J->conv_w + 4 * c, tmp);
                 for (long t = 0; t < len; ++t) dst[t * d + i] = tmp[t];
-                if (hout) /* the last three raw inputs, oldest first */
-                    for (int j = 0; j < 3; ++j) hout[j * C + c] = conv_input(xc, (long)H * d, hc, C, len - 3 + j);
+                /* the last three raw inputs, oldest first; a q/k channel shared by several value
+                 * heads is written by the first of them */
+                if (hout && (part == 2 || h % (H / Hk) == 0))
+                    for (int j = 0; j < 3; ++j) hout[j * C + c] = conv_input(xc, (long)heads * d, hc, C, len - 3 + j);
             }
         }
         free(tmp);
     }
 
     for (long t = 0; t < len; ++t) {
-        const long row = (bos + t) * H + h;
+        const long row = (bos + t) * H + h, krow = (bos + t) * Hk + hk;
         for (int i = 0; i < dk; ++i) {
-            qt[i] = cq ? cq[t * dk + i] : J->q[row * dk + i];
-            kt[i] = ck ? ck[t * dk + i] : J->k[row * dk + i];
+            qt[i] = cq ? cq[t * dk + i] : J->q[krow * dk + i];
+            kt[i] = ck ? ck[t * dk + i] : J->k[krow * dk + i];
         }
         for (int i = 0; i < dv; ++i) vt[i] = cv ? cv[t * dv + i] : J->v[row * dv + i];
         if (J->l2norm) {
@@ -180,10 +189,14 @@ static void* worker(void* arg) {
 
 /*
  * gdn_oracle_forward -- o and final state of the gated delta rule over packed sequences.
- *  q, k [T_tot,H,dk]; v [T_tot,H,dv]; g, beta [T_tot,H]; s0 [N,H,dv,dk] or NULL (zeros);
- *  cu [N+1] int64 offsets; conv_w [H*(2dk+dv),4] or NULL; conv_hist [N,3,H*(2dk+dv)] or NULL
- *  (zeros): the raw inputs before each sequence start; conv_hist_out [N,3,H*(2dk+dv)] or NULL:
- *  the last three raw inputs of each sequence (may not alias conv_hist); o [T_tot,H,dv] or NULL;
+ *  H value heads (state, gates, v, o) and Hk query/key heads, H a multiple of Hk: value head h
+ *  reads query/key head h / (H / Hk), so each query/key head serves H / Hk consecutive value
+ *  heads (Hk = H: one each).
+ *  q, k [T_tot,Hk,dk]; v [T_tot,H,dv]; g, beta [T_tot,H]; s0 [N,H,dv,dk] or NULL (zeros);
+ *  cu [N+1] int64 offsets; conv_w [C,4] or NULL with C = 2*Hk*dk + H*dv conv channels (q, k, v);
+ *  conv_hist [N,3,C] or NULL (zeros): the raw inputs before each sequence start; conv_hist_out
+ *  [N,3,C] or NULL: the last three raw inputs of each sequence (may not alias conv_hist);
+ *  o [T_tot,H,dv] or NULL;
  *  sfin [N,H,dv,dk] or NULL; mask [N*H] or NULL: only pairs with mask != 0 are computed (their
  *  o rows, final states and conv history channels are written; others are left untouched).
  *  nthreads <= 0: all cores.  Returns the number of threads used.
@@ -191,13 +204,14 @@ static void* worker(void* arg) {
 int gdn_oracle_forward(const double* q, const double* k, const double* v, const double* g,
                        const double* beta, const double* s0, const int64_t* cu,
                        const double* conv_w, const double* conv_hist, double* conv_hist_out, double* o,
-                       double* sfin, const unsigned char* mask, int N, int H, int dk, int dv, double scale,
-                       int l2norm, int nthreads) {
+                       double* sfin, const unsigned char* mask, int N, int H, int Hk, int dk, int dv,
+                       double scale, int l2norm, int nthreads) {
     job_t J;
     J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.s0 = s0; J.conv_w = conv_w;
     J.hist = conv_hist; J.hist_out = conv_hist_out;
     J.cu = cu; J.mask = mask; J.o = o; J.sfin = sfin;
-    J.N = N; J.H = H; J.dk = dk; J.dv = dv; J.l2norm = l2norm; J.scale = scale;
+    if (Hk < 1 || H % Hk != 0) return -1;
+    J.N = N; J.H = H; J.Hk = Hk; J.dk = dk; J.dv = dv; J.l2norm = l2norm; J.scale = scale;
     J.next_pair = 0;
     pthread_mutex_init(&J.lock, NULL);
     if (nthreads <= 0) nthreads = (int)sysconf(_SC_NPROCESSORS_ONLN);
@@ -214,22 +228,22 @@ int gdn_oracle_forward(const double* q, const double* k, const double* v, const 
 
 /*
  * gdn_oracle_step -- one decode token per sequence (the same update with T = 1), state
- * updated in place.  q, k [N,H,dk]; v [N,H,dv]; g, beta [N,H]; state [N,H,dv,dk]; o [N,H,dv];
- * conv_w [H*(2dk+dv),4] or NULL; conv_hist [N,3,H*(2dk+dv)] (with conv_w): the three previous
- * raw inputs, read and replaced by the three latest.
+ * updated in place.  q, k [N,Hk,dk]; v [N,H,dv]; g, beta [N,H]; state [N,H,dv,dk]; o [N,H,dv];
+ * conv_w [C,4] or NULL (C = 2*Hk*dk + H*dv); conv_hist [N,3,C] (with conv_w): the three
+ * previous raw inputs, read and replaced by the three latest.  Heads as for gdn_oracle_forward.
  * Page pzsr.cn/news/750, section a、增量更新: decay the whole state first, then erase and write
  * along the current key.
  */
 int gdn_oracle_step(const double* q, const double* k, const double* v, const double* g,
                     const double* beta, const double* conv_w, double* conv_hist, double* state, double* o,
-                    int N, int H, int dk, int dv, double scale, int l2norm, int nthreads) {
+                    int N, int H, int Hk, int dk, int dv, double scale, int l2norm, int nthreads) {
     int64_t* cu = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N + 1));
     for (int n = 0; n <= N; ++n) cu[n] = n;
     double* hout = NULL;
-    const size_t hn = (size_t)N * 3 * H * (2 * dk + dv);
+    const size_t hn = (size_t)N * 3 * (2 * (size_t)Hk * dk + (size_t)H * dv);
     if (conv_w) hout = (double*)malloc(sizeof(double) * hn);
     int used = gdn_oracle_forward(q, k, v, g, beta, state, cu, conv_w, conv_hist, hout, o, state, NULL, N, H,
-                                  dk, dv, scale, l2norm, nthreads);
+                                  Hk, dk, dv, scale, l2norm, nthreads);
     if (conv_w) {
         memcpy(conv_hist, hout, sizeof(double) * hn);
         free(hout);

@@ -489,3 +489,63 @@ def test_step_with_conv_is_forward_last_token():
     np.testing.assert_array_equal(o_s, o[last])
     np.testing.assert_array_equal(s_s, sf)
     np.testing.assert_array_equal(h_s, hf)
+
+
+def _expand_heads(x, r):
+    """[T, Hk, d] -> [T, Hk * r, d], each query/key head repeated for its r value heads."""
+    return np.repeat(x, r, axis=1)
+
+
+def _expand_conv_rows(w, Hk, r, dk, H, dv):
+    """Conv channels (rows of a [C, ...] array) of the grouped layout 2*Hk*dk + H*dv mapped to the
+    layout with one query/key head per value head (2*H*dk + H*dv)."""
+    q = w[:Hk * dk].reshape(Hk, dk, *w.shape[1:])
+    k = w[Hk * dk:2 * Hk * dk].reshape(Hk, dk, *w.shape[1:])
+    v = w[2 * Hk * dk:]
+    return np.concatenate([np.repeat(q, r, 0).reshape(H * dk, *w.shape[1:]),
+                           np.repeat(k, r, 0).reshape(H * dk, *w.shape[1:]), v])
+
+
+@pytest.mark.parametrize("Hk,H", [(1, 3), (2, 4), (3, 3)])
+def test_grouped_heads_equal_repeated_heads(Hk, H):
+    """Value heads sharing a query/key head: the result equals the one-to-one layout with every
+    query/key head (and its conv weights and history) repeated for the value heads that use it.
+    Bitwise, with the conv prologue, a history in and out, and a decode step."""
+    r = rnd(22 + Hk + H)
+    rep = H // Hk
+    lengths = [9, 0, 2, 14]
+    dk, dv = 4, 3
+    T = sum(lengths)
+    q, k = r.standard_normal((T, Hk, dk)), r.standard_normal((T, Hk, dk))
+    v = r.standard_normal((T, H, dv))
+    g, beta = gates(r, T, H)
+    s0 = r.standard_normal((len(lengths), H, dv, dk)) * 0.1
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    C = 2 * Hk * dk + H * dv
+    conv_w = r.normal(0, 0.5, size=(C, 4))
+    hist = r.standard_normal((len(lengths), 3, C))
+    o, sf, _, hf = oracle.forward(q, k, v, g, beta, s0, cu, conv_w, conv_hist=hist, want_conv_hist=True)
+    ew = _expand_conv_rows(conv_w, Hk, rep, dk, H, dv)
+    eh = np.ascontiguousarray(np.stack([_expand_conv_rows(hist[n].T, Hk, rep, dk, H, dv).T
+                                        for n in range(len(lengths))]))
+    o2, sf2, _, hf2 = oracle.forward(_expand_heads(q, rep), _expand_heads(k, rep), v, g, beta, s0, cu, ew,
+                                     conv_hist=eh, want_conv_hist=True)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(sf, sf2)
+    for n in range(len(lengths)):
+        np.testing.assert_array_equal(_expand_conv_rows(hf[n].T, Hk, rep, dk, H, dv).T, hf2[n])
+    # decode step
+    N = 5
+    qd, kd = r.standard_normal((N, Hk, dk)), r.standard_normal((N, Hk, dk))
+    vd = r.standard_normal((N, H, dv))
+    gd, bd = gates(r, N, H)
+    st = r.standard_normal((N, H, dv, dk))
+    hd = r.standard_normal((N, 3, C))
+    od, std, hdo = oracle.step(qd, kd, vd, gd, bd, st, conv_w=conv_w, conv_hist=hd)
+    ehd = np.ascontiguousarray(np.stack([_expand_conv_rows(hd[n].T, Hk, rep, dk, H, dv).T for n in range(N)]))
+    od2, std2, hdo2 = oracle.step(_expand_heads(qd, rep), _expand_heads(kd, rep), vd, gd, bd, st, conv_w=ew,
+                                  conv_hist=ehd)
+    np.testing.assert_array_equal(od, od2)
+    np.testing.assert_array_equal(std, std2)
+    for n in range(N):
+        np.testing.assert_array_equal(_expand_conv_rows(hdo[n].T, Hk, rep, dk, H, dv).T, hdo2[n])
