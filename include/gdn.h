@@ -22,7 +22,13 @@
  *     g = -exp(A_log[h]) * softplus(a + dt_bias[h]),   beta = 1 / (1 + exp(-b))
  * in fp32, softplus(x) = max(x, 0) + log1p(exp(-|x|)) (no threshold).  The inputs are not modified.
  *
- * Conv state (both entry points).  conv_state [N, 3, H*(2*dk + dv)] dtype holds, per sequence, the
+ * Heads (both entry points).  H value heads carry the states, gates, values and outputs; Hk query/key
+ * heads carry q and k, with H a multiple of Hk: value head h reads query/key head h / (H / Hk), so
+ * each query/key head serves H / Hk consecutive value heads (Hk = H: one query/key head per value
+ * head).  The model configuration on page "Gated DeltaNet 架构详解与 Qwen 3.5 的联系", section 6,
+ * counts the two separately; the grouping order is this library's reading.
+ *
+ * Conv state (both entry points).  conv_state [N, 3, C] dtype, C = 2*Hk*dk + H*dv, holds, per sequence, the
  * three raw inputs (before conv) that precede its next token, oldest first, in the channel order of
  * conv_w.  It makes the conv prologue continue across calls: a prefill reads it as the history
  * before each sequence start instead of zeros, and both entry points overwrite it in place with the
@@ -82,7 +88,7 @@ extern "C" {
  * The chunk size changes only the rounding, never the result in exact arithmetic.
  *
  * Arguments (T_tot = total tokens of all sequences, packed back to back):
- *  q, k        [T_tot, H, dk]  dtype   raw queries / keys (before conv, before L2 norm)
+ *  q, k        [T_tot, Hk, dk] dtype   raw queries / keys (before conv, before L2 norm)
  *  v           [T_tot, H, dv]  dtype   raw values
  *  g           [T_tot, H]      fp32    log decay, alpha = exp(g); g <= 0 expected (any finite g
  *                                      works); with gate_params: the raw a
@@ -93,14 +99,15 @@ extern "C" {
  *                                      cu_seqlens[0] = 0, cu_seqlens[N] = T_tot; NULL = N equal
  *                                      sequences of T_tot / N tokens (then N must divide T_tot).
  *                                      Zero-length sequences are allowed: final = initial, no o.
- *  conv_w      [H*(2*dk + dv), 4] fp32 NULL, or the depthwise causal conv1d (4 taps) applied per
+ *  conv_w      [C, 4] fp32             NULL, or the depthwise causal conv1d (4 taps) applied per
  *                                      channel to q, k and v before SiLU and the L2 norm (page
  *                                      maplevalley.com.cn/news/1910399, section 3.1, 卷积预处理).
- *                                      Channel c < H*dk is q channel (h*dk + i), the next H*dk are
- *                                      k channels, the last H*dv are v channels.  Tap j multiplies
+ *                                      C = 2*Hk*dk + H*dv: channel c < Hk*dk is q channel
+ *                                      (hk*dk + i), the next Hk*dk are k channels, the last H*dv
+ *                                      are v channels (h*dv + i).  Tap j multiplies
  *                                      token t-3+j (tap 3 = current token); history before a
  *                                      sequence start is conv_state, else zero; no bias.
- *  conv_state  [N, 3, H*(2*dk + dv)] dtype  NULL, or the conv history, read and overwritten in
+ *  conv_state  [N, 3, C] dtype         NULL, or the conv history, read and overwritten in
  *                                      place ("Conv state" above); requires conv_w.  Must not
  *                                      overlap any other buffer.
  *  o           [T_tot, H, dv]  dtype   output; must not alias any input
@@ -114,7 +121,8 @@ extern "C" {
  *                                      may be NULL only when the call needs no workspace.  The
  *                                      workspace must not overlap any other buffer; its contents
  *                                      on entry are ignored and on return are unspecified.
- *  N, T_tot, H, dk, dv                 sizes; dk, dv in {32, 64, 128}; N >= 1, T_tot >= 0, H >= 1
+ *  N, T_tot, H, Hk, dk, dv             sizes; dk, dv in {32, 64, 128}; N >= 1, T_tot >= 0, H >= 1,
+ *                                      1 <= Hk, H a multiple of Hk ("Heads" above)
  *  dtype       GDN_F32 or GDN_BF16     (fp32 path: exact fp32 arithmetic throughout; bf16 path:
  *                                      bf16 MFMA operands, fp32 accumulation, fp32 state)
  *  chunk       64                      chunk length; other values -> GDN_ERR_UNSUPPORTED
@@ -138,11 +146,12 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,
                   const float* conv_w, void* conv_state, void* o, float* final_state,
                   void* workspace, size_t* workspace_bytes, int N,
-                  int T_tot, int H, int dk, int dv, int dtype, int chunk, float scale,
+                  int T_tot, int H, int Hk, int dk, int dv, int dtype, int chunk, float scale,
                   unsigned flags, void* hip_stream);
 
 /*
- * gdn_chunk_workspace_size -- the workspace gdn_chunk_fwd needs for these sizes, flags and
+ * gdn_chunk_workspace_size -- the workspace gdn_chunk_fwd needs for these sizes (H = value heads;
+ * the workspace does not depend on the query/key head count), flags and
  * (nonzero = present) cu_seqlens / conv_w (0 bytes when the call runs as a single pass).  Host
  * function; with automatic segments it reads the compute-unit count of the current device (256
  * when no device can be queried), exactly as gdn_chunk_fwd does.  Returns GDN_OK and sets *bytes,
@@ -159,22 +168,22 @@ int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype,
  * current key with strength beta), which is the rule above with T = 1:
  *     u = beta (v - alpha S k),  S <- alpha S + u k^T,  o = scale * S q.
  *
- *  q, k   [N, H, dk] dtype;  v [N, H, dv] dtype;  g, beta [N, H] fp32 (raw a, b with
+ *  q, k   [N, Hk, dk] dtype;  v [N, H, dv] dtype;  g, beta [N, H] fp32 (raw a, b with
  *         gate_params)
  *  gate_params [2, H] fp32 or NULL, as for gdn_chunk_fwd
  *  state  [N, H, dv, dk] fp32, read and overwritten in place
- *  conv_w [H*(2*dk + dv), 4] fp32 and conv_state [N, 3, H*(2*dk + dv)] dtype: both NULL, or both
+ *  conv_w [C, 4] fp32 and conv_state [N, 3, C] dtype (C = 2*Hk*dk + H*dv): both NULL, or both
  *         given: then q, k and v are the raw inputs of the conv prologue, conv + SiLU (and the L2
  *         norm) run on them with the three previous raw inputs from conv_state, and conv_state is
  *         shifted in place by one token (the oldest dropped, this token's raw inputs appended)
  *  o      [N, H, dv] dtype, must not alias any input
- *  N, H >= 1 (N = 0 is a no-op returning GDN_OK); dk, dv in {32, 64, 128}
+ *  N, H, Hk >= 1 (N = 0 is a no-op returning GDN_OK), H a multiple of Hk; dk, dv in {32, 64, 128}
  *  dtype, scale, flags, hip_stream as for gdn_chunk_fwd
  */
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                        const float* beta, const float* gate_params, float* state,
-                       const float* conv_w, void* conv_state, void* o, int N, int H, int dk, int dv,
-                       int dtype, float scale, unsigned flags, void* hip_stream);
+                       const float* conv_w, void* conv_state, void* o, int N, int H, int Hk, int dk,
+                       int dv, int dtype, float scale, unsigned flags, void* hip_stream);
 
 /* gdn_status_string -- static, human-readable name of a status code (never NULL). */
 const char* gdn_status_string(int status);

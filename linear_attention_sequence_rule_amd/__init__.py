@@ -54,11 +54,11 @@ def load_library():
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, U, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_float
     lib.gdn_chunk_fwd.restype = I
-    lib.gdn_chunk_fwd.argtypes = [P] * 14 + [I] * 7 + [F, U, P]
+    lib.gdn_chunk_fwd.argtypes = [P] * 14 + [I] * 8 + [F, U, P]
     lib.gdn_chunk_workspace_size.restype = I
     lib.gdn_chunk_workspace_size.argtypes = [I] * 9 + [U, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdn_recurrent_step.restype = I
-    lib.gdn_recurrent_step.argtypes = [P] * 10 + [I] * 5 + [F, U, P]
+    lib.gdn_recurrent_step.argtypes = [P] * 10 + [I] * 6 + [F, U, P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [I]
     _lib = lib
@@ -113,17 +113,20 @@ def gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype=GDN_BF16, chunk=64, has_
 def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=None, *, N=None, o=None,
                   final_state=None, output_final_state=True, scale=1.0, l2norm=True, chunk=64, workspace=None,
                   segments=0, gate_params=None, conv_state=None, stream=None):
-    """Chunked prefill.  q, k [T_tot, H, dk]; v [T_tot, H, dv] (bf16 or fp32); g, beta [T_tot, H] fp32
-    (the raw a and b when gate_params [2, H] = (A_log, dt_bias) is given); initial_state [N, H, dv, dk]
-    fp32 or None; cu_seqlens [N+1] int32 or None (N equal sequences, N given or 1); conv_w
-    [H*(2dk+dv), 4] fp32 or None; conv_state [N, 3, H*(2dk+dv)] in the dtype of q, read as the conv
-    history and updated in place, or None; segments per sequence (0 = automatic).
+    """Chunked prefill.  q, k [T_tot, Hk, dk]; v [T_tot, H, dv] (bf16 or fp32; H a multiple of Hk, value
+    head h reads query/key head h // (H // Hk)); g, beta [T_tot, H] fp32 (the raw a and b when
+    gate_params [2, H] = (A_log, dt_bias) is given); initial_state [N, H, dv, dk] fp32 or None;
+    cu_seqlens [N+1] int32 or None (N equal sequences, N given or 1); conv_w [C, 4] fp32 or None,
+    C = 2*Hk*dk + H*dv; conv_state [N, 3, C] in the dtype of q, read as the conv history and
+    updated in place, or None; segments per sequence (0 = automatic).
     A workspace (uint8 device tensor) is allocated here when the call needs one and none large
     enough is given.  Returns (o, final_state or None)."""
     import torch
     lib = load_library()
-    T_tot, H, dk = q.shape
-    dv = v.shape[2]
+    T_tot, Hk, dk = q.shape
+    H, dv = v.shape[1], v.shape[2]
+    if tuple(k.shape) != tuple(q.shape):
+        raise ValueError("k must have the shape of q")
     dt = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("conv_state", conv_state)):
         _check_dev(name, t, q.dtype)
@@ -148,8 +151,8 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=
         ws_bytes = ctypes.c_size_t(need)
     st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate_params), _ptr(initial_state),
                            _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_state), _ptr(o), _ptr(final_state),
-                           _ptr(workspace), ctypes.byref(ws_bytes), N, T_tot, H, dk, dv, dt, chunk, float(scale), flags,
-                           _stream(stream))
+                           _ptr(workspace), ctypes.byref(ws_bytes), N, T_tot, H, Hk, dk, dv, dt, chunk, float(scale),
+                           flags, _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_fwd")
     return o, final_state
@@ -157,14 +160,16 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=
 
 def gdn_recurrent_step(q, k, v, g, beta, state, *, o=None, scale=1.0, l2norm=True, gate_params=None, conv_w=None,
                        conv_state=None, stream=None):
-    """One decode token per sequence.  q, k [N, H, dk]; v [N, H, dv]; g, beta [N, H] fp32 (the raw a
+    """One decode token per sequence.  q, k [N, Hk, dk]; v [N, H, dv]; g, beta [N, H] fp32 (the raw a
     and b when gate_params [2, H] is given); state [N, H, dv, dk] fp32, updated in place; conv_w
-    [H*(2dk+dv), 4] fp32 with conv_state [N, 3, H*(2dk+dv)] (dtype of q, updated in place), or
+    [C, 4] fp32 with conv_state [N, 3, C] (C = 2*Hk*dk + H*dv; dtype of q, updated in place), or
     neither.  Returns o [N, H, dv]."""
     import torch
     lib = load_library()
-    N, H, dk = q.shape
-    dv = v.shape[2]
+    N, Hk, dk = q.shape
+    H, dv = v.shape[1], v.shape[2]
+    if tuple(k.shape) != tuple(q.shape):
+        raise ValueError("k must have the shape of q")
     dt = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("conv_state", conv_state)):
         _check_dev(name, t, q.dtype)
@@ -174,7 +179,7 @@ def gdn_recurrent_step(q, k, v, g, beta, state, *, o=None, scale=1.0, l2norm=Tru
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     _check_dev("o", o, q.dtype)
     st = lib.gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate_params), _ptr(state),
-                                _ptr(conv_w), _ptr(conv_state), _ptr(o), N, H, dk, dv, dt, float(scale),
+                                _ptr(conv_w), _ptr(conv_state), _ptr(o), N, H, Hk, dk, dv, dt, float(scale),
                                 GDN_QK_L2NORM if l2norm else 0, _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_recurrent_step")

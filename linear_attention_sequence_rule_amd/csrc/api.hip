@@ -81,9 +81,10 @@ int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype,
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,
                   const float* conv_w, void* conv_state, void* o, float* final_state, void* workspace,
-                  size_t* workspace_bytes, int N, int T_tot, int H, int dk, int dv, int dtype, int chunk, float scale,
-                  unsigned flags, void* hip_stream) {
+                  size_t* workspace_bytes, int N, int T_tot, int H, int Hk, int dk, int dv, int dtype, int chunk,
+                  float scale, unsigned flags, void* hip_stream) {
     if (N < 1 || T_tot < 0) return GDN_ERR_INVALID_ARG;
+    if (Hk < 1 || H < 1 || H % Hk != 0) return GDN_ERR_INVALID_ARG;
     int st = check_common(H, dk, dv, dtype, scale, flags);
     if (st != GDN_OK) return st;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
@@ -95,11 +96,12 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
         if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
 
     const size_t es = dtype == GDN_BF16 ? 2 : 4;
-    const size_t tq = (size_t)T_tot * H * dk * es, tv = (size_t)T_tot * H * dv * es;
+    const size_t cc = (size_t)2 * Hk * dk + (size_t)H * dv;  // conv channels per token
+    const size_t tq = (size_t)T_tot * Hk * dk * es, tv = (size_t)T_tot * H * dv * es;
     const size_t tg = (size_t)T_tot * H * 4, ts = (size_t)N * H * dv * dk * 4;
-    const size_t tcu = cu_seqlens ? (size_t)(N + 1) * 4 : 0, tcw = conv_w ? (size_t)H * (2 * dk + dv) * 16 : 0;
+    const size_t tcu = cu_seqlens ? (size_t)(N + 1) * 4 : 0, tcw = conv_w ? cc * 16 : 0;
     const size_t tgp = gate_params ? (size_t)H * 8 : 0;
-    const size_t tcs = conv_state ? (size_t)N * 3 * H * (2 * dk + dv) * es : 0;
+    const size_t tcs = conv_state ? (size_t)N * 3 * cc * es : 0;
     // o must not overlap any input; final_state may equal initial_state exactly but not overlap otherwise.
     if (overlaps(o, tv, q, tq) || overlaps(o, tv, k, tq) || overlaps(o, tv, v, tv) || overlaps(o, tv, g, tg) ||
         overlaps(o, tv, beta, tg) || overlaps(o, tv, initial_state, ts) || overlaps(o, tv, final_state, ts) ||
@@ -159,6 +161,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     a.N = N;
     a.T_tot = T_tot;
     a.H = H;
+    a.Hk = Hk;
     a.dk = dk;
     a.dv = dv;
     a.bf16 = dtype == GDN_BF16;
@@ -173,8 +176,9 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
 
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
                        const float* gate_params, float* state, const float* conv_w, void* conv_state, void* o, int N,
-                       int H, int dk, int dv, int dtype, float scale, unsigned flags, void* hip_stream) {
+                       int H, int Hk, int dk, int dv, int dtype, float scale, unsigned flags, void* hip_stream) {
     if (N < 0 || (flags & kSegMask)) return GDN_ERR_INVALID_ARG;
+    if (Hk < 1 || H < 1 || H % Hk != 0) return GDN_ERR_INVALID_ARG;
     int st = check_common(H, dk, dv, dtype, scale, flags);
     if (st != GDN_OK) return st;
     if (N == 0) return GDN_OK;
@@ -184,10 +188,11 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
     const size_t es = dtype == GDN_BF16 ? 2 : 4;
-    const size_t tq = (size_t)N * H * dk * es, tv = (size_t)N * H * dv * es, tg = (size_t)N * H * 4;
+    const size_t cc = (size_t)2 * Hk * dk + (size_t)H * dv;  // conv channels per token
+    const size_t tq = (size_t)N * Hk * dk * es, tv = (size_t)N * H * dv * es, tg = (size_t)N * H * 4;
     const size_t ts = (size_t)N * H * dv * dk * 4, tgp = gate_params ? (size_t)H * 8 : 0;
-    const size_t tcw = conv_w ? (size_t)H * (2 * dk + dv) * 16 : 0;
-    const size_t tcs = conv_state ? (size_t)N * 3 * H * (2 * dk + dv) * es : 0;
+    const size_t tcw = conv_w ? cc * 16 : 0;
+    const size_t tcs = conv_state ? (size_t)N * 3 * cc * es : 0;
     // o, state and conv_state are written: none of them may share memory with another buffer.
     const void* bufs[] = {q, k, v, g, beta, gate_params, state, conv_w, conv_state, o};
     const size_t lens[] = {tq, tq, tv, tg, tg, tgp, ts, tcw, tcs, tv};
@@ -209,13 +214,33 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
     a.o = o;
     a.N = N;
     a.H = H;
+    a.Hk = Hk;
     a.dk = dk;
     a.dv = dv;
     a.bf16 = dtype == GDN_BF16;
     a.scale = scale;
     a.l2norm = (flags & GDN_QK_L2NORM) ? 1 : 0;
     a.stream = static_cast<hipStream_t>(hip_stream);
-    const hipError_t e = gdn::launch_step(a);
+    hipError_t e = gdn::launch_step(a);
+    if (e == hipSuccess && conv_w && Hk != H) {
+        // a query/key head's history is read by all its value heads' workgroups: shift the conv
+        // state afterwards, as the update after N sequences of one token each
+        gdn::ChunkArgs c{};
+        c.q = q;
+        c.k = k;
+        c.v = v;
+        c.cu = nullptr;
+        c.conv_state = conv_state;
+        c.N = N;
+        c.T_tot = N;
+        c.H = H;
+        c.Hk = Hk;
+        c.dk = dk;
+        c.dv = dv;
+        c.bf16 = a.bf16;
+        c.stream = a.stream;
+        e = gdn::launch_conv_state_update(c);
+    }
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 

@@ -226,12 +226,13 @@ struct Params {
     const __bf16 *q, *k, *v;
     const float *g, *beta, *s0, *conv_w;
     const float* gate_params;  // [2, H]: g and beta hold the raw a and b; or null
-    const __bf16* conv_state;  // [N, 3, H (2 DK + dv)]: conv history before each sequence; or null
+    const __bf16* conv_state;  // [N, 3, 2 Hk DK + H dv]: conv history before each sequence; or null
     const int32_t* cu;
     __bf16* o;
     float* sfin;   // end state per (segment, head): [N*P, H, dv, dk]
     int* negl;     // per (segment, head): 1 if the run stopped at the decay bound, else 0 (or null)
     int N, T_tot, H, dv, nv;
+    int Hk, grp;   // query/key heads; value heads per query/key head (H = Hk grp)
     int P;         // segments per sequence (1 = the sequence in one piece)
     int init;      // InitMode: S0 = s0[n] for segment 0 and zero for the others; IDENTITY = I
                    // (dv = dk rows); PREV = s0[(n P + p - 1) H + h], the state entering segment p
@@ -280,15 +281,15 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 
 template <int DK>
 __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned smb, int rawoff, long t0, int len, int h,
-                                          int vb, int wid, int lane) {
+                                          int hk, int vb, int wid, int lane) {
     lane = opaque(lane);
     using S = Smem<DK>;
     constexpr int PPR = DK / 8;       // 16-byte slots per K/Q row
     constexpr int RPI = 64 / PPR;     // rows per 1 KB instruction
-    const size_t tok0 = (size_t)t0 * p.H + h;
-    const __bf16* kb = uniform_ptr(p.k + tok0 * DK);
-    const __bf16* qb = uniform_ptr(p.q + tok0 * DK);
-    const unsigned rowq = (unsigned)(p.H * DK) * 2u;  // bytes between tokens
+    const size_t tok0 = (size_t)t0 * p.H + h, tokk = (size_t)t0 * p.Hk + hk;
+    const __bf16* kb = uniform_ptr(p.k + tokk * DK);
+    const __bf16* qb = uniform_ptr(p.q + tokk * DK);
+    const unsigned rowq = (unsigned)(p.Hk * DK) * 2u;  // bytes between tokens
 #pragma unroll
     for (int j = 0; j < 16 / RPI; ++j) {
         const int row0 = 16 * wid + RPI * j;
@@ -422,12 +423,13 @@ __device__ __forceinline__ PairLoc pair_loc(int pc) {
 __device__ __forceinline__ unsigned pair_addr(unsigned raw, const PairLoc& l, int r) {
     return raw + l.tile + 2u * (r * l.w + 8u * (l.slot ^ (r & l.mask)) + l.off);
 }
-// conv_w row of the first channel of pair pc (q channels, then k, then v)
+// conv_w row of the first channel of pair pc (q channels of the Hk query/key heads, then k, then
+// v of the H value heads)
 template <int DK>
-__device__ __forceinline__ int pair_wrow(const Params<DK>& p, int pc, int h, int vb) {
-    if (pc < DK / 2) return (p.H + h) * DK + 2 * pc;
-    if (pc < DK) return h * DK + 2 * (pc - DK / 2);
-    return 2 * p.H * DK + h * p.dv + vb * BV + 2 * (pc - DK);
+__device__ __forceinline__ int pair_wrow(const Params<DK>& p, int pc, int h, int hk, int vb) {
+    if (pc < DK / 2) return (p.Hk + hk) * DK + 2 * pc;
+    if (pc < DK) return hk * DK + 2 * (pc - DK / 2);
+    return 2 * p.Hk * DK + h * p.dv + vb * BV + 2 * (pc - DK);
 }
 
 // Halo before the first chunk, by `from`: HALO_ZERO; HALO_TOKENS, the three raw tokens before bos
@@ -435,10 +437,10 @@ __device__ __forceinline__ int pair_wrow(const Params<DK>& p, int pc, int h, int
 // start with conv_state).  Layout [3 rows][NP pairs] of 4-byte words, oldest row first.
 enum HaloFrom { HALO_ZERO = 0, HALO_TOKENS = 1, HALO_STATE = 2 };
 template <int DK>
-__device__ void conv_halo_init(const Params<DK>& p, unsigned halo, int tid, int n, int h, int vb, long bos,
+__device__ void conv_halo_init(const Params<DK>& p, unsigned halo, int tid, int n, int h, int hk, int vb, long bos,
                                int from) {
     constexpr int NP = ConvPlan<DK>::NP;
-    const size_t CC = (size_t)p.H * (2 * DK + p.dv);  // conv channels per token
+    const size_t CC = (size_t)2 * p.Hk * DK + (size_t)p.H * p.dv;  // conv channels per token
     for (int i = tid; i < 3 * NP; i += 512) {
         const int j = i / NP, pc = i % NP;
         uint32_t v = 0;
@@ -447,17 +449,17 @@ __device__ void conv_halo_init(const Params<DK>& p, unsigned halo, int tid, int 
             // one load per source tensor (no selected pointer, which the compiler would keep in memory)
             const int c2 = 2 * (isv ? pc - DK : (isq ? pc - DK / 2 : pc));  // channel within the head's block
             if (from == HALO_STATE) {
-                const size_t hc = isv ? (size_t)2 * p.H * DK + h * p.dv + vb * BV + c2
-                                      : (isq ? (size_t)h * DK + c2 : (size_t)(p.H + h) * DK + c2);
+                const size_t hc = isv ? (size_t)2 * p.Hk * DK + h * p.dv + vb * BV + c2
+                                      : (isq ? (size_t)hk * DK + c2 : (size_t)(p.Hk + hk) * DK + c2);
                 v = *reinterpret_cast<const uint32_t*>(p.conv_state + ((size_t)n * 3 + j) * CC + hc);
             } else {
                 const size_t t = (size_t)(bos - 3 + j);
                 if (isv)
                     v = *reinterpret_cast<const uint32_t*>(p.v + (t * p.H + h) * p.dv + vb * BV + c2);
                 else if (isq)
-                    v = *reinterpret_cast<const uint32_t*>(p.q + (t * p.H + h) * DK + c2);
+                    v = *reinterpret_cast<const uint32_t*>(p.q + (t * p.Hk + hk) * DK + c2);
                 else
-                    v = *reinterpret_cast<const uint32_t*>(p.k + (t * p.H + h) * DK + c2);
+                    v = *reinterpret_cast<const uint32_t*>(p.k + (t * p.Hk + hk) * DK + c2);
             }
         }
         st32(halo + 4u * (j * NP + pc), v);
@@ -471,13 +473,13 @@ struct ConvW {
     float w[ConvPlan<DK>::PER][8];  // taps 0..3 of the pair's first channel, then of the second
 };
 template <int DK>
-__device__ void conv_weights(ConvW<DK>& cw, const Params<DK>& p, int tid, int h, int vb) {
+__device__ void conv_weights(ConvW<DK>& cw, const Params<DK>& p, int tid, int h, int hk, int vb) {
     using CP = ConvPlan<DK>;
 #pragma unroll
     for (int q = 0; q < CP::PER; ++q) {
         const int it = tid + 512 * q, pc = it % CP::NP;
         const bool on = it < CP::ITEMS && !(pc >= DK && p.v_zero);
-        const float* w = p.conv_w + (size_t)(on ? pair_wrow<DK>(p, pc, h, vb) : 0) * 4;
+        const float* w = p.conv_w + (size_t)(on ? pair_wrow<DK>(p, pc, h, hk, vb) : 0) * 4;
 #pragma unroll
         for (int e = 0; e < 8; ++e) cw.w[q][e] = on ? w[e] : 0.f;
     }
@@ -1095,19 +1097,22 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     const bool is_state = wid < 2, is_out = wid == 2 || wid == 3, is_prep = wid >= 4;
     const int pw = wid - 4;  // prep wave index
 
-    // XCD-aware order: the nv row-block workgroups of one (segment, head) share blockIdx mod 8
-    // (same XCD, same L2) when the pair count allows it.
-    const int npairs = p.N * p.P * p.H;
-    int pair, vb;
+    // XCD-aware order: the grp * nv workgroups that read one (segment, query/key head) -- its
+    // value heads times their row blocks -- share blockIdx mod 8 (same XCD, same L2) when the
+    // group count allows it.
+    const int ngroups = p.N * p.P * p.Hk, wpg = p.grp * p.nv;
+    int group, within;
     const int b = blockIdx.x;
-    if (npairs % 8 == 0) {
-        vb = (b / 8) % p.nv;
-        pair = (b / (8 * p.nv)) * 8 + b % 8;
+    if (ngroups % 8 == 0) {
+        group = (b / (8 * wpg)) * 8 + b % 8;
+        within = (b / 8) % wpg;
     } else {
-        vb = b % p.nv;
-        pair = b / p.nv;
+        group = b / wpg;
+        within = b % wpg;
     }
-    const int nseg = pair / p.H, h = pair % p.H;
+    const int vb = within % p.nv;
+    const int pair = group * p.grp + within / p.nv;  // (segment, value head)
+    const int nseg = pair / p.H, h = pair % p.H, hk = h / p.grp;
     const int n = nseg / p.P, seg = nseg % p.P;
     if (p.skip_first && seg == 0) return;
     long bos, eos;
@@ -1169,12 +1174,12 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     const bool conv = p.conv_w != nullptr;
     ConvW<DK> cw;
     if (conv) {
-        conv_weights<DK>(cw, p, tid, h, vb);
+        conv_weights<DK>(cw, p, tid, h, hk, vb);
         const int from = seg > 0 ? (nchunks > 0 ? HALO_TOKENS : HALO_ZERO) : (p.conv_state ? HALO_STATE : HALO_ZERO);
-        conv_halo_init<DK>(p, smb + S::HB, tid, n, h, vb, bos, from);
+        conv_halo_init<DK>(p, smb + S::HB, tid, n, h, hk, vb, bos, from);
     }
     if (nchunks > 0 && is_prep) {
-        dma_chunk<DK>(p, smb, S::raw(0), bos, clen(0), h, vb, pw, lane);
+        dma_chunk<DK>(p, smb, S::raw(0), bos, clen(0), h, hk, vb, pw, lane);
         wait_loads();
         if constexpr (RAW) raw_gates<DK>(p, sm + S::raw(0), clen(0), pw, lane, h);
         zero_tail<DK>(sm + S::raw(0), clen(0), pw, lane);
@@ -1202,8 +1207,8 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
         if (nxt && pw == 3) prep_L<DK, 1>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
         // the loads of chunk k+2 from the output waves, which have slack here (rows 32 (w-2) ..)
         if (far && is_out) {
-            dma_chunk<DK>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, vb, 2 * (wid - 2), lane);
-            dma_chunk<DK>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, vb, 2 * (wid - 2) + 1, lane);
+            dma_chunk<DK>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2), lane);
+            dma_chunk<DK>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2) + 1, lane);
         }
         lds_barrier();
         // ---- B
@@ -1288,6 +1293,8 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     p.N = a.N;
     p.T_tot = a.T_tot;
     p.H = a.H;
+    p.Hk = a.Hk;
+    p.grp = a.H / a.Hk;
     p.dv = c.rows;
     p.nv = c.rows / BV;
     p.P = c.P;

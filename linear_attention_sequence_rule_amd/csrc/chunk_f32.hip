@@ -30,11 +30,11 @@ template <typename T>
 struct F32Params {
     const T *q, *k, *v;
     const float *g, *beta, *gate_params, *s0, *conv_w;
-    const T* conv_state;  // [N,3,H*(2dk+dv)] history before each sequence, or null (zeros)
+    const T* conv_state;  // [N,3,2Hk*dk+H*dv] history before each sequence, or null (zeros)
     const int32_t* cu;
     T* o;
     float* sfin;
-    int N, T_tot, H, dv;
+    int N, T_tot, H, Hk, dv;  // H value heads, Hk query/key heads
     float scale;
     int l2norm;
 };
@@ -91,8 +91,9 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(F32Params<T> p) {
         bos = (long)n * len;
         eos = bos + len;
     }
-    const int H = p.H, dv = p.dv;
-    const size_t hstride = (size_t)H * (2 * DK + dv);  // conv channels per token
+    const int H = p.H, Hk = p.Hk, dv = p.dv;
+    const int hk = h / (H / Hk);                         // query/key head of this value head
+    const size_t hstride = (size_t)2 * Hk * DK + (size_t)H * dv;  // conv channels per token
     const T* hist = p.conv_state ? p.conv_state + (size_t)n * 3 * hstride : nullptr;
     const size_t sbase = ((size_t)n * H + h) * dv * DK + (size_t)vb * BV * DK;
 
@@ -111,12 +112,12 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(F32Params<T> p) {
             if (r < len) {
                 const long t = cs + r;
                 if (p.conv_w) {
-                    const size_t cq = (size_t)h * DK + c, ck = (size_t)H * DK + cq;
-                    qv = conv_silu_at(p.q, p.conv_w + 4 * cq, t, bos, (size_t)H * DK, cq, hist ? hist + cq : nullptr, hstride);
-                    kv = conv_silu_at(p.k, p.conv_w + 4 * ck, t, bos, (size_t)H * DK, cq, hist ? hist + ck : nullptr, hstride);
+                    const size_t cq = (size_t)hk * DK + c, ck = (size_t)Hk * DK + cq;
+                    qv = conv_silu_at(p.q, p.conv_w + 4 * cq, t, bos, (size_t)Hk * DK, cq, hist ? hist + cq : nullptr, hstride);
+                    kv = conv_silu_at(p.k, p.conv_w + 4 * ck, t, bos, (size_t)Hk * DK, cq, hist ? hist + ck : nullptr, hstride);
                 } else {
-                    qv = load1(p.q + ((size_t)t * H + h) * DK + c);
-                    kv = load1(p.k + ((size_t)t * H + h) * DK + c);
+                    qv = load1(p.q + ((size_t)t * Hk + hk) * DK + c);
+                    kv = load1(p.k + ((size_t)t * Hk + hk) * DK + c);
                 }
             }
             sQ[r * L::QS + c] = qv;
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(F32Params<T> p) {
             if (r < len) {
                 const long t = cs + r;
                 const int ch = vb * BV + c;
-                const size_t cv = (size_t)2 * H * DK + (size_t)h * dv + ch;
+                const size_t cv = (size_t)2 * Hk * DK + (size_t)h * dv + ch;
                 vv = p.conv_w ? conv_silu_at(p.v, p.conv_w + 4 * cv, t, bos, (size_t)H * dv, (size_t)h * dv + ch,
                                              hist ? hist + cv : nullptr, hstride)
                               : load1(p.v + ((size_t)t * H + h) * dv + ch);
@@ -279,6 +280,7 @@ hipError_t launch_f32_t(const ChunkArgs& a) {
     p.N = a.N;
     p.T_tot = a.T_tot;
     p.H = a.H;
+    p.Hk = a.Hk;
     p.dv = a.dv;
     p.scale = a.scale;
     p.l2norm = a.l2norm;

@@ -19,9 +19,9 @@ namespace {
 template <typename T>
 __global__ __launch_bounds__(256) void conv_state_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                          const T* __restrict__ v, const int32_t* __restrict__ cu,
-                                                         T* __restrict__ hist, int N, int T_tot, int H, int dk,
-                                                         int dv) {
-    const long CC = (long)H * (2 * dk + dv);
+                                                         T* __restrict__ hist, int N, int T_tot, int H, int Hk,
+                                                         int dk, int dv) {
+    const long CC = 2L * Hk * dk + (long)H * dv;  // q, k channels of the Hk query/key heads, v of the H value heads
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= (long)N * CC) return;
     const int n = (int)(i / CC);
@@ -34,32 +34,34 @@ __global__ __launch_bounds__(256) void conv_state_kernel(const T* __restrict__ q
         bos = (long)n * (T_tot / N);
         eos = bos + T_tot / N;
     }
-    // channel c of token t: q channels, then k, then v ([T, H, d] rows are H d consecutive channels)
-    const T* src;
-    long width, col;
-    if (c < (long)H * dk) {
-        src = q, width = (long)H * dk, col = c;
-    } else if (c < 2L * H * dk) {
-        src = k, width = (long)H * dk, col = c - (long)H * dk;
-    } else {
-        src = v, width = (long)H * dv, col = c - 2L * H * dk;
-    }
+    // channel c of token t: q channels, then k, then v ([T, heads, d] rows are heads * d consecutive
+    // channels); one load per source tensor
+    const long Kc = (long)Hk * dk;
     T* hn = hist + (size_t)n * 3 * CC + c;
     const long len = eos - bos;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const long t = eos - 3 + j;
-        hn[j * CC] = t >= bos ? src[t * width + col] : hn[(j + len) * CC];
+        T x;
+        if (t < bos)
+            x = hn[(j + len) * CC];
+        else if (c < Kc)
+            x = q[t * Kc + c];
+        else if (c < 2 * Kc)
+            x = k[t * Kc + c - Kc];
+        else
+            x = v[t * (long)H * dv + c - 2 * Kc];
+        hn[j * CC] = x;
     }
 }
 
 template <typename T>
 hipError_t launch_t(const ChunkArgs& a) {
-    const long total = (long)a.N * a.H * (2 * a.dk + a.dv);
+    const long total = (long)a.N * (2L * a.Hk * a.dk + (long)a.H * a.dv);
     const unsigned grid = (unsigned)((total + 255) / 256);
     hipLaunchKernelGGL(conv_state_kernel<T>, dim3(grid), dim3(256), 0, a.stream, static_cast<const T*>(a.q),
                        static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.cu, static_cast<T*>(a.conv_state),
-                       a.N, a.T_tot, a.H, a.dk, a.dv);
+                       a.N, a.T_tot, a.H, a.Hk, a.dk, a.dv);
     return hipGetLastError();
 }
 

@@ -12,10 +12,10 @@ struct StepArgs {
     const float *g, *beta;
     const float* gate_params; // [2,H] (A_log, dt_bias): g, beta hold the raw a, b; or null
     float* state;
-    const float* conv_w;      // [H*(2dk+dv),4] or null
-    void* conv_state;         // [N,3,H*(2dk+dv)] dtype, with conv_w
+    const float* conv_w;      // [2Hk*dk+H*dv,4] or null
+    void* conv_state;         // [N,3,2Hk*dk+H*dv] dtype, with conv_w
     void* o;
-    int N, H, dk, dv;
+    int N, H, Hk, dk, dv;     // H value heads, Hk query/key heads (H a multiple of Hk)
     bool bf16;
     float scale;
     int l2norm;
@@ -28,13 +28,13 @@ struct ChunkArgs {
     const float* gate_params; // [2,H] (A_log, dt_bias): g, beta hold the raw a, b; or null
     const float* s0;          // [N,H,dv,dk] or null
     const int32_t* cu;        // [N+1] or null (equal lengths T_tot / N)
-    const float* conv_w;      // [H*(2dk+dv),4] or null
-    void* conv_state;         // [N,3,H*(2dk+dv)] dtype: history before each sequence, or null
+    const float* conv_w;      // [2Hk*dk+H*dv,4] or null
+    void* conv_state;         // [N,3,2Hk*dk+H*dv] dtype: history before each sequence, or null
     void* o;
     float* sfin;              // [N,H,dv,dk] or null
     void* workspace;
     size_t workspace_bytes;
-    int N, T_tot, H, dk, dv;
+    int N, T_tot, H, Hk, dk, dv;  // H value heads, Hk query/key heads (H a multiple of Hk)
     bool bf16;
     float scale;
     int l2norm;

@@ -21,37 +21,43 @@
 namespace gdn {
 
 // Conv prologue of one decode token (page maplevalley.com.cn/news/1910399, section 3.1, 卷积预处理):
-// channel i of the (n, h) pair's 2 DK + DV channels (q, then k, then v) becomes
-// SiLU(w0 h0 + w1 h1 + w2 h2 + w3 x) from the three previous raw inputs h0, h1, h2 (oldest first)
-// in conv_state [N, 3, H (2 DK + DV)] and the raw input x; the result goes to xs[i] (LDS) and the
-// channel's history is shifted by one token in place.  Every history entry is read and written by
-// the one lane that owns its channel, so the shift needs no synchronisation.
+// channel i of the (n, h) pair's 2 DK + DV channels (q and k of its query/key head hk, then v)
+// becomes SiLU(w0 h0 + w1 h1 + w2 h2 + w3 x) from the three previous raw inputs h0, h1, h2
+// (oldest first) in conv_state [N, 3, 2 Hk DK + H DV] and the raw input x; the result goes to
+// xs[i] (LDS).  With shift (each query/key head read by this workgroup only, Hk = H), the
+// channel's history is also shifted by one token in place: every history entry is read and
+// written by the one lane that owns its channel, so no synchronisation is needed.  When several
+// value heads share a query/key head, its history is read by several workgroups and a separate
+// launch shifts the whole conv state afterwards.
 template <int DK, int DV, typename T>
 __device__ __forceinline__ void conv_token(const T* q, const T* k, const T* v, const float* conv_w, T* conv_state,
-                                           float* xs, int nh, int H, int tid) {
-    const size_t CC = (size_t)H * (2 * DK + DV);  // conv channels per token
-    const int h = nh % H;
-    T* hs = conv_state + (size_t)(nh / H) * 3 * CC;
+                                           float* xs, int nh, int H, int Hk, int tid, bool shift) {
+    const size_t CC = (size_t)2 * Hk * DK + (size_t)H * DV;  // conv channels per token
+    const int n = nh / H, h = nh % H, hk = h / (H / Hk);
+    const size_t nk = (size_t)n * Hk + hk;
+    T* hs = conv_state + (size_t)n * 3 * CC;
     for (int i = tid; i < 2 * DK + DV; i += 256) {
         size_t c;
         float x;
         if (i < DK) {
-            c = (size_t)h * DK + i;
-            x = load1(q + (size_t)nh * DK + i);
+            c = (size_t)hk * DK + i;
+            x = load1(q + nk * DK + i);
         } else if (i < 2 * DK) {
-            c = (size_t)(H + h) * DK + (i - DK);
-            x = load1(k + (size_t)nh * DK + (i - DK));
+            c = (size_t)(Hk + hk) * DK + (i - DK);
+            x = load1(k + nk * DK + (i - DK));
         } else {
-            c = (size_t)2 * H * DK + (size_t)h * DV + (i - 2 * DK);
+            c = (size_t)2 * Hk * DK + (size_t)h * DV + (i - 2 * DK);
             x = load1(v + (size_t)nh * DV + (i - 2 * DK));
         }
         const float h0 = load1(hs + c), h1 = load1(hs + CC + c), h2 = load1(hs + 2 * CC + c);
         const float4 w = load4(conv_w + 4 * c);
         const float acc = w.x * h0 + w.y * h1 + w.z * h2 + w.w * x;
         xs[i] = acc / (1.f + expf(-acc));
-        store1(hs + c, h1);
-        store1(hs + CC + c, h2);
-        store1(hs + 2 * CC + c, x);
+        if (shift) {
+            store1(hs + c, h1);
+            store1(hs + CC + c, h2);
+            store1(hs + 2 * CC + c, x);
+        }
     }
 }
 
@@ -64,8 +70,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
                                                    const T* __restrict__ v, const float* __restrict__ g,
                                                    const float* __restrict__ beta, const float* __restrict__ gate_params,
                                                    float* __restrict__ state, const float* __restrict__ conv_w,
-                                                   T* __restrict__ conv_state, T* __restrict__ o, int H, float scale,
-                                                   int l2norm) {
+                                                   T* __restrict__ conv_state, T* __restrict__ o, int H, int Hk,
+                                                   float scale, int l2norm) {
     constexpr int LPR = DK / 4;             // lanes per state row
     constexpr int RPP = 256 / LPR;          // rows per pass of the workgroup
     constexpr int RPL = DV / RPP > 0 ? DV / RPP : 1;  // rows per lane
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     float4 kk, qq;
     float vr[RPL];
     if constexpr (CONV) {
-        conv_token<DK, DV, T>(q, k, v, conv_w, conv_state, xs, nh, H, tid);
+        conv_token<DK, DV, T>(q, k, v, conv_w, conv_state, xs, nh, H, Hk, tid, H == Hk);
         // LDS hand-off only: the barrier need not wait for the state loads in flight
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
@@ -106,8 +112,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 #pragma unroll
         for (int j = 0; j < RPL; ++j) vr[j] = active ? xs[2 * DK + r0 + j * RPP] : 0.f;
     } else {
-        kk = load4(k + (size_t)nh * DK + 4 * c);
-        qq = load4(q + (size_t)nh * DK + 4 * c);
+        const size_t nk = (size_t)(nh / H) * Hk + (nh % H) / (H / Hk);  // (sequence, query/key head)
+        kk = load4(k + nk * DK + 4 * c);
+        qq = load4(q + nk * DK + 4 * c);
 #pragma unroll
         for (int j = 0; j < RPL; ++j) vr[j] = active ? load1(v + (size_t)nh * DV + r0 + j * RPP) : 0.f;
     }
@@ -143,12 +150,12 @@ static hipError_t launch_step_t(const StepArgs& a) {
         hipLaunchKernelGGL((step_kernel<DK, DV, T, true>), dim3(a.N * a.H), dim3(256), 0, a.stream,
                            static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                            a.g, a.beta, a.gate_params, a.state, a.conv_w, static_cast<T*>(a.conv_state),
-                           static_cast<T*>(a.o), a.H, a.scale, a.l2norm);
+                           static_cast<T*>(a.o), a.H, a.Hk, a.scale, a.l2norm);
     else
         hipLaunchKernelGGL((step_kernel<DK, DV, T, false>), dim3(a.N * a.H), dim3(256), 0, a.stream,
                            static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                            a.g, a.beta, a.gate_params, a.state, nullptr, nullptr, static_cast<T*>(a.o), a.H,
-                           a.scale, a.l2norm);
+                           a.Hk, a.scale, a.l2norm);
     return hipGetLastError();
 }
 

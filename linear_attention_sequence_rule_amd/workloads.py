@@ -61,7 +61,8 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 class Workload:
     """Inputs of one gdn_chunk_fwd / gdn_recurrent_step call, host side.
 
-    q, k, v are uint16 bf16 bit patterns (dtype 'bf16') or float32 (dtype 'f32').
+    q, k, v are uint16 bf16 bit patterns (dtype 'bf16') or float32 (dtype 'f32').  H counts the
+    value heads; q and k have Hk query/key heads (``q.shape[1]``), Hk = H unless grouped.
     """
     name: str
     dtype: str
@@ -84,6 +85,10 @@ class Workload:
     @property
     def T_tot(self) -> int:
         return int(self.q.shape[0])
+
+    @property
+    def Hk(self) -> int:
+        return int(self.q.shape[1])
 
     def as_float(self, name: str) -> np.ndarray:
         """q/k/v (or any array field) widened exactly to float32."""
@@ -154,11 +159,12 @@ def raw_gate_inputs(seed, lengths, H):
     return a.astype(np.float32), b.astype(np.float32), np.ascontiguousarray(gp)
 
 
-def conv_inputs(seed, N, H, dk, dv, dtype):
-    """Conv weights ~N(0, 0.5) [H(2dk+dv), 4] float32 and a conv history [N, 3, H(2dk+dv)] of
-    standard normals in the storage dtype (bf16 bit patterns or float32): the three raw inputs
-    before each sequence, as a previous call would have left them."""
-    C = H * (2 * dk + dv)
+def conv_inputs(seed, N, H, dk, dv, dtype, Hk=None):
+    """Conv weights ~N(0, 0.5) [C, 4] float32 and a conv history [N, 3, C] of standard normals in
+    the storage dtype (bf16 bit patterns or float32): the three raw inputs before each sequence, as
+    a previous call would have left them.  C = 2 Hk dk + H dv conv channels (Hk = H by default)."""
+    Hk = H if Hk is None else Hk
+    C = 2 * Hk * dk + H * dv
     cw = _rng(seed, "conv_w").normal(0.0, 0.5, size=(C, 4)).astype(np.float32)
     x = _rng(seed, "conv_hist").standard_normal((N, 3, C), dtype=np.float32)
     return cw, (f32_to_bf16_bits(x) if dtype == "bf16" else x)
@@ -175,10 +181,11 @@ def _states(seed, N, H, dv, dk, std, pool):
 
 
 def make(name="custom", *, seed=0, N=1, T=None, lengths=None, H=2, dk=32, dv=32, dtype="bf16",
-         s0_std=None, conv=False, varlen=False, chunk=64) -> Workload:
+         s0_std=None, conv=False, varlen=False, chunk=64, Hk=None) -> Workload:
     """Draw one prefill workload.
 
     ``lengths`` (list) gives per-sequence token counts; otherwise N sequences of T tokens.
+    ``Hk`` query/key heads shared by groups of the H value heads (default: Hk = H).
     ``varlen`` marks the workload as packed (cu_seqlens passed to the kernels even when the
     lengths happen to be equal).  ``s0_std`` None means a zero initial state (passed as NULL).
     """
@@ -187,14 +194,15 @@ def make(name="custom", *, seed=0, N=1, T=None, lengths=None, H=2, dk=32, dv=32,
     lengths = np.asarray(lengths, dtype=np.int64)
     N = len(lengths)
     with ThreadPoolExecutor(_workers()) as pool:
-        q = _normal_tokens(seed, "q", lengths, H, dk, dtype, pool)
-        k = _normal_tokens(seed, "k", lengths, H, dk, dtype, pool)
+        Hk = H if Hk is None else Hk
+        q = _normal_tokens(seed, "q", lengths, Hk, dk, dtype, pool)
+        k = _normal_tokens(seed, "k", lengths, Hk, dk, dtype, pool)
         v = _normal_tokens(seed, "v", lengths, H, dv, dtype, pool)
         g, beta, A_log, dt_bias = _gates(seed, lengths, H)
         s0 = _states(seed, N, H, dv, dk, s0_std, pool) if s0_std is not None else None
     cw = None
     if conv:
-        cw = _rng(seed, "conv_w").normal(0.0, 0.5, size=(H * (2 * dk + dv), 4)).astype(np.float32)
+        cw = _rng(seed, "conv_w").normal(0.0, 0.5, size=(2 * Hk * dk + H * dv, 4)).astype(np.float32)
     cu = None
     if varlen:
         cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
@@ -263,14 +271,19 @@ class DecodeWorkload:
         x = getattr(self, name)
         return bf16_bits_to_f32(x) if x.dtype == np.uint16 else x
 
+    @property
+    def Hk(self) -> int:
+        return int(self.q.shape[1])
 
-def decode(N=256, H=32, dk=128, dv=128, dtype="bf16", seed=3, state_std=0.02, name="decode"):
+
+def decode(N=256, H=32, dk=128, dv=128, dtype="bf16", seed=3, state_std=0.02, name="decode", Hk=None):
     """One token per sequence: 256 sequences x 32 heads, d=128, bf16 q/k/v, fp32 state
     ~N(0, 0.02) (512 MiB), gates as for prefill, seed 3."""
     lengths = np.ones(N, dtype=np.int64)
     with ThreadPoolExecutor(_workers()) as pool:
-        q = _normal_tokens(seed, "q", lengths, H, dk, dtype, pool)
-        k = _normal_tokens(seed, "k", lengths, H, dk, dtype, pool)
+        Hk = H if Hk is None else Hk
+        q = _normal_tokens(seed, "q", lengths, Hk, dk, dtype, pool)
+        k = _normal_tokens(seed, "k", lengths, Hk, dk, dtype, pool)
         v = _normal_tokens(seed, "v", lengths, H, dv, dtype, pool)
         g, beta, _, _ = _gates(seed, lengths, H)
         st = _states(seed, N, H, dv, dk, state_std, pool)

@@ -47,12 +47,14 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every case below fails va
 
 def chunk(lib, **kw):
     a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, gp=None, s0=None, cu=None, conv=None,
-             cst=None, o=FAKE * 6, sf=None, ws=None, wsb=None, N=1, T=64, H=1, dk=32, dv=32, dtype=1, chunk=64,
-             scale=1.0, flags=1)
+             cst=None, o=FAKE * 6, sf=None, ws=None, wsb=None, N=1, T=64, H=1, Hk=None, dk=32, dv=32, dtype=1,
+             chunk=64, scale=1.0, flags=1)
     a.update(kw)
+    if a["Hk"] is None:
+        a["Hk"] = a["H"]
     return lib.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["gp"], a["s0"], a["cu"], a["conv"],
-                             a["cst"], a["o"], a["sf"], a["ws"], a["wsb"], a["N"], a["T"], a["H"], a["dk"], a["dv"],
-                             a["dtype"], a["chunk"], a["scale"], a["flags"], None)
+                             a["cst"], a["o"], a["sf"], a["ws"], a["wsb"], a["N"], a["T"], a["H"], a["Hk"], a["dk"],
+                             a["dv"], a["dtype"], a["chunk"], a["scale"], a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -78,6 +80,9 @@ def chunk(lib, **kw):
     (dict(conv=FAKE * 7, cst=FAKE + 256), gdn.GDN_ERR_INVALID_ARG),    # conv state inside q
     (dict(conv=FAKE * 7, cst=FAKE * 7 + 64), gdn.GDN_ERR_INVALID_ARG),  # conv state overlaps conv_w
     (dict(conv=FAKE * 7, cst=FAKE * 8 + 4), gdn.GDN_ERR_INVALID_ARG),   # misaligned conv state
+    (dict(H=4, Hk=3), gdn.GDN_ERR_INVALID_ARG),           # value heads not a multiple of query/key heads
+    (dict(H=2, Hk=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(H=2, Hk=4), gdn.GDN_ERR_INVALID_ARG),
 ])
 def test_chunk_validation(lib, kw, status):
     assert chunk(lib, **kw) == status
@@ -144,13 +149,17 @@ def test_workspace_size_validation(lib):
     (dict(conv=FAKE * 7, cst=FAKE * 8 + 2), gdn.GDN_ERR_INVALID_ARG),    # misaligned
     (dict(gp=FAKE * 100 + 16), gdn.GDN_ERR_INVALID_ARG),    # gate parameters inside o
     (dict(gp=FAKE * 9 + 4), gdn.GDN_ERR_INVALID_ARG),       # misaligned gate parameters
+    (dict(H=3, Hk=2), gdn.GDN_ERR_INVALID_ARG),             # value heads not a multiple of query/key heads
+    (dict(Hk=0), gdn.GDN_ERR_INVALID_ARG),
 ])
 def test_step_validation(lib, kw, status):
     a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, gp=None, state=FAKE * 6, conv=None, cst=None,
-             o=FAKE * 100, N=2, H=1, dk=32, dv=32, dtype=1, scale=1.0, flags=1)
+             o=FAKE * 100, N=2, H=1, Hk=None, dk=32, dv=32, dtype=1, scale=1.0, flags=1)
     a.update(kw)
+    if a["Hk"] is None:
+        a["Hk"] = a["H"]
     assert lib.gdn_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["gp"], a["state"], a["conv"],
-                                  a["cst"], a["o"], a["N"], a["H"], a["dk"], a["dv"], a["dtype"], a["scale"],
+                                  a["cst"], a["o"], a["N"], a["H"], a["Hk"], a["dk"], a["dv"], a["dtype"], a["scale"],
                                   a["flags"], None) == status
 
 

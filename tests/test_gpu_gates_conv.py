@@ -149,18 +149,18 @@ def test_conv_state_decode(dtype, dk, dv):
     np.testing.assert_array_equal(_hist_to_f64(cs), h_ref)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_prefill_split_then_decode_with_conv_and_raw_gates(dtype):
+@pytest.mark.parametrize("dtype,H,Hk", [("f32", 2, 2), ("bf16", 2, 2), ("f32", 4, 2), ("bf16", 6, 2)])
+def test_prefill_split_then_decode_with_conv_and_raw_gates(dtype, H, Hk):
     """One sequence set fed as prefill(part 1) -> prefill(part 2) -> three decode steps, carrying
     the state and the conv state through the calls, with raw gates throughout, against the oracle
-    over the whole sequences in one pass."""
+    over the whole sequences in one pass (also with value heads sharing query/key heads)."""
     from linear_attention_sequence_rule_amd import gdn_chunk_fwd, gdn_recurrent_step
     import torch
     dk = dv = 64 if dtype == "f32" else 128
     lengths = [150, 71, 5]
-    wl = W.make("pd_conv", seed=460, lengths=lengths, H=2, dk=dk, dv=dv, dtype=dtype, s0_std=0.05, conv=True,
-                varlen=True)
-    a, b, gp = W.raw_gate_inputs(460, wl.lengths, wl.H)
+    wl = W.make("pd_conv", seed=460 + H + Hk, lengths=lengths, H=H, Hk=Hk, dk=dk, dv=dv, dtype=dtype, s0_std=0.05,
+                conv=True, varlen=True)
+    a, b, gp = W.raw_gate_inputs(wl.meta["seed"], wl.lengths, wl.H)
     g, beta = _oracle_gates(a, b, gp)
     o_ref, s_ref, _, h_ref = _oracle(wl, g, beta)
     cu = np.concatenate([[0], np.cumsum(lengths)])
@@ -171,7 +171,7 @@ def test_prefill_split_then_decode_with_conv_and_raw_gates(dtype):
     dev = {name: TL.to_dev(getattr(wl, name)) for name in ("q", "k", "v")}
     da, db, dgp, dcw = TL.to_dev(a), TL.to_dev(b), TL.to_dev(gp), TL.to_dev(wl.conv_w)
     state = TL.to_dev(wl.s0)
-    cs = torch.zeros((wl.N, 3, wl.H * (2 * dk + dv)), dtype=dev["q"].dtype, device=state.device)
+    cs = torch.zeros((wl.N, 3, 2 * Hk * dk + H * dv), dtype=dev["q"].dtype, device=state.device)
     o_all = np.full((cu[-1], wl.H, dv), np.nan)
     for idx in parts:
         lens = [int(((idx >= cu[n]) & (idx < cu[n + 1])).sum()) for n in range(wl.N)]
@@ -189,4 +189,4 @@ def test_prefill_split_then_decode_with_conv_and_raw_gates(dtype):
         o_all[cu[1:] - 3 + j] = TL.o_to_f64(o)
     e = TL.compare(wl, o_all, state.cpu().numpy().astype(np.float64), o_ref, s_ref)
     np.testing.assert_array_equal(_hist_to_f64(cs), h_ref)
-    _flush("prefill->prefill->decode conv+raw gates %s %s" % (dtype, e))
+    _flush("prefill->prefill->decode conv+raw gates %s H=%d Hk=%d %s" % (dtype, H, Hk, e))
