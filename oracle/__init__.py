@@ -48,6 +48,8 @@ def _load():
         lib.gdn_oracle_step.restype = ctypes.c_int
         lib.gdn_oracle_step.argtypes = [P] * 9 + [ctypes.c_int] * 5 + [
             ctypes.c_double, ctypes.c_int, ctypes.c_int]
+        lib.gdn_oracle_gated_norm.restype = None
+        lib.gdn_oracle_gated_norm.argtypes = [P] * 4 + [ctypes.c_long, ctypes.c_int, ctypes.c_double]
         lib.gdn_oracle_gates.restype = None
         lib.gdn_oracle_gates.argtypes = [P] * 6 + [ctypes.c_long, ctypes.c_int]
         _lib = lib
@@ -147,3 +149,14 @@ def gates(a, b, A_log, dt_bias):
     _load().gdn_oracle_gates(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(g), _ptr(beta),
                              T, H)
     return g, beta
+
+
+def gated_norm(o, z, w, eps):
+    """Output epilogue in fp64: each row of o (last axis dv) divided by sqrt(mean(o^2) + eps), times
+    (1 + w) and sigmoid(z).  o, z [..., dv]; w [dv].  Returns a new array of o's shape."""
+    o, z, w = (_f64(x) for x in (o, z, w))
+    assert z.shape == o.shape and w.shape == (o.shape[-1],)
+    dv = o.shape[-1]
+    out = np.empty_like(o)
+    _load().gdn_oracle_gated_norm(_ptr(o), _ptr(z), _ptr(w), _ptr(out), o.size // dv if dv else 0, dv, float(eps))
+    return out

@@ -266,3 +266,22 @@ void gdn_oracle_gates(const double* a, const double* b, const double* A_log,
             beta[t * H + h] = 1.0 / (1.0 + exp(-b[t * H + h]));
         }
 }
+
+/* gdn_oracle_gated_norm -- the output epilogue: a zero-centred RMSNorm of each (token, head) row of
+ * o over dv (page maplevalley.com.cn/news/1910399, section 3.2 Zero-Centered RMSNorm: normalise by
+ * rsqrt(mean(x^2) + eps), with a learnable scale stored as an offset from 1 and initialised to
+ * zero), then a sigmoid output gate (page "GDN融合门控注意力的动态资源分配机制，AI智能体调动实战演练",
+ * section 2, the paragraph on the dynamics of Gated DeltaNet: a learned gate, usually a sigmoid,
+ * scales the output after the attention computation and before the residual connection):
+ *     out[r, i] = o[r, i] / sqrt(mean_i o[r, i]^2 + eps) * (1 + w[i]) * sigmoid(z[r, i]).
+ * o, z, out [rows, dv] (out may equal o); w [dv]. */
+void gdn_oracle_gated_norm(const double* o, const double* z, const double* w, double* out, long rows, int dv,
+                           double eps) {
+    for (long r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int i = 0; i < dv; ++i) ss += o[r * dv + i] * o[r * dv + i];
+        const double inv = 1.0 / sqrt(ss / dv + eps);
+        for (int i = 0; i < dv; ++i)
+            out[r * dv + i] = o[r * dv + i] * inv * (1.0 + w[i]) / (1.0 + exp(-z[r * dv + i]));
+    }
+}

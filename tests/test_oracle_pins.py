@@ -549,3 +549,34 @@ def test_grouped_heads_equal_repeated_heads(Hk, H):
     np.testing.assert_array_equal(std, std2)
     for n in range(N):
         np.testing.assert_array_equal(_expand_conv_rows(hdo[n].T, Hk, rep, dk, H, dv).T, hdo2[n])
+
+
+# -------------------------------------------------------------------------- output epilogue
+
+def test_gated_norm_hand_worked():
+    """o = (3, 4): mean square 12.5; w = (0, 1) gives scales (1, 2); z = 0 gives sigmoid 1/2."""
+    out = oracle.gated_norm(np.array([[3.0, 4.0]]), np.zeros((1, 2)), np.array([0.0, 1.0]), 0.0)
+    np.testing.assert_allclose(out[0], [3 / (2 * math.sqrt(12.5)), 4 / math.sqrt(12.5)], rtol=1e-15)
+
+
+def test_gated_norm_properties():
+    r = rnd(23)
+    o = r.standard_normal((7, 3, 16))
+    z = r.standard_normal(o.shape)
+    w = r.normal(0, 0.3, size=16)
+    # an open gate (sigmoid(40) = 1 in fp64) and w = 0: unit root mean square per row (eps = 0)
+    out = oracle.gated_norm(o, np.full(o.shape, 40.0), np.zeros(16), 0.0)
+    np.testing.assert_allclose(np.sqrt((out ** 2).mean(-1)), 1.0, rtol=1e-14)
+    # z = 0 halves the open-gate output exactly
+    half = oracle.gated_norm(o, np.zeros(o.shape), w, 1e-3)
+    full = oracle.gated_norm(o, np.full(o.shape, 40.0), w, 1e-3)
+    np.testing.assert_array_equal(half * 2, full)
+    # invariant under a positive rescaling of o when eps = 0
+    np.testing.assert_allclose(oracle.gated_norm(5.5 * o, z, w, 0.0), oracle.gated_norm(o, z, w, 0.0), rtol=1e-13)
+    # w = -1 closes every channel
+    assert not oracle.gated_norm(o, z, -np.ones(16), 1e-3).any()
+    # eps enters as mean(o^2) + eps: a row of zeros except o0 = 1, dv = 16, eps = 1/16 -> o0 / sqrt(1/8)
+    e = np.zeros((1, 16))
+    e[0, 0] = 1.0
+    out = oracle.gated_norm(e, np.full(e.shape, 40.0), np.zeros(16), 1.0 / 16)
+    assert out[0, 0] == pytest.approx(math.sqrt(8.0), rel=1e-15)
