@@ -37,6 +37,15 @@
  * stored in the input dtype exactly, so a prefill split at any point and resumed, or followed by
  * decode steps, sees the same conv inputs as one call over the whole sequence.
  *
+ * Output epilogue (both entry points).  out_gate z [rows of o, dv] dtype and norm_weight w [dv]
+ * fp32, both NULL or both given: then every (token, head) row of o leaves as
+ *     o * rsqrt(mean over dv of o^2 + norm_eps) * (1 + w) * sigmoid(z)
+ * -- a zero-centred RMSNorm (page maplevalley.com.cn/news/1910399, section 3.2: the learnable scale
+ * is stored as an offset from 1, initialised to zero; section 4.2 suggests an eps of 1e-3 in bf16)
+ * followed by a sigmoid output gate (page "GDN融合门控注意力的动态资源分配机制，AI智能体调动实战演练",
+ * section 2).  The decode step applies it inside its kernel; the prefill runs it as one more pass
+ * over o after the rule (a head's output row is spread over several workgroups there).
+ *
  * Conventions shared by every entry point
  *  - All pointers are DEVICE pointers to contiguous, row-major memory, 16-byte aligned, except
  *    where stated.  Nothing is copied to or from the host.
@@ -110,6 +119,8 @@ extern "C" {
  *  conv_state  [N, 3, C] dtype         NULL, or the conv history, read and overwritten in
  *                                      place ("Conv state" above); requires conv_w.  Must not
  *                                      overlap any other buffer.
+ *  out_gate    [T_tot, H, dv]  dtype   NULL, or z of the output epilogue (above); with norm_weight
+ *  norm_weight [dv]            fp32    NULL, or w of the output epilogue; with out_gate
  *  o           [T_tot, H, dv]  dtype   output; must not alias any input
  *  final_state [N, H, dv, dk] fp32     last state per (sequence, head), or NULL = not written.
  *                                      May alias initial_state exactly (same pointer).
@@ -126,7 +137,8 @@ extern "C" {
  *  dtype       GDN_F32 or GDN_BF16     (fp32 path: exact fp32 arithmetic throughout; bf16 path:
  *                                      bf16 MFMA operands, fp32 accumulation, fp32 state)
  *  chunk       64                      chunk length; other values -> GDN_ERR_UNSUPPORTED
- *  scale       output scale (1.0 = o_t = S_t q_t)
+ *  scale       output scale (1.0 = o_t = S_t q_t), applied before the epilogue
+ *  norm_eps    eps of the epilogue's RMSNorm (finite, >= 0; ignored without out_gate)
  *  flags       GDN_QK_L2NORM, optionally | GDN_SEGMENTS(n)
  *  hip_stream  hipStream_t to launch on
  *
@@ -144,10 +156,11 @@ extern "C" {
  */
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,
-                  const float* conv_w, void* conv_state, void* o, float* final_state,
-                  void* workspace, size_t* workspace_bytes, int N,
-                  int T_tot, int H, int Hk, int dk, int dv, int dtype, int chunk, float scale,
-                  unsigned flags, void* hip_stream);
+                  const float* conv_w, void* conv_state, const void* out_gate,
+                  const float* norm_weight, void* o, float* final_state, void* workspace,
+                  size_t* workspace_bytes, int N, int T_tot, int H, int Hk, int dk, int dv,
+                  int dtype, int chunk, float scale, float norm_eps, unsigned flags,
+                  void* hip_stream);
 
 /*
  * gdn_chunk_workspace_size -- the workspace gdn_chunk_fwd needs for these sizes (H = value heads;
@@ -176,14 +189,17 @@ int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype,
  *         given: then q, k and v are the raw inputs of the conv prologue, conv + SiLU (and the L2
  *         norm) run on them with the three previous raw inputs from conv_state, and conv_state is
  *         shifted in place by one token (the oldest dropped, this token's raw inputs appended)
+ *  out_gate [N, H, dv] dtype and norm_weight [dv] fp32: both NULL, or the output epilogue (above),
+ *         applied inside the step kernel
  *  o      [N, H, dv] dtype, must not alias any input
  *  N, H, Hk >= 1 (N = 0 is a no-op returning GDN_OK), H a multiple of Hk; dk, dv in {32, 64, 128}
- *  dtype, scale, flags, hip_stream as for gdn_chunk_fwd
+ *  dtype, scale, norm_eps, flags, hip_stream as for gdn_chunk_fwd
  */
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                        const float* beta, const float* gate_params, float* state,
-                       const float* conv_w, void* conv_state, void* o, int N, int H, int Hk, int dk,
-                       int dv, int dtype, float scale, unsigned flags, void* hip_stream);
+                       const float* conv_w, void* conv_state, const void* out_gate,
+                       const float* norm_weight, void* o, int N, int H, int Hk, int dk, int dv,
+                       int dtype, float scale, float norm_eps, unsigned flags, void* hip_stream);
 
 /* gdn_status_string -- static, human-readable name of a status code (never NULL). */
 const char* gdn_status_string(int status);

@@ -54,11 +54,11 @@ def load_library():
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, U, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_float
     lib.gdn_chunk_fwd.restype = I
-    lib.gdn_chunk_fwd.argtypes = [P] * 14 + [I] * 8 + [F, U, P]
+    lib.gdn_chunk_fwd.argtypes = [P] * 16 + [I] * 8 + [F, F, U, P]
     lib.gdn_chunk_workspace_size.restype = I
     lib.gdn_chunk_workspace_size.argtypes = [I] * 9 + [U, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdn_recurrent_step.restype = I
-    lib.gdn_recurrent_step.argtypes = [P] * 10 + [I] * 6 + [F, U, P]
+    lib.gdn_recurrent_step.argtypes = [P] * 12 + [I] * 6 + [F, F, U, P]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_status_string.argtypes = [I]
     _lib = lib
@@ -112,13 +112,16 @@ def gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype=GDN_BF16, chunk=64, has_
 
 def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=None, *, N=None, o=None,
                   final_state=None, output_final_state=True, scale=1.0, l2norm=True, chunk=64, workspace=None,
-                  segments=0, gate_params=None, conv_state=None, stream=None):
+                  segments=0, gate_params=None, conv_state=None, out_gate=None, norm_weight=None, norm_eps=1e-3,
+                  stream=None):
     """Chunked prefill.  q, k [T_tot, Hk, dk]; v [T_tot, H, dv] (bf16 or fp32; H a multiple of Hk, value
     head h reads query/key head h // (H // Hk)); g, beta [T_tot, H] fp32 (the raw a and b when
     gate_params [2, H] = (A_log, dt_bias) is given); initial_state [N, H, dv, dk] fp32 or None;
     cu_seqlens [N+1] int32 or None (N equal sequences, N given or 1); conv_w [C, 4] fp32 or None,
     C = 2*Hk*dk + H*dv; conv_state [N, 3, C] in the dtype of q, read as the conv history and
-    updated in place, or None; segments per sequence (0 = automatic).
+    updated in place, or None; segments per sequence (0 = automatic); out_gate [T_tot, H, dv] (dtype
+    of q) with norm_weight [dv] fp32: the output epilogue o * rsqrt(mean(o^2) + norm_eps) * (1 + w) *
+    sigmoid(z) (norm_eps default 1e-3, the value the pages suggest for bf16).
     A workspace (uint8 device tensor) is allocated here when the call needs one and none large
     enough is given.  Returns (o, final_state or None)."""
     import torch
@@ -128,10 +131,10 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=
     if tuple(k.shape) != tuple(q.shape):
         raise ValueError("k must have the shape of q")
     dt = _dtype_code(q)
-    for name, t in (("q", q), ("k", k), ("v", v), ("conv_state", conv_state)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("conv_state", conv_state), ("out_gate", out_gate)):
         _check_dev(name, t, q.dtype)
     for name, t in (("g", g), ("beta", beta), ("gate_params", gate_params), ("initial_state", initial_state),
-                    ("conv_w", conv_w), ("final_state", final_state)):
+                    ("conv_w", conv_w), ("final_state", final_state), ("norm_weight", norm_weight)):
         _check_dev(name, t, torch.float32)
     _check_dev("cu_seqlens", cu_seqlens, torch.int32)
     if cu_seqlens is not None:
@@ -150,20 +153,21 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = ctypes.c_size_t(need)
     st = lib.gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate_params), _ptr(initial_state),
-                           _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_state), _ptr(o), _ptr(final_state),
-                           _ptr(workspace), ctypes.byref(ws_bytes), N, T_tot, H, Hk, dk, dv, dt, chunk, float(scale),
-                           flags, _stream(stream))
+                           _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_state), _ptr(out_gate), _ptr(norm_weight),
+                           _ptr(o), _ptr(final_state), _ptr(workspace), ctypes.byref(ws_bytes), N, T_tot, H, Hk, dk,
+                           dv, dt, chunk, float(scale), float(norm_eps), flags, _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_fwd")
     return o, final_state
 
 
 def gdn_recurrent_step(q, k, v, g, beta, state, *, o=None, scale=1.0, l2norm=True, gate_params=None, conv_w=None,
-                       conv_state=None, stream=None):
+                       conv_state=None, out_gate=None, norm_weight=None, norm_eps=1e-3, stream=None):
     """One decode token per sequence.  q, k [N, Hk, dk]; v [N, H, dv]; g, beta [N, H] fp32 (the raw a
     and b when gate_params [2, H] is given); state [N, H, dv, dk] fp32, updated in place; conv_w
     [C, 4] fp32 with conv_state [N, 3, C] (C = 2*Hk*dk + H*dv; dtype of q, updated in place), or
-    neither.  Returns o [N, H, dv]."""
+    neither; out_gate [N, H, dv] with norm_weight [dv]: the output epilogue, as for gdn_chunk_fwd.
+    Returns o [N, H, dv]."""
     import torch
     lib = load_library()
     N, Hk, dk = q.shape
@@ -171,16 +175,18 @@ def gdn_recurrent_step(q, k, v, g, beta, state, *, o=None, scale=1.0, l2norm=Tru
     if tuple(k.shape) != tuple(q.shape):
         raise ValueError("k must have the shape of q")
     dt = _dtype_code(q)
-    for name, t in (("q", q), ("k", k), ("v", v), ("conv_state", conv_state)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("conv_state", conv_state), ("out_gate", out_gate)):
         _check_dev(name, t, q.dtype)
-    for name, t in (("g", g), ("beta", beta), ("gate_params", gate_params), ("state", state), ("conv_w", conv_w)):
+    for name, t in (("g", g), ("beta", beta), ("gate_params", gate_params), ("state", state), ("conv_w", conv_w),
+                    ("norm_weight", norm_weight)):
         _check_dev(name, t, torch.float32)
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     _check_dev("o", o, q.dtype)
     st = lib.gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate_params), _ptr(state),
-                                _ptr(conv_w), _ptr(conv_state), _ptr(o), N, H, Hk, dk, dv, dt, float(scale),
-                                GDN_QK_L2NORM if l2norm else 0, _stream(stream))
+                                _ptr(conv_w), _ptr(conv_state), _ptr(out_gate), _ptr(norm_weight), _ptr(o), N, H, Hk,
+                                dk, dv, dt, float(scale), float(norm_eps), GDN_QK_L2NORM if l2norm else 0,
+                                _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_recurrent_step")
     return o

@@ -80,9 +80,10 @@ int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype,
 
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,
-                  const float* conv_w, void* conv_state, void* o, float* final_state, void* workspace,
-                  size_t* workspace_bytes, int N, int T_tot, int H, int Hk, int dk, int dv, int dtype, int chunk,
-                  float scale, unsigned flags, void* hip_stream) {
+                  const float* conv_w, void* conv_state, const void* out_gate, const float* norm_weight, void* o,
+                  float* final_state, void* workspace, size_t* workspace_bytes, int N, int T_tot, int H, int Hk,
+                  int dk, int dv, int dtype, int chunk, float scale, float norm_eps, unsigned flags,
+                  void* hip_stream) {
     if (N < 1 || T_tot < 0) return GDN_ERR_INVALID_ARG;
     if (Hk < 1 || H < 1 || H % Hk != 0) return GDN_ERR_INVALID_ARG;
     int st = check_common(H, dk, dv, dtype, scale, flags);
@@ -91,7 +92,10 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     if (!cu_seqlens && T_tot % N != 0) return GDN_ERR_INVALID_ARG;
     if (T_tot > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_INVALID_ARG;
     if (conv_state && !conv_w) return GDN_ERR_INVALID_ARG;
-    const void* ptrs[] = {q, k, v, g, beta, gate_params, initial_state, cu_seqlens, conv_w, conv_state, o, final_state};
+    if ((out_gate == nullptr) != (norm_weight == nullptr)) return GDN_ERR_INVALID_ARG;
+    if (out_gate && !(isfinite(norm_eps) && norm_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, gate_params, initial_state, cu_seqlens, conv_w, conv_state, out_gate,
+                          norm_weight, o, final_state};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
 
@@ -102,7 +106,12 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     const size_t tcu = cu_seqlens ? (size_t)(N + 1) * 4 : 0, tcw = conv_w ? cc * 16 : 0;
     const size_t tgp = gate_params ? (size_t)H * 8 : 0;
     const size_t tcs = conv_state ? (size_t)N * 3 * cc * es : 0;
+    const size_t tz = out_gate ? tv : 0, tw = norm_weight ? (size_t)dv * 4 : 0;
     // o must not overlap any input; final_state may equal initial_state exactly but not overlap otherwise.
+    if (overlaps(o, tv, out_gate, tz) || overlaps(o, tv, norm_weight, tw) ||
+        overlaps(final_state, ts, out_gate, tz) || overlaps(final_state, ts, norm_weight, tw) ||
+        overlaps(conv_state, tcs, out_gate, tz) || overlaps(conv_state, tcs, norm_weight, tw))
+        return GDN_ERR_INVALID_ARG;
     if (overlaps(o, tv, q, tq) || overlaps(o, tv, k, tq) || overlaps(o, tv, v, tv) || overlaps(o, tv, g, tg) ||
         overlaps(o, tv, beta, tg) || overlaps(o, tv, initial_state, ts) || overlaps(o, tv, final_state, ts) ||
         overlaps(o, tv, cu_seqlens, tcu) || overlaps(o, tv, conv_w, tcw) || overlaps(o, tv, gate_params, tgp) ||
@@ -133,13 +142,14 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
             return GDN_ERR_WORKSPACE;
         }
         if (!aligned16(workspace)) return GDN_ERR_INVALID_ARG;
-        const size_t tw = *workspace_bytes;
-        if (overlaps(workspace, tw, q, tq) || overlaps(workspace, tw, k, tq) || overlaps(workspace, tw, v, tv) ||
-            overlaps(workspace, tw, g, tg) || overlaps(workspace, tw, beta, tg) ||
-            overlaps(workspace, tw, initial_state, ts) || overlaps(workspace, tw, final_state, ts) ||
-            overlaps(workspace, tw, o, tv) || overlaps(workspace, tw, cu_seqlens, tcu) ||
-            overlaps(workspace, tw, conv_w, tcw) || overlaps(workspace, tw, gate_params, tgp) ||
-            overlaps(workspace, tw, conv_state, tcs))
+        const size_t twk = *workspace_bytes;
+        if (overlaps(workspace, twk, q, tq) || overlaps(workspace, twk, k, tq) || overlaps(workspace, twk, v, tv) ||
+            overlaps(workspace, twk, g, tg) || overlaps(workspace, twk, beta, tg) ||
+            overlaps(workspace, twk, initial_state, ts) || overlaps(workspace, twk, final_state, ts) ||
+            overlaps(workspace, twk, o, tv) || overlaps(workspace, twk, cu_seqlens, tcu) ||
+            overlaps(workspace, twk, conv_w, tcw) || overlaps(workspace, twk, gate_params, tgp) ||
+            overlaps(workspace, twk, conv_state, tcs) || overlaps(workspace, twk, out_gate, tz) ||
+            overlaps(workspace, twk, norm_weight, tw))
             return GDN_ERR_INVALID_ARG;
     }
 
@@ -154,6 +164,9 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     a.cu = cu_seqlens;
     a.conv_w = conv_w;
     a.conv_state = conv_state;
+    a.out_gate = out_gate;
+    a.norm_weight = norm_weight;
+    a.norm_eps = norm_eps;
     a.o = o;
     a.sfin = final_state;
     a.workspace = workspace;
@@ -171,12 +184,15 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     a.stream = static_cast<hipStream_t>(hip_stream);
     hipError_t e = a.bf16 ? gdn::launch_chunk_bf16(a) : gdn::launch_chunk_f32(a);
     if (e == hipSuccess && conv_state) e = gdn::launch_conv_state_update(a);
+    if (e == hipSuccess && out_gate)
+        e = gdn::launch_gated_norm(o, a.out_gate, a.norm_weight, (long)T_tot * H, dv, a.norm_eps, a.bf16, a.stream);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                       const float* gate_params, float* state, const float* conv_w, void* conv_state, void* o, int N,
-                       int H, int Hk, int dk, int dv, int dtype, float scale, unsigned flags, void* hip_stream) {
+                       const float* gate_params, float* state, const float* conv_w, void* conv_state,
+                       const void* out_gate, const float* norm_weight, void* o, int N, int H, int Hk, int dk, int dv,
+                       int dtype, float scale, float norm_eps, unsigned flags, void* hip_stream) {
     if (N < 0 || (flags & kSegMask)) return GDN_ERR_INVALID_ARG;
     if (Hk < 1 || H < 1 || H % Hk != 0) return GDN_ERR_INVALID_ARG;
     int st = check_common(H, dk, dv, dtype, scale, flags);
@@ -184,7 +200,9 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
     if (N == 0) return GDN_OK;
     if (!q || !k || !v || !g || !beta || !state || !o) return GDN_ERR_INVALID_ARG;
     if ((conv_w == nullptr) != (conv_state == nullptr)) return GDN_ERR_INVALID_ARG;
-    const void* ptrs[] = {q, k, v, g, beta, gate_params, state, conv_w, conv_state, o};
+    if ((out_gate == nullptr) != (norm_weight == nullptr)) return GDN_ERR_INVALID_ARG;
+    if (out_gate && !(isfinite(norm_eps) && norm_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, gate_params, state, conv_w, conv_state, out_gate, norm_weight, o};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN_ERR_INVALID_ARG;
     const size_t es = dtype == GDN_BF16 ? 2 : 4;
@@ -193,14 +211,14 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
     const size_t ts = (size_t)N * H * dv * dk * 4, tgp = gate_params ? (size_t)H * 8 : 0;
     const size_t tcw = conv_w ? cc * 16 : 0;
     const size_t tcs = conv_state ? (size_t)N * 3 * cc * es : 0;
+    const size_t tz = out_gate ? tv : 0, tnw = norm_weight ? (size_t)dv * 4 : 0;
     // o, state and conv_state are written: none of them may share memory with another buffer.
-    const void* bufs[] = {q, k, v, g, beta, gate_params, state, conv_w, conv_state, o};
-    const size_t lens[] = {tq, tq, tv, tg, tg, tgp, ts, tcw, tcs, tv};
-    for (int w = 6; w < 10; ++w) {
-        if (w == 7) continue;  // conv_w is read only
-        for (int i = 0; i < 10; ++i)
+    const void* bufs[] = {q, k, v, g, beta, gate_params, conv_w, out_gate, norm_weight, state, conv_state, o};
+    const size_t lens[] = {tq, tq, tv, tg, tg, tgp, tcw, tz, tnw, ts, tcs, tv};
+    constexpr int nb = 12, first_written = 9;
+    for (int w = first_written; w < nb; ++w)
+        for (int i = 0; i < nb; ++i)
             if (i != w && overlaps(bufs[w], lens[w], bufs[i], lens[i])) return GDN_ERR_INVALID_ARG;
-    }
     gdn::StepArgs a;
     a.q = q;
     a.k = k;
@@ -211,6 +229,9 @@ int gdn_recurrent_step(const void* q, const void* k, const void* v, const float*
     a.state = state;
     a.conv_w = conv_w;
     a.conv_state = conv_state;
+    a.out_gate = out_gate;
+    a.norm_weight = norm_weight;
+    a.norm_eps = norm_eps;
     a.o = o;
     a.N = N;
     a.H = H;

@@ -14,6 +14,9 @@ struct StepArgs {
     float* state;
     const float* conv_w;      // [2Hk*dk+H*dv,4] or null
     void* conv_state;         // [N,3,2Hk*dk+H*dv] dtype, with conv_w
+    const void* out_gate;     // [N,H,dv] dtype: output gate z of the epilogue, or null
+    const float* norm_weight; // [dv]: zero-centred RMSNorm scale offset (with out_gate)
+    float norm_eps;
     void* o;
     int N, H, Hk, dk, dv;     // H value heads, Hk query/key heads (H a multiple of Hk)
     bool bf16;
@@ -30,6 +33,9 @@ struct ChunkArgs {
     const int32_t* cu;        // [N+1] or null (equal lengths T_tot / N)
     const float* conv_w;      // [2Hk*dk+H*dv,4] or null
     void* conv_state;         // [N,3,2Hk*dk+H*dv] dtype: history before each sequence, or null
+    const void* out_gate;     // [T_tot,H,dv] dtype: output gate z of the epilogue, or null
+    const float* norm_weight; // [dv]: zero-centred RMSNorm scale offset (with out_gate)
+    float norm_eps;
     void* o;
     float* sfin;              // [N,H,dv,dk] or null
     void* workspace;
@@ -61,6 +67,9 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a);
 // conv_state <- the three raw inputs before the token after each sequence (in place, after the
 // chunk kernels have read it as history).
 hipError_t launch_conv_state_update(const ChunkArgs& a);
+// o <- o * rsqrt(mean over dv of o^2 + eps) * (1 + w) * sigmoid(z), in place, rows of dv elements.
+hipError_t launch_gated_norm(void* o, const void* z, const float* w, long rows, int dv, float eps, bool is_bf16,
+                             hipStream_t stream);
 hipError_t launch_seg_combine(float* E, const float* A, const int* negl, float* sfin, int N, int P, int H, int dk,
                               int dv, hipStream_t stream);
 

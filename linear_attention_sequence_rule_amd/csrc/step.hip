@@ -63,25 +63,31 @@ __device__ __forceinline__ void conv_token(const T* q, const T* k, const T* v, c
 
 // With CONV, q, k and v are the raw inputs of the conv prologue (conv_token above) and conv_state
 // carries the history; with gate_params, g and beta are the raw a and b of the gate
-// parameterisation (section 2.1 of the same page).
+// parameterisation (section 2.1 of the same page).  With NORM, the output row goes through the
+// epilogue o * rsqrt(mean(o^2) + eps) * (1 + w) * sigmoid(z) before it is stored (zero-centred
+// RMSNorm, section 3.2 of the same page; sigmoid output gate, page
+// "GDN融合门控注意力的动态资源分配机制，AI智能体调动实战演练", section 2): the workgroup holds the
+// whole row, so the epilogue costs no extra pass over o.
 // At least 4 waves per SIMD (at most 128 VGPRs): the state streams through at full occupancy.
-template <int DK, int DV, typename T, bool CONV>
+template <int DK, int DV, typename T, bool CONV, bool NORM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const float* __restrict__ g,
                                                    const float* __restrict__ beta, const float* __restrict__ gate_params,
                                                    float* __restrict__ state, const float* __restrict__ conv_w,
-                                                   T* __restrict__ conv_state, T* __restrict__ o, int H, int Hk,
-                                                   float scale, int l2norm) {
+                                                   T* __restrict__ conv_state, const T* __restrict__ out_gate,
+                                                   const float* __restrict__ norm_weight, T* __restrict__ o, int H,
+                                                   int Hk, float scale, float norm_eps, int l2norm) {
     constexpr int LPR = DK / 4;             // lanes per state row
     constexpr int RPP = 256 / LPR;          // rows per pass of the workgroup
     constexpr int RPL = DV / RPP > 0 ? DV / RPP : 1;  // rows per lane
-    static_assert(DV % RPP == 0 || RPP > DV, "row tiling");
+    static_assert(DV % RPP == 0 && RPP <= DV, "row tiling: every lane owns rows (no lane leaves early)");
     __shared__ float xs[CONV ? 2 * DK + DV : 1];
+    __shared__ float xo[NORM ? DV : 1];     // the output row before the epilogue
+    __shared__ float red[NORM ? 4 : 1];     // per-wave sums of squares
     const int nh = blockIdx.x;
     const int tid = threadIdx.x;
     const int c = tid % LPR;        // float4 column of this lane
     const int r0 = tid / LPR;       // first row of this lane
-    const bool active = r0 < DV;    // only when RPP > DV (small heads)
 
     // the gates first: their temporaries are dead before the state rows arrive
     float gg = g[nh], b = beta[nh];
@@ -94,14 +100,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
 
     float* S = state + (size_t)nh * DV * DK;
     float4 s[RPL];
-    if (active) {
 #pragma unroll
-        for (int j = 0; j < RPL; ++j)
-            s[j] = nt_load4(S + (size_t)(r0 + j * RPP) * DK + 4 * c);
-    }
+    for (int j = 0; j < RPL; ++j) s[j] = nt_load4(S + (size_t)(r0 + j * RPP) * DK + 4 * c);
 
     float4 kk, qq;
-    float vr[RPL];
+    float vr[CONV ? 1 : RPL];  // values (with CONV they stay in LDS until used)
     if constexpr (CONV) {
         conv_token<DK, DV, T>(q, k, v, conv_w, conv_state, xs, nh, H, Hk, tid, H == Hk);
         // LDS hand-off only: the barrier need not wait for the state loads in flight
@@ -109,14 +112,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
         __builtin_amdgcn_s_barrier();
         qq = *reinterpret_cast<const float4*>(xs + 4 * c);
         kk = *reinterpret_cast<const float4*>(xs + DK + 4 * c);
-#pragma unroll
-        for (int j = 0; j < RPL; ++j) vr[j] = active ? xs[2 * DK + r0 + j * RPP] : 0.f;
     } else {
         const size_t nk = (size_t)(nh / H) * Hk + (nh % H) / (H / Hk);  // (sequence, query/key head)
         kk = load4(k + nk * DK + 4 * c);
         qq = load4(q + nk * DK + 4 * c);
 #pragma unroll
-        for (int j = 0; j < RPL; ++j) vr[j] = active ? load1(v + (size_t)nh * DV + r0 + j * RPP) : 0.f;
+        for (int j = 0; j < RPL; ++j) vr[j] = load1(v + (size_t)nh * DV + r0 + j * RPP);
     }
     if (l2norm) {
         float sk = group_sum<LPR>(kk.x * kk.x + kk.y * kk.y + kk.z * kk.z + kk.w * kk.w);
@@ -127,36 +128,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     }
     const float kq = group_sum<LPR>(kk.x * qq.x + kk.y * qq.y + kk.z * qq.z + kk.w * qq.w);
 
-    if (!active) return;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
         float r = group_sum<LPR>(s[j].x * kk.x + s[j].y * kk.y + s[j].z * kk.z + s[j].w * kk.w);
         float p = group_sum<LPR>(s[j].x * qq.x + s[j].y * qq.y + s[j].z * qq.z + s[j].w * qq.w);
-        const float u = b * (vr[j] - alpha * r);
+        const float vj = CONV ? xs[2 * DK + r0 + j * RPP] : vr[CONV ? 0 : j];
+        const float u = b * (vj - alpha * r);
         s[j].x = alpha * s[j].x + u * kk.x;
         s[j].y = alpha * s[j].y + u * kk.y;
         s[j].z = alpha * s[j].z + u * kk.z;
         s[j].w = alpha * s[j].w + u * kk.w;
-        if (c == 0) store1(o + (size_t)nh * DV + r0 + j * RPP, scale * (alpha * p + u * kq));
+        if (c == 0) {
+            const float ov = scale * (alpha * p + u * kq);
+            if constexpr (NORM)
+                xo[r0 + j * RPP] = ov;
+            else
+                store1(o + (size_t)nh * DV + r0 + j * RPP, ov);
+        }
     }
 #pragma unroll
     for (int j = 0; j < RPL; ++j)
         nt_store4(S + (size_t)(r0 + j * RPP) * DK + 4 * c, s[j]);
+    if constexpr (NORM) {
+        // the epilogue inputs of output element tid, loaded only now so that they hold no registers
+        // through the row loop; their latency overlaps the reduction
+        float zo = 0.f, wo = 0.f;
+        if (tid < DV) {
+            zo = load1(out_gate + (size_t)nh * DV + tid);
+            wo = norm_weight[tid];
+        }
+        // LDS hand-offs only: the barriers need not wait for the state stores in flight
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        const float x = tid < DV ? xo[tid] : 0.f;
+        const float ss = group_sum<64>(x * x);
+        if (tid % 64 == 0) red[tid / 64] = ss;
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) * (1.f / DV) + norm_eps);
+        if (tid < DV) store1(o + (size_t)nh * DV + tid, x * inv * (1.f + wo) / (1.f + expf(-zo)));
+    }
+}
+
+template <int DK, int DV, typename T, bool CONV, bool NORM>
+static hipError_t launch_step_v(const StepArgs& a) {
+    hipLaunchKernelGGL((step_kernel<DK, DV, T, CONV, NORM>), dim3(a.N * a.H), dim3(256), 0, a.stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.g, a.beta,
+                       a.gate_params, a.state, a.conv_w, static_cast<T*>(a.conv_state),
+                       static_cast<const T*>(a.out_gate), a.norm_weight, static_cast<T*>(a.o), a.H, a.Hk, a.scale,
+                       a.norm_eps, a.l2norm);
+    return hipGetLastError();
 }
 
 template <int DK, int DV, typename T>
 static hipError_t launch_step_t(const StepArgs& a) {
     if (a.conv_w)
-        hipLaunchKernelGGL((step_kernel<DK, DV, T, true>), dim3(a.N * a.H), dim3(256), 0, a.stream,
-                           static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                           a.g, a.beta, a.gate_params, a.state, a.conv_w, static_cast<T*>(a.conv_state),
-                           static_cast<T*>(a.o), a.H, a.Hk, a.scale, a.l2norm);
-    else
-        hipLaunchKernelGGL((step_kernel<DK, DV, T, false>), dim3(a.N * a.H), dim3(256), 0, a.stream,
-                           static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                           a.g, a.beta, a.gate_params, a.state, nullptr, nullptr, static_cast<T*>(a.o), a.H,
-                           a.Hk, a.scale, a.l2norm);
-    return hipGetLastError();
+        return a.out_gate ? launch_step_v<DK, DV, T, true, true>(a) : launch_step_v<DK, DV, T, true, false>(a);
+    return a.out_gate ? launch_step_v<DK, DV, T, false, true>(a) : launch_step_v<DK, DV, T, false, false>(a);
 }
 
 template <typename T>

@@ -47,14 +47,14 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every case below fails va
 
 def chunk(lib, **kw):
     a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, gp=None, s0=None, cu=None, conv=None,
-             cst=None, o=FAKE * 6, sf=None, ws=None, wsb=None, N=1, T=64, H=1, Hk=None, dk=32, dv=32, dtype=1,
-             chunk=64, scale=1.0, flags=1)
+             cst=None, z=None, nw=None, o=FAKE * 6, sf=None, ws=None, wsb=None, N=1, T=64, H=1, Hk=None, dk=32,
+             dv=32, dtype=1, chunk=64, scale=1.0, eps=1e-3, flags=1)
     a.update(kw)
     if a["Hk"] is None:
         a["Hk"] = a["H"]
     return lib.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["gp"], a["s0"], a["cu"], a["conv"],
-                             a["cst"], a["o"], a["sf"], a["ws"], a["wsb"], a["N"], a["T"], a["H"], a["Hk"], a["dk"],
-                             a["dv"], a["dtype"], a["chunk"], a["scale"], a["flags"], None)
+                             a["cst"], a["z"], a["nw"], a["o"], a["sf"], a["ws"], a["wsb"], a["N"], a["T"], a["H"],
+                             a["Hk"], a["dk"], a["dv"], a["dtype"], a["chunk"], a["scale"], a["eps"], a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -83,6 +83,13 @@ def chunk(lib, **kw):
     (dict(H=4, Hk=3), gdn.GDN_ERR_INVALID_ARG),           # value heads not a multiple of query/key heads
     (dict(H=2, Hk=0), gdn.GDN_ERR_INVALID_ARG),
     (dict(H=2, Hk=4), gdn.GDN_ERR_INVALID_ARG),
+    (dict(z=FAKE * 9), gdn.GDN_ERR_INVALID_ARG),                      # output gate without norm weight
+    (dict(nw=FAKE * 9), gdn.GDN_ERR_INVALID_ARG),                     # norm weight without output gate
+    (dict(z=FAKE * 9, nw=FAKE * 10, eps=-1.0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(z=FAKE * 9, nw=FAKE * 10, eps=float("inf")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(z=FAKE * 6 + 512, nw=FAKE * 10), gdn.GDN_ERR_INVALID_ARG),  # output gate overlaps o
+    (dict(z=FAKE * 9, nw=FAKE * 6 + 64), gdn.GDN_ERR_INVALID_ARG),    # norm weight inside o
+    (dict(z=FAKE * 9 + 8, nw=FAKE * 10), gdn.GDN_ERR_INVALID_ARG),    # misaligned
 ])
 def test_chunk_validation(lib, kw, status):
     assert chunk(lib, **kw) == status
@@ -151,16 +158,20 @@ def test_workspace_size_validation(lib):
     (dict(gp=FAKE * 9 + 4), gdn.GDN_ERR_INVALID_ARG),       # misaligned gate parameters
     (dict(H=3, Hk=2), gdn.GDN_ERR_INVALID_ARG),             # value heads not a multiple of query/key heads
     (dict(Hk=0), gdn.GDN_ERR_INVALID_ARG),
+    (dict(z=FAKE * 9), gdn.GDN_ERR_INVALID_ARG),                      # output gate without norm weight
+    (dict(z=FAKE * 9, nw=FAKE * 10, eps=float("nan")), gdn.GDN_ERR_INVALID_ARG),
+    (dict(z=FAKE * 100 + 64, nw=FAKE * 10), gdn.GDN_ERR_INVALID_ARG),  # output gate overlaps o
+    (dict(z=FAKE * 9, nw=FAKE * 6 + 256), gdn.GDN_ERR_INVALID_ARG),   # norm weight inside the state
 ])
 def test_step_validation(lib, kw, status):
     a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, g=FAKE * 4, beta=FAKE * 5, gp=None, state=FAKE * 6, conv=None, cst=None,
-             o=FAKE * 100, N=2, H=1, Hk=None, dk=32, dv=32, dtype=1, scale=1.0, flags=1)
+             z=None, nw=None, o=FAKE * 100, N=2, H=1, Hk=None, dk=32, dv=32, dtype=1, scale=1.0, eps=1e-3, flags=1)
     a.update(kw)
     if a["Hk"] is None:
         a["Hk"] = a["H"]
     assert lib.gdn_recurrent_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["gp"], a["state"], a["conv"],
-                                  a["cst"], a["o"], a["N"], a["H"], a["Hk"], a["dk"], a["dv"], a["dtype"], a["scale"],
-                                  a["flags"], None) == status
+                                  a["cst"], a["z"], a["nw"], a["o"], a["N"], a["H"], a["Hk"], a["dk"], a["dv"],
+                                  a["dtype"], a["scale"], a["eps"], a["flags"], None) == status
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch):

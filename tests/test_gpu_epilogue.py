@@ -1,0 +1,116 @@
+"""Parity of the output epilogue (zero-centred RMSNorm over dv, then a sigmoid output gate) through
+the C ABI against the fp64 oracle.
+
+Tolerances.  fp32 paths: max|gpu - ref| / max|ref| <= 1e-4, as for o.  bf16 decode: o is formed in
+fp32 inside the step kernel and rounded to bf16 once, after the epilogue: |gpu - ref| <= 2^-8 |ref|
++ 1e-5 elementwise.  bf16 prefill: the epilogue runs on the stored bf16 o, whose own bar is
+max|do| <= 2e-2; to first order the normalisation maps an error do in a row to
+m (do - o (o . do) / (dv ms)) / rms with m = (1 + w) sigmoid(z), which is at most 2 m max|do| / rms,
+so the bar is |gpu - ref| <= 2 m 2e-2 / rms_ref + 2^-8 |ref| + 1e-5 per element, rms_ref the
+oracle row's sqrt(mean o^2 + eps).
+"""
+import numpy as np
+import pytest
+
+import gdn_testlib as TL
+import oracle
+from linear_attention_sequence_rule_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+def _epilogue_inputs(seed, rows_shape, dv, dtype):
+    r = np.random.default_rng([seed, 77])
+    z = r.standard_normal(rows_shape + (dv,), dtype=np.float32)
+    w = r.normal(0.0, 0.2, size=dv).astype(np.float32)
+    return (W.f32_to_bf16_bits(z) if dtype == "bf16" else z), w
+
+
+def _zf(z):
+    return W.bf16_bits_to_f32(z) if z.dtype == np.uint16 else z
+
+
+@pytest.mark.parametrize("dtype,dk,dv,eps", [("f32", 32, 64, 1e-6), ("f32", 64, 32, 1e-3),
+                                             ("bf16", 128, 128, 1e-3), ("bf16", 64, 32, 1e-6)])
+def test_epilogue_prefill(dtype, dk, dv, eps):
+    from linear_attention_sequence_rule_amd import gdn_chunk_fwd
+    import torch
+    wl = W.make("epi", seed=600 + dk + dv, lengths=[130, 0, 64, 1, 77], H=3, dk=dk, dv=dv, dtype=dtype,
+                s0_std=0.05, varlen=True)
+    z, w = _epilogue_inputs(wl.meta["seed"], (wl.T_tot, wl.H), dv, dtype)
+    o, sf = gdn_chunk_fwd(TL.to_dev(wl.q), TL.to_dev(wl.k), TL.to_dev(wl.v), TL.to_dev(wl.g), TL.to_dev(wl.beta),
+                          TL.to_dev(wl.s0), TL.to_dev(wl.cu_seqlens), out_gate=TL.to_dev(z), norm_weight=TL.to_dev(w),
+                          norm_eps=eps)
+    torch.cuda.synchronize()
+    og, sg = TL.o_to_f64(o), sf.cpu().numpy().astype(np.float64)
+    o_ref, s_ref = TL.run_oracle(wl)
+    ref = oracle.gated_norm(o_ref, _zf(z), w, eps)
+    # the state is untouched by the epilogue
+    TL.compare(wl, o_ref, sg, o_ref, s_ref)
+    if dtype == "f32":
+        assert np.abs(og - ref).max() / np.abs(ref).max() <= TL.F32_REL
+    else:
+        m = (1.0 + w.astype(np.float64)) / (1.0 + np.exp(-_zf(z).astype(np.float64)))
+        rms = np.sqrt((o_ref ** 2).mean(-1, keepdims=True) + eps)
+        bound = 2 * m * TL.BF16_O_ABS / rms + 2.0 ** -8 * np.abs(ref) + 1e-5
+        excess = np.abs(og - ref) / bound
+        assert excess.max() <= 1.0, excess.max()
+        _flush("epilogue prefill bf16 %d %d: max err %.3g, max err/bound %.3g" % (dk, dv, np.abs(og - ref).max(),
+                                                                                   excess.max()))
+
+
+def test_epilogue_prefill_segments_and_conv():
+    """The epilogue after the segmented path with the conv prologue and grouped heads."""
+    from linear_attention_sequence_rule_amd import gdn_chunk_fwd
+    import torch
+    wl = W.make("epi_seg", seed=611, lengths=[64 * 36 + 11, 5], H=4, Hk=2, dk=128, dv=128, dtype="bf16",
+                s0_std=0.02, conv=True, varlen=True)
+    z, w = _epilogue_inputs(611, (wl.T_tot, wl.H), 128, "bf16")
+    o, _ = gdn_chunk_fwd(TL.to_dev(wl.q), TL.to_dev(wl.k), TL.to_dev(wl.v), TL.to_dev(wl.g), TL.to_dev(wl.beta),
+                         TL.to_dev(wl.s0), TL.to_dev(wl.cu_seqlens), TL.to_dev(wl.conv_w), segments=3,
+                         out_gate=TL.to_dev(z), norm_weight=TL.to_dev(w), norm_eps=1e-3)
+    torch.cuda.synchronize()
+    og = TL.o_to_f64(o)
+    o_ref, _ = TL.run_oracle(wl)
+    ref = oracle.gated_norm(o_ref, _zf(z), w, 1e-3)
+    m = (1.0 + w.astype(np.float64)) / (1.0 + np.exp(-_zf(z).astype(np.float64)))
+    rms = np.sqrt((o_ref ** 2).mean(-1, keepdims=True) + 1e-3)
+    excess = np.abs(og - ref) / (2 * m * TL.BF16_O_ABS / rms + 2.0 ** -8 * np.abs(ref) + 1e-5)
+    assert excess.max() <= 1.0, excess.max()
+    _flush("epilogue segments+conv+groups: max err %.3g, max err/bound %.3g" % (np.abs(og - ref).max(), excess.max()))
+
+
+@pytest.mark.parametrize("dtype,H,Hk,dk,dv,conv", [("f32", 3, 3, 64, 64, False), ("f32", 4, 2, 32, 128, True),
+                                                   ("bf16", 4, 4, 128, 128, False), ("bf16", 4, 2, 128, 128, True),
+                                                   ("bf16", 2, 1, 64, 32, True)])
+def test_epilogue_decode(dtype, H, Hk, dk, dv, conv):
+    from linear_attention_sequence_rule_amd import gdn_recurrent_step
+    import torch
+    seed = 620 + H + Hk + dk + dv
+    dw = W.decode(N=6, H=H, Hk=Hk, dk=dk, dv=dv, dtype=dtype, seed=seed, state_std=0.3)
+    z, w = _epilogue_inputs(seed, (dw.N, H), dv, dtype)
+    cw, hist = W.conv_inputs(seed, dw.N, H, dk, dv, dtype, Hk=Hk) if conv else (None, None)
+    st, cs = TL.to_dev(dw.state), TL.to_dev(hist)
+    o = gdn_recurrent_step(TL.to_dev(dw.q), TL.to_dev(dw.k), TL.to_dev(dw.v), TL.to_dev(dw.g), TL.to_dev(dw.beta),
+                           st, conv_w=TL.to_dev(cw), conv_state=cs, out_gate=TL.to_dev(z), norm_weight=TL.to_dev(w),
+                           norm_eps=1e-3)
+    torch.cuda.synchronize()
+    args = (dw.as_float("q"), dw.as_float("k"), dw.as_float("v"), dw.g, dw.beta, dw.state)
+    if conv:
+        o_ref, s_ref, _ = oracle.step(*args, conv_w=cw, conv_hist=_zf(hist))
+    else:
+        o_ref, s_ref = oracle.step(*args)
+    ref = oracle.gated_norm(o_ref, _zf(z), w, 1e-3)
+    og, sg = TL.o_to_f64(o), st.cpu().numpy().astype(np.float64)
+    if dtype == "f32":
+        assert np.abs(og - ref).max() / np.abs(ref).max() <= TL.F32_REL
+        assert np.abs(sg - s_ref).max() / np.abs(s_ref).max() <= TL.F32_REL
+    else:
+        assert (np.abs(og - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5).all(), np.abs(og - ref).max()
+        d = np.linalg.norm((sg - s_ref).reshape(dw.N * H, -1), axis=1)
+        r = np.linalg.norm(s_ref.reshape(dw.N * H, -1), axis=1)
+        assert (d / r).max() <= TL.BF16_S_RELF
