@@ -11,9 +11,10 @@ The JSON line reports prefill tokens/s as `value`, the HBM roofline of the prefi
 MFMA fraction under algorithmic flop accounting, the decode step (256 sequences x 32 heads, state
 updated in place) as GB/s against HBM, the long-sequence prefill (1 x 262144 tokens, 16 heads,
 segmented) and the packed variable-length prefill with the conv prologue (64 sequences of
-512..16384 tokens, 32 heads) as tokens/s and GB/s, the prefill step with raw gate inputs, the
-decode step with the conv prologue and a conv state, and the fp64 CPU oracle's throughput on the
-host cores.
+512..16384 tokens, 32 heads) as tokens/s and GB/s, the prefill step with raw gate inputs and with
+value heads sharing query/key heads and with the output epilogue, the decode step with the conv
+prologue and a conv state (and with the fused epilogue as well), and the fp64 CPU oracle's
+throughput on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
 """
@@ -218,6 +219,35 @@ def main():
             "hbm_alg_gbs": alg_bytes / rsec / 1e9, "hbm_frac": alg_bytes / rsec / 1e9 / HBM_PEAK_GBS}
         del ra, rb, rgp
 
+        # the prefill step with 16 value heads sharing 8 query/key heads (pairs of value heads read
+        # one query/key head): the q, k bytes per value head halve
+        gw = W.prefill(Hk=8)
+        gq, gk, gv, gg, gb, gs0 = (to_dev(x) for x in (gw.q, gw.k, gw.v, gw.g, gw.beta, gw.s0))
+        go, gsf = torch.empty_like(gv), torch.empty_like(gs0)
+        gsec = timed(lambda: gdn.gdn_chunk_fwd(gq, gk, gv, gg, gb, gs0, N=N, o=go, final_state=gsf, stream=stream), 20)
+        gbytes = tokens * (gw.Hk * 2 * dk * 2 + H * (dv * 2 * 2 + 8)) + 2 * N * H * dv * dk * 4
+        extra["prefill_grouped_heads"] = {
+            "workload": "prefill B=4 T=4096, 16 value heads sharing 8 query/key heads, dk=dv=128 bf16",
+            "value": tokens / gsec, "unit": "tokens/s", "us": gsec * 1e6,
+            "hbm_alg_gbs": gbytes / gsec / 1e9, "hbm_frac": gbytes / gsec / 1e9 / HBM_PEAK_GBS}
+        del gq, gk, gv, gg, gb, gs0, go, gsf, gw
+
+        # the prefill step followed by the output epilogue (zero-centred RMSNorm over dv, sigmoid
+        # output gate), one in-place pass over o
+        ez = to_dev(W.f32_to_bf16_bits(np.random.default_rng([1, 77]).standard_normal((tokens, H, dv),
+                                                                                      dtype=np.float32)))
+        ew = to_dev(np.random.default_rng([1, 78]).normal(0.0, 0.2, size=dv).astype(np.float32))
+        q, k, v, g, b, s0 = copies[0]
+        esec = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, g, b, s0, N=N, o=o, final_state=sf, out_gate=ez,
+                                               norm_weight=ew, stream=stream), 20)
+        ebytes = alg_bytes + tokens * H * dv * 2 + dv * 4
+        extra["prefill_epilogue"] = {
+            "workload": "prefill B=4 T=4096 H=16 dk=dv=128 bf16 + output epilogue (RMSNorm over dv, sigmoid gate z "
+                        "bf16 [T,H,dv]); the epilogue is a separate in-place pass over o",
+            "value": tokens / esec, "unit": "tokens/s", "us": esec * 1e6,
+            "hbm_alg_gbs": ebytes / esec / 1e9, "hbm_frac": ebytes / esec / 1e9 / HBM_PEAK_GBS}
+        del ez, ew
+
         # the decode step with the conv prologue on the raw token (history in a conv state updated in
         # place) and raw gates: the decode side of a layer whose prefill ran the conv
         cw, hist = W.conv_inputs(3, dw.N, dw.H, dw.dk, dw.dv, "bf16")
@@ -226,6 +256,18 @@ def main():
         csec = timed(lambda: gdn.gdn_recurrent_step(dq, dk_, dv_, da, dbr, st, o=od, gate_params=dgp, conv_w=dcw,
                                                     conv_state=dcs, stream=stream), 20)
         cbytes = dec_bytes + dw.N * 2 * 3 * dw.H * (2 * dw.dk + dw.dv) * 2 + dw.H * (2 * dw.dk + dw.dv) * 16
+        dz = to_dev(W.f32_to_bf16_bits(np.random.default_rng([3, 77]).standard_normal((dw.N, dw.H, dw.dv),
+                                                                                      dtype=np.float32)))
+        dwn = to_dev(np.random.default_rng([3, 78]).normal(0.0, 0.2, size=dw.dv).astype(np.float32))
+        nsec = timed(lambda: gdn.gdn_recurrent_step(dq, dk_, dv_, da, dbr, st, o=od, gate_params=dgp, conv_w=dcw,
+                                                    conv_state=dcs, out_gate=dz, norm_weight=dwn, stream=stream), 20)
+        nbytes = cbytes + dw.N * dw.H * dw.dv * 2 + dw.dv * 4
+        extra["decode_full"] = {
+            "workload": "decode 256 sequences x 32 heads, dk=dv=128: raw bf16 token -> conv(4)+SiLU (conv state in "
+                        "place), raw gates, fp32 state in place, output epilogue fused (RMSNorm, sigmoid gate)",
+            "value": nbytes / nsec / 1e9, "unit": "GB/s", "us_per_step": nsec * 1e6,
+            "hbm_frac": nbytes / nsec / 1e9 / HBM_PEAK_GBS}
+        del dz, dwn
         extra["decode_conv"] = {
             "workload": "decode 256 sequences x 32 heads, dk=dv=128, raw bf16 token -> conv(4)+SiLU with a bf16 conv "
                         "state updated in place, raw gates, fp32 state in place",

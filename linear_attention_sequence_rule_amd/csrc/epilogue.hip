@@ -54,31 +54,43 @@ __device__ __forceinline__ void store_vec(bf16* p, const float (&x)[E]) {
 template <typename T, int DV>
 __global__ __launch_bounds__(256) void gated_norm_kernel(T* __restrict__ o, const T* __restrict__ z,
                                                          const float* __restrict__ w, long rows, float eps) {
-    constexpr int E = 16 / sizeof(T);   // elements per lane
+    constexpr int E = 16 / sizeof(T);   // elements per lane and row
     constexpr int LPR = DV / E;         // lanes per row
-    constexpr int RPB = 256 / LPR;      // rows per workgroup
+    constexpr int RPP = 256 / LPR;      // rows per pass of the workgroup
+    constexpr int R = 4;                // passes: every lane has 2 R loads of 16 bytes in flight
     const int tid = threadIdx.x;
-    const long row = (long)blockIdx.x * RPB + tid / LPR;
+    const long row0 = (long)blockIdx.x * (R * RPP) + tid / LPR;
     const int c0 = (tid % LPR) * E;
-    // a row's lanes are LPR consecutive lanes of one wavefront, aligned: whole rows drop out together
-    if (row >= rows) return;
-    float x[E], zz[E], ww[E];
-    load_vec<E>(o + row * DV + c0, x);
-    load_vec<E>(z + row * DV + c0, zz);
+    float ww[E];
     load_vec<E>(w + c0, ww);
-    float ss = 0.f;
+    // a row's lanes are LPR consecutive lanes of one wavefront, aligned: whole rows drop out together
+    float x[R][E], zz[R][E];
 #pragma unroll
-    for (int i = 0; i < E; ++i) ss += x[i] * x[i];
-    ss = group_sum<LPR>(ss);
-    const float inv = rsqrtf(ss * (1.f / DV) + eps);
+    for (int r = 0; r < R; ++r) {
+        const long row = row0 + (long)r * RPP;
+        if (row < rows) {
+            load_vec<E>(o + row * DV + c0, x[r]);
+            load_vec<E>(z + row * DV + c0, zz[r]);
+        }
+    }
 #pragma unroll
-    for (int i = 0; i < E; ++i) x[i] = x[i] * inv * (1.f + ww[i]) / (1.f + expf(-zz[i]));
-    store_vec<E>(o + row * DV + c0, x);
+    for (int r = 0; r < R; ++r) {
+        const long row = row0 + (long)r * RPP;
+        if (row >= rows) break;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < E; ++i) ss += x[r][i] * x[r][i];
+        ss = group_sum<LPR>(ss);
+        const float inv = rsqrtf(ss * (1.f / DV) + eps);
+#pragma unroll
+        for (int i = 0; i < E; ++i) x[r][i] = x[r][i] * inv * (1.f + ww[i]) / (1.f + expf(-zz[r][i]));
+        store_vec<E>(o + row * DV + c0, x[r]);
+    }
 }
 
 template <typename T, int DV>
 hipError_t launch_t(void* o, const void* z, const float* w, long rows, float eps, hipStream_t stream) {
-    constexpr int RPB = 256 / (DV / (16 / (int)sizeof(T)));
+    constexpr int RPB = 4 * (256 / (DV / (16 / (int)sizeof(T))));  // rows per workgroup
     if (rows <= 0) return hipSuccess;
     const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
     hipLaunchKernelGGL((gated_norm_kernel<T, DV>), dim3(grid), dim3(256), 0, stream, static_cast<T*>(o),
