@@ -58,7 +58,7 @@ typedef float fx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int C = 64;        // chunk length
-constexpr int BV = 32;       // state rows per workgroup
+constexpr int BVMAX = 64;    // state rows per workgroup: BV = 64, or 32 when the state has 32 rows
 constexpr int TSTR = C + 8;  // bf16 row stride of T^T, Pm and L^T
 
 __device__ __forceinline__ fx4 mfma(bf16x8 a, bf16x8 b, fx4 c) {
@@ -186,8 +186,8 @@ struct Smem {
     // raw chunk buffer (K, Q, V swizzled, unpadded)
     static constexpr int rK = 0;                     // bf16 [C][DK]
     static constexpr int rQ = rK + C * DK * 2;       // bf16 [C][DK]
-    static constexpr int rV = rQ + C * DK * 2;       // bf16 [C][BV]
-    static constexpr int rG = rV + C * BV * 2;       // raw g [C]
+    static constexpr int rV = rQ + C * DK * 2;       // bf16 [C][BV] (room for BVMAX)
+    static constexpr int rG = rV + C * BVMAX * 2;    // raw g [C]
     static constexpr int rB = rG + C * 4;            // beta [C]
     static constexpr int rBytes = rB + C * 4;
     // gates of a chunk
@@ -204,13 +204,10 @@ struct Smem {
     static constexpr int PM = T + C * TSTR * 2;      // Pm bf16 [C][TSTR], row-major [i][m]
     static constexpr int L = PM + C * TSTR * 2;      // L^T bf16 [C][TSTR]: L^T[j][i] = L_ij
     static constexpr int ORQ = L + C * TSTR * 2;     // rq [C]
-    static constexpr int UH = ORQ + C * 4;           // U hand-off [2 waves][64 lanes][16 bf16]
-    static constexpr int UT = UH + 2 * 64 * 32;      // scaled U, state sub-stage A -> B [2 waves][64 lanes][16 bf16]
-    static constexpr int SH = UT + 2 * 64 * 32;      // S hand-off [2 waves][64 lanes][DK/32][8 bf16]
-    static constexpr int WL = SH + 2 * 64 * (DK / 32) * 16;  // L-prep scratch, per wave: rk, gamma log2e [2][2][C]
+    static constexpr int WL = ORQ + C * 4;           // L-prep scratch, per wave: rk, gamma log2e [2][2][C]
     static constexpr int WP = WL + 4 * C * 4;        // P-prep scratch, per wave: rq, gamma log2e [2][2][C]
     static constexpr int HB = WP + 4 * C * 4;        // conv halo: 3 raw rows [3][DK + BV/2] channel pairs
-    static constexpr int bytes = HB + 3 * (DK + BV / 2) * 4;
+    static constexpr int bytes = HB + 3 * (DK + BVMAX / 2) * 4;
     static_assert(rBytes % 16 == 0 && gBytes % 16 == 0, "alignment");
     static __device__ __forceinline__ int raw(int c) { return R0 + (c % 3) * rBytes; }
     static __device__ __forceinline__ int gates(int c) { return G0 + (c & 1) * gBytes; }
@@ -279,7 +276,7 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
     return reinterpret_cast<const T*>((static_cast<uintptr_t>(hi) << 32) | lo);
 }
 
-template <int DK>
+template <int DK, int BV>
 __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned smb, int rawoff, long t0, int len, int h,
                                           int hk, int vb, int wid, int lane) {
     lane = opaque(lane);
@@ -301,10 +298,16 @@ __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned smb, int
         dma16(qb, voff, lds_addr(smb + lo + S::rQ));
     }
     if (!p.v_zero) {
-        const int row = 16 * wid + lane / 4, slot = lane % 4, part = slot ^ (row % 4);
+        constexpr int VPR = BV / 8;    // 16-byte slots per V row
+        constexpr int VRI = 64 / VPR;  // rows per 1 KB instruction
         const __bf16* vbase = uniform_ptr(p.v + tok0 * p.dv + vb * BV);
-        const unsigned voff = (unsigned)min(row, len - 1) * (unsigned)(p.H * p.dv) * 2u + 16u * part;
-        dma16(vbase, voff, lds_addr(smb + rawoff + S::rV + 16 * wid * BV * 2));
+#pragma unroll
+        for (int j = 0; j < 16 / VRI; ++j) {
+            const int row0 = 16 * wid + VRI * j;
+            const int row = row0 + lane / VPR, slot = lane % VPR, part = slot ^ (row % VPR);
+            const unsigned voff = (unsigned)min(row, len - 1) * (unsigned)(p.H * p.dv) * 2u + 16u * part;
+            dma16(vbase, voff, lds_addr(smb + rawoff + S::rV + row0 * BV * 2));
+        }
     }
     if (wid < 2) {
         const float* gbase = uniform_ptr((wid == 0 ? p.g : p.beta) + tok0);
@@ -314,7 +317,7 @@ __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned smb, int
 }
 
 // After this wave's loads landed: clear its rows past the tail (last chunk of a sequence only).
-template <int DK>
+template <int DK, int BV>
 __device__ __forceinline__ void zero_tail(unsigned char* raw, int len, int wid, int lane) {
     lane = opaque(lane);
     using S = Smem<DK>;
@@ -394,7 +397,7 @@ __device__ __forceinline__ float silu(float x) {
     return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
 
-template <int DK>
+template <int DK, int BV>
 struct ConvPlan {
     static constexpr int NP = DK + BV / 2;              // channel pairs: K (DK/2), Q (DK/2), V (BV/2)
     static constexpr int ITEMS = NP * (C / 8);
@@ -407,7 +410,7 @@ struct ConvPlan {
 struct PairLoc {
     unsigned tile, w, mask, slot, off;
 };
-template <int DK>
+template <int DK, int BV>
 __device__ __forceinline__ PairLoc pair_loc(int pc) {
     using S = Smem<DK>;
     const bool isv = pc >= DK, isq = !isv && pc >= DK / 2;
@@ -425,7 +428,7 @@ __device__ __forceinline__ unsigned pair_addr(unsigned raw, const PairLoc& l, in
 }
 // conv_w row of the first channel of pair pc (q channels of the Hk query/key heads, then k, then
 // v of the H value heads)
-template <int DK>
+template <int DK, int BV>
 __device__ __forceinline__ int pair_wrow(const Params<DK>& p, int pc, int h, int hk, int vb) {
     if (pc < DK / 2) return (p.Hk + hk) * DK + 2 * pc;
     if (pc < DK) return hk * DK + 2 * (pc - DK / 2);
@@ -436,10 +439,10 @@ __device__ __forceinline__ int pair_wrow(const Params<DK>& p, int pc, int h, int
 // (a segment that starts inside a sequence); HALO_STATE, the conv history of sequence n (a sequence
 // start with conv_state).  Layout [3 rows][NP pairs] of 4-byte words, oldest row first.
 enum HaloFrom { HALO_ZERO = 0, HALO_TOKENS = 1, HALO_STATE = 2 };
-template <int DK>
+template <int DK, int BV>
 __device__ void conv_halo_init(const Params<DK>& p, unsigned halo, int tid, int n, int h, int hk, int vb, long bos,
                                int from) {
-    constexpr int NP = ConvPlan<DK>::NP;
+    constexpr int NP = ConvPlan<DK, BV>::NP;
     const size_t CC = (size_t)2 * p.Hk * DK + (size_t)p.H * p.dv;  // conv channels per token
     for (int i = tid; i < 3 * NP; i += 512) {
         const int j = i / NP, pc = i % NP;
@@ -468,18 +471,18 @@ __device__ void conv_halo_init(const Params<DK>& p, unsigned halo, int tid, int 
 }
 
 // The weights of a lane's items: the same items every chunk, so they are loaded once.
-template <int DK>
+template <int DK, int BV>
 struct ConvW {
-    float w[ConvPlan<DK>::PER][8];  // taps 0..3 of the pair's first channel, then of the second
+    float w[ConvPlan<DK, BV>::PER][8];  // taps 0..3 of the pair's first channel, then of the second
 };
-template <int DK>
-__device__ void conv_weights(ConvW<DK>& cw, const Params<DK>& p, int tid, int h, int hk, int vb) {
-    using CP = ConvPlan<DK>;
+template <int DK, int BV>
+__device__ void conv_weights(ConvW<DK, BV>& cw, const Params<DK>& p, int tid, int h, int hk, int vb) {
+    using CP = ConvPlan<DK, BV>;
 #pragma unroll
     for (int q = 0; q < CP::PER; ++q) {
         const int it = tid + 512 * q, pc = it % CP::NP;
         const bool on = it < CP::ITEMS && !(pc >= DK && p.v_zero);
-        const float* w = p.conv_w + (size_t)(on ? pair_wrow<DK>(p, pc, h, hk, vb) : 0) * 4;
+        const float* w = p.conv_w + (size_t)(on ? pair_wrow<DK, BV>(p, pc, h, hk, vb) : 0) * 4;
 #pragma unroll
         for (int e = 0; e < 8; ++e) cw.w[q][e] = on ? w[e] : 0.f;
     }
@@ -487,10 +490,10 @@ __device__ void conv_weights(ConvW<DK>& cw, const Params<DK>& p, int tid, int h,
 }
 
 // The conv + SiLU of one chunk (raw: LDS byte address of its raw buffer); called by every lane.
-template <int DK>
-__device__ void conv_chunk(const Params<DK>& p, const ConvW<DK>& cw, unsigned raw, unsigned halo, int len, int tid) {
+template <int DK, int BV>
+__device__ void conv_chunk(const Params<DK>& p, const ConvW<DK, BV>& cw, unsigned raw, unsigned halo, int len, int tid) {
     tid = opaque(tid);
-    using CP = ConvPlan<DK>;
+    using CP = ConvPlan<DK, BV>;
     constexpr int NP = CP::NP, PER = CP::PER;
     uint32_t xr[PER][11];
     bool act[PER];
@@ -499,7 +502,7 @@ __device__ void conv_chunk(const Params<DK>& p, const ConvW<DK>& cw, unsigned ra
         const int it = tid + 512 * q, pc = it % NP, rb = it / NP;
         act[q] = it < CP::ITEMS && !(pc >= DK && p.v_zero);
         if (!act[q]) continue;
-        const PairLoc l = pair_loc<DK>(pc);
+        const PairLoc l = pair_loc<DK, BV>(pc);
 #pragma unroll
         for (int j = 0; j < 3; ++j)
             xr[q][j] = ld32(rb == 0 ? halo + 4u * (j * NP + pc) : pair_addr(raw, l, 8 * rb - 3 + j));
@@ -512,7 +515,7 @@ __device__ void conv_chunk(const Params<DK>& p, const ConvW<DK>& cw, unsigned ra
     for (int q = 0; q < PER; ++q) {
         if (!act[q]) continue;
         const int it = tid + 512 * q, pc = it % NP, rb = it / NP;
-        const PairLoc l = pair_loc<DK>(pc);
+        const PairLoc l = pair_loc<DK, BV>(pc);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = 8 * rb + j;
@@ -880,30 +883,28 @@ __device__ __forceinline__ void copy_LBA(const __bf16* sLt, __bf16* Tt, const fl
 }
 
 // ------------------------------------------------------------------------------------------
-// state waves: the chain of one chunk for 16 state rows, in registers.
-// Only S stays in registers across the barriers (every wave carries the registers of every role,
-// so whatever one role keeps live is lost to the others).
+// row waves: state chain and output of one chunk for 16 state rows, in registers.
+// Across the barriers a row wave keeps S, the output accumulators of the chunk and U' (in the two
+// operand orders the two sub-stages need); every other value is recomputed or read from LDS.
 template <int DK>
-struct StateRegs {
+struct RowRegs {
     static constexpr int DT = DK / 16, KS = DK / 32;
     fx4 S[DT];       // S^T tiles: lane (c = l%16, g) holds S[c][kcol(dt, 4g + e)]
+    fx4 ot[4];       // O^T of the chunk, sub-stage A -> B
+    bf16x8 ub[2];    // U' (tokens 0..31, 32..63) for the output products
+    bf16x8 ut[2];    // U' diag(exp(gamma_C - gamma)) for the state update
 };
 
-// Hand-off slot i (16 bytes) of a lane: slots are stored slab by slab ([wave][slot][lane]), so
-// every 16-byte access instruction covers 1 KB of consecutive bytes.
-__device__ __forceinline__ bf16x8* handoff(unsigned char* sm, int base, int wave, int nslots, int slot, int lane) {
-    return reinterpret_cast<bf16x8*>(sm + base + ((wave * nslots + slot) * 64 + lane) * 16);
-}
-
-// Sub-stage A: K S^T, Y = beta rk V - beta Gamma rk^2 K S^T, U' = T' Y blockwise; U' goes to the
-// output wave, U' scaled for the state update to sub-stage B (both through LDS).
-template <int DK>
-__device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
-                                        const unsigned char* gb, int wave, int lane) {
+// Sub-stage A: K S^T and S Q^T (S in bf16 is the same operand for both), then
+// Y = beta rk V - beta Gamma rk^2 K S^T and U' = T' Y blockwise.
+template <int DK, int BV>
+__device__ __forceinline__ void row_A(RowRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
+                                      const unsigned char* gb, int wave, int lane) {
     lane = opaque(lane);
     using S = Smem<DK>;
     constexpr int KS = DK / 32;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
+    const __bf16* Q = reinterpret_cast<const __bf16*>(raw + S::rQ);
     const __bf16* V = reinterpret_cast<const __bf16*>(raw + S::rV);
     const __bf16* Tt = reinterpret_cast<const __bf16*>(sm + S::T);
     const float* gKK = reinterpret_cast<const float*>(gb + S::gKK);
@@ -911,21 +912,28 @@ __device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, co
     const float* gDR = reinterpret_cast<const float*>(gb + S::gDR);
     const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
 
-    bf16x8 sb[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sb[ks] = pack_chain(st.S[2 * ks], st.S[2 * ks + 1]);
-    // K S^T, k-step outer so that one k-step of K fragments is live at a time
+    // K S^T and S Q^T, k-step outer so that one k-step of K and Q fragments is live at a time
     fx4 ks_acc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) ks_acc[t] = zero4();
+    for (int t = 0; t < 4; ++t) {
+        ks_acc[t] = zero4();
+        st.ot[t] = zero4();
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 sb = pack_chain(st.S[2 * ks], st.S[2 * ks + 1]);
         const int o = off_nat<DK>(ks, g, l16);
-        bf16x8 kfr[4];
+        bf16x8 kfr[4], qfr[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) kfr[t] = lds_at<bf16x8>(K, o + 16 * t * DK);
+        for (int t = 0; t < 4; ++t) {
+            kfr[t] = lds_at<bf16x8>(K, o + 16 * t * DK);
+            qfr[t] = lds_at<bf16x8>(Q, o + 16 * t * DK);
+        }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) ks_acc[t] = mfma(kfr[t], sb[ks], ks_acc[t]);  // K S^T (M = token, N = c)
+        for (int t = 0; t < 4; ++t) {
+            ks_acc[t] = mfma(kfr[t], sb, ks_acc[t]);     // K S^T (M = token, N = c)
+            st.ot[t] = mfma(sb, qfr[t], st.ot[t]);       // S Q^T (M = c, N = token)
+        }
     }
     bf16x4 vv[4];
     fx4 bm[4], kk[4];
@@ -950,8 +958,8 @@ __device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, co
     fx4 u[4];
     u[0] = mfma(ta0, xa, zero4());
     u[1] = mfma(ta1, xa, zero4());
-    const bf16x8 ub0 = pack_chain(u[0], u[1]);
-    const fx4 y2 = mfma(la2, ub0, zero4()), y3 = mfma(la3, ub0, zero4());
+    st.ub[0] = pack_chain(u[0], u[1]);
+    const fx4 y2 = mfma(la2, st.ub[0], zero4()), y3 = mfma(la3, st.ub[0], zero4());
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         x[2][e] -= y2[e];
@@ -960,9 +968,7 @@ __device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, co
     const bf16x8 xb = pack_chain(x[2], x[3]);
     u[2] = mfma(tb2, xb, zero4());
     u[3] = mfma(tb3, xb, zero4());
-    const bf16x8 ub1 = pack_chain(u[2], u[3]);
-    *handoff(sm, S::UH, wave, 2, 0, lane) = ub0;
-    *handoff(sm, S::UH, wave, 2, 1, lane) = ub1;
+    st.ub[1] = pack_chain(u[2], u[3]);
 
     fx4 ut[4];
 #pragma unroll
@@ -971,28 +977,43 @@ __device__ __forceinline__ void state_A(StateRegs<DK>& st, unsigned char* sm, co
 #pragma unroll
         for (int e = 0; e < 4; ++e) ut[it][e] = u[it][e] * dr[e];
     }
-    *handoff(sm, S::UT, wave, 2, 0, lane) = pack_chain(ut[0], ut[1]);
-    *handoff(sm, S::UT, wave, 2, 1, lane) = pack_chain(ut[2], ut[3]);
+    st.ut[0] = pack_chain(ut[0], ut[1]);
+    st.ut[1] = pack_chain(ut[2], ut[3]);
 }
 
-// Sub-stage B: S^T <- Gamma_C S^T + K^T diag(exp(gamma_C - gamma)) U'; the new S in bf16 goes to
-// the output wave.
-template <int DK>
-__device__ __forceinline__ void state_B(StateRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
-                                        const unsigned char* gb, int wave, int lane) {
+// Sub-stage B: S^T <- Gamma_C S^T + K^T diag(exp(gamma_C - gamma)) U', and
+// O^T = [diag(Gamma) (S Q^T) + U'^T Pm'^T] diag(rq), stored (lane: token 16 it + l16, state rows
+// cbase + 4g .. +3).
+template <int DK, int BV>
+__device__ __forceinline__ void row_B(const Params<DK>& p, RowRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
+                                      const unsigned char* gb, int wave, int lane, long t0, int len, int h, int vb) {
     lane = opaque(lane);
     using S = Smem<DK>;
-    constexpr int DT = DK / 16, KS = DK / 32;
+    constexpr int DT = DK / 16;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
+    const __bf16* Pm = reinterpret_cast<const __bf16*>(sm + S::PM);
+    const float* orq = reinterpret_cast<const float*>(sm + S::ORQ);
+    const float* gam = reinterpret_cast<const float*>(gb + S::gGAM);
     const float gc = reinterpret_cast<const float*>(gb + S::gGC)[0];
-    const int g = lane / 16, l16 = lane % 16;
-    const bf16x8 utb[2] = {*handoff(sm, S::UT, wave, 2, 0, lane), *handoff(sm, S::UT, wave, 2, 1, lane)};
+    const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
     bf16x8 kt[DT][2];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         const int o = off_trk<DK>(dt, g, l16);
         kt[dt][0] = __builtin_shufflevector(tr_read(K + o), tr_read(K + o + 16 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
         kt[dt][1] = __builtin_shufflevector(tr_read(K + o + 32 * DK), tr_read(K + o + 48 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    bf16x8 pf[4][2];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+            if (s2 == 0 || it >= 2) pf[it][s2] = frag_chain(Pm + (16 * it + l16) * TSTR, 32 * s2, g);
+    float r[4], G[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        r[it] = orq[16 * it + l16];
+        G[it] = gam[16 * it + l16];
     }
     issue_fence();
 #pragma unroll
@@ -1002,69 +1023,15 @@ __device__ __forceinline__ void state_B(StateRegs<DK>& st, unsigned char* sm, co
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][s2], utb[s2], st.S[dt]);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) *handoff(sm, S::SH, wave, KS, ks, lane) = pack_chain(st.S[2 * ks], st.S[2 * ks + 1]);
-}
-
-// Output sub-stage A: O^T = S Q^T for 16 state rows (S from the state wave, in bf16).
-template <int DK>
-__device__ __forceinline__ void out_A(fx4 (&ot)[4], unsigned char* sm, const unsigned char* raw, int wave, int lane) {
-    lane = opaque(lane);
-    using S = Smem<DK>;
-    constexpr int KS = DK / 32;
-    const __bf16* Q = reinterpret_cast<const __bf16*>(raw + S::rQ);
-    const int g = lane / 16, l16 = lane % 16;
-    bf16x8 sb[KS], qfr[KS][4];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        sb[ks] = *handoff(sm, S::SH, wave, KS, ks, lane);
-        const int o = off_nat<DK>(ks, g, l16);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) qfr[ks][t] = lds_at<bf16x8>(Q, o + 16 * t * DK);
-    }
-    issue_fence();
-#pragma unroll
-    for (int t = 0; t < 4; ++t) ot[t] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) ot[t] = mfma(sb[ks], qfr[ks][t], ot[t]);  // S Q^T (M = c, N = token)
-}
-
-// Output sub-stage B: O^T = [diag(Gamma) (S Q^T) + U'^T Pm'^T] diag(rq), stored (lane: token
-// 16 it + l16, state rows cbase + 4g .. +3).
-template <int DK>
-__device__ __forceinline__ void out_B(const Params<DK>& p, fx4 (&ot)[4], unsigned char* sm, const unsigned char* gb,
-                                      int wave, int lane, long t0, int len, int h, int vb) {
-    lane = opaque(lane);
-    using S = Smem<DK>;
-    const __bf16* Pm = reinterpret_cast<const __bf16*>(sm + S::PM);
-    const float* orq = reinterpret_cast<const float*>(sm + S::ORQ);
-    const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
-    const bf16x8 ub0 = *handoff(sm, S::UH, wave, 2, 0, lane), ub1 = *handoff(sm, S::UH, wave, 2, 1, lane);
-    bf16x8 pf[4][2];
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-            if (s2 == 0 || it >= 2) pf[it][s2] = frag_chain(Pm + (16 * it + l16) * TSTR, 32 * s2, g);
-    const float* gam = reinterpret_cast<const float*>(gb + S::gGAM);
-    float r[4], G[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        r[it] = orq[16 * it + l16];
-        G[it] = gam[16 * it + l16];
-    }
-    issue_fence();
+        for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][s2], st.ut[s2], st.S[dt]);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ot[it][e] *= G[it];
-        ot[it] = mfma(ub0, pf[it][0], ot[it]);
-        if (it >= 2) ot[it] = mfma(ub1, pf[it][1], ot[it]);
+        for (int e = 0; e < 4; ++e) st.ot[it][e] *= G[it];
+        st.ot[it] = mfma(st.ub[0], pf[it][0], st.ot[it]);
+        if (it >= 2) st.ot[it] = mfma(st.ub[1], pf[it][1], st.ot[it]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ot[it][e] *= r[it];
+        for (int e = 0; e < 4; ++e) st.ot[it][e] *= r[it];
     }
     if (p.out != OUT_STORE) return;
 #pragma unroll
@@ -1073,7 +1040,7 @@ __device__ __forceinline__ void out_B(const Params<DK>& p, fx4 (&ot)[4], unsigne
         if (i < len) {
             bf16x4 out;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * ot[it][e]);
+            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e]);
             *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
         }
     }
@@ -1084,9 +1051,10 @@ __device__ __forceinline__ void out_B(const Params<DK>& p, fx4 (&ot)[4], unsigne
 // state carried in, its remaining contribution is far under fp32 rounding.
 constexpr float kExitLog = -27.7258872f;
 
+// BV: state rows of the workgroup (64, or 32 for a 32-row state): BV / 16 row waves.
 // RAW: g and beta hold the raw gate inputs (a separate instantiation, so that the plain one carries
 // no trace of the gate transform).
-template <int DK, bool RAW>
+template <int DK, int BV, bool RAW>
 __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     using S = Smem<DK>;
     extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
@@ -1094,7 +1062,8 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     const int wid = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
     const int g = lane / 16, l16 = lane % 16;
-    const bool is_state = wid < 2, is_out = wid == 2 || wid == 3, is_prep = wid >= 4;
+    // waves 0 .. 3 load the chunks (rows 16w .. 16w + 15 each); waves 0 .. BV/16 - 1 own state rows
+    const bool is_row = wid < BV / 16, is_load = wid < 4, is_prep = wid >= 4;
     const int pw = wid - 4;  // prep wave index
 
     // XCD-aware order: the grp * nv workgroups that read one (segment, query/key head) -- its
@@ -1145,17 +1114,17 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
             for (int r = 0; r < 3; ++r) reinterpret_cast<__bf16*>(sm + S::raw(r) + S::rV)[i] = (__bf16)0.f;
     }
 
-    StateRegs<DK> st;
-    const int row = vb * BV + 16 * wid + l16;  // state row of this lane (state waves)
+    RowRegs<DK> st;
+    const int row = vb * BV + 16 * wid + l16;  // state row of this lane (row waves)
     const size_t srow0 = ((size_t)pair * p.dv + row) * DK;
-    if (is_state) {
+    if (is_row) {
         const float* src = nullptr;
         if (p.init == INIT_S0 && p.s0 && seg == 0)
             src = p.s0 + (((size_t)n * p.H + h) * p.dv + row) * DK;
         else if (p.init == INIT_PREV)
             src = p.s0 + (((size_t)(nseg - 1) * p.H + h) * p.dv + row) * DK;
 #pragma unroll
-        for (int dt = 0; dt < StateRegs<DK>::DT; ++dt) {
+        for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
             if (src) {
                 const float4 v = *reinterpret_cast<const float4*>(src + kcol(dt, 4 * g));
                 st.S[dt] = fx4{v.x, v.y, v.z, v.w};
@@ -1166,29 +1135,26 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
                 st.S[dt] = zero4();
             }
         }
-#pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) *handoff(sm, S::SH, wid, DK / 32, ks, lane) = pack_chain(st.S[2 * ks], st.S[2 * ks + 1]);
     }
 
     const unsigned smb = lds_base(sm);
     const bool conv = p.conv_w != nullptr;
-    ConvW<DK> cw;
+    ConvW<DK, BV> cw;
     if (conv) {
-        conv_weights<DK>(cw, p, tid, h, hk, vb);
+        conv_weights<DK, BV>(cw, p, tid, h, hk, vb);
         const int from = seg > 0 ? (nchunks > 0 ? HALO_TOKENS : HALO_ZERO) : (p.conv_state ? HALO_STATE : HALO_ZERO);
-        conv_halo_init<DK>(p, smb + S::HB, tid, n, h, hk, vb, bos, from);
+        conv_halo_init<DK, BV>(p, smb + S::HB, tid, n, h, hk, vb, bos, from);
     }
     if (nchunks > 0 && is_prep) {
-        dma_chunk<DK>(p, smb, S::raw(0), bos, clen(0), h, hk, vb, pw, lane);
+        dma_chunk<DK, BV>(p, smb, S::raw(0), bos, clen(0), h, hk, vb, pw, lane);
         wait_loads();
         if constexpr (RAW) raw_gates<DK>(p, sm + S::raw(0), clen(0), pw, lane, h);
-        zero_tail<DK>(sm + S::raw(0), clen(0), pw, lane);
+        zero_tail<DK, BV>(sm + S::raw(0), clen(0), pw, lane);
     }
     lds_barrier();
-    if (conv && nchunks > 0) conv_chunk<DK>(p, cw, smb + S::raw(0), smb + S::HB, clen(0), tid);
+    if (conv && nchunks > 0) conv_chunk<DK, BV>(p, cw, smb + S::raw(0), smb + S::HB, clen(0), tid);
 
     // iteration k: state and output on chunk k, Pm of chunk k, L and T of chunk k+1, loads of k+2
-    fx4 ot[4];
     float decay = 0.f;  // log bound of the transition over the chunks the state has passed
     int stopped = 0;
     for (int k = -1; k < nchunks; ++k) {
@@ -1198,25 +1164,20 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
         if (cur) {
             unsigned char* rawk = sm + S::raw(k);
             unsigned char* gbk = sm + S::gates(k);
-            if (is_state) state_A<DK>(st, sm, rawk, gbk, wid, lane);
-            if (is_out) out_A<DK>(ot, sm, rawk, wid - 2, lane);
+            if (is_row) row_A<DK, BV>(st, sm, rawk, gbk, wid, lane);
             if (pw == 1) prep_P<DK, 0>(rawk, sm, lane, clen(k), p.l2norm);
             if (pw == 2) prep_P<DK, 1>(rawk, sm, lane, clen(k), p.l2norm);
         }
         if (nxt && pw == 0) prep_L<DK, 0>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
         if (nxt && pw == 3) prep_L<DK, 1>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
-        // the loads of chunk k+2 from the output waves, which have slack here (rows 32 (w-2) ..)
-        if (far && is_out) {
-            dma_chunk<DK>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2), lane);
-            dma_chunk<DK>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2) + 1, lane);
-        }
+        // the loads of chunk k+2 from waves 0 .. 3 (rows 16w ..), issued after their own reads
+        if (far && is_load) dma_chunk<DK, BV>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, wid, lane);
         lds_barrier();
         // ---- B
         if (cur) {
             unsigned char* rawk = sm + S::raw(k);
             unsigned char* gbk = sm + S::gates(k);
-            if (is_state) state_B<DK>(st, sm, rawk, gbk, wid, lane);
-            if (is_out) out_B<DK>(p, ot, sm, gbk, wid - 2, lane, tk, clen(k), h, vb);
+            if (is_row) row_B<DK, BV>(p, st, sm, rawk, gbk, wid, lane, tk, clen(k), h, vb);
             if (p.early_exit)
                 decay += __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                                                        int, reinterpret_cast<const float*>(gbk + S::gGC)[1])));
@@ -1237,14 +1198,10 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
                      reinterpret_cast<const float*>(sm + S::WL), reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB),
                      lane);
         if (nxt && pw == 3) make_gates<DK>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
-        if (far && is_out) {
+        if (far && is_load) {
             wait_loads();
-            if (RAW && wid == 2) {
-                raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 0, lane, h);
-                raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 1, lane, h);
-            }
-            zero_tail<DK>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2), lane);
-            zero_tail<DK>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2) + 1, lane);
+            if constexpr (RAW) raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), wid, lane, h);
+            zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), wid, lane);
         }
         lds_barrier();
         // every wave read the same bounds in the same order: the exit is uniform
@@ -1253,12 +1210,12 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
             break;
         }
         // ---- C (conv only): the prologue on chunk k+2, whose loads have all landed
-        if (conv && far) conv_chunk<DK>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
+        if (conv && far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
     }
 
-    if (is_state && p.sfin) {
+    if (is_row && p.sfin) {
 #pragma unroll
-        for (int dt = 0; dt < StateRegs<DK>::DT; ++dt) {
+        for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
             const fx4 v = st.S[dt];
             *reinterpret_cast<float4*>(p.sfin + srow0 + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
         }
@@ -1274,7 +1231,7 @@ struct Pass {
     int* negl;
 };
 
-template <int DK>
+template <int DK, int BV>
 hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     Params<DK> p;
     p.q = static_cast<const __bf16*>(a.q);
@@ -1311,21 +1268,27 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (e != hipSuccess) return e;
     if (lds_max < smem) return hipErrorInvalidConfiguration;  // needs the 160 KiB LDS of gfx950
-    const void* fn = a.gate_params ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, true>)
-                                   : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, false>);
+    const void* fn = a.gate_params ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, true>)
+                                   : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, false>);
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     const int grid = a.N * c.P * a.H * p.nv;
     if (a.gate_params)
-        hipLaunchKernelGGL((chunk_bf16_kernel<DK, true>), dim3(grid), dim3(512), smem, a.stream, p);
+        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, true>), dim3(grid), dim3(512), smem, a.stream, p);
     else
-        hipLaunchKernelGGL((chunk_bf16_kernel<DK, false>), dim3(grid), dim3(512), smem, a.stream, p);
+        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, false>), dim3(grid), dim3(512), smem, a.stream, p);
     return hipGetLastError();
+}
+
+// 64 state rows per workgroup, or 32 when the pass has a 32-row state
+template <int DK>
+hipError_t launch_rows(const ChunkArgs& a, const Pass& c) {
+    return c.rows >= 64 ? launch_t<DK, 64>(a, c) : launch_t<DK, 32>(a, c);
 }
 
 template <int DK>
 hipError_t run(const ChunkArgs& a, int P) {
-    if (P <= 1) return launch_t<DK>(a, Pass{1, INIT_S0, OUT_STORE, 0, 0, 0, a.dv, a.s0, a.sfin, nullptr});
+    if (P <= 1) return launch_rows<DK>(a, Pass{1, INIT_S0, OUT_STORE, 0, 0, 0, a.dv, a.s0, a.sfin, nullptr});
     // Segmented path for long sequences (each sequence cut into P segments of whole chunks).
     // The chunk map is affine in the state: S_out = S_in A_p + B_p.
     //  1. every segment from its own start: B_p (zero state in, the true initial state for p = 0)
@@ -1342,10 +1305,10 @@ hipError_t run(const ChunkArgs& a, int P) {
     float* A = reinterpret_cast<float*>(ws + L.off_A);
     int* negl = reinterpret_cast<int*>(ws + L.off_negl);
     const int ex = a.l2norm ? 1 : 0;
-    hipError_t e = launch_t<DK>(a, Pass{P, INIT_S0, OUT_STORE, 0, 0, 0, a.dv, a.s0, E, nullptr});
-    if (e == hipSuccess) e = launch_t<DK>(a, Pass{P, INIT_IDENTITY, OUT_NONE, 1, ex, 1, a.dk, nullptr, A, negl});
+    hipError_t e = launch_rows<DK>(a, Pass{P, INIT_S0, OUT_STORE, 0, 0, 0, a.dv, a.s0, E, nullptr});
+    if (e == hipSuccess) e = launch_rows<DK>(a, Pass{P, INIT_IDENTITY, OUT_NONE, 1, ex, 1, a.dk, nullptr, A, negl});
     if (e == hipSuccess) e = launch_seg_combine(E, A, negl, a.sfin, a.N, P, a.H, a.dk, a.dv, a.stream);
-    if (e == hipSuccess) e = launch_t<DK>(a, Pass{P, INIT_PREV, OUT_STORE, 0, ex, 1, a.dv, E, nullptr, nullptr});
+    if (e == hipSuccess) e = launch_rows<DK>(a, Pass{P, INIT_PREV, OUT_STORE, 0, ex, 1, a.dv, E, nullptr, nullptr});
     return e;
 }
 

@@ -57,7 +57,7 @@ struct SegLayout {
 };
 SegLayout seg_layout(int N, int H, int dk, int dv, int P);
 // Segments per sequence for a bf16 call: `requested` if > 0, else enough to give
-// every compute unit of the current device a workgroup when (sequence, head, row block) units
+// every compute unit of the current device a workgroup when (sequence, head, 64-row block) units
 // alone do not, and only for sequences of at least 16 chunks per segment.
 int plan_segments(int N, int T_tot, int H, int dv, int requested);
 

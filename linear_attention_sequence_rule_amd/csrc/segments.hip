@@ -93,7 +93,7 @@ int plan_segments(int N, int T_tot, int H, int dv, int requested) {
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
         cus = v;
-    const long units = (long)N * H * (dv / 32);
+    const long units = (long)N * H * (dv >= 64 ? dv / 64 : 1);  // workgroups of one pass: 64 state rows each
     if (units >= cus) return 1;
     const long chunks = ((long)T_tot / N + 63) / 64;
     long P = cus / units;
