@@ -216,6 +216,7 @@ struct Smem {
 // How a workgroup starts its state, and what it does with o (one launch runs one of the passes of
 // the segmented long-sequence path, or the plain single pass).
 enum InitMode { INIT_S0 = 0, INIT_IDENTITY = 1, INIT_PREV = 2 };
+enum NeglMode { NEGL_NONE = 0, NEGL_MARK = 1, NEGL_SKIP = 2 };
 enum OutMode { OUT_NONE = 0, OUT_STORE = 1 };
 
 template <int DK>
@@ -237,6 +238,8 @@ struct Params {
     int v_zero;    // values taken as zero (v is not read)
     int early_exit;  // stop once the product of the decays since the start is <= 2^-40
     int skip_first;  // segment 0 does nothing
+    int negl_mode;   // NEGL_MARK: record whether the whole segment's transition bound is <= 2^-40;
+                     // NEGL_SKIP: skip segments so marked, record a stop at the bound
     float scale;
     int l2norm;
 };
@@ -281,32 +284,39 @@ __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned smb, int
                                           int hk, int vb, int wid, int lane) {
     lane = opaque(lane);
     using S = Smem<DK>;
-    constexpr int PPR = DK / 8;       // 16-byte slots per K/Q row
-    constexpr int RPI = 64 / PPR;     // rows per 1 KB instruction
+    constexpr unsigned PPR = DK / 8;     // 16-byte slots per K/Q row
+    constexpr unsigned RPI = 64 / PPR;   // rows per 1 KB instruction
     const size_t tok0 = (size_t)t0 * p.H + h, tokk = (size_t)t0 * p.Hk + hk;
     const __bf16* kb = uniform_ptr(p.k + tokk * DK);
     const __bf16* qb = uniform_ptr(p.q + tokk * DK);
     const unsigned rowq = (unsigned)(p.Hk * DK) * 2u;  // bytes between tokens
+    const unsigned ul = (unsigned)lane, lrow = ul / PPR, slot = ul % PPR;
+    // Full chunks (every chunk but a sequence's last): lane offsets are a lane constant plus a
+    // wave-uniform row offset.
+    const unsigned lane_q = lrow * rowq;
 #pragma unroll
-    for (int j = 0; j < 16 / RPI; ++j) {
-        const int row0 = 16 * wid + RPI * j;
-        const int row = row0 + lane / PPR, slot = lane % PPR;
-        const int part = slot ^ (row % PPR);
-        const unsigned voff = (unsigned)min(row, len - 1) * rowq + 16u * part;
-        const int lo = rawoff + row0 * DK * 2;
+    for (unsigned j = 0; j < 16 / RPI; ++j) {
+        const unsigned row0 = 16u * (unsigned)wid + RPI * j;
+        const unsigned part = slot ^ ((row0 + lrow) % PPR);  // the swizzle key of the lane's row
+        const unsigned voff = len == C ? lane_q + row0 * rowq + 16u * part
+                                       : (unsigned)min((int)(row0 + lrow), len - 1) * rowq + 16u * part;
+        const int lo = rawoff + (int)row0 * DK * 2;
         dma16(kb, voff, lds_addr(smb + lo + S::rK));
         dma16(qb, voff, lds_addr(smb + lo + S::rQ));
     }
     if (!p.v_zero) {
-        constexpr int VPR = BV / 8;    // 16-byte slots per V row
-        constexpr int VRI = 64 / VPR;  // rows per 1 KB instruction
+        constexpr unsigned VPR = BV / 8;    // 16-byte slots per V row
+        constexpr unsigned VRI = 64 / VPR;  // rows per 1 KB instruction
         const __bf16* vbase = uniform_ptr(p.v + tok0 * p.dv + vb * BV);
+        const unsigned rowv = (unsigned)(p.H * p.dv) * 2u;
+        const unsigned vrow = ul / VPR, vslot = ul % VPR;
 #pragma unroll
-        for (int j = 0; j < 16 / VRI; ++j) {
-            const int row0 = 16 * wid + VRI * j;
-            const int row = row0 + lane / VPR, slot = lane % VPR, part = slot ^ (row % VPR);
-            const unsigned voff = (unsigned)min(row, len - 1) * (unsigned)(p.H * p.dv) * 2u + 16u * part;
-            dma16(vbase, voff, lds_addr(smb + rawoff + S::rV + row0 * BV * 2));
+        for (unsigned j = 0; j < 16 / VRI; ++j) {
+            const unsigned row0 = 16u * (unsigned)wid + VRI * j;
+            const unsigned part = vslot ^ ((row0 + vrow) % VPR);
+            const unsigned voff = len == C ? (vrow + row0) * rowv + 16u * part
+                                           : (unsigned)min((int)(row0 + vrow), len - 1) * rowv + 16u * part;
+            dma16(vbase, voff, lds_addr(smb + rawoff + S::rV + (int)row0 * BV * 2));
         }
     }
     if (wid < 2) {
@@ -1062,8 +1072,8 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     const int wid = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
     const int g = lane / 16, l16 = lane % 16;
-    // waves 0 .. 3 load the chunks (rows 16w .. 16w + 15 each); waves 0 .. BV/16 - 1 own state rows
-    const bool is_row = wid < BV / 16, is_load = wid < 4, is_prep = wid >= 4;
+    // waves 0 .. BV/16 - 1 own state rows; waves 2 and 3 also load the chunks
+    const bool is_row = wid < BV / 16, is_load = wid == 2 || wid == 3, is_prep = wid >= 4;
     const int pw = wid - 4;  // prep wave index
 
     // XCD-aware order: the grp * nv workgroups that read one (segment, query/key head) -- its
@@ -1084,6 +1094,7 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     const int nseg = pair / p.H, h = pair % p.H, hk = h / p.grp;
     const int n = nseg / p.P, seg = nseg % p.P;
     if (p.skip_first && seg == 0) return;
+    if (p.negl_mode == NEGL_SKIP && p.negl[pair]) return;  // the segment's transition is negligible
     long bos, eos;
     if (p.cu) {
         bos = p.cu[n];
@@ -1170,15 +1181,20 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
         }
         if (nxt && pw == 0) prep_L<DK, 0>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
         if (nxt && pw == 3) prep_L<DK, 1>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
-        // the loads of chunk k+2 from waves 0 .. 3 (rows 16w ..), issued after their own reads
-        if (far && is_load) dma_chunk<DK, BV>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, wid, lane);
+        // the loads of chunk k+2 from waves 2 and 3 (rows 32 (w - 2) .. + 31), after their row work:
+        // waves 0 and 1 share their SIMDs with the solve of the next sub-stage and wait for nothing.
+        // The buffer held chunk k-1, whose last reads were before the previous barrier.
+        if (far && is_load) {
+            dma_chunk<DK, BV>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2), lane);
+            dma_chunk<DK, BV>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2) + 1, lane);
+        }
         lds_barrier();
         // ---- B
         if (cur) {
             unsigned char* rawk = sm + S::raw(k);
             unsigned char* gbk = sm + S::gates(k);
             if (is_row) row_B<DK, BV>(p, st, sm, rawk, gbk, wid, lane, tk, clen(k), h, vb);
-            if (p.early_exit)
+            if (p.early_exit || p.negl_mode == NEGL_MARK)
                 decay += __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                                                        int, reinterpret_cast<const float*>(gbk + S::gGC)[1])));
         }
@@ -1200,8 +1216,12 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
         if (nxt && pw == 3) make_gates<DK>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
         if (far && is_load) {
             wait_loads();
-            if constexpr (RAW) raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), wid, lane, h);
-            zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), wid, lane);
+            if (RAW && wid == 2) {
+                raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 0, lane, h);
+                raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 1, lane, h);
+            }
+            zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2), lane);
+            zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2) + 1, lane);
         }
         lds_barrier();
         // every wave read the same bounds in the same order: the exit is uniform
@@ -1220,12 +1240,12 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
             *reinterpret_cast<float4*>(p.sfin + srow0 + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
         }
     }
-    if (p.negl && vb == 0 && tid == 0) p.negl[pair] = stopped;
+    if (p.negl && vb == 0 && tid == 0) p.negl[pair] = p.negl_mode == NEGL_MARK ? (decay <= kExitLog) : stopped;
 }
 
 // One pass of the kernel.  rows = state rows (dv, or dk for the transition pass).
 struct Pass {
-    int P, init, out, v_zero, early_exit, skip_first, rows;
+    int P, init, out, v_zero, early_exit, skip_first, negl_mode, rows;
     const float* s0;
     float* sfin;
     int* negl;
@@ -1260,6 +1280,7 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     p.v_zero = c.v_zero;
     p.early_exit = c.early_exit;
     p.skip_first = c.skip_first;
+    p.negl_mode = c.negl_mode;
     p.scale = a.scale;
     p.l2norm = a.l2norm;
     const int smem = Smem<DK>::bytes;
@@ -1288,13 +1309,14 @@ hipError_t launch_rows(const ChunkArgs& a, const Pass& c) {
 
 template <int DK>
 hipError_t run(const ChunkArgs& a, int P) {
-    if (P <= 1) return launch_rows<DK>(a, Pass{1, INIT_S0, OUT_STORE, 0, 0, 0, a.dv, a.s0, a.sfin, nullptr});
+    if (P <= 1) return launch_rows<DK>(a, Pass{1, INIT_S0, OUT_STORE, 0, 0, 0, NEGL_NONE, a.dv, a.s0, a.sfin, nullptr});
     // Segmented path for long sequences (each sequence cut into P segments of whole chunks).
     // The chunk map is affine in the state: S_out = S_in A_p + B_p.
     //  1. every segment from its own start: B_p (zero state in, the true initial state for p = 0)
-    //     and o without the contribution of the state entering the segment;
-    //  2. A_p = the transition of segment p (identity in, zero values), stopped once its norm
-    //     bound is below 2^-40 (then marked negligible);
+    //     and o without the contribution of the state entering the segment; from the gates alone,
+    //     whether the bound on the whole segment's transition is below 2^-40 (negligible);
+    //  2. A_p = the transition of segment p (identity in, zero values), for the segments not marked
+    //     negligible, stopped once its norm bound is below 2^-40 (then marked negligible);
     //  3. combine: E_0 = B_0, E_p = E_{p-1} A_p + B_p (the true end states), final = E_{P-1};
     //  4. rerun: segment p again from E_{p-1}, overwriting o, until the bound on the transition
     //     since the segment start is <= 2^-40; from there on the state of step 1 differs from the
@@ -1305,10 +1327,11 @@ hipError_t run(const ChunkArgs& a, int P) {
     float* A = reinterpret_cast<float*>(ws + L.off_A);
     int* negl = reinterpret_cast<int*>(ws + L.off_negl);
     const int ex = a.l2norm ? 1 : 0;
-    hipError_t e = launch_rows<DK>(a, Pass{P, INIT_S0, OUT_STORE, 0, 0, 0, a.dv, a.s0, E, nullptr});
-    if (e == hipSuccess) e = launch_rows<DK>(a, Pass{P, INIT_IDENTITY, OUT_NONE, 1, ex, 1, a.dk, nullptr, A, negl});
+    hipError_t e = launch_rows<DK>(a, Pass{P, INIT_S0, OUT_STORE, 0, 0, 0, NEGL_MARK, a.dv, a.s0, E, negl});
+    if (e == hipSuccess)
+        e = launch_rows<DK>(a, Pass{P, INIT_IDENTITY, OUT_NONE, 1, ex, 1, NEGL_SKIP, a.dk, nullptr, A, negl});
     if (e == hipSuccess) e = launch_seg_combine(E, A, negl, a.sfin, a.N, P, a.H, a.dk, a.dv, a.stream);
-    if (e == hipSuccess) e = launch_rows<DK>(a, Pass{P, INIT_PREV, OUT_STORE, 0, ex, 1, a.dv, E, nullptr, nullptr});
+    if (e == hipSuccess) e = launch_rows<DK>(a, Pass{P, INIT_PREV, OUT_STORE, 0, ex, 1, NEGL_NONE, a.dv, E, nullptr, nullptr});
     return e;
 }
 
