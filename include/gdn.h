@@ -86,6 +86,9 @@ extern "C" {
 /* Segments per sequence for gdn_chunk_fwd (bits 8..15; 0 = chosen automatically).  See
  * "Long sequences" under gdn_chunk_fwd.  Not accepted by gdn_recurrent_step. */
 #define GDN_SEGMENTS(n) ((((unsigned)(n)) & 0xFFu) << 8)
+/* bf16 prefill with conv_w: run the conv prologue inside the chunk kernel instead of as a separate
+ * pass into the workspace (see "Workspace" under gdn_chunk_fwd).  No effect otherwise. */
+#define GDN_CONV_FUSED (1u << 16)
 
 /*
  * gdn_chunk_fwd -- chunked prefill over packed variable-length sequences.
@@ -124,7 +127,10 @@ extern "C" {
  *  o           [T_tot, H, dv]  dtype   output; must not alias any input
  *  final_state [N, H, dv, dk] fp32     last state per (sequence, head), or NULL = not written.
  *                                      May alias initial_state exactly (same pointer).
- *  workspace, workspace_bytes          device scratch for the long-sequence path (below).  If
+ *  workspace, workspace_bytes          device scratch: the long-sequence path (below) and, for a
+ *                                      bf16 call with conv_w (unless GDN_CONV_FUSED), the convolved
+ *                                      q, k, v (T_tot * (2*Hk*dk + H*dv) bf16): the conv prologue then
+ *                                      runs as one streaming pass before the chunk kernel.  If
  *                                      *workspace_bytes is smaller than the size this call needs,
  *                                      the call sets *workspace_bytes to that size and returns
  *                                      GDN_ERR_WORKSPACE without launching (a NULL workspace with
@@ -139,7 +145,7 @@ extern "C" {
  *  chunk       64                      chunk length; other values -> GDN_ERR_UNSUPPORTED
  *  scale       output scale (1.0 = o_t = S_t q_t), applied before the epilogue
  *  norm_eps    eps of the epilogue's RMSNorm (finite, >= 0; ignored without out_gate)
- *  flags       GDN_QK_L2NORM, optionally | GDN_SEGMENTS(n)
+ *  flags       GDN_QK_L2NORM, optionally | GDN_SEGMENTS(n) | GDN_CONV_FUSED
  *  hip_stream  hipStream_t to launch on
  *
  * Long sequences (bf16 path).  Each sequence is cut into P segments of whole chunks
@@ -163,14 +169,13 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   void* hip_stream);
 
 /*
- * gdn_chunk_workspace_size -- the workspace gdn_chunk_fwd needs for these sizes (H = value heads;
- * the workspace does not depend on the query/key head count), flags and
+ * gdn_chunk_workspace_size -- the workspace gdn_chunk_fwd needs for these sizes, flags and
  * (nonzero = present) cu_seqlens / conv_w (0 bytes when the call runs as a single pass).  Host
  * function; with automatic segments it reads the compute-unit count of the current device (256
  * when no device can be queried), exactly as gdn_chunk_fwd does.  Returns GDN_OK and sets *bytes,
  * or the error code gdn_chunk_fwd would return for these arguments.
  */
-int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype, int chunk,
+int gdn_chunk_workspace_size(int N, int T_tot, int H, int Hk, int dk, int dv, int dtype, int chunk,
                              int has_cu_seqlens, int has_conv, unsigned flags, size_t* bytes);
 
 /*

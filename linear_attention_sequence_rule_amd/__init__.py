@@ -18,11 +18,12 @@ from typing import Optional
 __all__ = ["gdn_chunk_fwd", "gdn_recurrent_step", "gdn_status_string", "gdn_chunk_workspace_size",
            "GdnError", "lib_path", "load_library", "GDN_OK", "GDN_ERR_INVALID_ARG",
            "GDN_ERR_UNSUPPORTED", "GDN_ERR_WORKSPACE", "GDN_ERR_HIP", "GDN_F32", "GDN_BF16",
-           "GDN_QK_L2NORM", "GDN_SEGMENTS"]
+           "GDN_QK_L2NORM", "GDN_SEGMENTS", "GDN_CONV_FUSED"]
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 0, 1, 2, 3, 4
 GDN_F32, GDN_BF16 = 0, 1
 GDN_QK_L2NORM = 1
+GDN_CONV_FUSED = 1 << 16
 
 
 def GDN_SEGMENTS(n: int) -> int:
@@ -56,7 +57,7 @@ def load_library():
     lib.gdn_chunk_fwd.restype = I
     lib.gdn_chunk_fwd.argtypes = [P] * 16 + [I] * 8 + [F, F, U, P]
     lib.gdn_chunk_workspace_size.restype = I
-    lib.gdn_chunk_workspace_size.argtypes = [I] * 9 + [U, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_chunk_workspace_size.argtypes = [I] * 10 + [U, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdn_recurrent_step.restype = I
     lib.gdn_recurrent_step.argtypes = [P] * 12 + [I] * 6 + [F, F, U, P]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -101,9 +102,10 @@ def _check_dev(name, t, dtype=None):
 
 
 def gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype=GDN_BF16, chunk=64, has_cu_seqlens=False, has_conv=False,
-                             flags=GDN_QK_L2NORM) -> int:
+                             flags=GDN_QK_L2NORM, Hk=None) -> int:
     n = ctypes.c_size_t(0)
-    st = load_library().gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype, chunk, int(bool(has_cu_seqlens)),
+    Hk = H if Hk is None else Hk
+    st = load_library().gdn_chunk_workspace_size(N, T_tot, H, Hk, dk, dv, dtype, chunk, int(bool(has_cu_seqlens)),
                                                  int(bool(has_conv)), flags, ctypes.byref(n))
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_workspace_size")
@@ -113,7 +115,7 @@ def gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype=GDN_BF16, chunk=64, has_
 def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=None, *, N=None, o=None,
                   final_state=None, output_final_state=True, scale=1.0, l2norm=True, chunk=64, workspace=None,
                   segments=0, gate_params=None, conv_state=None, out_gate=None, norm_weight=None, norm_eps=1e-3,
-                  stream=None):
+                  conv_fused=False, stream=None):
     """Chunked prefill.  q, k [T_tot, Hk, dk]; v [T_tot, H, dv] (bf16 or fp32; H a multiple of Hk, value
     head h reads query/key head h // (H // Hk)); g, beta [T_tot, H] fp32 (the raw a and b when
     gate_params [2, H] = (A_log, dt_bias) is given); initial_state [N, H, dv, dk] fp32 or None;
@@ -146,9 +148,10 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=
     _check_dev("o", o, q.dtype)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dv, dk), dtype=torch.float32, device=q.device)
-    flags = (GDN_QK_L2NORM if l2norm else 0) | GDN_SEGMENTS(segments)
+    flags = (GDN_QK_L2NORM if l2norm else 0) | GDN_SEGMENTS(segments) | (GDN_CONV_FUSED if conv_fused else 0)
     ws_bytes = ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size())
-    need = gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dt, chunk, cu_seqlens is not None, conv_w is not None, flags)
+    need = gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dt, chunk, cu_seqlens is not None, conv_w is not None, flags,
+                                    Hk=Hk)
     if need > ws_bytes.value:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         ws_bytes = ctypes.c_size_t(need)

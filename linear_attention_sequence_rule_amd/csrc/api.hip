@@ -21,10 +21,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 constexpr unsigned kSegMask = 0xFFu << 8;
+constexpr unsigned kConvFused = 1u << 16;  // GDN_CONV_FUSED
 
 int check_common(int H, int dk, int dv, int dtype, float scale, unsigned flags) {
     if (H < 1) return GDN_ERR_INVALID_ARG;
-    if (flags & ~(GDN_QK_L2NORM | kSegMask)) return GDN_ERR_INVALID_ARG;
+    if (flags & ~(GDN_QK_L2NORM | kSegMask | kConvFused)) return GDN_ERR_INVALID_ARG;
     if (!isfinite(scale)) return GDN_ERR_INVALID_ARG;
     if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (!dim_ok(dk) || !dim_ok(dv)) return GDN_ERR_UNSUPPORTED;
@@ -44,8 +45,15 @@ int segments_for(int N, int T_tot, int H, int dv, int dtype, bool, unsigned flag
     return GDN_OK;
 }
 
-size_t workspace_for(int N, int H, int dk, int dv, int P) {
-    return P > 1 ? gdn::seg_layout(N, H, dk, dv, P).bytes : 0;
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Segment buffers first (the long-sequence path), then the convolved q, k, v of the conv pass.
+bool conv_pass(bool has_conv, int dtype, unsigned flags) {
+    return has_conv && dtype == GDN_BF16 && !(flags & kConvFused);
+}
+size_t seg_bytes(int N, int H, int dk, int dv, int P) { return P > 1 ? align256(gdn::seg_layout(N, H, dk, dv, P).bytes) : 0; }
+size_t workspace_for(int N, int T_tot, int H, int Hk, int dk, int dv, int P, bool conv) {
+    return seg_bytes(N, H, dk, dv, P) + (conv ? gdn::conv_prepass_bytes(T_tot, H, Hk, dk, dv) : 0);
 }
 
 }  // namespace
@@ -63,10 +71,11 @@ const char* gdn_status_string(int status) {
     return "GDN_ERR_UNKNOWN";
 }
 
-int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype, int chunk, int has_cu_seqlens,
-                             int has_conv, unsigned flags, size_t* bytes) {
+int gdn_chunk_workspace_size(int N, int T_tot, int H, int Hk, int dk, int dv, int dtype, int chunk,
+                             int has_cu_seqlens, int has_conv, unsigned flags, size_t* bytes) {
     if (!bytes) return GDN_ERR_INVALID_ARG;
     if (N < 1 || T_tot < 0) return GDN_ERR_INVALID_ARG;
+    if (Hk < 1 || H < 1 || H % Hk != 0) return GDN_ERR_INVALID_ARG;
     int st = check_common(H, dk, dv, dtype, 1.0f, flags);
     if (st != GDN_OK) return st;
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
@@ -74,7 +83,7 @@ int gdn_chunk_workspace_size(int N, int T_tot, int H, int dk, int dv, int dtype,
     int P = 1;
     st = segments_for(N, T_tot, H, dv, dtype, has_conv != 0, flags, &P);
     if (st != GDN_OK) return st;
-    *bytes = workspace_for(N, H, dk, dv, P);
+    *bytes = workspace_for(N, T_tot, H, Hk, dk, dv, P, conv_pass(has_conv != 0, dtype, flags));
     return GDN_OK;
 }
 
@@ -134,7 +143,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     int P = 1;
     st = segments_for(N, T_tot, H, dv, dtype, conv_w != nullptr, flags, &P);
     if (st != GDN_OK) return st;
-    const size_t need = workspace_for(N, H, dk, dv, P);
+    const bool cpass = conv_pass(conv_w != nullptr, dtype, flags);
+    const size_t need = workspace_for(N, T_tot, H, Hk, dk, dv, P, cpass);
     if (need > 0) {
         if (!workspace_bytes) return GDN_ERR_INVALID_ARG;
         if (!workspace || *workspace_bytes < need) {
@@ -182,7 +192,14 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     a.l2norm = (flags & GDN_QK_L2NORM) ? 1 : 0;
     a.segments = P;
     a.stream = static_cast<hipStream_t>(hip_stream);
-    hipError_t e = a.bf16 ? gdn::launch_chunk_bf16(a) : gdn::launch_chunk_f32(a);
+    hipError_t e;
+    if (cpass) {
+        gdn::ChunkArgs c;
+        e = gdn::launch_conv_prepass(a, static_cast<unsigned char*>(workspace) + seg_bytes(N, H, dk, dv, P), c);
+        if (e == hipSuccess) e = gdn::launch_chunk_bf16(c);
+    } else {
+        e = a.bf16 ? gdn::launch_chunk_bf16(a) : gdn::launch_chunk_f32(a);
+    }
     if (e == hipSuccess && conv_state) e = gdn::launch_conv_state_update(a);
     if (e == hipSuccess && out_gate)
         e = gdn::launch_gated_norm(o, a.out_gate, a.norm_weight, (long)T_tot * H, dv, a.norm_eps, a.bf16, a.stream);

@@ -64,6 +64,10 @@ int plan_segments(int N, int T_tot, int H, int dv, int requested);
 hipError_t launch_step(const StepArgs& a);
 hipError_t launch_chunk_f32(const ChunkArgs& a);
 hipError_t launch_chunk_bf16(const ChunkArgs& a);
+// Conv prologue of a bf16 prefill as a separate pass: q, k, v convolved (+ SiLU) into `out`
+// (conv_prepass_bytes of workspace); conv_args = a with q, k, v pointing there and no conv.
+size_t conv_prepass_bytes(int T_tot, int H, int Hk, int dk, int dv);
+hipError_t launch_conv_prepass(const ChunkArgs& a, void* out, ChunkArgs& conv_args);
 // conv_state <- the three raw inputs before the token after each sequence (in place, after the
 // chunk kernels have read it as history).
 hipError_t launch_conv_state_update(const ChunkArgs& a);

@@ -32,7 +32,8 @@ def o_to_f64(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def run_gpu(wl: W.Workload, *, scale=1.0, l2norm=True, pass_state=True, want_final=True, stream=None, segments=0):
+def run_gpu(wl: W.Workload, *, scale=1.0, l2norm=True, pass_state=True, want_final=True, stream=None, segments=0,
+            conv_fused=False):
     from linear_attention_sequence_rule_amd import gdn_chunk_fwd
     import torch
     q, k, v = to_dev(wl.q), to_dev(wl.k), to_dev(wl.v)
@@ -41,7 +42,7 @@ def run_gpu(wl: W.Workload, *, scale=1.0, l2norm=True, pass_state=True, want_fin
     cu = to_dev(wl.cu_seqlens)
     cw = to_dev(wl.conv_w)
     o, sf = gdn_chunk_fwd(q, k, v, g, beta, s0, cu, cw, N=wl.N, scale=scale, l2norm=l2norm,
-                          output_final_state=want_final, stream=stream, segments=segments)
+                          output_final_state=want_final, stream=stream, segments=segments, conv_fused=conv_fused)
     torch.cuda.synchronize()
     return o_to_f64(o), (sf.cpu().numpy().astype(np.float64) if sf is not None else None)
 

@@ -98,7 +98,7 @@ def test_chunk_validation(lib, kw, status):
 def test_workspace_query(lib):
     n = ctypes.c_size_t(0)
     # one long sequence, 16 heads: too few (head, row block) units for the device -> segments
-    assert lib.gdn_chunk_workspace_size(1, 262144, 16, 128, 128, gdn.GDN_BF16, 64, 0, 0, 1, ctypes.byref(n)) == 0
+    assert lib.gdn_chunk_workspace_size(1, 262144, 16, 16, 128, 128, gdn.GDN_BF16, 64, 0, 0, 1, ctypes.byref(n)) == 0
     need = n.value
     assert need > 0
     wsb = ctypes.c_size_t(0)
@@ -117,27 +117,27 @@ def test_workspace_segments_flag(lib):
     n = ctypes.c_size_t(0)
     seg = lambda p: (p & 0xFF) << 8
     # explicit single segment: no workspace; explicit 4 segments on a short input: workspace
-    assert lib.gdn_chunk_workspace_size(1, 262144, 16, 128, 128, 1, 64, 0, 0, 1 | seg(1), ctypes.byref(n)) == 0
+    assert lib.gdn_chunk_workspace_size(1, 262144, 16, 16, 128, 128, 1, 64, 0, 0, 1 | seg(1), ctypes.byref(n)) == 0
     assert n.value == 0
-    assert lib.gdn_chunk_workspace_size(2, 256, 2, 64, 32, 1, 64, 0, 0, 1 | seg(4), ctypes.byref(n)) == 0
+    assert lib.gdn_chunk_workspace_size(2, 256, 2, 2, 64, 32, 1, 64, 0, 0, 1 | seg(4), ctypes.byref(n)) == 0
     units = 2 * 4 * 2
     assert n.value >= units * (32 * 64 + 64 * 64 + 1) * 4
     # many (sequence, head) units: automatic single pass
-    assert lib.gdn_chunk_workspace_size(64, 64 * 4096, 32, 128, 128, 1, 64, 1, 0, 1, ctypes.byref(n)) == 0
+    assert lib.gdn_chunk_workspace_size(64, 64 * 4096, 32, 32, 128, 128, 1, 64, 1, 0, 1, ctypes.byref(n)) == 0
     assert n.value == 0
     # segments need the bf16 path (with or without conv)
-    assert lib.gdn_chunk_workspace_size(1, 4096, 1, 32, 32, 0, 64, 0, 0, 1 | seg(2), ctypes.byref(n)) == \
+    assert lib.gdn_chunk_workspace_size(1, 4096, 1, 1, 32, 32, 0, 64, 0, 0, 1 | seg(2), ctypes.byref(n)) == \
         gdn.GDN_ERR_UNSUPPORTED
-    assert lib.gdn_chunk_workspace_size(1, 4096, 1, 32, 32, 1, 64, 0, 1, 1 | seg(2), ctypes.byref(n)) == 0
+    assert lib.gdn_chunk_workspace_size(1, 4096, 1, 1, 32, 32, 1, 64, 0, 1, 1 | seg(2), ctypes.byref(n)) == 0
     assert n.value > 0
 
 
 def test_workspace_size_validation(lib):
     n = ctypes.c_size_t(0)
-    assert lib.gdn_chunk_workspace_size(1, 64, 1, 33, 32, 1, 64, 0, 0, 1, ctypes.byref(n)) == gdn.GDN_ERR_UNSUPPORTED
-    assert lib.gdn_chunk_workspace_size(3, 64, 1, 32, 32, 1, 64, 0, 0, 1, ctypes.byref(n)) == gdn.GDN_ERR_INVALID_ARG
-    assert lib.gdn_chunk_workspace_size(1, 64, 1, 32, 32, 1, 64, 0, 0, 1, None) == gdn.GDN_ERR_INVALID_ARG
-    assert lib.gdn_chunk_workspace_size(1, 64, 1, 32, 32, 1, 64, 0, 0, 1 << 16, ctypes.byref(n)) == \
+    assert lib.gdn_chunk_workspace_size(1, 64, 1, 1, 33, 32, 1, 64, 0, 0, 1, ctypes.byref(n)) == gdn.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_chunk_workspace_size(3, 64, 1, 1, 32, 32, 1, 64, 0, 0, 1, ctypes.byref(n)) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_chunk_workspace_size(1, 64, 1, 1, 32, 32, 1, 64, 0, 0, 1, None) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_chunk_workspace_size(1, 64, 1, 1, 32, 32, 1, 64, 0, 0, 1 << 20, ctypes.byref(n)) == \
         gdn.GDN_ERR_INVALID_ARG
 
 
@@ -179,3 +179,29 @@ def test_python_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(gdn, "_LIB_PATH", "/nonexistent/libgdn.so")
     with pytest.raises(RuntimeError, match="not built"):
         gdn.load_library()
+
+
+def test_workspace_conv_pass(lib):
+    """A bf16 call with conv weights needs room for the convolved q, k and v (the conv pass), unless
+    the conv runs inside the chunk kernel (GDN_CONV_FUSED); the fp32 path never does."""
+    n = ctypes.c_size_t(0)
+    a256 = lambda x: (x + 255) // 256 * 256
+    N, T, H, Hk, dk, dv = 2, 1000, 4, 2, 64, 32
+    one_seg = 1 | (1 << 8)
+    assert lib.gdn_chunk_workspace_size(N, T, H, Hk, dk, dv, 1, 64, 1, 1, one_seg, ctypes.byref(n)) == 0
+    assert n.value == 2 * a256(T * Hk * dk * 2) + a256(T * H * dv * 2)
+    assert lib.gdn_chunk_workspace_size(N, T, H, Hk, dk, dv, 1, 64, 1, 1, one_seg | gdn.GDN_CONV_FUSED,
+                                        ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.gdn_chunk_workspace_size(N, T, H, Hk, dk, dv, 0, 64, 1, 1, one_seg, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.gdn_chunk_workspace_size(N, T, H, Hk, dk, dv, 1, 64, 1, 0, one_seg, ctypes.byref(n)) == 0
+    assert n.value == 0
+    # a bf16 conv call without that workspace reports the size and launches nothing
+    big = 1 << 32
+    wsb = ctypes.c_size_t(0)
+    st = chunk(lib, N=N, T=T, H=H, Hk=Hk, dk=dk, dv=dv, q=big, k=2 * big, v=3 * big, g=4 * big, beta=5 * big,
+               o=6 * big, conv=7 * big, cu=8 * big, flags=one_seg, wsb=ctypes.byref(wsb))
+    assert st == gdn.GDN_ERR_WORKSPACE and wsb.value == 2 * a256(T * Hk * dk * 2) + a256(T * H * dv * 2)
+    # Hk must divide H here too
+    assert lib.gdn_chunk_workspace_size(N, T, 3, 2, dk, dv, 1, 64, 1, 1, 1, ctypes.byref(n)) == gdn.GDN_ERR_INVALID_ARG

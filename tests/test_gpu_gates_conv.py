@@ -31,12 +31,13 @@ def _oracle_gates(a, b, gp):
     return oracle.gates(a, b, gp[0], gp[1])
 
 
-def _prefill(wl, *, g, beta, gate_params=None, conv_state=None, segments=0):
+def _prefill(wl, *, g, beta, gate_params=None, conv_state=None, segments=0, conv_fused=False):
     from linear_attention_sequence_rule_amd import gdn_chunk_fwd
     import torch
     o, sf = gdn_chunk_fwd(TL.to_dev(wl.q), TL.to_dev(wl.k), TL.to_dev(wl.v), TL.to_dev(g), TL.to_dev(beta),
                           TL.to_dev(wl.s0), TL.to_dev(wl.cu_seqlens), TL.to_dev(wl.conv_w), N=wl.N,
-                          gate_params=TL.to_dev(gate_params), conv_state=conv_state, segments=segments)
+                          gate_params=TL.to_dev(gate_params), conv_state=conv_state, segments=segments,
+                          conv_fused=conv_fused)
     torch.cuda.synchronize()
     return TL.o_to_f64(o), sf.cpu().numpy().astype(np.float64)
 
@@ -104,14 +105,15 @@ def _check_step(dtype, og, sg, o_ref, s_ref):
 
 # ------------------------------------------------------------------------------ conv state
 
-@pytest.mark.parametrize("dtype,dk,dv", [("f32", 32, 64), ("bf16", 128, 128), ("bf16", 64, 32)])
-def test_conv_state_prefill(dtype, dk, dv):
+@pytest.mark.parametrize("dtype,dk,dv,fused", [("f32", 32, 64, False), ("bf16", 128, 128, False),
+                                               ("bf16", 64, 32, False), ("bf16", 128, 64, True)])
+def test_conv_state_prefill(dtype, dk, dv, fused):
     """History in, history out: sequences of 0, 1, 2 and 3 tokens keep part of the old history."""
     wl = W.make("conv_state", seed=430 + dk + dv, lengths=[130, 0, 1, 2, 3, 64, 77], H=2, dk=dk, dv=dv,
                 dtype=dtype, s0_std=0.05, conv=True, varlen=True)
     _, hist = W.conv_inputs(wl.meta["seed"], wl.N, wl.H, dk, dv, dtype)
     cs = TL.to_dev(hist)
-    o, s = _prefill(wl, g=wl.g, beta=wl.beta, conv_state=cs)
+    o, s = _prefill(wl, g=wl.g, beta=wl.beta, conv_state=cs, conv_fused=fused)
     o_ref, s_ref, _, h_ref = _oracle(wl, wl.g, wl.beta, hist=W.bf16_bits_to_f32(hist) if dtype == "bf16" else hist)
     e = TL.compare(wl, o, s, o_ref, s_ref)
     np.testing.assert_array_equal(_hist_to_f64(cs), h_ref)

@@ -75,25 +75,28 @@ def test_bf16_conv_varlen_small():
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 32), (32, 128), (128, 64)])
-def test_bf16_conv_dims(dk, dv):
+@pytest.mark.parametrize("fused", [False, True])
+def test_bf16_conv_dims(dk, dv, fused):
+    """The conv prologue as a separate pass (default) and inside the chunk kernel (GDN_CONV_FUSED)."""
     wl = W.make("bf16_conv", seed=300 + dk + dv, lengths=[200, 3, 64, 0, 131], H=3, dk=dk, dv=dv, dtype="bf16",
                 s0_std=0.05, conv=True, varlen=True)
-    o, s = TL.run_gpu(wl, scale=0.8)
+    o, s = TL.run_gpu(wl, scale=0.8, conv_fused=fused)
     o_ref, s_ref = TL.run_oracle(wl, scale=0.8)
     e = TL.compare(wl, o, s, o_ref, s_ref)
-    _flush("bf16_conv %d %d %s" % (dk, dv, e))
+    _flush("bf16_conv %d %d fused=%s %s" % (dk, dv, fused, e))
 
 
-def test_bf16_conv_segments():
+@pytest.mark.parametrize("fused", [False, True])
+def test_bf16_conv_segments(fused):
     """Conv prologue on the segmented path: segments that start inside a sequence take the three
     previous raw tokens as conv history; one head decays slowly so the corrections run long."""
     wl = W.make("conv_seg", seed=51, lengths=[700, 130, 1, 520], H=2, dk=128, dv=64, dtype="bf16", s0_std=0.02,
                 conv=True, varlen=True)
     wl.g[:, 1] = -1e-3
-    o, s = TL.run_gpu(wl, segments=3)
+    o, s = TL.run_gpu(wl, segments=3, conv_fused=fused)
     o_ref, s_ref = TL.run_oracle(wl)
     e = TL.compare(wl, o, s, o_ref, s_ref)
-    _flush("conv segments %s" % e)
+    _flush("conv segments fused=%s %s" % (fused, e))
 
 
 def test_bf16_slow_decay():
