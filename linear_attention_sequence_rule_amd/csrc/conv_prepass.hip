@@ -31,7 +31,15 @@ __device__ __forceinline__ void ld8(const bf16* p, float (&x)[CPL]) {
         x[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xffff0000u);
     }
 }
-__device__ __forceinline__ uint4 raw8(const bf16* p) { return *reinterpret_cast<const uint4*>(p); }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// streaming accesses: every raw and convolved element is touched once here
+__device__ __forceinline__ uint4 raw8(const bf16* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void out8(bf16* p, uint4 v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
 __device__ __forceinline__ void unpack8(uint4 v, float (&x)[CPL]) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(256) void conv_prepass_kernel(const bf16* __restric
                              wt[c + 1][3] * x[c + 1];
             o[c / 2] = (uint32_t)f32_to_bf16(silu_f(ya)) | ((uint32_t)f32_to_bf16(silu_f(yb)) << 16);
         }
-        *reinterpret_cast<uint4*>(dst + t * width) = make_uint4(o[0], o[1], o[2], o[3]);
+        out8(dst + t * width, make_uint4(o[0], o[1], o[2], o[3]));
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             h0[c] = h1[c];
