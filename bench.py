@@ -51,8 +51,8 @@ def decode_alg_bytes(N, H, dk, dv):
 
 
 def load_traffic(kernel_tag):
-    """HBM traffic per launch measured with rocprofv3 counters (profiles/traffic.json), valid
-    only while the kernel source hash matches the one recorded with the counters."""
+    """HBM traffic per call measured with rocprofv3 counters (profiles/traffic.json), valid only
+    while the hashes of the sources recorded with the counters still match."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -63,9 +63,13 @@ def load_traffic(kernel_tag):
         return None
     if not rec:
         return None
-    src = os.path.join(ROOT, "linear_attention_sequence_rule_amd", "csrc", rec["source"])
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return rec["bytes_per_launch"] if h == rec["source_sha"] else None
+    shas = dict(rec.get("also", {}))
+    shas[rec["source"]] = rec["source_sha"]
+    for name, want in shas.items():
+        src = os.path.join(ROOT, "linear_attention_sequence_rule_amd", "csrc", name)
+        if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != want:
+            return None
+    return rec["bytes_per_launch"]
 
 
 def main():
