@@ -1125,29 +1125,6 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
             for (int r = 0; r < 3; ++r) reinterpret_cast<__bf16*>(sm + S::raw(r) + S::rV)[i] = (__bf16)0.f;
     }
 
-    RowRegs<DK> st;
-    const int row = vb * BV + 16 * wid + l16;  // state row of this lane (row waves)
-    const size_t srow0 = ((size_t)pair * p.dv + row) * DK;
-    if (is_row) {
-        const float* src = nullptr;
-        if (p.init == INIT_S0 && p.s0 && seg == 0)
-            src = p.s0 + (((size_t)n * p.H + h) * p.dv + row) * DK;
-        else if (p.init == INIT_PREV)
-            src = p.s0 + (((size_t)(nseg - 1) * p.H + h) * p.dv + row) * DK;
-#pragma unroll
-        for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
-            if (src) {
-                const float4 v = *reinterpret_cast<const float4*>(src + kcol(dt, 4 * g));
-                st.S[dt] = fx4{v.x, v.y, v.z, v.w};
-            } else if (p.init == INIT_IDENTITY) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) st.S[dt][e] = (kcol(dt, 4 * g + e) == row) ? 1.f : 0.f;
-            } else {
-                st.S[dt] = zero4();
-            }
-        }
-    }
-
     const unsigned smb = lds_base(sm);
     const bool conv = p.conv_w != nullptr;
     ConvW<DK, BV> cw;
@@ -1165,82 +1142,118 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     lds_barrier();
     if (conv && nchunks > 0) conv_chunk<DK, BV>(p, cw, smb + S::raw(0), smb + S::HB, clen(0), tid);
 
-    // iteration k: state and output on chunk k, Pm of chunk k, L and T of chunk k+1, loads of k+2
+    // Iteration k: state and output on chunk k, Pm of chunk k, L and T of chunk k+1, loads of k+2.
+    // The row/load waves and the prep waves run separate copies of the loop with the same barrier
+    // sequence, so that each role's registers are allocated for its own code only.  Every wave
+    // reads the same transition bounds in the same order, so an early exit is uniform.
     float decay = 0.f;  // log bound of the transition over the chunks the state has passed
-    int stopped = 0;
-    for (int k = -1; k < nchunks; ++k) {
-        const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
-        const long tk = bos + (long)k * C;
-        // ---- A
-        if (cur) {
-            unsigned char* rawk = sm + S::raw(k);
-            unsigned char* gbk = sm + S::gates(k);
-            if (is_row) row_A<DK, BV>(st, sm, rawk, gbk, wid, lane);
-            if (pw == 1) prep_P<DK, 0>(rawk, sm, lane, clen(k), p.l2norm);
-            if (pw == 2) prep_P<DK, 1>(rawk, sm, lane, clen(k), p.l2norm);
-        }
-        if (nxt && pw == 0) prep_L<DK, 0>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
-        if (nxt && pw == 3) prep_L<DK, 1>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
-        // the loads of chunk k+2 from waves 2 and 3 (rows 32 (w - 2) .. + 31), after their row work:
-        // waves 0 and 1 share their SIMDs with the solve of the next sub-stage and wait for nothing.
-        // The buffer held chunk k-1, whose last reads were before the previous barrier.
-        if (far && is_load) {
-            dma_chunk<DK, BV>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2), lane);
-            dma_chunk<DK, BV>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2) + 1, lane);
-        }
-        lds_barrier();
-        // ---- B
-        if (cur) {
-            unsigned char* rawk = sm + S::raw(k);
-            unsigned char* gbk = sm + S::gates(k);
-            if (is_row) row_B<DK, BV>(p, st, sm, rawk, gbk, wid, lane, tk, clen(k), h, vb);
-            if (p.early_exit || p.negl_mode == NEGL_MARK)
-                decay += __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
-                                                       int, reinterpret_cast<const float*>(gbk + S::gGC)[1])));
-        }
-        if (nxt && (pw == 0 || pw == 1)) {
-            // the solve is this sub-stage's longest chain: its instructions go first on the SIMD
-            __builtin_amdgcn_s_setprio(3);
-            const __bf16* sLt = reinterpret_cast<const __bf16*>(sm + S::L);
-            __bf16* Tt = reinterpret_cast<__bf16*>(sm + S::T);
-            const float* rk = reinterpret_cast<const float*>(sm + S::WL);
-            const float* beta = reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB);
-            solve_diag(sLt, Tt, rk, beta, 2 * pw, lane);
-            solve_level1(sLt, Tt, rk, beta, 2 * pw, lane);
-            __builtin_amdgcn_s_setprio(0);
-        }
-        if (nxt && pw == 2)
-            copy_LBA(reinterpret_cast<const __bf16*>(sm + S::L), reinterpret_cast<__bf16*>(sm + S::T),
-                     reinterpret_cast<const float*>(sm + S::WL), reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB),
-                     lane);
-        if (nxt && pw == 3) make_gates<DK>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
-        if (far && is_load) {
-            wait_loads();
-            if (RAW && wid == 2) {
-                raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 0, lane, h);
-                raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 1, lane, h);
-            }
-            zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2), lane);
-            zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2) + 1, lane);
-        }
-        lds_barrier();
-        // every wave read the same bounds in the same order: the exit is uniform
-        if (p.early_exit && decay <= kExitLog) {
-            stopped = 1;
-            break;
-        }
-        // ---- C (conv only): the prologue on chunk k+2, whose loads have all landed
-        if (conv && far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
-    }
-
-    if (is_row && p.sfin) {
+    auto bound = [&](int k) {
+        if (p.early_exit || p.negl_mode == NEGL_MARK)
+            decay += __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                                                   int, reinterpret_cast<const float*>(sm + S::gates(k) + S::gGC)[1])));
+    };
+    if (!is_prep) {
+        RowRegs<DK> st;
+        const int row = vb * BV + 16 * wid + l16;  // state row of this lane (row waves)
+        if (is_row) {
+            const float* src = nullptr;
+            if (p.init == INIT_S0 && p.s0 && seg == 0)
+                src = p.s0 + (((size_t)n * p.H + h) * p.dv + row) * DK;
+            else if (p.init == INIT_PREV)
+                src = p.s0 + (((size_t)(nseg - 1) * p.H + h) * p.dv + row) * DK;
 #pragma unroll
-        for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
-            const fx4 v = st.S[dt];
-            *reinterpret_cast<float4*>(p.sfin + srow0 + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
+            for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
+                if (src) {
+                    const float4 v = *reinterpret_cast<const float4*>(src + kcol(dt, 4 * g));
+                    st.S[dt] = fx4{v.x, v.y, v.z, v.w};
+                } else if (p.init == INIT_IDENTITY) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) st.S[dt][e] = (kcol(dt, 4 * g + e) == row) ? 1.f : 0.f;
+                } else {
+                    st.S[dt] = zero4();
+                }
+            }
+        }
+        int stopped = 0;
+        for (int k = -1; k < nchunks; ++k) {
+            const bool cur = k >= 0, far = k + 2 < nchunks;
+            const long tk = bos + (long)k * C;
+            // ---- A
+            if (cur && is_row) row_A<DK, BV>(st, sm, sm + S::raw(k), sm + S::gates(k), wid, lane);
+            // the loads of chunk k+2 from waves 2 and 3 (rows 32 (w - 2) .. + 31), after their row
+            // work: waves 0 and 1 share their SIMDs with the solve of the next sub-stage and wait for
+            // nothing.  The buffer held chunk k-1, whose last reads were before the previous barrier.
+            if (far && is_load) {
+                dma_chunk<DK, BV>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2), lane);
+                dma_chunk<DK, BV>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2) + 1, lane);
+            }
+            lds_barrier();
+            // ---- B
+            if (cur) {
+                if (is_row) row_B<DK, BV>(p, st, sm, sm + S::raw(k), sm + S::gates(k), wid, lane, tk, clen(k), h, vb);
+                bound(k);
+            }
+            if (far && is_load) {
+                wait_loads();
+                if (RAW && wid == 2) {
+                    raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 0, lane, h);
+                    raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 1, lane, h);
+                }
+                zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2), lane);
+                zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2) + 1, lane);
+            }
+            lds_barrier();
+            if (p.early_exit && decay <= kExitLog) {
+                stopped = 1;
+                break;
+            }
+            // ---- C (conv only): the prologue on chunk k+2, whose loads have all landed
+            if (conv && far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
+        }
+        if (is_row && p.sfin) {
+            const size_t srow0 = ((size_t)pair * p.dv + row) * DK;
+#pragma unroll
+            for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
+                const fx4 v = st.S[dt];
+                *reinterpret_cast<float4*>(p.sfin + srow0 + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+        if (p.negl && vb == 0 && tid == 0) p.negl[pair] = p.negl_mode == NEGL_MARK ? (decay <= kExitLog) : stopped;
+    } else {
+        for (int k = -1; k < nchunks; ++k) {
+            const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
+            // ---- A
+            if (cur) {
+                unsigned char* rawk = sm + S::raw(k);
+                if (pw == 1) prep_P<DK, 0>(rawk, sm, lane, clen(k), p.l2norm);
+                if (pw == 2) prep_P<DK, 1>(rawk, sm, lane, clen(k), p.l2norm);
+            }
+            if (nxt && pw == 0) prep_L<DK, 0>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
+            if (nxt && pw == 3) prep_L<DK, 1>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
+            lds_barrier();
+            // ---- B
+            if (cur) bound(k);
+            if (nxt && (pw == 0 || pw == 1)) {
+                // the solve is this sub-stage's longest chain: its instructions go first on the SIMD
+                __builtin_amdgcn_s_setprio(3);
+                const __bf16* sLt = reinterpret_cast<const __bf16*>(sm + S::L);
+                __bf16* Tt = reinterpret_cast<__bf16*>(sm + S::T);
+                const float* rk = reinterpret_cast<const float*>(sm + S::WL);
+                const float* beta = reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB);
+                solve_diag(sLt, Tt, rk, beta, 2 * pw, lane);
+                solve_level1(sLt, Tt, rk, beta, 2 * pw, lane);
+                __builtin_amdgcn_s_setprio(0);
+            }
+            if (nxt && pw == 2)
+                copy_LBA(reinterpret_cast<const __bf16*>(sm + S::L), reinterpret_cast<__bf16*>(sm + S::T),
+                         reinterpret_cast<const float*>(sm + S::WL),
+                         reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB), lane);
+            if (nxt && pw == 3) make_gates<DK>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
+            lds_barrier();
+            if (p.early_exit && decay <= kExitLog) break;
+            if (conv && far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
         }
     }
-    if (p.negl && vb == 0 && tid == 0) p.negl[pair] = p.negl_mode == NEGL_MARK ? (decay <= kExitLog) : stopped;
 }
 
 // One pass of the kernel.  rows = state rows (dv, or dk for the transition pass).
