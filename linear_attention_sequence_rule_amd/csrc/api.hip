@@ -34,14 +34,14 @@ int check_common(int H, int dk, int dv, int dtype, float scale, unsigned flags) 
 
 // Segments per sequence for this call (1 = single pass).  A request for more than one segment is
 // honoured on the bf16 path only.
-int segments_for(int N, int T_tot, int H, int dv, int dtype, bool, unsigned flags, int* P) {
+int segments_for(int N, int T_tot, int H, int dk, int dv, int dtype, bool has_conv, unsigned flags, int* P) {
     const int req = (int)((flags & kSegMask) >> 8);
     if (dtype != GDN_BF16) {
         if (req > 1) return GDN_ERR_UNSUPPORTED;
         *P = 1;
         return GDN_OK;
     }
-    *P = gdn::plan_segments(N, T_tot, H, dv, req);
+    *P = gdn::plan_segments(N, T_tot, H, dk, dv, has_conv && (flags & kConvFused), req);
     return GDN_OK;
 }
 
@@ -81,7 +81,7 @@ int gdn_chunk_workspace_size(int N, int T_tot, int H, int Hk, int dk, int dv, in
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (!has_cu_seqlens && T_tot % N != 0) return GDN_ERR_INVALID_ARG;
     int P = 1;
-    st = segments_for(N, T_tot, H, dv, dtype, has_conv != 0, flags, &P);
+    st = segments_for(N, T_tot, H, dk, dv, dtype, has_conv != 0, flags, &P);
     if (st != GDN_OK) return st;
     *bytes = workspace_for(N, T_tot, H, Hk, dk, dv, P, conv_pass(has_conv != 0, dtype, flags));
     return GDN_OK;
@@ -141,7 +141,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
         return GDN_ERR_INVALID_ARG;
 
     int P = 1;
-    st = segments_for(N, T_tot, H, dv, dtype, conv_w != nullptr, flags, &P);
+    st = segments_for(N, T_tot, H, dk, dv, dtype, conv_w != nullptr, flags, &P);
     if (st != GDN_OK) return st;
     const bool cpass = conv_pass(conv_w != nullptr, dtype, flags);
     const size_t need = workspace_for(N, T_tot, H, Hk, dk, dv, P, cpass);

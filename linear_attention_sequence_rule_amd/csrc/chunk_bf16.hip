@@ -58,7 +58,8 @@ typedef float fx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int C = 64;        // chunk length
-constexpr int BVMAX = 64;    // state rows per workgroup: BV = 64, or 32 when the state has 32 rows
+constexpr int BVMAX = 64;    // state rows of a narrow workgroup: 64, or 32 when the state has 32 rows
+constexpr int BVW = 128;     // state rows of a wide workgroup (d_k = 128, no in-kernel conv)
 constexpr int TSTR = C + 8;  // bf16 row stride of T^T, Pm and L^T
 
 __device__ __forceinline__ fx4 mfma(bf16x8 a, bf16x8 b, fx4 c) {
@@ -180,16 +181,23 @@ __device__ __forceinline__ float sel4(fx4 v, int e) {
 }
 
 // ------------------------------------------------------------------------------------------
-// LDS layout (bytes).  Raw chunk buffers rotate by chunk index mod 3, gate buffers by chunk parity.
-template <int DK>
+// LDS layout (bytes).  A chunk's K, g and beta sit in one of three buffers that rotate by chunk
+// index mod 3.  Narrow workgroups (up to 64 state rows) keep its Q and V in the same buffer; wide
+// ones (128 rows) keep them in one of two buffers of their own that rotate by chunk parity: Q and V
+// are read only in the first sub-stage of the chunk's iteration, so they are loaded one chunk
+// ahead instead of two.  Gate buffers rotate by chunk parity.
+template <int DK, int BV>
 struct Smem {
-    // raw chunk buffer (K, Q, V swizzled, unpadded)
-    static constexpr int rK = 0;                     // bf16 [C][DK]
-    static constexpr int rQ = rK + C * DK * 2;       // bf16 [C][DK]
-    static constexpr int rV = rQ + C * DK * 2;       // bf16 [C][BV] (room for BVMAX)
-    static constexpr int rG = rV + C * BVMAX * 2;    // raw g [C]
-    static constexpr int rB = rG + C * 4;            // beta [C]
+    static constexpr bool WIDE = BV > BVMAX;
+    // K buffer (narrow: the whole raw chunk buffer); K, Q, V swizzled, unpadded
+    static constexpr int rK = 0;                                  // bf16 [C][DK]
+    static constexpr int rQ = WIDE ? 0 : rK + C * DK * 2;         // bf16 [C][DK] (wide: in the Q/V buffer)
+    static constexpr int rV = rQ + C * DK * 2;                    // bf16 [C][BV] (narrow: room for BVMAX)
+    static constexpr int rG = WIDE ? C * DK * 2 : rV + C * BVMAX * 2;  // raw g [C]
+    static constexpr int rB = rG + C * 4;                         // beta [C]
     static constexpr int rBytes = rB + C * 4;
+    static constexpr int qvBytes = WIDE ? rV + C * BV * 2 : 0;    // wide: Q/V buffer
+    static constexpr int NQV = WIDE ? 2 : 0;
     // gates of a chunk
     static constexpr int gKK = 0;                    // beta Gamma rk^2 [C]
     static constexpr int gVB = gKK + C * 4;          // beta rk [C]
@@ -199,17 +207,20 @@ struct Smem {
     static constexpr int gBytes = gGC + 64;
     // layout
     static constexpr int R0 = 0;
-    static constexpr int G0 = R0 + 3 * rBytes;
+    static constexpr int Q0 = R0 + 3 * rBytes;
+    static constexpr int G0 = Q0 + NQV * qvBytes;
     static constexpr int T = G0 + 2 * gBytes;        // T^T bf16 [C][TSTR] (T^T[m][i] = T_im); L_BA in the T_BA block
     static constexpr int PM = T + C * TSTR * 2;      // Pm bf16 [C][TSTR], row-major [i][m]
     static constexpr int L = PM + C * TSTR * 2;      // L^T bf16 [C][TSTR]: L^T[j][i] = L_ij
     static constexpr int ORQ = L + C * TSTR * 2;     // rq [C]
     static constexpr int WL = ORQ + C * 4;           // L-prep scratch, per wave: rk, gamma log2e [2][2][C]
     static constexpr int WP = WL + 4 * C * 4;        // P-prep scratch, per wave: rq, gamma log2e [2][2][C]
-    static constexpr int HB = WP + 4 * C * 4;        // conv halo: 3 raw rows [3][DK + BV/2] channel pairs
-    static constexpr int bytes = HB + 3 * (DK + BVMAX / 2) * 4;
-    static_assert(rBytes % 16 == 0 && gBytes % 16 == 0, "alignment");
-    static __device__ __forceinline__ int raw(int c) { return R0 + (c % 3) * rBytes; }
+    static constexpr int HB = WP + 4 * C * 4;        // conv halo (narrow): 3 raw rows [3][DK + BV/2] channel pairs
+    static constexpr int bytes = HB + (WIDE ? 0 : 3 * (DK + BVMAX / 2) * 4);
+    static_assert(rBytes % 16 == 0 && gBytes % 16 == 0 && qvBytes % 16 == 0, "alignment");
+    static_assert(bytes <= 160 * 1024, "LDS of one gfx950 compute unit");
+    static __device__ __forceinline__ int raw(int c) { return R0 + (c % 3) * rBytes; }  // K, g, beta (narrow: all)
+    static __device__ __forceinline__ int qv(int c) { return WIDE ? Q0 + (c & 1) * qvBytes : raw(c); }  // Q, V
     static __device__ __forceinline__ int gates(int c) { return G0 + (c & 1) * gBytes; }
 };
 
@@ -279,50 +290,71 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
     return reinterpret_cast<const T*>((static_cast<uintptr_t>(hi) << 32) | lo);
 }
 
+// Rows [r0, r0 + NR) of a swizzled W-wide bf16 tile (W/8 16-byte slots per row, swz<W>) from global
+// rows rowb bytes apart starting at base (wave-uniform: the chunk's first token); tile = LDS byte
+// address of the tile.  Rows past the tail re-read the last valid row.
+template <int W, int NR>
+__device__ __forceinline__ void dma_tile(const __bf16* base, unsigned rowb, unsigned tile, int len, unsigned r0,
+                                         unsigned ul) {
+    constexpr unsigned PPR = W / 8;    // 16-byte slots per row
+    constexpr unsigned RPI = 64 / PPR;  // rows per 1 KB instruction
+    static_assert(NR % RPI == 0, "whole instructions per part");
+    const unsigned lrow = ul / PPR, slot = ul % PPR;
+#pragma unroll
+    for (unsigned j = 0; j < NR / RPI; ++j) {
+        const unsigned row0 = r0 + RPI * j;
+        const unsigned part = slot ^ ((row0 + lrow) % PPR);  // the swizzle key of the lane's row
+        const unsigned voff = len == C ? (lrow + row0) * rowb + 16u * part
+                                       : (unsigned)min((int)(row0 + lrow), len - 1) * rowb + 16u * part;
+        dma16(base, voff, lds_addr(tile + row0 * W * 2));
+    }
+}
+// g (which = 0) or beta (1) of the chunk's tokens into [C] floats at LDS byte address dst
+template <int DK>
+__device__ __forceinline__ void dma_gates_in(const Params<DK>& p, unsigned dst, long t0, int len, int h, int which,
+                                             int lane) {
+    const float* gbase = uniform_ptr((which == 0 ? p.g : p.beta) + (size_t)t0 * p.H + h);
+    const unsigned voff = (unsigned)min(lane, len - 1) * (unsigned)p.H * 4u;
+    dma4(gbase, voff, lds_addr(dst));
+}
+template <int DK, int NR>
+__device__ __forceinline__ void dma_k(const Params<DK>& p, unsigned tile, long t0, int len, int hk, int r0, int lane) {
+    const size_t tokk = (size_t)t0 * p.Hk + hk;
+    dma_tile<DK, NR>(uniform_ptr(p.k + tokk * DK), (unsigned)(p.Hk * DK) * 2u, tile, len, r0, (unsigned)opaque(lane));
+}
+template <int DK, int NR>
+__device__ __forceinline__ void dma_q(const Params<DK>& p, unsigned tile, long t0, int len, int hk, int r0, int lane) {
+    const size_t tokk = (size_t)t0 * p.Hk + hk;
+    dma_tile<DK, NR>(uniform_ptr(p.q + tokk * DK), (unsigned)(p.Hk * DK) * 2u, tile, len, r0, (unsigned)opaque(lane));
+}
+template <int DK, int BV, int NR>
+__device__ __forceinline__ void dma_v(const Params<DK>& p, unsigned tile, long t0, int len, int h, int vb, int r0,
+                                      int lane) {
+    const size_t tok0 = (size_t)t0 * p.H + h;
+    dma_tile<BV, NR>(uniform_ptr(p.v + tok0 * p.dv + vb * BV), (unsigned)(p.H * p.dv) * 2u, tile, len, r0,
+                     (unsigned)opaque(lane));
+}
+
+// Narrow workgroups: part w (0..3) of a chunk is rows [16w, 16w + 16) of K, Q and V, and g (part 0)
+// or beta (part 1).
 template <int DK, int BV>
 __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned smb, int rawoff, long t0, int len, int h,
                                           int hk, int vb, int wid, int lane) {
-    lane = opaque(lane);
-    using S = Smem<DK>;
-    constexpr unsigned PPR = DK / 8;     // 16-byte slots per K/Q row
-    constexpr unsigned RPI = 64 / PPR;   // rows per 1 KB instruction
-    const size_t tok0 = (size_t)t0 * p.H + h, tokk = (size_t)t0 * p.Hk + hk;
-    const __bf16* kb = uniform_ptr(p.k + tokk * DK);
-    const __bf16* qb = uniform_ptr(p.q + tokk * DK);
-    const unsigned rowq = (unsigned)(p.Hk * DK) * 2u;  // bytes between tokens
-    const unsigned ul = (unsigned)lane, lrow = ul / PPR, slot = ul % PPR;
-    // Full chunks (every chunk but a sequence's last): lane offsets are a lane constant plus a
-    // wave-uniform row offset.
-    const unsigned lane_q = lrow * rowq;
-#pragma unroll
-    for (unsigned j = 0; j < 16 / RPI; ++j) {
-        const unsigned row0 = 16u * (unsigned)wid + RPI * j;
-        const unsigned part = slot ^ ((row0 + lrow) % PPR);  // the swizzle key of the lane's row
-        const unsigned voff = len == C ? lane_q + row0 * rowq + 16u * part
-                                       : (unsigned)min((int)(row0 + lrow), len - 1) * rowq + 16u * part;
-        const int lo = rawoff + (int)row0 * DK * 2;
-        dma16(kb, voff, lds_addr(smb + lo + S::rK));
-        dma16(qb, voff, lds_addr(smb + lo + S::rQ));
-    }
-    if (!p.v_zero) {
-        constexpr unsigned VPR = BV / 8;    // 16-byte slots per V row
-        constexpr unsigned VRI = 64 / VPR;  // rows per 1 KB instruction
-        const __bf16* vbase = uniform_ptr(p.v + tok0 * p.dv + vb * BV);
-        const unsigned rowv = (unsigned)(p.H * p.dv) * 2u;
-        const unsigned vrow = ul / VPR, vslot = ul % VPR;
-#pragma unroll
-        for (unsigned j = 0; j < 16 / VRI; ++j) {
-            const unsigned row0 = 16u * (unsigned)wid + VRI * j;
-            const unsigned part = vslot ^ ((row0 + vrow) % VPR);
-            const unsigned voff = len == C ? (vrow + row0) * rowv + 16u * part
-                                           : (unsigned)min((int)(row0 + vrow), len - 1) * rowv + 16u * part;
-            dma16(vbase, voff, lds_addr(smb + rawoff + S::rV + (int)row0 * BV * 2));
-        }
-    }
-    if (wid < 2) {
-        const float* gbase = uniform_ptr((wid == 0 ? p.g : p.beta) + tok0);
-        const unsigned voff = (unsigned)min(lane, len - 1) * (unsigned)p.H * 4u;
-        dma4(gbase, voff, lds_addr(smb + rawoff + (wid == 0 ? S::rG : S::rB)));
+    using S = Smem<DK, BV>;
+    dma_k<DK, 16>(p, smb + rawoff + S::rK, t0, len, hk, 16 * wid, lane);
+    dma_q<DK, 16>(p, smb + rawoff + S::rQ, t0, len, hk, 16 * wid, lane);
+    if (!p.v_zero) dma_v<DK, BV, 16>(p, smb + rawoff + S::rV, t0, len, h, vb, 16 * wid, lane);
+    if (wid < 2) dma_gates_in<DK>(p, smb + rawoff + (wid == 0 ? S::rG : S::rB), t0, len, h, wid, lane);
+}
+
+// Rows >= len of rows [r0, r0 + NR) of a W-wide tile set to zero (whole rows, so the swizzle does
+// not matter).
+template <int W, int NR>
+__device__ __forceinline__ void zero_rows(__bf16* M, int len, int r0, int lane) {
+    const __bf16 z = (__bf16)0.f;
+    for (int i = lane; i < NR * W; i += 64) {
+        const int row = r0 + i / W;
+        if (row >= len) M[row * W + i % W] = z;
     }
 }
 
@@ -330,23 +362,11 @@ __device__ __forceinline__ void dma_chunk(const Params<DK>& p, unsigned smb, int
 template <int DK, int BV>
 __device__ __forceinline__ void zero_tail(unsigned char* raw, int len, int wid, int lane) {
     lane = opaque(lane);
-    using S = Smem<DK>;
+    using S = Smem<DK, BV>;
     if (len >= C) return;
-    __bf16* K = reinterpret_cast<__bf16*>(raw + S::rK);
-    __bf16* Q = reinterpret_cast<__bf16*>(raw + S::rQ);
-    __bf16* V = reinterpret_cast<__bf16*>(raw + S::rV);
-    const __bf16 z = (__bf16)0.f;
-    for (int i = lane; i < 16 * DK; i += 64) {
-        const int row = 16 * wid + i / DK;
-        if (row >= len) {
-            K[row * DK + i % DK] = z;
-            Q[row * DK + i % DK] = z;
-        }
-    }
-    for (int i = lane; i < 16 * BV; i += 64) {
-        const int row = 16 * wid + i / BV;
-        if (row >= len) V[row * BV + i % BV] = z;
-    }
+    zero_rows<DK, 16>(reinterpret_cast<__bf16*>(raw + S::rK), len, 16 * wid, lane);
+    zero_rows<DK, 16>(reinterpret_cast<__bf16*>(raw + S::rQ), len, 16 * wid, lane);
+    zero_rows<BV, 16>(reinterpret_cast<__bf16*>(raw + S::rV), len, 16 * wid, lane);
     if (wid < 2 && lane >= len) reinterpret_cast<float*>(raw + (wid == 0 ? S::rG : S::rB))[lane] = 0.f;
 }
 
@@ -355,9 +375,9 @@ __device__ __forceinline__ void zero_tail(unsigned char* raw, int len, int wid, 
 // raw_decay / raw_beta, on the hardware exp2 / log2 / reciprocal: log1p(y) for y = exp(-|x|) in
 // (0, 1] is taken as log(1 + y), whose absolute error (below 2^-23) is far under the bf16 path's
 // rounding, and this runs once per token on the wave that loaded the chunk.
-template <int DK>
+template <int DK, int BV>
 __device__ __forceinline__ void raw_gates(const Params<DK>& p, unsigned char* raw, int len, int part, int lane, int h) {
-    using S = Smem<DK>;
+    using S = Smem<DK, BV>;
     if (part >= 2) return;
     float* x = reinterpret_cast<float*>(raw + (part == 0 ? S::rG : S::rB));
     if (lane < len) {
@@ -422,7 +442,7 @@ struct PairLoc {
 };
 template <int DK, int BV>
 __device__ __forceinline__ PairLoc pair_loc(int pc) {
-    using S = Smem<DK>;
+    using S = Smem<DK, BV>;
     const bool isv = pc >= DK, isq = !isv && pc >= DK / 2;
     const int c = 2 * (isv ? pc - DK : (isq ? pc - DK / 2 : pc));
     PairLoc l;
@@ -599,10 +619,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // M (those rows of L^T: bf16, L^T[j][i] = M_ij G_ij for j < i); part 0 also leaves the norms rk of
 // every row (from the four diagonal tiles) and gamma log2e for the next sub-stage.
 // exp(gamma_i - gamma_j) = exp2 of a non-positive number.
-template <int DK, int part>
+template <int DK, int BV, int part>
 __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* sm, int lane, int len, int l2norm) {
     lane = opaque(lane);
-    using S = Smem<DK>;
+    using S = Smem<DK, BV>;
     constexpr int KS = DK / 32;
     constexpr int t0 = part ? 1 : 0, t1 = part ? 2 : 3;  // my row tiles
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
@@ -672,11 +692,11 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
 }
 
 // Wave 7, sub-stage B, on chunk k+1: the gates, from rk and gamma log2e left by part 0 of prep_L.
-template <int DK>
+template <int DK, int BV>
 __device__ __forceinline__ void make_gates(const unsigned char* raw, unsigned char* gb, const unsigned char* sm,
                                            int lane, int l2norm) {
     lane = opaque(lane);
-    using S = Smem<DK>;
+    using S = Smem<DK, BV>;
     const float* own = reinterpret_cast<const float*>(sm + S::WL);  // part 0: rk [C], gamma log2e [C]
     const float b = reinterpret_cast<const float*>(raw + S::rB)[lane];
     const float rk = own[lane];
@@ -713,13 +733,14 @@ __device__ __forceinline__ void row_factors(float (&f)[4 * N], const float* rk, 
 // Waves 5, 6 on chunk k: row tiles {0, 3} (half 0) or {1, 2} (half 1) of Pm' = lower(M o Q K^T)
 // of the raw rows, computed as D = K Q^T so that a lane holds 4 consecutive m of row i (bf16,
 // row-major), and rq of those rows (diagonal of Q Q^T).
-template <int DK, int half>
-__device__ __forceinline__ void prep_P(const unsigned char* raw, unsigned char* sm, int lane, int len, int l2norm) {
+template <int DK, int BV, int half>
+__device__ __forceinline__ void prep_P(const unsigned char* raw, const unsigned char* qv, unsigned char* sm, int lane,
+                                       int len, int l2norm) {
     lane = opaque(lane);
-    using S = Smem<DK>;
+    using S = Smem<DK, BV>;
     constexpr int KS = DK / 32;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
-    const __bf16* Q = reinterpret_cast<const __bf16*>(raw + S::rQ);
+    const __bf16* Q = reinterpret_cast<const __bf16*>(qv + S::rQ);
     const float* gr = reinterpret_cast<const float*>(raw + S::rG);
     float* own = reinterpret_cast<float*>(sm + S::WP) + half * 2 * C;  // rq [C], gamma log2e [C]
     __bf16* Pm = reinterpret_cast<__bf16*>(sm + S::PM);
@@ -909,13 +930,13 @@ struct RowRegs {
 // Y = beta rk V - beta Gamma rk^2 K S^T and U' = T' Y blockwise.
 template <int DK, int BV>
 __device__ __forceinline__ void row_A(RowRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
-                                      const unsigned char* gb, int wave, int lane) {
+                                      const unsigned char* qv, const unsigned char* gb, int wave, int lane) {
     lane = opaque(lane);
-    using S = Smem<DK>;
+    using S = Smem<DK, BV>;
     constexpr int KS = DK / 32;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
-    const __bf16* Q = reinterpret_cast<const __bf16*>(raw + S::rQ);
-    const __bf16* V = reinterpret_cast<const __bf16*>(raw + S::rV);
+    const __bf16* Q = reinterpret_cast<const __bf16*>(qv + S::rQ);
+    const __bf16* V = reinterpret_cast<const __bf16*>(qv + S::rV);
     const __bf16* Tt = reinterpret_cast<const __bf16*>(sm + S::T);
     const float* gKK = reinterpret_cast<const float*>(gb + S::gKK);
     const float* gVB = reinterpret_cast<const float*>(gb + S::gVB);
@@ -992,27 +1013,32 @@ __device__ __forceinline__ void row_A(RowRegs<DK>& st, unsigned char* sm, const 
 }
 
 // Sub-stage B: S^T <- Gamma_C S^T + K^T diag(exp(gamma_C - gamma)) U', and
-// O^T = [diag(Gamma) (S Q^T) + U'^T Pm'^T] diag(rq), stored (lane: token 16 it + l16, state rows
-// cbase + 4g .. +3).
+// O^T = [diag(Gamma) (S Q^T) + U'^T Pm'^T] diag(rq) (lane: token 16 it + l16, state rows
+// cbase + 4g .. +3), stored by row_store.
 template <int DK, int BV>
-__device__ __forceinline__ void row_B(const Params<DK>& p, RowRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
-                                      const unsigned char* gb, int wave, int lane, long t0, int len, int h, int vb) {
+__device__ __forceinline__ void row_B(RowRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
+                                      const unsigned char* gb, int lane) {
     lane = opaque(lane);
-    using S = Smem<DK>;
+    using S = Smem<DK, BV>;
     constexpr int DT = DK / 16;
+    // wide workgroups (three waves per SIMD) read K^T one token half at a time
+    constexpr int NH = S::WIDE ? 1 : 2;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
     const __bf16* Pm = reinterpret_cast<const __bf16*>(sm + S::PM);
     const float* orq = reinterpret_cast<const float*>(sm + S::ORQ);
     const float* gam = reinterpret_cast<const float*>(gb + S::gGAM);
     const float gc = reinterpret_cast<const float*>(gb + S::gGC)[0];
-    const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
-    bf16x8 kt[DT][2];
+    const int g = lane / 16, l16 = lane % 16;
+    bf16x8 kt[DT][NH];
+    auto read_kt = [&](int s2, int slot) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        const int o = off_trk<DK>(dt, g, l16);
-        kt[dt][0] = __builtin_shufflevector(tr_read(K + o), tr_read(K + o + 16 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
-        kt[dt][1] = __builtin_shufflevector(tr_read(K + o + 32 * DK), tr_read(K + o + 48 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
-    }
+        for (int dt = 0; dt < DT; ++dt) {
+            const int o = off_trk<DK>(dt, g, l16) + 32 * s2 * DK;
+            kt[dt][slot] = __builtin_shufflevector(tr_read(K + o), tr_read(K + o + 16 * DK), 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+#pragma unroll
+    for (int s2 = 0; s2 < NH; ++s2) read_kt(s2, s2);
     bf16x8 pf[4][2];
 #pragma unroll
     for (int it = 0; it < 4; ++it)
@@ -1031,9 +1057,8 @@ __device__ __forceinline__ void row_B(const Params<DK>& p, RowRegs<DK>& st, unsi
 #pragma unroll
         for (int e = 0; e < 4; ++e) st.S[dt][e] *= gc;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][s2], st.ut[s2], st.S[dt]);
+    for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][0], st.ut[0], st.S[dt]);
+    if constexpr (NH == 1) read_kt(1, 0);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
 #pragma unroll
@@ -1043,6 +1068,16 @@ __device__ __forceinline__ void row_B(const Params<DK>& p, RowRegs<DK>& st, unsi
 #pragma unroll
         for (int e = 0; e < 4; ++e) st.ot[it][e] *= r[it];
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][NH - 1], st.ut[1], st.S[dt]);
+}
+// The chunk's output rows of this wave's state rows (after the wave's loads have been waited for:
+// the stores would count in the same wait).
+template <int DK, int BV>
+__device__ __forceinline__ void row_store(const Params<DK>& p, const RowRegs<DK>& st, int wave, int lane, long t0,
+                                          int len, int h, int vb) {
+    lane = opaque(lane);
+    const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
     if (p.out != OUT_STORE) return;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -1061,20 +1096,27 @@ __device__ __forceinline__ void row_B(const Params<DK>& p, RowRegs<DK>& st, unsi
 // state carried in, its remaining contribution is far under fp32 rounding.
 constexpr float kExitLog = -27.7258872f;
 
-// BV: state rows of the workgroup (64, or 32 for a 32-row state): BV / 16 row waves.
+// BV: state rows of the workgroup: BV / 16 row waves.  Narrow (BV = 64, or 32 for a 32-row
+// state): 8 waves, waves 2 and 3 load the chunks, waves 4..7 prepare them.  Wide (BV = 128): 12
+// waves, every row wave loads an eighth of each chunk, waves 8..11 prepare them; the preparation of
+// a chunk (L, T, Pm, the gates) is shared by all 128 rows.
 // RAW: g and beta hold the raw gate inputs (a separate instantiation, so that the plain one carries
 // no trace of the gate transform).
+template <int BV>
+constexpr int kernel_threads() { return BV > BVMAX ? 768 : 512; }
+
 template <int DK, int BV, bool RAW>
-__global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
-    using S = Smem<DK>;
+__global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params<DK> p) {
+    using S = Smem<DK, BV>;
+    constexpr bool WIDE = S::WIDE;
+    constexpr int NT = kernel_threads<BV>(), PW0 = NT / 64 - 4;
     extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
     const int tid = threadIdx.x;
     const int wid = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64;
     const int g = lane / 16, l16 = lane % 16;
-    // waves 0 .. BV/16 - 1 own state rows; waves 2 and 3 also load the chunks
-    const bool is_row = wid < BV / 16, is_load = wid == 2 || wid == 3, is_prep = wid >= 4;
-    const int pw = wid - 4;  // prep wave index
+    const bool is_row = wid < BV / 16, is_load = !WIDE && (wid == 2 || wid == 3), is_prep = wid >= PW0;
+    const int pw = wid - PW0;  // prep wave index
 
     // XCD-aware order: the grp * nv workgroups that read one (segment, query/key head) -- its
     // value heads times their row blocks -- share blockIdx mod 8 (same XCD, same L2) when the
@@ -1114,36 +1156,51 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
     auto clen = [&](int c) { return (int)min((long)C, eos - (bos + (long)c * C)); };
 
     // T^T blocks above the diagonal blocks and Pm tiles above the diagonal are read as zeros but
-    // never written: clear both once.  Zero values: clear V in every raw buffer.
-    for (int i = tid; i < C * TSTR; i += 512) {
+    // never written: clear both once.  Zero values: clear V in every buffer that holds it.
+    for (int i = tid; i < C * TSTR; i += NT) {
         reinterpret_cast<__bf16*>(sm + S::T)[i] = (__bf16)0.f;
         reinterpret_cast<__bf16*>(sm + S::PM)[i] = (__bf16)0.f;
     }
     if (p.v_zero) {
-        for (int i = tid; i < C * BV; i += 512)
+        for (int i = tid; i < C * BV; i += NT)
 #pragma unroll
-            for (int r = 0; r < 3; ++r) reinterpret_cast<__bf16*>(sm + S::raw(r) + S::rV)[i] = (__bf16)0.f;
+            for (int r = 0; r < (WIDE ? 2 : 3); ++r) reinterpret_cast<__bf16*>(sm + S::qv(r) + S::rV)[i] = (__bf16)0.f;
     }
 
     const unsigned smb = lds_base(sm);
-    const bool conv = p.conv_w != nullptr;
+    const bool conv = !WIDE && p.conv_w != nullptr;  // wide workgroups take convolved inputs
     ConvW<DK, BV> cw;
-    if (conv) {
-        conv_weights<DK, BV>(cw, p, tid, h, hk, vb);
-        const int from = seg > 0 ? (nchunks > 0 ? HALO_TOKENS : HALO_ZERO) : (p.conv_state ? HALO_STATE : HALO_ZERO);
-        conv_halo_init<DK, BV>(p, smb + S::HB, tid, n, h, hk, vb, bos, from);
+    if constexpr (!WIDE) {
+        if (conv) {
+            conv_weights<DK, BV>(cw, p, tid, h, hk, vb);
+            const int from = seg > 0 ? (nchunks > 0 ? HALO_TOKENS : HALO_ZERO) : (p.conv_state ? HALO_STATE : HALO_ZERO);
+            conv_halo_init<DK, BV>(p, smb + S::HB, tid, n, h, hk, vb, bos, from);
+        }
     }
+    // chunk 0 (wide: its K, g and beta; Q and V come with the first iteration's loads)
     if (nchunks > 0 && is_prep) {
-        dma_chunk<DK, BV>(p, smb, S::raw(0), bos, clen(0), h, hk, vb, pw, lane);
-        wait_loads();
-        if constexpr (RAW) raw_gates<DK>(p, sm + S::raw(0), clen(0), pw, lane, h);
-        zero_tail<DK, BV>(sm + S::raw(0), clen(0), pw, lane);
+        if constexpr (WIDE) {
+            dma_k<DK, 16>(p, smb + S::raw(0) + S::rK, bos, clen(0), hk, 16 * pw, lane);
+            if (pw < 2) dma_gates_in<DK>(p, smb + S::raw(0) + (pw == 0 ? S::rG : S::rB), bos, clen(0), h, pw, lane);
+            wait_loads();
+            if constexpr (RAW) raw_gates<DK, BV>(p, sm + S::raw(0), clen(0), pw, lane, h);
+            if (clen(0) < C) {
+                zero_rows<DK, 16>(reinterpret_cast<__bf16*>(sm + S::raw(0) + S::rK), clen(0), 16 * pw, opaque(lane));
+                if (pw < 2 && lane >= clen(0)) reinterpret_cast<float*>(sm + S::raw(0) + (pw == 0 ? S::rG : S::rB))[lane] = 0.f;
+            }
+        } else {
+            dma_chunk<DK, BV>(p, smb, S::raw(0), bos, clen(0), h, hk, vb, pw, lane);
+            wait_loads();
+            if constexpr (RAW) raw_gates<DK, BV>(p, sm + S::raw(0), clen(0), pw, lane, h);
+            zero_tail<DK, BV>(sm + S::raw(0), clen(0), pw, lane);
+        }
     }
     lds_barrier();
-    if (conv && nchunks > 0) conv_chunk<DK, BV>(p, cw, smb + S::raw(0), smb + S::HB, clen(0), tid);
+    if constexpr (!WIDE)
+        if (conv && nchunks > 0) conv_chunk<DK, BV>(p, cw, smb + S::raw(0), smb + S::HB, clen(0), tid);
 
-    // Iteration k: state and output on chunk k, Pm of chunk k, L and T of chunk k+1, loads of k+2.
-    // The row/load waves and the prep waves run separate copies of the loop with the same barrier
+    // Iteration k: state and output on chunk k, Pm of chunk k, L and T of chunk k+1, loads of k+2
+    // (wide: K, g, beta of k+2 and Q, V of k+1).  The row/load waves and the prep waves run separate copies of the loop with the same barrier
     // sequence, so that each role's registers are allocated for its own code only.  Every wave
     // reads the same transition bounds in the same order, so an early exit is uniform.
     float decay = 0.f;  // log bound of the transition over the chunks the state has passed
@@ -1176,39 +1233,75 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
         }
         int stopped = 0;
         for (int k = -1; k < nchunks; ++k) {
-            const bool cur = k >= 0, far = k + 2 < nchunks;
+            const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
             const long tk = bos + (long)k * C;
             // ---- A
-            if (cur && is_row) row_A<DK, BV>(st, sm, sm + S::raw(k), sm + S::gates(k), wid, lane);
-            // the loads of chunk k+2 from waves 2 and 3 (rows 32 (w - 2) .. + 31), after their row
-            // work: waves 0 and 1 share their SIMDs with the solve of the next sub-stage and wait for
-            // nothing.  The buffer held chunk k-1, whose last reads were before the previous barrier.
-            if (far && is_load) {
+            if (cur && is_row) row_A<DK, BV>(st, sm, sm + S::raw(k), sm + S::qv(k), sm + S::gates(k), wid, lane);
+            if constexpr (WIDE) {
+                // rows [8w, 8w + 8) of K of chunk k+2 (with g, beta: waves 0, 1) and of Q, V of chunk
+                // k+1.  K's buffer held chunk k-1 (last read in the previous sub-stage B), the Q/V
+                // buffer chunk k-1 (last read in the previous sub-stage A).
+                if (far) {
+                    dma_k<DK, 8>(p, smb + S::raw(k + 2) + S::rK, tk + 2 * C, clen(k + 2), hk, 8 * wid, lane);
+                    if (wid < 2)
+                        dma_gates_in<DK>(p, smb + S::raw(k + 2) + (wid == 0 ? S::rG : S::rB), tk + 2 * C, clen(k + 2), h,
+                                         wid, lane);
+                }
+                if (nxt) {
+                    dma_q<DK, 8>(p, smb + S::qv(k + 1) + S::rQ, tk + C, clen(k + 1), hk, 8 * wid, lane);
+                    if (!p.v_zero) dma_v<DK, BV, 8>(p, smb + S::qv(k + 1) + S::rV, tk + C, clen(k + 1), h, vb, 8 * wid, lane);
+                }
+            } else if (far && is_load) {
+                // the loads of chunk k+2 from waves 2 and 3 (rows 32 (w - 2) .. + 31), after their row
+                // work: waves 0 and 1 share their SIMDs with the solve of the next sub-stage and wait
+                // for nothing.  The buffer held chunk k-1, whose last reads were before the previous
+                // barrier.
                 dma_chunk<DK, BV>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2), lane);
                 dma_chunk<DK, BV>(p, smb, S::raw(k + 2), tk + 2 * C, clen(k + 2), h, hk, vb, 2 * (wid - 2) + 1, lane);
             }
             lds_barrier();
             // ---- B
             if (cur) {
-                if (is_row) row_B<DK, BV>(p, st, sm, sm + S::raw(k), sm + S::gates(k), wid, lane, tk, clen(k), h, vb);
+                if (is_row) row_B<DK, BV>(st, sm, sm + S::raw(k), sm + S::gates(k), lane);
                 bound(k);
             }
-            if (far && is_load) {
+            if constexpr (WIDE) {
+                if (far || nxt) {
+                    wait_loads();
+                    if (far) {
+                        if (RAW && wid < 2) raw_gates<DK, BV>(p, sm + S::raw(k + 2), clen(k + 2), wid, lane, h);
+                        if (clen(k + 2) < C) {
+                            zero_rows<DK, 8>(reinterpret_cast<__bf16*>(sm + S::raw(k + 2) + S::rK), clen(k + 2), 8 * wid,
+                                             opaque(lane));
+                            if (wid < 2 && lane >= clen(k + 2))
+                                reinterpret_cast<float*>(sm + S::raw(k + 2) + (wid == 0 ? S::rG : S::rB))[lane] = 0.f;
+                        }
+                    }
+                    if (nxt && clen(k + 1) < C) {
+                        zero_rows<DK, 8>(reinterpret_cast<__bf16*>(sm + S::qv(k + 1) + S::rQ), clen(k + 1), 8 * wid,
+                                         opaque(lane));
+                        zero_rows<BV, 8>(reinterpret_cast<__bf16*>(sm + S::qv(k + 1) + S::rV), clen(k + 1), 8 * wid,
+                                         opaque(lane));
+                    }
+                }
+            } else if (far && is_load) {
                 wait_loads();
                 if (RAW && wid == 2) {
-                    raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 0, lane, h);
-                    raw_gates<DK>(p, sm + S::raw(k + 2), clen(k + 2), 1, lane, h);
+                    raw_gates<DK, BV>(p, sm + S::raw(k + 2), clen(k + 2), 0, lane, h);
+                    raw_gates<DK, BV>(p, sm + S::raw(k + 2), clen(k + 2), 1, lane, h);
                 }
                 zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2), lane);
                 zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2) + 1, lane);
             }
+            if (cur && is_row) row_store<DK, BV>(p, st, wid, lane, tk, clen(k), h, vb);
             lds_barrier();
             if (p.early_exit && decay <= kExitLog) {
                 stopped = 1;
                 break;
             }
             // ---- C (conv only): the prologue on chunk k+2, whose loads have all landed
-            if (conv && far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
+            if constexpr (!WIDE)
+                if (conv && far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
         }
         if (is_row && p.sfin) {
             const size_t srow0 = ((size_t)pair * p.dv + row) * DK;
@@ -1225,11 +1318,11 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
             // ---- A
             if (cur) {
                 unsigned char* rawk = sm + S::raw(k);
-                if (pw == 1) prep_P<DK, 0>(rawk, sm, lane, clen(k), p.l2norm);
-                if (pw == 2) prep_P<DK, 1>(rawk, sm, lane, clen(k), p.l2norm);
+                if (pw == 1) prep_P<DK, BV, 0>(rawk, sm + S::qv(k), sm, lane, clen(k), p.l2norm);
+                if (pw == 2) prep_P<DK, BV, 1>(rawk, sm + S::qv(k), sm, lane, clen(k), p.l2norm);
             }
-            if (nxt && pw == 0) prep_L<DK, 0>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
-            if (nxt && pw == 3) prep_L<DK, 1>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
+            if (nxt && pw == 0) prep_L<DK, BV, 0>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
+            if (nxt && pw == 3) prep_L<DK, BV, 1>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
             lds_barrier();
             // ---- B
             if (cur) bound(k);
@@ -1248,10 +1341,11 @@ __global__ __launch_bounds__(512) void chunk_bf16_kernel(Params<DK> p) {
                 copy_LBA(reinterpret_cast<const __bf16*>(sm + S::L), reinterpret_cast<__bf16*>(sm + S::T),
                          reinterpret_cast<const float*>(sm + S::WL),
                          reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB), lane);
-            if (nxt && pw == 3) make_gates<DK>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
+            if (nxt && pw == 3) make_gates<DK, BV>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
             lds_barrier();
             if (p.early_exit && decay <= kExitLog) break;
-            if (conv && far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
+            if constexpr (!WIDE)
+                if (conv && far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
         }
     }
 }
@@ -1296,7 +1390,7 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     p.negl_mode = c.negl_mode;
     p.scale = a.scale;
     p.l2norm = a.l2norm;
-    const int smem = Smem<DK>::bytes;
+    const int smem = Smem<DK, BV>::bytes;
     int dev = 0, lds_max = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
@@ -1307,16 +1401,20 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     const int grid = a.N * c.P * a.H * p.nv;
+    constexpr int nt = kernel_threads<BV>();
     if (a.gate_params)
-        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, true>), dim3(grid), dim3(512), smem, a.stream, p);
+        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, true>), dim3(grid), dim3(nt), smem, a.stream, p);
     else
-        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, false>), dim3(grid), dim3(512), smem, a.stream, p);
+        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, false>), dim3(grid), dim3(nt), smem, a.stream, p);
     return hipGetLastError();
 }
 
-// 64 state rows per workgroup, or 32 when the pass has a 32-row state
+// 128 state rows per workgroup where chunk_rows_per_workgroup allows, else 64, or 32 when the
+// pass has a 32-row state
 template <int DK>
 hipError_t launch_rows(const ChunkArgs& a, const Pass& c) {
+    if constexpr (DK == 128)
+        if (chunk_rows_per_workgroup(DK, c.rows, a.conv_w != nullptr) == BVW) return launch_t<DK, BVW>(a, c);
     return c.rows >= 64 ? launch_t<DK, 64>(a, c) : launch_t<DK, 32>(a, c);
 }
 
@@ -1349,6 +1447,11 @@ hipError_t run(const ChunkArgs& a, int P) {
 }
 
 }  // namespace
+
+int chunk_rows_per_workgroup(int dk, int rows, bool in_kernel_conv) {
+    if (dk == 128 && rows % BVW == 0 && !in_kernel_conv) return BVW;
+    return rows >= 64 ? 64 : 32;
+}
 
 hipError_t launch_chunk_bf16(const ChunkArgs& a) {
     switch (a.dk) {

@@ -120,15 +120,17 @@ def test_prefill_workload_full():
 
 # ------------------------------------------------------------------- segmented long sequences
 
+@pytest.mark.parametrize("dv", [64, 128])
 @pytest.mark.parametrize("segs", [2, 3, 5])
-def test_bf16_segments_forced(segs):
+def test_bf16_segments_forced(segs, dv):
     """Sequences cut into segments (the last one empty for segs=5); workload gates, so transitions
-    and corrections stop at the decay bound after a chunk or two."""
-    wl = W.make("seg", seed=40 + segs, N=2, T=1000, H=3, dk=128, dv=64, dtype="bf16", s0_std=0.02)
+    and corrections stop at the decay bound after a chunk or two.  dv = 64: 64-row workgroups;
+    dv = 128: 128-row workgroups in every pass."""
+    wl = W.make("seg", seed=40 + segs + dv, N=2, T=1000, H=3, dk=128, dv=dv, dtype="bf16", s0_std=0.02)
     o, s = TL.run_gpu(wl, segments=segs)
     o_ref, s_ref = TL.run_oracle(wl)
     e = TL.compare(wl, o, s, o_ref, s_ref)
-    _flush("segments %d %s" % (segs, e))
+    _flush("segments %d dv=%d %s" % (segs, dv, e))
 
 
 def test_bf16_segments_slow_decay_mixed():
@@ -142,7 +144,7 @@ def test_bf16_segments_slow_decay_mixed():
     _flush("segments slow %s" % e)
 
 
-@pytest.mark.parametrize("dk,dv", [(64, 128), (32, 32)])
+@pytest.mark.parametrize("dk,dv", [(64, 128), (32, 32), (128, 128)])
 def test_bf16_segments_varlen(dk, dv):
     wl = W.make("seg_var", seed=48 + dk, lengths=[300, 0, 64, 1, 700], H=2, dk=dk, dv=dv, dtype="bf16",
                 s0_std=0.05, varlen=True)
