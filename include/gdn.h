@@ -87,7 +87,8 @@ extern "C" {
  * "Long sequences" under gdn_chunk_fwd.  Not accepted by gdn_recurrent_step. */
 #define GDN_SEGMENTS(n) ((((unsigned)(n)) & 0xFFu) << 8)
 /* bf16 prefill with conv_w: run the conv prologue inside the chunk kernel instead of as a separate
- * pass into the workspace (see "Workspace" under gdn_chunk_fwd).  No effect otherwise. */
+ * pass into the workspace (see "Workspace" under gdn_chunk_fwd).  For dk = 128 with dv a multiple
+ * of 128 the conv always runs inside the chunk kernel.  No effect otherwise. */
 #define GDN_CONV_FUSED (1u << 16)
 
 /*
@@ -128,8 +129,9 @@ extern "C" {
  *  final_state [N, H, dv, dk] fp32     last state per (sequence, head), or NULL = not written.
  *                                      May alias initial_state exactly (same pointer).
  *  workspace, workspace_bytes          device scratch: the long-sequence path (below) and, for a
- *                                      bf16 call with conv_w (unless GDN_CONV_FUSED), the convolved
- *                                      q, k, v (T_tot * (2*Hk*dk + H*dv) bf16): the conv prologue then
+ *                                      bf16 call with conv_w (unless GDN_CONV_FUSED, or dk = 128
+ *                                      with dv a multiple of 128), the convolved q, k, v
+ *                                      (T_tot * (2*Hk*dk + H*dv) bf16): the conv prologue then
  *                                      runs as one streaming pass before the chunk kernel.  If
  *                                      *workspace_bytes is smaller than the size this call needs,
  *                                      the call sets *workspace_bytes to that size and returns

@@ -34,22 +34,25 @@ int check_common(int H, int dk, int dv, int dtype, float scale, unsigned flags) 
 
 // Segments per sequence for this call (1 = single pass).  A request for more than one segment is
 // honoured on the bf16 path only.
-int segments_for(int N, int T_tot, int H, int dk, int dv, int dtype, bool has_conv, unsigned flags, int* P) {
+int segments_for(int N, int T_tot, int H, int dk, int dv, int dtype, unsigned flags, int* P) {
     const int req = (int)((flags & kSegMask) >> 8);
     if (dtype != GDN_BF16) {
         if (req > 1) return GDN_ERR_UNSUPPORTED;
         *P = 1;
         return GDN_OK;
     }
-    *P = gdn::plan_segments(N, T_tot, H, dk, dv, has_conv && (flags & kConvFused), req);
+    *P = gdn::plan_segments(N, T_tot, H, dk, dv, req);
     return GDN_OK;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Segment buffers first (the long-sequence path), then the convolved q, k, v of the conv pass.
-bool conv_pass(bool has_conv, int dtype, unsigned flags) {
-    return has_conv && dtype == GDN_BF16 && !(flags & kConvFused);
+// The bf16 path convolves inside the chunk kernel where its 128-row workgroups run (d_k = 128, d_v
+// a multiple of 128) or when GDN_CONV_FUSED asks for it; otherwise a separate streaming pass writes
+// the convolved inputs to the workspace first.
+bool conv_pass(bool has_conv, int dtype, unsigned flags, int dk, int dv) {
+    return has_conv && dtype == GDN_BF16 && !(flags & kConvFused) && gdn::chunk_rows_per_workgroup(dk, dv) != 128;
 }
 size_t seg_bytes(int N, int H, int dk, int dv, int P) { return P > 1 ? align256(gdn::seg_layout(N, H, dk, dv, P).bytes) : 0; }
 size_t workspace_for(int N, int T_tot, int H, int Hk, int dk, int dv, int P, bool conv) {
@@ -81,9 +84,9 @@ int gdn_chunk_workspace_size(int N, int T_tot, int H, int Hk, int dk, int dv, in
     if (chunk != 64) return GDN_ERR_UNSUPPORTED;
     if (!has_cu_seqlens && T_tot % N != 0) return GDN_ERR_INVALID_ARG;
     int P = 1;
-    st = segments_for(N, T_tot, H, dk, dv, dtype, has_conv != 0, flags, &P);
+    st = segments_for(N, T_tot, H, dk, dv, dtype, flags, &P);
     if (st != GDN_OK) return st;
-    *bytes = workspace_for(N, T_tot, H, Hk, dk, dv, P, conv_pass(has_conv != 0, dtype, flags));
+    *bytes = workspace_for(N, T_tot, H, Hk, dk, dv, P, conv_pass(has_conv != 0, dtype, flags, dk, dv));
     return GDN_OK;
 }
 
@@ -141,9 +144,9 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
         return GDN_ERR_INVALID_ARG;
 
     int P = 1;
-    st = segments_for(N, T_tot, H, dk, dv, dtype, conv_w != nullptr, flags, &P);
+    st = segments_for(N, T_tot, H, dk, dv, dtype, flags, &P);
     if (st != GDN_OK) return st;
-    const bool cpass = conv_pass(conv_w != nullptr, dtype, flags);
+    const bool cpass = conv_pass(conv_w != nullptr, dtype, flags, dk, dv);
     const size_t need = workspace_for(N, T_tot, H, Hk, dk, dv, P, cpass);
     if (need > 0) {
         if (!workspace_bytes) return GDN_ERR_INVALID_ARG;

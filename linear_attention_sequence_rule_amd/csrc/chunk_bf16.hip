@@ -59,7 +59,10 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int C = 64;        // chunk length
 constexpr int BVMAX = 64;    // state rows of a narrow workgroup: 64, or 32 when the state has 32 rows
-constexpr int BVW = 128;     // state rows of a wide workgroup (d_k = 128, no in-kernel conv)
+constexpr int BVW = 128;     // state rows of a wide workgroup (d_k = 128)
+// Threads of a workgroup: 8 waves (narrow), 12 (wide).
+template <int BV>
+constexpr int kernel_threads() { return BV > BVMAX ? 768 : 512; }
 constexpr int TSTR = C + 8;  // bf16 row stride of T^T, Pm and L^T
 
 __device__ __forceinline__ fx4 mfma(bf16x8 a, bf16x8 b, fx4 c) {
@@ -215,8 +218,8 @@ struct Smem {
     static constexpr int ORQ = L + C * TSTR * 2;     // rq [C]
     static constexpr int WL = ORQ + C * 4;           // L-prep scratch, per wave: rk, gamma log2e [2][2][C]
     static constexpr int WP = WL + 4 * C * 4;        // P-prep scratch, per wave: rq, gamma log2e [2][2][C]
-    static constexpr int HB = WP + 4 * C * 4;        // conv halo (narrow): 3 raw rows [3][DK + BV/2] channel pairs
-    static constexpr int bytes = HB + (WIDE ? 0 : 3 * (DK + BVMAX / 2) * 4);
+    static constexpr int HB = WP + 4 * C * 4;        // conv halo: 3 raw rows [3][DK + BV/2] channel pairs
+    static constexpr int bytes = HB + 3 * (DK + (WIDE ? BV : BVMAX) / 2) * 4;
     static_assert(rBytes % 16 == 0 && gBytes % 16 == 0 && qvBytes % 16 == 0, "alignment");
     static_assert(bytes <= 160 * 1024, "LDS of one gfx950 compute unit");
     static __device__ __forceinline__ int raw(int c) { return R0 + (c % 3) * rBytes; }  // K, g, beta (narrow: all)
@@ -414,7 +417,7 @@ __device__ __forceinline__ void lds_barrier() {
 // conv over 4 tokens (tap 3 = current token; before the sequence start the given conv history, else
 // zeros) and SiLU on every q, k and v channel, in place in the chunk's LDS tiles once all of its
 // loads have landed.
-// Work item = (channel pair, block of 8 rows), taken in turn by all 512 lanes.  An item first
+// Work item = (channel pair, block of 8 rows), taken in turn by all lanes.  An item first
 // reads its 8 raw rows and the 3 raw rows before them (from the tile, or for the first block from
 // the halo buffer that keeps the previous chunk's last 3 raw rows); after a barrier -- no raw row
 // is overwritten before every item has read it -- it writes its results, and the items of the last
@@ -431,7 +434,8 @@ template <int DK, int BV>
 struct ConvPlan {
     static constexpr int NP = DK + BV / 2;              // channel pairs: K (DK/2), Q (DK/2), V (BV/2)
     static constexpr int ITEMS = NP * (C / 8);
-    static constexpr int PER = (ITEMS + 511) / 512;     // items per lane, at most
+    static constexpr int NT = kernel_threads<BV>();
+    static constexpr int PER = (ITEMS + NT - 1) / NT;   // items per lane, at most
 };
 
 // Where channel pair pc lives in a raw buffer: tile offset, row width W (bf16), its 16-byte slot
@@ -474,7 +478,7 @@ __device__ void conv_halo_init(const Params<DK>& p, unsigned halo, int tid, int 
                                int from) {
     constexpr int NP = ConvPlan<DK, BV>::NP;
     const size_t CC = (size_t)2 * p.Hk * DK + (size_t)p.H * p.dv;  // conv channels per token
-    for (int i = tid; i < 3 * NP; i += 512) {
+    for (int i = tid; i < 3 * NP; i += ConvPlan<DK, BV>::NT) {
         const int j = i / NP, pc = i % NP;
         uint32_t v = 0;
         const bool isv = pc >= DK, isq = !isv && pc >= DK / 2;
@@ -510,7 +514,7 @@ __device__ void conv_weights(ConvW<DK, BV>& cw, const Params<DK>& p, int tid, in
     using CP = ConvPlan<DK, BV>;
 #pragma unroll
     for (int q = 0; q < CP::PER; ++q) {
-        const int it = tid + 512 * q, pc = it % CP::NP;
+        const int it = tid + CP::NT * q, pc = it % CP::NP;
         const bool on = it < CP::ITEMS && !(pc >= DK && p.v_zero);
         const float* w = p.conv_w + (size_t)(on ? pair_wrow<DK, BV>(p, pc, h, hk, vb) : 0) * 4;
 #pragma unroll
@@ -519,9 +523,14 @@ __device__ void conv_weights(ConvW<DK, BV>& cw, const Params<DK>& p, int tid, in
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of this stays pending into the chunk loop
 }
 
-// The conv + SiLU of one chunk (raw: LDS byte address of its raw buffer); called by every lane.
+// The conv + SiLU of one chunk's tiles; called by every lane.  rawK / rawQV: LDS byte addresses of
+// the buffers holding the K tile and the Q, V tiles (the same buffer for narrow workgroups; wide
+// ones convolve K of one chunk and Q, V of the previous one in the same call), lenK / lenQV the
+// valid rows of each; parts: bit 0 the K channels, bit 1 the Q and V channels.  The halo keeps the
+// last three raw rows of each channel pair, so each part must be convolved in chunk order.
 template <int DK, int BV>
-__device__ void conv_chunk(const Params<DK>& p, const ConvW<DK, BV>& cw, unsigned raw, unsigned halo, int len, int tid) {
+__device__ void conv_chunk(const Params<DK>& p, const ConvW<DK, BV>& cw, unsigned rawK, int lenK, unsigned rawQV,
+                           int lenQV, unsigned halo, int parts, int tid) {
     tid = opaque(tid);
     using CP = ConvPlan<DK, BV>;
     constexpr int NP = CP::NP, PER = CP::PER;
@@ -529,10 +538,12 @@ __device__ void conv_chunk(const Params<DK>& p, const ConvW<DK, BV>& cw, unsigne
     bool act[PER];
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-        const int it = tid + 512 * q, pc = it % NP, rb = it / NP;
-        act[q] = it < CP::ITEMS && !(pc >= DK && p.v_zero);
+        const int it = tid + CP::NT * q, pc = it % NP, rb = it / NP;
+        const bool isk = pc < DK / 2;
+        act[q] = it < CP::ITEMS && !(pc >= DK && p.v_zero) && (parts & (isk ? 1 : 2));
         if (!act[q]) continue;
         const PairLoc l = pair_loc<DK, BV>(pc);
+        const unsigned raw = isk ? rawK : rawQV;
 #pragma unroll
         for (int j = 0; j < 3; ++j)
             xr[q][j] = ld32(rb == 0 ? halo + 4u * (j * NP + pc) : pair_addr(raw, l, 8 * rb - 3 + j));
@@ -544,8 +555,11 @@ __device__ void conv_chunk(const Params<DK>& p, const ConvW<DK, BV>& cw, unsigne
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         if (!act[q]) continue;
-        const int it = tid + 512 * q, pc = it % NP, rb = it / NP;
+        const int it = tid + CP::NT * q, pc = it % NP, rb = it / NP;
+        const bool isk = pc < DK / 2;
         const PairLoc l = pair_loc<DK, BV>(pc);
+        const unsigned raw = isk ? rawK : rawQV;
+        const int len = isk ? lenK : lenQV;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = 8 * rb + j;
@@ -1092,6 +1106,21 @@ __device__ __forceinline__ void row_store(const Params<DK>& p, const RowRegs<DK>
 }
 
 // ------------------------------------------------------------------------------------------
+// The conv after iteration k, once its loads have landed: narrow workgroups, chunk k+2; wide ones,
+// K of chunk k+2 and Q, V of chunk k+1.
+template <int DK, int BV>
+__device__ __forceinline__ void conv_after(const Params<DK>& p, const ConvW<DK, BV>& cw, unsigned smb, int k, int len1,
+                                           int len2, bool far, bool nxt, int tid) {
+    using S = Smem<DK, BV>;
+    if constexpr (S::WIDE) {
+        if (far || nxt)
+            conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), len2, smb + S::qv(k + 1), len1, smb + S::HB,
+                               (far ? 1 : 0) | (nxt ? 2 : 0), tid);
+    } else {
+        if (far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), len2, smb + S::raw(k + 2), len2, smb + S::HB, 3, tid);
+    }
+}
+
 // exp(-27.73) = 2^-40: below this bound on the state transition since the start, whatever the
 // state carried in, its remaining contribution is far under fp32 rounding.
 constexpr float kExitLog = -27.7258872f;
@@ -1102,9 +1131,6 @@ constexpr float kExitLog = -27.7258872f;
 // a chunk (L, T, Pm, the gates) is shared by all 128 rows.
 // RAW: g and beta hold the raw gate inputs (a separate instantiation, so that the plain one carries
 // no trace of the gate transform).
-template <int BV>
-constexpr int kernel_threads() { return BV > BVMAX ? 768 : 512; }
-
 template <int DK, int BV, bool RAW>
 __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params<DK> p) {
     using S = Smem<DK, BV>;
@@ -1168,14 +1194,12 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     }
 
     const unsigned smb = lds_base(sm);
-    const bool conv = !WIDE && p.conv_w != nullptr;  // wide workgroups take convolved inputs
+    const bool conv = p.conv_w != nullptr;
     ConvW<DK, BV> cw;
-    if constexpr (!WIDE) {
-        if (conv) {
-            conv_weights<DK, BV>(cw, p, tid, h, hk, vb);
-            const int from = seg > 0 ? (nchunks > 0 ? HALO_TOKENS : HALO_ZERO) : (p.conv_state ? HALO_STATE : HALO_ZERO);
-            conv_halo_init<DK, BV>(p, smb + S::HB, tid, n, h, hk, vb, bos, from);
-        }
+    if (conv) {
+        conv_weights<DK, BV>(cw, p, tid, h, hk, vb);
+        const int from = seg > 0 ? (nchunks > 0 ? HALO_TOKENS : HALO_ZERO) : (p.conv_state ? HALO_STATE : HALO_ZERO);
+        conv_halo_init<DK, BV>(p, smb + S::HB, tid, n, h, hk, vb, bos, from);
     }
     // chunk 0 (wide: its K, g and beta; Q and V come with the first iteration's loads)
     if (nchunks > 0 && is_prep) {
@@ -1196,8 +1220,9 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         }
     }
     lds_barrier();
-    if constexpr (!WIDE)
-        if (conv && nchunks > 0) conv_chunk<DK, BV>(p, cw, smb + S::raw(0), smb + S::HB, clen(0), tid);
+    // conv of chunk 0 (wide: its K; Q and V with the first iteration's conv)
+    if (conv && nchunks > 0)
+        conv_chunk<DK, BV>(p, cw, smb + S::raw(0), clen(0), smb + S::raw(0), clen(0), smb + S::HB, WIDE ? 1 : 3, tid);
 
     // Iteration k: state and output on chunk k, Pm of chunk k, L and T of chunk k+1, loads of k+2
     // (wide: K, g, beta of k+2 and Q, V of k+1).  The row/load waves and the prep waves run separate copies of the loop with the same barrier
@@ -1299,9 +1324,8 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 stopped = 1;
                 break;
             }
-            // ---- C (conv only): the prologue on chunk k+2, whose loads have all landed
-            if constexpr (!WIDE)
-                if (conv && far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
+            // ---- C (conv only): the prologue on the chunks whose loads landed in this iteration
+            if (conv) conv_after<DK, BV>(p, cw, smb, k, clen(k + 1), clen(k + 2), far, nxt, tid);
         }
         if (is_row && p.sfin) {
             const size_t srow0 = ((size_t)pair * p.dv + row) * DK;
@@ -1344,8 +1368,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             if (nxt && pw == 3) make_gates<DK, BV>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
             lds_barrier();
             if (p.early_exit && decay <= kExitLog) break;
-            if constexpr (!WIDE)
-                if (conv && far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), smb + S::HB, clen(k + 2), tid);
+            if (conv) conv_after<DK, BV>(p, cw, smb, k, clen(k + 1), clen(k + 2), far, nxt, tid);
         }
     }
 }
@@ -1414,7 +1437,7 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
 template <int DK>
 hipError_t launch_rows(const ChunkArgs& a, const Pass& c) {
     if constexpr (DK == 128)
-        if (chunk_rows_per_workgroup(DK, c.rows, a.conv_w != nullptr) == BVW) return launch_t<DK, BVW>(a, c);
+        if (chunk_rows_per_workgroup(DK, c.rows) == BVW) return launch_t<DK, BVW>(a, c);
     return c.rows >= 64 ? launch_t<DK, 64>(a, c) : launch_t<DK, 32>(a, c);
 }
 
@@ -1448,8 +1471,8 @@ hipError_t run(const ChunkArgs& a, int P) {
 
 }  // namespace
 
-int chunk_rows_per_workgroup(int dk, int rows, bool in_kernel_conv) {
-    if (dk == 128 && rows % BVW == 0 && !in_kernel_conv) return BVW;
+int chunk_rows_per_workgroup(int dk, int rows) {
+    if (dk == 128 && rows % BVW == 0) return BVW;
     return rows >= 64 ? 64 : 32;
 }
 

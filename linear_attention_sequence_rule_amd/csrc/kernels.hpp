@@ -57,14 +57,14 @@ struct SegLayout {
 };
 SegLayout seg_layout(int N, int H, int dk, int dv, int P);
 // State rows per workgroup of the bf16 chunk kernel for a pass with `rows` state rows:
-// 128 (wide workgroups) for d_k = 128, rows a multiple of 128 and no conv inside the kernel; else
-// 64, or 32 for a 32-row state.
-int chunk_rows_per_workgroup(int dk, int rows, bool in_kernel_conv);
+// 128 (wide workgroups) for d_k = 128 and rows a multiple of 128; else 64, or 32 for a 32-row
+// state.
+int chunk_rows_per_workgroup(int dk, int rows);
 // Segments per sequence for a bf16 call: `requested` if > 0, else enough to give every compute
 // unit of the current device a workgroup when (sequence, head, row block) units alone do not
 // (row blocks of chunk_rows_per_workgroup rows), and only for sequences of at least 16 chunks per
 // segment.
-int plan_segments(int N, int T_tot, int H, int dk, int dv, bool in_kernel_conv, int requested);
+int plan_segments(int N, int T_tot, int H, int dk, int dv, int requested);
 
 hipError_t launch_step(const StepArgs& a);
 hipError_t launch_chunk_f32(const ChunkArgs& a);

@@ -86,14 +86,14 @@ SegLayout seg_layout(int N, int H, int dk, int dv, int P) {
     return L;
 }
 
-int plan_segments(int N, int T_tot, int H, int dk, int dv, bool in_kernel_conv, int requested) {
+int plan_segments(int N, int T_tot, int H, int dk, int dv, int requested) {
     if (requested > 0) return requested;
     int cus = 256;  // MI355X; the current device's count when it can be read
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
         cus = v;
-    const int rows = chunk_rows_per_workgroup(dk, dv, in_kernel_conv);
+    const int rows = chunk_rows_per_workgroup(dk, dv);
     const long units = (long)N * H * (dv >= rows ? dv / rows : 1);  // workgroups of one pass
     if (units >= cus) return 1;
     const long chunks = ((long)T_tot / N + 63) / 64;

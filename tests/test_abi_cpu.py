@@ -183,7 +183,8 @@ def test_python_binding_fails_loudly_without_library(monkeypatch):
 
 def test_workspace_conv_pass(lib):
     """A bf16 call with conv weights needs room for the convolved q, k and v (the conv pass), unless
-    the conv runs inside the chunk kernel (GDN_CONV_FUSED); the fp32 path never does."""
+    the conv runs inside the chunk kernel (GDN_CONV_FUSED, or dk = 128 with dv a multiple of 128);
+    the fp32 path never does."""
     n = ctypes.c_size_t(0)
     a256 = lambda x: (x + 255) // 256 * 256
     N, T, H, Hk, dk, dv = 2, 1000, 4, 2, 64, 32
@@ -196,6 +197,9 @@ def test_workspace_conv_pass(lib):
     assert lib.gdn_chunk_workspace_size(N, T, H, Hk, dk, dv, 0, 64, 1, 1, one_seg, ctypes.byref(n)) == 0
     assert n.value == 0
     assert lib.gdn_chunk_workspace_size(N, T, H, Hk, dk, dv, 1, 64, 1, 0, one_seg, ctypes.byref(n)) == 0
+    assert n.value == 0
+    # dk = dv = 128 (128-row workgroups): the conv runs inside the chunk kernel, no conv workspace
+    assert lib.gdn_chunk_workspace_size(64, 64 * 4096, 32, 32, 128, 128, 1, 64, 1, 1, one_seg, ctypes.byref(n)) == 0
     assert n.value == 0
     # a bf16 conv call without that workspace reports the size and launches nothing
     big = 1 << 32

@@ -74,10 +74,11 @@ def test_bf16_conv_varlen_small():
     _flush("bf16_conv %s" % e)
 
 
-@pytest.mark.parametrize("dk,dv", [(64, 32), (32, 128), (128, 64)])
+@pytest.mark.parametrize("dk,dv", [(64, 32), (32, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("fused", [False, True])
 def test_bf16_conv_dims(dk, dv, fused):
-    """The conv prologue as a separate pass (default) and inside the chunk kernel (GDN_CONV_FUSED)."""
+    """The conv prologue as a separate pass (default for 64/32-row workgroups) and inside the chunk
+    kernel (GDN_CONV_FUSED, and always for 128-row workgroups: dk = dv = 128)."""
     wl = W.make("bf16_conv", seed=300 + dk + dv, lengths=[200, 3, 64, 0, 131], H=3, dk=dk, dv=dv, dtype="bf16",
                 s0_std=0.05, conv=True, varlen=True)
     o, s = TL.run_gpu(wl, scale=0.8, conv_fused=fused)
@@ -86,17 +87,18 @@ def test_bf16_conv_dims(dk, dv, fused):
     _flush("bf16_conv %d %d fused=%s %s" % (dk, dv, fused, e))
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_bf16_conv_segments(fused):
+@pytest.mark.parametrize("dv,fused", [(64, False), (64, True), (128, False)])
+def test_bf16_conv_segments(dv, fused):
     """Conv prologue on the segmented path: segments that start inside a sequence take the three
-    previous raw tokens as conv history; one head decays slowly so the corrections run long."""
-    wl = W.make("conv_seg", seed=51, lengths=[700, 130, 1, 520], H=2, dk=128, dv=64, dtype="bf16", s0_std=0.02,
+    previous raw tokens as conv history; one head decays slowly so the corrections run long.
+    dv = 128: 128-row workgroups, conv inside the kernel in every pass."""
+    wl = W.make("conv_seg", seed=51 + dv, lengths=[700, 130, 1, 520], H=2, dk=128, dv=dv, dtype="bf16", s0_std=0.02,
                 conv=True, varlen=True)
     wl.g[:, 1] = -1e-3
     o, s = TL.run_gpu(wl, segments=3, conv_fused=fused)
     o_ref, s_ref = TL.run_oracle(wl)
     e = TL.compare(wl, o, s, o_ref, s_ref)
-    _flush("conv segments fused=%s %s" % (fused, e))
+    _flush("conv segments dv=%d fused=%s %s" % (dv, fused, e))
 
 
 def test_bf16_slow_decay():
