@@ -219,7 +219,8 @@ struct Smem {
     static constexpr int WL = ORQ + C * 4;           // L-prep scratch, per wave: rk, gamma log2e [2][2][C]
     static constexpr int WP = WL + 4 * C * 4;        // P-prep scratch, per wave: rq, gamma log2e [2][2][C]
     static constexpr int HB = WP + 4 * C * 4;        // conv halo: 3 raw rows [3][DK + BV/2] channel pairs
-    static constexpr int bytes = HB + 3 * (DK + (WIDE ? BV : BVMAX) / 2) * 4;
+    static constexpr int CW = HB + 3 * (DK + (WIDE ? BV : BVMAX) / 2) * 4;  // wide: conv weights [48][8][4] fp32
+    static constexpr int bytes = CW + (WIDE ? 48 * 8 * 16 : 0);
     static_assert(rBytes % 16 == 0 && gBytes % 16 == 0 && qvBytes % 16 == 0, "alignment");
     static_assert(bytes <= 160 * 1024, "LDS of one gfx950 compute unit");
     static __device__ __forceinline__ int raw(int c) { return R0 + (c % 3) * rBytes; }  // K, g, beta (narrow: all)
@@ -1106,16 +1107,94 @@ __device__ __forceinline__ void row_store(const Params<DK>& p, const RowRegs<DK>
 }
 
 // ------------------------------------------------------------------------------------------
+// Wide workgroups (dk = BV = 128: K, Q and V tiles of 16 slots of 16 bytes per row): the conv
+// weights live in LDS as [48 slots][8 channels][4 taps] (slots 0..15 the K channels, 16..31 Q,
+// 32..47 V), loaded once per workgroup.
+template <int DK, int BV>
+__device__ void conv_weights_wide(const Params<DK>& p, unsigned char* sm, int tid, int h, int hk, int vb) {
+    using S = Smem<DK, BV>;
+    static_assert(DK == 128 && BV == 128, "wide conv layout");
+    if (tid < 48 * 8) {
+        const int sl = tid / 8, tile = sl / 16, c = (sl % 16) * 8 + tid % 8;  // channel within its tile
+        const int row = tile == 0 ? (p.Hk + hk) * DK + c : (tile == 1 ? hk * DK + c : 2 * p.Hk * DK + h * p.dv + vb * BV + c);
+        const float4 w = *reinterpret_cast<const float4*>(p.conv_w + (size_t)row * 4);
+        *reinterpret_cast<float4*>(sm + S::CW + 16 * tid) = w;
+    }
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u128;
+__device__ __forceinline__ u32x4 ld128(unsigned a) { return *reinterpret_cast<lds_u128*>(static_cast<uintptr_t>(a)); }
+__device__ __forceinline__ void st128(unsigned a, u32x4 v) { *reinterpret_cast<lds_u128*>(static_cast<uintptr_t>(a)) = v; }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+// The conv + SiLU of one chunk's tiles in a wide workgroup (the same operation as conv_chunk).
+// Item = lane: 16-byte slot s = tid % 48 (8 channels of one tile) and rows 4 rb .. 4 rb + 3,
+// rb = tid / 48; it reads its 4 raw rows and the 3 before them (the halo for rb = 0), one 16-byte
+// read each, and after a barrier writes its 4 results; items of the last block keep their raw rows
+// 61..63 as the next chunk's halo ([3][48] slots of 16 bytes).
+template <int DK, int BV>
+__device__ void conv_chunk_wide(const Params<DK>& p, const unsigned char* sm, unsigned rawK, int lenK, unsigned rawQV,
+                                int lenQV, unsigned halo, int parts, int tid) {
+    using S = Smem<DK, BV>;
+    static_assert(DK == 128 && BV == 128 && kernel_threads<BV>() == 48 * 16, "one item per lane");
+    tid = opaque(tid);
+    const int sl = tid % 48, rb = tid / 48, tile = sl / 16, ts = sl % 16;
+    const bool act = (parts & (tile == 0 ? 1 : 2)) && !(tile == 2 && p.v_zero);
+    const unsigned base = tile == 0 ? rawK + S::rK : (tile == 1 ? rawQV + S::rQ : rawQV + S::rV);
+    const int len = tile == 0 ? lenK : lenQV;
+    auto at = [&](int r) { return base + 256u * r + 16u * (ts ^ (r & 15)); };  // swz<128>
+    u32x4 x[7];
+    if (act) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) x[j] = rb == 0 ? ld128(halo + 16u * (j * 48 + sl)) : ld128(at(4 * rb - 3 + j));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[3 + j] = ld128(at(4 * rb + j));
+    }
+    lds_barrier();  // every raw row has been read
+    if (act) {
+        float4 w[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) w[c] = *reinterpret_cast<const float4*>(sm + S::CW + 128 * sl + 16 * c);
+        float lo[7][4], hi[7][4];
+#pragma unroll
+        for (int j = 0; j < 7; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                lo[j][q] = bf_lo(x[j][q]);
+                hi[j][q] = bf_hi(x[j][q]);
+            }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 a = w[2 * q], b = w[2 * q + 1];
+                const float y0 = a.x * lo[r][q] + a.y * lo[r + 1][q] + a.z * lo[r + 2][q] + a.w * lo[r + 3][q];
+                const float y1 = b.x * hi[r][q] + b.y * hi[r + 1][q] + b.z * hi[r + 2][q] + b.w * hi[r + 3][q];
+                o[q] = pack_bf16(silu(y0), silu(y1));
+            }
+            if (4 * rb + r < len) st128(at(4 * rb + r), u32x4{o[0], o[1], o[2], o[3]});  // rows past the tail stay zero
+        }
+        if (rb == 15)
+#pragma unroll
+            for (int j = 0; j < 3; ++j) st128(halo + 16u * (j * 48 + sl), x[4 + j]);
+    }
+    lds_barrier();
+}
+
 // The conv after iteration k, once its loads have landed: narrow workgroups, chunk k+2; wide ones,
 // K of chunk k+2 and Q, V of chunk k+1.
 template <int DK, int BV>
-__device__ __forceinline__ void conv_after(const Params<DK>& p, const ConvW<DK, BV>& cw, unsigned smb, int k, int len1,
-                                           int len2, bool far, bool nxt, int tid) {
+__device__ __forceinline__ void conv_after(const Params<DK>& p, const ConvW<DK, BV>& cw, const unsigned char* sm,
+                                           unsigned smb, int k, int len1, int len2, bool far, bool nxt, int tid) {
     using S = Smem<DK, BV>;
     if constexpr (S::WIDE) {
         if (far || nxt)
-            conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), len2, smb + S::qv(k + 1), len1, smb + S::HB,
-                               (far ? 1 : 0) | (nxt ? 2 : 0), tid);
+            conv_chunk_wide<DK, BV>(p, sm, smb + S::raw(k + 2), len2, smb + S::qv(k + 1), len1, smb + S::HB,
+                                    (far ? 1 : 0) | (nxt ? 2 : 0), tid);
     } else {
         if (far) conv_chunk<DK, BV>(p, cw, smb + S::raw(k + 2), len2, smb + S::raw(k + 2), len2, smb + S::HB, 3, tid);
     }
@@ -1195,9 +1274,12 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
 
     const unsigned smb = lds_base(sm);
     const bool conv = p.conv_w != nullptr;
-    ConvW<DK, BV> cw;
+    ConvW<DK, BV> cw;  // narrow: the weights of the lane's items (wide: in LDS)
     if (conv) {
-        conv_weights<DK, BV>(cw, p, tid, h, hk, vb);
+        if constexpr (WIDE)
+            conv_weights_wide<DK, BV>(p, sm, tid, h, hk, vb);
+        else
+            conv_weights<DK, BV>(cw, p, tid, h, hk, vb);
         const int from = seg > 0 ? (nchunks > 0 ? HALO_TOKENS : HALO_ZERO) : (p.conv_state ? HALO_STATE : HALO_ZERO);
         conv_halo_init<DK, BV>(p, smb + S::HB, tid, n, h, hk, vb, bos, from);
     }
@@ -1221,8 +1303,12 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     }
     lds_barrier();
     // conv of chunk 0 (wide: its K; Q and V with the first iteration's conv)
-    if (conv && nchunks > 0)
-        conv_chunk<DK, BV>(p, cw, smb + S::raw(0), clen(0), smb + S::raw(0), clen(0), smb + S::HB, WIDE ? 1 : 3, tid);
+    if (conv && nchunks > 0) {
+        if constexpr (WIDE)
+            conv_chunk_wide<DK, BV>(p, sm, smb + S::raw(0), clen(0), smb + S::raw(0), clen(0), smb + S::HB, 1, tid);
+        else
+            conv_chunk<DK, BV>(p, cw, smb + S::raw(0), clen(0), smb + S::raw(0), clen(0), smb + S::HB, 3, tid);
+    }
 
     // Iteration k: state and output on chunk k, Pm of chunk k, L and T of chunk k+1, loads of k+2
     // (wide: K, g, beta of k+2 and Q, V of k+1).  The row/load waves and the prep waves run separate copies of the loop with the same barrier
@@ -1325,7 +1411,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 break;
             }
             // ---- C (conv only): the prologue on the chunks whose loads landed in this iteration
-            if (conv) conv_after<DK, BV>(p, cw, smb, k, clen(k + 1), clen(k + 2), far, nxt, tid);
+            if (conv) conv_after<DK, BV>(p, cw, sm, smb, k, clen(k + 1), clen(k + 2), far, nxt, tid);
         }
         if (is_row && p.sfin) {
             const size_t srow0 = ((size_t)pair * p.dv + row) * DK;
@@ -1368,7 +1454,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             if (nxt && pw == 3) make_gates<DK, BV>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
             lds_barrier();
             if (p.early_exit && decay <= kExitLog) break;
-            if (conv) conv_after<DK, BV>(p, cw, smb, k, clen(k + 1), clen(k + 2), far, nxt, tid);
+            if (conv) conv_after<DK, BV>(p, cw, sm, smb, k, clen(k + 1), clen(k + 2), far, nxt, tid);
         }
     }
 }
