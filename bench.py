@@ -75,8 +75,8 @@ def load_traffic(kernel_tag):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the long-sequence and varlen lines")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated through the timed loop")
@@ -114,6 +114,15 @@ def main():
         if x.dtype == np.uint16:
             return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    def settle(fn):
+        # untimed calls for at least 50 ms: the GPU idles while each workload is generated on the
+        # host, and its clocks need that long to come back up
+        t_w, n_w = time.perf_counter(), 0
+        while n_w < 2 or time.perf_counter() - t_w < 0.05:
+            fn()
+            torch.cuda.synchronize()
+            n_w += 1
 
     # ---------------------------------------------------------------- prefill (the step)
     wl = W.prefill()
@@ -154,9 +163,7 @@ def main():
     dw = W.decode()
     dq, dk_, dv_, dg, db, st = (to_dev(x) for x in (dw.q, dw.k, dw.v, dw.g, dw.beta, dw.state))
     od = torch.empty_like(dv_)
-    for _ in range(3):
-        gdn.gdn_recurrent_step(dq, dk_, dv_, dg, db, st, o=od, stream=stream)
-    torch.cuda.synchronize()
+    settle(lambda: gdn.gdn_recurrent_step(dq, dk_, dv_, dg, db, st, o=od, stream=stream))
     dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
     for a, b in dev_ev:
         a.record(stream)
@@ -169,8 +176,7 @@ def main():
 
     # ---------------------------------------------------------------- long sequence, varlen + conv
     def timed(fn, iters):
-        fn()
-        torch.cuda.synchronize()
+        settle(fn)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
         for a, b in ev:
             a.record(stream)
