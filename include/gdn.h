@@ -43,8 +43,9 @@
  * -- a zero-centred RMSNorm (page maplevalley.com.cn/news/1910399, section 3.2: the learnable scale
  * is stored as an offset from 1, initialised to zero; section 4.2 suggests an eps of 1e-3 in bf16)
  * followed by a sigmoid output gate (page "GDN融合门控注意力的动态资源分配机制，AI智能体调动实战演练",
- * section 2).  The decode step applies it inside its kernel; the prefill runs it as one more pass
- * over o after the rule (a head's output row is spread over several workgroups there).
+ * section 2).  The decode step applies it inside its kernel, and so does the bf16 prefill for
+ * dk = 128 with dv a multiple of 128 (one workgroup holds a head's whole output row); other
+ * prefill shapes run it as one more pass over o after the rule.
  *
  * Conventions shared by every entry point
  *  - All pointers are DEVICE pointers to contiguous, row-major memory, 16-byte aligned, except

@@ -204,7 +204,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
         e = a.bf16 ? gdn::launch_chunk_bf16(a) : gdn::launch_chunk_f32(a);
     }
     if (e == hipSuccess && conv_state) e = gdn::launch_conv_state_update(a);
-    if (e == hipSuccess && out_gate)
+    if (e == hipSuccess && out_gate && !gdn::chunk_fuses_epilogue(dk, dv, a.bf16))
         e = gdn::launch_gated_norm(o, a.out_gate, a.norm_weight, (long)T_tot * H, dv, a.norm_eps, a.bf16, a.stream);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

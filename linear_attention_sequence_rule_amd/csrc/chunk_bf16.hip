@@ -220,7 +220,9 @@ struct Smem {
     static constexpr int WP = WL + 4 * C * 4;        // P-prep scratch, per wave: rq, gamma log2e [2][2][C]
     static constexpr int HB = WP + 4 * C * 4;        // conv halo: 3 raw rows [3][DK + BV/2] channel pairs
     static constexpr int CW = HB + 3 * (DK + (WIDE ? BV : BVMAX) / 2) * 4;  // wide: conv weights [48][8][4] fp32
-    static constexpr int bytes = CW + (WIDE ? 48 * 8 * 16 : 0);
+    static constexpr int EP = CW + (WIDE ? 48 * 8 * 16 : 0);  // wide epilogue: row sums of o^2 [C][8 row waves]
+    static constexpr int NW = EP + (WIDE ? C * 8 * 4 : 0);    // wide epilogue: w of the block's rows [BV]
+    static constexpr int bytes = NW + (WIDE ? BV * 4 : 0);
     static_assert(rBytes % 16 == 0 && gBytes % 16 == 0 && qvBytes % 16 == 0, "alignment");
     static_assert(bytes <= 160 * 1024, "LDS of one gfx950 compute unit");
     static __device__ __forceinline__ int raw(int c) { return R0 + (c % 3) * rBytes; }  // K, g, beta (narrow: all)
@@ -242,6 +244,9 @@ struct Params {
     const __bf16* conv_state;  // [N, 3, 2 Hk DK + H dv]: conv history before each sequence; or null
     const int32_t* cu;
     __bf16* o;
+    const __bf16* out_gate;     // wide workgroups: z of the output epilogue [T_tot, H, dv], or null
+    const float* norm_weight;   // w of the output epilogue [dv] (with out_gate)
+    float norm_eps;
     float* sfin;   // end state per (segment, head): [N*P, H, dv, dk]
     int* negl;     // per (segment, head): 1 if the run stopped at the decay bound, else 0 (or null)
     int N, T_tot, H, dv, nv;
@@ -336,6 +341,14 @@ __device__ __forceinline__ void dma_v(const Params<DK>& p, unsigned tile, long t
                                       int lane) {
     const size_t tok0 = (size_t)t0 * p.H + h;
     dma_tile<BV, NR>(uniform_ptr(p.v + tok0 * p.dv + vb * BV), (unsigned)(p.H * p.dv) * 2u, tile, len, r0,
+                     (unsigned)opaque(lane));
+}
+
+template <int DK, int BV, int NR>
+__device__ __forceinline__ void dma_z(const Params<DK>& p, unsigned tile, long t0, int len, int h, int vb, int r0,
+                                      int lane) {
+    const size_t tok0 = (size_t)t0 * p.H + h;
+    dma_tile<BV, NR>(uniform_ptr(p.out_gate + tok0 * p.dv + vb * BV), (unsigned)(p.H * p.dv) * 2u, tile, len, r0,
                      (unsigned)opaque(lane));
 }
 
@@ -1185,6 +1198,62 @@ __device__ void conv_chunk_wide(const Params<DK>& p, const unsigned char* sm, un
     lds_barrier();
 }
 
+// ------------------------------------------------------------------------------------------
+// Output epilogue in a wide workgroup (page P2 section 4.2 reading: o <- o rsqrt(mean(o^2) + eps)
+// (1 + w) sigmoid(z) over the dv outputs of a (token, head); a wide workgroup holds all dv = BV of
+// them).  Sub-stage B: each row wave adds (scale o)^2 over its 16 rows for every token of the chunk
+// and leaves the sum in LDS, while two prep waves load the chunk's z tile into the chunk's Q tile
+// (read for the last time in sub-stage A); after the barrier (start of the next sub-stage A, or
+// after the loop) epi_store adds the eight sums of a token and stores the gated, normalised rows.
+// The Q tile of the next chunk, which shares the buffer parity with the one after it, is then
+// also loaded in sub-stage B, so no load lands in a z tile before every row wave has read it.
+template <int DK, int BV>
+__device__ __forceinline__ void epi_sums(const Params<DK>& p, const RowRegs<DK>& st, unsigned char* sm, int wave,
+                                         int lane) {
+    using S = Smem<DK, BV>;
+    lane = opaque(lane);
+    const int g = lane / 16, l16 = lane % 16;
+    float* ep = reinterpret_cast<float*>(sm + S::EP);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float o = p.scale * st.ot[it][e];
+            a += o * o;
+        }
+        a += __shfl_xor(a, 16);
+        a += __shfl_xor(a, 32);
+        if (g == 0) ep[(16 * it + l16) * 8 + wave] = a;
+    }
+}
+template <int DK, int BV>
+__device__ __forceinline__ void epi_store(const Params<DK>& p, const RowRegs<DK>& st, const unsigned char* sm, int wave,
+                                          int lane, long t0, int len, int h, int vb, const __bf16* zt) {
+    using S = Smem<DK, BV>;
+    lane = opaque(lane);
+    const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
+    const float* ep = reinterpret_cast<const float*>(sm + S::EP);
+    const fx4 w = *reinterpret_cast<const fx4*>(sm + S::NW + 4 * (cbase + 4 * g));
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int i = 16 * it + l16;
+        if (i < len) {
+            const fx4 a = *reinterpret_cast<const fx4*>(ep + 8 * i), b = *reinterpret_cast<const fx4*>(ep + 8 * i + 4);
+            const float ss = ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
+            const float rr = rsqrtf(ss * (1.f / BV) + p.norm_eps);
+            const bf16x4 z = *reinterpret_cast<const bf16x4*>(zt + swz<BV>(i, cbase + 4 * g));
+            bf16x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float zz = (float)z[e];
+                out[e] = (__bf16)(p.scale * st.ot[it][e] * rr * (1.f + w[e]) * __builtin_amdgcn_rcpf(1.f + __expf(-zz)));
+            }
+            *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
+        }
+    }
+}
+
 // The conv after iteration k, once its loads have landed: narrow workgroups, chunk k+2; wide ones,
 // K of chunk k+2 and Q, V of chunk k+1.
 template <int DK, int BV>
@@ -1210,10 +1279,11 @@ constexpr float kExitLog = -27.7258872f;
 // a chunk (L, T, Pm, the gates) is shared by all 128 rows.
 // RAW: g and beta hold the raw gate inputs (a separate instantiation, so that the plain one carries
 // no trace of the gate transform).
-template <int DK, int BV, bool RAW>
+template <int DK, int BV, bool RAW, bool EPI>
 __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params<DK> p) {
     using S = Smem<DK, BV>;
     constexpr bool WIDE = S::WIDE;
+    static_assert(!EPI || WIDE, "the fused output epilogue needs the whole row of a head");
     constexpr int NT = kernel_threads<BV>(), PW0 = NT / 64 - 4;
     extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
     const int tid = threadIdx.x;
@@ -1283,6 +1353,8 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         const int from = seg > 0 ? (nchunks > 0 ? HALO_TOKENS : HALO_ZERO) : (p.conv_state ? HALO_STATE : HALO_ZERO);
         conv_halo_init<DK, BV>(p, smb + S::HB, tid, n, h, hk, vb, bos, from);
     }
+    if constexpr (EPI)
+        if (tid < BV) reinterpret_cast<float*>(sm + S::NW)[tid] = p.norm_weight[vb * BV + tid];
     // chunk 0 (wide: its K, g and beta; Q and V come with the first iteration's loads)
     if (nchunks > 0 && is_prep) {
         if constexpr (WIDE) {
@@ -1343,10 +1415,17 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             }
         }
         int stopped = 0;
+        int pend = -1;  // epilogue: the chunk whose outputs st.ot holds, stored after the next barrier
         for (int k = -1; k < nchunks; ++k) {
             const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
             const long tk = bos + (long)k * C;
             // ---- A
+            if constexpr (EPI) {
+                if (pend >= 0)
+                    epi_store<DK, BV>(p, st, sm, wid, lane, bos + (long)pend * C, clen(pend), h, vb,
+                                      reinterpret_cast<const __bf16*>(sm + S::qv(pend) + S::rQ));
+                pend = -1;
+            }
             if (cur && is_row) row_A<DK, BV>(st, sm, sm + S::raw(k), sm + S::qv(k), sm + S::gates(k), wid, lane);
             if constexpr (WIDE) {
                 // rows [8w, 8w + 8) of K of chunk k+2 (with g, beta: waves 0, 1) and of Q, V of chunk
@@ -1359,7 +1438,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                                          wid, lane);
                 }
                 if (nxt) {
-                    dma_q<DK, 8>(p, smb + S::qv(k + 1) + S::rQ, tk + C, clen(k + 1), hk, 8 * wid, lane);
+                    if (!EPI) dma_q<DK, 8>(p, smb + S::qv(k + 1) + S::rQ, tk + C, clen(k + 1), hk, 8 * wid, lane);
                     if (!p.v_zero) dma_v<DK, BV, 8>(p, smb + S::qv(k + 1) + S::rV, tk + C, clen(k + 1), h, vb, 8 * wid, lane);
                 }
             } else if (far && is_load) {
@@ -1373,7 +1452,10 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             lds_barrier();
             // ---- B
             if (cur) {
-                if (is_row) row_B<DK, BV>(st, sm, sm + S::raw(k), sm + S::gates(k), lane);
+                if (is_row) {
+                    row_B<DK, BV>(st, sm, sm + S::raw(k), sm + S::gates(k), lane);
+                    if constexpr (EPI) epi_sums<DK, BV>(p, st, sm, wid, lane);
+                }
                 bound(k);
             }
             if constexpr (WIDE) {
@@ -1389,8 +1471,9 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                         }
                     }
                     if (nxt && clen(k + 1) < C) {
-                        zero_rows<DK, 8>(reinterpret_cast<__bf16*>(sm + S::qv(k + 1) + S::rQ), clen(k + 1), 8 * wid,
-                                         opaque(lane));
+                        if (!EPI)
+                            zero_rows<DK, 8>(reinterpret_cast<__bf16*>(sm + S::qv(k + 1) + S::rQ), clen(k + 1), 8 * wid,
+                                             opaque(lane));
                         zero_rows<BV, 8>(reinterpret_cast<__bf16*>(sm + S::qv(k + 1) + S::rV), clen(k + 1), 8 * wid,
                                          opaque(lane));
                     }
@@ -1404,7 +1487,12 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2), lane);
                 zero_tail<DK, BV>(sm + S::raw(k + 2), clen(k + 2), 2 * (wid - 2) + 1, lane);
             }
-            if (cur && is_row) row_store<DK, BV>(p, st, wid, lane, tk, clen(k), h, vb);
+            if (cur && is_row) {
+                if constexpr (EPI)
+                    pend = k;
+                else
+                    row_store<DK, BV>(p, st, wid, lane, tk, clen(k), h, vb);
+            }
             lds_barrier();
             if (p.early_exit && decay <= kExitLog) {
                 stopped = 1;
@@ -1413,6 +1501,10 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             // ---- C (conv only): the prologue on the chunks whose loads landed in this iteration
             if (conv) conv_after<DK, BV>(p, cw, sm, smb, k, clen(k + 1), clen(k + 2), far, nxt, tid);
         }
+        if constexpr (EPI)
+            if (pend >= 0)
+                epi_store<DK, BV>(p, st, sm, wid, lane, bos + (long)pend * C, clen(pend), h, vb,
+                                  reinterpret_cast<const __bf16*>(sm + S::qv(pend) + S::rQ));
         if (is_row && p.sfin) {
             const size_t srow0 = ((size_t)pair * p.dv + row) * DK;
 #pragma unroll
@@ -1425,6 +1517,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     } else {
         for (int k = -1; k < nchunks; ++k) {
             const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
+            const long tk = bos + (long)k * C;
             // ---- A
             if (cur) {
                 unsigned char* rawk = sm + S::raw(k);
@@ -1436,6 +1529,14 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             lds_barrier();
             // ---- B
             if (cur) bound(k);
+            if constexpr (EPI) {
+                // waves 10, 11: rows [32 (pw - 2), + 32) of z of chunk k (into its Q tile) and of Q of
+                // chunk k+1
+                if (pw >= 2) {
+                    if (cur) dma_z<DK, BV, 32>(p, smb + S::qv(k) + S::rQ, tk, clen(k), h, vb, 32 * (pw - 2), lane);
+                    if (nxt) dma_q<DK, 32>(p, smb + S::qv(k + 1) + S::rQ, tk + C, clen(k + 1), hk, 32 * (pw - 2), lane);
+                }
+            }
             if (nxt && (pw == 0 || pw == 1)) {
                 // the solve is this sub-stage's longest chain: its instructions go first on the SIMD
                 __builtin_amdgcn_s_setprio(3);
@@ -1452,11 +1553,33 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                          reinterpret_cast<const float*>(sm + S::WL),
                          reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB), lane);
             if (nxt && pw == 3) make_gates<DK, BV>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
+            if constexpr (EPI) {
+                if (pw >= 2 && (cur || nxt)) {
+                    wait_loads();
+                    if (nxt && clen(k + 1) < C)
+                        zero_rows<DK, 32>(reinterpret_cast<__bf16*>(sm + S::qv(k + 1) + S::rQ), clen(k + 1),
+                                          32 * (pw - 2), opaque(lane));
+                }
+            }
             lds_barrier();
             if (p.early_exit && decay <= kExitLog) break;
             if (conv) conv_after<DK, BV>(p, cw, sm, smb, k, clen(k + 1), clen(k + 2), far, nxt, tid);
         }
     }
+}
+
+template <int DK, int BV, bool EPI>
+hipError_t launch_k(const Params<DK>& p, const ChunkArgs& a, int grid, int smem) {
+    const void* fn = a.gate_params ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, true, EPI>)
+                                   : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, false, EPI>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    constexpr int nt = kernel_threads<BV>();
+    if (a.gate_params)
+        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, true, EPI>), dim3(grid), dim3(nt), smem, a.stream, p);
+    else
+        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, false, EPI>), dim3(grid), dim3(nt), smem, a.stream, p);
+    return hipGetLastError();
 }
 
 // One pass of the kernel.  rows = state rows (dv, or dk for the transition pass).
@@ -1499,23 +1622,23 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     p.negl_mode = c.negl_mode;
     p.scale = a.scale;
     p.l2norm = a.l2norm;
+    // the output epilogue in the kernel: wide workgroups of a pass that stores o
+    const bool epi = Smem<DK, BV>::WIDE && a.out_gate && c.out == OUT_STORE;
+    p.out_gate = static_cast<const __bf16*>(a.out_gate);
+    p.norm_weight = a.norm_weight;
+    p.norm_eps = a.norm_eps;
     const int smem = Smem<DK, BV>::bytes;
     int dev = 0, lds_max = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (e != hipSuccess) return e;
     if (lds_max < smem) return hipErrorInvalidConfiguration;  // needs the 160 KiB LDS of gfx950
-    const void* fn = a.gate_params ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, true>)
-                                   : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, false>);
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
     const int grid = a.N * c.P * a.H * p.nv;
-    constexpr int nt = kernel_threads<BV>();
-    if (a.gate_params)
-        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, true>), dim3(grid), dim3(nt), smem, a.stream, p);
-    else
-        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, false>), dim3(grid), dim3(nt), smem, a.stream, p);
-    return hipGetLastError();
+    if (epi) {
+        if constexpr (Smem<DK, BV>::WIDE) return launch_k<DK, BV, true>(p, a, grid, smem);
+        return hipErrorInvalidValue;
+    }
+    return launch_k<DK, BV, false>(p, a, grid, smem);
 }
 
 // 128 state rows per workgroup where chunk_rows_per_workgroup allows, else 64, or 32 when the
@@ -1561,6 +1684,8 @@ int chunk_rows_per_workgroup(int dk, int rows) {
     if (dk == 128 && rows % BVW == 0) return BVW;
     return rows >= 64 ? 64 : 32;
 }
+
+bool chunk_fuses_epilogue(int dk, int dv, bool bf16) { return bf16 && chunk_rows_per_workgroup(dk, dv) == BVW; }
 
 hipError_t launch_chunk_bf16(const ChunkArgs& a) {
     switch (a.dk) {

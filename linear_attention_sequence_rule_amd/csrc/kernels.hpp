@@ -60,6 +60,9 @@ SegLayout seg_layout(int N, int H, int dk, int dv, int P);
 // 128 (wide workgroups) for d_k = 128 and rows a multiple of 128; else 64, or 32 for a 32-row
 // state.
 int chunk_rows_per_workgroup(int dk, int rows);
+// Whether the chunk kernels apply the output epilogue themselves (bf16 with 128-row workgroups,
+// which hold a head's whole output row); otherwise it runs as a separate pass over o.
+bool chunk_fuses_epilogue(int dk, int dv, bool bf16);
 // Segments per sequence for a bf16 call: `requested` if > 0, else enough to give every compute
 // unit of the current device a workgroup when (sequence, head, row block) units alone do not
 // (row blocks of chunk_rows_per_workgroup rows), and only for sequences of at least 16 chunks per
