@@ -14,25 +14,25 @@
 // operands (exact); the norms come from the diagonals of K K^T and Q Q^T and are folded into the
 // row and column scalings above.  Every decay factor is exp of a non-positive number.
 //
-// Work decomposition: one workgroup of 8 wavefronts per (sequence n, head h, block of 32 state
-// rows); state rows are independent, so the split is exact.  Roles:
-//   waves 0, 1  state chain of 16 rows each, entirely in registers: K S^T, X, U, S update;
-//   waves 2, 3  output of the same 16 rows: S Q^T and Pm U, then the stores of o;
-//   waves 4..7  preparation: waves 4, 7 K K^T and the masked L of chunk k+1 (two row-tile halves,
-//               wave 4 also the norms); waves 5, 6 the masked Pm of chunk k (likewise);
-//               in the second sub-stage waves 4, 5 invert the two 32x32 diagonal blocks of I + L,
-//               wave 6 copies the off-diagonal block L_BA next to them and wave 7 writes the gates.
-//   The output waves also issue the direct global->LDS loads of chunk k+2 (after S Q^T) and wait
-//   for them after their stores.
+// Work decomposition: one workgroup per (segment of a sequence, head h, block of state rows); state
+// rows are independent, so the split is exact, and the per-chunk preparation (Grams, masks, solve,
+// gates) is shared by the rows of the block.  Wide workgroups (dk = 128, 128 rows = the whole head)
+// have 12 wavefronts, narrow ones (64 or 32 rows) 8.  Roles:
+//   row waves (0..7 wide, 0..3 narrow; 16 state rows each): S, the output accumulators and U in
+//     registers across the chunks.  Sub-stage A: K S^T and S Q^T, X, U = T X blockwise; sub-stage
+//     B: the S update and O.  Wide: every row wave also loads an eighth of the next chunks;
+//     narrow: waves 2 and 3 load them.
+//   prep waves (8..11 wide, 4..7 narrow; prep index pw = 0..3): sub-stage A: pw 0, 3 K K^T and the
+//     masked L of chunk k+1 (two row-tile halves, pw 0 also the norms); pw 1, 2 the masked Pm of
+//     chunk k (likewise).  Sub-stage B: pw 0, 1 invert the two 32x32 diagonal blocks of I + L,
+//     pw 2 copies the off-diagonal block L_BA next to them and pw 3 writes the gates of chunk k+1.
 // U = T X is applied blockwise, so T's off-diagonal 32x32 block is never formed:
 //   U_A = T_AA X_A,  U_B = T_BB (X_B - L_BA U_A).
-// Two barriers per chunk: sub-stage A (state: K S^T, X, U | output: S Q^T | prep: Gram products,
-// masks), sub-stage B (state: S update | output: O | prep: diagonal-block solves, load waits).
-// With the conv prologue a third sub-stage runs it on chunk k+2 once its loads have landed.
-// Hand-offs between waves go through LDS: U (state -> output, within a chunk) and S in bf16
-// (state -> output, for the next chunk).  Raw chunk inputs are triple buffered, the gates double
-// buffered, T, Pm, L and the hand-offs single buffered (each is rewritten only after the barrier
-// that ends its readers' sub-stage).
+// Two barriers per chunk; with the conv prologue a third sub-stage runs it on the chunks whose
+// loads have landed.  Narrow workgroups keep each chunk's K, Q, V, g, beta in one of three
+// buffers (loaded two chunks ahead); wide ones keep K, g, beta likewise but Q and V in two buffers
+// loaded one chunk ahead (read only in sub-stage A).  The gates are double buffered; T, Pm and L
+// single buffered (each is rewritten only after the barrier that ends its readers' sub-stage).
 // K, Q and V rows are stored unpadded with their 16-byte slots XOR-swizzled by the row index
 // (slot = part ^ (row mod parts-per-row)), which keeps every fragment read conflict-free and
 // lets a 1 KB load instruction fill whole rows.  Each 16x16 MFMA output tile is fed to the next
@@ -267,9 +267,9 @@ struct Params {
 // ------------------------------------------------------------------------------------------
 // chunk loads: direct global -> LDS (global_load_lds_dwordx4 / _dword).  One instruction moves
 // 1 KB (64 lanes x 16 B) into a contiguous LDS range; lane l fills 16-byte slot l of that range,
-// so each lane fetches the global part that the swizzle places in its slot.  Wave w loads rows
-// [16w, 16w + 16) of K, Q and V; wave 0 loads g, wave 1 beta.  Rows past the tail re-read the
-// last valid row and are cleared by zero_tail once the loads have landed.
+// so each lane fetches the global part that the swizzle places in its slot.  A wave loads a block
+// of rows of K, Q and V (and g or beta); rows past the tail re-read the last valid row and are
+// cleared once the loads have landed.
 // One global_load_lds instruction (scalar-base form): lane l copies 16 (or 4) bytes from
 // base + voff(l) to LDS byte address lds + 16 l (4 l).  base and lds are wave-uniform; voff is a
 // per-lane byte offset below 4 GiB (the base already points at the chunk's first token).  Issued
@@ -643,7 +643,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 //   S <- Gamma_C S + U'^T diag(exp(gamma_C - gamma)) K.
 // The masks need only the gates; f enters the solve as a row factor.
 
-// Waves 4 and 7 on chunk k+1: K K^T row tiles {0, 3} (part 0) or {1, 2} (part 1) masked with
+// Prep waves 0 and 3 on chunk k+1: K K^T row tiles {0, 3} (part 0) or {1, 2} (part 1) masked with
 // M (those rows of L^T: bf16, L^T[j][i] = M_ij G_ij for j < i); part 0 also leaves the norms rk of
 // every row (from the four diagonal tiles) and gamma log2e for the next sub-stage.
 // exp(gamma_i - gamma_j) = exp2 of a non-positive number.
@@ -719,7 +719,7 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
     }
 }
 
-// Wave 7, sub-stage B, on chunk k+1: the gates, from rk and gamma log2e left by part 0 of prep_L.
+// Prep wave 3, sub-stage B, on chunk k+1: the gates, from rk and gamma log2e left by part 0 of prep_L.
 template <int DK, int BV>
 __device__ __forceinline__ void make_gates(const unsigned char* raw, unsigned char* gb, const unsigned char* sm,
                                            int lane, int l2norm) {
@@ -758,7 +758,7 @@ __device__ __forceinline__ void row_factors(float (&f)[4 * N], const float* rk, 
     }
 }
 
-// Waves 5, 6 on chunk k: row tiles {0, 3} (half 0) or {1, 2} (half 1) of Pm' = lower(M o Q K^T)
+// Prep waves 1, 2 on chunk k: row tiles {0, 3} (half 0) or {1, 2} (half 1) of Pm' = lower(M o Q K^T)
 // of the raw rows, computed as D = K Q^T so that a lane holds 4 consecutive m of row i (bf16,
 // row-major), and rq of those rows (diagonal of Q Q^T).
 template <int DK, int BV, int half>
@@ -924,7 +924,7 @@ __device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, cons
     *reinterpret_cast<bf16x4*>(Tt + (c0 + l16) * TSTR + r0 + 4 * g) = out;
 }
 
-// Wave 6: L'_BA = diag(f) G_m (rows 32..63, columns 0..31) into the T_BA block of T^T, which the
+// Prep wave 2: L'_BA = diag(f) G_m (rows 32..63, columns 0..31) into the T_BA block of T^T, which the
 // state waves read in its place (U'_B = T'_BB (Y_B - L'_BA U'_A)).  Both are stored transposed.
 __device__ __forceinline__ void copy_LBA(const __bf16* sLt, __bf16* Tt, const float* rk, const float* beta, int lane) {
     lane = opaque(lane);
