@@ -443,6 +443,11 @@ __device__ __forceinline__ void st32(unsigned a, uint32_t v) { *reinterpret_cast
 __device__ __forceinline__ float silu(float x) {
     return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
 }
+typedef float fx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {  // one v_cvt_pk_bf16_f32
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(fx2{a, b}, bf16x2));
+}
 
 template <int DK, int BV>
 struct ConvPlan {
@@ -586,10 +591,8 @@ __device__ void conv_chunk(const Params<DK>& p, const ConvW<DK, BV>& cw, unsigne
             const float* a = cw.w[q];
             const float y0 = a[0] * lo[0] + a[1] * lo[1] + a[2] * lo[2] + a[3] * lo[3];
             const float y1 = a[4] * hi[0] + a[5] * hi[1] + a[6] * hi[2] + a[7] * hi[3];
-            const __bf16 o0 = (__bf16)silu(y0), o1 = (__bf16)silu(y1);
             if (r < len)  // rows past the tail stay zero
-                st32(pair_addr(raw, l, r),
-                     (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16));
+                st32(pair_addr(raw, l, r), pack_bf16(silu(y0), silu(y1)));
         }
         if (rb == C / 8 - 1)
 #pragma unroll
@@ -1140,9 +1143,6 @@ __device__ __forceinline__ u32x4 ld128(unsigned a) { return *reinterpret_cast<ld
 __device__ __forceinline__ void st128(unsigned a, u32x4 v) { *reinterpret_cast<lds_u128*>(static_cast<uintptr_t>(a)) = v; }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
-}
 // The conv + SiLU of one chunk's tiles in a wide workgroup (the same operation as conv_chunk).
 // Item = lane: 16-byte slot s = tid % 48 (8 channels of one tile) and rows 4 rb .. 4 rb + 3,
 // rb = tid / 48; it reads its 4 raw rows and the 3 before them (the halo for rb = 0), one 16-byte
