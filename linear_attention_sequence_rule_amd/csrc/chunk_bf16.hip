@@ -647,8 +647,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 // The masks need only the gates; f enters the solve as a row factor.
 
 // Prep waves 0 and 3 on chunk k+1: K K^T row tiles {0, 3} (part 0) or {1, 2} (part 1) masked with
-// M (those rows of L^T: bf16, L^T[j][i] = M_ij G_ij for j < i); part 0 also leaves the norms rk of
-// every row (from the four diagonal tiles) and gamma log2e for the next sub-stage.
+// M (those rows of L^T: bf16, L^T[j][i] = M_ij G_ij for j < i); each part also leaves the norms rk
+// of its rows (from its two diagonal tiles) and gamma log2e for the next sub-stage.
 // exp(gamma_i - gamma_j) = exp2 of a non-positive number.
 template <int DK, int BV, int part>
 __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* sm, int lane, int len, int l2norm) {
@@ -668,13 +668,11 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
     own[C + lane] = gam * kLog2e;
 
     // k-step outer: only one k-step of fragments is live at a time
-    constexpr int ot0 = part ? 0 : 1, ot1 = part ? 3 : 2;  // diagonal tiles of the other part's rows
-    fx4 acc[2][4], dg[2];
+    fx4 acc[2][4];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) acc[s2][jt] = zero4();
-        dg[s2] = zero4();
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -688,10 +686,6 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
                 if (jt <= it) acc[s2][jt] = mfma(kf[it], kf[jt], acc[s2][jt]);
-            if (part == 0) {  // part 0 computes the norms
-                const int od = s2 ? ot1 : ot0;
-                dg[s2] = mfma(kf[od], kf[od], dg[s2]);
-            }
         }
     }
     const float* g2 = own + C;
@@ -714,12 +708,11 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
             *reinterpret_cast<bf16x4*>(sLt + j * TSTR + i0) = out;
         }
     }
-    if (part == 0) {  // rk of every row, for the solve and the gates (next sub-stage)
-        write_norm(own, acc[0][t0], t0, lane, len, l2norm);
-        write_norm(own, acc[1][t1], t1, lane, len, l2norm);
-        write_norm(own, dg[0], ot0, lane, len, l2norm);
-        write_norm(own, dg[1], ot1, lane, len, l2norm);
-    }
+    // rk of this part's rows (from the diagonal tiles of its own Gram tiles), for the solve and
+    // the gates of the next sub-stage: both parts write part 0's rk array
+    float* rk = reinterpret_cast<float*>(sm + S::WL);
+    write_norm(rk, acc[0][t0], t0, lane, len, l2norm);
+    write_norm(rk, acc[1][t1], t1, lane, len, l2norm);
 }
 
 // Prep wave 3, sub-stage B, on chunk k+1: the gates, from rk and gamma log2e left by part 0 of prep_L.
