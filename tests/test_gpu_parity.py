@@ -255,3 +255,28 @@ def test_decode_then_prefill_consistency():
     assert (o_step.float() - o_full[last].float()).abs().max().item() <= TL.BF16_O_ABS
     rel = ((s_a - s_full).norm() / s_full.norm()).item()
     assert rel <= TL.BF16_S_RELF
+
+
+def test_side_stream_and_no_final_state():
+    """Both calls on a caller-provided stream (created at the default priority, waiting for the
+    uploads on the current stream); the 128-row segmented path without a final state."""
+    from linear_attention_sequence_rule_amd import gdn_chunk_fwd, gdn_recurrent_step
+    import torch
+    wl = W.make("side", seed=91, lengths=[700, 65, 3], H=2, dk=128, dv=128, dtype="bf16", s0_std=0.02, varlen=True)
+    q, k, v = TL.to_dev(wl.q), TL.to_dev(wl.k), TL.to_dev(wl.v)
+    g, beta, s0, cu = TL.to_dev(wl.g), TL.to_dev(wl.beta), TL.to_dev(wl.s0), TL.to_dev(wl.cu_seqlens)
+    dw = W.decode(N=4, H=2, seed=92)
+    dq, dk_, dv_, dg, db, st = (TL.to_dev(x) for x in (dw.q, dw.k, dw.v, dw.g, dw.beta, dw.state))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o, sf = gdn_chunk_fwd(q, k, v, g, beta, s0, cu, N=wl.N, segments=2, output_final_state=False, stream=side)
+        od = gdn_recurrent_step(dq, dk_, dv_, dg, db, st, stream=side)
+    side.synchronize()
+    assert sf is None
+    o_ref, _ = TL.run_oracle(wl)
+    TL.compare(wl, TL.o_to_f64(o), None, o_ref, None)
+    od_ref, st_ref = oracle.step(dw.as_float("q"), dw.as_float("k"), dw.as_float("v"), dw.g, dw.beta, dw.state)
+    assert np.abs(TL.o_to_f64(od) - od_ref).max() <= TL.BF16_O_ABS
+    d = np.linalg.norm((st.cpu().numpy().astype(np.float64) - st_ref).reshape(dw.N * dw.H, -1), axis=1)
+    assert (d / np.linalg.norm(st_ref.reshape(dw.N * dw.H, -1), axis=1)).max() <= TL.BF16_S_RELF
