@@ -1262,6 +1262,28 @@ __device__ __forceinline__ void conv_after(const Params<DK>& p, const ConvW<DK, 
     }
 }
 
+// The sequence of rank r when sequences are ordered by length, longest first (ties: lower index
+// first); called by every thread of the workgroup (it has barriers); N <= NT.  ws: N + 1 ints of LDS.
+template <int NT>
+__device__ int longest_first(const int32_t* cu, int N, int r, int tid, int* ws) {
+    // every barrier is reached once by every wave (none sits in lane-dependent control flow)
+    if (tid <= N) ws[tid] = cu[tid];
+    __syncthreads();
+    if (tid < N) {
+        const int lm = ws[tid + 1] - ws[tid];
+        int rank = 0;
+        for (int j = 0; j < N; ++j) {
+            const int lj = ws[j + 1] - ws[j];
+            rank += (lj > lm || (lj == lm && j < tid)) ? 1 : 0;
+        }
+        if (rank == r) ws[N + 1] = tid;  // ranks are distinct: exactly one writer
+    }
+    __syncthreads();
+    const int m = ws[N + 1];
+    __syncthreads();  // ws is reused by the caller
+    return m;
+}
+
 // exp(-27.73) = 2^-40: below this bound on the state transition since the start, whatever the
 // state carried in, its remaining contribution is far under fp32 rounding.
 constexpr float kExitLog = -27.7258872f;
@@ -1300,9 +1322,17 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         within = b % wpg;
     }
     const int vb = within % p.nv;
-    const int pair = group * p.grp + within / p.nv;  // (segment, value head)
-    const int nseg = pair / p.H, h = pair % p.H, hk = h / p.grp;
-    const int n = nseg / p.P, seg = nseg % p.P;
+    int pair = group * p.grp + within / p.nv;  // (segment, value head)
+    const int h = pair % p.H, hk = h / p.grp;
+    int n = pair / p.H / p.P;
+    const int seg = pair / p.H % p.P;
+    if (p.P == 1 && p.cu && p.N <= NT) {
+        // Packed sequences of unequal lengths in one pass: the workgroups that start first (low
+        // block index) take the longest sequences, so no long sequence starts last.
+        n = longest_first<NT>(p.cu, p.N, n, tid, reinterpret_cast<int*>(sm + S::T));
+        pair = n * p.H + h;
+    }
+    const int nseg = pair / p.H;
     if (p.skip_first && seg == 0) return;
     if (p.negl_mode == NEGL_SKIP && p.negl[pair]) return;  // the segment's transition is negligible
     long bos, eos;
