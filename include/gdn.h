@@ -154,14 +154,17 @@ extern "C" {
  * Long sequences (bf16 path).  Each sequence is cut into P segments of whole chunks
  * that run in parallel; the exact affine map of a segment, S_out = S_in A_p + B_p, joins them:
  * the segments run from a zero state (B_p and o), then as transitions (A_p: identity in, zero
- * values), a P-step combine gives the true entering states E_p, and a last pass reruns each
- * segment from E_{p-1}, overwriting o.  A transition and a rerun stop once the bound
- * exp(sum of g since the segment start) on the segment's transition is <= 2^-40: past that
- * point the state entering the segment has no effect above that factor (the bound holds with
- * GDN_QK_L2NORM and 0 <= beta <= 2; otherwise nothing stops early and every pass runs the whole
- * segment).  P = 1 is the plain single pass.  With
- * GDN_SEGMENTS(0), P is chosen so that (N * P * H * dv/32) workgroups cover the current device's
- * compute units, with at least 16 chunks per segment.
+ * values), and a last pass reruns each segment from its true entering state E_{p-1}
+ * (E_0 = B_0, E_p = E_{p-1} A_p + B_p, formed by that pass itself), overwriting o.  A transition
+ * and a rerun stop once the bound exp(sum of g since the segment start) on the segment's
+ * transition is <= 2^-40: past that point the state entering the segment has no effect above that
+ * factor (the bound holds with GDN_QK_L2NORM and 0 <= beta <= 2; otherwise nothing stops early
+ * and every pass runs the whole segment).  A transition whose bound over the whole segment is
+ * already below 2^-40 is not formed (E_p = B_p), and a rerun whose first chunk reaches the bound
+ * reuses that chunk's prepared operands from the first pass.  P = 1 is the plain single pass.
+ * With GDN_SEGMENTS(0), P is chosen so that (N * P * H * dv / R) workgroups cover the current
+ * device's compute units (R = 128 state rows per workgroup for dk = 128 and dv a multiple of 128,
+ * else 64, or 32 for dv = 32), with at least 16 chunks per segment.
  */
 int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,

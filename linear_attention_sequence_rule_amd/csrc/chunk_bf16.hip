@@ -230,11 +230,25 @@ struct Smem {
     static __device__ __forceinline__ int gates(int c) { return G0 + (c & 1) * gBytes; }
 };
 
+// The prepared operands of a segment's first chunk as kept in the workspace, per (segment, head):
+// the T region (T'^T with L'_BA in its BA block), Pm, rq and the chunk's gates, each as laid out
+// in LDS.  The same for every DK and row block.
+constexpr int PRE_T = 0;                       // bf16 [C][TSTR]
+constexpr int PRE_PM = PRE_T + C * TSTR * 2;   // bf16 [C][TSTR]
+constexpr int PRE_RQ = PRE_PM + C * TSTR * 2;  // fp32 [C]
+constexpr int PRE_G = PRE_RQ + C * 4;          // gates [gBytes]
+constexpr int PRE_BYTES = PRE_G + Smem<32, 32>::gBytes;
+static_assert(PRE_BYTES == (int)kSegPrepBytes, "workspace layout of the kept operands");
+static_assert(Smem<128, 128>::PM == Smem<128, 128>::T + C * TSTR * 2 && PRE_BYTES % 16 == 0, "layout");
+
 // How a workgroup starts its state, and what it does with o (one launch runs one of the passes of
 // the segmented long-sequence path, or the plain single pass).
 enum InitMode { INIT_S0 = 0, INIT_IDENTITY = 1, INIT_PREV = 2 };
 enum NeglMode { NEGL_NONE = 0, NEGL_MARK = 1, NEGL_SKIP = 2 };
 enum OutMode { OUT_NONE = 0, OUT_STORE = 1 };
+// The prepared operands of a segment's first chunk: kept by the first pass of the segmented path,
+// used by the rerun when that chunk alone brings the transition bound below 2^-40.
+enum PreMode { PRE_NONE = 0, PRE_KEEP = 1, PRE_USE = 2 };
 
 template <int DK>
 struct Params {
@@ -248,7 +262,7 @@ struct Params {
     const float* norm_weight;   // w of the output epilogue [dv] (with out_gate)
     float norm_eps;
     float* sfin;   // end state per (segment, head): [N*P, H, dv, dk]
-    int* negl;     // per (segment, head): 1 if the run stopped at the decay bound, else 0 (or null)
+    int* negl;     // per (segment, head): nonzero if the segment's transition is negligible (or null)
     int N, T_tot, H, dv, nv;
     int Hk, grp;   // query/key heads; value heads per query/key head (H = Hk grp)
     int P;         // segments per sequence (1 = the sequence in one piece)
@@ -260,6 +274,15 @@ struct Params {
     int skip_first;  // segment 0 does nothing
     int negl_mode;   // NEGL_MARK: record whether the whole segment's transition bound is <= 2^-40;
                      // NEGL_SKIP: skip segments so marked, record a stop at the bound
+    unsigned char* pre;  // per (segment, head): the first chunk's prepared operands [PRE_BYTES]
+    int pre_mode;        // PreMode
+    // rerun of the segmented path: the state entering segment p is formed here from the end
+    // states B_j (s0), the transitions A_j and their marks (1 = negligible)
+    const int* marks;     // [N*P, H], or null (no chaining)
+    const float* trans;   // A_j [N*P, H, DK, DK]
+    float* ein;           // per (segment, head): the entering state where it had to be chained
+    float* fin;           // the final state [N, H, dv, DK], by the last segment's workgroups (first pass:
+                          // when A_{P-1} is negligible by its gates; rerun: otherwise); or null
     float scale;
     int l2norm;
 };
@@ -1288,6 +1311,209 @@ __device__ int longest_first(const int32_t* cu, int N, int r, int tid, int* ws) 
 // state carried in, its remaining contribution is far under fp32 rounding.
 constexpr float kExitLog = -27.7258872f;
 
+// BYTES (a multiple of 16) from LDS byte offset `lds` to global dst, by thread t of NTH: all reads,
+// then all stores.
+template <int BYTES, int NTH>
+__device__ __forceinline__ void keep_to_global(const unsigned char* sm, int lds, unsigned char* dst, int t) {
+    constexpr int NU = BYTES / 16, IT = (NU + NTH - 1) / NTH;
+    u32x4 v[IT];
+#pragma unroll
+    for (int j = 0; j < IT; ++j)
+        if (t + j * NTH < NU) v[j] = *reinterpret_cast<const u32x4*>(sm + lds + 16 * (t + j * NTH));
+#pragma unroll
+    for (int j = 0; j < IT; ++j)
+        if (t + j * NTH < NU) *reinterpret_cast<u32x4*>(dst + 16 * (t + j * NTH)) = v[j];
+}
+
+// E_j = E_{j-1} A_j + B_j for j = j0+1 .. j1 (E_{j0} = B_{j0}, or E_{j1} = B_{j1} when A_{j1} is
+// negligible), rows [vb BV, +BV) of sequence n, head h, in fp32: E in the row waves' registers in
+// the state-tile layout, A_j staged transposed in LDS by every wave, the product on the fp32 MFMA
+// (16x16x4) as D^T = A_j^T E^T so that D lands in the same layout.  E_{mid} (mid < j1, if mid >= j0)
+// is stored to dmid and E_{j1} to dend (row blocks [BV][DK], either may be null).  Every thread of
+// the workgroup calls this (it has barriers); it uses all of LDS.
+template <int DK, int BV>
+__device__ void chain_states(const Params<DK>& p, unsigned char* sm, int n, int h, int vb, int j0, int j1, int mid,
+                             float* dmid, float* dend, int tid) {
+    constexpr int DT = DK / 16, NT = kernel_threads<BV>(), ATS = DK + 4;  // At row stride (floats)
+    static_assert(DK * ATS * 4 <= 160 * 1024, "A_j^T in LDS");
+    const int wid = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64, g = lane / 16, l16 = lane % 16;
+    const bool is_row = wid < BV / 16;
+    const int row = vb * BV + 16 * wid + l16;
+    float* At = reinterpret_cast<float*>(sm);
+    auto slot = [&](int j) { return (size_t)(n * p.P + j) * p.H + h; };
+    auto ld_rows = [&](const float* base, fx4 (&x)[DT]) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const float4 v = *reinterpret_cast<const float4*>(base + (size_t)row * DK + kcol(dt, 4 * g));
+            x[dt] = fx4{v.x, v.y, v.z, v.w};
+        }
+    };
+    auto st_rows = [&](float* base, const fx4 (&x)[DT]) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<float4*>(base + (size_t)row * DK + kcol(dt, 4 * g)) = make_float4(x[dt][0], x[dt][1], x[dt][2], x[dt][3]);
+    };
+    fx4 E[DT];
+    int lazy = j0;  // E_lazy = B_lazy, not yet loaded (-1: E is in the registers)
+    auto held = [&]() {
+        if (lazy >= 0 && is_row) ld_rows(p.s0 + slot(lazy) * p.dv * DK, E);
+        lazy = -1;
+    };
+    if (dmid && mid == j0) {
+        held();
+        if (is_row) st_rows(dmid, E);
+    }
+    for (int j = j0 + 1; j <= j1; ++j) {
+        const float* Bj = p.s0 + slot(j) * p.dv * DK;
+        if (p.marks[slot(j)]) {  // A_j negligible
+            lazy = j;
+        } else {
+            held();
+            const float* Aj = p.trans + slot(j) * DK * DK;
+            lds_barrier();  // the previous product's reads of At are done
+            for (int i = tid; i < DK * DK / 4; i += NT) {
+                const float4 v = *reinterpret_cast<const float4*>(Aj + 4 * i);
+                const int r = 4 * i / DK, c = 4 * i % DK;
+                At[(c + 0) * ATS + r] = v.x;
+                At[(c + 1) * ATS + r] = v.y;
+                At[(c + 2) * ATS + r] = v.z;
+                At[(c + 3) * ATS + r] = v.w;
+            }
+            lds_barrier();
+            if (is_row) {
+                fx4 acc[DT];
+                ld_rows(Bj, acc);
+#pragma unroll
+                for (int dp = 0; dp < DT; ++dp)
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        // lane (m = l16, k = g): A_j[kcol(dp, 4g + e)][kcol(dt, m)], e = 0..3
+                        const fx4 a = *reinterpret_cast<const fx4*>(At + kcol(dt, l16) * ATS + kcol(dp, 4 * g));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], E[dp][e], acc[dt], 0, 0, 0);
+                    }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) E[dt] = acc[dt];
+            }
+        }
+        if (dmid && j == mid) {
+            held();
+            if (is_row) st_rows(dmid, E);
+        }
+    }
+    if (dend) {
+        held();
+        if (is_row) st_rows(dend, E);
+    }
+    lds_barrier();  // LDS is free again
+}
+
+// rows [vb BV, +BV) of a [rows][DK] fp32 block from src to dst, by threads t of nt
+template <int DK, int BV>
+__device__ __forceinline__ void copy_rows(const float* src, float* dst, int vb, int t, int nt) {
+    const float4* s4 = reinterpret_cast<const float4*>(src + (size_t)vb * BV * DK);
+    float4* d4 = reinterpret_cast<float4*>(dst + (size_t)vb * BV * DK);
+    constexpr int NU = BV * DK / 4, B = 8;
+    for (int i0 = t; i0 < NU; i0 += B * nt) {
+        float4 v[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (i0 + j * nt < NU) v[j] = s4[i0 + j * nt];
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (i0 + j * nt < NU) d4[i0 + j * nt] = v[j];
+    }
+}
+
+// Rerun of segment p >= 1 when the bound on the transition of its first chunk is already below
+// 2^-40: from the state entering the segment (E_{p-1}, rows at ein), only that chunk's outputs change,
+// and the first pass's o stands after it.  The chunk's prepared operands (T', Pm, rq, the gates)
+// are the ones the first pass formed from the same tokens, kept in the workspace, so nothing is
+// prepared here: one load phase (state, K, Q, V, the kept operands; z for the epilogue), then the
+// row waves' two sub-stages on the chunk, while the other waves copy fsrc to fdst (the final
+// state, when it is an end state B_j as it stands; else null).
+template <int DK, int BV, bool EPI>
+__device__ void rerun_first_chunk(const Params<DK>& p, unsigned char* sm, const unsigned char* kept, long bos, int len,
+                                  int h, int hk, int vb, const float* ein, const float* fsrc, float* fdst, int tid) {
+    using S = Smem<DK, BV>;
+    constexpr bool WIDE = S::WIDE;
+    constexpr int NT = kernel_threads<BV>(), PW0 = NT / 64 - 4;
+    const int wid = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, g = lane / 16, l16 = lane % 16;
+    const bool is_row = wid < BV / 16, is_prep = wid >= PW0;
+    const int pw = wid - PW0;
+    const unsigned smb = lds_base(sm);
+    RowRegs<DK> st;
+    if (is_row) {
+        const float* src = ein + (size_t)(vb * BV + 16 * wid + l16) * DK;
+#pragma unroll
+        for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
+            const float4 v = *reinterpret_cast<const float4*>(src + kcol(dt, 4 * g));
+            st.S[dt] = fx4{v.x, v.y, v.z, v.w};
+        }
+    }
+    if constexpr (WIDE) {
+        if (is_prep) {
+            dma_k<DK, 16>(p, smb + S::raw(0) + S::rK, bos, len, hk, 16 * pw, lane);
+            // z of the epilogue into the spare Q/V buffer
+            if (EPI && pw >= 2) dma_z<DK, BV, 32>(p, smb + S::qv(1) + S::rQ, bos, len, h, vb, 32 * (pw - 2), lane);
+        }
+        if (is_row) {
+            dma_q<DK, 8>(p, smb + S::qv(0) + S::rQ, bos, len, hk, 8 * wid, lane);
+            dma_v<DK, BV, 8>(p, smb + S::qv(0) + S::rV, bos, len, h, vb, 8 * wid, lane);
+        }
+    } else if (is_prep) {
+        dma_chunk<DK, BV>(p, smb, S::raw(0), bos, len, h, hk, vb, pw, lane);
+    }
+    if constexpr (EPI)
+        if (tid < BV) reinterpret_cast<float*>(sm + S::NW)[tid] = p.norm_weight[vb * BV + tid];
+    // the kept operands, by plain loads
+    constexpr int NU = PRE_BYTES / 16, IT = (NU + NT - 1) / NT;
+    u32x4 kv[IT];
+#pragma unroll
+    for (int j = 0; j < IT; ++j)
+        if (tid + j * NT < NU) kv[j] = *reinterpret_cast<const u32x4*>(kept + 16 * (tid + j * NT));
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+        const int b = 16 * (tid + j * NT);
+        if (b < PRE_BYTES) {
+            const int dst = b < PRE_PM ? S::T + b
+                                       : (b < PRE_RQ ? S::PM + (b - PRE_PM)
+                                                     : (b < PRE_G ? S::ORQ + (b - PRE_RQ) : S::gates(0) + (b - PRE_G)));
+            *reinterpret_cast<u32x4*>(sm + dst) = kv[j];
+        }
+    }
+    wait_loads();
+    if (len < C) {
+        if constexpr (WIDE) {
+            if (is_prep) zero_rows<DK, 16>(reinterpret_cast<__bf16*>(sm + S::raw(0) + S::rK), len, 16 * pw, opaque(lane));
+            if (is_row) {
+                zero_rows<DK, 8>(reinterpret_cast<__bf16*>(sm + S::qv(0) + S::rQ), len, 8 * wid, opaque(lane));
+                zero_rows<BV, 8>(reinterpret_cast<__bf16*>(sm + S::qv(0) + S::rV), len, 8 * wid, opaque(lane));
+            }
+        } else if (is_prep) {
+            zero_tail<DK, BV>(sm + S::raw(0), len, pw, lane);
+        }
+    }
+    lds_barrier();
+    // the final state, where it is a copy, by the waves that have nothing else to do
+    if (fdst && is_prep) copy_rows<DK, BV>(fsrc, fdst, vb, tid - 64 * PW0, NT - 64 * PW0);
+    if (is_row) {
+        row_A<DK, BV>(st, sm, sm + S::raw(0), sm + S::qv(0), sm + S::gates(0), wid, lane);
+        row_B<DK, BV>(st, sm, sm + S::raw(0), sm + S::gates(0), lane);
+        if constexpr (EPI)
+            epi_sums<DK, BV>(p, st, sm, wid, lane);
+        else
+            row_store<DK, BV>(p, st, wid, lane, bos, len, h, vb);
+    }
+    if constexpr (EPI) {
+        lds_barrier();
+        if (is_row)
+            epi_store<DK, BV>(p, st, sm, wid, lane, bos, len, h, vb,
+                              reinterpret_cast<const __bf16*>(sm + S::qv(1) + S::rQ));
+    }
+}
+
 // BV: state rows of the workgroup: BV / 16 row waves.  Narrow (BV = 64, or 32 for a 32-row
 // state): 8 waves, waves 2 and 3 load the chunks, waves 4..7 prepare them.  Wide (BV = 128): 12
 // waves, every row wave loads an eighth of each chunk, waves 8..11 prepare them; the preparation of
@@ -1352,6 +1578,50 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     }
     const int nchunks = (int)((eos - bos + C - 1) / C);
     auto clen = [&](int c) { return (int)min((long)C, eos - (bos + (long)c * C)); };
+    // The state entering this segment (rerun: [rows][DK] block): E_{seg-1} = E_{seg-2} A_{seg-1} +
+    // B_{seg-1}, E_0 = B_0, and E_j = B_j where A_j is negligible -- B_{seg-1} itself in the usual
+    // case, else chained here from the last negligible link.  The last segment's workgroups also
+    // form the final state E_{P-1}.
+    // The last segment's marks tell how the final state E_{P-1} stands: 1 = A_{P-1} negligible by
+    // its gates, and the first pass wrote B_{P-1} as the final state; 2 = the transition stopped at
+    // the bound (B_{P-1} to be copied); 0 = chained.
+    const float* ein = p.s0 + (size_t)((nseg - 1) * p.H + h) * p.dv * DK;
+    const float* fsrc = nullptr;  // the final state as a copy of B_{P-1}
+    float* fdst = nullptr;
+    const bool fast_ok = p.pre_mode == PRE_USE && seg > 0 && nchunks > 0 && p.early_exit && !p.conv_w;
+    const unsigned char* kept = p.pre + (size_t)pair * PRE_BYTES;
+    if (p.marks && seg > 0) {
+        // the loads this choice needs, issued together
+        const bool last = p.fin && seg == p.P - 1;
+        const int mprev = p.marks[(size_t)(n * p.P + seg - 1) * p.H + h];
+        const int mlast = last ? p.marks[pair] : 1;
+        int j0 = seg - 1;
+        if (j0 > 0 && !mprev)
+            do --j0;
+            while (j0 > 0 && !p.marks[(size_t)(n * p.P + j0) * p.H + h]);
+        if (mlast == 2) {
+            fsrc = p.s0 + (size_t)pair * p.dv * DK;
+            fdst = p.fin + ((size_t)n * p.H + h) * p.dv * DK;
+        }
+        const bool fin = mlast == 0;
+        if (j0 < seg - 1 || fin) {
+            float* own = p.ein + (size_t)pair * p.dv * DK;
+            chain_states<DK, BV>(p, sm, n, h, vb, j0, fin ? seg : seg - 1, seg - 1, j0 < seg - 1 ? own : nullptr,
+                                 fin ? p.fin + ((size_t)n * p.H + h) * p.dv * DK : nullptr, tid);
+            if (j0 < seg - 1) ein = own;
+        }
+    }
+    if (fast_ok) {
+        const float b0 = __builtin_bit_cast(
+            float, __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(kept + PRE_G + S::gGC + 4)));
+        if (b0 <= kExitLog) {
+            rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, fsrc, fdst, tid);
+            return;
+        }
+    }
+    if (fdst) copy_rows<DK, BV>(fsrc, fdst, vb, tid, NT);
+    // the first pass keeps its first chunk's prepared operands for the rerun (one copy per head)
+    const bool keep = p.pre_mode == PRE_KEEP && seg > 0 && vb == 0;
 
     // T^T blocks above the diagonal blocks and Pm tiles above the diagonal are read as zeros but
     // never written: clear both once.  Zero values: clear V in every buffer that holds it.
@@ -1423,7 +1693,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             if (p.init == INIT_S0 && p.s0 && seg == 0)
                 src = p.s0 + (((size_t)n * p.H + h) * p.dv + row) * DK;
             else if (p.init == INIT_PREV)
-                src = p.s0 + (((size_t)(nseg - 1) * p.H + h) * p.dv + row) * DK;
+                src = ein + (size_t)row * DK;
 #pragma unroll
             for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
                 if (src) {
@@ -1536,7 +1806,18 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 *reinterpret_cast<float4*>(p.sfin + srow0 + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
             }
         }
-        if (p.negl && vb == 0 && tid == 0) p.negl[pair] = p.negl_mode == NEGL_MARK ? (decay <= kExitLog) : stopped;
+        // first pass, last segment, transition negligible by its gates: B_{P-1} is the final state
+        if (is_row && p.fin && !p.marks && seg == p.P - 1 && p.negl_mode == NEGL_MARK && decay <= kExitLog) {
+            const size_t frow0 = ((size_t)n * p.H + h) * p.dv * DK + (size_t)row * DK;
+#pragma unroll
+            for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
+                const fx4 v = st.S[dt];
+                *reinterpret_cast<float4*>(p.fin + frow0 + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+        // marks: 1 = negligible by the gates (first pass), 2 = stopped at the bound (transition)
+        if (p.negl && vb == 0 && tid == 0)
+            p.negl[pair] = p.negl_mode == NEGL_MARK ? (decay <= kExitLog ? 1 : 0) : (stopped ? 2 : 0);
     } else {
         for (int k = -1; k < nchunks; ++k) {
             const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
@@ -1549,6 +1830,13 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             }
             if (nxt && pw == 0) prep_L<DK, BV, 0>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
             if (nxt && pw == 3) prep_L<DK, BV, 1>(sm + S::raw(k + 1), sm, lane, clen(k + 1), p.l2norm);
+            // T' and the gates of chunk 0, complete since the previous barrier (T' is rewritten in
+            // this iteration's sub-stage B)
+            if (keep && k == 0 && pw < 2) {
+                unsigned char* kd = p.pre + (size_t)pair * PRE_BYTES;
+                keep_to_global<C * TSTR * 2, 128>(sm, S::T, kd + PRE_T, tid - 64 * PW0);
+                keep_to_global<Smem<DK, BV>::gBytes, 128>(sm, S::gates(0), kd + PRE_G, tid - 64 * PW0);
+            }
             lds_barrier();
             // ---- B
             if (cur) bound(k);
@@ -1576,6 +1864,13 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                          reinterpret_cast<const float*>(sm + S::WL),
                          reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB), lane);
             if (nxt && pw == 3) make_gates<DK, BV>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
+            // Pm and rq of chunk 0, formed in sub-stage A (rewritten in the next iteration's), by
+            // the solve waves, which have time to spare here and never wait for their stores
+            if (keep && k == 0 && pw < 2) {
+                unsigned char* kd = p.pre + (size_t)pair * PRE_BYTES;
+                keep_to_global<C * TSTR * 2, 128>(sm, S::PM, kd + PRE_PM, tid - 64 * PW0);
+                keep_to_global<C * 4, 128>(sm, S::ORQ, kd + PRE_RQ, tid - 64 * PW0);
+            }
             if constexpr (EPI) {
                 if (pw >= 2 && (cur || nxt)) {
                     wait_loads();
@@ -1611,6 +1906,12 @@ struct Pass {
     const float* s0;
     float* sfin;
     int* negl;
+    unsigned char* pre;
+    int pre_mode;
+    const int* marks;
+    const float* trans;
+    float* ein;
+    float* fin;
 };
 
 template <int DK, int BV>
@@ -1643,6 +1944,12 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     p.early_exit = c.early_exit;
     p.skip_first = c.skip_first;
     p.negl_mode = c.negl_mode;
+    p.pre = c.pre;
+    p.pre_mode = c.pre_mode;
+    p.marks = c.marks;
+    p.trans = c.trans;
+    p.ein = c.ein;
+    p.fin = c.fin;
     p.scale = a.scale;
     p.l2norm = a.l2norm;
     // the output epilogue in the kernel: wide workgroups of a pass that stores o
@@ -1683,21 +1990,30 @@ hipError_t run(const ChunkArgs& a, int P) {
     //     whether the bound on the whole segment's transition is below 2^-40 (negligible);
     //  2. A_p = the transition of segment p (identity in, zero values), for the segments not marked
     //     negligible, stopped once its norm bound is below 2^-40 (then marked negligible);
-    //  3. combine: E_0 = B_0, E_p = E_{p-1} A_p + B_p (the true end states), final = E_{P-1};
-    //  4. rerun: segment p again from E_{p-1}, overwriting o, until the bound on the transition
+    //  3. rerun: E_{p-1} (E_0 = B_0, E_j = E_{j-1} A_j + B_j, B_j itself where A_j is negligible),
+    //     formed in segment p's own workgroups (final = E_{P-1} in the last segment's), then
+    //     segment p again from E_{p-1}, overwriting o, until the bound on the transition
     //     since the segment start is <= 2^-40; from there on the state of step 1 differs from the
-    //     true one by less than that factor of |E_{p-1}|, so step 1's o stands.
+    //     true one by less than that factor of |E_{p-1}|, so step 1's o stands.  Where the first
+    //     chunk alone reaches the bound (the usual case), step 1 keeps that chunk's prepared
+    //     operands and the rerun only redoes the chunk's state and output products.
     const SegLayout L = seg_layout(a.N, a.H, a.dk, a.dv, P);
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
     float* E = reinterpret_cast<float*>(ws + L.off_E);
     float* A = reinterpret_cast<float*>(ws + L.off_A);
     int* negl = reinterpret_cast<int*>(ws + L.off_negl);
     const int ex = a.l2norm ? 1 : 0;
-    hipError_t e = launch_rows<DK>(a, Pass{P, INIT_S0, OUT_STORE, 0, 0, 0, NEGL_MARK, a.dv, a.s0, E, negl});
+    // the kept operands serve only a rerun that stops early and has no conv inside the kernel
+    const bool keep = ex && !a.conv_w;
+    unsigned char* pre = keep ? ws + L.off_pre : nullptr;
+    hipError_t e = launch_rows<DK>(a, Pass{P, INIT_S0, OUT_STORE, 0, 0, 0, NEGL_MARK, a.dv, a.s0, E, negl, pre,
+                                           keep ? PRE_KEEP : PRE_NONE, nullptr, nullptr, nullptr, a.sfin});
     if (e == hipSuccess)
         e = launch_rows<DK>(a, Pass{P, INIT_IDENTITY, OUT_NONE, 1, ex, 1, NEGL_SKIP, a.dk, nullptr, A, negl});
-    if (e == hipSuccess) e = launch_seg_combine(E, A, negl, a.sfin, a.N, P, a.H, a.dk, a.dv, a.stream);
-    if (e == hipSuccess) e = launch_rows<DK>(a, Pass{P, INIT_PREV, OUT_STORE, 0, ex, 1, NEGL_NONE, a.dv, E, nullptr, nullptr});
+    if (e == hipSuccess)
+        e = launch_rows<DK>(a, Pass{P, INIT_PREV, OUT_STORE, 0, ex, 1, NEGL_NONE, a.dv, E, nullptr, nullptr, pre,
+                                    keep ? PRE_USE : PRE_NONE, negl, A, reinterpret_cast<float*>(ws + L.off_ein),
+                                    a.sfin});
     return e;
 }
 

@@ -50,11 +50,16 @@ struct ChunkArgs {
 
 // Workspace of the segmented long-sequence path (P segments per sequence), byte offsets.
 struct SegLayout {
-    size_t off_E;     // fp32 [N*P, H, dv, dk]: B_p, overwritten by the true end states E_p
+    size_t off_E;     // fp32 [N*P, H, dv, dk]: B_p, the end states from a zero start
     size_t off_A;     // fp32 [N*P, H, dk, dk]: segment transitions A_p
     size_t off_negl;  // int32 [N*P, H]: 1 where A_p is below the decay bound
+    size_t off_pre;   // [N*P, H] x kSegPrepBytes: prepared operands of each segment's first chunk
+    size_t off_ein;   // fp32 [N*P, H, dv, dk]: entering states E_{p-1} that had to be chained
     size_t bytes;
 };
+// Bytes per (segment, head) of the first chunk's prepared operands that the first pass keeps for
+// the rerun (two 64 x 72 bf16 tiles, 64 fp32, and the chunk's 1088 bytes of gates).
+constexpr size_t kSegPrepBytes = 2 * 64 * 72 * 2 + 64 * 4 + 1088;
 SegLayout seg_layout(int N, int H, int dk, int dv, int P);
 // State rows per workgroup of the bf16 chunk kernel for a pass with `rows` state rows:
 // 128 (wide workgroups) for d_k = 128 and rows a multiple of 128; else 64, or 32 for a 32-row
@@ -82,7 +87,5 @@ hipError_t launch_conv_state_update(const ChunkArgs& a);
 // o <- o * rsqrt(mean over dv of o^2 + eps) * (1 + w) * sigmoid(z), in place, rows of dv elements.
 hipError_t launch_gated_norm(void* o, const void* z, const float* w, long rows, int dv, float eps, bool is_bf16,
                              hipStream_t stream);
-hipError_t launch_seg_combine(float* E, const float* A, const int* negl, float* sfin, int N, int P, int H, int dk,
-                              int dv, hipStream_t stream);
 
 }  // namespace gdn

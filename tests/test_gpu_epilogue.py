@@ -86,6 +86,31 @@ def test_epilogue_prefill_segments_and_conv():
     _flush("epilogue segments+conv+groups: max err %.3g, max err/bound %.3g" % (np.abs(og - ref).max(), excess.max()))
 
 
+def test_epilogue_prefill_segments_grouped():
+    """The epilogue on the segmented path without the conv, grouped heads: reruns whose first chunk
+    reaches the decay bound redo only that chunk (one of them a partial chunk: the last segment of
+    the 138-token sequence has 10 tokens), while head 3, slowly decaying, reruns in full."""
+    from linear_attention_sequence_rule_amd import gdn_chunk_fwd
+    import torch
+    wl = W.make("epi_seg_gqa", seed=612, lengths=[64 * 30 + 17, 64 * 2 + 10, 40], H=4, Hk=2, dk=128, dv=128,
+                dtype="bf16", s0_std=0.02, varlen=True)
+    wl.g[:, 3] = -2e-3
+    z, w = _epilogue_inputs(612, (wl.T_tot, wl.H), 128, "bf16")
+    o, sf = gdn_chunk_fwd(TL.to_dev(wl.q), TL.to_dev(wl.k), TL.to_dev(wl.v), TL.to_dev(wl.g), TL.to_dev(wl.beta),
+                          TL.to_dev(wl.s0), TL.to_dev(wl.cu_seqlens), segments=3, out_gate=TL.to_dev(z),
+                          norm_weight=TL.to_dev(w), norm_eps=1e-3)
+    torch.cuda.synchronize()
+    og, sg = TL.o_to_f64(o), sf.cpu().numpy().astype(np.float64)
+    o_ref, s_ref = TL.run_oracle(wl)
+    TL.compare(wl, o_ref, sg, o_ref, s_ref)
+    ref = oracle.gated_norm(o_ref, _zf(z), w, 1e-3)
+    m = (1.0 + w.astype(np.float64)) / (1.0 + np.exp(-_zf(z).astype(np.float64)))
+    rms = np.sqrt((o_ref ** 2).mean(-1, keepdims=True) + 1e-3)
+    excess = np.abs(og - ref) / (2 * m * TL.BF16_O_ABS / rms + 2.0 ** -8 * np.abs(ref) + 1e-5)
+    assert excess.max() <= 1.0, excess.max()
+    _flush("epilogue segments+groups: max err %.3g, max err/bound %.3g" % (np.abs(og - ref).max(), excess.max()))
+
+
 @pytest.mark.parametrize("dtype,H,Hk,dk,dv,conv", [("f32", 3, 3, 64, 64, False), ("f32", 4, 2, 32, 128, True),
                                                    ("bf16", 4, 4, 128, 128, False), ("bf16", 4, 2, 128, 128, True),
                                                    ("bf16", 2, 1, 64, 32, True)])
