@@ -281,8 +281,9 @@ struct Params {
     const int* marks;     // [N*P, H], or null (no chaining)
     const float* trans;   // A_j [N*P, H, DK, DK]
     float* ein;           // per (segment, head): the entering state where it had to be chained
-    float* fin;           // the final state [N, H, dv, DK], by the last segment's workgroups (first pass:
-                          // when A_{P-1} is negligible by its gates; rerun: otherwise); or null
+    float* fin;           // the final state [N, H, dv, DK], or null: the first pass stores B_{P-1} there
+                          // (not in its slot of s0), which is E_{P-1} where A_{P-1} is negligible; the
+                          // rerun of the last segment chains E_{P-1} over it otherwise
     float scale;
     int l2norm;
 };
@@ -1311,18 +1312,13 @@ __device__ int longest_first(const int32_t* cu, int N, int r, int tid, int* ws) 
 // state carried in, its remaining contribution is far under fp32 rounding.
 constexpr float kExitLog = -27.7258872f;
 
-// BYTES (a multiple of 16) from LDS byte offset `lds` to global dst, by thread t of NTH: all reads,
-// then all stores.
+// BYTES (a multiple of 16) from LDS byte offset `lds` to global dst, by thread t of NTH, 16 bytes
+// at a time (a rolled loop: it sits inside the chunk loop, whose registers it must not take).
 template <int BYTES, int NTH>
 __device__ __forceinline__ void keep_to_global(const unsigned char* sm, int lds, unsigned char* dst, int t) {
-    constexpr int NU = BYTES / 16, IT = (NU + NTH - 1) / NTH;
-    u32x4 v[IT];
-#pragma unroll
-    for (int j = 0; j < IT; ++j)
-        if (t + j * NTH < NU) v[j] = *reinterpret_cast<const u32x4*>(sm + lds + 16 * (t + j * NTH));
-#pragma unroll
-    for (int j = 0; j < IT; ++j)
-        if (t + j * NTH < NU) *reinterpret_cast<u32x4*>(dst + 16 * (t + j * NTH)) = v[j];
+#pragma unroll 1
+    for (int i = t; i < BYTES / 16; i += NTH)
+        *reinterpret_cast<u32x4*>(dst + 16 * i) = *reinterpret_cast<const u32x4*>(sm + lds + 16 * i);
 }
 
 // E_j = E_{j-1} A_j + B_j for j = j0+1 .. j1 (E_{j0} = B_{j0}, or E_{j1} = B_{j1} when A_{j1} is
@@ -1353,10 +1349,14 @@ __device__ void chain_states(const Params<DK>& p, unsigned char* sm, int n, int 
         for (int dt = 0; dt < DT; ++dt)
             *reinterpret_cast<float4*>(base + (size_t)row * DK + kcol(dt, 4 * g)) = make_float4(x[dt][0], x[dt][1], x[dt][2], x[dt][3]);
     };
+    // B_j (B_{P-1} is in the final state's place, see Params::fin)
+    auto bj = [&](int j) {
+        return p.fin && j == p.P - 1 ? p.fin + ((size_t)n * p.H + h) * p.dv * DK : p.s0 + slot(j) * p.dv * DK;
+    };
     fx4 E[DT];
     int lazy = j0;  // E_lazy = B_lazy, not yet loaded (-1: E is in the registers)
     auto held = [&]() {
-        if (lazy >= 0 && is_row) ld_rows(p.s0 + slot(lazy) * p.dv * DK, E);
+        if (lazy >= 0 && is_row) ld_rows(bj(lazy), E);
         lazy = -1;
     };
     if (dmid && mid == j0) {
@@ -1364,7 +1364,7 @@ __device__ void chain_states(const Params<DK>& p, unsigned char* sm, int n, int 
         if (is_row) st_rows(dmid, E);
     }
     for (int j = j0 + 1; j <= j1; ++j) {
-        const float* Bj = p.s0 + slot(j) * p.dv * DK;
+        const float* Bj = bj(j);
         if (p.marks[slot(j)]) {  // A_j negligible
             lazy = j;
         } else {
@@ -1408,33 +1408,16 @@ __device__ void chain_states(const Params<DK>& p, unsigned char* sm, int n, int 
     lds_barrier();  // LDS is free again
 }
 
-// rows [vb BV, +BV) of a [rows][DK] fp32 block from src to dst, by threads t of nt
-template <int DK, int BV>
-__device__ __forceinline__ void copy_rows(const float* src, float* dst, int vb, int t, int nt) {
-    const float4* s4 = reinterpret_cast<const float4*>(src + (size_t)vb * BV * DK);
-    float4* d4 = reinterpret_cast<float4*>(dst + (size_t)vb * BV * DK);
-    constexpr int NU = BV * DK / 4, B = 8;
-    for (int i0 = t; i0 < NU; i0 += B * nt) {
-        float4 v[B];
-#pragma unroll
-        for (int j = 0; j < B; ++j)
-            if (i0 + j * nt < NU) v[j] = s4[i0 + j * nt];
-#pragma unroll
-        for (int j = 0; j < B; ++j)
-            if (i0 + j * nt < NU) d4[i0 + j * nt] = v[j];
-    }
-}
 
 // Rerun of segment p >= 1 when the bound on the transition of its first chunk is already below
 // 2^-40: from the state entering the segment (E_{p-1}, rows at ein), only that chunk's outputs change,
 // and the first pass's o stands after it.  The chunk's prepared operands (T', Pm, rq, the gates)
 // are the ones the first pass formed from the same tokens, kept in the workspace, so nothing is
 // prepared here: one load phase (state, K, Q, V, the kept operands; z for the epilogue), then the
-// row waves' two sub-stages on the chunk, while the other waves copy fsrc to fdst (the final
-// state, when it is an end state B_j as it stands; else null).
+// row waves' two sub-stages on the chunk.
 template <int DK, int BV, bool EPI>
 __device__ void rerun_first_chunk(const Params<DK>& p, unsigned char* sm, const unsigned char* kept, long bos, int len,
-                                  int h, int hk, int vb, const float* ein, const float* fsrc, float* fdst, int tid) {
+                                  int h, int hk, int vb, const float* ein, int tid) {
     using S = Smem<DK, BV>;
     constexpr bool WIDE = S::WIDE;
     constexpr int NT = kernel_threads<BV>(), PW0 = NT / 64 - 4;
@@ -1496,8 +1479,6 @@ __device__ void rerun_first_chunk(const Params<DK>& p, unsigned char* sm, const 
         }
     }
     lds_barrier();
-    // the final state, where it is a copy, by the waves that have nothing else to do
-    if (fdst && is_prep) copy_rows<DK, BV>(fsrc, fdst, vb, tid - 64 * PW0, NT - 64 * PW0);
     if (is_row) {
         row_A<DK, BV>(st, sm, sm + S::raw(0), sm + S::qv(0), sm + S::gates(0), wid, lane);
         row_B<DK, BV>(st, sm, sm + S::raw(0), sm + S::gates(0), lane);
@@ -1582,12 +1563,9 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     // B_{seg-1}, E_0 = B_0, and E_j = B_j where A_j is negligible -- B_{seg-1} itself in the usual
     // case, else chained here from the last negligible link.  The last segment's workgroups also
     // form the final state E_{P-1}.
-    // The last segment's marks tell how the final state E_{P-1} stands: 1 = A_{P-1} negligible by
-    // its gates, and the first pass wrote B_{P-1} as the final state; 2 = the transition stopped at
-    // the bound (B_{P-1} to be copied); 0 = chained.
+    // The last segment's workgroups chain the final state E_{P-1} over B_{P-1} where A_{P-1} is not
+    // negligible.
     const float* ein = p.s0 + (size_t)((nseg - 1) * p.H + h) * p.dv * DK;
-    const float* fsrc = nullptr;  // the final state as a copy of B_{P-1}
-    float* fdst = nullptr;
     const bool fast_ok = p.pre_mode == PRE_USE && seg > 0 && nchunks > 0 && p.early_exit && !p.conv_w;
     const unsigned char* kept = p.pre + (size_t)pair * PRE_BYTES;
     if (p.marks && seg > 0) {
@@ -1599,11 +1577,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         if (j0 > 0 && !mprev)
             do --j0;
             while (j0 > 0 && !p.marks[(size_t)(n * p.P + j0) * p.H + h]);
-        if (mlast == 2) {
-            fsrc = p.s0 + (size_t)pair * p.dv * DK;
-            fdst = p.fin + ((size_t)n * p.H + h) * p.dv * DK;
-        }
-        const bool fin = mlast == 0;
+        const bool fin = mlast == 0;  // else B_{P-1}, in place, is the final state
         if (j0 < seg - 1 || fin) {
             float* own = p.ein + (size_t)pair * p.dv * DK;
             chain_states<DK, BV>(p, sm, n, h, vb, j0, fin ? seg : seg - 1, seg - 1, j0 < seg - 1 ? own : nullptr,
@@ -1615,11 +1589,10 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         const float b0 = __builtin_bit_cast(
             float, __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(kept + PRE_G + S::gGC + 4)));
         if (b0 <= kExitLog) {
-            rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, fsrc, fdst, tid);
+            rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, tid);
             return;
         }
     }
-    if (fdst) copy_rows<DK, BV>(fsrc, fdst, vb, tid, NT);
     // the first pass keeps its first chunk's prepared operands for the rerun (one copy per head)
     const bool keep = p.pre_mode == PRE_KEEP && seg > 0 && vb == 0;
 
@@ -1799,25 +1772,17 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 epi_store<DK, BV>(p, st, sm, wid, lane, bos + (long)pend * C, clen(pend), h, vb,
                                   reinterpret_cast<const __bf16*>(sm + S::qv(pend) + S::rQ));
         if (is_row && p.sfin) {
-            const size_t srow0 = ((size_t)pair * p.dv + row) * DK;
+            // first pass, last segment: B_{P-1} into the final state (see Params::fin)
+            float* dst = (p.fin && seg == p.P - 1 ? p.fin + ((size_t)n * p.H + h) * p.dv * DK
+                                                  : p.sfin + (size_t)pair * p.dv * DK) +
+                         (size_t)row * DK;
 #pragma unroll
             for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
                 const fx4 v = st.S[dt];
-                *reinterpret_cast<float4*>(p.sfin + srow0 + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(dst + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
             }
         }
-        // first pass, last segment, transition negligible by its gates: B_{P-1} is the final state
-        if (is_row && p.fin && !p.marks && seg == p.P - 1 && p.negl_mode == NEGL_MARK && decay <= kExitLog) {
-            const size_t frow0 = ((size_t)n * p.H + h) * p.dv * DK + (size_t)row * DK;
-#pragma unroll
-            for (int dt = 0; dt < RowRegs<DK>::DT; ++dt) {
-                const fx4 v = st.S[dt];
-                *reinterpret_cast<float4*>(p.fin + frow0 + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
-            }
-        }
-        // marks: 1 = negligible by the gates (first pass), 2 = stopped at the bound (transition)
-        if (p.negl && vb == 0 && tid == 0)
-            p.negl[pair] = p.negl_mode == NEGL_MARK ? (decay <= kExitLog ? 1 : 0) : (stopped ? 2 : 0);
+        if (p.negl && vb == 0 && tid == 0) p.negl[pair] = p.negl_mode == NEGL_MARK ? (decay <= kExitLog) : stopped;
     } else {
         for (int k = -1; k < nchunks; ++k) {
             const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
