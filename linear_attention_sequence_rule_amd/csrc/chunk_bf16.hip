@@ -1500,8 +1500,10 @@ __device__ void rerun_first_chunk(const Params<DK>& p, unsigned char* sm, const 
 // waves, every row wave loads an eighth of each chunk, waves 8..11 prepare them; the preparation of
 // a chunk (L, T, Pm, the gates) is shared by all 128 rows.
 // RAW: g and beta hold the raw gate inputs (a separate instantiation, so that the plain one carries
-// no trace of the gate transform).
-template <int DK, int BV, bool RAW, bool EPI>
+// no trace of the gate transform).  EPI: the output epilogue.  LEAN: without the rerun pass's code
+// (entering states, the one-chunk rerun); the first and transition passes without the epilogue
+// run this one: the chunk loop schedules better without that code beside it.
+template <int DK, int BV, bool RAW, bool EPI, bool LEAN>
 __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params<DK> p) {
     using S = Smem<DK, BV>;
     constexpr bool WIDE = S::WIDE;
@@ -1566,9 +1568,9 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     // The last segment's workgroups chain the final state E_{P-1} over B_{P-1} where A_{P-1} is not
     // negligible.
     const float* ein = p.s0 + (size_t)((nseg - 1) * p.H + h) * p.dv * DK;
-    const bool fast_ok = p.pre_mode == PRE_USE && seg > 0 && nchunks > 0 && p.early_exit && !p.conv_w;
+    const bool fast_ok = !LEAN && p.pre_mode == PRE_USE && seg > 0 && nchunks > 0 && p.early_exit && !p.conv_w;
     const unsigned char* kept = p.pre + (size_t)pair * PRE_BYTES;
-    if (p.marks && seg > 0) {
+    if (!LEAN && p.marks && seg > 0) {
         // the loads this choice needs, issued together
         const bool last = p.fin && seg == p.P - 1;
         const int mprev = p.marks[(size_t)(n * p.P + seg - 1) * p.H + h];
@@ -1580,8 +1582,9 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         const bool fin = mlast == 0;  // else B_{P-1}, in place, is the final state
         if (j0 < seg - 1 || fin) {
             float* own = p.ein + (size_t)pair * p.dv * DK;
-            chain_states<DK, BV>(p, sm, n, h, vb, j0, fin ? seg : seg - 1, seg - 1, j0 < seg - 1 ? own : nullptr,
-                                 fin ? p.fin + ((size_t)n * p.H + h) * p.dv * DK : nullptr, tid);
+            if constexpr (!LEAN)
+                chain_states<DK, BV>(p, sm, n, h, vb, j0, fin ? seg : seg - 1, seg - 1, j0 < seg - 1 ? own : nullptr,
+                                     fin ? p.fin + ((size_t)n * p.H + h) * p.dv * DK : nullptr, tid);
             if (j0 < seg - 1) ein = own;
         }
     }
@@ -1589,7 +1592,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         const float b0 = __builtin_bit_cast(
             float, __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(kept + PRE_G + S::gGC + 4)));
         if (b0 <= kExitLog) {
-            rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, tid);
+            if constexpr (!LEAN) rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, tid);
             return;
         }
     }
@@ -1853,15 +1856,28 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
 
 template <int DK, int BV, bool EPI>
 hipError_t launch_k(const Params<DK>& p, const ChunkArgs& a, int grid, int smem) {
-    const void* fn = a.gate_params ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, true, EPI>)
-                                   : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, false, EPI>);
+    // the lean instantiation (no rerun code) for every pass but the rerun, unless the epilogue is on
+    constexpr bool L = !EPI;
+    const bool lean = L && p.init != INIT_PREV;
+    const void* fn = a.gate_params
+                         ? (lean ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, true, EPI, L>)
+                                 : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, true, EPI, false>))
+                         : (lean ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, false, EPI, L>)
+                                 : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, false, EPI, false>));
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     constexpr int nt = kernel_threads<BV>();
-    if (a.gate_params)
-        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, true, EPI>), dim3(grid), dim3(nt), smem, a.stream, p);
-    else
-        hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, false, EPI>), dim3(grid), dim3(nt), smem, a.stream, p);
+    if (a.gate_params) {
+        if (lean)
+            hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, true, EPI, L>), dim3(grid), dim3(nt), smem, a.stream, p);
+        else
+            hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, true, EPI, false>), dim3(grid), dim3(nt), smem, a.stream, p);
+    } else {
+        if (lean)
+            hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, false, EPI, L>), dim3(grid), dim3(nt), smem, a.stream, p);
+        else
+            hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, false, EPI, false>), dim3(grid), dim3(nt), smem, a.stream, p);
+    }
     return hipGetLastError();
 }
 
