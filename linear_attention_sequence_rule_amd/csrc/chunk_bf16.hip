@@ -1414,10 +1414,11 @@ __device__ void chain_states(const Params<DK>& p, unsigned char* sm, int n, int 
 // and the first pass's o stands after it.  The chunk's prepared operands (T', Pm, rq, the gates)
 // are the ones the first pass formed from the same tokens, kept in the workspace, so nothing is
 // prepared here: one load phase (state, K, Q, V, the kept operands; z for the epilogue), then the
-// row waves' two sub-stages on the chunk.
-template <int DK, int BV, bool EPI>
-__device__ void rerun_first_chunk(const Params<DK>& p, unsigned char* sm, const unsigned char* kept, long bos, int len,
-                                  int h, int hk, int vb, const float* ein, int tid) {
+// row waves' two sub-stages on the chunk.  go() (uniform) is asked once the loads are in flight:
+// false drops them (waited for, so that LDS is free again) and returns false.
+template <int DK, int BV, bool EPI, typename Go>
+__device__ bool rerun_first_chunk(const Params<DK>& p, unsigned char* sm, const unsigned char* kept, long bos, int len,
+                                  int h, int hk, int vb, const float* ein, int tid, Go go) {
     using S = Smem<DK, BV>;
     constexpr bool WIDE = S::WIDE;
     constexpr int NT = kernel_threads<BV>(), PW0 = NT / 64 - 4;
@@ -1456,6 +1457,11 @@ __device__ void rerun_first_chunk(const Params<DK>& p, unsigned char* sm, const 
 #pragma unroll
     for (int j = 0; j < IT; ++j)
         if (tid + j * NT < NU) kv[j] = *reinterpret_cast<const u32x4*>(kept + 16 * (tid + j * NT));
+    if (!go()) {
+        wait_loads();
+        lds_barrier();
+        return false;
+    }
 #pragma unroll
     for (int j = 0; j < IT; ++j) {
         const int b = 16 * (tid + j * NT);
@@ -1493,6 +1499,7 @@ __device__ void rerun_first_chunk(const Params<DK>& p, unsigned char* sm, const 
             epi_store<DK, BV>(p, st, sm, wid, lane, bos, len, h, vb,
                               reinterpret_cast<const __bf16*>(sm + S::qv(1) + S::rQ));
     }
+    return true;
 }
 
 // BV: state rows of the workgroup: BV / 16 row waves.  Narrow (BV = 64, or 32 for a 32-row
@@ -1570,6 +1577,23 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     const float* ein = p.s0 + (size_t)((nseg - 1) * p.H + h) * p.dv * DK;
     const bool fast_ok = !LEAN && p.pre_mode == PRE_USE && seg > 0 && nchunks > 0 && p.early_exit && !p.conv_w;
     const unsigned char* kept = p.pre + (size_t)pair * PRE_BYTES;
+    auto kept_bound = [&]() {  // the bound of the first chunk's transition, from the kept gates
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(kept + PRE_G + S::gGC + 4)));
+    };
+    if constexpr (!LEAN) {
+        // The usual case, taken on trust while its loads are in flight: E_{seg-1} = B_{seg-1} in
+        // place, no final state to chain, and the first chunk reaches the bound.
+        if (fast_ok && p.marks) {
+            auto usual = [&]() {
+                const int mprev = p.marks[(size_t)(n * p.P + seg - 1) * p.H + h];
+                const int mlast = p.fin && seg == p.P - 1 ? p.marks[pair] : 1;
+                const float b0 = kept_bound();
+                return (seg == 1 || mprev != 0) && mlast != 0 && b0 <= kExitLog;
+            };
+            if (rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, tid, usual)) return;
+        }
+    }
     if (!LEAN && p.marks && seg > 0) {
         // the loads this choice needs, issued together
         const bool last = p.fin && seg == p.P - 1;
@@ -1588,13 +1612,9 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             if (j0 < seg - 1) ein = own;
         }
     }
-    if (fast_ok) {
-        const float b0 = __builtin_bit_cast(
-            float, __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(kept + PRE_G + S::gGC + 4)));
-        if (b0 <= kExitLog) {
-            if constexpr (!LEAN) rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, tid);
-            return;
-        }
+    if (fast_ok && kept_bound() <= kExitLog) {
+        if constexpr (!LEAN) rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, tid, [] { return true; });
+        return;
     }
     // the first pass keeps its first chunk's prepared operands for the rerun (one copy per head)
     const bool keep = p.pre_mode == PRE_KEEP && seg > 0 && vb == 0;
