@@ -7,7 +7,8 @@ To keep the 256 MB Infinity Cache from serving the inputs, the timed loop rotate
 independent copies of the inputs (more than twice the cache in total).
 
 The JSON line reports prefill tokens/s as `value`, the HBM roofline of the prefill kernel
-(algorithmic bytes per launch / mean launch time from HIP events on the launch stream), the bf16
+(algorithmic bytes per call / mean call time, from one pair of HIP events on the launch stream
+around the timed region), the bf16
 MFMA fraction under algorithmic flop accounting, the decode step (256 sequences x 32 heads, state
 updated in place) as GB/s against HBM, the long-sequence prefill (1 x 262144 tokens, 16 heads,
 segmented) and the packed variable-length prefill with the conv prologue (64 sequences of
@@ -132,26 +133,30 @@ def main():
     copies = [base] + [[t.clone() for t in base] for _ in range(args.copies - 1)]
     outs = [(torch.empty((tokens, H, dv), dtype=torch.bfloat16, device=dev),
              torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)) for _ in copies]
+    # the segment workspace, allocated once as a caller would (the binding would otherwise
+    # allocate one per call)
+    ws = torch.empty(max(gdn.gdn_chunk_workspace_size(N, tokens, H, dk, dv), 16), dtype=torch.uint8, device=dev)
 
     def step(i):
         q, k, v, g, b, s0 = copies[i % len(copies)]
         o, sf = outs[i % len(outs)]
-        gdn.gdn_chunk_fwd(q, k, v, g, b, s0, N=N, o=o, final_state=sf, stream=stream)
+        gdn.gdn_chunk_fwd(q, k, v, g, b, s0, N=N, o=o, final_state=sf, workspace=ws, stream=stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # one pair of HIP events around the timed region on the launch stream: per-call events would
+    # add their own commands between the calls
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        evs[i][0].record(stream)
         step(i)
-        evs[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in evs]
     ms_per_step = wall * 1e3 / args.steps
-    mean_launch_s = sum(launch_ms) / len(launch_ms) * 1e-3
+    mean_launch_s = ev0.elapsed_time(ev1) / args.steps * 1e-3
 
     alg_bytes = prefill_alg_bytes(tokens, N, H, dk, dv)
     alg_flops = tokens * H * prefill_alg_flops_per_token_head(dk, dv)
@@ -228,7 +233,7 @@ def main():
         q, k, v, _, _, s0 = copies[0]
         o, sf = outs[0]
         rsec = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, ra, rb, s0, N=N, o=o, final_state=sf, gate_params=rgp,
-                                               stream=stream), 20)
+                                               workspace=ws, stream=stream), 20)
         extra["prefill_raw_gates"] = {
             "workload": "prefill B=4 T=4096 H=16 dk=dv=128 bf16, raw gate inputs a, b [T,H] fp32 + A_log, dt_bias [H]",
             "value": tokens / rsec, "unit": "tokens/s", "us": rsec * 1e6,
@@ -240,7 +245,8 @@ def main():
         gw = W.prefill(Hk=8)
         gq, gk, gv, gg, gb, gs0 = (to_dev(x) for x in (gw.q, gw.k, gw.v, gw.g, gw.beta, gw.s0))
         go, gsf = torch.empty_like(gv), torch.empty_like(gs0)
-        gsec = timed(lambda: gdn.gdn_chunk_fwd(gq, gk, gv, gg, gb, gs0, N=N, o=go, final_state=gsf, stream=stream), 20)
+        gsec = timed(lambda: gdn.gdn_chunk_fwd(gq, gk, gv, gg, gb, gs0, N=N, o=go, final_state=gsf, workspace=ws,
+                                               stream=stream), 20)
         gbytes = tokens * (gw.Hk * 2 * dk * 2 + H * (dv * 2 * 2 + 8)) + 2 * N * H * dv * dk * 4
         extra["prefill_grouped_heads"] = {
             "workload": "prefill B=4 T=4096, 16 value heads sharing 8 query/key heads, dk=dv=128 bf16",
@@ -248,14 +254,14 @@ def main():
             "hbm_alg_gbs": gbytes / gsec / 1e9, "hbm_frac": gbytes / gsec / 1e9 / HBM_PEAK_GBS}
         del gq, gk, gv, gg, gb, gs0, go, gsf, gw
 
-        # the prefill step followed by the output epilogue (zero-centred RMSNorm over dv, sigmoid
-        # output gate), one in-place pass over o
+        # the prefill step with the output epilogue (zero-centred RMSNorm over dv, sigmoid output
+        # gate), applied by the chunk kernel to its fp32 o
         ez = to_dev(W.f32_to_bf16_bits(np.random.default_rng([1, 77]).standard_normal((tokens, H, dv),
                                                                                       dtype=np.float32)))
         ew = to_dev(np.random.default_rng([1, 78]).normal(0.0, 0.2, size=dv).astype(np.float32))
         q, k, v, g, b, s0 = copies[0]
         esec = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, g, b, s0, N=N, o=o, final_state=sf, out_gate=ez,
-                                               norm_weight=ew, stream=stream), 20)
+                                               norm_weight=ew, workspace=ws, stream=stream), 20)
         ebytes = alg_bytes + tokens * H * dv * 2 + dv * 4
         extra["prefill_epilogue"] = {
             "workload": "prefill B=4 T=4096 H=16 dk=dv=128 bf16 + output epilogue (RMSNorm over dv, sigmoid gate z "
