@@ -9,9 +9,11 @@
 // The second line is o = S_new q expanded, so S is read once and written once.
 //
 // HBM-bound: 2 * dv * dk * 4 bytes of state traffic per (n, h) against 2 * dv * dk * 3 flops.
-// Layout: one workgroup (256 lanes) per (n, h).  A row of dk fp32 is dk/4 lanes x float4, so
-// each load instruction of a wavefront covers whole contiguous rows; all ROWS_PER_LANE row
-// loads of a lane are issued before the first use (many KB in flight per CU).  Row dot
+// Layout: one workgroup per (n, h), of step_threads lanes (1024 for dk = dv = 128: many waves with
+// few loads each keep HBM busier than few waves with many; 173 us against 189 us with 256 lanes
+// on the 256 x 32-head decode).  A row of dk fp32 is dk/4 lanes x float4, so each load
+// instruction of a wavefront covers whole contiguous rows; all of a lane's row loads are issued
+// before the first use.  Row dot
 // products reduce over the dk/4 lanes of a row with DPP/swizzle moves.  State loads and
 // stores are non-temporal: each state byte is touched once per step.
 #include "common.hpp"
@@ -19,6 +21,12 @@
 #include "prologue.hpp"
 
 namespace gdn {
+
+// lanes per workgroup: up to 1024, and no more than one float4 of the state per lane per pass
+template <int DK, int DV>
+constexpr int step_threads() {
+    return 1024 < DV * (DK / 4) ? 1024 : DV * (DK / 4);
+}
 
 // Conv prologue of one decode token (page maplevalley.com.cn/news/1910399, section 3.1, 卷积预处理):
 // channel i of the (n, h) pair's 2 DK + DV channels (q and k of its query/key head hk, then v)
@@ -36,7 +44,7 @@ __device__ __forceinline__ void conv_token(const T* q, const T* k, const T* v, c
     const int n = nh / H, h = nh % H, hk = h / (H / Hk);
     const size_t nk = (size_t)n * Hk + hk;
     T* hs = conv_state + (size_t)n * 3 * CC;
-    for (int i = tid; i < 2 * DK + DV; i += 256) {
+    for (int i = tid; i < 2 * DK + DV; i += step_threads<DK, DV>()) {
         size_t c;
         float x;
         if (i < DK) {
@@ -70,7 +78,7 @@ __device__ __forceinline__ void conv_token(const T* q, const T* k, const T* v, c
 // whole row, so the epilogue costs no extra pass over o.
 // At least 4 waves per SIMD (at most 128 VGPRs): the state streams through at full occupancy.
 template <int DK, int DV, typename T, bool CONV, bool NORM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__((step_threads<DK, DV>())) __attribute__((amdgpu_waves_per_eu(4))) void step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, const float* __restrict__ g,
                                                    const float* __restrict__ beta, const float* __restrict__ gate_params,
                                                    float* __restrict__ state, const float* __restrict__ conv_w,
@@ -78,12 +86,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
                                                    const float* __restrict__ norm_weight, T* __restrict__ o, int H,
                                                    int Hk, float scale, float norm_eps, int l2norm) {
     constexpr int LPR = DK / 4;             // lanes per state row
-    constexpr int RPP = 256 / LPR;          // rows per pass of the workgroup
+    constexpr int NTH = step_threads<DK, DV>();
+    constexpr int RPP = NTH / LPR;          // rows per pass of the workgroup
     constexpr int RPL = DV / RPP > 0 ? DV / RPP : 1;  // rows per lane
     static_assert(DV % RPP == 0 && RPP <= DV, "row tiling: every lane owns rows (no lane leaves early)");
     __shared__ float xs[CONV ? 2 * DK + DV : 1];
     __shared__ float xo[NORM ? DV : 1];     // the output row before the epilogue
-    __shared__ float red[NORM ? 4 : 1];     // per-wave sums of squares
+    __shared__ float red[NORM ? NTH / 64 : 1];  // per-wave sums of squares
     const int nh = blockIdx.x;
     const int tid = threadIdx.x;
     const int c = tid % LPR;        // float4 column of this lane
@@ -165,14 +174,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
         if (tid % 64 == 0) red[tid / 64] = ss;
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
-        const float inv = rsqrtf((red[0] + red[1] + red[2] + red[3]) * (1.f / DV) + norm_eps);
+        float rs = 0.f;
+#pragma unroll
+        for (int w = 0; w < NTH / 64; ++w) rs += red[w];
+        const float inv = rsqrtf(rs * (1.f / DV) + norm_eps);
         if (tid < DV) store1(o + (size_t)nh * DV + tid, x * inv * (1.f + wo) / (1.f + expf(-zo)));
     }
 }
 
 template <int DK, int DV, typename T, bool CONV, bool NORM>
 static hipError_t launch_step_v(const StepArgs& a) {
-    hipLaunchKernelGGL((step_kernel<DK, DV, T, CONV, NORM>), dim3(a.N * a.H), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((step_kernel<DK, DV, T, CONV, NORM>), dim3(a.N * a.H), dim3(step_threads<DK, DV>()), 0, a.stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.g, a.beta,
                        a.gate_params, a.state, a.conv_w, static_cast<T*>(a.conv_state),
                        static_cast<const T*>(a.out_gate), a.norm_weight, static_cast<T*>(a.o), a.H, a.Hk, a.scale,
