@@ -44,7 +44,7 @@ def test_prefill_no_l2norm(dtype, dk, dv):
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64)])
 def test_prefill_no_l2norm_segments(dk, dv):
-    """Forced segments without the norm: every transition, combine product and rerun runs in full."""
+    """Forced segments without the norm: every transition, entering-state chain and rerun runs in full."""
     wl = _prepare(W.make("nonorm_seg", seed=710 + dv, N=1, T=1000, H=2, dk=dk, dv=dv, dtype="bf16", s0_std=0.02))
     o, s = TL.run_gpu(wl, l2norm=False, segments=3)
     o_ref, s_ref = TL.run_oracle(wl, l2norm=False)

@@ -136,7 +136,7 @@ def test_bf16_segments_forced(segs, dv):
 
 
 def test_bf16_segments_slow_decay_mixed():
-    """Head 0 decays slowly (g = -1e-3: full transitions A_p, full corrections, combine products);
+    """Head 0 decays slowly (g = -1e-3: full transitions A_p, full reruns, chained entering states);
     heads 1, 2 keep the workload gates (negligible transitions).  No initial state passed."""
     wl = W.make("seg_slow", seed=47, N=1, T=1024, H=3, dk=128, dv=128, dtype="bf16")
     wl.g[:, 0] = -1e-3
