@@ -132,6 +132,21 @@ def test_workspace_segments_flag(lib):
     assert n.value > 0
 
 
+def test_workspace_segments_layout(lib):
+    """The segmented path's workspace: per (sequence, segment, head) the end state B_p, the
+    transition A_p, its mark, the first chunk's kept operands (19,776 bytes) and the chained
+    entering state, each region rounded up to 256 bytes."""
+    n = ctypes.c_size_t(0)
+    seg = lambda p: (p & 0xFF) << 8
+    a256 = lambda x: (x + 255) // 256 * 256
+    for N, H, dk, dv, P in ((2, 2, 64, 32, 4), (1, 16, 128, 128, 16), (3, 5, 32, 64, 3)):
+        assert lib.gdn_chunk_workspace_size(N, N * 64 * P, H, H, dk, dv, 1, 64, 0, 0, 1 | seg(P), ctypes.byref(n)) == 0
+        units = N * P * H
+        want = (a256(units * dv * dk * 4) + a256(units * dk * dk * 4) + a256(units * 4) + a256(units * 19776)
+                + a256(units * dv * dk * 4))
+        assert n.value == want, (N, H, dk, dv, P, n.value, want)
+
+
 def test_workspace_size_validation(lib):
     n = ctypes.c_size_t(0)
     assert lib.gdn_chunk_workspace_size(1, 64, 1, 1, 33, 32, 1, 64, 0, 0, 1, ctypes.byref(n)) == gdn.GDN_ERR_UNSUPPORTED
