@@ -267,7 +267,8 @@ struct Params {
     int Hk, grp;   // query/key heads; value heads per query/key head (H = Hk grp)
     int P;         // segments per sequence (1 = the sequence in one piece)
     int init;      // InitMode: S0 = s0[n] for segment 0 and zero for the others; IDENTITY = I
-                   // (dv = dk rows); PREV = s0[(n P + p - 1) H + h], the state entering segment p
+                   // (dv = dk rows); PREV = the state entering segment p: s0[(n P + p - 1) H + h]
+                   // (B_{p-1}) where A_{p-1} is negligible, else the chain formed in place (ein)
     int out;       // OutMode: o stored, or not written
     int v_zero;    // values taken as zero (v is not read)
     int early_exit;  // stop once the product of the decays since the start is <= 2^-40
@@ -277,7 +278,7 @@ struct Params {
     unsigned char* pre;  // per (segment, head): the first chunk's prepared operands [PRE_BYTES]
     int pre_mode;        // PreMode
     // rerun of the segmented path: the state entering segment p is formed here from the end
-    // states B_j (s0), the transitions A_j and their marks (1 = negligible)
+    // states B_j (s0), the transitions A_j and their marks (nonzero = negligible)
     const int* marks;     // [N*P, H], or null (no chaining)
     const float* trans;   // A_j [N*P, H, DK, DK]
     float* ein;           // per (segment, head): the entering state where it had to be chained
