@@ -125,7 +125,9 @@ extern "C" {
  *                                      place ("Conv state" above); requires conv_w.  Must not
  *                                      overlap any other buffer.
  *  out_gate    [T_tot, H, dv]  dtype   NULL, or z of the output epilogue (above); with norm_weight
- *  norm_weight [dv]            fp32    NULL, or w of the output epilogue; with out_gate
+ *  norm_weight [dv]            fp32    NULL, or w of the output epilogue; with out_gate.  When
+ *                                      T_tot = 0 either may be NULL alone (nothing to gate) and
+ *                                      neither is read.
  *  o           [T_tot, H, dv]  dtype   output; must not alias any input
  *  final_state [N, H, dv, dk] fp32     last state per (sequence, head), or NULL = not written.
  *                                      May alias initial_state exactly (same pointer).

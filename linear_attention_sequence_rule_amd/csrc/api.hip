@@ -104,8 +104,10 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     if (!cu_seqlens && T_tot % N != 0) return GDN_ERR_INVALID_ARG;
     if (T_tot > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_INVALID_ARG;
     if (conv_state && !conv_w) return GDN_ERR_INVALID_ARG;
-    if ((out_gate == nullptr) != (norm_weight == nullptr)) return GDN_ERR_INVALID_ARG;
+    // with no token there is no output to gate: out_gate (an empty tensor) may then be NULL alone
+    if (T_tot > 0 && (out_gate == nullptr) != (norm_weight == nullptr)) return GDN_ERR_INVALID_ARG;
     if (out_gate && !(isfinite(norm_eps) && norm_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+    if (T_tot == 0) out_gate = norm_weight = nullptr;
     const void* ptrs[] = {q, k, v, g, beta, gate_params, initial_state, cu_seqlens, conv_w, conv_state, out_gate,
                           norm_weight, o, final_state};
     for (const void* p : ptrs)
