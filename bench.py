@@ -73,6 +73,74 @@ def load_traffic(kernel_tag):
     return rec["bytes_per_launch"]
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl):
+    """The fp64 oracle timed on this host's cores: the prefill workload on all cores (the headline
+    baseline) and on one thread, and bounded samples of the long, decode and varlen workloads."""
+    import numpy as np
+    import oracle
+    from linear_attention_sequence_rule_amd import workloads as W
+
+    def fwd(w, nthreads=0, pairs=None):
+        cu = np.concatenate([[0], np.cumsum(w.lengths)])
+        t = time.perf_counter()
+        _, _, used = oracle.forward(w.as_float("q"), w.as_float("k"), w.as_float("v"), w.g, w.beta, w.s0, cu,
+                                    w.conv_w, nthreads=nthreads, pairs=pairs)
+        return time.perf_counter() - t, int(used)
+
+    tokens = wl.T_tot
+    all_s, used = fwd(wl)
+    # one thread: the first sequence's 16 heads (a quarter of the prefill workload's chains)
+    one = [(0, h) for h in range(wl.H)]
+    one_s, _ = fwd(wl, nthreads=1, pairs=one)
+    one_tok = int(wl.lengths[0])  # the sequence's tokens, every head
+    extra = {}
+    # long prefill: all 16 heads (262144 tokens each), all cores
+    lw = W.long_prefill()
+    ls, lu = fwd(lw)
+    extra["long_prefill"] = {"value": lw.T_tot / ls, "unit": "tokens/s", "cores": lu, "seconds": ls,
+                             "sample": "the whole workload (1 x 262144 tokens, 16 heads)"}
+    del lw
+    # decode: the whole step (256 x 32 chains of one token), all cores and one thread
+    dw = W.decode()
+    t = time.perf_counter()
+    oracle.step(dw.as_float("q"), dw.as_float("k"), dw.as_float("v"), dw.g, dw.beta, dw.state)
+    ds = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.step(dw.as_float("q"), dw.as_float("k"), dw.as_float("v"), dw.g, dw.beta, dw.state, nthreads=1)
+    d1 = time.perf_counter() - t
+    dbytes = decode_alg_bytes(dw.N, dw.H, dw.dk, dw.dv)
+    extra["decode"] = {"value": dbytes / ds / 1e9, "unit": "GB/s", "seconds": ds, "one_thread_seconds": d1,
+                       "one_thread_value": dbytes / d1 / 1e9,
+                       "sample": "the whole step (256 sequences x 32 heads, fp64 state copy included)"}
+    del dw
+    # varlen: the 16 shortest-index sequences (a quarter of the 64), every head, conv prologue
+    vw = W.varlen()
+    vs = list(range(16))
+    vpairs = [(n, h) for n in vs for h in range(vw.H)]
+    vsec, vu = fwd(vw, pairs=vpairs)
+    vtok = int(np.sum(vw.lengths[vs]))
+    extra["varlen"] = {"value": vtok / vsec, "unit": "tokens/s", "cores": vu, "seconds": vsec,
+                       "sample": "sequences 0..15 of the 64 (%d tokens), all 32 heads, conv + SiLU" % vtok}
+    del vw
+    return {"value": tokens / all_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": "the whole prefill workload (4 x 4096 tokens, 16 heads), fp64 token-by-token recurrence, "
+                      "threads over (sequence, head) chains; %.2f s" % all_s,
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "one_thread": {"value": one_tok / one_s, "unit": "tokens/s", "cores": 1, "seconds": one_s,
+                           "sample": "sequence 0 of the prefill workload (4096 tokens x 16 heads) on one thread"},
+            "workloads": extra}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,24 +213,40 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # one pair of HIP events around the timed region on the launch stream: per-call events would
-    # add their own commands between the calls
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the clocks come up only after tens of milliseconds of work: at least 50 ms of untimed calls
+    # after the warm-up, whatever --warmup says
+    n_settle = [args.warmup]
+
+    def settle_step():
+        step(n_settle[0])
+        n_settle[0] += 1
+    settle(settle_step)
+    # the K timed calls in groups of G consecutive calls, each group between two HIP events on the
+    # launch stream (an event between every pair of calls would add its own command to each call);
+    # the step time is the median over the groups of the per-call mean
+    G = max(1, args.steps // 10)
+    groups = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range((args.steps + G - 1) // G)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
+    i = 0
+    for a, b in groups:
+        a.record(stream)
+        for _ in range(min(G, args.steps - i)):
+            step(n_settle[0] + i)
+            i += 1
+        b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    mean_launch_s = ev0.elapsed_time(ev1) / args.steps * 1e-3
+    wall_per_step = (time.perf_counter() - t0) / args.steps
+    per_call = sorted(a.elapsed_time(b) * 1e-3 / min(G, args.steps - G * j) for j, (a, b) in enumerate(groups))
+    m = len(per_call)
+    median_s = per_call[m // 2] if m % 2 else 0.5 * (per_call[m // 2 - 1] + per_call[m // 2])
+    ms_per_step = median_s * 1e3
 
     alg_bytes = prefill_alg_bytes(tokens, N, H, dk, dv)
     alg_flops = tokens * H * prefill_alg_flops_per_token_head(dk, dv)
-    gbs = alg_bytes / mean_launch_s / 1e9
-    tflops = alg_flops / mean_launch_s / 1e12
-    value = tokens / (ms_per_step * 1e-3)
+    gbs = alg_bytes / median_s / 1e9
+    tflops = alg_flops / median_s / 1e12
+    value = tokens / median_s
 
     # ---------------------------------------------------------------- decode
     dw = W.decode()
@@ -270,6 +354,19 @@ def main():
             "hbm_alg_gbs": ebytes / esec / 1e9, "hbm_frac": ebytes / esec / 1e9 / HBM_PEAK_GBS}
         del ez, ew
 
+        # the prefill step with slow decay everywhere (g = -1e-3, beta as drawn): no segment transition
+        # is negligible, so every pass of the segmented path covers whole segments -- its worst case
+        sg = torch.full_like(copies[0][3], -1e-3)
+        q, k, v, _, b, s0 = copies[0]
+        ssec = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, sg, b, s0, N=N, o=o, final_state=sf, workspace=ws,
+                                               stream=stream), 20)
+        extra["prefill_slow_decay"] = {
+            "workload": "prefill B=4 T=4096 H=16 dk=dv=128 bf16 with g = -1e-3 for every token (full segment "
+                        "transitions and reruns)",
+            "value": tokens / ssec, "unit": "tokens/s", "us": ssec * 1e6,
+            "hbm_alg_gbs": alg_bytes / ssec / 1e9, "hbm_frac": alg_bytes / ssec / 1e9 / HBM_PEAK_GBS}
+        del sg
+
         # the decode step with the conv prologue on the raw token (history in a conv state updated in
         # place) and raw gates: the decode side of a layer whose prefill ran the conv
         cw, hist = W.conv_inputs(3, dw.N, dw.H, dw.dk, dw.dv, "bf16")
@@ -300,15 +397,7 @@ def main():
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        cu = np.concatenate([[0], np.cumsum(wl.lengths)])
-        qf, kf, vf = wl.as_float("q"), wl.as_float("k"), wl.as_float("v")
-        t1 = time.perf_counter()
-        _, _, used = oracle.forward(qf, kf, vf, wl.g, wl.beta, wl.s0, cu, None)
-        cpu_s = time.perf_counter() - t1
-        cpu = {"value": tokens / cpu_s, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
-               "sample": "the whole prefill workload (4 x 4096 tokens, 16 heads), fp64 token-by-token "
-                         "recurrence, threads over (sequence, head) chains; %.2f s" % cpu_s}
+        cpu = cpu_baseline(wl)
 
     out = {
         "metric": "GDN chunked-prefill tokens/s (+% bf16 MFMA peak); decode-step GB/s (+% HBM)",
@@ -329,7 +418,9 @@ def main():
                      "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic("chunk_bf16_kernel")},
         "mfma": {"achieved_tflops_alg": tflops, "peak": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS,
                  "flops_per_token_head": prefill_alg_flops_per_token_head(dk, dv)},
-        "prefill_kernel_us": mean_launch_s * 1e6,
+        "prefill_call_us": median_s * 1e6,
+        "prefill_timing": "median over %d groups of %d consecutive calls (HIP events on the launch stream) of the "
+                          "per-call mean; host wall clock %.1f us per call" % (len(groups), G, wall_per_step * 1e6),
         "decode": {"workload": "decode 256 sequences x 32 heads, dk=dv=128, bf16 tokens, fp32 state in place",
                    "value": dec_gbs, "unit": "GB/s", "us_per_step": dec_s * 1e6,
                    "tokens_per_s": dw.N / dec_s,

@@ -101,6 +101,18 @@ def _check_dev(name, t, dtype=None):
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
+def _check_shape(name, t, shape):
+    """Raise ValueError unless tensor t (when given) has exactly this shape: the C ABI cannot see
+    device buffer sizes, so a short buffer would be read or written out of bounds."""
+    if t is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(int(x) for x in shape), tuple(t.shape)))
+
+
+def _check_rank(name, t, rank):
+    if t.dim() != rank:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, rank, tuple(t.shape)))
+
+
 def gdn_chunk_workspace_size(N, T_tot, H, dk, dv, dtype=GDN_BF16, chunk=64, has_cu_seqlens=False, has_conv=False,
                              flags=GDN_QK_L2NORM, Hk=None) -> int:
     n = ctypes.c_size_t(0)
@@ -127,11 +139,30 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=
     A workspace (uint8 device tensor) is allocated here when the call needs one and none large
     enough is given.  Returns (o, final_state or None)."""
     import torch
-    lib = load_library()
+    _check_rank("q", q, 3)
+    _check_rank("v", v, 3)
     T_tot, Hk, dk = q.shape
     H, dv = v.shape[1], v.shape[2]
-    if tuple(k.shape) != tuple(q.shape):
-        raise ValueError("k must have the shape of q")
+    if cu_seqlens is not None:
+        _check_rank("cu_seqlens", cu_seqlens, 1)
+        N = cu_seqlens.shape[0] - 1
+    elif N is None:
+        N = initial_state.shape[0] if initial_state is not None else 1
+    # every shape against the header's, before anything reaches the library
+    _check_shape("k", k, (T_tot, Hk, dk))
+    _check_shape("v", v, (T_tot, H, dv))
+    _check_shape("g", g, (T_tot, H))
+    _check_shape("beta", beta, (T_tot, H))
+    _check_shape("gate_params", gate_params, (2, H))
+    _check_shape("initial_state", initial_state, (N, H, dv, dk))
+    _check_shape("final_state", final_state, (N, H, dv, dk))
+    _check_shape("o", o, (T_tot, H, dv))
+    cc = 2 * Hk * dk + H * dv
+    _check_shape("conv_w", conv_w, (cc, 4))
+    _check_shape("conv_state", conv_state, (N, 3, cc))
+    _check_shape("out_gate", out_gate, (T_tot, H, dv))
+    _check_shape("norm_weight", norm_weight, (dv,))
+    lib = load_library()
     dt = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("conv_state", conv_state), ("out_gate", out_gate)):
         _check_dev(name, t, q.dtype)
@@ -139,10 +170,6 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=
                     ("conv_w", conv_w), ("final_state", final_state), ("norm_weight", norm_weight)):
         _check_dev(name, t, torch.float32)
     _check_dev("cu_seqlens", cu_seqlens, torch.int32)
-    if cu_seqlens is not None:
-        N = cu_seqlens.shape[0] - 1
-    elif N is None:
-        N = initial_state.shape[0] if initial_state is not None else 1
     if o is None:
         o = torch.empty((T_tot, H, dv), dtype=q.dtype, device=q.device)
     _check_dev("o", o, q.dtype)
@@ -172,11 +199,23 @@ def gdn_recurrent_step(q, k, v, g, beta, state, *, o=None, scale=1.0, l2norm=Tru
     neither; out_gate [N, H, dv] with norm_weight [dv]: the output epilogue, as for gdn_chunk_fwd.
     Returns o [N, H, dv]."""
     import torch
-    lib = load_library()
+    _check_rank("q", q, 3)
+    _check_rank("v", v, 3)
     N, Hk, dk = q.shape
     H, dv = v.shape[1], v.shape[2]
-    if tuple(k.shape) != tuple(q.shape):
-        raise ValueError("k must have the shape of q")
+    _check_shape("k", k, (N, Hk, dk))
+    _check_shape("v", v, (N, H, dv))
+    _check_shape("g", g, (N, H))
+    _check_shape("beta", beta, (N, H))
+    _check_shape("gate_params", gate_params, (2, H))
+    _check_shape("state", state, (N, H, dv, dk))
+    _check_shape("o", o, (N, H, dv))
+    cc = 2 * Hk * dk + H * dv
+    _check_shape("conv_w", conv_w, (cc, 4))
+    _check_shape("conv_state", conv_state, (N, 3, cc))
+    _check_shape("out_gate", out_gate, (N, H, dv))
+    _check_shape("norm_weight", norm_weight, (dv,))
+    lib = load_library()
     dt = _dtype_code(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("conv_state", conv_state), ("out_gate", out_gate)):
         _check_dev(name, t, q.dtype)

@@ -179,6 +179,17 @@ __device__ __forceinline__ bf16x8 pack_chain(fx4 a, fx4 b) {
     r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
     return r;
 }
+// The bf16 rounding residuals of pack_chain(a, b) = hi: a + b - hi in bf16, so that hi + lo carries
+// the fp32 values to about 16 significant bits.
+__device__ __forceinline__ bf16x8 pack_chain_lo(fx4 a, fx4 b, bf16x8 hi) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = (__bf16)(a[e] - (float)hi[e]);
+        r[4 + e] = (__bf16)(b[e] - (float)hi[4 + e]);
+    }
+    return r;
+}
 __device__ __forceinline__ float sel4(fx4 v, int e) {
     return e == 0 ? v[0] : (e == 1 ? v[1] : (e == 2 ? v[2] : v[3]));
 }
@@ -285,6 +296,10 @@ struct Params {
     float* fin;           // the final state [N, H, dv, DK], or null: the first pass stores B_{P-1} there
                           // (not in its slot of s0), which is E_{P-1} where A_{P-1} is negligible; the
                           // rerun of the last segment chains E_{P-1} over it otherwise
+    int fin_in_slot;      // the final state is the initial state's buffer (read by the first pass's
+                          // segment 0 while the last segment would write it): the first pass then
+                          // keeps B_{P-1} in its slot of s0 and the rerun of the last segment always
+                          // writes the final state (a copy of B_{P-1} where A_{P-1} is negligible)
     float scale;
     int l2norm;
 };
@@ -1034,10 +1049,13 @@ __device__ __forceinline__ void row_A(RowRegs<DK>& st, unsigned char* sm, const 
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[t][e] = bm[t][e] * (float)vv[t][e] - kk[t][e] * ks_acc[t][e];
 
-    const bf16x8 xa = pack_chain(x[0], x[1]);
+    // X enters the solve as a bf16 pair (hi + lo): the value path V -> X -> U' -> O otherwise
+    // rounds the rows that dominate their own outputs twice more to bf16 (each about 2^-9 of the
+    // row), which with large convolved values comes close to the o tolerance
+    const bf16x8 xa = pack_chain(x[0], x[1]), xal = pack_chain_lo(x[0], x[1], xa);
     fx4 u[4];
-    u[0] = mfma(ta0, xa, zero4());
-    u[1] = mfma(ta1, xa, zero4());
+    u[0] = mfma(ta0, xal, mfma(ta0, xa, zero4()));
+    u[1] = mfma(ta1, xal, mfma(ta1, xa, zero4()));
     st.ub[0] = pack_chain(u[0], u[1]);
     const fx4 y2 = mfma(la2, st.ub[0], zero4()), y3 = mfma(la3, st.ub[0], zero4());
 #pragma unroll
@@ -1045,9 +1063,9 @@ __device__ __forceinline__ void row_A(RowRegs<DK>& st, unsigned char* sm, const 
         x[2][e] -= y2[e];
         x[3][e] -= y3[e];
     }
-    const bf16x8 xb = pack_chain(x[2], x[3]);
-    u[2] = mfma(tb2, xb, zero4());
-    u[3] = mfma(tb3, xb, zero4());
+    const bf16x8 xb = pack_chain(x[2], x[3]), xbl = pack_chain_lo(x[2], x[3], xb);
+    u[2] = mfma(tb2, xbl, mfma(tb2, xb, zero4()));
+    u[3] = mfma(tb3, xbl, mfma(tb3, xb, zero4()));
     st.ub[1] = pack_chain(u[2], u[3]);
 
     fx4 ut[4];
@@ -1352,7 +1370,8 @@ __device__ void chain_states(const Params<DK>& p, unsigned char* sm, int n, int 
     };
     // B_j (B_{P-1} is in the final state's place, see Params::fin)
     auto bj = [&](int j) {
-        return p.fin && j == p.P - 1 ? p.fin + ((size_t)n * p.H + h) * p.dv * DK : p.s0 + slot(j) * p.dv * DK;
+        return p.fin && !p.fin_in_slot && j == p.P - 1 ? p.fin + ((size_t)n * p.H + h) * p.dv * DK
+                                                         : p.s0 + slot(j) * p.dv * DK;
     };
     fx4 E[DT];
     int lazy = j0;  // E_lazy = B_lazy, not yet loaded (-1: E is in the registers)
@@ -1588,7 +1607,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         if (fast_ok && p.marks) {
             auto usual = [&]() {
                 const int mprev = p.marks[(size_t)(n * p.P + seg - 1) * p.H + h];
-                const int mlast = p.fin && seg == p.P - 1 ? p.marks[pair] : 1;
+                const int mlast = p.fin && seg == p.P - 1 ? (p.fin_in_slot ? 0 : p.marks[pair]) : 1;
                 const float b0 = kept_bound();
                 return (seg == 1 || mprev != 0) && mlast != 0 && b0 <= kExitLog;
             };
@@ -1599,12 +1618,14 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         // the loads this choice needs, issued together
         const bool last = p.fin && seg == p.P - 1;
         const int mprev = p.marks[(size_t)(n * p.P + seg - 1) * p.H + h];
-        const int mlast = last ? p.marks[pair] : 1;
+        const int mlast = last ? (p.fin_in_slot ? 0 : p.marks[pair]) : 1;
         int j0 = seg - 1;
         if (j0 > 0 && !mprev)
             do --j0;
             while (j0 > 0 && !p.marks[(size_t)(n * p.P + j0) * p.H + h]);
         const bool fin = mlast == 0;  // else B_{P-1}, in place, is the final state
+        // (with fin_in_slot the chain to the final state runs even where A_{P-1} is negligible:
+        // it then copies B_{P-1} from its slot)
         if (j0 < seg - 1 || fin) {
             float* own = p.ein + (size_t)pair * p.dv * DK;
             if constexpr (!LEAN)
@@ -1797,7 +1818,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                                   reinterpret_cast<const __bf16*>(sm + S::qv(pend) + S::rQ));
         if (is_row && p.sfin) {
             // first pass, last segment: B_{P-1} into the final state (see Params::fin)
-            float* dst = (p.fin && seg == p.P - 1 ? p.fin + ((size_t)n * p.H + h) * p.dv * DK
+            float* dst = (p.fin && !p.fin_in_slot && seg == p.P - 1 ? p.fin + ((size_t)n * p.H + h) * p.dv * DK
                                                   : p.sfin + (size_t)pair * p.dv * DK) +
                          (size_t)row * DK;
 #pragma unroll
@@ -1914,6 +1935,7 @@ struct Pass {
     const float* trans;
     float* ein;
     float* fin;
+    int fin_in_slot;
 };
 
 template <int DK, int BV>
@@ -1952,6 +1974,7 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     p.trans = c.trans;
     p.ein = c.ein;
     p.fin = c.fin;
+    p.fin_in_slot = c.fin_in_slot;
     p.scale = a.scale;
     p.l2norm = a.l2norm;
     // the output epilogue in the kernel: wide workgroups of a pass that stores o
@@ -2008,14 +2031,20 @@ hipError_t run(const ChunkArgs& a, int P) {
     // the kept operands serve only a rerun that stops early and has no conv inside the kernel
     const bool keep = ex && !a.conv_w;
     unsigned char* pre = keep ? ws + L.off_pre : nullptr;
+    // final_state == initial_state: segment 0 of the first pass reads the initial state while its
+    // last segment would write B_{P-1} to the same buffer in the same launch, in no guaranteed
+    // order.  B_{P-1} then stays in its slot and the rerun (after the first pass has finished
+    // reading the initial state) writes the final state.
+    const int in_slot = a.sfin && a.sfin == a.s0 ? 1 : 0;
     hipError_t e = launch_rows<DK>(a, Pass{P, INIT_S0, OUT_STORE, 0, 0, 0, NEGL_MARK, a.dv, a.s0, E, negl, pre,
-                                           keep ? PRE_KEEP : PRE_NONE, nullptr, nullptr, nullptr, a.sfin});
+                                           keep ? PRE_KEEP : PRE_NONE, nullptr, nullptr, nullptr,
+                                           in_slot ? nullptr : a.sfin, 0});
     if (e == hipSuccess)
         e = launch_rows<DK>(a, Pass{P, INIT_IDENTITY, OUT_NONE, 1, ex, 1, NEGL_SKIP, a.dk, nullptr, A, negl});
     if (e == hipSuccess)
         e = launch_rows<DK>(a, Pass{P, INIT_PREV, OUT_STORE, 0, ex, 1, NEGL_NONE, a.dv, E, nullptr, nullptr, pre,
                                     keep ? PRE_USE : PRE_NONE, negl, A, reinterpret_cast<float*>(ws + L.off_ein),
-                                    a.sfin});
+                                    a.sfin, in_slot});
     return e;
 }
 

@@ -86,14 +86,18 @@ def compare(wl, o_gpu, s_gpu, o_ref, s_ref, pairs=None, f32=None):
     f32 = (wl.dtype == "f32") if f32 is None else f32
     if pairs is None:
         pairs = wl.pairs()
-    errs = {"o_abs": 0.0, "o_ref_max": 0.0, "s_relF_worst": 0.0, "s_abs": 0.0, "s_ref_max": 0.0}
+    errs = {"o_abs": 0.0, "o_ref_max": 0.0, "s_relF_worst": 0.0, "s_abs": 0.0, "s_ref_max": 0.0,
+            "o_worst_pair": None, "s_worst_pair": None}
     s_num = s_den = 0.0
     for n, h in pairs:
         rows, hh = pair_rows(wl, n, h)
         a, b = o_gpu[rows, hh], o_ref[rows, hh]
         assert np.all(np.isfinite(a)), "non-finite o at pair %s" % ((n, h),)
         if a.size:
-            errs["o_abs"] = max(errs["o_abs"], float(np.abs(a - b).max()))
+            oe = float(np.abs(a - b).max())
+            if errs["o_worst_pair"] is None or oe > errs["o_abs"]:
+                errs["o_worst_pair"] = (int(n), int(h))
+            errs["o_abs"] = max(errs["o_abs"], oe)
             errs["o_ref_max"] = max(errs["o_ref_max"], float(np.abs(b).max()))
         if s_gpu is not None:
             sa, sb = s_gpu[n, h], s_ref[n, h]
@@ -102,6 +106,8 @@ def compare(wl, o_gpu, s_gpu, o_ref, s_ref, pairs=None, f32=None):
             r = float(np.linalg.norm(sb))
             s_num += d * d
             s_den += r * r
+            if errs["s_worst_pair"] is None or d / max(r, 1e-30) > errs["s_relF_worst"]:
+                errs["s_worst_pair"] = (int(n), int(h))
             errs["s_relF_worst"] = max(errs["s_relF_worst"], d / max(r, 1e-30))
             errs["s_abs"] = max(errs["s_abs"], float(np.abs(sa - sb).max()))
             errs["s_ref_max"] = max(errs["s_ref_max"], float(np.abs(sb).max()))

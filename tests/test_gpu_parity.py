@@ -1,8 +1,7 @@
 """Parity of the HIP path (through the C ABI) against the fp64 oracle on identical seeded inputs.
 
-Sizes span several 64-token chunks and ragged tails; the named workloads run at full size where
-the oracle finishes in seconds, and on sampled (sequence, head) chains otherwise (chains are
-independent, so a sampled chain is checked exactly as in a full run).
+Sizes span several 64-token chunks and ragged tails; the named workloads run at full size (the long
+prefill and the varlen workload, every chain of each, in test_gpu_full_workloads.py).
 """
 import numpy as np
 import pytest
@@ -163,38 +162,6 @@ def test_bf16_segments_without_final_state():
     assert s is None
     o_ref, _ = TL.run_oracle(wl)
     TL.compare(wl, o, None, o_ref, None)
-
-
-def test_long_prefill_workload_sampled():
-    """B=1, T=262144, H=16, d=128, bf16, zero initial state: the automatic segmented path at full
-    size, every output and final state of three sampled heads checked against the oracle."""
-    import torch
-    from linear_attention_sequence_rule_amd import gdn_chunk_workspace_size
-    wl = W.long_prefill()
-    need = gdn_chunk_workspace_size(wl.N, wl.T_tot, wl.H, wl.dk, wl.dv, has_cu_seqlens=False)
-    _flush("long prefill workspace %d bytes" % need)
-    o, s = TL.run_gpu(wl)
-    heads = [0, 7, 15]
-    sub = TL.head_slice(wl, heads)
-    o_ref, s_ref = TL.run_oracle(sub)
-    e = TL.compare(sub, o[:, heads], s[:, heads], o_ref, s_ref)
-    _flush("long prefill sampled heads %s %s" % (heads, e))
-
-
-def test_varlen_workload_sampled():
-    """64 sequences, lengths ~U{512..16384}, H=32, d=128, bf16, conv + SiLU, per-sequence initial
-    states, seed 4: the whole workload on the GPU; 3 heads x 6 sequences (shortest, longest and
-    four others) checked against the oracle."""
-    wl = W.varlen()
-    o, s = TL.run_gpu(wl)
-    heads = [0, 13, 31]
-    order = np.argsort(wl.lengths)
-    seqs = sorted({int(order[0]), int(order[-1]), 5, 17, 40, 63})
-    sub = TL.head_slice(wl, heads)
-    pairs = [(n, j) for n in seqs for j in range(len(heads))]
-    o_ref, s_ref = TL.run_oracle(sub, pairs=pairs)
-    e = TL.compare(sub, o[:, heads], s[:, heads], o_ref, s_ref, pairs=pairs)
-    _flush("varlen sampled %s" % e)
 
 
 # ----------------------------------------------------------------------------------- decode
