@@ -79,6 +79,15 @@ __device__ __forceinline__ int opaque(int x) {
 // Keep every instruction before this point (typically a batch of LDS operand reads) ahead of
 // everything after it: with one wavefront per SIMD the reads must be in flight early.
 __device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+// Make this wave's LDS writes visible to its other lanes.  The hardware runs a wave's LDS
+// accesses in order, but the compiler models every lane as a thread of its own: without a
+// synchronising operation it may treat a lane's read of another lane's write as a race and, for
+// instance, forward the lane's own stored value instead of reading LDS.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Swizzled row-major tile of R rows x W bf16 (W/8 16-byte slots per row): element (r, c) lives at
 // r*W + 8*((c/8) ^ (r % (W/8))) + c%8.
@@ -182,13 +191,13 @@ __device__ __forceinline__ bf16x8 pack_chain(fx4 a, fx4 b) {
 // The bf16 rounding residuals of pack_chain(a, b) = hi: a + b - hi in bf16, so that hi + lo carries
 // the fp32 values to about 16 significant bits.
 __device__ __forceinline__ bf16x8 pack_chain_lo(fx4 a, fx4 b, bf16x8 hi) {
-    bf16x8 r;
+    fx4 ra, rb;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        r[e] = (__bf16)(a[e] - (float)hi[e]);
-        r[4 + e] = (__bf16)(b[e] - (float)hi[4 + e]);
+        ra[e] = a[e] - (float)hi[e];
+        rb[e] = b[e] - (float)hi[4 + e];
     }
-    return r;
+    return pack_chain(ra, rb);
 }
 __device__ __forceinline__ float sel4(fx4 v, int e) {
     return e == 0 ? v[0] : (e == 1 ? v[1] : (e == 2 ? v[2] : v[3]));
@@ -698,14 +707,13 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
     constexpr int t0 = part ? 1 : 0, t1 = part ? 2 : 3;  // my row tiles
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
     const float* gr = reinterpret_cast<const float*>(raw + S::rG);
-    const float* br = reinterpret_cast<const float*>(raw + S::rB);
     __bf16* sLt = reinterpret_cast<__bf16*>(sm + S::L);
     float* own = reinterpret_cast<float*>(sm + S::WL) + part * 2 * C;  // rk [C], gamma log2e [C]
     const int g = lane / 16, l16 = lane % 16;
 
     const float gam = wave_scan(gr[lane], lane);
-    const float b = br[lane];
     own[C + lane] = gam * kLog2e;
+    wave_sync();  // the masks read other lanes' prefix sums
 
     // k-step outer: only one k-step of fragments is live at a time
     fx4 acc[2][4];
@@ -794,9 +802,10 @@ __device__ __forceinline__ void row_factors(float (&f)[4 * N], const float* rk, 
     }
 }
 
-// Prep waves 1, 2 on chunk k: row tiles {0, 3} (half 0) or {1, 2} (half 1) of Pm' = lower(M o Q K^T)
-// of the raw rows, computed as D = K Q^T so that a lane holds 4 consecutive m of row i (bf16,
-// row-major), and rq of those rows (diagonal of Q Q^T).
+// Prep waves 1, 2 on chunk k: row tiles {0, 3} (half 0) or {1, 2} (half 1) of
+// Pm' = diag(rq) lower(M o Q K^T) of the raw rows, computed as D = K Q^T so that a lane holds 4
+// consecutive m of row i (bf16, row-major; rq_i enters as log2 rq_i in the exponent of the mask),
+// and Gamma rq of those rows (rq from the diagonal of Q Q^T): the factor of the state part of O.
 template <int DK, int BV, int half>
 __device__ __forceinline__ void prep_P(const unsigned char* raw, const unsigned char* qv, unsigned char* sm, int lane,
                                        int len, int l2norm) {
@@ -813,6 +822,7 @@ __device__ __forceinline__ void prep_P(const unsigned char* raw, const unsigned 
     constexpr int t0 = half ? 1 : 0, t1 = half ? 2 : 3;  // my row tiles
 
     own[C + lane] = wave_scan(gr[lane], lane) * kLog2e;
+    wave_sync();  // the masks read other lanes' prefix sums
 
     fx4 acc[2][4], dq[2];
 #pragma unroll
@@ -839,12 +849,16 @@ __device__ __forceinline__ void prep_P(const unsigned char* raw, const unsigned 
             dq[s] = mfma(qf[s], qf[s], dq[s]);
         }
     }
+    write_norm(own, dq[0], t0, lane, len, l2norm);
+    write_norm(own, dq[1], t1, lane, len, l2norm);
+    wave_sync();  // each row's norm was written by the lane holding its diagonal element
     const float* g2 = own + C;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const int it = s ? t1 : t0;
         const int i = 16 * it + l16;
-        const float ai = g2[i];
+        // rq_i = 0 past the tail: log2 gives -inf and the row is zero
+        const float ai = g2[i] + __builtin_amdgcn_logf(own[i]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             if (mt > it) continue;
@@ -859,9 +873,7 @@ __device__ __forceinline__ void prep_P(const unsigned char* raw, const unsigned 
             *reinterpret_cast<bf16x4*>(Pm + i * TSTR + m0) = out;
         }
     }
-    write_norm(own, dq[0], t0, lane, len, l2norm);
-    write_norm(own, dq[1], t1, lane, len, l2norm);
-    if (lane / 16 == t0 || lane / 16 == t1) orq[lane] = own[lane];
+    if (lane / 16 == t0 || lane / 16 == t1) orq[lane] = own[lane] * __builtin_amdgcn_exp2f(g2[lane]);
 }
 
 // Solve level 0: invert the 16x16 unit-lower diagonal blocks b0, b0+1 of (I + L) by forward
@@ -1080,8 +1092,8 @@ __device__ __forceinline__ void row_A(RowRegs<DK>& st, unsigned char* sm, const 
 }
 
 // Sub-stage B: S^T <- Gamma_C S^T + K^T diag(exp(gamma_C - gamma)) U', and
-// O^T = [diag(Gamma) (S Q^T) + U'^T Pm'^T] diag(rq) (lane: token 16 it + l16, state rows
-// cbase + 4g .. +3), stored by row_store.
+// O^T = (S Q^T) diag(Gamma rq) + U'^T Pm'^T with Pm' = diag(rq) lower(M o Q K^T) (lane: token
+// 16 it + l16, state rows cbase + 4g .. +3), stored by row_store.
 template <int DK, int BV>
 __device__ __forceinline__ void row_B(RowRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
                                       const unsigned char* gb, int lane) {
@@ -1092,8 +1104,7 @@ __device__ __forceinline__ void row_B(RowRegs<DK>& st, unsigned char* sm, const 
     constexpr int NH = S::WIDE ? 1 : 2;
     const __bf16* K = reinterpret_cast<const __bf16*>(raw + S::rK);
     const __bf16* Pm = reinterpret_cast<const __bf16*>(sm + S::PM);
-    const float* orq = reinterpret_cast<const float*>(sm + S::ORQ);
-    const float* gam = reinterpret_cast<const float*>(gb + S::gGAM);
+    const float* orq = reinterpret_cast<const float*>(sm + S::ORQ);  // Gamma rq per token
     const float gc = reinterpret_cast<const float*>(gb + S::gGC)[0];
     const int g = lane / 16, l16 = lane % 16;
     bf16x8 kt[DT][NH];
@@ -1112,12 +1123,9 @@ __device__ __forceinline__ void row_B(RowRegs<DK>& st, unsigned char* sm, const 
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
             if (s2 == 0 || it >= 2) pf[it][s2] = frag_chain(Pm + (16 * it + l16) * TSTR, 32 * s2, g);
-    float r[4], G[4];
+    float r[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        r[it] = orq[16 * it + l16];
-        G[it] = gam[16 * it + l16];
-    }
+    for (int it = 0; it < 4; ++it) r[it] = orq[16 * it + l16];
     issue_fence();
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -1126,14 +1134,13 @@ __device__ __forceinline__ void row_B(RowRegs<DK>& st, unsigned char* sm, const 
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][0], st.ut[0], st.S[dt]);
     if constexpr (NH == 1) read_kt(1, 0);
+    // O^T = (S Q^T) diag(Gamma rq) + U'^T Pm'^T (rq already in Pm')
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st.ot[it][e] *= G[it];
+        for (int e = 0; e < 4; ++e) st.ot[it][e] *= r[it];
         st.ot[it] = mfma(st.ub[0], pf[it][0], st.ot[it]);
         if (it >= 2) st.ot[it] = mfma(st.ub[1], pf[it][1], st.ot[it]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st.ot[it][e] *= r[it];
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][NH - 1], st.ut[1], st.S[dt]);
@@ -1866,6 +1873,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 const float* rk = reinterpret_cast<const float*>(sm + S::WL);
                 const float* beta = reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB);
                 solve_diag(sLt, Tt, rk, beta, 2 * pw, lane);
+                wave_sync();  // the level-1 products read the diagonal blocks other lanes wrote
                 solve_level1(sLt, Tt, rk, beta, 2 * pw, lane);
                 __builtin_amdgcn_s_setprio(0);
             }
