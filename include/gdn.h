@@ -51,9 +51,10 @@
  *  - All pointers are DEVICE pointers to contiguous, row-major memory, 16-byte aligned, except
  *    where stated.  Nothing is copied to or from the host.
  *  - Ownership: the caller allocates and frees every buffer.  The library allocates nothing,
- *    frees nothing, keeps no mutable global state, launches only on `hip_stream` (a
- *    hipStream_t; NULL = the null stream) and never synchronises.  Buffers must stay alive until
- *    the stream's work has completed.  Calls are asynchronous: a returned GDN_OK means the
+ *    frees nothing, launches only on `hip_stream` (a hipStream_t; NULL = the null stream) and
+ *    never synchronises.  Its only mutable state is the static scratch of gdn_chunk_fwd_noalloc
+ *    (and the device addresses of it).  Buffers must stay alive until the stream's work has
+ *    completed.  Calls are asynchronous: a returned GDN_OK means the
  *    arguments were valid and the launches were enqueued without a launch error.
  *  - Errors: every argument check runs on the host before any HIP call; on an invalid argument
  *    nothing is launched and nothing is written.  No C++ exception crosses this ABI.  Device-side
@@ -77,6 +78,8 @@ extern "C" {
 #define GDN_ERR_UNSUPPORTED 2  /* shape/dtype/chunk this build does not implement                  */
 #define GDN_ERR_WORKSPACE 3    /* workspace missing or smaller than *workspace_bytes               */
 #define GDN_ERR_HIP 4          /* a HIP launch reported an error (hipGetLastError after launch)    */
+#define GDN_ERR_SCRATCH 5      /* gdn_chunk_fwd_noalloc: the call needs more scratch than the
+                                  library's static buffer holds (GDN_NOALLOC_SCRATCH_BYTES)         */
 
 /* Element types of q, k, v and o.  g, beta and every state are always fp32. */
 #define GDN_F32 0
@@ -175,6 +178,33 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   size_t* workspace_bytes, int N, int T_tot, int H, int Hk, int dk, int dv,
                   int dtype, int chunk, float scale, float norm_eps, unsigned flags,
                   void* hip_stream);
+
+/*
+ * gdn_chunk_fwd_noalloc -- gdn_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It calls no allocating routine: where gdn_chunk_fwd needs a workspace
+ * (gdn_chunk_workspace_size > 0), this entry point uses a static device buffer of the library,
+ * GDN_NOALLOC_SCRATCH_BYTES on every device it runs on, held until the process ends.
+ *
+ *  Arguments, results and errors: as gdn_chunk_fwd, without workspace and workspace_bytes; a call
+ *  whose workspace would exceed GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_SCRATCH and launches
+ *  nothing (the automatic segment plans of the long-sequence path stay below it on a 256-CU
+ *  device; the separate conv pass of shapes other than dk = 128 with dv a multiple of 128 needs
+ *  T_tot * (2*Hk*dk + H*dv) * 2 bytes, so long inputs there need GDN_CONV_FUSED or gdn_chunk_fwd).
+ *  The buffer's contents never need clearing (each call writes every part it reads).
+ *  Concurrency: all calls on one device share its buffer; calls that overlap in time on one device
+ *  (two streams, or two host threads) race on it and give undefined results.  Calls on different
+ *  devices do not interact.
+ *  The first call on a device resolves the buffer's device address (a host-side runtime query, no
+ *  allocation); a failure there returns GDN_ERR_HIP.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,
+                          const float* conv_w, void* conv_state, const void* out_gate,
+                          const float* norm_weight, void* o, float* final_state, int N, int T_tot, int H,
+                          int Hk, int dk, int dv, int dtype, int chunk, float scale, float norm_eps,
+                          unsigned flags, void* hip_stream);
 
 /*
  * gdn_chunk_workspace_size -- the workspace gdn_chunk_fwd needs for these sizes, flags and

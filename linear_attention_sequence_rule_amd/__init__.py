@@ -15,12 +15,13 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["gdn_chunk_fwd", "gdn_recurrent_step", "gdn_status_string", "gdn_chunk_workspace_size",
-           "GdnError", "lib_path", "load_library", "GDN_OK", "GDN_ERR_INVALID_ARG",
-           "GDN_ERR_UNSUPPORTED", "GDN_ERR_WORKSPACE", "GDN_ERR_HIP", "GDN_F32", "GDN_BF16",
-           "GDN_QK_L2NORM", "GDN_SEGMENTS", "GDN_CONV_FUSED"]
+__all__ = ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_recurrent_step", "gdn_status_string",
+           "gdn_chunk_workspace_size", "GdnError", "lib_path", "load_library", "GDN_OK", "GDN_ERR_INVALID_ARG",
+           "GDN_ERR_UNSUPPORTED", "GDN_ERR_WORKSPACE", "GDN_ERR_HIP", "GDN_ERR_SCRATCH", "GDN_F32", "GDN_BF16",
+           "GDN_QK_L2NORM", "GDN_SEGMENTS", "GDN_CONV_FUSED", "GDN_NOALLOC_SCRATCH_BYTES"]
 
-GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 0, 1, 2, 3, 4
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP, GDN_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
 GDN_F32, GDN_BF16 = 0, 1
 GDN_QK_L2NORM = 1
 GDN_CONV_FUSED = 1 << 16
@@ -56,6 +57,8 @@ def load_library():
     P, I, U, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_float
     lib.gdn_chunk_fwd.restype = I
     lib.gdn_chunk_fwd.argtypes = [P] * 16 + [I] * 8 + [F, F, U, P]
+    lib.gdn_chunk_fwd_noalloc.restype = I
+    lib.gdn_chunk_fwd_noalloc.argtypes = [P] * 14 + [I] * 8 + [F, F, U, P]
     lib.gdn_chunk_workspace_size.restype = I
     lib.gdn_chunk_workspace_size.argtypes = [I] * 10 + [U, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdn_recurrent_step.restype = I
@@ -188,6 +191,53 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, conv_w=
                            dv, dt, chunk, float(scale), float(norm_eps), flags, _stream(stream))
     if st != GDN_OK:
         raise GdnError(st, "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, initial_state, cu_seqlens, conv_w, *, o, final_state, N=None,
+                          scale=1.0, l2norm=True, chunk=64, segments=0, gate_params=None, conv_state=None,
+                          out_gate=None, norm_weight=None, norm_eps=1e-3, conv_fused=False, stream=None):
+    """gdn_chunk_fwd through the entry point that allocates nothing: the workspace is the library's
+    static device scratch.  The outputs o [T_tot, H, dv] and final_state [N, H, dv, dk] (or None) are
+    the caller's; this wrapper allocates nothing either.  Arguments otherwise as gdn_chunk_fwd."""
+    import torch
+    _check_rank("q", q, 3)
+    _check_rank("v", v, 3)
+    T_tot, Hk, dk = q.shape
+    H, dv = v.shape[1], v.shape[2]
+    if cu_seqlens is not None:
+        _check_rank("cu_seqlens", cu_seqlens, 1)
+        N = cu_seqlens.shape[0] - 1
+    elif N is None:
+        N = initial_state.shape[0] if initial_state is not None else 1
+    _check_shape("k", k, (T_tot, Hk, dk))
+    _check_shape("v", v, (T_tot, H, dv))
+    _check_shape("g", g, (T_tot, H))
+    _check_shape("beta", beta, (T_tot, H))
+    _check_shape("gate_params", gate_params, (2, H))
+    _check_shape("initial_state", initial_state, (N, H, dv, dk))
+    _check_shape("final_state", final_state, (N, H, dv, dk))
+    _check_shape("o", o, (T_tot, H, dv))
+    cc = 2 * Hk * dk + H * dv
+    _check_shape("conv_w", conv_w, (cc, 4))
+    _check_shape("conv_state", conv_state, (N, 3, cc))
+    _check_shape("out_gate", out_gate, (T_tot, H, dv))
+    _check_shape("norm_weight", norm_weight, (dv,))
+    lib = load_library()
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("conv_state", conv_state), ("out_gate", out_gate), ("o", o)):
+        _check_dev(name, t, q.dtype)
+    for name, t in (("g", g), ("beta", beta), ("gate_params", gate_params), ("initial_state", initial_state),
+                    ("conv_w", conv_w), ("final_state", final_state), ("norm_weight", norm_weight)):
+        _check_dev(name, t, torch.float32)
+    _check_dev("cu_seqlens", cu_seqlens, torch.int32)
+    flags = (GDN_QK_L2NORM if l2norm else 0) | GDN_SEGMENTS(segments) | (GDN_CONV_FUSED if conv_fused else 0)
+    st = lib.gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate_params),
+                                   _ptr(initial_state), _ptr(cu_seqlens), _ptr(conv_w), _ptr(conv_state),
+                                   _ptr(out_gate), _ptr(norm_weight), _ptr(o), _ptr(final_state), N, T_tot, H, Hk,
+                                   dk, dv, dt, chunk, float(scale), float(norm_eps), flags, _stream(stream))
+    if st != GDN_OK:
+        raise GdnError(st, "gdn_chunk_fwd_noalloc")
     return o, final_state
 
 

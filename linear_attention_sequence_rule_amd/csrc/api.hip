@@ -1,11 +1,20 @@
 // api.hip -- the C ABI of libgdn.so (declared in include/gdn.h): host-side argument checks, then
-// dispatch to the gfx950 kernels on the caller's stream.  No allocation, no synchronisation, no
-// global mutable state; every check runs before the first HIP call.
+// dispatch to the gfx950 kernels on the caller's stream.  No allocation and no synchronisation;
+// every check runs before the first HIP call.  The only state the library keeps is the static
+// scratch of gdn_chunk_fwd_noalloc and the per-device addresses of it.
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/gdn.h"
 #include "kernels.hpp"
+
+// Scratch of gdn_chunk_fwd_noalloc: device memory the library holds itself, for callers that
+// cannot allocate.  Every device the library runs on keeps one copy until the process ends.  In
+// host code the name stands for a host-side shadow, not the device address: the address comes
+// from hipGetSymbolAddress, once per device (scratch_for_current_device).
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -54,6 +63,26 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool conv_pass(bool has_conv, int dtype, unsigned flags, int dk, int dv) {
     return has_conv && dtype == GDN_BF16 && !(flags & kConvFused) && gdn::chunk_rows_per_workgroup(dk, dv) != 128;
 }
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch array, resolved with that device current
+// the first time a call runs on it.
+int scratch_for_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return GDN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GDN_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GDN_OK;
+}
+
 size_t seg_bytes(int N, int H, int dk, int dv, int P) { return P > 1 ? align256(gdn::seg_layout(N, H, dk, dv, P).bytes) : 0; }
 size_t workspace_for(int N, int T_tot, int H, int Hk, int dk, int dv, int P, bool conv) {
     return seg_bytes(N, H, dk, dv, P) + (conv ? gdn::conv_prepass_bytes(T_tot, H, Hk, dk, dv) : 0);
@@ -70,6 +99,7 @@ const char* gdn_status_string(int status) {
         case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
         case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
         case GDN_ERR_HIP: return "GDN_ERR_HIP";
+        case GDN_ERR_SCRATCH: return "GDN_ERR_SCRATCH";
     }
     return "GDN_ERR_UNKNOWN";
 }
@@ -90,12 +120,16 @@ int gdn_chunk_workspace_size(int N, int T_tot, int H, int Hk, int dk, int dv, in
     return GDN_OK;
 }
 
-int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                  const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,
-                  const float* conv_w, void* conv_state, const void* out_gate, const float* norm_weight, void* o,
-                  float* final_state, void* workspace, size_t* workspace_bytes, int N, int T_tot, int H, int Hk,
-                  int dk, int dv, int dtype, int chunk, float scale, float norm_eps, unsigned flags,
-                  void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// gdn_chunk_fwd with the caller's workspace, or (own_scratch) with the library's static scratch.
+int chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+              const float* gate_params, const float* initial_state, const int32_t* cu_seqlens, const float* conv_w,
+              void* conv_state, const void* out_gate, const float* norm_weight, void* o, float* final_state,
+              void* workspace, size_t* workspace_bytes, bool own_scratch, int N, int T_tot, int H, int Hk, int dk,
+              int dv, int dtype, int chunk, float scale, float norm_eps, unsigned flags, void* hip_stream) {
     if (N < 1 || T_tot < 0) return GDN_ERR_INVALID_ARG;
     if (Hk < 1 || H < 1 || H % Hk != 0) return GDN_ERR_INVALID_ARG;
     int st = check_common(H, dk, dv, dtype, scale, flags);
@@ -150,7 +184,18 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     if (st != GDN_OK) return st;
     const bool cpass = conv_pass(conv_w != nullptr, dtype, flags, dk, dv);
     const size_t need = workspace_for(N, T_tot, H, Hk, dk, dv, P, cpass);
-    if (need > 0) {
+    size_t have = workspace_bytes ? *workspace_bytes : 0;
+    if (own_scratch) {
+        // every part of the workspace is written before it is read: nothing to clear
+        if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
+        workspace = nullptr;
+        have = 0;
+        if (need > 0) {
+            st = scratch_for_current_device(&workspace);
+            if (st != GDN_OK) return st;
+            have = (size_t)GDN_NOALLOC_SCRATCH_BYTES;
+        }
+    } else if (need > 0) {
         if (!workspace_bytes) return GDN_ERR_INVALID_ARG;
         if (!workspace || *workspace_bytes < need) {
             *workspace_bytes = need;
@@ -185,7 +230,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     a.o = o;
     a.sfin = final_state;
     a.workspace = workspace;
-    a.workspace_bytes = workspace_bytes ? *workspace_bytes : 0;
+    a.workspace_bytes = have;
     a.N = N;
     a.T_tot = T_tot;
     a.H = H;
@@ -209,6 +254,31 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     if (e == hipSuccess && out_gate && !gdn::chunk_fuses_epilogue(dk, dv, a.bf16))
         e = gdn::launch_gated_norm(o, a.out_gate, a.norm_weight, (long)T_tot * H, dv, a.norm_eps, a.bf16, a.stream);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,
+                  const float* conv_w, void* conv_state, const void* out_gate, const float* norm_weight, void* o,
+                  float* final_state, void* workspace, size_t* workspace_bytes, int N, int T_tot, int H, int Hk,
+                  int dk, int dv, int dtype, int chunk, float scale, float norm_eps, unsigned flags,
+                  void* hip_stream) {
+    return chunk_fwd(q, k, v, g, beta, gate_params, initial_state, cu_seqlens, conv_w, conv_state, out_gate,
+                     norm_weight, o, final_state, workspace, workspace_bytes, false, N, T_tot, H, Hk, dk, dv, dtype,
+                     chunk, scale, norm_eps, flags, hip_stream);
+}
+
+int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                          const float* gate_params, const float* initial_state, const int32_t* cu_seqlens,
+                          const float* conv_w, void* conv_state, const void* out_gate, const float* norm_weight,
+                          void* o, float* final_state, int N, int T_tot, int H, int Hk, int dk, int dv, int dtype,
+                          int chunk, float scale, float norm_eps, unsigned flags, void* hip_stream) {
+    return chunk_fwd(q, k, v, g, beta, gate_params, initial_state, cu_seqlens, conv_w, conv_state, out_gate,
+                     norm_weight, o, final_state, nullptr, nullptr, true, N, T_tot, H, Hk, dk, dv, dtype, chunk, scale,
+                     norm_eps, flags, hip_stream);
 }
 
 int gdn_recurrent_step(const void* q, const void* k, const void* v, const float* g, const float* beta,

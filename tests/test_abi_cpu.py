@@ -27,8 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gdn_chunk_fwd", "gdn_chunk_workspace_size", "gdn_recurrent_step",
-                                    "gdn_status_string"]
+    assert declared_functions() == ["gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_workspace_size",
+                                    "gdn_recurrent_step", "gdn_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -39,6 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     assert gdn.gdn_status_string(0) == "GDN_OK"
     assert gdn.gdn_status_string(3) == "GDN_ERR_WORKSPACE"
+    assert gdn.gdn_status_string(5) == "GDN_ERR_SCRATCH"
     assert gdn.gdn_status_string(99) == "GDN_ERR_UNKNOWN"
 
 
@@ -224,3 +225,19 @@ def test_workspace_conv_pass(lib):
     assert st == gdn.GDN_ERR_WORKSPACE and wsb.value == 2 * a256(T * Hk * dk * 2) + a256(T * H * dv * 2)
     # Hk must divide H here too
     assert lib.gdn_chunk_workspace_size(N, T, 3, 2, dk, dv, 1, 64, 1, 1, 1, ctypes.byref(n)) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """gdn_chunk_fwd_noalloc: a call whose workspace exceeds the static scratch (here the separate
+    conv pass of a long 64-wide input: T_tot (2 Hk dk + H dv) 2 bytes) returns GDN_ERR_SCRATCH on the
+    host, before any launch; argument errors come first, as for gdn_chunk_fwd."""
+    big = 1 << 36
+    T, H, dk, dv = 1 << 20, 32, 64, 64
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_workspace_size(1, T, H, H, dk, dv, 1, 64, 1, 1, 1 | (1 << 8), ctypes.byref(n)) == 0
+    assert n.value > gdn.GDN_NOALLOC_SCRATCH_BYTES
+    args = [big, 2 * big, 3 * big, 4 * big, 5 * big, None, None, 6 * big, 7 * big, None, None, None, 8 * big, None]
+    st = lib.gdn_chunk_fwd_noalloc(*args, 1, T, H, H, dk, dv, 1, 64, 1.0, 1e-3, 1 | (1 << 8), None)
+    assert st == gdn.GDN_ERR_SCRATCH
+    st = lib.gdn_chunk_fwd_noalloc(*args, 1, T, H, H, 48, dv, 1, 64, 1.0, 1e-3, 1 | (1 << 8), None)
+    assert st == gdn.GDN_ERR_UNSUPPORTED
