@@ -222,9 +222,10 @@ def main():
         n_settle[0] += 1
     settle(settle_step)
     # the K timed calls in groups of G consecutive calls, each group between two HIP events on the
-    # launch stream (an event between every pair of calls would add its own command to each call);
-    # the step time is the median over the groups of the per-call mean
-    G = max(1, args.steps // 10)
+    # launch stream; the step time is the median over the groups of the per-call mean.  A group
+    # holds at least 10 calls: the two event commands around a group cost the stream some
+    # microseconds, which a group of 2 calls of ~100 us would report as ~5% of the step
+    G = max(1, min(args.steps, max(10, args.steps // 10)))
     groups = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range((args.steps + G - 1) // G)]
     t0 = time.perf_counter()

@@ -59,7 +59,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int C = 64;        // chunk length
 constexpr int BVMAX = 64;    // state rows of a narrow workgroup: 64, or 32 when the state has 32 rows
-constexpr int BVW = 128;     // state rows of a wide workgroup (d_k = 128)
+constexpr int BVW = 128;     // state rows of a wide workgroup (d_k = 128; chunk_rows_per_workgroup)
 // Threads of a workgroup: 8 waves (narrow), 12 (wide).
 template <int BV>
 constexpr int kernel_threads() { return BV > BVMAX ? 768 : 512; }
@@ -1914,7 +1914,7 @@ hipError_t launch_k(const Params<DK>& p, const ChunkArgs& a, int grid, int smem)
                                  : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, true, EPI, false>))
                          : (lean ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, false, EPI, L>)
                                  : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, false, EPI, false>));
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    hipError_t e = set_dynamic_lds(fn, smem);
     if (e != hipSuccess) return e;
     constexpr int nt = kernel_threads<BV>();
     if (a.gate_params) {
@@ -1991,11 +1991,10 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     p.norm_weight = a.norm_weight;
     p.norm_eps = a.norm_eps;
     const int smem = Smem<DK, BV>::bytes;
-    int dev = 0, lds_max = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    DeviceInfo dinfo;
+    const hipError_t e = current_device_info(&dinfo);
     if (e != hipSuccess) return e;
-    if (lds_max < smem) return hipErrorInvalidConfiguration;  // needs the 160 KiB LDS of gfx950
+    if (dinfo.lds_max < smem) return hipErrorInvalidConfiguration;  // needs the 160 KiB LDS of gfx950
     const int grid = a.N * c.P * a.H * p.nv;
     if (epi) {
         if constexpr (Smem<DK, BV>::WIDE) return launch_k<DK, BV, true>(p, a, grid, smem);
@@ -2057,13 +2056,6 @@ hipError_t run(const ChunkArgs& a, int P) {
 }
 
 }  // namespace
-
-int chunk_rows_per_workgroup(int dk, int rows) {
-    if (dk == 128 && rows % BVW == 0) return BVW;
-    return rows >= 64 ? 64 : 32;
-}
-
-bool chunk_fuses_epilogue(int dk, int dv, bool bf16) { return bf16 && chunk_rows_per_workgroup(dk, dv) == BVW; }
 
 hipError_t launch_chunk_bf16(const ChunkArgs& a) {
     switch (a.dk) {

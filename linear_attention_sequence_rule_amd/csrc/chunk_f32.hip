@@ -179,6 +179,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(F32Params<T> p) {
             const int i = idx / C, j = idx % C;
             float kk = 0.f, qk = 0.f;
             if (j <= i) {
+#pragma unroll 8
                 for (int d = 0; d < DK; ++d) {
                     kk += sK[i * L::QS + d] * sK[j * L::QS + d];
                     qk += sQ[i * L::QS + d] * sK[j * L::QS + d];
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(F32Params<T> p) {
             const int idx = tid + 256 * e;
             const int i = idx / BV, c = idx % BV;
             float ks = 0.f, qv = 0.f;
+#pragma unroll 8
             for (int d = 0; d < DK; ++d) {
                 const float s = sS[c * L::QS + d];
                 ks += sK[i * L::QS + d] * s;
@@ -249,6 +251,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(F32Params<T> p) {
         for (int idx = tid; idx < BV * DK; idx += 256) {
             const int c = idx / DK, d = idx % DK;
             float acc = gC * sS[c * L::QS + d];
+#pragma unroll 8
             for (int i = 0; i < C; ++i) acc += sU[i * L::VS + c] * sD[i] * sK[i * L::QS + d];
             sS[c * L::QS + d] = acc;
         }
@@ -285,8 +288,7 @@ hipError_t launch_f32_t(const ChunkArgs& a) {
     p.scale = a.scale;
     p.l2norm = a.l2norm;
     const size_t smem = F32Smem<DK, BV>::bytes;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_f32_kernel<DK, BV, T>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(&chunk_f32_kernel<DK, BV, T>), (int)smem);
     if (e != hipSuccess) return e;
     const int nv = a.dv / BV;
     hipLaunchKernelGGL((chunk_f32_kernel<DK, BV, T>), dim3(a.N * a.H * nv), dim3(256), smem, a.stream, p);

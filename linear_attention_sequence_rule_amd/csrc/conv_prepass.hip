@@ -151,11 +151,6 @@ __global__ __launch_bounds__(256) void conv_prepass_kernel(const bf16* __restric
 
 }  // namespace
 
-size_t conv_prepass_bytes(int T_tot, int H, int Hk, int dk, int dv) {
-    auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    return 2 * a256((size_t)T_tot * Hk * dk * 2) + a256((size_t)T_tot * H * dv * 2);
-}
-
 hipError_t launch_conv_prepass(const ChunkArgs& a, void* out, ChunkArgs& conv_args) {
     auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
     unsigned char* base = static_cast<unsigned char*>(out);

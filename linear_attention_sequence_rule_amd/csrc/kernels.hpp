@@ -73,6 +73,16 @@ bool chunk_fuses_epilogue(int dk, int dv, bool bf16);
 // (row blocks of chunk_rows_per_workgroup rows), and only for sequences of at least 16 chunks per
 // segment.
 int plan_segments(int N, int T_tot, int H, int dk, int dv, int requested);
+// Facts of the current device, read from the runtime on its first use and kept (a call to
+// hipDeviceGetAttribute per launch would cost host time on every prefill).
+struct DeviceInfo {
+    int cus = 0;      // compute units
+    int lds_max = 0;  // bytes of LDS one workgroup may use
+};
+hipError_t current_device_info(DeviceInfo* out);
+// hipFuncSetAttribute(fn, MaxDynamicSharedMemorySize, bytes) on the current device, once per
+// (kernel, device, size): later calls return at once.
+hipError_t set_dynamic_lds(const void* fn, int bytes);
 
 hipError_t launch_step(const StepArgs& a);
 hipError_t launch_chunk_f32(const ChunkArgs& a);

@@ -172,3 +172,63 @@ def test_epilogue_prefill_raw_gates_conv_history():
     assert excess.max() <= 1.0, excess.max()
     _flush("epilogue raw gates+conv history+groups+segments: max err %.3g, max err/bound %.3g"
            % (np.abs(og - ref).max(), excess.max()))
+
+
+# ------------------------------------------------ the epilogue against the norm of the kernel's own o
+
+U_BF16 = 2.0 ** -8  # unit roundoff of bf16 (8 significant bits, round to nearest even)
+
+ROUNDING_CASES = [
+    # name, workload kwargs, segments, fused (the 128-row kernel applies the epilogue to its fp32 o)
+    ("prefill_bench_shape", None, 0, True),
+    ("wide_conv_groups_segments", dict(lengths=[64 * 9 + 5, 130, 1], H=4, Hk=2, dk=128, dv=128, dtype="bf16",
+                                       conv=True), 3, True),
+    ("narrow_128x64", dict(lengths=[300, 64, 7], H=4, dk=128, dv=64, dtype="bf16"), 2, False),
+    ("narrow_64x32_conv", dict(lengths=[200, 1, 90], H=3, dk=64, dv=32, dtype="bf16", conv=True), 0, False),
+    ("f32_64x64", dict(lengths=[150, 33], H=3, dk=64, dv=64, dtype="f32"), 0, False),
+]
+
+
+@pytest.mark.parametrize("name,kw,segments,fused", ROUNDING_CASES, ids=[c[0] for c in ROUNDING_CASES])
+def test_epilogue_is_the_norm_of_its_own_output(name, kw, segments, fused):
+    """The same call with and without the epilogue: the gated output must be the fp64 gated norm of
+    the un-gated output up to the roundings the path takes, a bar set by bf16 rounding alone rather
+    than by the o parity bar.
+
+    Fused (128-row kernel, bf16): the kernel normalises its fp32 o and rounds once, while the
+    un-gated call rounds that same o to bf16.  A relative change of at most u = 2^-8 in every element
+    of a row moves each o_i / rms by at most 2u |o_i| / rms to first order (u from o_i, u from rms), and
+    the final rounding adds u: |gated - gated_norm(o_plain)| <= 3u |ref|.  Separate pass (other
+    shapes, bf16): the norm reads the stored bf16 o, which is o_plain itself, and rounds once: u |ref|.
+    fp32: the norm reads the stored fp32 o; only fp32 arithmetic separates them.  A relative 1e-5
+    covers the fp32 arithmetic of the norm (rsqrt, exp, reciprocal) and an absolute 1e-6 of the row's
+    largest value covers elements that cancel to ~0."""
+    import torch
+    from linear_attention_sequence_rule_amd import gdn_chunk_fwd
+    if kw is None:
+        wl = W.prefill()
+    else:
+        wl = W.make("epi_round_" + name, seed=650 + len(name), s0_std=0.05, varlen=True, **kw)
+    z, w = _epilogue_inputs(660 + len(name), (wl.T_tot, wl.H), wl.dv, wl.dtype)
+    d = dict(q=TL.to_dev(wl.q), k=TL.to_dev(wl.k), v=TL.to_dev(wl.v), g=TL.to_dev(wl.g), beta=TL.to_dev(wl.beta),
+             s0=TL.to_dev(wl.s0), cu=TL.to_dev(wl.cu_seqlens), cw=TL.to_dev(wl.conv_w))
+    zd, wd = TL.to_dev(z), TL.to_dev(w)
+
+    def run(gated):
+        o, sf = gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["cu"], d["cw"], N=wl.N,
+                              segments=segments, out_gate=zd if gated else None, norm_weight=wd if gated else None,
+                              norm_eps=1e-3)
+        torch.cuda.synchronize()
+        return o, sf
+
+    o_plain, s_plain = run(False)
+    o_gated, s_gated = run(True)
+    assert torch.equal(s_plain, s_gated), "the epilogue leaves the final state alone"
+    og = TL.o_to_f64(o_gated)
+    ref = oracle.gated_norm(TL.o_to_f64(o_plain), _zf(z), w, 1e-3)
+    rel = (3 * U_BF16 if fused else U_BF16) if wl.dtype == "bf16" else 0.0
+    bound = (rel + 1e-5) * np.abs(ref) + 1e-6 * np.abs(ref).max(-1, keepdims=True)
+    excess = np.abs(og - ref) / bound
+    _flush("epilogue rounding %s: max |err|/|ref| %.3g, max err/bound %.3g"
+           % (name, (np.abs(og - ref) / np.maximum(np.abs(ref), 1e-30)).max(), excess.max()))
+    assert excess.max() <= 1.0, excess.max()
