@@ -6,9 +6,9 @@ prefill row of the path runs inside it.  Inputs are resident in HBM before the t
 To keep the 256 MB Infinity Cache from serving the inputs, the timed loop rotates over several
 independent copies of the inputs (more than twice the cache in total).
 
-The JSON line reports prefill tokens/s as `value`, the HBM roofline of the prefill kernel
-(algorithmic bytes per call / mean call time, from one pair of HIP events on the launch stream
-around the timed region), the bf16
+The JSON line reports prefill tokens/s as `value` (the K timed calls in groups of at least 10
+consecutive calls between HIP events on the launch stream; the median over the groups of the mean
+call time), the HBM roofline of the prefill kernel (algorithmic bytes per call / that time), the bf16
 MFMA fraction under algorithmic flop accounting, the decode step (256 sequences x 32 heads, state
 updated in place) as GB/s against HBM, the long-sequence prefill (1 x 262144 tokens, 16 heads,
 segmented) and the packed variable-length prefill with the conv prologue (64 sequences of
@@ -18,6 +18,10 @@ prologue and a conv state (and with the fused epilogue as well), and the fp64 CP
 throughput on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+       python bench.py --record-traffic DIR   (no GPU: writes profiles/traffic.json from the
+           rocprofv3 counter runs DIR/{fetch,write,cfetch,cwrite}/run_counter_collection.csv:
+           FETCH_SIZE and WRITE_SIZE over `bench.py --steps 3 --warmup 1 --no-cpu-baseline
+           --copies 1 --no-extra` and over `bench.py --copy-calibration`)
 """
 import argparse
 import json
@@ -54,7 +58,6 @@ def decode_alg_bytes(N, H, dk, dv):
 def load_traffic(kernel_tag):
     """HBM traffic per call measured with rocprofv3 counters (profiles/traffic.json), valid only
     while the hashes of the sources recorded with the counters still match."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -67,10 +70,60 @@ def load_traffic(kernel_tag):
     shas = dict(rec.get("also", {}))
     shas[rec["source"]] = rec["source_sha"]
     for name, want in shas.items():
-        src = os.path.join(ROOT, "linear_attention_sequence_rule_amd", "csrc", name)
-        if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != want:
+        if source_sha(name) != want:
             return None
     return rec["bytes_per_launch"]
+
+
+def source_sha(name):
+    import hashlib
+    src = os.path.join(ROOT, "linear_attention_sequence_rule_amd", "csrc", name)
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def record_traffic(d):
+    """profiles/traffic.json from four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, KiB per
+    dispatch, over a short bench run and over the plain-copy calibration).  The copy calibration
+    gives the scale of each counter: bytes the copy moves each way / what the counter reads.  A
+    prefill call is its chunk_bf16 dispatches (main, transition and rerun pass: the rerun pass,
+    the one instantiation with the rerun code, is counted once per call)."""
+    import csv
+    from collections import defaultdict
+
+    def load(sub):
+        per = defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(d, sub, "run_counter_collection.csv"))):
+            per[(int(r["Dispatch_Id"]), r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        return {k: sum(v) for k, v in per.items()}  # one value per dispatch (summed over dimensions)
+
+    scale = {}
+    for sub, ctr in (("cfetch", "FETCH_SIZE"), ("cwrite", "WRITE_SIZE")):
+        vals = [v for (_, name), v in load(sub).items() if "copyBuffer" in name]
+        assert vals, "no copy kernel in " + sub
+        scale[ctr] = (1 << 30) / (sum(vals) / len(vals) * 1024.0)
+    out = {}
+    fetch, write = load("fetch"), load("write")
+    for tag, src, also in (("chunk_bf16_kernel", "chunk_bf16.hip", ("segments.hip", "api.hip")),
+                           ("step_kernel", "step.hip", ())):
+        fb = sum(v for (_, n), v in fetch.items() if tag in n) * 1024.0 * scale["FETCH_SIZE"]
+        wb = sum(v for (_, n), v in write.items() if tag in n) * 1024.0 * scale["WRITE_SIZE"]
+        if tag == "chunk_bf16_kernel":
+            # the rerun pass has the only instantiation with rerun code: <..., false> last
+            calls_f = sum(1 for (_, n) in fetch if tag in n and n.rstrip(")").split(">")[0].endswith("false"))
+            calls_w = sum(1 for (_, n) in write if tag in n and n.rstrip(")").split(">")[0].endswith("false"))
+            per = "prefill step: main pass + transition pass + rerun pass"
+        else:
+            calls_f = sum(1 for (_, n) in fetch if tag in n)
+            calls_w = sum(1 for (_, n) in write if tag in n)
+            per = "decode step"
+        assert calls_f and calls_w, tag
+        out[tag] = {"source": src, "source_sha": source_sha(src), "also": {a: source_sha(a) for a in also},
+                    "bytes_per_launch": fb / calls_f + wb / calls_w, "fetch_bytes": fb / calls_f,
+                    "write_bytes": wb / calls_w, "calls": [calls_f, calls_w], "per": per,
+                    "counter_scale": dict(scale)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def cpu_model():
@@ -151,7 +204,12 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated through the timed loop")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="write profiles/traffic.json from the rocprofv3 counter runs under DIR (no GPU)")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs the gated delta rule on a single device "
               "(no collectives); run with --gpus 1", file=sys.stderr)
@@ -210,24 +268,31 @@ def main():
         o, sf = outs[i % len(outs)]
         gdn.gdn_chunk_fwd(q, k, v, g, b, s0, N=N, o=o, final_state=sf, workspace=ws, stream=stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # the clocks come up only after tens of milliseconds of work: at least 50 ms of untimed calls
-    # after the warm-up, whatever --warmup says
-    n_settle = [args.warmup]
-
-    def settle_step():
-        step(n_settle[0])
-        n_settle[0] += 1
-    settle(settle_step)
     # the K timed calls in groups of G consecutive calls, each group between two HIP events on the
     # launch stream; the step time is the median over the groups of the per-call mean.  A group
     # holds at least 10 calls: the two event commands around a group cost the stream some
-    # microseconds, which a group of 2 calls of ~100 us would report as ~5% of the step
+    # microseconds, which a group of 2 calls of ~100 us would report as ~5% of the step.  The
+    # events are recorded once before anything is timed: the first use of timing events in a
+    # process has been seen to hold the host for tens of milliseconds, during which the GPU idles
+    # and its clocks drop.
     G = max(1, min(args.steps, max(10, args.steps // 10)))
     groups = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range((args.steps + G - 1) // G)]
+    for a, b in groups:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    # then calls back to back, as in the timed region, for at least 0.2 s whatever --warmup says:
+    # the clocks settle to their level under this load only after tens of milliseconds of it
+    n_settle, t_s = args.warmup, time.perf_counter()
+    while time.perf_counter() - t_s < 0.2:
+        for _ in range(20):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
+    n_settle = [n_settle]
     t0 = time.perf_counter()
     i = 0
     for a, b in groups:

@@ -239,7 +239,7 @@ struct Smem {
     static constexpr int WL = ORQ + C * 4;           // L-prep scratch, per wave: rk, gamma log2e [2][2][C]
     static constexpr int WP = WL + 4 * C * 4;        // P-prep scratch, per wave: rq, gamma log2e [2][2][C]
     static constexpr int HB = WP + 4 * C * 4;        // conv halo: 3 raw rows [3][DK + BV/2] channel pairs
-    static constexpr int CW = HB + 3 * (DK + (WIDE ? BV : BVMAX) / 2) * 4;  // wide: conv weights [48][8][4] fp32
+    static constexpr int CW = HB + 3 * (DK + (WIDE ? BV : BVMAX) / 2) * 4;  // wide: conv weights [8][48][4] fp32 (x -log2 e)
     static constexpr int EP = CW + (WIDE ? 48 * 8 * 16 : 0);  // wide epilogue: row sums of o^2 [C][8 row waves]
     static constexpr int NW = EP + (WIDE ? C * 8 * 4 : 0);    // wide epilogue: w of the block's rows [BV]
     static constexpr int bytes = NW + (WIDE ? BV * 4 : 0);
@@ -1166,9 +1166,12 @@ __device__ __forceinline__ void row_store(const Params<DK>& p, const RowRegs<DK>
 }
 
 // ------------------------------------------------------------------------------------------
-// Wide workgroups (dk = BV = 128: K, Q and V tiles of 16 slots of 16 bytes per row): the conv
-// weights live in LDS as [48 slots][8 channels][4 taps] (slots 0..15 the K channels, 16..31 Q,
-// 32..47 V), loaded once per workgroup.
+// Wide workgroups (dk = BV = 128: K, Q and V tiles of 16 slots of 16 bytes (8 channels) per row):
+// the conv weights live in LDS as [8 channels][48 slots][4 taps] (slots 0..15 the K channels,
+// 16..31 Q, 32..47 V), loaded once per workgroup and multiplied by -log2(e) (see silu_of_scaled).
+// Channel-major, so that the lanes of a wave, which hold consecutive slots, read consecutive
+// 16-byte words (slot-major would put the 64 lanes on a few banks).
+constexpr float kNegLog2e = -1.44269504088896341f;
 template <int DK, int BV>
 __device__ void conv_weights_wide(const Params<DK>& p, unsigned char* sm, int tid, int h, int hk, int vb) {
     using S = Smem<DK, BV>;
@@ -1177,20 +1180,27 @@ __device__ void conv_weights_wide(const Params<DK>& p, unsigned char* sm, int ti
         const int sl = tid / 8, tile = sl / 16, c = (sl % 16) * 8 + tid % 8;  // channel within its tile
         const int row = tile == 0 ? (p.Hk + hk) * DK + c : (tile == 1 ? hk * DK + c : 2 * p.Hk * DK + h * p.dv + vb * BV + c);
         const float4 w = *reinterpret_cast<const float4*>(p.conv_w + (size_t)row * 4);
-        *reinterpret_cast<float4*>(sm + S::CW + 16 * tid) = w;
+        *reinterpret_cast<float4*>(sm + S::CW + 16 * ((tid % 8) * 48 + sl)) =
+            make_float4(w.x * kNegLog2e, w.y * kNegLog2e, w.z * kNegLog2e, w.w * kNegLog2e);
     }
 }
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u128;
 __device__ __forceinline__ u32x4 ld128(unsigned a) { return *reinterpret_cast<lds_u128*>(static_cast<uintptr_t>(a)); }
 __device__ __forceinline__ void st128(unsigned a, u32x4 v) { *reinterpret_cast<lds_u128*>(static_cast<uintptr_t>(a)) = v; }
+// SiLU(y) from t = -log2(e) y: y / (1 + e^-y) = t / (-log2(e) (1 + 2^t)), the factor folded into
+// one fma (y -> -inf: 2^t = inf and the result -0; y -> +inf: 2^t = 0 and the result y).
+__device__ __forceinline__ float silu_of_scaled(float t) {
+    return t * __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(t), kNegLog2e, kNegLog2e));
+}
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 // The conv + SiLU of one chunk's tiles in a wide workgroup (the same operation as conv_chunk).
 // Item = lane: 16-byte slot s = tid % 48 (8 channels of one tile) and rows 4 rb .. 4 rb + 3,
 // rb = tid / 48; it reads its 4 raw rows and the 3 before them (the halo for rb = 0), one 16-byte
 // read each, and after a barrier writes its 4 results; items of the last block keep their raw rows
-// 61..63 as the next chunk's halo ([3][48] slots of 16 bytes).
+// 61..63 as the next chunk's halo ([3][48] slots of 16 bytes).  (Items of 4 channels x 8 rows with
+// 8-byte accesses take fewer conversions but more LDS instructions, and measured slower.)
 template <int DK, int BV>
 __device__ void conv_chunk_wide(const Params<DK>& p, const unsigned char* sm, unsigned rawK, int lenK, unsigned rawQV,
                                 int lenQV, unsigned halo, int parts, int tid) {
@@ -1211,9 +1221,9 @@ __device__ void conv_chunk_wide(const Params<DK>& p, const unsigned char* sm, un
     }
     lds_barrier();  // every raw row has been read
     if (act) {
-        float4 w[8];
+        float4 w[8];  // taps of channel c (scaled by -log2 e)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) w[c] = *reinterpret_cast<const float4*>(sm + S::CW + 128 * sl + 16 * c);
+        for (int c = 0; c < 8; ++c) w[c] = *reinterpret_cast<const float4*>(sm + S::CW + 16 * (48 * c + sl));
         float lo[7][4], hi[7][4];
 #pragma unroll
         for (int j = 0; j < 7; ++j)
@@ -1228,9 +1238,9 @@ __device__ void conv_chunk_wide(const Params<DK>& p, const unsigned char* sm, un
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 a = w[2 * q], b = w[2 * q + 1];
-                const float y0 = a.x * lo[r][q] + a.y * lo[r + 1][q] + a.z * lo[r + 2][q] + a.w * lo[r + 3][q];
-                const float y1 = b.x * hi[r][q] + b.y * hi[r + 1][q] + b.z * hi[r + 2][q] + b.w * hi[r + 3][q];
-                o[q] = pack_bf16(silu(y0), silu(y1));
+                const float t0 = a.x * lo[r][q] + a.y * lo[r + 1][q] + a.z * lo[r + 2][q] + a.w * lo[r + 3][q];
+                const float t1 = b.x * hi[r][q] + b.y * hi[r + 1][q] + b.z * hi[r + 2][q] + b.w * hi[r + 3][q];
+                o[q] = pack_bf16(silu_of_scaled(t0), silu_of_scaled(t1));
             }
             if (4 * rb + r < len) st128(at(4 * rb + r), u32x4{o[0], o[1], o[2], o[3]});  // rows past the tail stay zero
         }
