@@ -201,6 +201,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the long-sequence and varlen lines")
+    ap.add_argument("--lines", default=None,
+                    help="comma-separated subset of the extra lines to run (long_prefill, varlen, prefill_raw_gates, "
+                         "prefill_grouped_heads, prefill_epilogue, prefill_slow_decay, decode_conv: with decode_full); "
+                         "default all")
     ap.add_argument("--copies", type=int, default=4, help="input copies rotated through the timed loop")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -342,7 +346,12 @@ def main():
         return ts[len(ts) // 2] * 1e-3
 
     extra = {}
-    if not args.no_extra:
+    picked = None if args.lines is None else set(args.lines.split(","))
+
+    def want(name):
+        return picked is None or name in picked
+
+    if not args.no_extra and want("long_prefill"):
         lw = W.long_prefill()
         lq, lk, lv, lg, lb = (to_dev(x) for x in (lw.q, lw.k, lw.v, lw.g, lw.beta))
         lo = torch.empty_like(lv)
@@ -357,6 +366,7 @@ def main():
             "value": lw.T_tot / ls, "unit": "tokens/s", "us": ls * 1e6, "workspace_bytes": need,
             "hbm_alg_gbs": lbytes / ls / 1e9, "hbm_frac": lbytes / ls / 1e9 / HBM_PEAK_GBS}
         del lq, lk, lv, lg, lb, lo, lsf, lws, lw
+    if not args.no_extra and want("varlen"):
         vw = W.varlen()
         vq, vk, vv, vg, vb, vs0, vcu, vcw = (to_dev(x) for x in (vw.q, vw.k, vw.v, vw.g, vw.beta, vw.s0, vw.cu_seqlens,
                                                                   vw.conv_w))
@@ -378,6 +388,7 @@ def main():
         del vq, vk, vv, vg, vb, vs0, vcu, vcw, vo, vsf, vw, vws
         torch.cuda.empty_cache()
 
+    if not args.no_extra and want("prefill_raw_gates"):
         # the prefill step again, the gates formed in the kernel from the raw a, b, A_log, dt_bias
         ra, rb, rgp = (to_dev(x) for x in W.raw_gate_inputs(wl.meta["seed"], wl.lengths, H))
         q, k, v, _, _, s0 = copies[0]
@@ -390,6 +401,7 @@ def main():
             "hbm_alg_gbs": alg_bytes / rsec / 1e9, "hbm_frac": alg_bytes / rsec / 1e9 / HBM_PEAK_GBS}
         del ra, rb, rgp
 
+    if not args.no_extra and want("prefill_grouped_heads"):
         # the prefill step with 16 value heads sharing 8 query/key heads (pairs of value heads read
         # one query/key head): the q, k bytes per value head halve
         gw = W.prefill(Hk=8)
@@ -404,12 +416,14 @@ def main():
             "hbm_alg_gbs": gbytes / gsec / 1e9, "hbm_frac": gbytes / gsec / 1e9 / HBM_PEAK_GBS}
         del gq, gk, gv, gg, gb, gs0, go, gsf, gw
 
+    if not args.no_extra and want("prefill_epilogue"):
         # the prefill step with the output epilogue (zero-centred RMSNorm over dv, sigmoid output
         # gate), applied by the chunk kernel to its fp32 o
         ez = to_dev(W.f32_to_bf16_bits(np.random.default_rng([1, 77]).standard_normal((tokens, H, dv),
                                                                                       dtype=np.float32)))
         ew = to_dev(np.random.default_rng([1, 78]).normal(0.0, 0.2, size=dv).astype(np.float32))
         q, k, v, g, b, s0 = copies[0]
+        o, sf = outs[0]
         esec = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, g, b, s0, N=N, o=o, final_state=sf, out_gate=ez,
                                                norm_weight=ew, workspace=ws, stream=stream), 20)
         ebytes = alg_bytes + tokens * H * dv * 2 + dv * 4
@@ -420,10 +434,12 @@ def main():
             "hbm_alg_gbs": ebytes / esec / 1e9, "hbm_frac": ebytes / esec / 1e9 / HBM_PEAK_GBS}
         del ez, ew
 
+    if not args.no_extra and want("prefill_slow_decay"):
         # the prefill step with slow decay everywhere (g = -1e-3, beta as drawn): no segment transition
         # is negligible, so every pass of the segmented path covers whole segments -- its worst case
         sg = torch.full_like(copies[0][3], -1e-3)
         q, k, v, _, b, s0 = copies[0]
+        o, sf = outs[0]
         ssec = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, sg, b, s0, N=N, o=o, final_state=sf, workspace=ws,
                                                stream=stream), 20)
         extra["prefill_slow_decay"] = {
@@ -433,6 +449,7 @@ def main():
             "hbm_alg_gbs": alg_bytes / ssec / 1e9, "hbm_frac": alg_bytes / ssec / 1e9 / HBM_PEAK_GBS}
         del sg
 
+    if not args.no_extra and want("decode_conv"):
         # the decode step with the conv prologue on the raw token (history in a conv state updated in
         # place) and raw gates: the decode side of a layer whose prefill ran the conv
         cw, hist = W.conv_inputs(3, dw.N, dw.H, dw.dk, dw.dv, "bf16")

@@ -71,9 +71,13 @@ __device__ __forceinline__ fx4 mfma(bf16x8 a, bf16x8 b, fx4 c) {
 __device__ __forceinline__ fx4 zero4() { return fx4{0.f, 0.f, 0.f, 0.f}; }
 // A copy of x that the compiler cannot see through: lane-dependent address arithmetic derived
 // from it is recomputed where it is used instead of being hoisted out of the chunk loop, where
-// it would stay live in registers across every role's code.
+// it would stay live in registers across every role's code.  x is a lane or thread index: the
+// range is restated after the asm, so that x / 16, x % 4 and the like stay single shifts and
+// masks (for an int the compiler cannot prove non-negative they are signed divisions, five
+// instructions each).
 __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
+    __builtin_assume(x >= 0 && x < 1024);
     return x;
 }
 // Keep every instruction before this point (typically a batch of LDS operand reads) ahead of
@@ -92,8 +96,9 @@ __device__ __forceinline__ void wave_sync() {
 // Swizzled row-major tile of R rows x W bf16 (W/8 16-byte slots per row): element (r, c) lives at
 // r*W + 8*((c/8) ^ (r % (W/8))) + c%8.
 template <int W>
-__device__ __forceinline__ int swz(int r, int c) {
-    return r * W + 8 * ((c / 8) ^ (r % (W / 8))) + (c % 8);
+__device__ __forceinline__ int swz(int r, int c) {  // r, c >= 0: unsigned arithmetic, masks and shifts
+    const unsigned ur = (unsigned)r, uc = (unsigned)c;
+    return (int)(ur * W + 8u * ((uc / 8u) ^ (ur % (W / 8))) + (uc % 8u));
 }
 // 16-byte natural-order fragment of a swizzled tile: row r, columns kb + 8g .. +7
 template <int W>
