@@ -1688,16 +1688,25 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     }
     if constexpr (EPI)
         if (tid < BV) reinterpret_cast<float*>(sm + S::NW)[tid] = p.norm_weight[vb * BV + tid];
-    // chunk 0 (wide: its K, g and beta; Q and V come with the first iteration's loads)
+    // chunk 0 (wide: its K, g and beta, and without the epilogue its Q and V; with the epilogue
+    // Q and V come with the first iteration's loads)
     if (nchunks > 0 && is_prep) {
         if constexpr (WIDE) {
             dma_k<DK, 16>(p, smb + S::raw(0) + S::rK, bos, clen(0), hk, 16 * pw, lane);
             if (pw < 2) dma_gates_in<DK>(p, smb + S::raw(0) + (pw == 0 ? S::rG : S::rB), bos, clen(0), h, pw, lane);
+            if constexpr (!EPI) {
+                dma_q<DK, 16>(p, smb + S::qv(0) + S::rQ, bos, clen(0), hk, 16 * pw, lane);
+                if (!p.v_zero) dma_v<DK, BV, 16>(p, smb + S::qv(0) + S::rV, bos, clen(0), h, vb, 16 * pw, lane);
+            }
             wait_loads();
             if constexpr (RAW) raw_gates<DK, BV>(p, sm + S::raw(0), clen(0), pw, lane, h);
             if (clen(0) < C) {
                 zero_rows<DK, 16>(reinterpret_cast<__bf16*>(sm + S::raw(0) + S::rK), clen(0), 16 * pw, opaque(lane));
                 if (pw < 2 && lane >= clen(0)) reinterpret_cast<float*>(sm + S::raw(0) + (pw == 0 ? S::rG : S::rB))[lane] = 0.f;
+                if constexpr (!EPI) {
+                    zero_rows<DK, 16>(reinterpret_cast<__bf16*>(sm + S::qv(0) + S::rQ), clen(0), 16 * pw, opaque(lane));
+                    zero_rows<BV, 16>(reinterpret_cast<__bf16*>(sm + S::qv(0) + S::rV), clen(0), 16 * pw, opaque(lane));
+                }
             }
         } else {
             dma_chunk<DK, BV>(p, smb, S::raw(0), bos, clen(0), h, hk, vb, pw, lane);
@@ -1760,20 +1769,28 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 pend = -1;
             }
             if (cur && is_row) row_A<DK, BV>(st, sm, sm + S::raw(k), sm + S::qv(k), sm + S::gates(k), wid, lane);
-            if constexpr (WIDE) {
-                // rows [8w, 8w + 8) of K of chunk k+2 (with g, beta: waves 0, 1) and of Q, V of chunk
+            if constexpr (WIDE && !EPI) {
+                // rows [16w, 16w + 16) of K of chunk k+2 (with g, beta: waves 0, 1), on waves 0..3,
+                // which finish their row work first.  K's buffer held chunk k-1 (last read in the
+                // previous sub-stage B).  Q and V come from the prep waves, a chunk further ahead.
+                if (far && wid < 4) {
+                    dma_k<DK, 16>(p, smb + S::raw(k + 2) + S::rK, tk + 2 * C, clen(k + 2), hk, 16 * wid, lane);
+                    if (wid < 2)
+                        dma_gates_in<DK>(p, smb + S::raw(k + 2) + (wid == 0 ? S::rG : S::rB), tk + 2 * C, clen(k + 2), h,
+                                         wid, lane);
+                }
+            } else if constexpr (WIDE) {
+                // rows [8w, 8w + 8) of K of chunk k+2 (with g, beta: waves 0, 1) and of V of chunk
                 // k+1.  K's buffer held chunk k-1 (last read in the previous sub-stage B), the Q/V
-                // buffer chunk k-1 (last read in the previous sub-stage A).
+                // buffer chunk k-1 (last read in the previous sub-stage A; its Q tile then held z).
                 if (far) {
                     dma_k<DK, 8>(p, smb + S::raw(k + 2) + S::rK, tk + 2 * C, clen(k + 2), hk, 8 * wid, lane);
                     if (wid < 2)
                         dma_gates_in<DK>(p, smb + S::raw(k + 2) + (wid == 0 ? S::rG : S::rB), tk + 2 * C, clen(k + 2), h,
                                          wid, lane);
                 }
-                if (nxt) {
-                    if (!EPI) dma_q<DK, 8>(p, smb + S::qv(k + 1) + S::rQ, tk + C, clen(k + 1), hk, 8 * wid, lane);
-                    if (!p.v_zero) dma_v<DK, BV, 8>(p, smb + S::qv(k + 1) + S::rV, tk + C, clen(k + 1), h, vb, 8 * wid, lane);
-                }
+                if (nxt && !p.v_zero)
+                    dma_v<DK, BV, 8>(p, smb + S::qv(k + 1) + S::rV, tk + C, clen(k + 1), h, vb, 8 * wid, lane);
             } else if (far && is_load) {
                 // the loads of chunk k+2 from waves 2 and 3 (rows 32 (w - 2) .. + 31), after their row
                 // work: waves 0 and 1 share their SIMDs with the solve of the next sub-stage and wait
@@ -1791,7 +1808,18 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 }
                 bound(k);
             }
-            if constexpr (WIDE) {
+            if constexpr (WIDE && !EPI) {
+                if (far && wid < 4) {
+                    wait_loads();
+                    if (RAW && wid < 2) raw_gates<DK, BV>(p, sm + S::raw(k + 2), clen(k + 2), wid, lane, h);
+                    if (clen(k + 2) < C) {
+                        zero_rows<DK, 16>(reinterpret_cast<__bf16*>(sm + S::raw(k + 2) + S::rK), clen(k + 2), 16 * wid,
+                                          opaque(lane));
+                        if (wid < 2 && lane >= clen(k + 2))
+                            reinterpret_cast<float*>(sm + S::raw(k + 2) + (wid == 0 ? S::rG : S::rB))[lane] = 0.f;
+                    }
+                }
+            } else if constexpr (WIDE) {
                 if (far || nxt) {
                     wait_loads();
                     if (far) {
@@ -1803,13 +1831,9 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                                 reinterpret_cast<float*>(sm + S::raw(k + 2) + (wid == 0 ? S::rG : S::rB))[lane] = 0.f;
                         }
                     }
-                    if (nxt && clen(k + 1) < C) {
-                        if (!EPI)
-                            zero_rows<DK, 8>(reinterpret_cast<__bf16*>(sm + S::qv(k + 1) + S::rQ), clen(k + 1), 8 * wid,
-                                             opaque(lane));
+                    if (nxt && clen(k + 1) < C)
                         zero_rows<BV, 8>(reinterpret_cast<__bf16*>(sm + S::qv(k + 1) + S::rV), clen(k + 1), 8 * wid,
                                          opaque(lane));
-                    }
                 }
             } else if (far && is_load) {
                 wait_loads();
@@ -1872,6 +1896,27 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             lds_barrier();
             // ---- B
             if (cur) bound(k);
+            if constexpr (WIDE && !EPI) {
+                // first thing in sub-stage B, while the row waves issue no memory instructions: Q, V of
+                // chunk k+1 (loaded at the start of the previous sub-stage B) have landed: their tail rows
+                // set to zero; then Q, V of chunk k+2 into the buffer of chunk k, whose last reads were
+                // in this iteration's sub-stage A.  Rows [16 pw, 16 pw + 16) each: the loads have an
+                // iteration and a half to land, where the row waves' wait would be on the chain.
+                if (nxt) {
+                    wait_loads();
+                    if (clen(k + 1) < C) {
+                        zero_rows<DK, 16>(reinterpret_cast<__bf16*>(sm + S::qv(k + 1) + S::rQ), clen(k + 1), 16 * pw,
+                                          opaque(lane));
+                        zero_rows<BV, 16>(reinterpret_cast<__bf16*>(sm + S::qv(k + 1) + S::rV), clen(k + 1), 16 * pw,
+                                          opaque(lane));
+                    }
+                }
+                if (far) {
+                    dma_q<DK, 16>(p, smb + S::qv(k + 2) + S::rQ, tk + 2 * C, clen(k + 2), hk, 16 * pw, lane);
+                    if (!p.v_zero)
+                        dma_v<DK, BV, 16>(p, smb + S::qv(k + 2) + S::rV, tk + 2 * C, clen(k + 2), h, vb, 16 * pw, lane);
+                }
+            }
             if constexpr (EPI) {
                 // waves 10, 11: rows [32 (pw - 2), + 32) of z of chunk k (into its Q tile) and of Q of
                 // chunk k+1
@@ -1916,6 +1961,9 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             if (p.early_exit && decay <= kExitLog) break;
             if (conv) conv_after<DK, BV>(p, cw, sm, smb, k, clen(k + 1), clen(k + 2), far, nxt, tid);
         }
+        // an early exit can leave Q, V loads of a later chunk in flight: none may land in LDS after
+        // the workgroup has ended
+        wait_loads();
     }
 }
 
