@@ -1158,14 +1158,35 @@ __device__ __forceinline__ void row_store(const Params<DK>& p, const RowRegs<DK>
     lane = opaque(lane);
     const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
     if (p.out != OUT_STORE) return;
+    // Lane (g, l16) holds columns cbase + 4g .. + 3 of token 16 it + l16 in each tile.  Tiles it and
+    // it + 1 trade rows of 16 lanes (v_permlane16_swap: rows 1, 3 of the first with rows 0, 2 of the
+    // second), after which lane (g, l16) holds columns cbase + 8 (g / 2) .. + 7 of token
+    // 16 (it + g % 2) + l16: one 16-byte store per lane and tile pair instead of two 8-byte ones.
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int i = 16 * it + l16;
+    for (int it = 0; it < 4; it += 2) {
+        bf16x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = (__bf16)(p.scale * st.ot[it][e]);
+            b[e] = (__bf16)(p.scale * st.ot[it + 1][e]);
+        }
+        uint32_t ua[2], ub[2];
+        __builtin_memcpy(ua, &a, 8);
+        __builtin_memcpy(ub, &b, 8);
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto r = __builtin_amdgcn_permlane16_swap(ua[w], ub[w], false, false);
+            ua[w] = r[0];
+            ub[w] = r[1];
+        }
+        const int i = 16 * (it + g % 2) + l16;
         if (i < len) {
-            bf16x4 out;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(p.scale * st.ot[it][e]);
-            *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
+            uint4 v;
+            v.x = ua[0];
+            v.y = ua[1];
+            v.z = ub[0];
+            v.w = ub[1];
+            *reinterpret_cast<uint4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 8 * (g / 2)) = v;
         }
     }
 }
