@@ -1900,6 +1900,9 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
             const long tk = bos + (long)k * C;
             // ---- A
+            // the prep waves end sub-stage A last (each shares its SIMD with two row waves, which
+            // reach the barrier early): their instructions go first until the barrier
+            __builtin_amdgcn_s_setprio(1);
             if (cur) {
                 unsigned char* rawk = sm + S::raw(k);
                 if (pw == 1) prep_P<DK, BV, 0>(rawk, sm + S::qv(k), sm, lane, clen(k), p.l2norm);
@@ -1914,6 +1917,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 keep_to_global<C * TSTR * 2, 128>(sm, S::T, kd + PRE_T, tid - 64 * PW0);
                 keep_to_global<Smem<DK, BV>::gBytes, 128>(sm, S::gates(0), kd + PRE_G, tid - 64 * PW0);
             }
+            __builtin_amdgcn_s_setprio(0);
             lds_barrier();
             // ---- B
             if (cur) bound(k);
