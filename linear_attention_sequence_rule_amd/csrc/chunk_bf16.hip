@@ -1222,19 +1222,24 @@ __device__ __forceinline__ float silu_of_scaled(float t) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 // The conv + SiLU of one chunk's tiles in a wide workgroup (the same operation as conv_chunk).
-// Item = lane: 16-byte slot s = tid % 48 (8 channels of one tile) and rows 4 rb .. 4 rb + 3,
-// rb = tid / 48; it reads its 4 raw rows and the 3 before them (the halo for rb = 0), one 16-byte
-// read each, and after a barrier writes its 4 results; items of the last block keep their raw rows
-// 61..63 as the next chunk's halo ([3][48] slots of 16 bytes).  (Items of 4 channels x 8 rows with
-// 8-byte accesses take fewer conversions but more LDS instructions, and measured slower.)
+// Item = lane: 16-byte slot s (8 channels of one tile) and rows 4 rb .. 4 rb + 3.  Wave w owns
+// slots 4w .. 4w + 3 (waves 0..3 the K tile, 4..7 Q, 8..11 V) in every row block: lane l takes slot
+// 4w + l % 4 and block rb = l / 4.  An item reads its 4 raw rows and the 3 before them (the halo,
+// for rb = 0 the previous chunk's last 3 raw rows), one 16-byte read each, then writes its 4
+// results; the items of block 15 keep their raw rows 61..63 as the next chunk's halo ([3][48]
+// slots of 16 bytes).  Every row an item reads but does not write belongs to an item of the same
+// wave, so the wave's own ordering of its LDS accesses (all reads before any write) is enough: no
+// workgroup barrier between the reads and the writes.  A 16-lane pass of the reads touches 4 rows
+// 4 apart x 4 slots: 16 distinct swizzled slots, no bank conflict.  (Items of 4 channels x 8 rows
+// with 8-byte accesses take fewer conversions but more LDS instructions, and measured slower.)
 template <int DK, int BV>
 __device__ void conv_chunk_wide(const Params<DK>& p, const unsigned char* sm, unsigned rawK, int lenK, unsigned rawQV,
                                 int lenQV, unsigned halo, int parts, int tid) {
     using S = Smem<DK, BV>;
     static_assert(DK == 128 && BV == 128 && kernel_threads<BV>() == 48 * 16, "one item per lane");
     tid = opaque(tid);
-    const int sl = tid % 48, rb = tid / 48, tile = sl / 16, ts = sl % 16;
-    const bool act = (parts & (tile == 0 ? 1 : 2)) && !(tile == 2 && p.v_zero);
+    const int sl = 4 * (tid / 64) + tid % 4, rb = (tid % 64) / 4, tile = sl / 16, ts = sl % 16;
+    const bool act = (parts & (tile == 0 ? 1 : 2)) && !(tile == 2 && p.v_zero);  // uniform per wave
     const unsigned base = tile == 0 ? rawK + S::rK : (tile == 1 ? rawQV + S::rQ : rawQV + S::rV);
     const int len = tile == 0 ? lenK : lenQV;
     auto at = [&](int r) { return base + 256u * r + 16u * (ts ^ (r & 15)); };  // swz<128>
@@ -1245,7 +1250,7 @@ __device__ void conv_chunk_wide(const Params<DK>& p, const unsigned char* sm, un
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[3 + j] = ld128(at(4 * rb + j));
     }
-    lds_barrier();  // every raw row has been read
+    wave_sync();  // every raw row this wave's items read has been read before any is written
     if (act) {
         float4 w[8];  // taps of channel c (scaled by -log2 e)
 #pragma unroll
