@@ -1319,10 +1319,14 @@ __device__ __forceinline__ void epi_store(const Params<DK>& p, const RowRegs<DK>
     const int g = lane / 16, l16 = lane % 16, cbase = 16 * wave;
     const float* ep = reinterpret_cast<const float*>(sm + S::EP);
     const fx4 w = *reinterpret_cast<const fx4*>(sm + S::NW + 4 * (cbase + 4 * g));
+    // tiles it, it + 1 formed by every lane (rows past len too: in-bounds reads, never stored), then
+    // paired as in row_store (v_permlane16_swap) for one 16-byte store per lane and tile pair
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int i = 16 * it + l16;
-        if (i < len) {
+    for (int it = 0; it < 4; it += 2) {
+        uint32_t u2[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = 16 * (it + u) + l16;
             const fx4 a = *reinterpret_cast<const fx4*>(ep + 8 * i), b = *reinterpret_cast<const fx4*>(ep + 8 * i + 4);
             const float ss = ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
             const float rr = rsqrtf(ss * (1.f / BV) + p.norm_eps);
@@ -1331,9 +1335,24 @@ __device__ __forceinline__ void epi_store(const Params<DK>& p, const RowRegs<DK>
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float zz = (float)z[e];
-                out[e] = (__bf16)(p.scale * st.ot[it][e] * rr * (1.f + w[e]) * __builtin_amdgcn_rcpf(1.f + __expf(-zz)));
+                out[e] = (__bf16)(p.scale * st.ot[it + u][e] * rr * (1.f + w[e]) * __builtin_amdgcn_rcpf(1.f + __expf(-zz)));
             }
-            *reinterpret_cast<bf16x4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 4 * g) = out;
+            __builtin_memcpy(u2[u], &out, 8);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const auto r = __builtin_amdgcn_permlane16_swap(u2[0][q], u2[1][q], false, false);
+            u2[0][q] = r[0];
+            u2[1][q] = r[1];
+        }
+        const int i = 16 * (it + g % 2) + l16;
+        if (i < len) {
+            uint4 v;
+            v.x = u2[0][0];
+            v.y = u2[0][1];
+            v.z = u2[1][0];
+            v.w = u2[1][1];
+            *reinterpret_cast<uint4*>(p.o + ((size_t)(t0 + i) * p.H + h) * p.dv + vb * BV + cbase + 8 * (g / 2)) = v;
         }
     }
 }
