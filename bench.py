@@ -81,7 +81,7 @@ def source_sha(name):
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def record_traffic(d):
+def record_traffic(d, out_path=None):
     """profiles/traffic.json from four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, KiB per
     dispatch, over a short bench run and over the plain-copy calibration).  The copy calibration
     gives the scale of each counter: bytes the copy moves each way / what the counter reads.  A
@@ -121,9 +121,10 @@ def record_traffic(d):
                     "bytes_per_launch": fb / calls_f + wb / calls_w, "fetch_bytes": fb / calls_f,
                     "write_bytes": wb / calls_w, "calls": [calls_f, calls_w], "per": per,
                     "counter_scale": dict(scale)}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = out_path or os.path.join(ROOT, "profiles", "traffic.json")
     json.dump(out, open(path, "w"), indent=1)
     print(json.dumps(out, indent=1))
+    return out
 
 
 def cpu_model():
