@@ -1009,7 +1009,7 @@ struct RowRegs {
 
 // Sub-stage A: K S^T and S Q^T (S in bf16 is the same operand for both), then
 // Y = beta rk V - beta Gamma rk^2 K S^T and U' = T' Y blockwise.
-template <int DK, int BV>
+template <int DK, int BV, bool OUT = true>
 __device__ __forceinline__ void row_A(RowRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
                                       const unsigned char* qv, const unsigned char* gb, int wave, int lane) {
     lane = opaque(lane);
@@ -1039,12 +1039,12 @@ __device__ __forceinline__ void row_A(RowRegs<DK>& st, unsigned char* sm, const 
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             kfr[t] = lds_at<bf16x8>(K, o + 16 * t * DK);
-            qfr[t] = lds_at<bf16x8>(Q, o + 16 * t * DK);
+            if constexpr (OUT) qfr[t] = lds_at<bf16x8>(Q, o + 16 * t * DK);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            ks_acc[t] = mfma(kfr[t], sb, ks_acc[t]);     // K S^T (M = token, N = c)
-            st.ot[t] = mfma(sb, qfr[t], st.ot[t]);       // S Q^T (M = c, N = token)
+            ks_acc[t] = mfma(kfr[t], sb, ks_acc[t]);                        // K S^T (M = token, N = c)
+            if constexpr (OUT) st.ot[t] = mfma(sb, qfr[t], st.ot[t]);       // S Q^T (M = c, N = token)
         }
     }
     bf16x4 vv[4];
@@ -1099,7 +1099,7 @@ __device__ __forceinline__ void row_A(RowRegs<DK>& st, unsigned char* sm, const 
 // Sub-stage B: S^T <- Gamma_C S^T + K^T diag(exp(gamma_C - gamma)) U', and
 // O^T = (S Q^T) diag(Gamma rq) + U'^T Pm'^T with Pm' = diag(rq) lower(M o Q K^T) (lane: token
 // 16 it + l16, state rows cbase + 4g .. +3), stored by row_store.
-template <int DK, int BV>
+template <int DK, int BV, bool OUT = true>
 __device__ __forceinline__ void row_B(RowRegs<DK>& st, unsigned char* sm, const unsigned char* raw,
                                       const unsigned char* gb, int lane) {
     lane = opaque(lane);
@@ -1123,14 +1123,16 @@ __device__ __forceinline__ void row_B(RowRegs<DK>& st, unsigned char* sm, const 
 #pragma unroll
     for (int s2 = 0; s2 < NH; ++s2) read_kt(s2, s2);
     bf16x8 pf[4][2];
-#pragma unroll
-    for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-            if (s2 == 0 || it >= 2) pf[it][s2] = frag_chain(Pm + (16 * it + l16) * TSTR, 32 * s2, g);
     float r[4];
+    if constexpr (OUT) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) r[it] = orq[16 * it + l16];
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                if (s2 == 0 || it >= 2) pf[it][s2] = frag_chain(Pm + (16 * it + l16) * TSTR, 32 * s2, g);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) r[it] = orq[16 * it + l16];
+    }
     issue_fence();
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -1140,12 +1142,14 @@ __device__ __forceinline__ void row_B(RowRegs<DK>& st, unsigned char* sm, const 
     for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][0], st.ut[0], st.S[dt]);
     if constexpr (NH == 1) read_kt(1, 0);
     // O^T = (S Q^T) diag(Gamma rq) + U'^T Pm'^T (rq already in Pm')
+    if constexpr (OUT) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+        for (int it = 0; it < 4; ++it) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st.ot[it][e] *= r[it];
-        st.ot[it] = mfma(st.ub[0], pf[it][0], st.ot[it]);
-        if (it >= 2) st.ot[it] = mfma(st.ub[1], pf[it][1], st.ot[it]);
+            for (int e = 0; e < 4; ++e) st.ot[it][e] *= r[it];
+            st.ot[it] = mfma(st.ub[0], pf[it][0], st.ot[it]);
+            if (it >= 2) st.ot[it] = mfma(st.ub[1], pf[it][1], st.ot[it]);
+        }
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) st.S[dt] = mfma(kt[dt][NH - 1], st.ut[1], st.S[dt]);
@@ -1597,9 +1601,11 @@ __device__ bool rerun_first_chunk(const Params<DK>& p, unsigned char* sm, const 
 // no trace of the gate transform).  EPI: the output epilogue.  LEAN: without the rerun pass's code
 // (entering states, the one-chunk rerun); the first and transition passes without the epilogue
 // run this one: the chunk loop schedules better without that code beside it.
-template <int DK, int BV, bool RAW, bool EPI, bool LEAN>
+template <int DK, int BV, bool RAW, bool EPI, bool LEAN, bool TRANS = false>
 __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params<DK> p) {
     using S = Smem<DK, BV>;
+    // TRANS: the transition pass (no output): nothing of Q, Pm' or O is formed
+    constexpr bool OUT = !TRANS;
     constexpr bool WIDE = S::WIDE;
     static_assert(!EPI || WIDE, "the fused output epilogue needs the whole row of a head");
     constexpr int NT = kernel_threads<BV>(), PW0 = NT / 64 - 4;
@@ -1740,7 +1746,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             dma_k<DK, 16>(p, smb + S::raw(0) + S::rK, bos, clen(0), hk, 16 * pw, lane);
             if (pw < 2) dma_gates_in<DK>(p, smb + S::raw(0) + (pw == 0 ? S::rG : S::rB), bos, clen(0), h, pw, lane);
             if constexpr (!EPI) {
-                dma_q<DK, 16>(p, smb + S::qv(0) + S::rQ, bos, clen(0), hk, 16 * pw, lane);
+                if constexpr (OUT) dma_q<DK, 16>(p, smb + S::qv(0) + S::rQ, bos, clen(0), hk, 16 * pw, lane);
                 if (!p.v_zero) dma_v<DK, BV, 16>(p, smb + S::qv(0) + S::rV, bos, clen(0), h, vb, 16 * pw, lane);
             }
             wait_loads();
@@ -1813,7 +1819,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                                       reinterpret_cast<const __bf16*>(sm + S::qv(pend) + S::rQ));
                 pend = -1;
             }
-            if (cur && is_row) row_A<DK, BV>(st, sm, sm + S::raw(k), sm + S::qv(k), sm + S::gates(k), wid, lane);
+            if (cur && is_row) row_A<DK, BV, OUT>(st, sm, sm + S::raw(k), sm + S::qv(k), sm + S::gates(k), wid, lane);
             if constexpr (WIDE && !EPI) {
                 // rows [16w, 16w + 16) of K of chunk k+2 (with g, beta: waves 0, 1), on waves 0..3,
                 // which finish their row work first.  K's buffer held chunk k-1 (last read in the
@@ -1848,7 +1854,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             // ---- B
             if (cur) {
                 if (is_row) {
-                    row_B<DK, BV>(st, sm, sm + S::raw(k), sm + S::gates(k), lane);
+                    row_B<DK, BV, OUT>(st, sm, sm + S::raw(k), sm + S::gates(k), lane);
                     if constexpr (EPI) epi_sums<DK, BV>(p, st, sm, wid, lane);
                 }
                 bound(k);
@@ -1927,7 +1933,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             // the prep waves end sub-stage A last (each shares its SIMD with two row waves, which
             // reach the barrier early): their instructions go first until the barrier
             __builtin_amdgcn_s_setprio(1);
-            if (cur) {
+            if (cur && OUT) {
                 unsigned char* rawk = sm + S::raw(k);
                 if (pw == 1) prep_P<DK, BV, 0>(rawk, sm + S::qv(k), sm, lane, clen(k), p.l2norm);
                 if (pw == 2) prep_P<DK, BV, 1>(rawk, sm + S::qv(k), sm, lane, clen(k), p.l2norm);
@@ -1961,7 +1967,8 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                     }
                 }
                 if (far) {
-                    dma_q<DK, 16>(p, smb + S::qv(k + 2) + S::rQ, tk + 2 * C, clen(k + 2), hk, 16 * pw, lane);
+                    if constexpr (OUT)
+                        dma_q<DK, 16>(p, smb + S::qv(k + 2) + S::rQ, tk + 2 * C, clen(k + 2), hk, 16 * pw, lane);
                     if (!p.v_zero)
                         dma_v<DK, BV, 16>(p, smb + S::qv(k + 2) + S::rV, tk + 2 * C, clen(k + 2), h, vb, 16 * pw, lane);
                 }
@@ -2016,31 +2023,31 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     }
 }
 
+template <int DK, int BV, bool RAW, bool EPI, bool LEAN, bool TRANS>
+hipError_t launch_one(const Params<DK>& p, const ChunkArgs& a, int grid, int smem) {
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, RAW, EPI, LEAN, TRANS>), smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, RAW, EPI, LEAN, TRANS>), dim3(grid), dim3(kernel_threads<BV>()), smem,
+                       a.stream, p);
+    return hipGetLastError();
+}
+
 template <int DK, int BV, bool EPI>
 hipError_t launch_k(const Params<DK>& p, const ChunkArgs& a, int grid, int smem) {
-    // the lean instantiation (no rerun code) for every pass but the rerun, unless the epilogue is on
+    // the lean instantiation (no rerun code) for every pass but the rerun, unless the epilogue is on;
+    // the transition pass (no output) has one of its own
     constexpr bool L = !EPI;
     const bool lean = L && p.init != INIT_PREV;
-    const void* fn = a.gate_params
-                         ? (lean ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, true, EPI, L>)
-                                 : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, true, EPI, false>))
-                         : (lean ? reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, false, EPI, L>)
-                                 : reinterpret_cast<const void*>(&chunk_bf16_kernel<DK, BV, false, EPI, false>));
-    hipError_t e = set_dynamic_lds(fn, smem);
-    if (e != hipSuccess) return e;
-    constexpr int nt = kernel_threads<BV>();
-    if (a.gate_params) {
-        if (lean)
-            hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, true, EPI, L>), dim3(grid), dim3(nt), smem, a.stream, p);
-        else
-            hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, true, EPI, false>), dim3(grid), dim3(nt), smem, a.stream, p);
-    } else {
-        if (lean)
-            hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, false, EPI, L>), dim3(grid), dim3(nt), smem, a.stream, p);
-        else
-            hipLaunchKernelGGL((chunk_bf16_kernel<DK, BV, false, EPI, false>), dim3(grid), dim3(nt), smem, a.stream, p);
+    if constexpr (L) {
+        if (lean && p.out == OUT_NONE)
+            return a.gate_params ? launch_one<DK, BV, true, EPI, true, true>(p, a, grid, smem)
+                                 : launch_one<DK, BV, false, EPI, true, true>(p, a, grid, smem);
     }
-    return hipGetLastError();
+    if (a.gate_params)
+        return lean ? launch_one<DK, BV, true, EPI, L, false>(p, a, grid, smem)
+                    : launch_one<DK, BV, true, EPI, false, false>(p, a, grid, smem);
+    return lean ? launch_one<DK, BV, false, EPI, L, false>(p, a, grid, smem)
+                : launch_one<DK, BV, false, EPI, false, false>(p, a, grid, smem);
 }
 
 // One pass of the kernel.  rows = state rows (dv, or dk for the transition pass).
