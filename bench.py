@@ -81,6 +81,12 @@ def source_sha(name):
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
+def _rerun_instantiation(name):
+    """True for a chunk_bf16_kernel name whose LEAN template argument (the fifth) is false."""
+    args = name.split("chunk_bf16_kernel<", 1)[1].split(">", 1)[0].split(",")
+    return args[4].strip() == "false"
+
+
 def record_traffic(d, out_path=None):
     """profiles/traffic.json from four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, KiB per
     dispatch, over a short bench run and over the plain-copy calibration).  The copy calibration
@@ -108,9 +114,10 @@ def record_traffic(d, out_path=None):
         fb = sum(v for (_, n), v in fetch.items() if tag in n) * 1024.0 * scale["FETCH_SIZE"]
         wb = sum(v for (_, n), v in write.items() if tag in n) * 1024.0 * scale["WRITE_SIZE"]
         if tag == "chunk_bf16_kernel":
-            # the rerun pass has the only instantiation with rerun code: <..., false> last
-            calls_f = sum(1 for (_, n) in fetch if tag in n and n.rstrip(")").split(">")[0].endswith("false"))
-            calls_w = sum(1 for (_, n) in write if tag in n and n.rstrip(")").split(">")[0].endswith("false"))
+            # the rerun pass has the only instantiation with rerun code: template argument LEAN
+            # (the fifth: <DK, BV, RAW, EPI, LEAN, ...>) false
+            calls_f = sum(1 for (_, n) in fetch if tag in n and _rerun_instantiation(n))
+            calls_w = sum(1 for (_, n) in write if tag in n and _rerun_instantiation(n))
             per = "prefill step: main pass + transition pass + rerun pass"
         else:
             calls_f = sum(1 for (_, n) in fetch if tag in n)

@@ -12,8 +12,9 @@ import bench
 HEADER = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
           "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
           "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
-MAIN = "void gdn::(anonymous namespace)::chunk_bf16_kernel<128, 128, false, false, true>(gdn::Params<128>)"
-RERUN = "void gdn::(anonymous namespace)::chunk_bf16_kernel<128, 128, false, false, false>(gdn::Params<128>)"
+MAIN = "void gdn::(anonymous namespace)::chunk_bf16_kernel<128, 128, false, false, true, false>(gdn::Params<128>)"
+TRANS = "void gdn::(anonymous namespace)::chunk_bf16_kernel<128, 128, false, false, true, true>(gdn::Params<128>)"
+RERUN = "void gdn::(anonymous namespace)::chunk_bf16_kernel<128, 128, false, false, false, false>(gdn::Params<128>)"
 STEP = "void gdn::step_kernel<128, 128, gdn::bf16, false, false>(gdn::bf16 const*)"
 COPY = "__amd_rocclr_copyBuffer"
 
@@ -35,7 +36,7 @@ def test_record_traffic(tmp_path):
     _write(os.path.join(d, "cfetch", "run_counter_collection.csv"), "FETCH_SIZE", [(COPY, 524288.0)] * 3)
     _write(os.path.join(d, "cwrite", "run_counter_collection.csv"), "WRITE_SIZE", [(COPY, 1048576.0)] * 3)
     # two prefill calls (main, transition, rerun) and one decode step, KiB per dispatch
-    calls = [(MAIN, 100.0), (MAIN, 1.0), (RERUN, 10.0)] * 2 + [(STEP, 50.0)]
+    calls = [(MAIN, 100.0), (TRANS, 1.0), (RERUN, 10.0)] * 2 + [(STEP, 50.0)]
     _write(os.path.join(d, "fetch", "run_counter_collection.csv"), "FETCH_SIZE", calls)
     _write(os.path.join(d, "write", "run_counter_collection.csv"), "WRITE_SIZE",
            [(n, k / 2) for n, k in calls])
