@@ -241,7 +241,7 @@ struct Smem {
     static constexpr int PM = T + C * TSTR * 2;      // Pm bf16 [C][TSTR], row-major [i][m]
     static constexpr int L = PM + C * TSTR * 2;      // L^T bf16 [C][TSTR]: L^T[j][i] = L_ij
     static constexpr int ORQ = L + C * TSTR * 2;     // rq [C]
-    static constexpr int WL = ORQ + C * 4;           // L-prep scratch, per wave: rk, gamma log2e [2][2][C]
+    static constexpr int WL = ORQ + C * 4;           // L-prep scratch [4][C]: rk, gamma log2e (part 0), f, gamma log2e (part 1)
     static constexpr int WP = WL + 4 * C * 4;        // P-prep scratch, per wave: rq, gamma log2e [2][2][C]
     static constexpr int HB = WP + 4 * C * 4;        // conv halo: 3 raw rows [3][DK + BV/2] channel pairs
     static constexpr int CW = HB + 3 * (DK + (WIDE ? BV : BVMAX) / 2) * 4;  // wide: conv weights [8][48][4] fp32 (x -log2 e)
@@ -688,6 +688,19 @@ __device__ __forceinline__ void write_norm(float* dst, fx4 diag, int t, int lane
     }
 }
 
+// write_norm for the K rows of L', which also leaves the row factor f_i = beta_i rk_i^2 of L'.
+__device__ __forceinline__ void write_norm_f(float* rk, float* f, const float* beta, fx4 diag, int t, int lane, int len,
+                                             int l2norm) {
+    const int g = lane / 16, l16 = lane % 16;
+    if (g == l16 / 4) {
+        const int i = 16 * t + l16;
+        const float x = sel4(diag, l16 % 4);
+        const float r = i < len ? (l2norm ? rsqrtf(x + kL2Eps) : 1.f) : 0.f;
+        rk[i] = r;
+        f[i] = beta[i] * r * r;
+    }
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 
@@ -761,11 +774,13 @@ __device__ __forceinline__ void prep_L(const unsigned char* raw, unsigned char* 
             *reinterpret_cast<bf16x4*>(sLt + j * TSTR + i0) = out;
         }
     }
-    // rk of this part's rows (from the diagonal tiles of its own Gram tiles), for the solve and
-    // the gates of the next sub-stage: both parts write part 0's rk array
+    // rk of this part's rows (from the diagonal tiles of its own Gram tiles) for the gates of the
+    // next sub-stage, and the row factors f = beta rk^2 of L' for the solve: both parts write
+    // part 0's rk array and the f array
     float* rk = reinterpret_cast<float*>(sm + S::WL);
-    write_norm(rk, acc[0][t0], t0, lane, len, l2norm);
-    write_norm(rk, acc[1][t1], t1, lane, len, l2norm);
+    const float* beta = reinterpret_cast<const float*>(raw + S::rB);
+    write_norm_f(rk, rk + 2 * C, beta, acc[0][t0], t0, lane, len, l2norm);
+    write_norm_f(rk, rk + 2 * C, beta, acc[1][t1], t1, lane, len, l2norm);
 }
 
 // Prep wave 3, sub-stage B, on chunk k+1: the gates, from rk and gamma log2e left by part 0 of prep_L.
@@ -796,14 +811,14 @@ __device__ __forceinline__ void make_gates(const unsigned char* raw, unsigned ch
     }
 }
 
-// Row factors f_i = beta_i rk_i^2 of L' for rows i0 .. i0 + 4n - 1 (rk from part 0 of prep_L).
+// Row factors f_i = beta_i rk_i^2 of L' for rows i0 .. i0 + 4n - 1 (left by prep_L).
 template <int N>
-__device__ __forceinline__ void row_factors(float (&f)[4 * N], const float* rk, const float* beta, int i0) {
+__device__ __forceinline__ void row_factors(float (&f)[4 * N], const float* fr, int i0) {
 #pragma unroll
     for (int q = 0; q < N; ++q) {
-        const fx4 r = *reinterpret_cast<const fx4*>(rk + i0 + 4 * q), bb = *reinterpret_cast<const fx4*>(beta + i0 + 4 * q);
+        const fx4 r = *reinterpret_cast<const fx4*>(fr + i0 + 4 * q);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[4 * q + e] = bb[e] * r[e] * r[e];
+        for (int e = 0; e < 4; ++e) f[4 * q + e] = r[e];
     }
 }
 
@@ -883,12 +898,15 @@ __device__ __forceinline__ void prep_P(const unsigned char* raw, const unsigned 
 
 // Solve level 0: invert the 16x16 unit-lower diagonal blocks b0, b0+1 of (I + L) by forward
 // substitution, one column per lane (lanes 0..15 block b0, 16..31 block b0+1; lanes 32..63 compute
-// a duplicate and discard it).  Each lane reads its own column of L once (row j of L^T, two
-// 16-byte loads); at step m the column of lane m is broadcast within the 16-lane row with the DPP
-// row broadcast (as a DPP operand of the FMA), so the substitution reads nothing else from LDS.  The right-looking update keeps
-// one FMA on the critical path per step.  Writes the blocks of T^T (bf16; column j of T = row j
-// of T^T).
-// step M: t_M is final; acc[i] += L[i][M] t_M for i > M, L[i][M] taken from lane M of the row by
+// a duplicate and discard it).  With L = diag(f) G (G strictly lower), lane j solves for
+// z = T e_j - e_j, i.e. (I + L) z = -L e_j: z_m = -f_m (G_mj + sum_{i<m} G_mi z_i), which is zero
+// for m <= j, so every lane runs the same steps with no select; the unit diagonal is written
+// afterwards.  Each lane reads its own column of G once (row j of G^T, two 16-byte loads), which
+// is also the start of its accumulators; at step m the column of lane m is broadcast within the
+// 16-lane row with the DPP row broadcast (as a DPP operand of the FMA), so the substitution reads
+// nothing else from LDS.  The right-looking update keeps one FMA on the critical path per step.
+// Writes the blocks of T^T (bf16; column j of T = row j of T^T).
+// step M: z_M is final; acc[i] += G[i][M] z_M for i > M, G[i][M] taken from lane M of the row by
 // the FMA's DPP row-broadcast operand
 template <int M>
 __device__ __forceinline__ void fmac_bcast(float& acc, float l, float t) {  // acc += (lane M's l) * t
@@ -897,23 +915,22 @@ __device__ __forceinline__ void fmac_bcast(float& acc, float l, float t) {  // a
 }
 template <int M>
 __device__ __forceinline__ void solve_step(const float (&col)[16], const float (&f)[16], float (&acc)[16],
-                                           float (&t)[16], int j) {
-    const float tm = M == j ? 1.f : (M > j ? -f[M] * acc[M] : 0.f);
+                                           float (&t)[16]) {
+    const float tm = __builtin_fmaf(-f[M], acc[M], 0.f);  // + 0: a zero z_M is +0
     t[M] = tm;
 #pragma unroll
     for (int i = M + 1; i < 16; ++i) fmac_bcast<M>(acc[i], col[i], tm);
 }
 template <int... Ms>
 __device__ __forceinline__ void solve_steps(const float (&col)[16], const float (&f)[16], float (&acc)[16],
-                                            float (&t)[16], int j, std::integer_sequence<int, Ms...>) {
-    (solve_step<Ms>(col, f, acc, t, j), ...);
+                                            float (&t)[16], std::integer_sequence<int, Ms...>) {
+    (solve_step<Ms>(col, f, acc, t), ...);
 }
-__device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, const float* rk, const float* beta, int b0,
-                                           int lane) {
+__device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, const float* fr, int b0, int lane) {
     lane = opaque(lane);
     const int b = b0 + (lane / 16) % 2, j = lane % 16, base = 16 * b;
     float f[16];  // row factors of the block
-    row_factors<4>(f, rk, beta, base);
+    row_factors<4>(f, fr, base);
     const bf16x8 c0 = *reinterpret_cast<const bf16x8*>(sLt + (base + j) * TSTR + base);
     const bf16x8 c1 = *reinterpret_cast<const bf16x8*>(sLt + (base + j) * TSTR + base + 8);
     float col[16], acc[16], t[16];
@@ -923,14 +940,14 @@ __device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, const 
         col[8 + e] = (float)c1[e];
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[i] = col[i];
     // two wait states between the VALU writes of col and its first DPP read; the operands pin the
     // writes before this point
     asm volatile("s_nop 1"
                  : "+v"(col[0]), "+v"(col[1]), "+v"(col[2]), "+v"(col[3]), "+v"(col[4]), "+v"(col[5]),
                    "+v"(col[6]), "+v"(col[7]), "+v"(col[8]), "+v"(col[9]), "+v"(col[10]), "+v"(col[11]),
                    "+v"(col[12]), "+v"(col[13]), "+v"(col[14]), "+v"(col[15]));
-    solve_steps(col, f, acc, t, j, std::make_integer_sequence<int, 16>{});
+    solve_steps(col, f, acc, t, std::make_integer_sequence<int, 16>{});
     if (lane < 32) {
         bf16x8 lo, hi;
 #pragma unroll
@@ -938,16 +955,17 @@ __device__ __forceinline__ void solve_diag(const __bf16* sLt, __bf16* Tt, const 
             lo[e] = (__bf16)t[e];
             hi[e] = (__bf16)t[8 + e];
         }
-        *reinterpret_cast<bf16x8*>(Tt + (base + j) * TSTR + base) = lo;
-        *reinterpret_cast<bf16x8*>(Tt + (base + j) * TSTR + base + 8) = hi;
+        __bf16* row = Tt + (base + j) * TSTR + base;
+        *reinterpret_cast<bf16x8*>(row) = lo;
+        *reinterpret_cast<bf16x8*>(row + 8) = hi;
+        row[j] = (__bf16)1.f;  // T = I + (z columns): after the row's store, in the wave's order
     }
 }
 
 // Solve level 1: T_{b+1,b} = -T_{b+1,b+1} (L_{b+1,b} T_{b,b}) for the 16x16 block pair (b, b+1)
 // (L' = diag(f) G_m: the row factor is applied to the first product).  bf16 operands (K = 16 real,
 // padded to 32 with zeros).
-__device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, const float* rk, const float* beta, int b,
-                                             int lane) {
+__device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, const float* fr, int b, int lane) {
     lane = opaque(lane);
     const int g = lane / 16, l16 = lane % 16;
     const int r0 = 16 * (b + 1), c0 = 16 * b;
@@ -962,7 +980,7 @@ __device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, cons
         bt = zb;
     }
     float f[4];
-    row_factors<1>(f, rk, beta, r0 + 4 * g);
+    row_factors<1>(f, fr, r0 + 4 * g);
     const fx4 y = mfma(a, bt, zero4()) * fx4{f[0], f[1], f[2], f[3]};  // rows r0 + 4g + e
     // T_{b+1,b} = -T_{b+1,b+1} Y: A = rows of T_{b+1,b+1} (chain order, k = 4g+e real), B = Y
     const bf16x4 tr = tr4(Tt, TSTR, r0 + 4 * g, r0, l16);  // T[r0 + l16][r0 + 4g .. +3]
@@ -979,11 +997,11 @@ __device__ __forceinline__ void solve_level1(const __bf16* sLt, __bf16* Tt, cons
 
 // Prep wave 2: L'_BA = diag(f) G_m (rows 32..63, columns 0..31) into the T_BA block of T^T, which the
 // state waves read in its place (U'_B = T'_BB (Y_B - L'_BA U'_A)).  Both are stored transposed.
-__device__ __forceinline__ void copy_LBA(const __bf16* sLt, __bf16* Tt, const float* rk, const float* beta, int lane) {
+__device__ __forceinline__ void copy_LBA(const __bf16* sLt, __bf16* Tt, const float* fr, int lane) {
     lane = opaque(lane);
     const int m = lane / 2, c = 32 + 16 * (lane % 2);
     float f[16];
-    row_factors<4>(f, rk, beta, c);
+    row_factors<4>(f, fr, c);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(sLt + m * TSTR + c + 8 * hf);
@@ -1986,17 +2004,15 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 __builtin_amdgcn_s_setprio(3);
                 const __bf16* sLt = reinterpret_cast<const __bf16*>(sm + S::L);
                 __bf16* Tt = reinterpret_cast<__bf16*>(sm + S::T);
-                const float* rk = reinterpret_cast<const float*>(sm + S::WL);
-                const float* beta = reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB);
-                solve_diag(sLt, Tt, rk, beta, 2 * pw, lane);
+                const float* fr = reinterpret_cast<const float*>(sm + S::WL) + 2 * C;  // f of L'
+                solve_diag(sLt, Tt, fr, 2 * pw, lane);
                 wave_sync();  // the level-1 products read the diagonal blocks other lanes wrote
-                solve_level1(sLt, Tt, rk, beta, 2 * pw, lane);
+                solve_level1(sLt, Tt, fr, 2 * pw, lane);
                 __builtin_amdgcn_s_setprio(0);
             }
             if (nxt && pw == 2)
                 copy_LBA(reinterpret_cast<const __bf16*>(sm + S::L), reinterpret_cast<__bf16*>(sm + S::T),
-                         reinterpret_cast<const float*>(sm + S::WL),
-                         reinterpret_cast<const float*>(sm + S::raw(k + 1) + S::rB), lane);
+                         reinterpret_cast<const float*>(sm + S::WL) + 2 * C, lane);
             if (nxt && pw == 3) make_gates<DK, BV>(sm + S::raw(k + 1), sm + S::gates(k + 1), sm, lane, p.l2norm);
             // Pm and rq of chunk 0, formed in sub-stage A (rewritten in the next iteration's), by
             // the solve waves, which have time to spare here and never wait for their stores
