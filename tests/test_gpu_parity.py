@@ -65,6 +65,18 @@ def test_bf16_ragged_varlen(dk, dv):
     np.testing.assert_array_equal(s[1], wl.s0[1])
 
 
+@pytest.mark.parametrize("dk,dv,segs", [(128, 128, 0), (64, 32, 0), (128, 128, 3), (128, 64, 2)])
+def test_bf16_output_scale(dk, dv, segs):
+    """A negative, non-unit output scale.  The chunk kernels carry it inside the prepared output
+    operands (Pm' and the state part's row factors), including the first-chunk operands that the
+    first pass keeps for the segment reruns, so the segmented cases cover those too."""
+    wl = W.make("bf16_scale", seed=500 + dk + dv + segs, N=2, T=700, H=3, dk=dk, dv=dv, dtype="bf16", s0_std=0.02)
+    o, s = TL.run_gpu(wl, scale=-0.37, segments=segs)
+    o_ref, s_ref = TL.run_oracle(wl, scale=-0.37)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("bf16 scale -0.37 %d %d segs=%d %s" % (dk, dv, segs, e))
+
+
 def test_bf16_conv_varlen_small():
     wl = W.varlen(lengths=[520, 64, 7, 1000], H=4)
     o, s = TL.run_gpu(wl)
