@@ -76,6 +76,23 @@ def test_raw_gates_prefill_segments():
         _flush("raw_gates segments=%d %s" % (segs, e))
 
 
+def test_raw_gates_segments_slow_decay():
+    """Raw gates with slow decay (A_log = log 1e-3, so g is about -1e-3 per token): no segment's
+    transition is negligible, so the transition pass runs in full on its raw-gate instantiation
+    (no output work), and the reruns cover whole segments."""
+    wl = W.make("raw_gates_slow", seed=412, lengths=[64 * 12 + 9, 64 * 5], H=2, dk=128, dv=128, dtype="bf16",
+                s0_std=0.02, varlen=True)
+    a, b, gp = W.raw_gate_inputs(wl.meta["seed"], wl.lengths, wl.H)
+    gp = gp.copy()
+    gp[0, :] = np.log(1e-3)
+    g, beta = _oracle_gates(a, b, gp)
+    assert g.max() < 0.0 and g.min() > -0.05, (g.min(), g.max())
+    o_ref, s_ref = _oracle(wl, g, beta)[:2]
+    o, s = _prefill(wl, g=a, beta=b, gate_params=gp, segments=3)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("raw_gates slow decay segments=3 %s" % e)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_raw_gates_decode(dtype):
     from linear_attention_sequence_rule_amd import gdn_recurrent_step

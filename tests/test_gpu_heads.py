@@ -55,16 +55,22 @@ def test_grouped_heads_prefill(dtype, H, Hk, dk, dv, conv):
     _flush("gqa %s H=%d Hk=%d %d %d conv=%s %s" % (dtype, H, Hk, dk, dv, conv, e))
 
 
-def test_grouped_heads_prefill_segments():
+@pytest.mark.parametrize("slow", [False, True])
+def test_grouped_heads_prefill_segments(slow):
+    """Grouped heads on the segmented path; with `slow`, value head 1 (query/key head 0) decays at
+    g = -1.5e-3, so its transitions are not negligible and the transition pass (which loads only
+    the shared K) and full reruns run for it beside the fast heads."""
     wl = W.make("gqa_seg", seed=531, lengths=[64 * 40 + 9, 300], H=4, Hk=2, dk=128, dv=128, dtype="bf16",
                 s0_std=0.02, conv=True, varlen=True)
+    if slow:
+        wl.g[:, 1] = -1.5e-3
     hist = W.conv_inputs(531, wl.N, 4, 128, 128, "bf16", Hk=2)[1]
     ref = _oracle(wl, hist)
     for segs in (1, 4):
         o, s, cs = _run(wl, conv_state=hist, segments=segs)
         e = TL.compare(wl, o, s, ref[0], ref[1])
         np.testing.assert_array_equal(_hist_to_f64(cs), ref[3])
-        _flush("gqa segments=%d %s" % (segs, e))
+        _flush("gqa segments=%d slow=%s %s" % (segs, slow, e))
 
 
 @pytest.mark.parametrize("dtype,H,Hk,dk,dv,conv", [
