@@ -91,8 +91,9 @@ def record_traffic(d, out_path=None):
     """profiles/traffic.json from four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, KiB per
     dispatch, over a short bench run and over the plain-copy calibration).  The copy calibration
     gives the scale of each counter: bytes the copy moves each way / what the counter reads.  A
-    prefill call is its chunk_bf16 dispatches (main, transition and rerun pass: the rerun pass,
-    the one instantiation with the rerun code, is counted once per call)."""
+    prefill call is its chunk_bf16 dispatches: the main pass, then the transition and rerun passes
+    in one launch (chunk_bf16_tail_kernel, counted once per call); where those two run as launches
+    of their own, the rerun pass, the one instantiation with the rerun code, is counted instead."""
     import csv
     from collections import defaultdict
 
@@ -111,14 +112,20 @@ def record_traffic(d, out_path=None):
     fetch, write = load("fetch"), load("write")
     for tag, src, also in (("chunk_bf16_kernel", "chunk_bf16.hip", ("segments.hip", "api.hip")),
                            ("step_kernel", "step.hip", ())):
-        fb = sum(v for (_, n), v in fetch.items() if tag in n) * 1024.0 * scale["FETCH_SIZE"]
-        wb = sum(v for (_, n), v in write.items() if tag in n) * 1024.0 * scale["WRITE_SIZE"]
+        tags = (tag, "chunk_bf16_tail_kernel") if tag == "chunk_bf16_kernel" else (tag,)
+        fb = sum(v for (_, n), v in fetch.items() if any(t in n for t in tags)) * 1024.0 * scale["FETCH_SIZE"]
+        wb = sum(v for (_, n), v in write.items() if any(t in n for t in tags)) * 1024.0 * scale["WRITE_SIZE"]
         if tag == "chunk_bf16_kernel":
-            # the rerun pass has the only instantiation with rerun code: template argument LEAN
-            # (the fifth: <DK, BV, RAW, EPI, LEAN, ...>) false
-            calls_f = sum(1 for (_, n) in fetch if tag in n and _rerun_instantiation(n))
-            calls_w = sum(1 for (_, n) in write if tag in n and _rerun_instantiation(n))
-            per = "prefill step: main pass + transition pass + rerun pass"
+            calls_f = sum(1 for (_, n) in fetch if "chunk_bf16_tail_kernel" in n)
+            calls_w = sum(1 for (_, n) in write if "chunk_bf16_tail_kernel" in n)
+            per = "prefill step: main pass + transition and rerun passes (one launch)"
+            if not calls_f:
+                # separate transition and rerun launches: the rerun pass has the only
+                # instantiation with rerun code, template argument LEAN (the fifth:
+                # <DK, BV, RAW, EPI, LEAN, ...>) false
+                calls_f = sum(1 for (_, n) in fetch if tag in n and _rerun_instantiation(n))
+                calls_w = sum(1 for (_, n) in write if tag in n and _rerun_instantiation(n))
+                per = "prefill step: main pass + transition pass + rerun pass"
         else:
             calls_f = sum(1 for (_, n) in fetch if tag in n)
             calls_w = sum(1 for (_, n) in write if tag in n)

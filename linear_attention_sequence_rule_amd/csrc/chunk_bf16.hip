@@ -314,9 +314,19 @@ struct Params {
                           // segment 0 while the last segment would write it): the first pass then
                           // keeps B_{P-1} in its slot of s0 and the rerun of the last segment always
                           // writes the final state (a copy of B_{P-1} where A_{P-1} is negligible)
+    // transition and rerun in one launch (chunk_bf16_tail_kernel): a workgroup that forms its
+    // pair's transition adds its completion to the pair's mark, and a rerun waits for the marks it
+    // reads (wait_transitions)
+    int tr_signal;  // transition: add 4 (+ stopped, first row block) to negl[pair] at the end
+    int tr_wait;    // rerun: the mark of a pair whose transition has finished is >= this (0: no wait)
     float scale;
     int l2norm;
 };
+
+// A pair's mark: 1 = negligible from the first pass's gate bound; otherwise 0 until its transition
+// workgroups finish (in a launch of their own: 0 or 1 = whether they stopped at the bound; with
+// the reruns in the same launch: 4 per workgroup plus that bit).  Bit 0 says negligible.
+__device__ __forceinline__ bool mark_negligible(int m) { return (m & 1) != 0; }
 
 // ------------------------------------------------------------------------------------------
 // chunk loads: direct global -> LDS (global_load_lds_dwordx4 / _dword).  One instruction moves
@@ -1474,7 +1484,7 @@ __device__ void chain_states(const Params<DK>& p, unsigned char* sm, int n, int 
     }
     for (int j = j0 + 1; j <= j1; ++j) {
         const float* Bj = bj(j);
-        if (p.marks[slot(j)]) {  // A_j negligible
+        if (mark_negligible(p.marks[slot(j)])) {  // A_j negligible
             lazy = j;
         } else {
             held();
@@ -1517,6 +1527,60 @@ __device__ void chain_states(const Params<DK>& p, unsigned char* sm, int n, int 
     lds_barrier();  // LDS is free again
 }
 
+
+// Spin bound of wait_transitions: each poll sleeps ~1,000 clocks, so about 10-20 s in all.
+constexpr unsigned kWaitSpins = 1u << 23;
+
+// A rerun in the launch of the transitions (Params::tr_wait) waits for the transitions A_j, j <= j1,
+// that its entering state may need: each is formed by the workgroup of segment j's pair, whose
+// block index lies below this one's (same head, earlier segment), before that workgroup waits for
+// anything (at most the one-chunk rerun, which never waits, comes first).  The workgroups of a
+// launch start in index order on each XCD, so every transition that a rerun waits for runs to its
+// end.  Wave 0 polls the marks (lane j - 1 that of
+// segment j) until each is 1 (negligible by the first pass: no transition runs) or at least tr_wait
+// (every workgroup of its transition has counted itself), then its acquire fence invalidates the
+// caches that could hold stale lines of the transitions; the verdict goes to the other waves
+// through LDS word 0, so that all take the same path.  False if a mark did not get there within
+// the spin bound.  Called by every thread, with LDS free.
+template <int DK>
+__device__ bool wait_transitions(const Params<DK>& p, unsigned char* sm, int n, int h, int j1, int tid) {
+    int* verdict = reinterpret_cast<int*>(sm);
+    if (tid < 64) {
+        bool late = false;
+        for (int j = 1 + tid; j <= j1; j += 64) {
+            int* m = const_cast<int*>(p.marks) + (size_t)(n * p.P + j) * p.H + h;
+            for (unsigned spin = 0;; ++spin) {
+                const int v = __hip_atomic_load(m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v == 1 || v >= p.tr_wait) break;
+                if (spin >= kWaitSpins) {
+                    late = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(16);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const bool ok = __ballot(late) == 0;
+        if (tid == 0) *verdict = ok ? 1 : 0;
+    }
+    lds_barrier();
+    const bool ok = *reinterpret_cast<volatile int*>(verdict) != 0;
+    lds_barrier();  // LDS free again
+    return ok;
+}
+
+// A rerun whose wait ran out: NaN in its outputs (and the final state's rows, for the last
+// segment) instead of a result formed from unfinished transitions.
+template <int DK, int BV>
+__device__ void poison_segment(const Params<DK>& p, int n, int h, int vb, long bos, long eos, bool last, int tid) {
+    constexpr int NT = kernel_threads<BV>();
+    const __bf16 qnan = __builtin_bit_cast(__bf16, (unsigned short)0x7fc0);
+    for (long i = tid; i < (eos - bos) * BV; i += NT)
+        p.o[((bos + i / BV) * p.H + h) * p.dv + vb * BV + i % BV] = qnan;
+    if (last)
+        for (int i = tid; i < BV * DK; i += NT)
+            p.fin[((size_t)n * p.H + h) * p.dv * DK + (size_t)vb * BV * DK + i] = __builtin_nanf("");
+}
 
 // Rerun of segment p >= 1 when the bound on the transition of its first chunk is already below
 // 2^-40: from the state entering the segment (E_{p-1}, rows at ein), only that chunk's outputs change,
@@ -1619,8 +1683,15 @@ __device__ bool rerun_first_chunk(const Params<DK>& p, unsigned char* sm, const 
 // no trace of the gate transform).  EPI: the output epilogue.  LEAN: without the rerun pass's code
 // (entering states, the one-chunk rerun); the first and transition passes without the epilogue
 // run this one: the chunk loop schedules better without that code beside it.
-template <int DK, int BV, bool RAW, bool EPI, bool LEAN, bool TRANS = false>
-__global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params<DK> p) {
+// What chunk_body runs of a rerun (Params::init = INIT_PREV) and what it reports: BODY_FAST tries
+// only the one-chunk rerun of the usual case, BODY_REST skips that attempt; the result has BODY_DONE
+// once the segment's outputs are final, and BODY_TRANS where the pair's own transition may still
+// be needed (the transition pass itself decides).
+enum BodyPhase { BODY_ALL = 0, BODY_FAST = 1, BODY_REST = 2 };
+enum BodyResult { BODY_DONE = 1, BODY_TRANS = 2 };
+
+template <int DK, int BV, bool RAW, bool EPI, bool LEAN, bool TRANS>
+__device__ __forceinline__ int chunk_body(const Params<DK>& p, const int b, const int phase = BODY_ALL) {
     using S = Smem<DK, BV>;
     // TRANS: the transition pass (no output): nothing of Q, Pm' or O is formed
     constexpr bool OUT = !TRANS;
@@ -1640,7 +1711,6 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     // group count allows it.
     const int ngroups = p.N * p.P * p.Hk, wpg = p.grp * p.nv;
     int group, within;
-    const int b = blockIdx.x;
     if (ngroups % 8 == 0) {
         group = (b / (8 * wpg)) * 8 + b % 8;
         within = (b / 8) % wpg;
@@ -1660,8 +1730,8 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         pair = n * p.H + h;
     }
     const int nseg = pair / p.H;
-    if (p.skip_first && seg == 0) return;
-    if (p.negl_mode == NEGL_SKIP && p.negl[pair]) return;  // the segment's transition is negligible
+    if (p.skip_first && seg == 0) return BODY_DONE;
+    if (p.negl_mode == NEGL_SKIP && p.negl[pair]) return BODY_DONE;  // the segment's transition is negligible
     long bos, eos;
     if (p.cu) {
         bos = p.cu[n];
@@ -1695,26 +1765,34 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     if constexpr (!LEAN) {
         // The usual case, taken on trust while its loads are in flight: E_{seg-1} = B_{seg-1} in
         // place, no final state to chain, and the first chunk reaches the bound.
-        if (fast_ok && p.marks) {
+        if (phase != BODY_REST && fast_ok && p.marks) {
+            bool own_negl = false;  // this segment's own transition negligible by the first pass
             auto usual = [&]() {
-                const int mprev = p.marks[(size_t)(n * p.P + seg - 1) * p.H + h];
-                const int mlast = p.fin && seg == p.P - 1 ? (p.fin_in_slot ? 0 : p.marks[pair]) : 1;
+                own_negl = mark_negligible(p.marks[pair]);
+                const bool mprev = mark_negligible(p.marks[(size_t)(n * p.P + seg - 1) * p.H + h]);
+                const bool mlast = p.fin && seg == p.P - 1 ? (!p.fin_in_slot && mark_negligible(p.marks[pair])) : true;
                 const float b0 = kept_bound();
-                return (seg == 1 || mprev != 0) && mlast != 0 && b0 <= kExitLog;
+                return (seg == 1 || mprev) && mlast && b0 <= kExitLog;
             };
-            if (rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, tid, usual)) return;
+            if (rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, tid, usual))
+                return BODY_DONE | (own_negl ? 0 : BODY_TRANS);
         }
+        if (phase == BODY_FAST) return BODY_TRANS;
     }
     if (!LEAN && p.marks && seg > 0) {
         // the loads this choice needs, issued together
         const bool last = p.fin && seg == p.P - 1;
-        const int mprev = p.marks[(size_t)(n * p.P + seg - 1) * p.H + h];
-        const int mlast = last ? (p.fin_in_slot ? 0 : p.marks[pair]) : 1;
+        if (p.tr_wait && !wait_transitions<DK>(p, sm, n, h, last ? seg : seg - 1, tid)) {
+            poison_segment<DK, BV>(p, n, h, vb, bos, eos, last, tid);
+            return BODY_DONE;
+        }
+        const bool mprev = mark_negligible(p.marks[(size_t)(n * p.P + seg - 1) * p.H + h]);
+        const bool mlast = last ? (!p.fin_in_slot && mark_negligible(p.marks[pair])) : true;
         int j0 = seg - 1;
         if (j0 > 0 && !mprev)
             do --j0;
-            while (j0 > 0 && !p.marks[(size_t)(n * p.P + j0) * p.H + h]);
-        const bool fin = mlast == 0;  // else B_{P-1}, in place, is the final state
+            while (j0 > 0 && !mark_negligible(p.marks[(size_t)(n * p.P + j0) * p.H + h]));
+        const bool fin = !mlast;  // else B_{P-1}, in place, is the final state
         // (with fin_in_slot the chain to the final state runs even where A_{P-1} is negligible:
         // it then copies B_{P-1} from its slot)
         if (j0 < seg - 1 || fin) {
@@ -1727,7 +1805,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
     }
     if (fast_ok && kept_bound() <= kExitLog) {
         if constexpr (!LEAN) rerun_first_chunk<DK, BV, EPI>(p, sm, kept, bos, clen(0), h, hk, vb, ein, tid, [] { return true; });
-        return;
+        return BODY_DONE;
     }
     // the first pass keeps its first chunk's prepared operands for the rerun (one copy per head)
     const bool keep = p.pre_mode == PRE_KEEP && seg > 0 && vb == 0;
@@ -1803,6 +1881,7 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
             decay += __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
                                                    int, reinterpret_cast<const float*>(sm + S::gates(k) + S::gGC)[1])));
     };
+    int stopped = 0;  // the chain stopped at the decay bound (row waves)
     if (!is_prep) {
         RowRegs<DK> st;
         const int row = vb * BV + 16 * wid + l16;  // state row of this lane (row waves)
@@ -1825,7 +1904,6 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 }
             }
         }
-        int stopped = 0;
         int pend = -1;  // epilogue: the chunk whose outputs st.ot holds, stored after the next barrier
         for (int k = -1; k < nchunks; ++k) {
             const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
@@ -1942,7 +2020,11 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
                 *reinterpret_cast<float4*>(dst + kcol(dt, 4 * g)) = make_float4(v[0], v[1], v[2], v[3]);
             }
         }
-        if (p.negl && vb == 0 && tid == 0) p.negl[pair] = p.negl_mode == NEGL_MARK ? (decay <= kExitLog) : stopped;
+        if (p.negl && vb == 0 && tid == 0 && !p.tr_signal)
+            p.negl[pair] = p.negl_mode == NEGL_MARK ? (decay <= kExitLog) : stopped;
+        // this wave's stores of A_j have reached L2 (vmcnt counts stores) before the workgroup
+        // counts itself; the count's release then writes L2 back once for the whole workgroup
+        if (p.tr_signal) wait_loads();
     } else {
         for (int k = -1; k < nchunks; ++k) {
             const bool cur = k >= 0, nxt = k + 1 < nchunks, far = k + 2 < nchunks;
@@ -2037,6 +2119,39 @@ __global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params
         // the workgroup has ended
         wait_loads();
     }
+    if (p.tr_signal) {
+        // every row wave's rows of A_j are in L2 (above): count this workgroup into the mark
+        lds_barrier();
+        if (tid == 0)
+            __hip_atomic_fetch_add(p.negl + pair, 4 + (vb == 0 ? stopped : 0), __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return BODY_DONE;
+}
+
+template <int DK, int BV, bool RAW, bool EPI, bool LEAN, bool TRANS = false>
+__global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_kernel(Params<DK> p) {
+    chunk_body<DK, BV, RAW, EPI, LEAN, TRANS>(p, blockIdx.x);
+}
+
+// The transition and rerun passes of the segmented path in one launch (d_k = d_v, so both passes
+// map a block to the same (segment, head, row block)).  A block first tries the one-chunk rerun of
+// the usual case (nothing to wait for); then, where the first pass left its pair's transition marked
+// not negligible, it forms that transition and counts itself into the mark; then, if the first try
+// did not apply, it reruns its segment, waiting where that needs a transition of an earlier segment
+// (wait_transitions).  In the usual case, where the first pass marked every transition negligible,
+// a block reads the marks with the rerun's loads in flight and forms no transition.
+template <int DK, int BV, bool RAW, bool EPI>
+__global__ __launch_bounds__(kernel_threads<BV>()) void chunk_bf16_tail_kernel(Params<DK> pt, Params<DK> pr) {
+    const int r = chunk_body<DK, BV, RAW, EPI, false, false>(pr, blockIdx.x, BODY_FAST);
+    if (r & BODY_TRANS) {
+        lds_barrier();  // LDS free for the transition
+        chunk_body<DK, BV, RAW, false, true, true>(pt, blockIdx.x);
+    }
+    if (!(r & BODY_DONE)) {
+        lds_barrier();  // LDS free for the rerun
+        chunk_body<DK, BV, RAW, EPI, false, false>(pr, blockIdx.x, BODY_REST);
+    }
 }
 
 template <int DK, int BV, bool RAW, bool EPI, bool LEAN, bool TRANS>
@@ -2082,7 +2197,7 @@ struct Pass {
 };
 
 template <int DK, int BV>
-hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
+Params<DK> make_params(const ChunkArgs& a, const Pass& c) {
     Params<DK> p;
     p.q = static_cast<const __bf16*>(a.q);
     p.k = static_cast<const __bf16*>(a.k);
@@ -2118,19 +2233,34 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     p.ein = c.ein;
     p.fin = c.fin;
     p.fin_in_slot = c.fin_in_slot;
+    p.tr_signal = 0;
+    p.tr_wait = 0;
     p.scale = a.scale;
     p.l2norm = a.l2norm;
-    // the output epilogue in the kernel: wide workgroups of a pass that stores o
-    const bool epi = Smem<DK, BV>::WIDE && a.out_gate && c.out == OUT_STORE;
     p.out_gate = static_cast<const __bf16*>(a.out_gate);
     p.norm_weight = a.norm_weight;
     p.norm_eps = a.norm_eps;
-    const int smem = Smem<DK, BV>::bytes;
+    return p;
+}
+
+// the LDS a workgroup of this width needs (160 KiB on gfx950)
+template <int DK, int BV>
+hipError_t check_lds() {
     DeviceInfo dinfo;
     const hipError_t e = current_device_info(&dinfo);
     if (e != hipSuccess) return e;
-    if (dinfo.lds_max < smem) return hipErrorInvalidConfiguration;  // needs the 160 KiB LDS of gfx950
+    return dinfo.lds_max < Smem<DK, BV>::bytes ? hipErrorInvalidConfiguration : hipSuccess;
+}
+
+template <int DK, int BV>
+hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
+    const Params<DK> p = make_params<DK, BV>(a, c);
+    const int smem = Smem<DK, BV>::bytes;
+    const hipError_t e = check_lds<DK, BV>();
+    if (e != hipSuccess) return e;
     const int grid = a.N * c.P * a.H * p.nv;
+    // the output epilogue in the kernel: wide workgroups of a pass that stores o
+    const bool epi = Smem<DK, BV>::WIDE && a.out_gate && c.out == OUT_STORE;
     if (epi) {
         if constexpr (Smem<DK, BV>::WIDE) return launch_k<DK, BV, true>(p, a, grid, smem);
         return hipErrorInvalidValue;
@@ -2138,13 +2268,64 @@ hipError_t launch_t(const ChunkArgs& a, const Pass& c) {
     return launch_k<DK, BV, false>(p, a, grid, smem);
 }
 
+template <int DK, int BV, bool RAW, bool EPI>
+hipError_t launch_tail_one(const Params<DK>& pt, const Params<DK>& pr, const ChunkArgs& a, int grid) {
+    const int smem = Smem<DK, BV>::bytes;
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(&chunk_bf16_tail_kernel<DK, BV, RAW, EPI>), smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_bf16_tail_kernel<DK, BV, RAW, EPI>), dim3(grid), dim3(kernel_threads<BV>()), smem,
+                       a.stream, pt, pr);
+    return hipGetLastError();
+}
+
+// The transition pass ct and the rerun pass cr in one launch (d_k = d_v: the same workgroups).
+template <int DK, int BV>
+hipError_t launch_tail_t(const ChunkArgs& a, const Pass& ct, const Pass& cr) {
+    Params<DK> pt = make_params<DK, BV>(a, ct), pr = make_params<DK, BV>(a, cr);
+    pt.tr_signal = 1;
+    pr.tr_wait = 4 * pt.nv;
+    const hipError_t e = check_lds<DK, BV>();
+    if (e != hipSuccess) return e;
+    const int grid = a.N * cr.P * a.H * pr.nv;
+    if constexpr (Smem<DK, BV>::WIDE) {
+        if (a.out_gate)
+            return a.gate_params ? launch_tail_one<DK, BV, true, true>(pt, pr, a, grid)
+                                 : launch_tail_one<DK, BV, false, true>(pt, pr, a, grid);
+    }
+    return a.gate_params ? launch_tail_one<DK, BV, true, false>(pt, pr, a, grid)
+                         : launch_tail_one<DK, BV, false, false>(pt, pr, a, grid);
+}
+
 // 128 state rows per workgroup where chunk_rows_per_workgroup allows, else 64, or 32 when the
 // pass has a 32-row state
 template <int DK>
+int width_for(int rows) {
+    if (DK == 128 && chunk_rows_per_workgroup(DK, rows) == BVW) return BVW;
+    return rows >= 64 ? 64 : 32;
+}
+
+template <int DK>
 hipError_t launch_rows(const ChunkArgs& a, const Pass& c) {
     if constexpr (DK == 128)
-        if (chunk_rows_per_workgroup(DK, c.rows) == BVW) return launch_t<DK, BVW>(a, c);
+        if (width_for<DK>(c.rows) == BVW) return launch_t<DK, BVW>(a, c);
     return c.rows >= 64 ? launch_t<DK, 64>(a, c) : launch_t<DK, 32>(a, c);
+}
+
+// The transition pass and the rerun: one launch where d_k = d_v (the two passes then have the same
+// workgroups), else one launch each.
+template <int DK>
+hipError_t launch_tail(const ChunkArgs& a, const Pass& ct, const Pass& cr) {
+    const int w = width_for<DK>(ct.rows);
+    if (ct.rows == cr.rows) {
+        if constexpr (DK == 128) {
+            if (w == BVW) return launch_tail_t<DK, BVW>(a, ct, cr);
+        } else {
+            return w == 64 ? launch_tail_t<DK, 64>(a, ct, cr) : launch_tail_t<DK, 32>(a, ct, cr);
+        }
+    }
+    hipError_t e = launch_rows<DK>(a, ct);
+    if (e == hipSuccess) e = launch_rows<DK>(a, cr);
+    return e;
 }
 
 template <int DK>
@@ -2182,11 +2363,10 @@ hipError_t run(const ChunkArgs& a, int P) {
                                            keep ? PRE_KEEP : PRE_NONE, nullptr, nullptr, nullptr,
                                            in_slot ? nullptr : a.sfin, 0});
     if (e == hipSuccess)
-        e = launch_rows<DK>(a, Pass{P, INIT_IDENTITY, OUT_NONE, 1, ex, 1, NEGL_SKIP, a.dk, nullptr, A, negl});
-    if (e == hipSuccess)
-        e = launch_rows<DK>(a, Pass{P, INIT_PREV, OUT_STORE, 0, ex, 1, NEGL_NONE, a.dv, E, nullptr, nullptr, pre,
-                                    keep ? PRE_USE : PRE_NONE, negl, A, reinterpret_cast<float*>(ws + L.off_ein),
-                                    a.sfin, in_slot});
+        e = launch_tail<DK>(a, Pass{P, INIT_IDENTITY, OUT_NONE, 1, ex, 1, NEGL_SKIP, a.dk, nullptr, A, negl},
+                            Pass{P, INIT_PREV, OUT_STORE, 0, ex, 1, NEGL_NONE, a.dv, E, nullptr, nullptr, pre,
+                                 keep ? PRE_USE : PRE_NONE, negl, A, reinterpret_cast<float*>(ws + L.off_ein), a.sfin,
+                                 in_slot});
     return e;
 }
 

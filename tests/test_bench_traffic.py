@@ -1,6 +1,8 @@
 """bench.py --record-traffic on synthetic rocprofv3 counter files (CPU): the per-call bytes of the
-chunk kernels (three dispatches per prefill call, the rerun pass being the one instantiation
-with rerun code) and of the decode kernel, each scaled by the plain-copy calibration."""
+chunk kernels (two dispatches per prefill call, the main pass and the launch that holds the
+transition and rerun passes; or three, the rerun pass being the one instantiation with rerun code,
+where those two run as launches of their own) and of the decode kernel, each scaled by the
+plain-copy calibration."""
 import csv
 import json
 import os
@@ -15,6 +17,8 @@ HEADER = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id",
 MAIN = "void gdn::(anonymous namespace)::chunk_bf16_kernel<128, 128, false, false, true, false>(gdn::Params<128>)"
 TRANS = "void gdn::(anonymous namespace)::chunk_bf16_kernel<128, 128, false, false, true, true>(gdn::Params<128>)"
 RERUN = "void gdn::(anonymous namespace)::chunk_bf16_kernel<128, 128, false, false, false, false>(gdn::Params<128>)"
+TAIL = ("void gdn::(anonymous namespace)::chunk_bf16_tail_kernel<128, 128, false, false>(gdn::Params<128>, "
+        "gdn::Params<128>)")
 STEP = "void gdn::step_kernel<128, 128, gdn::bf16, false, false>(gdn::bf16 const*)"
 COPY = "__amd_rocclr_copyBuffer"
 
@@ -30,13 +34,16 @@ def _write(path, counter, rows):
                 w.writerow([d, d, 1, 1, 1, 1, 64, 1, name, 256, 0, 0, 0, 0, 0, counter, kib * part, 0, 1])
 
 
-def test_record_traffic(tmp_path):
+@pytest.mark.parametrize("fused", [True, False])
+def test_record_traffic(tmp_path, fused):
     d = str(tmp_path)
     # calibration: a 1 GiB copy that FETCH_SIZE reports as half its bytes, WRITE_SIZE exactly
     _write(os.path.join(d, "cfetch", "run_counter_collection.csv"), "FETCH_SIZE", [(COPY, 524288.0)] * 3)
     _write(os.path.join(d, "cwrite", "run_counter_collection.csv"), "WRITE_SIZE", [(COPY, 1048576.0)] * 3)
-    # two prefill calls (main, transition, rerun) and one decode step, KiB per dispatch
-    calls = [(MAIN, 100.0), (TRANS, 1.0), (RERUN, 10.0)] * 2 + [(STEP, 50.0)]
+    # two prefill calls (main, then transition + rerun in one launch or in two) and one decode step,
+    # KiB per dispatch
+    tail = [(TAIL, 11.0)] if fused else [(TRANS, 1.0), (RERUN, 10.0)]
+    calls = ([(MAIN, 100.0)] + tail) * 2 + [(STEP, 50.0)]
     _write(os.path.join(d, "fetch", "run_counter_collection.csv"), "FETCH_SIZE", calls)
     _write(os.path.join(d, "write", "run_counter_collection.csv"), "WRITE_SIZE",
            [(n, k / 2) for n, k in calls])
