@@ -157,6 +157,21 @@ def test_bf16_segments_slow_decay_mixed():
     _flush("segments slow %s" % e)
 
 
+@pytest.mark.parametrize("dk", [32, 64, 128])
+def test_bf16_segments_queued_slow_decay(dk):
+    """d_k = d_v: the transition and rerun passes share one launch.  3 sequences x 8 segments x 16
+    heads = 384 workgroups, more than the 256 compute units hold at once (one per unit at every
+    width), and every third head decays slowly (g = -1e-3), so its transitions are formed in full
+    and the reruns of later segments wait for them, some of them for workgroups that start only
+    after others have begun to wait."""
+    wl = W.make("seg_queue", seed=50 + dk, N=3, T=1024, H=16, dk=dk, dv=dk, dtype="bf16", s0_std=0.02)
+    wl.g[:, ::3] = -1e-3
+    o, s = TL.run_gpu(wl, segments=8)
+    o_ref, s_ref = TL.run_oracle(wl)
+    e = TL.compare(wl, o, s, o_ref, s_ref)
+    _flush("segments queued slow dk=dv=%d %s" % (dk, e))
+
+
 @pytest.mark.parametrize("dk,dv", [(64, 128), (32, 32), (128, 128)])
 def test_bf16_segments_varlen(dk, dv):
     wl = W.make("seg_var", seed=48 + dk, lengths=[300, 0, 64, 1, 700], H=2, dk=dk, dv=dv, dtype="bf16",
