@@ -1536,12 +1536,12 @@ constexpr unsigned kWaitSpins = 1u << 23;
 // block index lies below this one's (same head, earlier segment), before that workgroup waits for
 // anything (at most the one-chunk rerun, which never waits, comes first).  The workgroups of a
 // launch start in index order on each XCD, so every transition that a rerun waits for runs to its
-// end.  Wave 0 polls the marks (lane j - 1 that of
-// segment j) until each is 1 (negligible by the first pass: no transition runs) or at least tr_wait
-// (every workgroup of its transition has counted itself), then its acquire fence invalidates the
-// caches that could hold stale lines of the transitions; the verdict goes to the other waves
-// through LDS word 0, so that all take the same path.  False if a mark did not get there within
-// the spin bound.  Called by every thread, with LDS free.
+// end.  Wave 0 polls the marks (lane j - 1 that of segment j) until each is 1 (negligible by the
+// first pass: no transition runs) or at least tr_wait (every workgroup of its transition has
+// counted itself), then its acquire fence invalidates the caches that could hold stale lines of the
+// transitions; the verdict goes to the other waves through LDS word 0, so that all take the same
+// path.  False if a mark did not get there within the spin bound.  Called by every thread, with
+// LDS free.
 template <int DK>
 __device__ bool wait_transitions(const Params<DK>& p, unsigned char* sm, int n, int h, int j1, int tid) {
     int* verdict = reinterpret_cast<int*>(sm);
