@@ -198,6 +198,39 @@ def test_epilogue_prefill_raw_gates_conv_history():
            % (np.abs(og - ref).max(), excess.max()))
 
 
+def test_epilogue_raw_gates_slow_decay_queued():
+    """The transition and rerun passes in one launch on the instantiation with raw gates and the
+    epilogue: 3 sequences x 8 segments x 16 value heads = 384 workgroups (more than the compute
+    units hold at once) on 8 query/key heads, and every fourth head decaying slowly (A_log =
+    log 1e-3, g about -1e-3 per token), so those transitions are formed in full and later reruns
+    wait for them; the other heads' reruns redo one chunk from the kept operands."""
+    from linear_attention_sequence_rule_amd import gdn_chunk_fwd
+    import torch
+    wl = W.make("epi_raw_slow", seed=631, N=3, T=1024, H=16, Hk=8, dk=128, dv=128, dtype="bf16", s0_std=0.02,
+                varlen=True)
+    a, b, gp = W.raw_gate_inputs(631, wl.lengths, wl.H)
+    gp = gp.copy()
+    gp[0, ::4] = np.log(1e-3)
+    z, w = _epilogue_inputs(631, (wl.T_tot, wl.H), 128, "bf16")
+    o, sf = gdn_chunk_fwd(TL.to_dev(wl.q), TL.to_dev(wl.k), TL.to_dev(wl.v), TL.to_dev(a), TL.to_dev(b),
+                          TL.to_dev(wl.s0), TL.to_dev(wl.cu_seqlens), N=wl.N, gate_params=TL.to_dev(gp), segments=8,
+                          out_gate=TL.to_dev(z), norm_weight=TL.to_dev(w), norm_eps=1e-3)
+    torch.cuda.synchronize()
+    og, sg = TL.o_to_f64(o), sf.cpu().numpy().astype(np.float64)
+    g, beta = oracle.gates(a, b, gp[0], gp[1])
+    assert g[:, ::4].min() > -0.05 and g[:, 1::4].mean() < -0.2
+    cu = np.concatenate([[0], np.cumsum(wl.lengths)])
+    o_ref, s_ref, _ = oracle.forward(wl.as_float("q"), wl.as_float("k"), wl.as_float("v"), g, beta, wl.s0, cu)
+    TL.compare(wl, o_ref, sg, o_ref, s_ref)
+    ref = oracle.gated_norm(o_ref, _zf(z), w, 1e-3)
+    m = (1.0 + w.astype(np.float64)) / (1.0 + np.exp(-_zf(z).astype(np.float64)))
+    rms = np.sqrt((o_ref ** 2).mean(-1, keepdims=True) + 1e-3)
+    excess = np.abs(og - ref) / (2 * m * TL.BF16_O_ABS / rms + 2.0 ** -8 * np.abs(ref) + 1e-5)
+    assert excess.max() <= 1.0, excess.max()
+    _flush("epilogue raw gates slow decay queued: max err %.3g, max err/bound %.3g" % (np.abs(og - ref).max(),
+                                                                                      excess.max()))
+
+
 # ------------------------------------------------ the epilogue against the norm of the kernel's own o
 
 U_BF16 = 2.0 ** -8  # unit roundoff of bf16 (8 significant bits, round to nearest even)
